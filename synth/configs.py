@@ -1,0 +1,174 @@
+"""The five synthetic workloads and their seeded generators.
+
+Workloads (sizes as measured):
+  0. AdamW step over a tiny GPT parameter tree, f32 (V=92, D=64, L=2):
+     28 leaves, 108 032 parameters.
+  1. Causal row softmax, f32 scores [8,16,1024,1024] viewed as 131 072 rows x 1024.
+  2. AdamW step over a Llama-style tree (16 layers, D=2048, FFN 5632,
+     vocab 32000): 145 leaves, 887 685 120 parameters; bf16 param and grad,
+     f32 moments.
+  3. Residual add + RMSNorm + gamma + GELU, bf16 [16384, 4096].
+  4. Seeded random 64-node elementwise chain over A [16384,16384],
+     B [16384,1], C [1,16384], all f32.
+
+Distributions: N(0, s) means standard deviation s (presk language reference,
+"Initializers").  bf16 tensors are drawn in f32 and rounded to nearest even
+(presk native chapter, "The realization").  Every tensor, or leaf slot, gets a
+generator of its own derived from (seed, index), so a leaf's values do not
+depend on how many leaves precede it.
+
+No function here computes anything a fusion group computes.
+"""
+from __future__ import annotations
+
+import math
+import os
+from typing import Dict, List, Sequence, Tuple
+
+import torch
+
+from .dag import Node, parse_dag, random_chain_dag
+
+SEED_BASE = 1000
+
+ADAMW_HP = dict(lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, t=10)
+
+
+def _gen(device, seed: int, *idx: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    s = seed
+    for k in idx:
+        s = (s * 1_000_003 + k + 1) % (2**63 - 1)
+    g.manual_seed(s)
+    return g
+
+
+# ---------------------------------------------------------------- param trees
+def tiny_gpt_leaves(V: int = 92, D: int = 64, L: int = 2, T: int = 32) -> List[Tuple[str, Tuple[int, ...]]]:
+    leaves = [("tok_emb", (V, D)), ("pos_emb", (T, D))]
+    for l in range(L):
+        p = f"blocks.{l}."
+        leaves += [
+            (p + "ln1.g", (D,)), (p + "ln1.b", (D,)),
+            (p + "attn.Wqkv", (D, 3 * D)), (p + "attn.bqkv", (3 * D,)),
+            (p + "attn.Wo", (D, D)), (p + "attn.bo", (D,)),
+            (p + "ln2.g", (D,)), (p + "ln2.b", (D,)),
+            (p + "ff.W1", (D, 4 * D)), (p + "ff.b1", (4 * D,)),
+            (p + "ff.W2", (4 * D, D)), (p + "ff.b2", (D,)),
+        ]
+    leaves += [("lnf.g", (D,)), ("lnf.b", (D,))]
+    return leaves
+
+
+def llama_leaves(L: int = 16, D: int = 2048, F: int = 5632, V: int = 32000) -> List[Tuple[str, Tuple[int, ...]]]:
+    leaves = [("embedding", (V, D))]
+    for l in range(L):
+        p = f"layers.{l}."
+        leaves += [
+            (p + "Wq", (D, D)), (p + "Wk", (D, D)), (p + "Wv", (D, D)), (p + "Wo", (D, D)),
+            (p + "W_gate", (D, F)), (p + "W_up", (D, F)), (p + "W_down", (F, D)),
+            (p + "norm1", (D,)), (p + "norm2", (D,)),
+        ]
+    return leaves
+
+
+def numel(shape: Sequence[int]) -> int:
+    return int(math.prod(shape))
+
+
+def adamw_state(shapes: Sequence[Sequence[int]], theta_dtype=torch.float32, grad_dtype=torch.float32,
+                mv_dtype=torch.float32, device="cpu", seed: int = SEED_BASE) -> List[Dict[str, torch.Tensor]]:
+    """theta N(0,0.02), grad N(0,1e-2), m N(0,1e-3), v |N(0,1e-4)|; one
+    generator per (leaf, slot).  Each leaf slot is its own allocation."""
+    out = []
+    for i, shp in enumerate(shapes):
+        n = numel(shp)
+        d = {}
+        for slot, (name, std, dt, absval) in enumerate((
+                ("theta", 0.02, theta_dtype, False), ("grad", 1e-2, grad_dtype, False),
+                ("m", 1e-3, mv_dtype, False), ("v", 1e-4, mv_dtype, True))):
+            x = torch.randn(n, generator=_gen(device, seed, i, slot), device=device, dtype=torch.float32)
+            if absval:
+                x.abs_()
+            x.mul_(std)
+            d[name] = x.to(dt) if dt != torch.float32 else x
+        out.append(d)
+    return out
+
+
+# ------------------------------------------------------------ row workloads
+def softmax_scores(rows: int, cols: int, device="cpu", seed: int = SEED_BASE + 1, std: float = 3.0) -> torch.Tensor:
+    x = torch.randn(rows, cols, generator=_gen(device, seed, 0), device=device, dtype=torch.float32)
+    return x.mul_(std)
+
+
+def rmsnorm_inputs(rows: int, cols: int, device="cpu", seed: int = SEED_BASE + 3):
+    x = torch.randn(rows, cols, generator=_gen(device, seed, 0), device=device).to(torch.bfloat16)
+    r = torch.randn(rows, cols, generator=_gen(device, seed, 1), device=device).to(torch.bfloat16)
+    g = torch.randn(cols, generator=_gen(device, seed, 2), device=device).mul_(0.1).add_(1.0).to(torch.bfloat16)
+    return x, r, g
+
+
+def chain_inputs(rows: int, cols: int, device="cpu", seed: int = SEED_BASE + 4):
+    """A [rows, cols], B [rows, 1], C [1, cols], all U(-1, 1) f32."""
+    def u(shape, k):
+        t = torch.rand(*shape, generator=_gen(device, seed, k), device=device, dtype=torch.float32)
+        return t.mul_(2.0).sub_(1.0)
+    return u((rows, cols), 0), u((rows, 1), 1), u((1, cols), 2)
+
+
+# ------------------------------------------------------------- group DAGs
+def softmax_causal_dag(scale: float = 0.125, period: int = 1024) -> List[Node]:
+    """scale, causal mask (refused positions become -inf), row max, subtract,
+    exp, row sum, divide."""
+    return parse_dag(f"""
+        %0 = input 0
+        %1 = const {float(scale).hex()}
+        %2 = mul %0 %1
+        %3 = causal_mask %2 {period}
+        %4 = row_max %3
+        %5 = sub %3 %4
+        %6 = exp %5
+        %7 = row_sum %6
+        %8 = div %6 %7
+    """)
+
+
+def rmsnorm_gelu_dag(eps_f32: float) -> List[Node]:
+    """h = x + res; y = h / sqrt(mean(h*h) + eps) * gamma; gelu(y)."""
+    return parse_dag(f"""
+        %0 = input 0
+        %1 = input 1
+        %2 = input 2
+        %3 = add %0 %1
+        %4 = pow2 %3
+        %5 = row_mean %4
+        %6 = const {float(eps_f32).hex()}
+        %7 = add %5 %6
+        %8 = sqrt %7
+        %9 = div %3 %8
+        %10 = mul %9 %2
+        %11 = gelu %10
+    """)
+
+
+def f32(x: float) -> float:
+    """Round a Python float to the nearest f32 value (an input conversion)."""
+    return float(torch.tensor(x, dtype=torch.float32).item())
+
+
+CHAIN_DAG_SEED = SEED_BASE + 4
+
+
+def chain_dag_candidate(seed: int = CHAIN_DAG_SEED) -> List[Node]:
+    return random_chain_dag(seed)
+
+
+CHAIN64_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "tests", "golden", "chain64_dag.txt")
+
+
+def chain64_dag() -> List[Node]:
+    """The accepted 64-node chain (written by tests/golden/make_chain64_dag.py)."""
+    with open(CHAIN64_PATH) as f:
+        return parse_dag(f.read())
