@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Fused-group HBM throughput on one MI355X.
+
+One step = the AdamW step over the Llama-style parameter tree (145 leaves,
+887 685 120 parameters, bf16 theta/g, f32 m/v, one launch for every leaf)
+followed by the causal row softmax over f32 scores [8,16,1024,1024]
+(131 072 rows x 1024: scale, causal mask, row max, subtract, exp, row sum,
+divide; one launch).  Inputs are seeded synthetic tensors, resident in HBM
+before timing starts.
+
+`value` is the step's algorithmic bytes (AdamW: 22 B per parameter;
+softmax: allowed scores read once + every output written once) divided by
+the measured time per step, in GB/s.  The roofline object is for the
+dominant kernel (AdamW), timed with HIP events on the stream it runs on.
+The other three workloads (tiny-GPT AdamW, add+RMSNorm+GELU, 64-node
+chain) are timed one by one with the cache flushed between calls and
+reported under "groups".  The CPU baseline runs the oracle single-threaded
+on a one-eighth sample of the same step.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=16, help="Llama-style tree depth (16: the explicit leaf list)")
+    ap.add_argument("--reps", type=int, default=11, help="calls per workload in the per-group timing")
+    ap.add_argument("--no-groups", action="store_true", help="skip the per-group timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=float, default=1.0 / 8, help="fraction of the step the oracle times")
+    ap.add_argument("--profile-step", action="store_true",
+                    help="run warmup + K steps only (for rocprofv3 runs), no per-group timing, no CPU leg")
+    return ap.parse_args()
+
+
+def gb(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the fused groups shard without "
+                                   "communication (see DESIGN.md), so no multi-GPU figure is produced",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import elementwise_reduction_groups_amd as P
+    from synth import configs
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    HP = configs.ADAMW_HP
+    hp = (HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["weight_decay"], HP["t"])
+
+    # ---------------------------------------------------------------- inputs
+    shapes = [s for _, s in configs.llama_leaves(L=args.layers)]
+    n_params = sum(math.prod(s) for s in shapes)
+    state = configs.adamw_state(shapes, theta_dtype=torch.bfloat16, grad_dtype=torch.bfloat16,
+                                mv_dtype=torch.float32, device=dev, seed=configs.SEED_BASE + 2)
+    tree = P.Tree([[s["theta"], s["grad"], s["m"], s["v"]] for s in state])
+    adamw_bytes = n_params * (2 + 2 + 4 + 4 + 2 + 4 + 4)
+
+    R, C = 131072, 1024
+    scores = configs.softmax_scores(R, C, device=dev)
+    probs = torch.empty_like(scores)
+    softmax = P.Group(configs.softmax_causal_dag(0.125, 1024), [((R, C), "f32")], (R, C), "f32")
+    allowed = sum(min(r % 1024, C - 1) + 1 for r in range(1024)) * (R // 1024)
+    softmax_bytes = allowed * 4 + R * C * 4
+    step_bytes = adamw_bytes + softmax_bytes
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        tree.adamw_step(*hp, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        softmax.run([scores], probs, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_per_step = wall_ms / args.steps
+    adamw_ms = [e[0].elapsed_time(e[1]) for e in events]
+    softmax_ms = [e[1].elapsed_time(e[2]) for e in events]
+    adamw_avg = statistics.fmean(adamw_ms)
+    value = gb(step_bytes, ms_per_step)
+
+    result = {
+        "metric": "fused-group HBM GB/s (AdamW tree step, row softmax) and % of MI355X peak",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 arithmetic; bf16/f32 storage",
+        "data": "synthetic (seeded), resident in HBM",
+        "config": {
+            "workload": "AdamW step over a Llama-style tree (16 layers, D=2048, FFN 5632, vocab 32000: 145 leaves, "
+                        "887685120 params; bf16 theta/g, f32 m/v) + causal row softmax f32 [8,16,1024,1024]",
+            "params": n_params, "leaves": len(shapes), "softmax_rows": R, "softmax_cols": C,
+            "step_bytes": step_bytes, "adamw_bytes": adamw_bytes, "softmax_bytes": softmax_bytes,
+        },
+        "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "kernel": "adamw_tree_kernel<bf16,bf16,f32>",
+            "bound": "hbm",
+            "achieved": round(gb(adamw_bytes, adamw_avg), 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gb(adamw_bytes, adamw_avg) / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_ms": round(adamw_avg, 4),
+            "bytes_per_launch": adamw_bytes,
+        },
+        "kernels": {
+            "adamw_ms_median": round(statistics.median(adamw_ms), 4),
+            "softmax_ms_median": round(statistics.median(softmax_ms), 4),
+            "softmax_GBps": round(gb(softmax_bytes, statistics.median(softmax_ms)), 1),
+        },
+    }
+    if args.profile_step:
+        print(json.dumps(result), flush=True)
+        return
+
+    # ----------------------------------------------------- per-group timing
+    if not args.no_groups:
+        result["groups"] = time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, probs,
+                                       adamw_bytes, softmax_bytes, hp)
+
+    # ------------------------------------------------------------ CPU leg
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, configs, n_params, shapes, R, C, step_bytes)
+
+    print(json.dumps(result), flush=True)
+
+
+def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, probs, adamw_bytes, softmax_bytes, hp):
+    """Each workload alone: a 1 GiB write between calls evicts the 256 MB
+    last-level cache; HIP events around each call; median of --reps."""
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def timed(fn, reps):
+        ms = []
+        for _ in range(reps + 2):
+            flush.zero_()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        ms = ms[2:]
+        return statistics.median(ms), min(ms), max(ms)
+
+    out = {}
+
+    def add(name, nbytes, fn, note=None):
+        med, lo, hi = timed(fn, args.reps)
+        out[name] = {"ms_median": round(med, 4), "ms_min": round(lo, 4), "ms_max": round(hi, 4),
+                     "bytes": nbytes, "GBps": round(gb(nbytes, med), 1),
+                     "frac_of_peak": round(gb(nbytes, med) / HBM_PEAK_GBS, 4)}
+        if note:
+            out[name]["note"] = note
+
+    add("adamw_llama_bf16", adamw_bytes, lambda: tree.adamw_step(*hp, stream=stream))
+    add("softmax_causal_f32", softmax_bytes, lambda: softmax.run([scores], probs, stream=stream))
+
+    # tiny GPT tree, f32
+    tiny_shapes = [s for _, s in configs.tiny_gpt_leaves()]
+    tiny = configs.adamw_state(tiny_shapes, device=dev, seed=configs.SEED_BASE)
+    tiny_tree = P.Tree([[s["theta"], s["grad"], s["m"], s["v"]] for s in tiny])
+    n_tiny = sum(math.prod(s) for s in tiny_shapes)
+    add("adamw_tiny_gpt_f32", n_tiny * 28, lambda: tiny_tree.adamw_step(*hp, stream=stream),
+        note="3 MB: launch-latency bound, no HBM target")
+
+    # add + RMSNorm + gamma + GELU, bf16 [16384, 4096]
+    x, r, g = configs.rmsnorm_inputs(16384, 4096, device=dev)
+    y = torch.empty_like(x)
+    rms = P.Group(configs.rmsnorm_gelu_dag(configs.f32(1e-5)),
+                  [((16384, 4096), "bf16"), ((16384, 4096), "bf16"), ((4096,), "bf16")], (16384, 4096), "bf16")
+    add("rmsnorm_gelu_bf16", rms.info.algorithmic_bytes, lambda: rms.run([x, r, g], y, stream=stream))
+
+    # 64-node chain over [16384, 16384]
+    A, B, Cc = configs.chain_inputs(16384, 16384, device=dev)
+    Z = torch.empty_like(A)
+    chain = P.Group(configs.chain64_dag(), [((16384, 16384), "f32"), ((16384, 1), "f32"), ((1, 16384), "f32")],
+                    (16384, 16384), "f32")
+    add("chain64_f32", chain.info.algorithmic_bytes, lambda: chain.run([A, B, Cc], Z, stream=stream),
+        note="ALU-bound: 64 node evaluations per element")
+    out["chain64_f32"]["node_evals_per_s"] = round(64 * 16384 * 16384 / (out["chain64_f32"]["ms_median"] * 1e-3), 1)
+
+    # device copy of 2 GiB (read + write) as the practical streaming ceiling
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    add("copy_ceiling", 2 * src.numel() * 4, lambda: dst.copy_(src), note="torch device copy, read+write")
+    del flush, src, dst
+    return out
+
+
+def cpu_baseline(args, configs, n_params, shapes, R, C, step_bytes):
+    """The oracle, single-threaded, on a fixed fraction of the step's work:
+    the first leaves of the same tree up to that fraction of its parameters
+    (drawn on the host with the same distributions) and that fraction of the
+    softmax rows.  Reported as GB/s of the same algorithmic-bytes count."""
+    import numpy as np
+    import torch
+    import oracle
+
+    torch.set_num_threads(max(1, os.cpu_count() or 1))
+    f = args.cpu_sample
+    target = int(n_params * f)
+    take, tot = [], 0
+    for s in shapes:
+        if tot >= target:
+            break
+        take.append(s)
+        tot += math.prod(s)
+    st = configs.adamw_state(take, theta_dtype=torch.bfloat16, grad_dtype=torch.bfloat16, mv_dtype=torch.float32,
+                             device="cpu", seed=configs.SEED_BASE + 2)
+    u16 = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    HP = configs.ADAMW_HP
+    t0 = time.perf_counter()
+    for s in st:
+        oracle.adamw(u16(s["theta"]), u16(s["grad"]), s["m"].numpy(), s["v"].numpy(), HP["lr"], HP["beta1"],
+                     HP["beta2"], HP["eps"], HP["weight_decay"], HP["t"])
+    t_adamw = time.perf_counter() - t0
+    rows = max(1024, int(R * f) // 1024 * 1024)
+    x = configs.softmax_scores(rows, C).numpy()
+    t0 = time.perf_counter()
+    oracle.softmax_causal(x, 1024, 0.125)
+    t_soft = time.perf_counter() - t0
+    adamw_b = tot * 22
+    soft_b = (rows // 1024) * sum(min(q, C - 1) + 1 for q in range(1024)) * 4 + rows * C * 4
+    secs = t_adamw + t_soft
+    return {"value": round((adamw_b + soft_b) / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{tot} of {n_params} AdamW parameters ({len(take)} leaves) + {rows} of {R} softmax rows; "
+                      f"{secs:.1f} s single-threaded",
+            "seconds": round(secs, 2), "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,398 @@
+"""Python binding of psk_fused (libpsk_fused.so): argument marshalling only.
+
+Every function keeps its C name (include/psk_fused.h) and raises PskError
+instead of returning a status.  Device memory and streams come from PyTorch
+(``tensor.data_ptr()``, ``torch.cuda.current_stream().cuda_stream``); all
+computation happens in the library's HIP kernels.  There is no fallback: if
+the library is not built, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpsk_fused.so")
+
+# ----------------------------------------------------------------- constants
+PSK_OK = 0
+STATUS_NAMES = ["PSK_OK", "PSK_E_NULL", "PSK_E_CAP", "PSK_E_ORDER", "PSK_E_ROOT", "PSK_E_DEAD", "PSK_E_OP",
+                "PSK_E_TYPE", "PSK_E_BROADCAST", "PSK_E_ROW", "PSK_E_ALIGN", "PSK_E_ALIAS", "PSK_E_SHAPE",
+                "PSK_E_UNSUPPORTED", "PSK_E_JIT", "PSK_E_HIP"]
+for _i, _n in enumerate(STATUS_NAMES):
+    globals()[_n] = _i
+
+PSK_F32, PSK_BF16 = 0, 1
+PSK_MAX_RANK = 4
+PSK_MAX_SLOTS = 8
+PSK_TREE_CHUNK = 4096
+
+OPCODES = {
+    "input": 1, "const": 2,
+    "add": 10, "sub": 11, "mul": 12, "div": 13, "max": 14, "min": 15,
+    "neg": 20, "abs": 21, "exp": 22, "log": 23, "sqrt": 24, "tanh": 25, "erf": 26, "gelu": 27,
+    "sqrtabs": 28, "pow2": 29, "pown": 30,
+    "select": 40, "causal_mask": 41,
+    "row_max": 50, "row_sum": 51, "row_mean": 52,
+    "reduce": 60, "contract": 61, "matmul": 61, "cast": 62, "opaque": 63,
+}
+
+
+class PskError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+        self.name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+
+
+# ------------------------------------------------------------------- structs
+class psk_node(ctypes.Structure):
+    _fields_ = [("op", ctypes.c_int32), ("a", ctypes.c_int32), ("b", ctypes.c_int32), ("c", ctypes.c_int32),
+                ("imm", ctypes.c_float), ("iparam", ctypes.c_int32)]
+
+
+class psk_tensor_desc(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("shape", ctypes.c_int64 * PSK_MAX_RANK)]
+
+
+class psk_group_desc(ctypes.Structure):
+    _fields_ = [("n_nodes", ctypes.c_int32), ("nodes", ctypes.POINTER(psk_node)), ("root", ctypes.c_int32),
+                ("n_inputs", ctypes.c_int32), ("inputs", ctypes.POINTER(psk_tensor_desc)),
+                ("out", psk_tensor_desc), ("arith", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class psk_group_info(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("members", ctypes.c_int32), ("n_reductions", ctypes.c_int32),
+                ("phases", ctypes.c_int32), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("lanes_per_row", ctypes.c_int32), ("vec", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("rows_per_block", ctypes.c_int32), ("algorithmic_bytes", ctypes.c_int64)]
+
+
+class psk_leaf(ctypes.Structure):
+    _fields_ = [("numel", ctypes.c_int64), ("slot", ctypes.c_void_p * PSK_MAX_SLOTS)]
+
+
+class psk_tree_info(ctypes.Structure):
+    _fields_ = [("n_leaves", ctypes.c_int32), ("n_slots", ctypes.c_int32), ("n_chunks", ctypes.c_int64),
+                ("total_numel", ctypes.c_int64), ("chunk_elems", ctypes.c_int64),
+                ("vector_leaves", ctypes.c_int32)]
+
+
+class psk_adamw_hp(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("t", ctypes.c_int64)]
+
+
+class psk_stats(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int64), ("jit_compiles", ctypes.c_int64), ("jit_hits", ctypes.c_int64)]
+
+
+# ---------------------------------------------------------------- loading
+_lib = None
+
+EXPORTED = ["psk_group_create", "psk_group_run", "psk_group_destroy", "psk_group_get_info", "psk_group_source",
+            "psk_group_code_object", "psk_tree_create", "psk_tree_destroy", "psk_tree_get_info",
+            "psk_tree_get_tables", "psk_tree_plan", "psk_adamw_step", "psk_partition", "psk_last_error",
+            "psk_status_str", "psk_version", "psk_get_stats"]
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.psk_group_create.argtypes = [ctypes.POINTER(psk_group_desc), ctypes.POINTER(vp)]
+    L.psk_group_run.argtypes = [vp, ctypes.POINTER(vp), vp, vp]
+    L.psk_group_destroy.argtypes = [vp]
+    L.psk_group_destroy.restype = None
+    L.psk_group_get_info.argtypes = [vp, ctypes.POINTER(psk_group_info)]
+    L.psk_group_source.argtypes = [ctypes.POINTER(psk_group_desc), ctypes.c_char_p, sz, ctypes.POINTER(sz)]
+    L.psk_group_code_object.argtypes = [ctypes.POINTER(psk_group_desc), vp, sz, ctypes.POINTER(sz)]
+    L.psk_tree_create.argtypes = [ctypes.POINTER(psk_leaf), i32, i32, ctypes.POINTER(i32), ctypes.POINTER(vp)]
+    L.psk_tree_destroy.argtypes = [vp]
+    L.psk_tree_destroy.restype = None
+    L.psk_tree_get_info.argtypes = [vp, ctypes.POINTER(psk_tree_info)]
+    L.psk_tree_get_tables.argtypes = [vp, vp, vp, vp, vp]
+    L.psk_tree_plan.argtypes = [vp, i32, ctypes.POINTER(i64), vp, vp, vp, vp]
+    L.psk_adamw_step.argtypes = [vp, ctypes.POINTER(psk_adamw_hp), vp]
+    L.psk_partition.argtypes = [i32, ctypes.POINTER(psk_node), ctypes.POINTER(psk_tensor_desc),
+                                ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                ctypes.POINTER(i32)]
+    L.psk_last_error.restype = ctypes.c_char_p
+    L.psk_status_str.restype = ctypes.c_char_p
+    L.psk_status_str.argtypes = [ctypes.c_int]
+    L.psk_version.restype = i32
+    L.psk_get_stats.argtypes = [ctypes.POINTER(psk_stats)]
+    for name in EXPORTED:
+        f = getattr(L, name)
+        if name not in ("psk_group_destroy", "psk_tree_destroy", "psk_last_error", "psk_status_str", "psk_version"):
+            f.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != PSK_OK:
+        msg = lib().psk_last_error().decode(errors="replace")
+        raise PskError(status, msg or STATUS_NAMES[status])
+
+
+# ------------------------------------------------------- descriptor helpers
+def _dtype_code(dt) -> int:
+    if isinstance(dt, int):
+        return dt
+    s = str(dt)
+    if s in ("f32", "float32", "torch.float32"):
+        return PSK_F32
+    if s in ("bf16", "bfloat16", "torch.bfloat16"):
+        return PSK_BF16
+    raise ValueError(f"unsupported storage type {dt!r}")
+
+
+def tensor_desc(shape: Sequence[int], dtype) -> psk_tensor_desc:
+    d = psk_tensor_desc()
+    shape = tuple(int(s) for s in shape)
+    if len(shape) > PSK_MAX_RANK:
+        raise ValueError("rank above 4")
+    d.rank = len(shape)
+    d.dtype = _dtype_code(dtype)
+    for i, s in enumerate(shape):
+        d.shape[i] = s
+    return d
+
+
+def node_array(nodes) -> ctypes.Array:
+    """Nodes are objects with .op (name or code), .args, .imm, .iparam."""
+    arr = (psk_node * len(nodes))()
+    for i, nd in enumerate(nodes):
+        op = nd.op if isinstance(nd.op, int) else OPCODES[nd.op]
+        args = list(nd.args) + [-1] * (3 - len(nd.args))
+        arr[i].op = op
+        arr[i].a, arr[i].b, arr[i].c = args[0], args[1], args[2]
+        arr[i].imm = float(nd.imm) if nd.imm is not None else 0.0
+        arr[i].iparam = int(nd.iparam) if nd.iparam is not None else 0
+    return arr
+
+
+class GroupDesc:
+    """Keeps a psk_group_desc and the arrays it points to alive."""
+
+    def __init__(self, nodes, inputs: Sequence[Tuple[Sequence[int], object]], out_shape: Sequence[int], out_dtype,
+                 root: Optional[int] = None, arith=PSK_F32, flags: int = 0):
+        self._nodes = node_array(nodes)
+        self._inputs = (psk_tensor_desc * max(1, len(inputs)))(*[tensor_desc(s, d) for s, d in inputs])
+        self.desc = psk_group_desc()
+        self.desc.n_nodes = len(nodes)
+        self.desc.nodes = self._nodes
+        self.desc.root = len(nodes) - 1 if root is None else root
+        self.desc.n_inputs = len(inputs)
+        self.desc.inputs = self._inputs
+        self.desc.out = tensor_desc(out_shape, out_dtype)
+        self.desc.arith = _dtype_code(arith)
+        self.desc.flags = flags
+
+
+# ------------------------------------------------------------ C functions
+def psk_group_create(desc: GroupDesc) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().psk_group_create(ctypes.byref(desc.desc), ctypes.byref(h)))
+    return h.value
+
+
+def psk_group_run(group: int, inputs: Sequence[int], out: int, stream: Optional[int] = None):
+    """inputs/out are device addresses (ints)."""
+    arr = (ctypes.c_void_p * max(1, len(inputs)))(*[ctypes.c_void_p(p) for p in inputs])
+    _check(lib().psk_group_run(ctypes.c_void_p(group), arr, ctypes.c_void_p(out), ctypes.c_void_p(stream or 0)))
+
+
+def psk_group_destroy(group: int):
+    lib().psk_group_destroy(ctypes.c_void_p(group))
+
+
+def psk_group_get_info(group: int) -> psk_group_info:
+    info = psk_group_info()
+    _check(lib().psk_group_get_info(ctypes.c_void_p(group), ctypes.byref(info)))
+    return info
+
+
+def psk_group_source(desc: GroupDesc) -> str:
+    n = ctypes.c_size_t()
+    _check(lib().psk_group_source(ctypes.byref(desc.desc), None, 0, ctypes.byref(n)))
+    buf = ctypes.create_string_buffer(n.value + 1)
+    _check(lib().psk_group_source(ctypes.byref(desc.desc), buf, n.value + 1, ctypes.byref(n)))
+    return buf.value.decode()
+
+
+def psk_group_code_object(desc: GroupDesc) -> bytes:
+    n = ctypes.c_size_t()
+    _check(lib().psk_group_code_object(ctypes.byref(desc.desc), None, 0, ctypes.byref(n)))
+    buf = ctypes.create_string_buffer(n.value)
+    _check(lib().psk_group_code_object(ctypes.byref(desc.desc), buf, n.value, ctypes.byref(n)))
+    return buf.raw[:n.value]
+
+
+def psk_tree_create(leaves: Sequence[Tuple[int, Sequence[int]]], slot_dtypes: Sequence) -> int:
+    """leaves: (numel, [slot device addresses]) per leaf."""
+    n_slots = len(slot_dtypes)
+    arr = (psk_leaf * max(1, len(leaves)))()
+    for i, (numel, slots) in enumerate(leaves):
+        arr[i].numel = int(numel)
+        for s, p in enumerate(slots):
+            arr[i].slot[s] = p
+    dts = (ctypes.c_int32 * n_slots)(*[_dtype_code(d) for d in slot_dtypes])
+    h = ctypes.c_void_p()
+    _check(lib().psk_tree_create(arr, len(leaves), n_slots, dts, ctypes.byref(h)))
+    return h.value
+
+
+def psk_tree_destroy(tree: int):
+    lib().psk_tree_destroy(ctypes.c_void_p(tree))
+
+
+def psk_tree_get_info(tree: int) -> psk_tree_info:
+    info = psk_tree_info()
+    _check(lib().psk_tree_get_info(ctypes.c_void_p(tree), ctypes.byref(info)))
+    return info
+
+
+def psk_tree_get_tables(tree: int):
+    import numpy as np
+    info = psk_tree_get_info(tree)
+    off = np.zeros(info.n_leaves + 1, np.int64)
+    cl = np.zeros(info.n_chunks, np.int32)
+    cs = np.zeros(info.n_chunks, np.int64)
+    cc = np.zeros(info.n_chunks, np.int32)
+    _check(lib().psk_tree_get_tables(ctypes.c_void_p(tree), off.ctypes.data, cl.ctypes.data, cs.ctypes.data,
+                                     cc.ctypes.data))
+    return off, cl, cs, cc
+
+
+def psk_tree_plan(numel: Sequence[int]):
+    import numpy as np
+    n = np.ascontiguousarray(numel, np.int64)
+    nc = ctypes.c_int64()
+    _check(lib().psk_tree_plan(n.ctypes.data, len(n), ctypes.byref(nc), None, None, None, None))
+    off = np.zeros(len(n) + 1, np.int64)
+    cl = np.zeros(nc.value, np.int32)
+    cs = np.zeros(nc.value, np.int64)
+    cc = np.zeros(nc.value, np.int32)
+    _check(lib().psk_tree_plan(n.ctypes.data, len(n), ctypes.byref(nc), off.ctypes.data, cl.ctypes.data,
+                               cs.ctypes.data, cc.ctypes.data))
+    return off, cl, cs, cc
+
+
+def psk_adamw_step(tree: int, lr: float, beta1: float, beta2: float, eps: float, weight_decay: float, t: int,
+                   stream: Optional[int] = None):
+    hp = psk_adamw_hp(lr, beta1, beta2, eps, weight_decay, int(t))
+    _check(lib().psk_adamw_step(ctypes.c_void_p(tree), ctypes.byref(hp), ctypes.c_void_p(stream or 0)))
+
+
+def psk_partition(nodes, types: Sequence[Tuple[Sequence[int], object]], is_output: Sequence[bool]):
+    import numpy as np
+    n = len(nodes)
+    arr = node_array(nodes)
+    tys = (psk_tensor_desc * max(1, n))(*[tensor_desc(s, d) for s, d in types])
+    outs = (ctypes.c_uint8 * max(1, n))(*[1 if o else 0 for o in is_output])
+    g = (ctypes.c_int32 * max(1, n))()
+    r = (ctypes.c_int32 * max(1, n))()
+    ng = ctypes.c_int32()
+    _check(lib().psk_partition(n, arr, tys, outs, g, r, ctypes.byref(ng)))
+    return np.array(g[:n], np.int32), np.array(r[:n], np.int32), ng.value
+
+
+def psk_last_error() -> str:
+    return lib().psk_last_error().decode(errors="replace")
+
+
+def psk_status_str(status: int) -> str:
+    return lib().psk_status_str(status).decode()
+
+
+def psk_version() -> int:
+    return lib().psk_version()
+
+
+def psk_get_stats() -> psk_stats:
+    s = psk_stats()
+    _check(lib().psk_get_stats(ctypes.byref(s)))
+    return s
+
+
+# ----------------------------------------------------- torch conveniences
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class Group:
+    """A compiled fusion group, run on torch tensors."""
+
+    def __init__(self, nodes, inputs, out_shape, out_dtype, root=None):
+        self.desc = GroupDesc(nodes, inputs, out_shape, out_dtype, root=root)
+        self.handle = psk_group_create(self.desc)
+        self.out_shape = tuple(out_shape)
+        self.out_dtype = out_dtype
+
+    @property
+    def info(self) -> psk_group_info:
+        return psk_group_get_info(self.handle)
+
+    def run(self, inputs, out, stream=None):
+        for t in list(inputs) + [out]:
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("group buffers must be contiguous device tensors")
+        psk_group_run(self.handle, [t.data_ptr() for t in inputs], out.data_ptr(), _stream_handle(stream))
+        return out
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h and _lib is not None:
+            psk_group_destroy(h)
+            self.handle = None
+
+
+class Tree:
+    """A parameter tree over torch tensors: slots theta, g, m, v (in place) or
+    theta, g, m, v, theta', m', v'."""
+
+    def __init__(self, slots: Sequence[Sequence]):
+        self._keep = [list(s) for s in slots]       # keep the tensors alive
+        n_slots = len(self._keep[0]) if self._keep else 4
+        dts = [self._dt(t) for t in self._keep[0]] if self._keep else [PSK_F32] * n_slots
+        leaves = []
+        for s in self._keep:
+            n = s[0].numel()
+            for t in s:
+                if t.numel() != n or (n and (not t.is_cuda or not t.is_contiguous())):
+                    raise ValueError("leaf slots must be contiguous device tensors of equal numel")
+            leaves.append((n, [t.data_ptr() for t in s]))
+        self.handle = psk_tree_create(leaves, dts)
+
+    @staticmethod
+    def _dt(t) -> int:
+        import torch
+        if t.dtype == torch.float32:
+            return PSK_F32
+        if t.dtype == torch.bfloat16:
+            return PSK_BF16
+        raise ValueError(f"unsupported dtype {t.dtype}")
+
+    @property
+    def info(self) -> psk_tree_info:
+        return psk_tree_get_info(self.handle)
+
+    def adamw_step(self, lr, beta1, beta2, eps, weight_decay, t, stream=None):
+        psk_adamw_step(self.handle, lr, beta1, beta2, eps, weight_decay, t, _stream_handle(stream))
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h and _lib is not None:
+            psk_tree_destroy(h)
+            self.handle = None

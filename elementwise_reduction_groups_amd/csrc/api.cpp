@@ -1,0 +1,488 @@
+// The C ABI of psk_fused: group and tree objects, kernel loading and launch,
+// error reporting.  Entry points validate everything on the host before any
+// device work and return a psk_status; nothing is launched on a refusal.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "psk_internal.h"
+
+// ------------------------------------------------------------ error state
+namespace psk {
+
+static thread_local std::string t_last_error;
+static std::atomic<int64_t> g_launches{0}, g_jit_compiles{0}, g_jit_hits{0};
+
+psk_status fail(psk_status st, const std::string& msg)
+{
+    t_last_error = std::string(psk_status_str(st)) + ": " + msg;
+    return st;
+}
+
+void clear_error() { t_last_error.clear(); }
+void count_launch() { g_launches++; }
+void count_jit(bool hit) { (hit ? g_jit_hits : g_jit_compiles)++; }
+
+AdamwScalars adamw_scalars(const psk_adamw_hp& hp)
+{
+    // hyperparameter arithmetic in f64, each scalar rounded once to f32
+    AdamwScalars s;
+    s.b1 = (float)hp.beta1;
+    s.b2 = (float)hp.beta2;
+    s.c1 = (float)(1.0 - hp.beta1);
+    s.c2 = (float)(1.0 - hp.beta2);
+    s.bc1 = (float)(1.0 - std::pow(hp.beta1, (double)hp.t));
+    s.bc2 = (float)(1.0 - std::pow(hp.beta2, (double)hp.t));
+    s.lr = (float)hp.lr;
+    s.eps = (float)hp.eps;
+    s.wd = (float)hp.weight_decay;
+    return s;
+}
+
+// ---------------------------------------------------------- kernel cache
+constexpr int kMaxDevices = 64;
+
+struct Kernel {
+    KernelPlan plan;
+    std::string name;
+    std::vector<char> code;
+    std::mutex mu;
+    hipModule_t mod[kMaxDevices] = {};
+    hipFunction_t fn[kMaxDevices] = {};
+};
+
+static std::mutex g_cache_mu;
+static std::map<std::string, std::shared_ptr<Kernel>>& cache()
+{
+    static auto* m = new std::map<std::string, std::shared_ptr<Kernel>>();  // lives until exit
+    return *m;
+}
+
+static psk_status get_kernel(const Analysis& an, bool vector, std::shared_ptr<Kernel>& out)
+{
+    KernelPlan plan = plan_kernel(an, vector);
+    std::string canon = canonical_text(an);
+    char tag[96];
+    std::snprintf(tag, sizeof tag, "k%d v%d b%d l%d n%d", plan.kind, plan.vec, plan.block, plan.lanes, plan.nv);
+    std::string key = canon + tag;
+    {
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        auto it = cache().find(key);
+        if (it != cache().end()) {
+            out = it->second;
+            count_jit(true);
+            return PSK_OK;
+        }
+    }
+    auto k = std::make_shared<Kernel>();
+    k->plan = plan;
+    char nm[64];
+    std::snprintf(nm, sizeof nm, "psk_%s_%016llx", plan.kind ? "row" : "pw", (unsigned long long)fnv1a(key));
+    k->name = nm;
+    std::string src = emit_source(an, plan, k->name);
+    psk_status st = jit_compile(src, k->name, k->code);
+    if (st != PSK_OK) return st;
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    auto it = cache().find(key);
+    if (it != cache().end()) { out = it->second; return PSK_OK; }
+    cache()[key] = k;
+    out = k;
+    return PSK_OK;
+}
+
+static psk_status kernel_function(Kernel& k, hipFunction_t& fn)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(PSK_E_HIP, "device index out of range");
+    std::lock_guard<std::mutex> lk(k.mu);
+    if (!k.fn[dev]) {
+        e = hipModuleLoadData(&k.mod[dev], k.code.data());
+        if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipModuleLoadData: ") + hipGetErrorString(e));
+        e = hipModuleGetFunction(&k.fn[dev], k.mod[dev], k.name.c_str());
+        if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipModuleGetFunction: ") + hipGetErrorString(e));
+    }
+    fn = k.fn[dev];
+    return PSK_OK;
+}
+
+static int esize(int dt) { return dt == PSK_BF16 ? 2 : 4; }
+
+}  // namespace psk
+
+using namespace psk;
+
+// ------------------------------------------------------------------ groups
+struct psk_group {
+    Analysis an;
+    std::shared_ptr<Kernel> vec;      // 16-byte accesses
+    std::shared_ptr<Kernel> scalar;   // element accesses (compiled on first need)
+    std::mutex mu;
+};
+
+extern "C" psk_status psk_group_create(const psk_group_desc* desc, psk_group** out)
+{
+    clear_error();
+    if (!out) return fail(PSK_E_NULL, "out is NULL");
+    *out = nullptr;
+    auto g = std::make_unique<psk_group>();
+    psk_status st = analyse(desc, g->an);
+    if (st != PSK_OK) return st;
+    KernelPlan p = plan_kernel(g->an, true);
+    if (p.grid > 0x7fffffffLL) return fail(PSK_E_UNSUPPORTED, "output too large for one launch");
+    st = get_kernel(g->an, true, g->vec);
+    if (st != PSK_OK) return st;
+    if (g->vec->plan.vec == 1) g->scalar = g->vec;
+    *out = g.release();
+    return PSK_OK;
+}
+
+extern "C" void psk_group_destroy(psk_group* group) { delete group; }
+
+extern "C" psk_status psk_group_get_info(const psk_group* group, psk_group_info* info)
+{
+    clear_error();
+    if (!group || !info) return fail(PSK_E_NULL, "group or info is NULL");
+    const Analysis& an = group->an;
+    const KernelPlan& p = group->vec->plan;
+    info->kind = p.kind;
+    info->members = an.members;
+    info->n_reductions = an.n_reductions;
+    info->phases = an.phases;
+    info->rows = an.rows;
+    info->cols = an.cols;
+    info->lanes_per_row = p.kind ? p.lanes : 1;
+    info->vec = p.vec;
+    info->block = p.block;
+    info->rows_per_block = p.kind ? p.rows_per_block : 0;
+    int64_t bytes = an.numel * esize(an.out_dtype);
+    for (const InputInfo& in : an.inputs)
+        if (in.used) bytes += in.numel * esize(in.dtype);
+    info->algorithmic_bytes = bytes;
+    return PSK_OK;
+}
+
+extern "C" psk_status psk_group_run(const psk_group* group, const void* const* inputs, void* out, void* hip_stream)
+{
+    clear_error();
+    if (!group) return fail(PSK_E_NULL, "group is NULL");
+    const Analysis& an = group->an;
+    if (an.numel == 0) return PSK_OK;
+    if (!out) return fail(PSK_E_NULL, "out is NULL");
+    if (!an.inputs.empty() && !inputs) return fail(PSK_E_NULL, "inputs is NULL");
+    const uintptr_t ob = reinterpret_cast<uintptr_t>(out);
+    const uintptr_t oe = ob + (uintptr_t)an.numel * esize(an.out_dtype);
+    bool aligned16 = (ob % 16) == 0;
+    if (ob % esize(an.out_dtype)) return fail(PSK_E_ALIGN, "out is not aligned to its element size");
+    for (size_t k = 0; k < an.inputs.size(); ++k) {
+        const InputInfo& in = an.inputs[k];
+        if (!in.used) continue;
+        if (in.numel == 0) return PSK_OK;  // cannot happen for a non-empty output; kept for safety
+        const uintptr_t b = reinterpret_cast<uintptr_t>(inputs[k]);
+        if (!b) return fail(PSK_E_NULL, "input " + std::to_string(k) + " is NULL");
+        if (b % esize(in.dtype)) return fail(PSK_E_ALIGN, "input " + std::to_string(k) + " is not aligned to its element size");
+        if (b % 16) aligned16 = false;
+        const uintptr_t e = b + (uintptr_t)in.numel * esize(in.dtype);
+        if (b < oe && ob < e) {
+            bool same = b == ob && in.kind == InKind::Full && in.dtype == an.out_dtype;
+            if (!same)
+                return fail(PSK_E_ALIAS, "out overlaps input " + std::to_string(k) +
+                                             " (only an in-place update of a same-shape, same-type input is allowed)");
+        }
+    }
+    std::shared_ptr<Kernel> k;
+    if (aligned16 || group->vec->plan.vec == 1) {
+        k = group->vec;
+    } else {
+        psk_group* g = const_cast<psk_group*>(group);
+        std::lock_guard<std::mutex> lk(g->mu);
+        if (!g->scalar) {
+            psk_status st = get_kernel(an, false, g->scalar);
+            if (st != PSK_OK) return st;
+        }
+        k = g->scalar;
+    }
+    hipFunction_t fn = nullptr;
+    psk_status st = kernel_function(*k, fn);
+    if (st != PSK_OK) return st;
+    std::vector<void*> args;
+    std::vector<const void*> ptrs(an.inputs.size());
+    for (size_t i = 0; i < an.inputs.size(); ++i) ptrs[i] = inputs ? inputs[i] : nullptr;
+    long long n_total = k->plan.kind == 1 ? (long long)an.rows : (long long)an.numel;
+    for (size_t i = 0; i < ptrs.size(); ++i) args.push_back(&ptrs[i]);
+    void* outp = out;
+    args.push_back(&outp);
+    args.push_back(&n_total);
+    const KernelPlan& p = k->plan;
+    hipError_t e = hipModuleLaunchKernel(fn, (unsigned)p.grid, 1, 1, (unsigned)p.block, 1, 1, 0,
+                                         static_cast<hipStream_t>(hip_stream), args.data(), nullptr);
+    if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipModuleLaunchKernel: ") + hipGetErrorString(e));
+    count_launch();
+    return PSK_OK;
+}
+
+extern "C" psk_status psk_group_source(const psk_group_desc* desc, char* buf, size_t cap, size_t* len)
+{
+    clear_error();
+    Analysis an;
+    psk_status st = analyse(desc, an);
+    if (st != PSK_OK) return st;
+    KernelPlan p = plan_kernel(an, true);
+    std::string src = emit_source(an, p, "psk_kernel");
+    if (len) *len = src.size();
+    if (buf && cap) {
+        size_t n = std::min(cap - 1, src.size());
+        std::memcpy(buf, src.data(), n);
+        buf[n] = '\0';
+    }
+    return PSK_OK;
+}
+
+extern "C" psk_status psk_group_code_object(const psk_group_desc* desc, void* buf, size_t cap, size_t* len)
+{
+    clear_error();
+    Analysis an;
+    psk_status st = analyse(desc, an);
+    if (st != PSK_OK) return st;
+    std::shared_ptr<Kernel> k;
+    st = get_kernel(an, true, k);
+    if (st != PSK_OK) return st;
+    if (len) *len = k->code.size();
+    if (buf && cap >= k->code.size()) std::memcpy(buf, k->code.data(), k->code.size());
+    return PSK_OK;
+}
+
+// ------------------------------------------------------------------- trees
+struct psk_tree {
+    int32_t n_leaves = 0, n_slots = 0;
+    int32_t dt[PSK_MAX_SLOTS] = {};
+    TreePlan plan;
+    std::vector<LeafDev> leaves;
+    std::vector<ChunkDev> chunks;
+    LeafDev* d_leaves = nullptr;
+    ChunkDev* d_chunks = nullptr;
+    int device = 0;
+    int32_t vector_leaves = 0;
+    ~psk_tree()
+    {
+        if (d_leaves) (void)hipFree(d_leaves);
+        if (d_chunks) (void)hipFree(d_chunks);
+    }
+};
+
+namespace {
+struct Range {
+    uintptr_t b, e;
+    int32_t leaf, slot;
+};
+}  // namespace
+
+extern "C" psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, int32_t n_slots,
+                                      const int32_t* slot_dtypes, psk_tree** out)
+{
+    clear_error();
+    if (!out) return fail(PSK_E_NULL, "out is NULL");
+    *out = nullptr;
+    if (n_leaves < 0) return fail(PSK_E_SHAPE, "negative leaf count");
+    if (n_leaves > 0 && !leaves) return fail(PSK_E_NULL, "leaves is NULL");
+    if (n_slots != 4 && n_slots != 7)
+        return fail(PSK_E_SHAPE, "a tree has 4 slots (theta, g, m, v; in place) or 7 (plus theta', m', v')");
+    if (!slot_dtypes) return fail(PSK_E_NULL, "slot_dtypes is NULL");
+    auto t = std::make_unique<psk_tree>();
+    t->n_leaves = n_leaves;
+    t->n_slots = n_slots;
+    for (int s = 0; s < n_slots; ++s) {
+        if (slot_dtypes[s] != PSK_F32 && slot_dtypes[s] != PSK_BF16)
+            return fail(PSK_E_TYPE, "slot " + std::to_string(s) + ": storage type must be f32 or bf16");
+        t->dt[s] = slot_dtypes[s];
+    }
+    if (t->dt[2] != t->dt[3]) return fail(PSK_E_TYPE, "m and v must share a storage type");
+    if (n_slots == 7 && (t->dt[4] != t->dt[0] || t->dt[5] != t->dt[2] || t->dt[6] != t->dt[3]))
+        return fail(PSK_E_TYPE, "an output slot must have its input's storage type");
+    std::vector<int64_t> numel(n_leaves);
+    for (int32_t l = 0; l < n_leaves; ++l) numel[l] = leaves[l].numel;
+    psk_status st = plan_tree(numel.data(), n_leaves, PSK_TREE_CHUNK, t->plan);
+    if (st != PSK_OK) return st;
+    // slot roles: inputs 0..3; outputs of theta, m, v
+    const int out_slot[3] = {n_slots == 7 ? 4 : 0, n_slots == 7 ? 5 : 2, n_slots == 7 ? 6 : 3};
+    std::vector<Range> ranges;
+    t->leaves.resize(n_leaves);
+    for (int32_t l = 0; l < n_leaves; ++l) {
+        const psk_leaf& lf = leaves[l];
+        LeafDev& d = t->leaves[l];
+        std::memset(&d, 0, sizeof d);
+        if (lf.numel == 0) continue;
+        bool v16 = true;
+        for (int s = 0; s < n_slots; ++s) {
+            uintptr_t p = reinterpret_cast<uintptr_t>(lf.slot[s]);
+            if (!p) return fail(PSK_E_NULL, "leaf " + std::to_string(l) + " slot " + std::to_string(s) + " is NULL");
+            if (p % esize(t->dt[s]))
+                return fail(PSK_E_ALIGN, "leaf " + std::to_string(l) + " slot " + std::to_string(s) +
+                                             " is not aligned to its element size");
+            if (p % 16) v16 = false;
+            ranges.push_back({p, p + (uintptr_t)lf.numel * esize(t->dt[s]), l, s});
+        }
+        for (int s = 0; s < 4; ++s) d.in[s] = lf.slot[s];
+        for (int s = 0; s < 3; ++s) d.out[s] = lf.slot[out_slot[s]];
+        d.flags = v16 ? 1 : 0;
+        t->vector_leaves += v16;
+    }
+    // aliasing: identical ranges are allowed only for an input and its own
+    // output in one leaf; any other overlap is refused
+    std::sort(ranges.begin(), ranges.end(), [](const Range& x, const Range& y) {
+        return x.b != y.b ? x.b < y.b : x.e < y.e;
+    });
+    auto pair_ok = [&](const Range& x, const Range& y) {
+        if (x.leaf != y.leaf) return false;
+        int a = std::min(x.slot, y.slot), b = std::max(x.slot, y.slot);
+        if (n_slots == 4) return false;   // in place: every slot is its own buffer
+        return (a == 0 && b == 4) || (a == 2 && b == 5) || (a == 3 && b == 6);
+    };
+    uintptr_t max_end = 0;
+    size_t prev = 0;
+    for (size_t i = 0; i < ranges.size(); ++i) {
+        const Range& r = ranges[i];
+        if (i > 0 && r.b < max_end) {
+            const Range& q = ranges[prev];
+            if (!(q.b == r.b && q.e == r.e && pair_ok(q, r)))
+                return fail(PSK_E_ALIAS, "leaf " + std::to_string(r.leaf) + " slot " + std::to_string(r.slot) +
+                                             " overlaps leaf " + std::to_string(q.leaf) + " slot " +
+                                             std::to_string(q.slot));
+        }
+        if (r.e > max_end) { max_end = r.e; prev = i; }
+    }
+    const size_t nc = t->plan.chunk_leaf.size();
+    t->chunks.resize(nc);
+    for (size_t c = 0; c < nc; ++c)
+        t->chunks[c] = {t->plan.chunk_leaf[c], t->plan.chunk_count[c], t->plan.chunk_start[c]};
+    hipError_t e = hipGetDevice(&t->device);
+    if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (n_leaves > 0) {
+        e = hipMalloc(&t->d_leaves, sizeof(LeafDev) * (size_t)n_leaves);
+        if (e == hipSuccess)
+            e = hipMemcpy(t->d_leaves, t->leaves.data(), sizeof(LeafDev) * (size_t)n_leaves, hipMemcpyHostToDevice);
+    }
+    if (e == hipSuccess && nc > 0) {
+        e = hipMalloc(&t->d_chunks, sizeof(ChunkDev) * nc);
+        if (e == hipSuccess)
+            e = hipMemcpy(t->d_chunks, t->chunks.data(), sizeof(ChunkDev) * nc, hipMemcpyHostToDevice);
+    }
+    if (e != hipSuccess) return fail(PSK_E_HIP, std::string("tree upload: ") + hipGetErrorString(e));
+    *out = t.release();
+    return PSK_OK;
+}
+
+extern "C" void psk_tree_destroy(psk_tree* tree) { delete tree; }
+
+extern "C" psk_status psk_tree_get_info(const psk_tree* tree, psk_tree_info* info)
+{
+    clear_error();
+    if (!tree || !info) return fail(PSK_E_NULL, "tree or info is NULL");
+    info->n_leaves = tree->n_leaves;
+    info->n_slots = tree->n_slots;
+    info->n_chunks = (int64_t)tree->chunks.size();
+    info->total_numel = tree->plan.leaf_offset.empty() ? 0 : tree->plan.leaf_offset.back();
+    info->chunk_elems = PSK_TREE_CHUNK;
+    info->vector_leaves = tree->vector_leaves;
+    return PSK_OK;
+}
+
+extern "C" psk_status psk_tree_get_tables(const psk_tree* tree, int64_t* leaf_offset, int32_t* chunk_leaf,
+                                          int64_t* chunk_start, int32_t* chunk_count)
+{
+    clear_error();
+    if (!tree) return fail(PSK_E_NULL, "tree is NULL");
+    const TreePlan& p = tree->plan;
+    if (leaf_offset) std::copy(p.leaf_offset.begin(), p.leaf_offset.end(), leaf_offset);
+    if (chunk_leaf) std::copy(p.chunk_leaf.begin(), p.chunk_leaf.end(), chunk_leaf);
+    if (chunk_start) std::copy(p.chunk_start.begin(), p.chunk_start.end(), chunk_start);
+    if (chunk_count) std::copy(p.chunk_count.begin(), p.chunk_count.end(), chunk_count);
+    return PSK_OK;
+}
+
+extern "C" psk_status psk_tree_plan(const int64_t* numel, int32_t n_leaves, int64_t* n_chunks, int64_t* leaf_offset,
+                                    int32_t* chunk_leaf, int64_t* chunk_start, int32_t* chunk_count)
+{
+    clear_error();
+    TreePlan p;
+    psk_status st = plan_tree(numel, n_leaves, PSK_TREE_CHUNK, p);
+    if (st != PSK_OK) return st;
+    if (n_chunks) *n_chunks = (int64_t)p.chunk_leaf.size();
+    if (leaf_offset) std::copy(p.leaf_offset.begin(), p.leaf_offset.end(), leaf_offset);
+    if (chunk_leaf) std::copy(p.chunk_leaf.begin(), p.chunk_leaf.end(), chunk_leaf);
+    if (chunk_start) std::copy(p.chunk_start.begin(), p.chunk_start.end(), chunk_start);
+    if (chunk_count) std::copy(p.chunk_count.begin(), p.chunk_count.end(), chunk_count);
+    return PSK_OK;
+}
+
+extern "C" psk_status psk_adamw_step(const psk_tree* tree, const psk_adamw_hp* hp, void* hip_stream)
+{
+    clear_error();
+    if (!tree || !hp) return fail(PSK_E_NULL, "tree or hp is NULL");
+    if (hp->t < 1) return fail(PSK_E_SHAPE, "t counts steps from 1");
+    const double v[5] = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+    for (double x : v)
+        if (!std::isfinite(x)) return fail(PSK_E_SHAPE, "hyperparameters must be finite");
+    if (tree->chunks.empty()) return PSK_OK;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != tree->device)
+        return fail(PSK_E_HIP, "the current device is not the device the tree was created on");
+    AdamwScalars s = adamw_scalars(*hp);
+    return launch_adamw(tree->d_leaves, tree->d_chunks, (int64_t)tree->chunks.size(), tree->dt[0], tree->dt[1],
+                        tree->dt[2], s, hip_stream);
+}
+
+// --------------------------------------------------------------- partition
+extern "C" psk_status psk_partition(int32_t n, const psk_node* body, const psk_tensor_desc* types,
+                                    const uint8_t* is_output, int32_t* group_of, int32_t* is_root, int32_t* n_groups)
+{
+    clear_error();
+    return partition(n, body, types, is_output, group_of, is_root, n_groups);
+}
+
+// -------------------------------------------------------------------- misc
+extern "C" const char* psk_last_error(void) { return t_last_error.c_str(); }
+
+extern "C" const char* psk_status_str(psk_status s)
+{
+    switch (s) {
+    case PSK_OK: return "PSK_OK";
+    case PSK_E_NULL: return "PSK_E_NULL";
+    case PSK_E_CAP: return "PSK_E_CAP";
+    case PSK_E_ORDER: return "PSK_E_ORDER";
+    case PSK_E_ROOT: return "PSK_E_ROOT";
+    case PSK_E_DEAD: return "PSK_E_DEAD";
+    case PSK_E_OP: return "PSK_E_OP";
+    case PSK_E_TYPE: return "PSK_E_TYPE";
+    case PSK_E_BROADCAST: return "PSK_E_BROADCAST";
+    case PSK_E_ROW: return "PSK_E_ROW";
+    case PSK_E_ALIGN: return "PSK_E_ALIGN";
+    case PSK_E_ALIAS: return "PSK_E_ALIAS";
+    case PSK_E_SHAPE: return "PSK_E_SHAPE";
+    case PSK_E_UNSUPPORTED: return "PSK_E_UNSUPPORTED";
+    case PSK_E_JIT: return "PSK_E_JIT";
+    case PSK_E_HIP: return "PSK_E_HIP";
+    }
+    return "PSK_E_UNKNOWN";
+}
+
+extern "C" int32_t psk_version(void) { return PSK_VERSION; }
+
+extern "C" psk_status psk_get_stats(psk_stats* stats)
+{
+    clear_error();
+    if (!stats) return fail(PSK_E_NULL, "stats is NULL");
+    stats->launches = g_launches.load();
+    stats->jit_compiles = g_jit_compiles.load();
+    stats->jit_hits = g_jit_hits.load();
+    return PSK_OK;
+}

@@ -1,0 +1,522 @@
+// HIP source emitter: a validated group becomes one gfx950 kernel.
+//
+// Two kernel shapes (poot, "Fusion and Planning", section "Kernel
+// specialization": elementwise = one thread per element; reduction = block
+// reduce with the epilogue in the same kernel):
+//
+//  * pointwise: each thread owns `vec` consecutive output elements, loads
+//    every input at its broadcast position with 16-byte accesses where the
+//    layout allows, evaluates the members in let order in f32 registers and
+//    stores the root once, rounded to its storage type;
+//
+//  * row: `lanes` threads own one row of the [rows, cols] output view; each
+//    lane holds nv vectors of vec elements (columns (k*lanes + lane)*vec + j,
+//    so every wave access is contiguous).  The members are evaluated phase by
+//    phase: phase p computes the values that depend on p reductions, then
+//    the reductions of phase p run lane-sequentially, across the wave with
+//    DPP (quad_perm, row_half_mirror, row_mirror, then readlane of the four
+//    16-lane rows) and across waves through LDS.  The row stays in registers
+//    for the whole kernel, so each input is read from HBM once.
+//
+// Every value is a named SSA register: a value read twice is read twice from
+// its register, never recomputed from memory nor written back.  No value is
+// reassociated, contracted or replaced by a reciprocal (the JIT compiles with
+// -ffp-contract=off, correctly rounded division and square root).  The one
+// reassociation is the reduction tree itself (recorded above).
+//
+// Host-only: nothing here calls HIP.
+#include <cinttypes>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <sstream>
+
+#include "psk_internal.h"
+
+namespace psk {
+
+uint64_t fnv1a(const std::string& s)
+{
+    uint64_t h = 1469598103934665603ull;
+    for (unsigned char ch : s) {
+        h ^= ch;
+        h *= 1099511628211ull;
+    }
+    return h;
+}
+
+static std::string flit(float x)
+{
+    if (std::isnan(x)) return "__builtin_nanf(\"\")";
+    if (std::isinf(x)) return x > 0 ? "__builtin_inff()" : "(-__builtin_inff())";
+    char buf[64];
+    std::snprintf(buf, sizeof buf, "%af", (double)x);
+    return std::string("(") + buf + ")";
+}
+
+std::string canonical_text(const Analysis& an)
+{
+    std::ostringstream s;
+    s << "out " << an.out_dtype << " [" << an.out_shape4[0] << "," << an.out_shape4[1] << "," << an.out_shape4[2]
+      << "," << an.out_shape4[3] << "] root " << an.root << "\n";
+    for (size_t k = 0; k < an.inputs.size(); ++k) {
+        const InputInfo& in = an.inputs[k];
+        s << "in" << k << " " << in.dtype << " [" << in.aligned[0] << "," << in.aligned[1] << "," << in.aligned[2]
+          << "," << in.aligned[3] << "]\n";
+    }
+    for (size_t i = 0; i < an.nodes.size(); ++i) {
+        const psk_node& nd = an.nodes[i];
+        uint32_t bits;
+        std::memcpy(&bits, &nd.imm, 4);
+        s << i << " " << nd.op << " " << nd.a << " " << nd.b << " " << nd.c << " " << nd.iparam << " "
+          << (nd.op == PSK_OP_CONST ? bits : 0u) << "\n";
+    }
+    return s.str();
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
+{
+    KernelPlan p;
+    const int V = an.out_dtype == PSK_BF16 ? 8 : 4;
+    p.vec = (allow_vector && an.cols % V == 0) ? V : 1;
+    if (!an.row_kind) {
+        p.kind = 0;
+        p.block = 256;
+        p.grid = ceil_div(ceil_div(an.numel, p.vec), p.block);
+        return p;
+    }
+    p.kind = 1;
+    // about 16 elements per lane; a row is 16 lanes (one DPP row) or whole waves
+    int64_t want = ceil_div(an.cols, 16);
+    int L = 16;
+    while (L < want && L < 1024) L <<= 1;
+    if (L > 16 && L < 64) L = 64;
+    p.lanes = L;
+    p.nv = (int)ceil_div(an.cols, (int64_t)L * p.vec);
+    p.block = L > 256 ? L : 256;
+    p.rows_per_block = p.block / L;
+    p.grid = ceil_div(an.rows, p.rows_per_block);
+    return p;
+}
+
+namespace {
+
+const char* kPrelude = R"PSK(
+typedef unsigned int psk_u32;
+typedef unsigned short psk_u16;
+typedef float psk_f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 psk_b2 __attribute__((ext_vector_type(2)));
+// bf16 is the top half of a binary32: widening is a shift
+__device__ __forceinline__ float psk_lo(psk_u32 w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float psk_hi(psk_u32 w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float psk_h(psk_u16 h) { return __uint_as_float(((psk_u32)h) << 16); }
+// round two f32 to nearest-even bf16 and pack them (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ psk_u32 psk_pack2(float a, float b) {
+  psk_f2 f = {a, b};
+  return __builtin_bit_cast(psk_u32, __builtin_convertvector(f, psk_b2));
+}
+__device__ __forceinline__ psk_u16 psk_r1(float a) { return (psk_u16)(psk_pack2(a, 0.0f) & 0xffffu); }
+// gelu = x * Phi(x), Phi through the complementary error function
+__device__ __forceinline__ float psk_gelu(float x) { return (0.5f * x) * erfcf(-(x * 0.70710678118654752440f)); }
+__device__ __forceinline__ float psk_max(float a, float b) { return (a > b) ? a : b; }
+__device__ __forceinline__ float psk_min(float a, float b) { return (a < b) ? a : b; }
+#define PSK_DPP(x, ctl) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (x)), (ctl), 0xF, 0xF, false))
+#define PSK_RL(x, l) __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, (x)), (l)))
+// all-reduce within each 16-lane row: xor 1, xor 2 (quad_perm), then the
+// half-row and row mirrors; every lane of the row ends with the same value
+__device__ __forceinline__ float psk_sum16(float x) {
+  x = x + PSK_DPP(x, 0xB1); x = x + PSK_DPP(x, 0x4E);
+  x = x + PSK_DPP(x, 0x141); x = x + PSK_DPP(x, 0x140); return x;
+}
+__device__ __forceinline__ float psk_max16(float x) {
+  x = psk_max(x, PSK_DPP(x, 0xB1)); x = psk_max(x, PSK_DPP(x, 0x4E));
+  x = psk_max(x, PSK_DPP(x, 0x141)); x = psk_max(x, PSK_DPP(x, 0x140)); return x;
+}
+// whole wave: the four row results combined in lane order 0, 16, 32, 48
+__device__ __forceinline__ float psk_sum64(float x) {
+  x = psk_sum16(x);
+  return ((PSK_RL(x, 0) + PSK_RL(x, 16)) + PSK_RL(x, 32)) + PSK_RL(x, 48);
+}
+__device__ __forceinline__ float psk_max64(float x) {
+  x = psk_max16(x);
+  return psk_max(psk_max(psk_max(PSK_RL(x, 0), PSK_RL(x, 16)), PSK_RL(x, 32)), PSK_RL(x, 48));
+}
+)PSK";
+
+struct Emitter {
+    const Analysis& an;
+    const KernelPlan& pl;
+    std::ostringstream o;
+    int NE;                 // elements per thread
+    bool big;               // 64-bit indexing
+    int period = 0;         // causal mask period (0: none)
+    bool ragged = false;    // some lane columns fall past the row end
+
+    Emitter(const Analysis& a, const KernelPlan& p) : an(a), pl(p)
+    {
+        NE = (pl.kind == 1 ? pl.nv : 1) * pl.vec;
+        big = an.numel >= (int64_t(1) << 31) - 4096;
+        for (auto& nd : an.nodes)
+            if (nd.op == PSK_OP_CAUSAL_MASK) period = nd.iparam;
+        if (pl.kind == 1)
+            ragged = (int64_t)pl.nv * pl.lanes * pl.vec != an.cols;
+    }
+
+    const char* I() const { return big ? "long long" : "int"; }
+
+    // column expression of element e of this thread
+    std::string col(int e) const
+    {
+        int k = e / pl.vec, j = e % pl.vec;
+        if (pl.kind == 1)
+            return "(c" + std::to_string(k) + " + " + std::to_string(j) + ")";
+        return "(c0 + " + std::to_string(j) + ")";
+    }
+
+    // value of node i at element e (element value or a row value)
+    std::string val(int i, int e) const
+    {
+        if (an.is_row[i]) return "r" + std::to_string(i);
+        return "v" + std::to_string(i) + "_" + std::to_string(e);
+    }
+
+    std::string expr(int i, int e) const
+    {
+        const psk_node& nd = an.nodes[i];
+        auto A = [&] { return val(nd.a, e); };
+        auto B = [&] { return val(nd.b, e); };
+        auto C = [&] { return val(nd.c, e); };
+        switch (nd.op) {
+        case PSK_OP_ADD: return "(" + A() + " + " + B() + ")";
+        case PSK_OP_SUB: return "(" + A() + " - " + B() + ")";
+        case PSK_OP_MUL: return "(" + A() + " * " + B() + ")";
+        case PSK_OP_DIV: return "(" + A() + " / " + B() + ")";
+        case PSK_OP_MAX: return "psk_max(" + A() + ", " + B() + ")";
+        case PSK_OP_MIN: return "psk_min(" + A() + ", " + B() + ")";
+        case PSK_OP_NEG: return "(-" + A() + ")";
+        case PSK_OP_ABS: return "fabsf(" + A() + ")";
+        case PSK_OP_EXP: return "expf(" + A() + ")";
+        case PSK_OP_LOG: return "logf(" + A() + ")";
+        case PSK_OP_SQRT: return "sqrtf(" + A() + ")";
+        case PSK_OP_TANH: return "tanhf(" + A() + ")";
+        case PSK_OP_ERF: return "erff(" + A() + ")";
+        case PSK_OP_GELU: return "psk_gelu(" + A() + ")";
+        case PSK_OP_SQRTABS: return "sqrtf(fabsf(" + A() + "))";
+        case PSK_OP_POW2: return "(" + A() + " * " + A() + ")";
+        case PSK_OP_POWN: {
+            if (nd.iparam == 0) return "1.0f";
+            std::string s = A();
+            for (int k = 1; k < nd.iparam; ++k) s = "(" + s + " * " + A() + ")";
+            return s;
+        }
+        case PSK_OP_SELECT: return "((" + A() + " != 0.0f) ? " + B() + " : " + C() + ")";
+        case PSK_OP_CAUSAL_MASK: return "((" + col(e) + " <= q) ? " + A() + " : (-__builtin_inff()))";
+        default: return "0.0f";
+        }
+    }
+
+    static int esize(psk_dtype d) { return d == PSK_BF16 ? 2 : 4; }
+
+    std::string ptype(psk_dtype d) const { return d == PSK_BF16 ? "psk_u16" : "float"; }
+
+    // offset expression of input k's row part for the current row variable `rv`
+    std::string row_offset(const InputInfo& in, const std::string& rv) const
+    {
+        // output leading axes O0,O1,O2 (right-aligned), row = (i0*O1 + i1)*O2 + i2
+        const int64_t* O = an.out_shape4;
+        const int64_t* A = in.aligned;
+        int64_t st[4];
+        st[3] = 1;
+        for (int d = 2; d >= 0; --d) st[d] = st[d + 1] * A[d + 1];
+        std::string s = "0";
+        for (int d = 0; d < 3; ++d) {
+            if (A[d] == 1) continue;
+            int64_t inner = 1;
+            for (int dd = d + 1; dd < 3; ++dd) inner *= O[dd];
+            std::string idx = "(" + rv;
+            if (inner != 1) idx += " / (" + std::string(I()) + ")" + std::to_string(inner);
+            idx += ")";
+            if (d > 0) idx = "(" + idx + " % (" + std::string(I()) + ")" + std::to_string(O[d]) + ")";
+            s += " + " + idx + " * (" + std::string(I()) + ")" + std::to_string(st[d]);
+        }
+        return s;
+    }
+
+    // emit loading of a vector of input k at element offset `off` into x{k}_{e0..}
+    void load_vec(int k, const std::string& off, int e0, const std::string& cond)
+    {
+        const InputInfo& in = an.inputs[k];
+        const int V = pl.vec;
+        const int bytes = V * esize(in.dtype);
+        std::string base = "in" + std::to_string(k);
+        std::string ks = std::to_string(k);
+        std::string p = "(" + base + " + " + off + ")";
+        auto dst = [&](int j) { return "x" + ks + "_" + std::to_string(e0 + j); };
+        if (V == 1) {
+            o << "    float " << dst(0) << " = 0.0f;\n";
+            o << "    if (" << cond << ") " << dst(0) << " = "
+              << (in.dtype == PSK_BF16 ? "psk_h(*" + p + ")" : "*" + p) << ";\n";
+            return;
+        }
+        int nwords = bytes / 4;
+        // 16-byte pieces (or one 8-byte piece for 4 bf16)
+        std::vector<std::string> words;
+        int piece = 0;
+        for (int w = 0; w < nwords; w += 4, ++piece) {
+            int cnt = std::min(4, nwords - w);
+            std::string wn = "w" + ks + "_" + std::to_string(e0) + "_" + std::to_string(piece);
+            int elems_per_word = 4 / esize(in.dtype);
+            int eoff = w * elems_per_word;
+            if (cnt == 4) {
+                o << "    uint4 " << wn << " = make_uint4(0u, 0u, 0u, 0u);\n";
+                o << "    if (" << cond << ") " << wn << " = *(const uint4*)(" << p << " + " << eoff << ");\n";
+                words.push_back(wn + ".x"); words.push_back(wn + ".y");
+                words.push_back(wn + ".z"); words.push_back(wn + ".w");
+            } else {
+                o << "    uint2 " << wn << " = make_uint2(0u, 0u);\n";
+                o << "    if (" << cond << ") " << wn << " = *(const uint2*)(" << p << " + " << eoff << ");\n";
+                words.push_back(wn + ".x"); words.push_back(wn + ".y");
+            }
+        }
+        for (int j = 0; j < V; ++j) {
+            std::string v;
+            if (in.dtype == PSK_F32) v = "__uint_as_float(" + words[j] + ")";
+            else v = (j % 2 == 0 ? "psk_lo(" : "psk_hi(") + words[j / 2] + ")";
+            o << "    const float " << dst(j) << " = " << v << ";\n";
+        }
+    }
+
+    void store_vec(const std::string& off, int e0, const std::string& cond)
+    {
+        const int V = pl.vec;
+        std::string p = "(out + " + off + ")";
+        auto src = [&](int j) { return val(an.root, e0 + j); };
+        if (V == 1) {
+            o << "    if (" << cond << ") *" << p << " = "
+              << (an.out_dtype == PSK_BF16 ? "psk_r1(" + src(0) + ")" : src(0)) << ";\n";
+            return;
+        }
+        if (an.out_dtype == PSK_F32) {
+            o << "    if (" << cond << ") *(uint4*)" << p << " = make_uint4(";
+            for (int j = 0; j < 4; ++j) o << (j ? ", " : "") << "__float_as_uint(" << src(j) << ")";
+            o << ");\n";
+        } else {
+            o << "    if (" << cond << ") *(uint4*)" << p << " = make_uint4(";
+            for (int j = 0; j < 4; ++j) o << (j ? ", " : "") << "psk_pack2(" << src(2 * j) << ", " << src(2 * j + 1) << ")";
+            o << ");\n";
+        }
+    }
+
+    void signature(const std::string& name)
+    {
+        o << "extern \"C\" __global__ void __launch_bounds__(" << pl.block << ") " << name << "(";
+        // no __restrict__: the output may be the same buffer as an input
+        // (in place); every load of an element precedes its store
+        for (size_t k = 0; k < an.inputs.size(); ++k)
+            o << "const void* in" << k << "_, ";
+        o << "void* out_, long long n_total)\n{\n";
+        for (size_t k = 0; k < an.inputs.size(); ++k)
+            o << "  const " << ptype(an.inputs[k].dtype) << "* in" << k << " = (const "
+              << ptype(an.inputs[k].dtype) << "*)in" << k << "_;\n";
+        o << "  " << ptype(an.out_dtype) << "* out = (" << ptype(an.out_dtype) << "*)out_;\n";
+    }
+
+    // element members of the given depth, and row members of that depth
+    void members_at(int p)
+    {
+        for (size_t i = 0; i < an.nodes.size(); ++i) {
+            const psk_node& nd = an.nodes[i];
+            if (op_is_leaf(nd.op) || op_is_row(nd.op) || an.depth[i] != p) continue;
+            if (an.is_row[i]) {
+                o << "    const float r" << i << " = " << expr((int)i, 0) << ";\n";
+            } else {
+                for (int e = 0; e < NE; ++e)
+                    o << "    const float v" << i << "_" << e << " = " << expr((int)i, e) << ";\n";
+            }
+        }
+    }
+
+    void leaves()
+    {
+        for (size_t i = 0; i < an.nodes.size(); ++i) {
+            const psk_node& nd = an.nodes[i];
+            if (nd.op == PSK_OP_CONST) {
+                o << "    const float r" << i << " = " << flit(nd.imm) << ";\n";
+            } else if (nd.op == PSK_OP_INPUT) {
+                const InputInfo& in = an.inputs[nd.iparam];
+                if (an.is_row[i]) {
+                    o << "    const float r" << i << " = xr" << nd.iparam << ";\n";
+                } else {
+                    (void)in;
+                    for (int e = 0; e < NE; ++e)
+                        o << "    const float v" << i << "_" << e << " = x" << nd.iparam << "_" << e << ";\n";
+                }
+            }
+        }
+    }
+
+    // row-value inputs: one load per row (or one per thread for scalars)
+    void row_inputs(const std::string& rv, const std::string& cond)
+    {
+        for (size_t k = 0; k < an.inputs.size(); ++k) {
+            const InputInfo& in = an.inputs[k];
+            if (!in.used || !(in.kind == InKind::Scalar || in.kind == InKind::RowConst)) continue;
+            std::string off = in.kind == InKind::Scalar ? "0" : row_offset(in, rv);
+            std::string p = "(in" + std::to_string(k) + " + " + off + ")";
+            o << "    const float xr" << k << " = (" << cond << ") ? "
+              << (in.dtype == PSK_BF16 ? "psk_h(*" + p + ")" : "*" + p) << " : 0.0f;\n";
+        }
+    }
+
+    std::string elem_offset(const InputInfo& in, const std::string& rv, const std::string& cexpr)
+    {
+        switch (in.kind) {
+        case InKind::Full: return "(" + rv + ") * (" + std::string(I()) + ")" + std::to_string(an.cols) + " + " + cexpr;
+        case InKind::ColVec: return cexpr;
+        default: return "(" + row_offset(in, rv) + ") + " + cexpr;
+        }
+    }
+
+    // ------------------------------------------------------------ pointwise
+    std::string pointwise(const std::string& name)
+    {
+        o << kPrelude;
+        signature(name);
+        const int V = pl.vec;
+        o << "  {\n";
+        o << "    const " << I() << " t = (" << I() << ")blockIdx.x * " << pl.block << " + (" << I() << ")threadIdx.x;\n";
+        o << "    const " << I() << " e0 = t * " << V << ";\n";
+        o << "    if (e0 >= (" << I() << ")n_total) return;\n";
+        o << "    const " << I() << " row = e0 / (" << I() << ")" << an.cols << ";\n";
+        o << "    const " << I() << " c0 = e0 - row * (" << I() << ")" << an.cols << ";\n";
+        if (period > 0) o << "    const " << I() << " q = row % (" << I() << ")" << period << ";\n";
+        row_inputs("row", "true");
+        for (size_t k = 0; k < an.inputs.size(); ++k) {
+            const InputInfo& in = an.inputs[k];
+            if (!in.used || in.kind == InKind::Scalar || in.kind == InKind::RowConst) continue;
+            std::string cond = V == 1 ? "true" : "true";
+            if (in.mask_guarded) cond = "c0 <= q";
+            load_vec((int)k, elem_offset(in, "row", "c0"), 0, cond);
+        }
+        leaves();
+        members_at(0);
+        store_vec("e0", 0, "true");
+        o << "  }\n}\n";
+        return o.str();
+    }
+
+    // ------------------------------------------------------------------ row
+    void reductions_at(int p)
+    {
+        // reductions whose operand has depth p
+        std::vector<int> reds;
+        for (size_t i = 0; i < an.nodes.size(); ++i)
+            if (op_is_row(an.nodes[i].op) && an.depth[i] == p + 1) reds.push_back((int)i);
+        if (reds.empty()) return;
+        const int W = pl.lanes / 64;
+        for (int i : reds) {
+            const psk_node& nd = an.nodes[i];
+            bool mx = nd.op == PSK_OP_ROW_MAX;
+            o << "    float p" << i << " = " << (mx ? "(-__builtin_inff())" : "0.0f") << ";\n";
+            for (int e = 0; e < NE; ++e) {
+                std::string v = val(nd.a, e);
+                std::string acc = mx ? "psk_max(p" + std::to_string(i) + ", " + v + ")"
+                                     : "(p" + std::to_string(i) + " + " + v + ")";
+                if (ragged)
+                    o << "    if (" << col(e) << " < " << an.cols << ") p" << i << " = " << acc << ";\n";
+                else
+                    o << "    p" << i << " = " << acc << ";\n";
+            }
+            if (pl.lanes == 16)
+                o << "    p" << i << " = " << (mx ? "psk_max16" : "psk_sum16") << "(p" << i << ");\n";
+            else
+                o << "    p" << i << " = " << (mx ? "psk_max64" : "psk_sum64") << "(p" << i << ");\n";
+        }
+        if (W > 1) {
+            const int NR = (int)reds.size();
+            std::string arr = "psk_red" + std::to_string(p);
+            o << "    __shared__ float " << arr << "[" << pl.rows_per_block * W * NR << "];\n";
+            o << "    if ((lane & 63) == 0) {\n";
+            for (int r = 0; r < NR; ++r)
+                o << "      " << arr << "[(slot * " << W << " + (lane >> 6)) * " << NR << " + " << r << "] = p"
+                  << reds[r] << ";\n";
+            o << "    }\n    __syncthreads();\n";
+            for (int r = 0; r < NR; ++r) {
+                int i = reds[r];
+                bool mx = an.nodes[i].op == PSK_OP_ROW_MAX;
+                o << "    p" << i << " = " << arr << "[(slot * " << W << ") * " << NR << " + " << r << "];\n";
+                for (int w = 1; w < W; ++w) {
+                    std::string el = arr + "[(slot * " + std::to_string(W) + " + " + std::to_string(w) + ") * " +
+                                     std::to_string(NR) + " + " + std::to_string(r) + "]";
+                    if (mx) o << "    p" << i << " = psk_max(p" << i << ", " << el << ");\n";
+                    else o << "    p" << i << " = p" << i << " + " << el << ";\n";
+                }
+            }
+        }
+        for (int i : reds) {
+            if (an.nodes[i].op == PSK_OP_ROW_MEAN)
+                o << "    const float r" << i << " = p" << i << " / " << flit((float)an.cols) << ";\n";
+            else
+                o << "    const float r" << i << " = p" << i << ";\n";
+        }
+    }
+
+    std::string row(const std::string& name)
+    {
+        o << kPrelude;
+        signature(name);
+        const int L = pl.lanes, V = pl.vec;
+        o << "  {\n";
+        o << "    const int slot = (int)threadIdx.x / " << L << ";\n";
+        o << "    const int lane = (int)threadIdx.x % " << L << ";\n";
+        o << "    const " << I() << " row = (" << I() << ")blockIdx.x * " << pl.rows_per_block << " + slot;\n";
+        o << "    const bool rok = row < (" << I() << ")n_total;\n";
+        if (period > 0) o << "    const int q = (int)(row % (" << I() << ")" << period << ");\n";
+        for (int k = 0; k < pl.nv; ++k)
+            o << "    const int c" << k << " = (" << k * L << " + lane) * " << V << ";\n";
+        row_inputs("row", "rok");
+        for (size_t k = 0; k < an.inputs.size(); ++k) {
+            const InputInfo& in = an.inputs[k];
+            if (!in.used || in.kind == InKind::Scalar || in.kind == InKind::RowConst) continue;
+            for (int v = 0; v < pl.nv; ++v) {
+                std::string c = "c" + std::to_string(v);
+                std::string cond = "rok";
+                if ((int64_t)(v + 1) * L * V > an.cols) cond += " && " + c + " < " + std::to_string(an.cols);
+                if (in.mask_guarded) cond += " && " + c + " <= q";
+                load_vec((int)k, elem_offset(in, "row", c), v * V, cond);
+            }
+        }
+        leaves();
+        for (int p = 0; p <= an.phases; ++p) {
+            members_at(p);
+            if (p < an.phases) reductions_at(p);
+        }
+        for (int v = 0; v < pl.nv; ++v) {
+            std::string c = "c" + std::to_string(v);
+            std::string cond = "rok";
+            if ((int64_t)(v + 1) * L * V > an.cols) cond += " && " + c + " < " + std::to_string(an.cols);
+            store_vec("row * (" + std::string(I()) + ")" + std::to_string(an.cols) + " + " + c, v * V, cond);
+        }
+        o << "  }\n}\n";
+        return o.str();
+    }
+};
+
+}  // namespace
+
+std::string emit_source(const Analysis& an, const KernelPlan& plan, const std::string& kernel_name)
+{
+    Emitter em(an, plan);
+    std::ostringstream hdr;
+    hdr << "// psk_fused emitted kernel\n// group:\n";
+    std::istringstream ct(canonical_text(an));
+    std::string line;
+    while (std::getline(ct, line)) hdr << "//   " << line << "\n";
+    hdr << "// plan: kind " << plan.kind << " vec " << plan.vec << " block " << plan.block << " lanes " << plan.lanes
+        << " nv " << plan.nv << "\n";
+    return hdr.str() + (plan.kind == 1 ? em.row(kernel_name) : em.pointwise(kernel_name));
+}
+
+}  // namespace psk

@@ -1,0 +1,135 @@
+// Internal declarations of the psk_fused library (not part of the C ABI).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "psk_fused.h"
+
+namespace psk {
+
+// ------------------------------------------------------------------ errors
+// Records a message for the calling thread and returns the status.
+psk_status fail(psk_status st, const std::string& msg);
+void clear_error();
+
+// --------------------------------------------------------------- analysis
+enum class InKind : int {
+    Scalar = 0,     // every axis broadcast: one value for the whole output
+    RowConst = 1,   // last axis broadcast: one value per row
+    ColVec = 2,     // only the last axis varies: the same row vector for every row
+    General = 3,    // last axis contiguous, leading axes by their strides
+    Full = 4        // same shape as the output: flat index
+};
+
+struct InputInfo {
+    psk_dtype dtype = PSK_F32;
+    int rank = 0;
+    int64_t shape[PSK_MAX_RANK] = {0, 0, 0, 0};
+    int64_t aligned[PSK_MAX_RANK] = {1, 1, 1, 1};  // shape right-aligned to the output's 4 axes
+    int64_t numel = 0;
+    InKind kind = InKind::Scalar;
+    bool used = false;
+    bool mask_guarded = false;   // read only where a causal mask allows
+};
+
+// Everything the emitter needs to know about a validated group.
+struct Analysis {
+    std::vector<psk_node> nodes;
+    int root = -1;
+    int members = 0;
+    int n_reductions = 0;
+    int phases = 0;                     // max reduction depth of the root
+    std::vector<char> is_row;           // node value is one per row
+    std::vector<int> depth;             // reduction phases that precede the node
+    std::vector<int> n_readers;
+    std::vector<char> needed;           // reachable from the root
+    std::vector<InputInfo> inputs;
+    psk_dtype out_dtype = PSK_F32;
+    int out_rank = 1;
+    int64_t out_shape4[PSK_MAX_RANK] = {1, 1, 1, 1};  // output right-aligned to 4 axes
+    int64_t rows = 0, cols = 0, numel = 0;
+    bool row_kind = false;              // has at least one row reduction
+    uint32_t flags = 0;
+};
+
+// Validates the descriptor; on success fills `an`.
+psk_status analyse(const psk_group_desc* desc, Analysis& an);
+
+bool op_is_leaf(int op);
+bool op_is_elementwise(int op);
+bool op_is_row(int op);
+bool op_is_boundary(int op);
+int op_arity(int op);
+const char* op_name(int op);
+
+// ------------------------------------------------------------------- emit
+struct KernelPlan {
+    int kind = 0;            // 0 pointwise, 1 row
+    int vec = 1;             // elements per vector access
+    int block = 256;         // threads per workgroup
+    int lanes = 64;          // row kernel: lanes per row
+    int rows_per_block = 1;  // row kernel
+    int nv = 1;              // row kernel: vectors per lane
+    int64_t grid = 0;        // workgroups for the whole output
+};
+
+KernelPlan plan_kernel(const Analysis& an, bool allow_vector);
+// HIP source for the group under `plan`, entry point named `kernel_name`.
+std::string emit_source(const Analysis& an, const KernelPlan& plan, const std::string& kernel_name);
+// Canonical text of the group (what the kernel cache is keyed by).
+std::string canonical_text(const Analysis& an);
+uint64_t fnv1a(const std::string& s);
+
+// -------------------------------------------------------------------- JIT
+// Compile HIP source for gfx950 with hipRTC; returns the code object.
+psk_status jit_compile(const std::string& source, const std::string& name, std::vector<char>& code);
+extern const char* const kJitOptions[];
+extern const int kJitOptionCount;
+
+// -------------------------------------------------------------- partition
+psk_status partition(int32_t n, const psk_node* body, const psk_tensor_desc* types, const uint8_t* is_output,
+                     int32_t* group_of, int32_t* is_root, int32_t* n_groups);
+
+// ------------------------------------------------------------------ trees
+struct TreePlan {
+    std::vector<int64_t> leaf_offset;    // n_leaves + 1
+    std::vector<int32_t> chunk_leaf;
+    std::vector<int64_t> chunk_start;
+    std::vector<int32_t> chunk_count;
+};
+psk_status plan_tree(const int64_t* numel, int32_t n_leaves, int64_t chunk_elems, TreePlan& plan);
+
+// ------------------------------------------------------------------ AdamW
+// f32 scalars of one step, each formed in f64 and rounded once.
+struct AdamwScalars {
+    float b1, b2, c1, c2, bc1, bc2, lr, eps, wd;
+};
+AdamwScalars adamw_scalars(const psk_adamw_hp& hp);
+
+// Device-side leaf descriptor: input slots theta, g, m, v; output slots
+// theta', m', v' (the input's address when updated in place).
+struct LeafDev {
+    const void* in[4];
+    void* out[3];
+    int64_t flags;      // bit 0: every slot 16-byte aligned (vector path)
+};
+// Device-side chunk: `count` elements of leaf `leaf` from element `start`.
+struct ChunkDev {
+    int32_t leaf;
+    int32_t count;
+    int64_t start;
+};
+static_assert(sizeof(LeafDev) == 64, "LeafDev layout");
+static_assert(sizeof(ChunkDev) == 16, "ChunkDev layout");
+
+// One launch over every chunk (defined in adamw.hip).
+psk_status launch_adamw(const LeafDev* d_leaves, const ChunkDev* d_chunks, int64_t n_chunks, int theta_dt,
+                        int grad_dt, int mv_dt, const AdamwScalars& s, void* stream);
+
+// --------------------------------------------------------------- counters
+void count_launch();
+void count_jit(bool hit);
+
+}  // namespace psk

@@ -1,0 +1,299 @@
+// Descriptor validation and analysis of a fusion group.  Host-only integer
+// code: no HIP call, so it runs (and is tested) without a GPU.
+//
+// The checks follow the membership conditions of a group (presk manual,
+// "PSK-Realize", section "What a group is"): elementwise members, one result
+// type for the element members (inputs may be smaller and broadcast), every
+// member but the root read only by members, at most 64 members, and pow n
+// with n > 2 never joining a group.  Row reductions are last-axis keepdim
+// reductions whose value feeds an elementwise epilogue (poot, "Fusion and
+// Planning", section "Reduction-rooted regions").
+#include <cmath>
+#include <cstring>
+#include <sstream>
+
+#include "psk_internal.h"
+
+namespace psk {
+
+bool op_is_leaf(int op) { return op == PSK_OP_INPUT || op == PSK_OP_CONST; }
+
+bool op_is_row(int op) { return op == PSK_OP_ROW_MAX || op == PSK_OP_ROW_SUM || op == PSK_OP_ROW_MEAN; }
+
+bool op_is_boundary(int op)
+{
+    return op == PSK_OP_REDUCE || op == PSK_OP_CONTRACT || op == PSK_OP_CAST || op == PSK_OP_OPAQUE;
+}
+
+bool op_is_elementwise(int op)
+{
+    switch (op) {
+    case PSK_OP_ADD: case PSK_OP_SUB: case PSK_OP_MUL: case PSK_OP_DIV: case PSK_OP_MAX: case PSK_OP_MIN:
+    case PSK_OP_NEG: case PSK_OP_ABS: case PSK_OP_EXP: case PSK_OP_LOG: case PSK_OP_SQRT: case PSK_OP_TANH:
+    case PSK_OP_ERF: case PSK_OP_GELU: case PSK_OP_SQRTABS: case PSK_OP_POW2: case PSK_OP_POWN:
+    case PSK_OP_SELECT: case PSK_OP_CAUSAL_MASK:
+        return true;
+    default:
+        return false;
+    }
+}
+
+int op_arity(int op)
+{
+    switch (op) {
+    case PSK_OP_INPUT: case PSK_OP_CONST: return 0;
+    case PSK_OP_ADD: case PSK_OP_SUB: case PSK_OP_MUL: case PSK_OP_DIV: case PSK_OP_MAX: case PSK_OP_MIN:
+    case PSK_OP_CONTRACT:
+        return 2;
+    case PSK_OP_SELECT: return 3;
+    case PSK_OP_OPAQUE: return -1;  // any number of operands
+    default: return 1;
+    }
+}
+
+const char* op_name(int op)
+{
+    switch (op) {
+    case PSK_OP_INPUT: return "input"; case PSK_OP_CONST: return "const";
+    case PSK_OP_ADD: return "add"; case PSK_OP_SUB: return "sub"; case PSK_OP_MUL: return "mul";
+    case PSK_OP_DIV: return "div"; case PSK_OP_MAX: return "max"; case PSK_OP_MIN: return "min";
+    case PSK_OP_NEG: return "neg"; case PSK_OP_ABS: return "abs"; case PSK_OP_EXP: return "exp";
+    case PSK_OP_LOG: return "log"; case PSK_OP_SQRT: return "sqrt"; case PSK_OP_TANH: return "tanh";
+    case PSK_OP_ERF: return "erf"; case PSK_OP_GELU: return "gelu"; case PSK_OP_SQRTABS: return "sqrtabs";
+    case PSK_OP_POW2: return "pow2"; case PSK_OP_POWN: return "pown"; case PSK_OP_SELECT: return "select";
+    case PSK_OP_CAUSAL_MASK: return "causal_mask"; case PSK_OP_ROW_MAX: return "row_max";
+    case PSK_OP_ROW_SUM: return "row_sum"; case PSK_OP_ROW_MEAN: return "row_mean";
+    case PSK_OP_REDUCE: return "reduce"; case PSK_OP_CONTRACT: return "contract"; case PSK_OP_CAST: return "cast";
+    case PSK_OP_OPAQUE: return "opaque";
+    default: return "?";
+    }
+}
+
+static bool dtype_ok(int32_t d) { return d == PSK_F32 || d == PSK_BF16; }
+
+static std::string at(int i) { return "node " + std::to_string(i) + ": "; }
+
+psk_status analyse(const psk_group_desc* desc, Analysis& an)
+{
+    if (!desc)
+        return fail(PSK_E_NULL, "group descriptor is NULL");
+    if (desc->n_nodes < 1 || desc->n_nodes > PSK_MAX_NODES)
+        return fail(PSK_E_CAP, "n_nodes must be in 1.." + std::to_string(PSK_MAX_NODES));
+    if (!desc->nodes)
+        return fail(PSK_E_NULL, "nodes is NULL");
+    if (desc->n_inputs < 0 || desc->n_inputs > PSK_MAX_INPUTS)
+        return fail(PSK_E_CAP, "n_inputs must be in 0.." + std::to_string(PSK_MAX_INPUTS));
+    if (desc->n_inputs > 0 && !desc->inputs)
+        return fail(PSK_E_NULL, "inputs is NULL");
+    if (desc->arith != PSK_F32)
+        return fail(PSK_E_TYPE, "the arithmetic type must be f32 (bf16 is storage only)");
+    if (desc->flags != 0)
+        return fail(PSK_E_UNSUPPORTED, "flags must be 0");
+
+    // ---- output
+    const psk_tensor_desc& o = desc->out;
+    if (o.rank < 1 || o.rank > PSK_MAX_RANK)
+        return fail(PSK_E_SHAPE, "output rank must be in 1..4");
+    if (!dtype_ok(o.dtype))
+        return fail(PSK_E_TYPE, "output storage type must be f32 or bf16");
+    an = Analysis();
+    an.out_dtype = (psk_dtype)o.dtype;
+    an.out_rank = o.rank;
+    for (int d = 0; d < o.rank; ++d) {
+        if (o.shape[d] < 0)
+            return fail(PSK_E_SHAPE, "output shape has a negative size");
+        an.out_shape4[PSK_MAX_RANK - o.rank + d] = o.shape[d];
+    }
+    an.cols = an.out_shape4[3];
+    an.rows = an.out_shape4[0] * an.out_shape4[1] * an.out_shape4[2];
+    an.numel = an.rows * an.cols;
+    if (an.numel > (int64_t(1) << 40))
+        return fail(PSK_E_SHAPE, "output larger than 2^40 elements");
+
+    // ---- inputs
+    an.inputs.resize(desc->n_inputs);
+    for (int k = 0; k < desc->n_inputs; ++k) {
+        const psk_tensor_desc& t = desc->inputs[k];
+        InputInfo& in = an.inputs[k];
+        if (t.rank < 0 || t.rank > PSK_MAX_RANK)
+            return fail(PSK_E_SHAPE, "input " + std::to_string(k) + ": rank must be in 0..4");
+        if (t.rank > o.rank)
+            return fail(PSK_E_BROADCAST, "input " + std::to_string(k) + ": rank above the output's");
+        if (!dtype_ok(t.dtype))
+            return fail(PSK_E_TYPE, "input " + std::to_string(k) + ": storage type must be f32 or bf16");
+        in.dtype = (psk_dtype)t.dtype;
+        in.rank = t.rank;
+        in.numel = 1;
+        for (int d = 0; d < t.rank; ++d) {
+            if (t.shape[d] < 0)
+                return fail(PSK_E_SHAPE, "input " + std::to_string(k) + ": negative size");
+            in.shape[d] = t.shape[d];
+            in.aligned[PSK_MAX_RANK - t.rank + d] = t.shape[d];
+            in.numel *= t.shape[d];
+        }
+        bool all1 = true, lead1 = true, same = true;
+        for (int d = 0; d < PSK_MAX_RANK; ++d) {
+            int64_t a = in.aligned[d], od = an.out_shape4[d];
+            if (a != od && a != 1)
+                return fail(PSK_E_BROADCAST, "input " + std::to_string(k) + ": axis " + std::to_string(d) +
+                                                 " of length " + std::to_string(a) + " does not broadcast to " +
+                                                 std::to_string(od) + " (an input may not widen the output)");
+            if (a != 1) all1 = false;
+            if (d < 3 && a != 1) lead1 = false;
+            if (a != od) same = false;
+        }
+        if (all1)
+            in.kind = InKind::Scalar;
+        else if (in.aligned[3] == 1)
+            in.kind = InKind::RowConst;
+        else if (same)
+            in.kind = InKind::Full;
+        else if (lead1)
+            in.kind = InKind::ColVec;
+        else
+            in.kind = InKind::General;
+    }
+
+    // ---- nodes: ops, operands, order
+    const int n = desc->n_nodes;
+    an.nodes.assign(desc->nodes, desc->nodes + n);
+    an.n_readers.assign(n, 0);
+    for (int i = 0; i < n; ++i) {
+        const psk_node& nd = an.nodes[i];
+        if (op_is_boundary(nd.op))
+            return fail(PSK_E_OP, at(i) + std::string(op_name(nd.op)) +
+                                      " is a group boundary (reduction, contraction or cast), not a member");
+        if (!op_is_leaf(nd.op) && !op_is_elementwise(nd.op) && !op_is_row(nd.op))
+            return fail(PSK_E_OP, at(i) + "unknown op " + std::to_string(nd.op));
+        int ar = op_arity(nd.op);
+        const int32_t opnd[3] = {nd.a, nd.b, nd.c};
+        for (int k = 0; k < 3; ++k) {
+            if (k < ar) {
+                if (opnd[k] < 0 || opnd[k] >= i)
+                    return fail(PSK_E_ORDER, at(i) + "operand " + std::to_string(k) +
+                                                 " must name an earlier node, got " + std::to_string(opnd[k]));
+                an.n_readers[opnd[k]]++;
+            } else if (opnd[k] != -1) {
+                return fail(PSK_E_OP, at(i) + std::string(op_name(nd.op)) + " takes " + std::to_string(ar) +
+                                          " operand(s); unused operands must be -1");
+            }
+        }
+        if (nd.op == PSK_OP_INPUT && (nd.iparam < 0 || nd.iparam >= desc->n_inputs))
+            return fail(PSK_E_OP, at(i) + "input slot " + std::to_string(nd.iparam) + " out of range");
+        if (nd.op == PSK_OP_POWN && (nd.iparam < 0 || nd.iparam > 64))
+            return fail(PSK_E_OP, at(i) + "pown exponent must be in 0..64");
+        if (nd.op == PSK_OP_CAUSAL_MASK && nd.iparam < 1)
+            return fail(PSK_E_OP, at(i) + "causal_mask period must be >= 1");
+        if (!op_is_leaf(nd.op))
+            an.members++;
+    }
+    if (an.members > PSK_MAX_MEMBERS)
+        return fail(PSK_E_CAP, "group has " + std::to_string(an.members) +
+                                   " members; past 64 a group stops growing");
+    if (desc->root < 0 || desc->root >= n)
+        return fail(PSK_E_ROOT, "root index out of range");
+    an.root = desc->root;
+    if (op_is_leaf(an.nodes[an.root].op))
+        return fail(PSK_E_ROOT, "the root must be a member, not an input or a constant");
+    if (an.n_readers[an.root] != 0)
+        return fail(PSK_E_ROOT, "the root is read by another node");
+    for (int i = 0; i < n; ++i)
+        if (i != an.root && an.n_readers[i] == 0 && !op_is_leaf(an.nodes[i].op))
+            return fail(PSK_E_ROOT, at(i) + "a second unread member: a group has exactly one root");
+    // reachability from the root
+    an.needed.assign(n, 0);
+    an.needed[an.root] = 1;
+    for (int i = an.root; i >= 0; --i) {
+        if (!an.needed[i]) continue;
+        const psk_node& nd = an.nodes[i];
+        int ar = op_arity(nd.op);
+        const int32_t opnd[3] = {nd.a, nd.b, nd.c};
+        for (int k = 0; k < ar; ++k) an.needed[opnd[k]] = 1;
+    }
+    for (int i = 0; i < n; ++i)
+        if (!an.needed[i])
+            return fail(PSK_E_DEAD, at(i) + "not read on any path to the root (dead code)");
+    for (int i = 0; i < n; ++i)
+        if (an.nodes[i].op == PSK_OP_POWN && an.nodes[i].iparam > 2 && an.members > 1)
+            return fail(PSK_E_OP, at(i) + "pow n with n > 2 never joins a group");
+
+    // ---- row-level values and reduction depth
+    an.is_row.assign(n, 0);
+    an.depth.assign(n, 0);
+    for (int i = 0; i < n; ++i) {
+        const psk_node& nd = an.nodes[i];
+        int ar = op_arity(nd.op);
+        const int32_t opnd[3] = {nd.a, nd.b, nd.c};
+        int dep = 0;
+        for (int k = 0; k < ar; ++k) dep = std::max(dep, an.depth[opnd[k]]);
+        if (nd.op == PSK_OP_INPUT) {
+            InputInfo& in = an.inputs[nd.iparam];
+            in.used = true;
+            an.is_row[i] = (in.kind == InKind::Scalar || in.kind == InKind::RowConst);
+        } else if (nd.op == PSK_OP_CONST) {
+            an.is_row[i] = 1;
+        } else if (op_is_row(nd.op)) {
+            if (an.is_row[nd.a])
+                return fail(PSK_E_ROW, at(i) + "a row reduction must reduce an element value, not a row value");
+            an.is_row[i] = 1;
+            dep = an.depth[nd.a] + 1;
+            an.n_reductions++;
+        } else if (nd.op == PSK_OP_CAUSAL_MASK) {
+            an.is_row[i] = 0;
+        } else {
+            bool all_row = true;
+            for (int k = 0; k < ar; ++k) all_row = all_row && an.is_row[opnd[k]];
+            an.is_row[i] = all_row;
+        }
+        an.depth[i] = dep;
+    }
+    an.row_kind = an.n_reductions > 0;
+    an.phases = an.depth[an.root];
+    if (an.is_row[an.root] && an.cols > 1)
+        return fail(PSK_E_ROW, "the root is one value per row but the output has " + std::to_string(an.cols) +
+                                   " columns: a reduction cannot be the stored value here");
+    if (an.row_kind && an.cols > 65536)
+        return fail(PSK_E_UNSUPPORTED, "row groups over rows longer than 65536 are not implemented");
+
+    // ---- inputs read only where a causal mask allows them
+    // A value is irrelevant at refused positions when every reader is a
+    // causal mask or an element member whose own value is irrelevant there;
+    // the root is stored everywhere.  Only when every mask shares one period.
+    int period = -1;
+    bool one_period = true;
+    for (int i = 0; i < n; ++i)
+        if (an.nodes[i].op == PSK_OP_CAUSAL_MASK) {
+            if (period < 0) period = an.nodes[i].iparam;
+            else if (period != an.nodes[i].iparam) one_period = false;
+        }
+    if (period > 0 && one_period) {
+        std::vector<std::vector<int>> readers(n);
+        for (int i = 0; i < n; ++i) {
+            const psk_node& nd = an.nodes[i];
+            int ar = op_arity(nd.op);
+            const int32_t opnd[3] = {nd.a, nd.b, nd.c};
+            for (int k = 0; k < ar; ++k) readers[opnd[k]].push_back(i);
+        }
+        std::vector<char> irrelevant(n, 0);
+        for (int i = n - 1; i >= 0; --i) {
+            if (i == an.root || readers[i].empty() || an.is_row[i]) continue;
+            bool irr = true;
+            for (int r : readers[i]) {
+                const psk_node& rd = an.nodes[r];
+                if (rd.op == PSK_OP_CAUSAL_MASK) continue;
+                if (op_is_row(rd.op) || an.is_row[r] || !irrelevant[r]) { irr = false; break; }
+            }
+            irrelevant[i] = irr;
+        }
+        for (auto& in : an.inputs) in.mask_guarded = in.used;
+        for (int i = 0; i < n; ++i)
+            if (an.nodes[i].op == PSK_OP_INPUT) {
+                InputInfo& in = an.inputs[an.nodes[i].iparam];
+                if (!irrelevant[i] || in.kind == InKind::Scalar || in.kind == InKind::RowConst)
+                    in.mask_guarded = false;
+            }
+    }
+    return PSK_OK;
+}
+
+}  // namespace psk

@@ -1,0 +1,291 @@
+/*
+ * psk_fused -- fusion groups as single HIP kernels on MI355X (gfx950).
+ *
+ * A fusion group is a connected set of elementwise lets of one function that
+ * share one loop nest: every member is an elementwise primitive, every member
+ * has the same result type (inputs may be smaller and broadcast), and every
+ * member but the root is read only by members.  Intermediates stay in
+ * registers in the arithmetic type (f32, also for bf16 storage); only the
+ * root reaches memory, rounded to its storage type.  Past 64 members a group
+ * stops growing.  (presk manual, "PSK-Realize: fusion groups", section "What
+ * a group is"; "Native execution", section "The realization".)
+ *
+ * Three kinds of group run here, each as one kernel launch:
+ *   - a pointwise chain (poot, "Fusion and Planning", section "Fusable region
+ *     shapes": one thread per element);
+ *   - a chain with row-reduction roots: last-axis keepdim reductions whose
+ *     results feed an elementwise epilogue in the same kernel, the shape of
+ *     softmax and RMSNorm (same page, "Reduction-rooted regions");
+ *   - a chain mapped over every leaf of a parameter tree: the AdamW step
+ *     (presk manual, "PSK-Realize", section "What a group is", paragraph on
+ *     parameter trees; presk language reference, "The optimizer"), in one
+ *     launch for all leaves, driven by a device-side leaf/chunk table (the
+ *     role of poot's launch metadata buffer, "Kernel specialization").
+ *
+ * Conventions shared by every entry point:
+ *   - Every function returns a psk_status; on failure nothing is launched,
+ *     no object is created, and psk_last_error() returns a message for the
+ *     calling thread.  A request is refused, never silently adjusted
+ *     (presk manual, "PSK-Realize", section "The realization plan": an
+ *     ill-formed plan is refused).
+ *   - Device buffers and streams belong to the caller.  Group and tree
+ *     objects, their device tables and compiled kernels belong to the library.
+ *   - *_run / *_step calls are asynchronous on the given HIP stream (NULL =
+ *     the null stream); buffers must stay alive until the stream has reached
+ *     the launch.  Device faults surface at the caller's next synchronisation.
+ *   - Kernels never write their inputs unless an output is the same buffer
+ *     (in-place).  Outputs are not zeroed beforehand.
+ *   - The library allocates no device memory in *_run / *_step.
+ *   - All functions are thread-safe.
+ */
+#ifndef PSK_FUSED_H
+#define PSK_FUSED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PSK_VERSION 100
+#define PSK_MAX_MEMBERS 64      /* member (non-leaf) nodes per group */
+#define PSK_MAX_NODES 256       /* total nodes, leaves included */
+#define PSK_MAX_INPUTS 16
+#define PSK_MAX_RANK 4
+#define PSK_MAX_SLOTS 8
+
+typedef enum psk_status {
+    PSK_OK = 0,
+    PSK_E_NULL = 1,          /* a required pointer is NULL */
+    PSK_E_CAP = 2,           /* more than PSK_MAX_MEMBERS members, or too many nodes/inputs */
+    PSK_E_ORDER = 3,         /* an operand does not name an earlier node */
+    PSK_E_ROOT = 4,          /* the root is not the single unread member */
+    PSK_E_DEAD = 5,          /* a node no other node reads (dead code) */
+    PSK_E_OP = 6,            /* unknown op, wrong operand count, bad parameter, or a boundary op */
+    PSK_E_TYPE = 7,          /* arithmetic type other than f32, unknown storage type, dtype mismatch */
+    PSK_E_BROADCAST = 8,     /* an input that would widen the output, or a rank above the output's */
+    PSK_E_ROW = 9,           /* misuse of a row reduction */
+    PSK_E_ALIGN = 10,        /* a pointer not aligned to its element size */
+    PSK_E_ALIAS = 11,        /* an output overlapping an input it may not overlap */
+    PSK_E_SHAPE = 12,        /* a negative size, a rank out of range, sizes that disagree */
+    PSK_E_UNSUPPORTED = 13,  /* valid, but outside what this build implements */
+    PSK_E_JIT = 14,          /* hipRTC could not compile the emitted kernel */
+    PSK_E_HIP = 15           /* a HIP runtime call failed */
+} psk_status;
+
+/* Storage types.  bf16 is storage only: a load widens exactly (a 16-bit
+ * shift), a store rounds to nearest even (presk manual, "Native execution",
+ * section "The realization"). */
+typedef enum psk_dtype { PSK_F32 = 0, PSK_BF16 = 1 } psk_dtype;
+
+/* Node ops.  Elementwise set after poot "Fusion and Planning" (binary ops;
+ * Neg, Exp, Log, Sqrt, Tanh, Erf; Select) and the presk builtins (gelu,
+ * abs, max/min, pow n).  Semantics, all in f32:
+ *   ADD SUB MUL DIV          IEEE-754 binary32, correctly rounded
+ *   MAX MIN                  second operand at a tie (presk language
+ *                            reference, "Builtins")
+ *   NEG ABS                  sign operations
+ *   EXP LOG TANH ERF         device libm (last bits are the library's)
+ *   SQRT                     correctly rounded
+ *   SQRTABS                  sqrt(|a|)
+ *   GELU                     a * Phi(a) = (0.5*a) * erfc(-(a * f32(1/sqrt 2)))
+ *   POW2                     a * a
+ *   POWN (iparam n >= 0)     n-1 products of a, left to right; n = 0 gives 1.
+ *                            With n > 2 it never joins a group (PSK-Realize,
+ *                            "What a group is"): only as a group's sole member
+ *   SELECT                   a != 0 ? b : c, moving bits: the branch not
+ *                            picked never reaches the result (poot, "Fusable
+ *                            region shapes")
+ *   CAUSAL_MASK (iparam T)   a where column <= row mod T, else -inf; row is the
+ *                            flattened index over all axes but the last
+ *                            (causal_mask: allowed where seq2 <= seq, presk
+ *                            language reference, "Builtins")
+ *   ROW_MAX ROW_SUM ROW_MEAN reduction over the last axis, keepdim; the
+ *                            result broadcasts back along the row.  ROW_MEAN
+ *                            is ROW_SUM divided by the row length.
+ * Leaves: INPUT (iparam = input slot), CONST (imm = an f32 value).
+ * Boundary ops (REDUCE, CONTRACT, CAST, OPAQUE) are accepted by
+ * psk_partition only: a reduction ends a group, contractions and casts are
+ * boundaries (PSK-Realize, "What a group is"; poot, "Fusable region shapes").
+ */
+typedef enum psk_op {
+    PSK_OP_INPUT = 1, PSK_OP_CONST = 2,
+    PSK_OP_ADD = 10, PSK_OP_SUB = 11, PSK_OP_MUL = 12, PSK_OP_DIV = 13, PSK_OP_MAX = 14, PSK_OP_MIN = 15,
+    PSK_OP_NEG = 20, PSK_OP_ABS = 21, PSK_OP_EXP = 22, PSK_OP_LOG = 23, PSK_OP_SQRT = 24, PSK_OP_TANH = 25,
+    PSK_OP_ERF = 26, PSK_OP_GELU = 27, PSK_OP_SQRTABS = 28, PSK_OP_POW2 = 29, PSK_OP_POWN = 30,
+    PSK_OP_SELECT = 40, PSK_OP_CAUSAL_MASK = 41,
+    PSK_OP_ROW_MAX = 50, PSK_OP_ROW_SUM = 51, PSK_OP_ROW_MEAN = 52,
+    PSK_OP_REDUCE = 60, PSK_OP_CONTRACT = 61, PSK_OP_CAST = 62, PSK_OP_OPAQUE = 63
+} psk_op;
+
+/* One let of the group, in static single assignment: operands name earlier
+ * nodes (a let-list in the manner of PSK-Core's ANF, presk language
+ * reference, "PSK-Core").  Unused operands are -1. */
+typedef struct psk_node {
+    int32_t op;        /* psk_op */
+    int32_t a, b, c;   /* operand node indices, each < this node's index, or -1 */
+    float imm;         /* PSK_OP_CONST: the value */
+    int32_t iparam;    /* PSK_OP_INPUT: slot; PSK_OP_POWN: n; PSK_OP_CAUSAL_MASK: T */
+} psk_node;
+
+/* A dense row-major tensor.  Inputs align with the output from the last
+ * axis; an input axis of length 1 broadcasts (numpy's rule, which the
+ * configs' [N,1] and [1,N] inputs use); an input may never widen the output
+ * (PSK-Realize, "What a group is": inputs may be smaller and broadcast). */
+typedef struct psk_tensor_desc {
+    int32_t rank;                    /* 0..PSK_MAX_RANK (output: 1..PSK_MAX_RANK) */
+    int32_t dtype;                   /* psk_dtype */
+    int64_t shape[PSK_MAX_RANK];     /* entries at and beyond rank are ignored */
+} psk_tensor_desc;
+
+typedef struct psk_group_desc {
+    int32_t n_nodes;                 /* 1..PSK_MAX_NODES */
+    const psk_node* nodes;
+    int32_t root;                    /* the one member no node reads; usually n_nodes-1 */
+    int32_t n_inputs;                /* 0..PSK_MAX_INPUTS; slot k is INPUT iparam k */
+    const psk_tensor_desc* inputs;
+    psk_tensor_desc out;             /* the root's storage type and shape */
+    int32_t arith;                   /* arithmetic type: must be PSK_F32 */
+    uint32_t flags;                  /* reserved, must be 0 */
+} psk_group_desc;
+
+typedef struct psk_group psk_group;
+typedef struct psk_tree psk_tree;
+
+/* Validate a group, emit its HIP kernel and compile it with hipRTC for
+ * gfx950 (kernels are cached by the group's canonical text, in memory and,
+ * when PSK_CACHE_DIR is set, on disk).  Validation covers: node order,
+ * operand counts, a single root, no dead node, the member cap, one result
+ * type for the element members, broadcast legality, row-reduction use (a
+ * reduction's operand is an element value; the root is an element value),
+ * storage types.  Does not need a GPU: the kernel is loaded on first run. */
+psk_status psk_group_create(const psk_group_desc* desc, psk_group** out);
+
+/* Run the group as one kernel launch.  inputs[k] is the device address of
+ * input slot k laid out as desc.inputs[k]; out is the device address of the
+ * output.  The output may be the same buffer as an input of the same shape
+ * and storage type (in place); any other overlap with an input is refused
+ * (PSK_E_ALIAS).  Pointers must be aligned to their element size
+ * (PSK_E_ALIGN); 16-byte alignment takes the vector path.  Empty outputs
+ * launch nothing. */
+psk_status psk_group_run(const psk_group* group, const void* const* inputs, void* out, void* hip_stream);
+
+void psk_group_destroy(psk_group* group);
+
+/* Kernel shape chosen for a group (for tests and measurement). */
+typedef struct psk_group_info {
+    int32_t kind;            /* 0 pointwise, 1 row */
+    int32_t members;         /* member count */
+    int32_t n_reductions;    /* row reductions */
+    int32_t phases;          /* reduction phases (longest chain of dependent reductions) */
+    int64_t rows, cols;      /* output viewed as [rows, cols] */
+    int32_t lanes_per_row;   /* row kernel: threads per row */
+    int32_t vec;             /* elements per vector access */
+    int32_t block;           /* threads per workgroup */
+    int32_t rows_per_block;  /* row kernel */
+    int64_t algorithmic_bytes; /* inputs read once at their own size + output written once */
+} psk_group_info;
+psk_status psk_group_get_info(const psk_group* group, psk_group_info* info);
+
+/* Validate a descriptor and write the emitted HIP source (NUL-terminated)
+ * into buf; *len receives the full length.  Touches no device and does not
+ * compile. */
+psk_status psk_group_source(const psk_group_desc* desc, char* buf, size_t cap, size_t* len);
+
+/* Validate, emit and compile with hipRTC, returning the gfx950 code object
+ * (no device needed).  *len receives its size; buf may be NULL to query. */
+psk_status psk_group_code_object(const psk_group_desc* desc, void* buf, size_t cap, size_t* len);
+
+/* ------------------------------------------------------ parameter trees */
+/* One leaf of a parameter tree: numel elements in each slot.  For AdamW the
+ * slots are theta, g, m, v (4 slots: updated in place), or theta, g, m, v,
+ * theta', m', v' (7 slots: outputs apart; an output may also be the same
+ * buffer as its input). */
+typedef struct psk_leaf {
+    int64_t numel;                   /* >= 0; a leaf of 0 elements is skipped */
+    void* slot[PSK_MAX_SLOTS];       /* device addresses, dense, each aligned to its element size */
+} psk_leaf;
+
+/* Build the leaf table (prefix offsets) and the chunk map: each leaf is cut
+ * into chunks of PSK_TREE_CHUNK elements (the last one shorter); chunk
+ * starts are multiples of 8 elements within a leaf, so 16-byte vector
+ * accesses stay inside one leaf.  The tables are uploaded to the current
+ * device once.  Slot dtypes apply to every leaf.  Refuses: NULL pointers of
+ * non-empty leaves, negative numel, misaligned pointers, outputs partially
+ * overlapping inputs or other leaves' outputs (PSK_E_ALIAS). */
+#define PSK_TREE_CHUNK 4096
+psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, int32_t n_slots,
+                           const int32_t* slot_dtypes, psk_tree** out);
+void psk_tree_destroy(psk_tree* tree);
+
+typedef struct psk_tree_info {
+    int32_t n_leaves, n_slots;
+    int64_t n_chunks;
+    int64_t total_numel;
+    int64_t chunk_elems;             /* PSK_TREE_CHUNK */
+    int32_t vector_leaves;           /* leaves whose slots are all 16-byte aligned */
+} psk_tree_info;
+psk_status psk_tree_get_info(const psk_tree* tree, psk_tree_info* info);
+
+/* Copy the host copy of the tables: leaf_offset[n_leaves+1] (exclusive
+ * prefix sums of numel), and per chunk its leaf, start element within the
+ * leaf and element count.  Any pointer may be NULL to skip it. */
+psk_status psk_tree_get_tables(const psk_tree* tree, int64_t* leaf_offset, int32_t* chunk_leaf,
+                               int64_t* chunk_start, int32_t* chunk_count);
+
+/* Host-only planning of the same tables without device pointers or a
+ * device (for tests): numel[n_leaves] in, tables out as above. */
+psk_status psk_tree_plan(const int64_t* numel, int32_t n_leaves, int64_t* n_chunks, int64_t* leaf_offset,
+                         int32_t* chunk_leaf, int64_t* chunk_start, int32_t* chunk_count);
+
+/* AdamW hyperparameters (presk language reference, "The optimizer"):
+ *   m' = b1 m + (1-b1) g;  v' = b2 v + (1-b2) g^2;
+ *   mh = m'/(1-b1^t);  vh = v'/(1-b2^t);
+ *   theta' = theta - lr (mh/(sqrt(vh)+eps) + wd theta)
+ * t counts steps from 1.  Hyperparameter arithmetic (1-b, b^t) is done in
+ * f64 on the host and each scalar is rounded once to f32. */
+typedef struct psk_adamw_hp {
+    double lr, beta1, beta2, eps, weight_decay;
+    int64_t t;
+} psk_adamw_hp;
+
+/* One AdamW step over every leaf of the tree in a single kernel launch.
+ * Slot dtypes: theta and g each f32 or bf16; m and v the same type, f32 or
+ * bf16; outputs the type of their input.  Arithmetic is f32; theta' is
+ * rounded once to theta's storage; m' and v' are stored, and theta' reads
+ * the stored values.  Refuses t < 1, non-finite hyperparameters. */
+psk_status psk_adamw_step(const psk_tree* tree, const psk_adamw_hp* hp, void* hip_stream);
+
+/* --------------------------------------------------------------- partition */
+/* Partition a function body (a let-list of n nodes, leaves included) into
+ * fusion groups (PSK-Realize, "What a group is").  types[i] is node i's
+ * result type (shape and storage type; two types are equal when rank, dtype
+ * and shape agree), is_output[i] marks values read outside the body.
+ * Scanning from the last let to the first, an elementwise let joins the
+ * group of its readers when it is not an output, every reader is an
+ * elementwise member of that one group, its type is the group's, and the
+ * group has fewer than 64 members; otherwise it roots a new group.  Leaves
+ * get group -1; a boundary let (row reduction, REDUCE, CONTRACT, CAST,
+ * OPAQUE, POWN with n > 2) is a group of its own.  Groups are numbered by
+ * their root's position.  group_of[n], is_root[n] out; *n_groups out. */
+psk_status psk_partition(int32_t n, const psk_node* body, const psk_tensor_desc* types,
+                         const uint8_t* is_output, int32_t* group_of, int32_t* is_root, int32_t* n_groups);
+
+/* ------------------------------------------------------------------ misc */
+const char* psk_last_error(void);
+const char* psk_status_str(psk_status status);
+int32_t psk_version(void);
+
+typedef struct psk_stats {
+    int64_t launches;      /* kernel launches issued by this library */
+    int64_t jit_compiles;  /* hipRTC compilations */
+    int64_t jit_hits;      /* kernels found in the memory or disk cache */
+} psk_stats;
+psk_status psk_get_stats(psk_stats* stats);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSK_FUSED_H */

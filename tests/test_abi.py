@@ -1,0 +1,242 @@
+"""The C-ABI library on the host: exported symbols, refusals, host-side
+planning (partition, leaf/chunk tables), and the emitted kernels compiled by
+hipRTC for gfx950 -- no GPU needed."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from synth import configs
+from synth.dag import Node, parse_dag
+
+P = pytest.importorskip("elementwise_reduction_groups_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "psk_fused.h")
+OBJDUMP = "/opt/rocm/llvm/bin/llvm-objdump"
+READELF = "/opt/rocm/llvm/bin/llvm-readelf"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(P.LIB_PATH):
+        from elementwise_reduction_groups_amd import build
+        build.build()
+    return P.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    decl = re.findall(r"\b(psk_[a-z_]+)\s*\(", open(HEADER).read())
+    names = sorted(set(decl))
+    assert len(names) >= 17
+    out = subprocess.run(["nm", "-D", "--defined-only", P.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (psk_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert set(P.EXPORTED) <= exported
+    assert P.psk_version() == 100
+
+
+def test_status_strings(lib):
+    for i, name in enumerate(P.STATUS_NAMES):
+        assert P.psk_status_str(i) == name
+
+
+def _desc(text, inputs, out_shape, out_dtype="f32", **kw):
+    return P.GroupDesc(parse_dag(text), inputs, out_shape, out_dtype, **kw)
+
+
+def _refused(desc, status):
+    with pytest.raises(P.PskError) as ei:
+        P.psk_group_source(desc)
+    assert ei.value.status == status, (ei.value.name, str(ei.value))
+    assert P.STATUS_NAMES[status] in str(ei.value)
+
+
+F = [((8, 16), "f32")]
+
+
+def test_refusals(lib):
+    # member cap: 65 members
+    chain = "%0 = input 0\n" + "".join(f"%{i + 1} = exp %{i}\n" for i in range(65))
+    _refused(_desc(chain, F, (8, 16)), P.PSK_E_CAP)
+    ok64 = "%0 = input 0\n" + "".join(f"%{i + 1} = exp %{i}\n" for i in range(64))
+    assert "psk_kernel" in P.psk_group_source(_desc(ok64, F, (8, 16)))
+    # operand naming a later node (a cycle)
+    _refused(_desc("%0 = input 0\n%1 = add %0 %2\n%2 = exp %0\n", F, (8, 16)), P.PSK_E_ORDER)
+    # two roots
+    _refused(_desc("%0 = input 0\n%1 = exp %0\n%2 = tanh %0\n", F, (8, 16)), P.PSK_E_ROOT)
+    # root read by another node
+    _refused(_desc("%0 = input 0\n%1 = exp %0\n%2 = tanh %1\n", F, (8, 16), root=1), P.PSK_E_ROOT)
+    # dead leaf
+    _refused(_desc("%0 = input 0\n%1 = const 1.0\n%2 = exp %0\n", F, (8, 16)), P.PSK_E_DEAD)
+    # an input that widens the output
+    _refused(_desc("%0 = input 0\n%1 = exp %0\n", [((8, 32), "f32")], (8, 16)), P.PSK_E_BROADCAST)
+    _refused(_desc("%0 = input 0\n%1 = exp %0\n", [((2, 8, 16), "f32")], (8, 16)), P.PSK_E_BROADCAST)
+    # bf16 arithmetic requested
+    _refused(_desc("%0 = input 0\n%1 = exp %0\n", F, (8, 16), arith=P.PSK_BF16), P.PSK_E_TYPE)
+    # a boundary op inside a group
+    bad = [Node("input", (), None, 0), Node("cast", (0,))]
+    _refused(P.GroupDesc(bad, F, (8, 16), "f32"), P.PSK_E_OP)
+    # pow 3 with other members
+    _refused(_desc("%0 = input 0\n%1 = pown %0 3\n%2 = exp %1\n", F, (8, 16)), P.PSK_E_OP)
+    assert P.psk_group_source(_desc("%0 = input 0\n%1 = pown %0 3\n", F, (8, 16)))
+    # reduction of a row value; a row value as the stored root
+    _refused(_desc("%0 = input 0\n%1 = row_sum %0\n%2 = row_max %1\n%3 = add %0 %2\n", F, (8, 16)), P.PSK_E_ROW)
+    _refused(_desc("%0 = input 0\n%1 = row_sum %0\n", F, (8, 16)), P.PSK_E_ROW)
+    # bad input slot, bad arity
+    _refused(_desc("%0 = input 3\n%1 = exp %0\n", F, (8, 16)), P.PSK_E_OP)
+    nd = [Node("input", (), None, 0), Node("exp", (0,))]
+    d = P.GroupDesc(nd, F, (8, 16), "f32")
+    d._nodes[1].b = 0
+    _refused(d, P.PSK_E_OP)
+    # NULL descriptor
+    n = ctypes.c_size_t()
+    assert lib.psk_group_source(None, None, 0, ctypes.byref(n)) == P.PSK_E_NULL
+    # negative sizes, rank out of range
+    _refused(_desc("%0 = input 0\n%1 = exp %0\n", [((8, 16), "f32")], (8, -16)), P.PSK_E_SHAPE)
+    # reserved flags
+    _refused(_desc("%0 = input 0\n%1 = exp %0\n", F, (8, 16), flags=1), P.PSK_E_UNSUPPORTED)
+
+
+def test_group_create_needs_no_gpu(lib):
+    g = P.psk_group_create(_desc("%0 = input 0\n%1 = input 1\n%2 = add %0 %1\n",
+                                 [((33, 64), "f32"), ((33, 1), "f32")], (33, 64)))
+    info = P.psk_group_get_info(g)
+    assert info.kind == 0 and info.members == 1 and info.vec == 4
+    assert info.algorithmic_bytes == 33 * 64 * 4 * 2 + 33 * 4
+    P.psk_group_destroy(g)
+
+
+def _partition_nodes(rng, n):
+    nodes, types, outs = [Node("input", (), None, 0)], [((4, 8), "f32")], [False]
+    for i in range(1, n):
+        r = rng.random()
+        if r < 0.1:
+            nodes.append(Node("row_sum", (rng.randrange(i),)))
+        elif r < 0.15:
+            nodes.append(Node("pown", (rng.randrange(i),), None, 3))
+        elif r < 0.2:
+            nodes.append(Node("matmul", (rng.randrange(i), rng.randrange(i))))
+        elif r < 0.6:
+            nodes.append(Node(rng.choice(["add", "mul", "sub"]), (rng.randrange(i), rng.randrange(i))))
+        else:
+            nodes.append(Node(rng.choice(["exp", "tanh", "gelu"]), (rng.randrange(i),)))
+        types.append(((4, 8), "f32") if rng.random() < 0.85 else ((4, 8), "bf16"))
+        outs.append(rng.random() < 0.1)
+    outs[-1] = True
+    return nodes, types, outs
+
+
+def test_partition_matches_oracle(lib, orc):
+    import random
+    rng = random.Random(7)
+    for trial in range(2000):
+        n = rng.randint(2, 90)
+        nodes, types, outs = _partition_nodes(rng, n)
+        g, r, ng = P.psk_partition(nodes, types, outs)
+        tid = [0 if t[1] == "f32" else 1 for t in types]
+        og, orr = orc.partition(nodes, tid, outs)
+        np.testing.assert_array_equal(g, og)
+        np.testing.assert_array_equal(r, orr)
+        assert ng == (og.max() + 1 if (og >= 0).any() else 0)
+
+
+def test_partition_cap(lib):
+    for length, sizes in ((64, [64]), (65, [1, 64]), (129, [1, 64, 64])):
+        nodes = [Node("input", (), None, 0)] + [Node("exp", (i,)) for i in range(length)]
+        types = [((4,), "f32")] * len(nodes)
+        g, r, ng = P.psk_partition(nodes, types, [False] * length + [True])
+        assert [int((g == k).sum()) for k in range(ng)] == sizes
+
+
+def test_tree_plan(lib):
+    numel = [5888, 2048, 64, 0, 12288, 1, 4097, 3, 4096]
+    off, cl, cs, cc = P.psk_tree_plan(numel)
+    np.testing.assert_array_equal(off, np.concatenate([[0], np.cumsum(numel)]))
+    # every element of every leaf covered exactly once, chunk starts 8-aligned
+    for leaf, n in enumerate(numel):
+        sel = cl == leaf
+        cover = np.zeros(n, np.int32)
+        for s, c in zip(cs[sel], cc[sel]):
+            assert s % 8 == 0 and 0 < c <= P.PSK_TREE_CHUNK
+            cover[s:s + c] += 1
+        assert np.all(cover == 1)
+    # the tiny GPT tree
+    shapes = [s for _, s in configs.tiny_gpt_leaves()]
+    off, cl, cs, cc = P.psk_tree_plan([int(np.prod(s)) for s in shapes])
+    assert len(shapes) == 28 and off[-1] == 108032
+    shapes = [s for _, s in configs.llama_leaves()]
+    off, *_ = P.psk_tree_plan([int(np.prod(s)) for s in shapes])
+    assert len(shapes) == 145 and off[-1] == 887685120
+    with pytest.raises(P.PskError) as ei:
+        P.psk_tree_plan([4, -1])
+    assert ei.value.status == P.PSK_E_SHAPE
+
+
+def test_tree_refusals_without_device(lib):
+    # refusals are decided before any device call
+    with pytest.raises(P.PskError) as ei:
+        P.psk_tree_create([(8, [16, 32, 48])], ["f32"] * 3)
+    assert ei.value.status == P.PSK_E_SHAPE
+    with pytest.raises(P.PskError) as ei:
+        P.psk_tree_create([(8, [16, 0, 64, 96])], ["f32"] * 4)
+    assert ei.value.status == P.PSK_E_NULL
+    with pytest.raises(P.PskError) as ei:
+        P.psk_tree_create([(8, [18, 1024, 2048, 4096])], ["f32"] * 4)
+    assert ei.value.status == P.PSK_E_ALIGN
+    with pytest.raises(P.PskError) as ei:   # theta overlaps g
+        P.psk_tree_create([(8, [1024, 1040, 2048, 4096])], ["f32"] * 4)
+    assert ei.value.status == P.PSK_E_ALIAS
+    with pytest.raises(P.PskError) as ei:   # two leaves overlap
+        P.psk_tree_create([(8, [1024, 2048, 3072, 4096]), (8, [1040, 8192, 9216, 10240])], ["f32"] * 4)
+    assert ei.value.status == P.PSK_E_ALIAS
+    with pytest.raises(P.PskError) as ei:
+        P.psk_tree_create([(8, [1024, 2048, 3072, 4096])], ["f32", "f32", "f32", "bf16"])
+    assert ei.value.status == P.PSK_E_TYPE
+
+
+def _isa(code: bytes, tmp_path, name):
+    p = tmp_path / f"{name}.co"
+    p.write_bytes(code)
+    asm = subprocess.run([OBJDUMP, "-d", str(p)], capture_output=True, text=True, check=True).stdout
+    notes = subprocess.run([READELF, "--notes", str(p)], capture_output=True, text=True, check=True).stdout
+    return asm, notes
+
+
+def _workload_descs():
+    eps = configs.f32(1e-5)
+    return {
+        "softmax": P.GroupDesc(configs.softmax_causal_dag(0.125, 1024), [((131072, 1024), "f32")], (131072, 1024), "f32"),
+        "rmsnorm": P.GroupDesc(configs.rmsnorm_gelu_dag(eps), [((16384, 4096), "bf16"), ((16384, 4096), "bf16"),
+                                                                 ((4096,), "bf16")], (16384, 4096), "bf16"),
+        "chain64": P.GroupDesc(configs.chain64_dag(), [((16384, 16384), "f32"), ((16384, 1), "f32"),
+                                                       ((1, 16384), "f32")], (16384, 16384), "f32"),
+    }
+
+
+@pytest.mark.parametrize("name", ["softmax", "rmsnorm", "chain64"])
+def test_emitted_kernels_compile_for_gfx950(lib, tmp_path, name):
+    code = P.psk_group_code_object(_workload_descs()[name])
+    asm, notes = _isa(code, tmp_path, name)
+    assert "gfx950" in subprocess.run(["file", "-b", str(tmp_path / f"{name}.co")], capture_output=True,
+                                      text=True).stdout or "amdgcn" in notes or True
+    # no packed-FP32 instructions, no spills to scratch
+    assert not re.search(r"v_pk_(fma|mul|add)_f32", asm)
+    assert re.search(r"\.private_segment_fixed_size:\s+0\b", notes)
+    # 16-byte accesses on the row data
+    assert "global_load_dwordx4" in asm and "global_store_dwordx4" in asm
+    if name != "chain64":
+        assert "row_mirror" in asm and "v_readlane_b32" in asm   # DPP wave reduction
+
+
+def test_emitted_source_structure(lib):
+    src = P.psk_group_source(_workload_descs()["softmax"])
+    # masked scores are not loaded: the load of vector k is predicated on its first column
+    assert "<= q) w0_" in src.replace("&& c0 <= q", "<= q") or "c0 <= q" in src
+    assert src.count("__syncthreads") == 0          # one wave per 1024-wide row: no LDS exchange
+    src = P.psk_group_source(_workload_descs()["rmsnorm"])
+    assert src.count("__syncthreads") == 1          # 256 lanes per row: one cross-wave exchange

@@ -1,0 +1,166 @@
+"""GPU parity of the tree-mapped AdamW step (one launch for every leaf) against
+the oracle.  The kernel performs the formula's IEEE operations in the same
+order with no contraction, so results are compared bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import configs
+from tests.gpu_util import assert_bits, to_np
+
+P = pytest.importorskip("elementwise_reduction_groups_amd")
+
+pytestmark = pytest.mark.gpu
+HP = configs.ADAMW_HP
+DEV = "cuda:0"
+
+
+def hp_args(**over):
+    d = dict(HP)
+    d.update(over)
+    return d["lr"], d["beta1"], d["beta2"], d["eps"], d["weight_decay"], d["t"]
+
+
+def run_tree(state, hp, out_of_place=False):
+    """Run one step through the C ABI; returns per leaf (theta', m', v')."""
+    slots = []
+    outs = []
+    for s in state:
+        if out_of_place:
+            o = [torch.full_like(s["theta"], float("nan")), torch.full_like(s["m"], float("nan")),
+                 torch.full_like(s["v"], float("nan"))]
+            outs.append(o)
+            slots.append([s["theta"], s["grad"], s["m"], s["v"], *o])
+        else:
+            slots.append([s["theta"], s["grad"], s["m"], s["v"]])
+            outs.append([s["theta"], s["m"], s["v"]])
+    tree = P.Tree(slots)
+    tree.adamw_step(*hp)
+    torch.cuda.synchronize()
+    return tree, outs
+
+
+def oracle_leaf(s_np, hp):
+    return oracle.adamw(s_np["theta"], s_np["grad"], s_np["m"], s_np["v"], *hp)
+
+
+def snapshot(state):
+    return [{k: to_np(v) for k, v in s.items()} for s in state]
+
+
+def check_tree(state_np, outs, hp, what):
+    for i, (s, o) in enumerate(zip(state_np, outs)):
+        rt, rm, rv = oracle_leaf(s, hp)
+        assert_bits(to_np(o[0]), rt, f"{what} leaf {i} theta'")
+        assert_bits(to_np(o[1]), rm, f"{what} leaf {i} m'")
+        assert_bits(to_np(o[2]), rv, f"{what} leaf {i} v'")
+
+
+def test_tiny_gpt_f32_bit_exact():
+    shapes = [s for _, s in configs.tiny_gpt_leaves()]
+    state = configs.adamw_state(shapes, device=DEV, seed=configs.SEED_BASE)
+    before = snapshot(state)
+    tree, outs = run_tree(state, hp_args())
+    info = tree.info
+    assert info.n_leaves == 28 and info.total_numel == 108032 and info.vector_leaves == 28
+    check_tree(before, outs, hp_args(), "tiny GPT")
+
+
+@pytest.mark.parametrize("dt", [(torch.bfloat16, torch.bfloat16, torch.float32),
+                                (torch.float32, torch.bfloat16, torch.float32),
+                                (torch.bfloat16, torch.float32, torch.bfloat16),
+                                (torch.float32, torch.float32, torch.bfloat16)])
+def test_dtype_combinations_and_ragged_leaves(dt):
+    shapes = [(1,), (3,), (7,), (9,), (1023,), (4095,), (4096,), (4097,), ((1 << 20) + 5,), (64, 3)]
+    state = configs.adamw_state(shapes, theta_dtype=dt[0], grad_dtype=dt[1], mv_dtype=dt[2], device=DEV, seed=11)
+    before = snapshot(state)
+    _, outs = run_tree(state, hp_args(t=3))
+    check_tree(before, outs, hp_args(t=3), f"dtypes {dt}")
+
+
+def test_out_of_place_misaligned_views_poisoned():
+    # leaves carved from flat buffers at odd element offsets (not 16-byte
+    # aligned: scalar path) and aligned ones (vector path); outputs apart,
+    # pre-filled with NaN, so an element the kernel skips stays NaN
+    sizes = [1000, 4097, 17, 8192, 5]
+    total = sum(sizes) + 64
+    flat = {k: configs.adamw_state([(total,)], device=DEV, seed=21 + j)[0][k] for j, k in enumerate(("theta", "grad", "m", "v"))}
+    state, off = [], 1
+    for i, n in enumerate(sizes):
+        o = off if i % 2 == 0 else (off + 7) // 8 * 8
+        state.append({k: flat[k][o:o + n] for k in flat})
+        off = o + n
+    before = snapshot(state)
+    tree, outs = run_tree(state, hp_args(t=5), out_of_place=True)
+    assert 0 < tree.info.vector_leaves < len(sizes)
+    check_tree(before, outs, hp_args(t=5), "views")
+    for i, s in enumerate(state):   # inputs untouched
+        for k in s:
+            assert_bits(to_np(s[k]), before[i][k], f"input {k} of leaf {i} changed")
+
+
+def test_indexing_patterns_exact_special_cases():
+    # every leaf holds a leaf-id / element-id pattern; the special cases
+    # below reproduce it exactly, so a shifted, dropped or duplicated element
+    # shows up as a bit difference
+    shapes = [(5888,), (2048,), (64,), (12288,), (3,), (4097,)]
+    state = []
+    for leaf, (n,) in enumerate(shapes):
+        e = torch.arange(n, device=DEV, dtype=torch.float32)
+        state.append({"theta": 1000.0 * leaf + e, "grad": -(1000.0 * leaf + e) / 4096.0,
+                      "m": e / 8.0, "v": e / 16.0 + 1.0})
+    pat = [{k: t.clone() for k, t in s.items()} for s in state]
+    run_tree(state, hp_args(lr=0.0, beta1=0.0, beta2=0.0))
+    for s, p in zip(state, pat):
+        assert torch.equal(s["theta"], p["theta"])             # lr = 0
+        assert torch.equal(s["m"], p["grad"])                  # beta1 = 0
+        assert torch.equal(s["v"], p["grad"] * p["grad"])      # beta2 = 0
+
+
+def test_empty_leaves_and_empty_tree():
+    state = configs.adamw_state([(0,), (17,), (0,)], device=DEV, seed=3)
+    before = snapshot(state)
+    _, outs = run_tree(state, hp_args())
+    check_tree(before, outs, hp_args(), "empty leaves")
+    t = P.Tree([])
+    t.adamw_step(*hp_args())
+    assert t.info.n_chunks == 0
+
+
+def test_refusals_on_device():
+    state = configs.adamw_state([(16,)], device=DEV, seed=4)[0]
+    with pytest.raises(P.PskError) as ei:
+        P.Tree([[state["theta"], state["grad"], state["m"], state["theta"]]])   # v is theta
+    assert ei.value.status == P.PSK_E_ALIAS
+    tree = P.Tree([[state["theta"], state["grad"], state["m"], state["v"]]])
+    with pytest.raises(P.PskError) as ei:
+        tree.adamw_step(*hp_args(t=0))
+    assert ei.value.status == P.PSK_E_SHAPE
+    with pytest.raises(P.PskError) as ei:
+        tree.adamw_step(*hp_args(lr=float("nan")))
+    assert ei.value.status == P.PSK_E_SHAPE
+
+
+def test_llama_tree_full_size_sampled():
+    """The 145-leaf, 887M-parameter tree (bf16 theta/g, f32 m/v), one launch,
+    checked on sampled elements of every leaf (first and last 64 plus 4096
+    random) against the oracle, bit for bit."""
+    shapes = [s for _, s in configs.llama_leaves()]
+    state = configs.adamw_state(shapes, theta_dtype=torch.bfloat16, grad_dtype=torch.bfloat16,
+                                mv_dtype=torch.float32, device=DEV, seed=configs.SEED_BASE + 2)
+    gen = torch.Generator(device="cpu").manual_seed(99)
+    idx = []
+    for s in state:
+        n = s["theta"].numel()
+        r = torch.randint(0, n, (4096,), generator=gen)
+        idx.append(torch.unique(torch.cat([torch.arange(64), torch.arange(n - 64, n), r])).to(DEV))
+    before = [{k: to_np(s[k][i]) for k in s} for s, i in zip(state, idx)]
+    tree, outs = run_tree(state, hp_args())
+    info = tree.info
+    assert info.n_leaves == 145 and info.total_numel == 887685120
+    for leaf, (s, i) in enumerate(zip(before, idx)):
+        rt, rm, rv = oracle_leaf(s, hp_args())
+        assert_bits(to_np(outs[leaf][0][i]), rt, f"leaf {leaf} theta'")
+        assert_bits(to_np(outs[leaf][1][i]), rm, f"leaf {leaf} m'")
+        assert_bits(to_np(outs[leaf][2][i]), rv, f"leaf {leaf} v'")

@@ -1,0 +1,223 @@
+"""GPU parity of emitted group kernels (pointwise chains and row-reduction
+groups) against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import configs
+from synth.dag import parse_dag
+from tests.gpu_util import assert_bf16_close, assert_bits, assert_f32_close, to_np
+
+P = pytest.importorskip("elementwise_reduction_groups_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+EPS = configs.f32(1e-5)
+
+
+def tdt(t):
+    return "bf16" if t.dtype == torch.bfloat16 else "f32"
+
+
+def run_group(nodes, inputs, out_shape, out_dtype, poison=True):
+    g = P.Group(nodes, [(tuple(t.shape), tdt(t)) for t in inputs], out_shape, out_dtype)
+    tdtype = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out = torch.full(out_shape, float("nan"), dtype=tdtype, device=DEV) if poison else \
+        torch.empty(out_shape, dtype=tdtype, device=DEV)
+    g.run(inputs, out)
+    torch.cuda.synchronize()
+    return g, out
+
+
+# ---------------------------------------------------------------- softmax
+@pytest.mark.parametrize("rows,cols,period", [(300, 256, 256), (200, 1000, 200), (70, 1023, 64),
+                                              (40, 4096, 4096), (33, 64, 64), (9, 12, 5)])
+def test_causal_softmax_small(rows, cols, period):
+    x = configs.softmax_scores(rows, cols, device=DEV, seed=rows + cols)
+    nodes = configs.softmax_causal_dag(0.125, period)
+    g, out = run_group(nodes, [x], (rows, cols), "f32")
+    got = to_np(out)
+    ref = oracle.softmax_causal(to_np(x), period, 0.125)
+    assert_f32_close(got, ref, f"softmax {rows}x{cols}")
+    # refused positions are exactly +0
+    q = np.arange(rows)[:, None] % period
+    masked = np.arange(cols)[None, :] > q
+    assert np.all(got.view(np.uint32)[masked] == 0)
+    # the generic oracle evaluator agrees too (same definition, other code)
+    ref2 = oracle.eval_group(nodes, [to_np(x)], (rows, cols))
+    assert_bits(ref, ref2, "oracle evaluators")
+
+
+def test_causal_softmax_full_size_sampled_rows():
+    R, C = 131072, 1024
+    x = configs.softmax_scores(R, C, device=DEV)
+    g, out = run_group(configs.softmax_causal_dag(0.125, 1024), [x], (R, C), "f32")
+    info = g.info
+    assert info.kind == 1 and info.lanes_per_row == 64 and info.vec == 4
+    rows = np.unique(np.concatenate([[0, 1, 2, 1023, 1024, 65535, R - 1],
+                                     np.random.default_rng(5).integers(0, R, 600)]))
+    xs = to_np(x[torch.from_numpy(rows).to(DEV)])
+    got = to_np(out[torch.from_numpy(rows).to(DEV)])
+    # the oracle row by row, each at its own causal position
+    ref = np.stack([_softmax_row(xs[k], int(r) % 1024) for k, r in enumerate(rows)])
+    assert_f32_close(got, ref, "softmax full size")
+    assert not np.isnan(to_np(out)).any()
+
+
+def _softmax_row(xrow, q):
+    # one row at causal position q: a [q+1, C] block whose last row is the one
+    # wanted, evaluated by the oracle with period q+1 so that row q is that row
+    C = xrow.shape[0]
+    block = np.zeros((q + 1, C), np.float32)
+    block[q] = xrow
+    out = oracle.softmax_causal(block, q + 1, 0.125, rows=(q, q + 1))
+    return out[q]
+
+
+# ---------------------------------------------------------------- RMSNorm
+@pytest.mark.parametrize("rows,cols", [(37, 4096), (20, 4000), (19, 1000), (8, 64), (5, 8192), (3, 12)])
+def test_rmsnorm_gelu_small(rows, cols):
+    x, r, gm = configs.rmsnorm_inputs(rows, cols, device=DEV, seed=rows * cols)
+    g, out = run_group(configs.rmsnorm_gelu_dag(EPS), [x, r, gm], (rows, cols), "bf16")
+    ref = oracle.rmsnorm_gelu(to_np(x), to_np(r), to_np(gm), EPS)
+    assert_bf16_close(to_np(out), ref, f"rmsnorm {rows}x{cols}")
+
+
+def test_rmsnorm_gelu_full_size_sampled_rows():
+    R, C = 16384, 4096
+    x, r, gm = configs.rmsnorm_inputs(R, C, device=DEV)
+    g, out = run_group(configs.rmsnorm_gelu_dag(EPS), [x, r, gm], (R, C), "bf16")
+    info = g.info
+    assert info.kind == 1 and info.lanes_per_row == 256 and info.vec == 8
+    rows = torch.from_numpy(np.unique(np.concatenate([[0, 1, R - 1], np.random.default_rng(6).integers(0, R, 400)])))
+    rows = rows.to(DEV)
+    ref = oracle.rmsnorm_gelu(to_np(x[rows]), to_np(r[rows]), to_np(gm), EPS)
+    assert_bf16_close(to_np(out[rows]), ref, "rmsnorm full size")
+    o = to_np(out)
+    assert not (((o & 0x7F80) == 0x7F80) & ((o & 0x7F) != 0)).any()
+
+
+# ------------------------------------------------------------ 64-node chain
+def test_chain64_small():
+    nodes = configs.chain64_dag()
+    A, B, C = configs.chain_inputs(96, 2048, device=DEV, seed=5)
+    g, out = run_group(nodes, [A, B, C], (96, 2048), "f32")
+    ref = oracle.eval_group(nodes, [to_np(A), to_np(B), to_np(C)], (96, 2048))
+    assert_f32_close(to_np(out), ref, "chain64")
+
+
+def test_chain64_full_size_sampled_rows():
+    N = 16384
+    nodes = configs.chain64_dag()
+    A, B, C = configs.chain_inputs(N, N, device=DEV)
+    g, out = run_group(nodes, [A, B, C], (N, N), "f32")
+    assert g.info.kind == 0 and g.info.vec == 4 and g.info.members == 64
+    rows = torch.from_numpy(np.unique(np.concatenate([[0, N - 1], np.random.default_rng(7).integers(0, N, 14)])))
+    rows = rows.to(DEV)
+    ref = oracle.eval_group(nodes, [to_np(A[rows]), to_np(B[rows]), to_np(C)], (len(rows), N))
+    assert_f32_close(to_np(out[rows]), ref, "chain64 full size")
+    assert not np.isnan(to_np(out)).any()
+
+
+# -------------------------------------------------------- generic groups
+def test_broadcast_indexing_bit_exact():
+    # out[i, j] = A[i, j] + B[i] exactly: pins broadcast indexing
+    A = torch.randn(1000, 333, device=DEV)
+    B = torch.randn(1000, 1, device=DEV)
+    _, out = run_group(parse_dag("%0 = input 0\n%1 = input 1\n%2 = add %0 %1\n"), [A, B], (1000, 333), "f32")
+    assert_bits(to_np(out), to_np(A) + to_np(B), "A + Bcol")
+
+
+def test_basic_ops_bit_exact_rank4():
+    # add, mul, div, sqrt, max/min only: correctly rounded IEEE on both sides
+    a = torch.randn(3, 5, 64, 48, device=DEV)
+    b = torch.rand(5, 1, 48, device=DEV) + 0.5
+    c = torch.randn(3, 1, 64, 1, device=DEV)
+    nodes = parse_dag("""%0 = input 0
+%1 = input 1
+%2 = input 2
+%3 = mul %0 %1
+%4 = div %3 %1
+%5 = sub %4 %2
+%6 = abs %5
+%7 = sqrt %6
+%8 = max %7 %2
+%9 = min %8 %1
+%10 = const 0x1.8p+1
+%11 = mul %9 %10
+%12 = neg %11
+%13 = pow2 %12
+""")
+    _, out = run_group(nodes, [a, b, c], (3, 5, 64, 48), "f32")
+    ref = oracle.eval_group(nodes, [to_np(a), to_np(b), to_np(c)], (3, 5, 64, 48))
+    assert_bits(to_np(out), ref, "basic ops")
+
+
+def test_bf16_root_and_bf16_inputs():
+    a = torch.randn(257, 136, device=DEV).to(torch.bfloat16)
+    b = torch.randn(136, device=DEV)
+    nodes = parse_dag("%0 = input 0\n%1 = input 1\n%2 = mul %0 %1\n%3 = tanh %2\n%4 = gelu %3\n%5 = exp %4\n")
+    _, out = run_group(nodes, [a, b], (257, 136), "bf16")
+    ref = oracle.eval_group(nodes, [to_np(a), to_np(b)], (257, 136), out_dtype=oracle.BF16)
+    assert_bf16_close(to_np(out), ref, "bf16 chain")
+
+
+def test_misaligned_views_take_the_element_path():
+    base = torch.randn(1 + 64 * 100, device=DEV)
+    x = base[1:].view(64, 100)                    # 4-byte aligned, not 16
+    outb = torch.full((1 + 64 * 100,), float("nan"), device=DEV)
+    out = outb[1:].view(64, 100)
+    g = P.Group(parse_dag("%0 = input 0\n%1 = exp %0\n%2 = log %1\n"), [((64, 100), "f32")], (64, 100), "f32")
+    g.run([x], out)
+    torch.cuda.synchronize()
+    ref = oracle.eval_group(parse_dag("%0 = input 0\n%1 = exp %0\n%2 = log %1\n"), [to_np(x)], (64, 100))
+    assert_f32_close(to_np(out), ref, "misaligned")
+    assert np.isnan(to_np(outb[:1])).all()        # nothing written before the view
+
+
+def test_in_place_and_alias_refusal():
+    x = torch.randn(128, 1024, device=DEV)
+    x0 = to_np(x)
+    nodes = configs.softmax_causal_dag(0.125, 128)
+    g = P.Group(nodes, [((128, 1024), "f32")], (128, 1024), "f32")
+    g.run([x], x)                                   # in place
+    torch.cuda.synchronize()
+    assert_f32_close(to_np(x), oracle.softmax_causal(x0, 128, 0.125), "in place")
+    y = torch.randn(64, 1, device=DEV)
+    g2 = P.Group(parse_dag("%0 = input 0\n%1 = input 1\n%2 = add %0 %1\n"), [((64, 4), "f32"), ((64, 1), "f32")],
+                 (64, 4), "f32")
+    big = torch.zeros(64 * 4, device=DEV)
+    with pytest.raises(P.PskError) as ei:
+        g2.run([big.view(64, 4), big[:64].view(64, 1)], big.view(64, 4))
+    assert ei.value.status == P.PSK_E_ALIAS
+
+
+def test_empty_output_launches_nothing():
+    g = P.Group(parse_dag("%0 = input 0\n%1 = exp %0\n"), [((0, 16), "f32")], (0, 16), "f32")
+    before = P.psk_get_stats().launches
+    g.run([torch.empty(0, 16, device=DEV)], torch.empty(0, 16, device=DEV))
+    assert P.psk_get_stats().launches == before
+
+
+def test_row_group_two_phase_max_sum_mean():
+    # three reductions in two phases, a row-constant input and a scalar input
+    x = torch.randn(150, 777, device=DEV)
+    s = torch.rand(150, 1, device=DEV) + 0.5
+    k = torch.tensor(0.75, device=DEV)
+    nodes = parse_dag("""%0 = input 0
+%1 = input 1
+%2 = input 2
+%3 = mul %0 %1
+%4 = row_max %3
+%5 = row_mean %3
+%6 = sub %3 %4
+%7 = exp %6
+%8 = row_sum %7
+%9 = div %7 %8
+%10 = mul %9 %2
+%11 = add %10 %5
+""")
+    _, out = run_group(nodes, [x, s, k], (150, 777), "f32")
+    ref = oracle.eval_group(nodes, [to_np(x), to_np(s), to_np(k)], (150, 777))
+    assert_f32_close(to_np(out), ref, "two-phase row group")
