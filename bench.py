@@ -15,7 +15,7 @@ dominant kernel (AdamW), timed with HIP events on the stream it runs on.
 The other three workloads (tiny-GPT AdamW, add+RMSNorm+GELU, 64-node
 chain) are timed one by one with the cache flushed between calls and
 reported under "groups".  The CPU baseline runs the oracle single-threaded
-on a one-eighth sample of the same step.
+on the same step (inputs drawn on the host).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -41,9 +41,11 @@ def parse():
     ap.add_argument("--reps", type=int, default=11, help="calls per workload in the per-group timing")
     ap.add_argument("--no-groups", action="store_true", help="skip the per-group timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=float, default=1.0 / 8, help="fraction of the step the oracle times")
+    ap.add_argument("--cpu-sample", type=float, default=1.0, help="fraction of the step the oracle times")
     ap.add_argument("--profile-step", action="store_true",
                     help="run warmup + K steps only (for rocprofv3 runs), no per-group timing, no CPU leg")
+    ap.add_argument("--pmc-calib", action="store_true",
+                    help="first run one 1 GiB device copy, a known-size reference for the HBM byte counters")
     return ap.parse_args()
 
 
@@ -89,6 +91,14 @@ def main():
     softmax_bytes = allowed * 4 + R * C * 4
     step_bytes = adamw_bytes + softmax_bytes
     torch.cuda.synchronize()
+    if args.pmc_calib:
+        # 2^28 f32 = 1 GiB read and 1 GiB written by one torch copy kernel
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(ev=None):
         if ev is not None:
