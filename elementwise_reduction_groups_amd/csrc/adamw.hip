@@ -3,14 +3,13 @@
 // The optimizer step is one elementwise chain over every parameter (presk
 // manual, "PSK-Realize", section "What a group is", parameter trees; the
 // formula is the presk language reference's, "The optimizer").  Here the
-// chain is mapped over all leaves in a single launch: workgroup b takes chunk
-// b of a device-side chunk table (leaf index, first element, count), reads
-// the leaf's slot addresses from a device-side leaf table, and streams its
-// 4096 elements.  Each thread handles 8 consecutive elements per step with
-// 16-byte accesses (one for 8 bf16, two for 8 f32), two steps per thread,
-// with every load of both steps issued before the arithmetic.  The three
-// results theta', m', v' are stored once each; theta' reads m' and v' as
-// stored (they are outputs), which matters only for bf16 moments.
+// chain is mapped over all leaves in a single launch: a device-side chunk
+// table (leaf index, first element, count; 4096 elements per chunk) is split
+// into 8 workgroups per chunk; a workgroup reads its chunk entry and the
+// leaf's slot addresses from a device-side leaf table and streams 512
+// elements, 4 consecutive ones per thread.  The three results theta', m', v'
+// are stored once each; theta' reads m' and v' as stored (they are outputs),
+// which matters only for bf16 moments.
 //
 // Arithmetic is f32, one rounding per operation in the formula's order: this
 // file is compiled with -ffp-contract=off, correctly rounded division and
@@ -23,13 +22,20 @@
 namespace psk {
 namespace {
 
-constexpr int kBlock = 256;
-constexpr int kPer = 8;                          // elements per thread per step
-constexpr int kSteps = PSK_TREE_CHUNK / (kBlock * kPer);
-static_assert(kSteps * kBlock * kPer == PSK_TREE_CHUNK, "chunk must be a whole number of steps");
+// Launch shape, chosen by measurement on MI355X: small
+// workgroups of 128 threads, 4 elements per thread (8-byte bf16 and 16-byte
+// f32 accesses, one per stream), nontemporal loads and stores (every byte is
+// touched once), and each XCD given one contiguous eighth of the chunks.
+constexpr int kBlock = 128;
+constexpr int kPer = 4;                                   // elements per thread
+constexpr int kSub = PSK_TREE_CHUNK / (kBlock * kPer);   // workgroups per chunk
+static_assert(kSub * kBlock * kPer == PSK_TREE_CHUNK, "a chunk must split into whole workgroups");
+constexpr int kXcds = 8;
 
 typedef float f2v __attribute__((ext_vector_type(2)));
 typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+typedef unsigned u2v __attribute__((ext_vector_type(2)));
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ unsigned pack_bf16(float a, float b)
 {
@@ -40,43 +46,37 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b)
 template <typename T> struct Io;
 
 template <> struct Io<float> {
-    static __device__ __forceinline__ void load8(const void* p, int64_t e, float* x)
+    static __device__ __forceinline__ void load4(const void* p, int64_t e, float* x)
     {
-        const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + e);
-        float4 a = q[0], b = q[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        u4v w = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(static_cast<const float*>(p) + e));
+        x[0] = __uint_as_float(w[0]); x[1] = __uint_as_float(w[1]);
+        x[2] = __uint_as_float(w[2]); x[3] = __uint_as_float(w[3]);
     }
     static __device__ __forceinline__ float load1(const void* p, int64_t e) { return static_cast<const float*>(p)[e]; }
-    static __device__ __forceinline__ void store8(void* p, int64_t e, const float* x)
+    static __device__ __forceinline__ void store4(void* p, int64_t e, const float* x)
     {
-        float4* q = reinterpret_cast<float4*>(static_cast<float*>(p) + e);
-        q[0] = make_float4(x[0], x[1], x[2], x[3]);
-        q[1] = make_float4(x[4], x[5], x[6], x[7]);
+        u4v w = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+        __builtin_nontemporal_store(w, reinterpret_cast<u4v*>(static_cast<float*>(p) + e));
     }
     static __device__ __forceinline__ void store1(void* p, int64_t e, float x) { static_cast<float*>(p)[e] = x; }
     static __device__ __forceinline__ float through(float x) { return x; }
 };
 
 template <> struct Io<__bf16> {
-    static __device__ __forceinline__ void load8(const void* p, int64_t e, float* x)
+    static __device__ __forceinline__ void load4(const void* p, int64_t e, float* x)
     {
-        uint4 w = *reinterpret_cast<const uint4*>(static_cast<const unsigned short*>(p) + e);
-        const unsigned ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            x[2 * k] = __uint_as_float(ws[k] << 16);
-            x[2 * k + 1] = __uint_as_float(ws[k] & 0xffff0000u);
-        }
+        u2v w = __builtin_nontemporal_load(reinterpret_cast<const u2v*>(static_cast<const unsigned short*>(p) + e));
+        x[0] = __uint_as_float(w[0] << 16); x[1] = __uint_as_float(w[0] & 0xffff0000u);
+        x[2] = __uint_as_float(w[1] << 16); x[3] = __uint_as_float(w[1] & 0xffff0000u);
     }
     static __device__ __forceinline__ float load1(const void* p, int64_t e)
     {
         return __uint_as_float(((unsigned)static_cast<const unsigned short*>(p)[e]) << 16);
     }
-    static __device__ __forceinline__ void store8(void* p, int64_t e, const float* x)
+    static __device__ __forceinline__ void store4(void* p, int64_t e, const float* x)
     {
-        *reinterpret_cast<uint4*>(static_cast<unsigned short*>(p) + e) =
-            make_uint4(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7]));
+        u2v w = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+        __builtin_nontemporal_store(w, reinterpret_cast<u2v*>(static_cast<unsigned short*>(p) + e));
     }
     static __device__ __forceinline__ void store1(void* p, int64_t e, float x)
     {
@@ -89,80 +89,83 @@ template <> struct Io<__bf16> {
     }
 };
 
+// Workgroups are dispatched to the XCDs round robin (block b runs on XCD
+// b mod 8).  The grid is padded to 8 * per blocks and block b takes virtual
+// block (b mod 8) * per + b / 8, so XCD x works through the contiguous range
+// [x * per, (x + 1) * per); virtual blocks past the end exit.
+__device__ __forceinline__ unsigned xcd_block(unsigned b, unsigned per) { return (b % kXcds) * per + b / kXcds; }
+
 template <typename TP, typename TG, typename TM>
 __global__ void __launch_bounds__(kBlock)
-adamw_tree_kernel(const LeafDev* __restrict__ leaves, const ChunkDev* __restrict__ chunks, AdamwScalars s)
+adamw_tree_kernel(const LeafDev* __restrict__ leaves, const ChunkDev* __restrict__ chunks, unsigned n_virtual,
+                  unsigned per_xcd, AdamwScalars s)
 {
-    const ChunkDev ch = chunks[blockIdx.x];
+    const unsigned vb = xcd_block(blockIdx.x, per_xcd);
+    if (vb >= n_virtual) return;
+    const ChunkDev ch = chunks[vb / kSub];
     const LeafDev L = leaves[ch.leaf];
-    const bool vec = (L.flags & 1) != 0;
+    const int i0 = ((int)(vb % kSub) * kBlock + (int)threadIdx.x) * kPer;   // offset within the chunk
+    const int cnt = ch.count - i0;
+    if (cnt <= 0) return;
+    const int64_t e0 = ch.start + i0;
+    const bool full = (L.flags & 1) != 0 && cnt >= kPer;
 
-    float th[kSteps][kPer], g[kSteps][kPer], m[kSteps][kPer], v[kSteps][kPer];
-    int64_t e0[kSteps];
-    bool full[kSteps];
-    int cnt[kSteps];
+    float th[kPer], g[kPer], m[kPer], v[kPer];
+    if (full) {
+        Io<TP>::load4(L.in[0], e0, th);
+        Io<TG>::load4(L.in[1], e0, g);
+        Io<TM>::load4(L.in[2], e0, m);
+        Io<TM>::load4(L.in[3], e0, v);
+    } else {
 #pragma unroll
-    for (int u = 0; u < kSteps; ++u) {
-        const int i0 = (u * kBlock + (int)threadIdx.x) * kPer;   // offset within the chunk
-        e0[u] = ch.start + i0;
-        cnt[u] = ch.count - i0;
-        full[u] = vec && cnt[u] >= kPer;
-        if (full[u]) {
-            Io<TP>::load8(L.in[0], e0[u], th[u]);
-            Io<TG>::load8(L.in[1], e0[u], g[u]);
-            Io<TM>::load8(L.in[2], e0[u], m[u]);
-            Io<TM>::load8(L.in[3], e0[u], v[u]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < kPer; ++j) {
-                th[u][j] = g[u][j] = m[u][j] = v[u][j] = 0.0f;
-                if (j < cnt[u]) {
-                    th[u][j] = Io<TP>::load1(L.in[0], e0[u] + j);
-                    g[u][j] = Io<TG>::load1(L.in[1], e0[u] + j);
-                    m[u][j] = Io<TM>::load1(L.in[2], e0[u] + j);
-                    v[u][j] = Io<TM>::load1(L.in[3], e0[u] + j);
-                }
+        for (int j = 0; j < kPer; ++j) {
+            th[j] = g[j] = m[j] = v[j] = 0.0f;
+            if (j < cnt) {
+                th[j] = Io<TP>::load1(L.in[0], e0 + j);
+                g[j] = Io<TG>::load1(L.in[1], e0 + j);
+                m[j] = Io<TM>::load1(L.in[2], e0 + j);
+                v[j] = Io<TM>::load1(L.in[3], e0 + j);
             }
         }
     }
+    float to[kPer], mo[kPer], vo[kPer];
 #pragma unroll
-    for (int u = 0; u < kSteps; ++u) {
-        if (cnt[u] <= 0) continue;
-        float to[kPer], mo[kPer], vo[kPer];
+    for (int j = 0; j < kPer; ++j) {
+        const float gj = g[j];
+        float m2 = s.b1 * m[j] + s.c1 * gj;
+        float v2 = s.b2 * v[j] + s.c2 * (gj * gj);
+        m2 = Io<TM>::through(m2);
+        v2 = Io<TM>::through(v2);
+        const float mh = m2 / s.bc1;
+        const float vh = v2 / s.bc2;
+        const float upd = mh / (sqrtf(vh) + s.eps) + s.wd * th[j];
+        to[j] = th[j] - s.lr * upd;
+        mo[j] = m2;
+        vo[j] = v2;
+    }
+    if (full) {
+        Io<TP>::store4(L.out[0], e0, to);
+        Io<TM>::store4(L.out[1], e0, mo);
+        Io<TM>::store4(L.out[2], e0, vo);
+    } else {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const float gj = g[u][j];
-            float m2 = s.b1 * m[u][j] + s.c1 * gj;
-            float v2 = s.b2 * v[u][j] + s.c2 * (gj * gj);
-            m2 = Io<TM>::through(m2);
-            v2 = Io<TM>::through(v2);
-            const float mh = m2 / s.bc1;
-            const float vh = v2 / s.bc2;
-            const float upd = mh / (sqrtf(vh) + s.eps) + s.wd * th[u][j];
-            to[j] = th[u][j] - s.lr * upd;
-            mo[j] = m2;
-            vo[j] = v2;
-        }
-        if (full[u]) {
-            Io<TP>::store8(L.out[0], e0[u], to);
-            Io<TM>::store8(L.out[1], e0[u], mo);
-            Io<TM>::store8(L.out[2], e0[u], vo);
-        } else {
-#pragma unroll
-            for (int j = 0; j < kPer; ++j)
-                if (j < cnt[u]) {
-                    Io<TP>::store1(L.out[0], e0[u] + j, to[j]);
-                    Io<TM>::store1(L.out[1], e0[u] + j, mo[j]);
-                    Io<TM>::store1(L.out[2], e0[u] + j, vo[j]);
-                }
-        }
+        for (int j = 0; j < kPer; ++j)
+            if (j < cnt) {
+                Io<TP>::store1(L.out[0], e0 + j, to[j]);
+                Io<TM>::store1(L.out[1], e0 + j, mo[j]);
+                Io<TM>::store1(L.out[2], e0 + j, vo[j]);
+            }
     }
 }
 
 template <typename TP, typename TG, typename TM>
-hipError_t launch(const LeafDev* l, const ChunkDev* c, int64_t n, const AdamwScalars& s, hipStream_t st)
+hipError_t launch(const LeafDev* l, const ChunkDev* c, int64_t n_chunks, const AdamwScalars& s, hipStream_t st)
 {
-    hipLaunchKernelGGL((adamw_tree_kernel<TP, TG, TM>), dim3((unsigned)n), dim3(kBlock), 0, st, l, c, s);
+    const int64_t n_virtual = n_chunks * kSub;
+    const int64_t per = (n_virtual + kXcds - 1) / kXcds;
+    if (per * kXcds > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((adamw_tree_kernel<TP, TG, TM>), dim3((unsigned)(per * kXcds)), dim3(kBlock), 0, st, l, c,
+                       (unsigned)n_virtual, (unsigned)per, s);
     return hipGetLastError();
 }
 
