@@ -70,9 +70,7 @@ static psk_status get_kernel(const Analysis& an, bool vector, std::shared_ptr<Ke
 {
     KernelPlan plan = plan_kernel(an, vector);
     std::string canon = canonical_text(an);
-    char tag[96];
-    std::snprintf(tag, sizeof tag, "k%d v%d b%d l%d n%d", plan.kind, plan.vec, plan.block, plan.lanes, plan.nv);
-    std::string key = canon + tag;
+    std::string key = canon + plan.key();
     {
         std::lock_guard<std::mutex> lk(g_cache_mu);
         auto it = cache().find(key);

@@ -28,6 +28,7 @@
 #include <cinttypes>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <sstream>
 
@@ -76,28 +77,75 @@ std::string canonical_text(const Analysis& an)
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Layout overrides for measurement, "key=value" pairs separated by commas in
+// PSK_LAYOUT: nt=0|1, xcd=0|1, block=64..1024 (pointwise, and row kernels
+// whose rows are narrower than a block), lanes=16|64|128|...|1024 (row
+// kernel; changes the reduction tree).  A layout never changes which
+// elements are computed.
+static int layout_value(const char* key, int dflt)
+{
+    const char* env = std::getenv("PSK_LAYOUT");
+    if (!env) return dflt;
+    std::string s(env), k = std::string(key) + "=";
+    size_t pos = 0;
+    while (pos < s.size()) {
+        size_t end = s.find(',', pos);
+        if (end == std::string::npos) end = s.size();
+        std::string item = s.substr(pos, end - pos);
+        if (item.compare(0, k.size(), k) == 0) return std::atoi(item.c_str() + k.size());
+        pos = end + 1;
+    }
+    return dflt;
+}
+
+std::string KernelPlan::key() const
+{
+    char b[160];
+    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld", kind, vec, block, lanes, nv, (int)nt, (int)xcd,
+                  (long long)blocks);
+    return b;
+}
+
 KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
 {
     KernelPlan p;
     const int V = an.out_dtype == PSK_BF16 ? 8 : 4;
     p.vec = (allow_vector && an.cols % V == 0) ? V : 1;
+    p.nt = layout_value("nt", 1) != 0;
+    p.xcd = layout_value("xcd", an.row_kind ? 0 : 1) != 0;
+    int block = layout_value("block", 256);
+    if (block < 64 || block > 1024 || (block & (block - 1))) block = 256;
     if (!an.row_kind) {
         p.kind = 0;
-        p.block = 256;
-        p.grid = ceil_div(ceil_div(an.numel, p.vec), p.block);
-        return p;
+        p.block = block;
+        p.blocks = ceil_div(ceil_div(an.numel, p.vec), p.block);
+    } else {
+        p.kind = 1;
+        // about 32 bytes of output per lane (8 f32 or 16 bf16 elements); a
+        // row is 16 lanes (one DPP row) or whole waves; a workgroup of at
+        // least 128 threads, one row per workgroup once a row has 128 lanes
+        const int epl = an.out_dtype == PSK_BF16 ? 16 : 8;
+        int64_t want = ceil_div(an.cols, epl);
+        int L = 16;
+        while (L < want && L < 1024) L <<= 1;
+        if (L > 16 && L < 64) L = 64;
+        int Lo = layout_value("lanes", L);
+        if (Lo == 16 || (Lo >= 64 && Lo <= 1024 && !(Lo & (Lo - 1)))) L = Lo;
+        p.lanes = L;
+        p.nv = (int)ceil_div(an.cols, (int64_t)L * p.vec);
+        if (L >= 128) block = layout_value("block", 128);
+        if (block < 64 || block > 1024 || (block & (block - 1))) block = 128;
+        p.block = L > block ? L : block;
+        p.rows_per_block = p.block / L;
+        p.blocks = ceil_div(an.rows, p.rows_per_block);
     }
-    p.kind = 1;
-    // about 16 elements per lane; a row is 16 lanes (one DPP row) or whole waves
-    int64_t want = ceil_div(an.cols, 16);
-    int L = 16;
-    while (L < want && L < 1024) L <<= 1;
-    if (L > 16 && L < 64) L = 64;
-    p.lanes = L;
-    p.nv = (int)ceil_div(an.cols, (int64_t)L * p.vec);
-    p.block = L > 256 ? L : 256;
-    p.rows_per_block = p.block / L;
-    p.grid = ceil_div(an.rows, p.rows_per_block);
+    if (p.xcd) {
+        p.per_xcd = ceil_div(p.blocks, 8);
+        p.grid = p.per_xcd * 8;
+    } else {
+        p.per_xcd = p.blocks;
+        p.grid = p.blocks;
+    }
     return p;
 }
 
@@ -108,6 +156,24 @@ typedef unsigned int psk_u32;
 typedef unsigned short psk_u16;
 typedef float psk_f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 psk_b2 __attribute__((ext_vector_type(2)));
+typedef unsigned psk_u4v __attribute__((ext_vector_type(4)));
+typedef unsigned psk_u2v __attribute__((ext_vector_type(2)));
+// every input byte is read once and every output byte written once:
+// nontemporal accesses when PSK_NT is set
+template <typename T> __device__ __forceinline__ T psk_ld(const T* p) {
+#if PSK_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+template <typename T> __device__ __forceinline__ void psk_st(T* p, T v) {
+#if PSK_NT
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
 // bf16 is the top half of a binary32: widening is a shift
 __device__ __forceinline__ float psk_lo(psk_u32 w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float psk_hi(psk_u32 w) { return __uint_as_float(w & 0xffff0000u); }
@@ -118,8 +184,46 @@ __device__ __forceinline__ psk_u32 psk_pack2(float a, float b) {
   return __builtin_bit_cast(psk_u32, __builtin_convertvector(f, psk_b2));
 }
 __device__ __forceinline__ psk_u16 psk_r1(float a) { return (psk_u16)(psk_pack2(a, 0.0f) & 0xffffu); }
-// gelu = x * Phi(x), Phi through the complementary error function
-__device__ __forceinline__ float psk_gelu(float x) { return (0.5f * x) * erfcf(-(x * 0.70710678118654752440f)); }
+// gelu(x) = x * Phi(x) with Phi(x) = erfc(-x/sqrt 2) / 2.  erfc(w), w >= 0,
+// is the Chebyshev-fitted form of Press, Teukolsky, Vetterling and Flannery,
+// Numerical Recipes (2nd ed.), section 6.2: erfc(w) = t exp(-w^2 + P(t)),
+// t = 1/(1 + w/2), fractional error below 1.2e-7 for all w >= 0.  The
+// exponential takes -w^2 as the exact pair hi + lo (an fma gives the
+// rounding error of w*w) and reduces it Cody-Waite style with the
+// 15-significant-bit split of ln 2, so the large term never rounds; the
+// reduced argument (|r| < 0.35) goes through the hardware 2^x.  For x > 0,
+// Phi = 1 - erfc(w)/2.  w is clamped at 10, where erfc(w) < 2^-149: Phi is
+// then 0 or 1, also for infinite x (a NaN x stays NaN through x * Phi).
+__device__ __forceinline__ float psk_gelu(float x) {
+  const float w = fminf(fabsf(x) * 0.70710678118654752440f, 10.0f);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, w, 1.0f));
+  float p = 0.17087277f;
+  p = fmaf(p, t, -0.82215223f); p = fmaf(p, t, 1.48851587f); p = fmaf(p, t, -1.13520398f);
+  p = fmaf(p, t, 0.27886807f);  p = fmaf(p, t, -0.18628806f); p = fmaf(p, t, 0.09678418f);
+  p = fmaf(p, t, 0.37409196f);  p = fmaf(p, t, 1.00002368f);  p = fmaf(p, t, -1.26551223f);
+  const float hi = w * w;
+  const float lo = fmaf(w, w, -hi);
+  const float k = __builtin_rintf(hi * -1.44269504088896341f);
+  float r = fmaf(k, -0.693145751953125f, -hi);
+  r = fmaf(k, -1.42860682030941723212e-6f, r);
+  r = r + (p - lo);
+  const float ec = t * __builtin_ldexpf(__builtin_amdgcn_exp2f(r * 1.44269504088896341f), (int)k);
+  const float phi = (x > 0.0f) ? fmaf(-0.5f, ec, 1.0f) : 0.5f * ec;
+  return x * phi;
+}
+// a / b for a value b shared by the whole row, given y = 1/b correctly
+// rounded: q = a*y is within an ulp of a/b; the fma gives the exact
+// remainder a - b*q, and one more fma rounds q + remainder*y to the
+// correctly rounded quotient (Markstein's correction).  That holds while
+// b lies in [2^-40, 2^40] and a is zero or in [2^-86, 2^87] (no underflow of
+// the remainder, no overflow of q); `bad` records a lane where it may not,
+// and the caller then redoes that member's elements with IEEE division.
+__device__ __forceinline__ float psk_divr(float a, float b, float y, bool& bad) {
+  const float q = a * y;
+  const float rem = fmaf(-q, b, a);
+  bad |= !((fabsf(a) >= 0x1p-86f || a == 0.0f) && fabsf(a) <= 0x1p87f);
+  return fmaf(rem, y, q);
+}
 __device__ __forceinline__ float psk_max(float a, float b) { return (a > b) ? a : b; }
 __device__ __forceinline__ float psk_min(float a, float b) { return (a < b) ? a : b; }
 #define PSK_DPP(x, ctl) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (x)), (ctl), 0xF, 0xF, false))
@@ -178,8 +282,66 @@ struct Emitter {
     // value of node i at element e (element value or a row value)
     std::string val(int i, int e) const
     {
+        if (use_refused) return refused(i);
         if (an.is_row[i]) return "r" + std::to_string(i);
         return "v" + std::to_string(i) + "_" + std::to_string(e);
+    }
+
+    // node i's value at a refused position: a row value
+    std::string refused(int i) const
+    {
+        if (an.is_row[i]) return "r" + std::to_string(i);
+        return "u" + std::to_string(i);
+    }
+
+    std::string refused_expr(int i) const
+    {
+        const psk_node& nd = an.nodes[i];
+        if (nd.op == PSK_OP_CAUSAL_MASK) return "(-__builtin_inff())";
+        // the member's own expression with every operand at its refused value
+        Emitter& self = const_cast<Emitter&>(*this);
+        self.use_refused = true;
+        std::string s = expr(i, 0);
+        self.use_refused = false;
+        return s;
+    }
+
+    bool use_refused = false;
+    bool divr_ok = true;          // row-value divisors use psk_divr
+
+    // a row value that divides element values: its reciprocal, once per row
+    void row_reciprocal(int i)
+    {
+        if (!divr_ok) return;
+        bool used = false;
+        for (size_t j = 0; j < an.nodes.size(); ++j)
+            if (an.nodes[j].op == PSK_OP_DIV && an.nodes[j].b == i && !an.is_row[j]) used = true;
+        if (!used) return;
+        o << "    const float y" << i << " = 1.0f / r" << i << ";\n";
+        o << "    const bool yok" << i << " = fabsf(r" << i << ") >= 0x1p-40f && fabsf(r" << i << ") <= 0x1p40f;\n";
+    }
+
+    // element division by a row value: Markstein's correction
+    bool divr_node(int i) const
+    {
+        const psk_node& nd = an.nodes[i];
+        return !use_refused && divr_ok && nd.op == PSK_OP_DIV && !an.is_row[i] && an.is_row[nd.b];
+    }
+
+    // elements of member i (given as element indices) written through
+    // psk_divr: declare the lane flag before, redo with IEEE division after
+    void divr_open(int i)
+    {
+        if (divr_node(i)) o << "    bool bad" << i << " = !yok" << an.nodes[i].b << ";\n";
+    }
+    void divr_close(int i, const std::vector<int>& elems, const char* indent)
+    {
+        if (!divr_node(i)) return;
+        const psk_node& nd = an.nodes[i];
+        o << indent << "if (bad" << i << ") {\n";
+        for (int e : elems)
+            o << indent << "  v" << i << "_" << e << " = " << val(nd.a, e) << " / " << val(nd.b, e) << ";\n";
+        o << indent << "}\n";
     }
 
     std::string expr(int i, int e) const
@@ -192,7 +354,10 @@ struct Emitter {
         case PSK_OP_ADD: return "(" + A() + " + " + B() + ")";
         case PSK_OP_SUB: return "(" + A() + " - " + B() + ")";
         case PSK_OP_MUL: return "(" + A() + " * " + B() + ")";
-        case PSK_OP_DIV: return "(" + A() + " / " + B() + ")";
+        case PSK_OP_DIV:
+            if (divr_node(i))
+                return "psk_divr(" + A() + ", " + B() + ", y" + std::to_string(nd.b) + ", bad" + std::to_string(i) + ")";
+            return "(" + A() + " / " + B() + ")";
         case PSK_OP_MAX: return "psk_max(" + A() + ", " + B() + ")";
         case PSK_OP_MIN: return "psk_min(" + A() + ", " + B() + ")";
         case PSK_OP_NEG: return "(-" + A() + ")";
@@ -257,7 +422,7 @@ struct Emitter {
         if (V == 1) {
             o << "    float " << dst(0) << " = 0.0f;\n";
             o << "    if (" << cond << ") " << dst(0) << " = "
-              << (in.dtype == PSK_BF16 ? "psk_h(*" + p + ")" : "*" + p) << ";\n";
+              << (in.dtype == PSK_BF16 ? "psk_h(psk_ld(" + p + "))" : "psk_ld(" + p + ")") << ";\n";
             return;
         }
         int nwords = bytes / 4;
@@ -270,14 +435,13 @@ struct Emitter {
             int elems_per_word = 4 / esize(in.dtype);
             int eoff = w * elems_per_word;
             if (cnt == 4) {
-                o << "    uint4 " << wn << " = make_uint4(0u, 0u, 0u, 0u);\n";
-                o << "    if (" << cond << ") " << wn << " = *(const uint4*)(" << p << " + " << eoff << ");\n";
-                words.push_back(wn + ".x"); words.push_back(wn + ".y");
-                words.push_back(wn + ".z"); words.push_back(wn + ".w");
+                o << "    psk_u4v " << wn << " = {0u, 0u, 0u, 0u};\n";
+                o << "    if (" << cond << ") " << wn << " = psk_ld((const psk_u4v*)(" << p << " + " << eoff << "));\n";
+                for (int q = 0; q < 4; ++q) words.push_back(wn + "[" + std::to_string(q) + "]");
             } else {
-                o << "    uint2 " << wn << " = make_uint2(0u, 0u);\n";
-                o << "    if (" << cond << ") " << wn << " = *(const uint2*)(" << p << " + " << eoff << ");\n";
-                words.push_back(wn + ".x"); words.push_back(wn + ".y");
+                o << "    psk_u2v " << wn << " = {0u, 0u};\n";
+                o << "    if (" << cond << ") " << wn << " = psk_ld((const psk_u2v*)(" << p << " + " << eoff << "));\n";
+                for (int q = 0; q < 2; ++q) words.push_back(wn + "[" + std::to_string(q) + "]");
             }
         }
         for (int j = 0; j < V; ++j) {
@@ -294,18 +458,32 @@ struct Emitter {
         std::string p = "(out + " + off + ")";
         auto src = [&](int j) { return val(an.root, e0 + j); };
         if (V == 1) {
-            o << "    if (" << cond << ") *" << p << " = "
-              << (an.out_dtype == PSK_BF16 ? "psk_r1(" + src(0) + ")" : src(0)) << ";\n";
+            o << "    if (" << cond << ") psk_st(" << p << ", "
+              << (an.out_dtype == PSK_BF16 ? "psk_r1(" + src(0) + ")" : src(0)) << ");\n";
             return;
         }
         if (an.out_dtype == PSK_F32) {
-            o << "    if (" << cond << ") *(uint4*)" << p << " = make_uint4(";
+            o << "    if (" << cond << ") psk_st((psk_u4v*)" << p << ", (psk_u4v){";
             for (int j = 0; j < 4; ++j) o << (j ? ", " : "") << "__float_as_uint(" << src(j) << ")";
-            o << ");\n";
+            o << "});\n";
         } else {
-            o << "    if (" << cond << ") *(uint4*)" << p << " = make_uint4(";
+            o << "    if (" << cond << ") psk_st((psk_u4v*)" << p << ", (psk_u4v){";
             for (int j = 0; j < 4; ++j) o << (j ? ", " : "") << "psk_pack2(" << src(2 * j) << ", " << src(2 * j + 1) << ")";
-            o << ");\n";
+            o << "});\n";
+        }
+    }
+
+    // Workgroups go to the 8 XCDs round robin; with the XCD layout block b
+    // takes virtual block (b mod 8) * per + b / 8, so each XCD streams one
+    // contiguous eighth of the output.  The grid is padded to a multiple of
+    // 8; padding blocks exit (whole workgroups, before any barrier).
+    void block_index()
+    {
+        if (pl.xcd) {
+            o << "    const unsigned vb = (blockIdx.x % 8u) * " << pl.per_xcd << "u + blockIdx.x / 8u;\n";
+            o << "    if (vb >= " << pl.blocks << "u) return;\n";
+        } else {
+            o << "    const unsigned vb = blockIdx.x;\n";
         }
     }
 
@@ -323,14 +501,82 @@ struct Emitter {
         o << "  " << ptype(an.out_dtype) << "* out = (" << ptype(an.out_dtype) << "*)out_;\n";
     }
 
+    // Row kernel with a causal mask: a lane's vector k whose first column
+    // lies past the row's last allowed column is refused entirely.  There,
+    // members uniform at refused positions take their per-row refused value,
+    // members irrelevant at refused positions are not computed, and the rest
+    // are computed as usual.
+    bool skip_refused() const
+    {
+        if (pl.kind != 1 || an.mask_period <= 0) return false;
+        for (size_t i = 0; i < an.nodes.size(); ++i)
+            if (an.uniform[i] && an.nodes[i].op != PSK_OP_CAUSAL_MASK) return true;
+        return false;
+    }
+
+    void members_at_skipping(int p)
+    {
+        const int n = (int)an.nodes.size();
+        std::vector<int> elems;
+        for (int i = 0; i < n; ++i) {
+            const psk_node& nd = an.nodes[i];
+            if (op_is_leaf(nd.op) || op_is_row(nd.op) || an.depth[i] != p) continue;
+            if (an.is_row[i]) {
+                o << "    const float r" << i << " = " << expr(i, 0) << ";\n";
+                row_reciprocal(i);
+            } else {
+                elems.push_back(i);
+            }
+        }
+        for (int i : elems)
+            if (an.uniform[i]) o << "    const float u" << i << " = " << refused_expr(i) << ";\n";
+        for (int k = 0; k < pl.nv; ++k) {
+            for (int i : elems)
+                for (int j = 0; j < pl.vec; ++j) o << "    float v" << i << "_" << k * pl.vec + j << ";\n";
+            o << "    if (c" << k << " <= q) {\n";
+            for (int i : elems) {
+                divr_open(i);
+                std::vector<int> es;
+                for (int j = 0; j < pl.vec; ++j) {
+                    int e = k * pl.vec + j;
+                    o << "      v" << i << "_" << e << " = " << expr(i, e) << ";\n";
+                    es.push_back(e);
+                }
+                divr_close(i, es, "      ");
+            }
+            o << "    } else {\n";
+            for (int i : elems)
+                for (int j = 0; j < pl.vec; ++j) {
+                    int e = k * pl.vec + j;
+                    o << "      v" << i << "_" << e << " = ";
+                    if (an.uniform[i]) o << "u" << i;
+                    else if (an.irrelevant[i]) o << "0.0f";
+                    else if (divr_node(i)) o << val(an.nodes[i].a, e) << " / " << val(an.nodes[i].b, e);
+                    else o << expr(i, e);
+                    o << ";\n";
+                }
+            o << "    }\n";
+        }
+    }
+
     // element members of the given depth, and row members of that depth
     void members_at(int p)
     {
+        if (skip_refused()) { members_at_skipping(p); return; }
         for (size_t i = 0; i < an.nodes.size(); ++i) {
             const psk_node& nd = an.nodes[i];
             if (op_is_leaf(nd.op) || op_is_row(nd.op) || an.depth[i] != p) continue;
             if (an.is_row[i]) {
                 o << "    const float r" << i << " = " << expr((int)i, 0) << ";\n";
+                row_reciprocal((int)i);
+            } else if (divr_node((int)i)) {
+                divr_open((int)i);
+                std::vector<int> es;
+                for (int e = 0; e < NE; ++e) {
+                    o << "    float v" << i << "_" << e << " = " << expr((int)i, e) << ";\n";
+                    es.push_back(e);
+                }
+                divr_close((int)i, es, "    ");
             } else {
                 for (int e = 0; e < NE; ++e)
                     o << "    const float v" << i << "_" << e << " = " << expr((int)i, e) << ";\n";
@@ -344,10 +590,12 @@ struct Emitter {
             const psk_node& nd = an.nodes[i];
             if (nd.op == PSK_OP_CONST) {
                 o << "    const float r" << i << " = " << flit(nd.imm) << ";\n";
+                row_reciprocal((int)i);
             } else if (nd.op == PSK_OP_INPUT) {
                 const InputInfo& in = an.inputs[nd.iparam];
                 if (an.is_row[i]) {
                     o << "    const float r" << i << " = xr" << nd.iparam << ";\n";
+                    row_reciprocal((int)i);
                 } else {
                     (void)in;
                     for (int e = 0; e < NE; ++e)
@@ -382,11 +630,12 @@ struct Emitter {
     // ------------------------------------------------------------ pointwise
     std::string pointwise(const std::string& name)
     {
-        o << kPrelude;
+        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n" << kPrelude;
         signature(name);
         const int V = pl.vec;
         o << "  {\n";
-        o << "    const " << I() << " t = (" << I() << ")blockIdx.x * " << pl.block << " + (" << I() << ")threadIdx.x;\n";
+        block_index();
+        o << "    const " << I() << " t = (" << I() << ")vb * " << pl.block << " + (" << I() << ")threadIdx.x;\n";
         o << "    const " << I() << " e0 = t * " << V << ";\n";
         o << "    if (e0 >= (" << I() << ")n_total) return;\n";
         o << "    const " << I() << " row = e0 / (" << I() << ")" << an.cols << ";\n";
@@ -460,18 +709,20 @@ struct Emitter {
                 o << "    const float r" << i << " = p" << i << " / " << flit((float)an.cols) << ";\n";
             else
                 o << "    const float r" << i << " = p" << i << ";\n";
+            row_reciprocal(i);
         }
     }
 
     std::string row(const std::string& name)
     {
-        o << kPrelude;
+        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n" << kPrelude;
         signature(name);
         const int L = pl.lanes, V = pl.vec;
         o << "  {\n";
         o << "    const int slot = (int)threadIdx.x / " << L << ";\n";
         o << "    const int lane = (int)threadIdx.x % " << L << ";\n";
-        o << "    const " << I() << " row = (" << I() << ")blockIdx.x * " << pl.rows_per_block << " + slot;\n";
+        block_index();
+        o << "    const " << I() << " row = (" << I() << ")vb * " << pl.rows_per_block << " + slot;\n";
         o << "    const bool rok = row < (" << I() << ")n_total;\n";
         if (period > 0) o << "    const int q = (int)(row % (" << I() << ")" << period << ");\n";
         for (int k = 0; k < pl.nv; ++k)
@@ -514,8 +765,7 @@ std::string emit_source(const Analysis& an, const KernelPlan& plan, const std::s
     std::istringstream ct(canonical_text(an));
     std::string line;
     while (std::getline(ct, line)) hdr << "//   " << line << "\n";
-    hdr << "// plan: kind " << plan.kind << " vec " << plan.vec << " block " << plan.block << " lanes " << plan.lanes
-        << " nv " << plan.nv << "\n";
+    hdr << "// plan: " << plan.key() << "\n";
     return hdr.str() + (plan.kind == 1 ? em.row(kernel_name) : em.pointwise(kernel_name));
 }
 

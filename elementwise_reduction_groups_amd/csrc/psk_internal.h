@@ -45,6 +45,10 @@ struct Analysis {
     std::vector<int> depth;             // reduction phases that precede the node
     std::vector<int> n_readers;
     std::vector<char> needed;           // reachable from the root
+    // causal masks (one period): values at refused positions
+    int mask_period = 0;                // 0: no causal mask, or masks of different periods
+    std::vector<char> irrelevant;       // element value never used at a refused position
+    std::vector<char> uniform;          // element value at refused positions is one value per row
     std::vector<InputInfo> inputs;
     psk_dtype out_dtype = PSK_F32;
     int out_rank = 1;
@@ -72,7 +76,12 @@ struct KernelPlan {
     int lanes = 64;          // row kernel: lanes per row
     int rows_per_block = 1;  // row kernel
     int nv = 1;              // row kernel: vectors per lane
-    int64_t grid = 0;        // workgroups for the whole output
+    bool nt = true;          // nontemporal loads and stores
+    bool xcd = true;         // each XCD takes a contiguous eighth of the blocks
+    int64_t blocks = 0;      // workgroups that carry work
+    int64_t per_xcd = 0;     // blocks per XCD (xcd layout)
+    int64_t grid = 0;        // workgroups launched (blocks, padded to 8 * per_xcd)
+    std::string key() const;
 };
 
 KernelPlan plan_kernel(const Analysis& an, bool allow_vector);

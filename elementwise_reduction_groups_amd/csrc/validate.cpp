@@ -274,7 +274,9 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
             const int32_t opnd[3] = {nd.a, nd.b, nd.c};
             for (int k = 0; k < ar; ++k) readers[opnd[k]].push_back(i);
         }
-        std::vector<char> irrelevant(n, 0);
+        an.mask_period = period;
+        std::vector<char>& irrelevant = an.irrelevant;
+        irrelevant.assign(n, 0);
         for (int i = n - 1; i >= 0; --i) {
             if (i == an.root || readers[i].empty() || an.is_row[i]) continue;
             bool irr = true;
@@ -284,6 +286,20 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
                 if (op_is_row(rd.op) || an.is_row[r] || !irrelevant[r]) { irr = false; break; }
             }
             irrelevant[i] = irr;
+        }
+        // An element value is uniform at refused positions when it is a
+        // causal mask (-inf there) or an elementwise member whose operands
+        // are all uniform there or one value per row.
+        an.uniform.assign(n, 0);
+        for (int i = 0; i < n; ++i) {
+            const psk_node& nd = an.nodes[i];
+            if (an.is_row[i] || op_is_leaf(nd.op) || op_is_row(nd.op)) continue;
+            if (nd.op == PSK_OP_CAUSAL_MASK) { an.uniform[i] = 1; continue; }
+            int ar = op_arity(nd.op);
+            const int32_t opnd[3] = {nd.a, nd.b, nd.c};
+            bool u = true;
+            for (int k = 0; k < ar; ++k) u = u && (an.is_row[opnd[k]] || an.uniform[opnd[k]]);
+            an.uniform[i] = u;
         }
         for (auto& in : an.inputs) in.mask_guarded = in.used;
         for (int i = 0; i < n; ++i)

@@ -12,6 +12,14 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
+@pytest.fixture(autouse=True)
+def _seed_torch(request):
+    # every test draws from its own fixed seed (derived from its name)
+    import zlib
+    import torch
+    torch.manual_seed(zlib.crc32(request.node.nodeid.encode()) & 0x7FFFFFFF)
+
+
 @pytest.fixture(scope="session")
 def orc():
     import oracle

@@ -237,6 +237,6 @@ def test_emitted_source_structure(lib):
     src = P.psk_group_source(_workload_descs()["softmax"])
     # masked scores are not loaded: the load of vector k is predicated on its first column
     assert "<= q) w0_" in src.replace("&& c0 <= q", "<= q") or "c0 <= q" in src
-    assert src.count("__syncthreads") == 0          # one wave per 1024-wide row: no LDS exchange
+    assert src.count("__syncthreads") == 2          # two waves per 1024-wide row: one LDS exchange per phase
     src = P.psk_group_source(_workload_descs()["rmsnorm"])
     assert src.count("__syncthreads") == 1          # 256 lanes per row: one cross-wave exchange
