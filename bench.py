@@ -46,6 +46,8 @@ def parse():
                     help="run warmup + K steps only (for rocprofv3 runs), no per-group timing, no CPU leg")
     ap.add_argument("--pmc-calib", action="store_true",
                     help="first run one 1 GiB device copy, a known-size reference for the HBM byte counters")
+    ap.add_argument("--profile-all", action="store_true",
+                    help="with --profile-step: after the steps run each other workload twice (for rocprofv3)")
     return ap.parse_args()
 
 
@@ -163,7 +165,12 @@ def main():
             "softmax_GBps": round(gb(softmax_bytes, statistics.median(softmax_ms)), 1),
         },
     }
+    traffic = committed_traffic()
+    if traffic is not None:
+        result["roofline"]["traffic"] = traffic
     if args.profile_step:
+        if args.profile_all:
+            profile_others(P, configs, torch, dev, stream, hp)
         print(json.dumps(result), flush=True)
         return
 
@@ -177,6 +184,58 @@ def main():
         result["cpu_baseline"] = cpu_baseline(args, configs, n_params, shapes, R, C, step_bytes)
 
     print(json.dumps(result), flush=True)
+
+
+ADAMW_COUNTERS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                              "adamw_tree_kernel_llama16_bf16.txt")
+ADAMW_SOURCES = ["elementwise_reduction_groups_amd/csrc/adamw.hip", "elementwise_reduction_groups_amd/csrc/psk_internal.h"]
+
+
+def kernel_source_sha(paths):
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel in paths:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic():
+    """HBM bytes per AdamW launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a copy kernel), or None when the
+    kernel source has changed since the counters were taken."""
+    try:
+        kv = {}
+        for line in open(ADAMW_COUNTERS):
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") != kernel_source_sha(ADAMW_SOURCES):
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def profile_others(P, configs, torch, dev, stream, hp):
+    tiny_shapes = [s for _, s in configs.tiny_gpt_leaves()]
+    tiny = configs.adamw_state(tiny_shapes, device=dev, seed=configs.SEED_BASE)
+    tiny_tree = P.Tree([[s["theta"], s["grad"], s["m"], s["v"]] for s in tiny])
+    x, r, g = configs.rmsnorm_inputs(16384, 4096, device=dev)
+    y = torch.empty_like(x)
+    rms = P.Group(configs.rmsnorm_gelu_dag(configs.f32(1e-5)),
+                  [((16384, 4096), "bf16"), ((16384, 4096), "bf16"), ((4096,), "bf16")], (16384, 4096), "bf16")
+    A, B, Cc = configs.chain_inputs(16384, 16384, device=dev)
+    Z = torch.empty_like(A)
+    chain = P.Group(configs.chain64_dag(), [((16384, 16384), "f32"), ((16384, 1), "f32"), ((1, 16384), "f32")],
+                    (16384, 16384), "f32")
+    torch.cuda.synchronize()
+    for _ in range(2):
+        tiny_tree.adamw_step(*hp, stream=stream)
+        rms.run([x, r, g], y, stream=stream)
+        chain.run([A, B, Cc], Z, stream=stream)
+    torch.cuda.synchronize()
 
 
 def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, probs, adamw_bytes, softmax_bytes, hp):

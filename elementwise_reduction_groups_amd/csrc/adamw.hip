@@ -2,7 +2,7 @@
 //
 // The optimizer step is one elementwise chain over every parameter (presk
 // manual, "PSK-Realize", section "What a group is", parameter trees; the
-// formula is the presk language reference's, "The optimizer").  Here the
+// formula is the presk language reference's, section "Configuration blocks", the optimizer).  Here the
 // chain is mapped over all leaves in a single launch: a device-side chunk
 // table (leaf index, first element, count; 4096 elements per chunk) is split
 // into 8 workgroups per chunk; a workgroup reads its chunk entry and the

@@ -18,7 +18,7 @@
  *     softmax and RMSNorm (same page, "Reduction-rooted regions");
  *   - a chain mapped over every leaf of a parameter tree: the AdamW step
  *     (presk manual, "PSK-Realize", section "What a group is", paragraph on
- *     parameter trees; presk language reference, "The optimizer"), in one
+ *     parameter trees; presk language reference, section "Configuration blocks", the optimizer), in one
  *     launch for all leaves, driven by a device-side leaf/chunk table (the
  *     role of poot's launch metadata buffer, "Kernel specialization").
  *
@@ -84,12 +84,15 @@ typedef enum psk_dtype { PSK_F32 = 0, PSK_BF16 = 1 } psk_dtype;
  * abs, max/min, pow n).  Semantics, all in f32:
  *   ADD SUB MUL DIV          IEEE-754 binary32, correctly rounded
  *   MAX MIN                  second operand at a tie (presk language
- *                            reference, "Builtins")
+ *                            reference, section "Typing", builtins)
  *   NEG ABS                  sign operations
  *   EXP LOG TANH ERF         device libm (last bits are the library's)
  *   SQRT                     correctly rounded
  *   SQRTABS                  sqrt(|a|)
- *   GELU                     a * Phi(a) = (0.5*a) * erfc(-(a * f32(1/sqrt 2)))
+ *   GELU                     a * Phi(a), Phi(a) = erfc(-a/sqrt 2) / 2 (the
+ *                            exact x * Phi(x) through the error function,
+ *                            presk manual, "Native execution", "The
+ *                            realization"); relative error ~1e-7
  *   POW2                     a * a
  *   POWN (iparam n >= 0)     n-1 products of a, left to right; n = 0 gives 1.
  *                            With n > 2 it never joins a group (PSK-Realize,
@@ -100,7 +103,7 @@ typedef enum psk_dtype { PSK_F32 = 0, PSK_BF16 = 1 } psk_dtype;
  *   CAUSAL_MASK (iparam T)   a where column <= row mod T, else -inf; row is the
  *                            flattened index over all axes but the last
  *                            (causal_mask: allowed where seq2 <= seq, presk
- *                            language reference, "Builtins")
+ *                            language reference, section "Typing", builtins)
  *   ROW_MAX ROW_SUM ROW_MEAN reduction over the last axis, keepdim; the
  *                            result broadcasts back along the row.  ROW_MEAN
  *                            is ROW_SUM divided by the row length.
@@ -239,7 +242,7 @@ psk_status psk_tree_get_tables(const psk_tree* tree, int64_t* leaf_offset, int32
 psk_status psk_tree_plan(const int64_t* numel, int32_t n_leaves, int64_t* n_chunks, int64_t* leaf_offset,
                          int32_t* chunk_leaf, int64_t* chunk_start, int32_t* chunk_count);
 
-/* AdamW hyperparameters (presk language reference, "The optimizer"):
+/* AdamW hyperparameters (presk language reference, section "Configuration blocks", the optimizer):
  *   m' = b1 m + (1-b1) g;  v' = b2 v + (1-b2) g^2;
  *   mh = m'/(1-b1^t);  vh = v'/(1-b2^t);
  *   theta' = theta - lr (mh/(sqrt(vh)+eps) + wd theta)

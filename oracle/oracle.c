@@ -101,7 +101,7 @@ static float orc_gelu(float x)
 }
 
 /* max and min give their second operand at a tie (presk language reference,
- * "Builtins"). */
+ * section "Typing", builtins). */
 static float orc_max(float x, float y) { return (x > y) ? x : y; }
 static float orc_min(float x, float y) { return (x < y) ? x : y; }
 
@@ -157,7 +157,7 @@ static int64_t bcast_offset(int out_rank, const int64_t *out_shape, int64_t r, i
  *   row_sum:  s = v[0]; s = s + v[c]
  *   row_mean: row_sum, then s / C
  * A causal mask replaces a refused position by -inf: column c of row r is
- * allowed where c <= r mod T (presk language reference, "Builtins":
+ * allowed where c <= r mod T (presk language reference, section "Typing", builtins:
  * causal_mask is true where seq2 <= seq), which gives the bits of the
  * softmax over the allowed positions (presk manual, "Native execution").
  *
@@ -270,7 +270,7 @@ int orc_eval_group(int n_nodes, const orc_node *nodes, int root,
 
 /* ---------------------------------------------------------------- AdamW */
 /*
- * One AdamW step over one leaf (presk language reference, "The optimizer"):
+ * One AdamW step over one leaf (presk language reference, section "Configuration blocks", the optimizer):
  *   m' = b1*m + (1-b1)*g
  *   v' = b2*v + (1-b2)*g^2
  *   mh = m' / (1 - b1^t),  vh = v' / (1 - b2^t)

@@ -12,7 +12,7 @@ Workloads (sizes as measured):
      B [16384,1], C [1,16384], all f32.
 
 Distributions: N(0, s) means standard deviation s (presk language reference,
-"Initializers").  bf16 tensors are drawn in f32 and rounded to nearest even
+section "Initializers").  bf16 tensors are drawn in f32 and rounded to nearest even
 (presk native chapter, "The realization").  Every tensor, or leaf slot, gets a
 generator of its own derived from (seed, index), so a leaf's values do not
 depend on how many leaves precede it.

@@ -1,4 +1,4 @@
-"""Pins for the oracle's AdamW step (presk language reference, "The optimizer")."""
+"""Pins for the oracle's AdamW step (presk language reference, section "Configuration blocks", the optimizer)."""
 import math
 
 import numpy as np

@@ -139,7 +139,7 @@ def test_pown_and_select(orc):
 
 
 def test_max_min_tie_gives_second_operand(orc):
-    # presk language reference, "Builtins": at a tie max and min give their
+    # presk language reference, section "Typing", builtins: at a tie max and min give their
     # second operand; +0 and -0 compare equal, so the sign bit shows which
     x = np.array([0.0, -0.0, 1.0, 2.0], np.float32)
     y = np.array([-0.0, 0.0, 2.0, 1.0], np.float32)
