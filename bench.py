@@ -269,6 +269,12 @@ def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, pro
 
     add("adamw_llama_bf16", adamw_bytes, lambda: tree.adamw_step(*hp, stream=stream))
     add("softmax_causal_f32", softmax_bytes, lambda: softmax.run([scores], probs, stream=stream))
+    # the same tree with global-norm clipping and a cosine schedule: a
+    # sum-of-squares pass over g (2 B/param more) and the step
+    n_params = adamw_bytes // 22
+    add("adamw_llama_bf16_clip_cosine", adamw_bytes + 2 * n_params,
+        lambda: tree.adamw_step(*hp, stream=stream, total=1000, warmup=100, schedule="cosine", grad_clip=1.0),
+        note="three launches: per-chunk sums of squares (f64), a one-workgroup combine, the clipped step")
 
     # tiny GPT tree, f32
     tiny_shapes = [s for _, s in configs.tiny_gpt_leaves()]

@@ -84,6 +84,16 @@ class psk_adamw_hp(ctypes.Structure):
                 ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("t", ctypes.c_int64)]
 
 
+class psk_adamw_config(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("t", ctypes.c_int64),
+                ("total", ctypes.c_int64), ("warmup", ctypes.c_int64), ("schedule", ctypes.c_int32),
+                ("grad_clip", ctypes.c_double)]
+
+
+PSK_SCHED = {"constant": 0, "linear": 1, "cosine": 2}
+
+
 class psk_stats(ctypes.Structure):
     _fields_ = [("launches", ctypes.c_int64), ("jit_compiles", ctypes.c_int64), ("jit_hits", ctypes.c_int64)]
 
@@ -93,7 +103,8 @@ _lib = None
 
 EXPORTED = ["psk_group_create", "psk_group_run", "psk_group_destroy", "psk_group_get_info", "psk_group_source",
             "psk_group_code_object", "psk_tree_create", "psk_tree_destroy", "psk_tree_get_info",
-            "psk_tree_get_tables", "psk_tree_plan", "psk_adamw_step", "psk_partition", "psk_last_error",
+            "psk_tree_get_tables", "psk_tree_plan", "psk_adamw_step", "psk_adamw_step_config", "psk_adamw_lr",
+            "psk_tree_clip_result", "psk_partition", "psk_last_error",
             "psk_status_str", "psk_version", "psk_get_stats"]
 
 
@@ -120,6 +131,9 @@ def lib() -> ctypes.CDLL:
     L.psk_tree_get_tables.argtypes = [vp, vp, vp, vp, vp]
     L.psk_tree_plan.argtypes = [vp, i32, ctypes.POINTER(i64), vp, vp, vp, vp]
     L.psk_adamw_step.argtypes = [vp, ctypes.POINTER(psk_adamw_hp), vp]
+    L.psk_adamw_step_config.argtypes = [vp, ctypes.POINTER(psk_adamw_config), vp]
+    L.psk_adamw_lr.argtypes = [ctypes.POINTER(psk_adamw_config), ctypes.POINTER(ctypes.c_double)]
+    L.psk_tree_clip_result.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_float)]
     L.psk_partition.argtypes = [i32, ctypes.POINTER(psk_node), ctypes.POINTER(psk_tensor_desc),
                                 ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(i32), ctypes.POINTER(i32),
                                 ctypes.POINTER(i32)]
@@ -292,6 +306,28 @@ def psk_adamw_step(tree: int, lr: float, beta1: float, beta2: float, eps: float,
     _check(lib().psk_adamw_step(ctypes.c_void_p(tree), ctypes.byref(hp), ctypes.c_void_p(stream or 0)))
 
 
+def adamw_config(lr, beta1, beta2, eps, weight_decay, t, total=0, warmup=0, schedule="constant",
+                 grad_clip=0.0) -> psk_adamw_config:
+    return psk_adamw_config(lr, beta1, beta2, eps, weight_decay, int(t), int(total), int(warmup),
+                            PSK_SCHED[schedule] if isinstance(schedule, str) else int(schedule), grad_clip)
+
+
+def psk_adamw_step_config(tree: int, cfg: psk_adamw_config, stream: Optional[int] = None):
+    _check(lib().psk_adamw_step_config(ctypes.c_void_p(tree), ctypes.byref(cfg), ctypes.c_void_p(stream or 0)))
+
+
+def psk_adamw_lr(cfg: psk_adamw_config) -> float:
+    x = ctypes.c_double()
+    _check(lib().psk_adamw_lr(ctypes.byref(cfg), ctypes.byref(x)))
+    return x.value
+
+
+def psk_tree_clip_result(tree: int):
+    ss, f = ctypes.c_double(), ctypes.c_float()
+    _check(lib().psk_tree_clip_result(ctypes.c_void_p(tree), ctypes.byref(ss), ctypes.byref(f)))
+    return ss.value, f.value
+
+
 def psk_partition(nodes, types: Sequence[Tuple[Sequence[int], object]], is_output: Sequence[bool]):
     import numpy as np
     n = len(nodes)
@@ -388,8 +424,17 @@ class Tree:
     def info(self) -> psk_tree_info:
         return psk_tree_get_info(self.handle)
 
-    def adamw_step(self, lr, beta1, beta2, eps, weight_decay, t, stream=None):
-        psk_adamw_step(self.handle, lr, beta1, beta2, eps, weight_decay, t, _stream_handle(stream))
+    def adamw_step(self, lr, beta1, beta2, eps, weight_decay, t, stream=None, **config):
+        """One AdamW step; keyword arguments total, warmup, schedule and
+        grad_clip select psk_adamw_step_config."""
+        if config:
+            cfg = adamw_config(lr, beta1, beta2, eps, weight_decay, t, **config)
+            psk_adamw_step_config(self.handle, cfg, _stream_handle(stream))
+        else:
+            psk_adamw_step(self.handle, lr, beta1, beta2, eps, weight_decay, t, _stream_handle(stream))
+
+    def clip_result(self):
+        return psk_tree_clip_result(self.handle)
 
     def __del__(self):
         h = getattr(self, "handle", None)

@@ -95,10 +95,10 @@ template <> struct Io<__bf16> {
 // [x * per, (x + 1) * per); virtual blocks past the end exit.
 __device__ __forceinline__ unsigned xcd_block(unsigned b, unsigned per) { return (b % kXcds) * per + b / kXcds; }
 
-template <typename TP, typename TG, typename TM>
+template <typename TP, typename TG, typename TM, bool SCALE>
 __global__ void __launch_bounds__(kBlock)
 adamw_tree_kernel(const LeafDev* __restrict__ leaves, const ChunkDev* __restrict__ chunks, unsigned n_virtual,
-                  unsigned per_xcd, AdamwScalars s)
+                  unsigned per_xcd, AdamwScalars s, const float* __restrict__ gscale)
 {
     const unsigned vb = xcd_block(blockIdx.x, per_xcd);
     if (vb >= n_virtual) return;
@@ -129,9 +129,10 @@ adamw_tree_kernel(const LeafDev* __restrict__ leaves, const ChunkDev* __restrict
         }
     }
     float to[kPer], mo[kPer], vo[kPer];
+    const float gs = SCALE ? *gscale : 1.0f;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-        const float gj = g[j];
+        const float gj = SCALE ? g[j] * gs : g[j];
         float m2 = s.b1 * m[j] + s.c1 * gj;
         float v2 = s.b2 * v[j] + s.c2 * (gj * gj);
         m2 = Io<TM>::through(m2);
@@ -159,34 +160,135 @@ adamw_tree_kernel(const LeafDev* __restrict__ leaves, const ChunkDev* __restrict
 }
 
 template <typename TP, typename TG, typename TM>
-hipError_t launch(const LeafDev* l, const ChunkDev* c, int64_t n_chunks, const AdamwScalars& s, hipStream_t st)
+hipError_t launch(const LeafDev* l, const ChunkDev* c, int64_t n_chunks, const AdamwScalars& s, const float* gscale,
+                  hipStream_t st)
 {
     const int64_t n_virtual = n_chunks * kSub;
     const int64_t per = (n_virtual + kXcds - 1) / kXcds;
     if (per * kXcds > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((adamw_tree_kernel<TP, TG, TM>), dim3((unsigned)(per * kXcds)), dim3(kBlock), 0, st, l, c,
-                       (unsigned)n_virtual, (unsigned)per, s);
+    if (gscale)
+        hipLaunchKernelGGL((adamw_tree_kernel<TP, TG, TM, true>), dim3((unsigned)(per * kXcds)), dim3(kBlock), 0, st,
+                           l, c, (unsigned)n_virtual, (unsigned)per, s, gscale);
+    else
+        hipLaunchKernelGGL((adamw_tree_kernel<TP, TG, TM, false>), dim3((unsigned)(per * kXcds)), dim3(kBlock), 0,
+                           st, l, c, (unsigned)n_virtual, (unsigned)per, s, gscale);
     return hipGetLastError();
+}
+
+// ------------------------------------------------------ global-norm clipping
+constexpr int kClipBlock = 256;
+constexpr int kClipPer = PSK_TREE_CHUNK / kClipBlock;      // 16 elements per thread
+static_assert(kClipPer % 4 == 0, "clip pass reads 4 elements at a time");
+
+__device__ __forceinline__ double wave_sum(double x)
+{
+    // butterfly over the 64 lanes; every lane ends with the same sum
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+template <typename TG>
+__global__ void __launch_bounds__(kClipBlock)
+sumsq_kernel(const LeafDev* __restrict__ leaves, const ChunkDev* __restrict__ chunks,
+             double* __restrict__ partials)
+{
+    __shared__ double red[kClipBlock / 64];
+    const ChunkDev ch = chunks[blockIdx.x];
+    const LeafDev L = leaves[ch.leaf];
+    const bool vec = (L.flags & 1) != 0;
+    double acc = 0.0;
+    // squares of f32 values are exact in f64; the sum runs in f64
+#pragma unroll
+    for (int k = 0; k < kClipPer / 4; ++k) {
+        const int i0 = (k * kClipBlock + (int)threadIdx.x) * 4;
+        const int cnt = ch.count - i0;
+        float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (vec && cnt >= 4) {
+            Io<TG>::load4(L.in[1], ch.start + i0, x);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j < cnt) x[j] = Io<TG>::load1(L.in[1], ch.start + i0 + j);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc += (double)x[j] * (double)x[j];
+    }
+    acc = wave_sum(acc);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double p = red[0];
+        for (int w = 1; w < kClipBlock / 64; ++w) p += red[w];
+        partials[blockIdx.x] = p;
+    }
+}
+
+// One workgroup: the chunk partials combined in a fixed order (each thread
+// a fixed strided subset in increasing order, then a fixed tree), so the
+// result is reproducible; then the factor, formed in f64.
+constexpr int kFinalBlock = 1024;
+__global__ void __launch_bounds__(kFinalBlock)
+clip_finalize_kernel(const double* __restrict__ partials, unsigned n, ClipOut* out, double c)
+{
+    __shared__ double red[kFinalBlock / 64];
+    double s = 0.0;
+    for (unsigned i = threadIdx.x; i < n; i += kFinalBlock) s += partials[i];
+    s = wave_sum(s);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = red[0];
+        for (int w = 1; w < kFinalBlock / 64; ++w) t += red[w];
+        double f = c / (sqrt(t) + 1e-6);
+        if (!(f < 1.0)) f = 1.0;
+        out->sumsq = t;
+        out->factor = (float)f;
+    }
 }
 
 }  // namespace
 
+psk_status launch_clip(const LeafDev* d_leaves, const ChunkDev* d_chunks, int64_t n_chunks, int grad_dt,
+                       double* partials, ClipOut* out, double c, void* stream)
+{
+    if (n_chunks <= 0) return PSK_OK;
+    if (n_chunks > 0x7fffffffLL) return fail(PSK_E_UNSUPPORTED, "too many chunks");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (grad_dt == PSK_BF16)
+        hipLaunchKernelGGL((sumsq_kernel<__bf16>), dim3((unsigned)n_chunks), dim3(kClipBlock), 0, st, d_leaves,
+                           d_chunks, partials);
+    else
+        hipLaunchKernelGGL((sumsq_kernel<float>), dim3((unsigned)n_chunks), dim3(kClipBlock), 0, st, d_leaves,
+                           d_chunks, partials);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(clip_finalize_kernel, dim3(1), dim3(kFinalBlock), 0, st, (const double*)partials,
+                           (unsigned)n_chunks, out, c);
+        e = hipGetLastError();
+    }
+    if (e != hipSuccess) return fail(PSK_E_HIP, std::string("clip launch: ") + hipGetErrorString(e));
+    count_launch();
+    count_launch();
+    return PSK_OK;
+}
+
 psk_status launch_adamw(const LeafDev* d_leaves, const ChunkDev* d_chunks, int64_t n_chunks, int theta_dt,
-                        int grad_dt, int mv_dt, const AdamwScalars& s, void* stream)
+                        int grad_dt, int mv_dt, const AdamwScalars& s, const float* gscale, void* stream)
 {
     if (n_chunks <= 0) return PSK_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int key = (theta_dt == PSK_BF16) * 4 + (grad_dt == PSK_BF16) * 2 + (mv_dt == PSK_BF16);
     hipError_t e;
     switch (key) {
-    case 0: e = launch<float, float, float>(d_leaves, d_chunks, n_chunks, s, st); break;
-    case 1: e = launch<float, float, __bf16>(d_leaves, d_chunks, n_chunks, s, st); break;
-    case 2: e = launch<float, __bf16, float>(d_leaves, d_chunks, n_chunks, s, st); break;
-    case 3: e = launch<float, __bf16, __bf16>(d_leaves, d_chunks, n_chunks, s, st); break;
-    case 4: e = launch<__bf16, float, float>(d_leaves, d_chunks, n_chunks, s, st); break;
-    case 5: e = launch<__bf16, float, __bf16>(d_leaves, d_chunks, n_chunks, s, st); break;
-    case 6: e = launch<__bf16, __bf16, float>(d_leaves, d_chunks, n_chunks, s, st); break;
-    default: e = launch<__bf16, __bf16, __bf16>(d_leaves, d_chunks, n_chunks, s, st); break;
+    case 0: e = launch<float, float, float>(d_leaves, d_chunks, n_chunks, s, gscale, st); break;
+    case 1: e = launch<float, float, __bf16>(d_leaves, d_chunks, n_chunks, s, gscale, st); break;
+    case 2: e = launch<float, __bf16, float>(d_leaves, d_chunks, n_chunks, s, gscale, st); break;
+    case 3: e = launch<float, __bf16, __bf16>(d_leaves, d_chunks, n_chunks, s, gscale, st); break;
+    case 4: e = launch<__bf16, float, float>(d_leaves, d_chunks, n_chunks, s, gscale, st); break;
+    case 5: e = launch<__bf16, float, __bf16>(d_leaves, d_chunks, n_chunks, s, gscale, st); break;
+    case 6: e = launch<__bf16, __bf16, float>(d_leaves, d_chunks, n_chunks, s, gscale, st); break;
+    default: e = launch<__bf16, __bf16, __bf16>(d_leaves, d_chunks, n_chunks, s, gscale, st); break;
     }
     if (e != hipSuccess) return fail(PSK_E_HIP, std::string("AdamW launch: ") + hipGetErrorString(e));
     count_launch();

@@ -268,12 +268,16 @@ struct psk_tree {
     std::vector<ChunkDev> chunks;
     LeafDev* d_leaves = nullptr;
     ChunkDev* d_chunks = nullptr;
+    double* d_partials = nullptr;   // clipping: one partial sum of squares per chunk
+    ClipOut* d_clip = nullptr;      // clipping: squared norm and factor
     int device = 0;
     int32_t vector_leaves = 0;
     ~psk_tree()
     {
         if (d_leaves) (void)hipFree(d_leaves);
         if (d_chunks) (void)hipFree(d_chunks);
+        if (d_partials) (void)hipFree(d_partials);
+        if (d_clip) (void)hipFree(d_clip);
     }
 };
 
@@ -374,6 +378,12 @@ extern "C" psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, 
         if (e == hipSuccess)
             e = hipMemcpy(t->d_chunks, t->chunks.data(), sizeof(ChunkDev) * nc, hipMemcpyHostToDevice);
     }
+    if (e == hipSuccess && nc > 0) {
+        // device state of the clipping pass, owned by the tree
+        e = hipMalloc(&t->d_partials, sizeof(double) * nc);
+        if (e == hipSuccess) e = hipMalloc(&t->d_clip, sizeof(ClipOut));
+        if (e == hipSuccess) e = hipMemset(t->d_clip, 0, sizeof(ClipOut));
+    }
     if (e != hipSuccess) return fail(PSK_E_HIP, std::string("tree upload: ") + hipGetErrorString(e));
     *out = t.release();
     return PSK_OK;
@@ -436,7 +446,74 @@ extern "C" psk_status psk_adamw_step(const psk_tree* tree, const psk_adamw_hp* h
         return fail(PSK_E_HIP, "the current device is not the device the tree was created on");
     AdamwScalars s = adamw_scalars(*hp);
     return launch_adamw(tree->d_leaves, tree->d_chunks, (int64_t)tree->chunks.size(), tree->dt[0], tree->dt[1],
-                        tree->dt[2], s, hip_stream);
+                        tree->dt[2], s, nullptr, hip_stream);
+}
+
+static psk_status schedule_lr(const psk_adamw_config* c, double* lr)
+{
+    if (c->t < 1) return fail(PSK_E_SHAPE, "t counts steps from 1");
+    if (c->schedule == PSK_SCHED_CONSTANT) {
+        *lr = c->lr;
+        return PSK_OK;
+    }
+    if (c->schedule != PSK_SCHED_LINEAR && c->schedule != PSK_SCHED_COSINE)
+        return fail(PSK_E_OP, "unknown schedule");
+    if (c->warmup < 0 || c->warmup >= c->total) return fail(PSK_E_SHAPE, "warmup must satisfy 0 <= warmup < total");
+    if (c->t > c->total) return fail(PSK_E_SHAPE, "t is past total");
+    const double t = (double)c->t, w = (double)c->warmup, T = (double)c->total;
+    if (c->t <= c->warmup) *lr = c->lr * t / w;
+    else if (c->schedule == PSK_SCHED_LINEAR) *lr = c->lr * (T - t) / (T - w);
+    else *lr = c->lr * 0.5 * (1.0 + std::cos(3.14159265358979323846 * (t - w) / (T - w)));
+    return PSK_OK;
+}
+
+extern "C" psk_status psk_adamw_lr(const psk_adamw_config* cfg, double* lr)
+{
+    clear_error();
+    if (!cfg || !lr) return fail(PSK_E_NULL, "cfg or lr is NULL");
+    return schedule_lr(cfg, lr);
+}
+
+extern "C" psk_status psk_adamw_step_config(const psk_tree* tree, const psk_adamw_config* cfg, void* hip_stream)
+{
+    clear_error();
+    if (!tree || !cfg) return fail(PSK_E_NULL, "tree or cfg is NULL");
+    const double v[6] = {cfg->lr, cfg->beta1, cfg->beta2, cfg->eps, cfg->weight_decay, cfg->grad_clip};
+    for (double x : v)
+        if (!std::isfinite(x)) return fail(PSK_E_SHAPE, "hyperparameters must be finite");
+    double lr = 0.0;
+    psk_status st = schedule_lr(cfg, &lr);
+    if (st != PSK_OK) return st;
+    if (tree->chunks.empty()) return PSK_OK;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != tree->device)
+        return fail(PSK_E_HIP, "the current device is not the device the tree was created on");
+    psk_adamw_hp hp = {lr, cfg->beta1, cfg->beta2, cfg->eps, cfg->weight_decay, cfg->t};
+    AdamwScalars s = adamw_scalars(hp);
+    const int64_t nc = (int64_t)tree->chunks.size();
+    const float* gscale = nullptr;
+    if (cfg->grad_clip > 0.0) {
+        st = launch_clip(tree->d_leaves, tree->d_chunks, nc, tree->dt[1], tree->d_partials, tree->d_clip,
+                         cfg->grad_clip, hip_stream);
+        if (st != PSK_OK) return st;
+        gscale = &tree->d_clip->factor;
+    }
+    return launch_adamw(tree->d_leaves, tree->d_chunks, nc, tree->dt[0], tree->dt[1], tree->dt[2], s, gscale,
+                        hip_stream);
+}
+
+extern "C" psk_status psk_tree_clip_result(const psk_tree* tree, double* sumsq, float* factor)
+{
+    clear_error();
+    if (!tree) return fail(PSK_E_NULL, "tree is NULL");
+    ClipOut h = {0.0, 0.0f, 0.0f};
+    if (tree->d_clip) {
+        hipError_t e = hipMemcpy(&h, tree->d_clip, sizeof h, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipMemcpy: ") + hipGetErrorString(e));
+    }
+    if (sumsq) *sumsq = h.sumsq;
+    if (factor) *factor = h.factor;
+    return PSK_OK;
 }
 
 // --------------------------------------------------------------- partition

@@ -133,9 +133,24 @@ struct ChunkDev {
 static_assert(sizeof(LeafDev) == 64, "LeafDev layout");
 static_assert(sizeof(ChunkDev) == 16, "ChunkDev layout");
 
-// One launch over every chunk (defined in adamw.hip).
+// Result of a tree-wide clipping pass, in device memory owned by the tree.
+struct ClipOut {
+    double sumsq;
+    float factor;
+    float pad;
+};
+
+// One launch over every chunk (defined in adamw.hip).  gscale: NULL, or a
+// device f32 that multiplies every gradient element first.
 psk_status launch_adamw(const LeafDev* d_leaves, const ChunkDev* d_chunks, int64_t n_chunks, int theta_dt,
-                        int grad_dt, int mv_dt, const AdamwScalars& s, void* stream);
+                        int grad_dt, int mv_dt, const AdamwScalars& s, const float* gscale, void* stream);
+
+// Tree-wide sum of squares of the gradient slot and the clipping factor
+// min(1, c / (sqrt(sumsq) + 1e-6)): one launch writes a partial sum per
+// chunk into `partials` (n_chunks doubles), a second, one-workgroup launch
+// combines them in a fixed order and writes `out`.
+psk_status launch_clip(const LeafDev* d_leaves, const ChunkDev* d_chunks, int64_t n_chunks, int grad_dt,
+                       double* partials, ClipOut* out, double c, void* stream);
 
 // --------------------------------------------------------------- counters
 void count_launch();

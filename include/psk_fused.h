@@ -260,6 +260,42 @@ typedef struct psk_adamw_hp {
  * the stored values.  Refuses t < 1, non-finite hyperparameters. */
 psk_status psk_adamw_step(const psk_tree* tree, const psk_adamw_hp* hp, void* hip_stream);
 
+/* Learning-rate schedules (presk language reference, section "Configuration
+ * blocks", the optimizer): constant: lr; linear(warmup w): lr*t/w for t <= w,
+ * then lr*(total - t)/(total - w); cosine(warmup w): lr*t/w for t <= w, then
+ * lr/2 * (1 + cos(pi (t - w)/(total - w))); both reach 0 at total. */
+typedef enum psk_schedule { PSK_SCHED_CONSTANT = 0, PSK_SCHED_LINEAR = 1, PSK_SCHED_COSINE = 2 } psk_schedule;
+
+/* A full AdamW configuration.  With grad_clip = c > 0 the gradient is first
+ * scaled by min(1, c / (||g||_2 + 1e-6)), ||g||_2 the global norm over every
+ * leaf of the tree (as clip_grad_norm_ does); the squared norm is
+ * accumulated in f64 and the factor, formed in f64, is rounded once to f32
+ * and multiplies each gradient element in f32 before the step.  The
+ * schedule's lr(t, total) is computed in f64 on the host and rounded once. */
+typedef struct psk_adamw_config {
+    double lr, beta1, beta2, eps, weight_decay;
+    int64_t t;            /* step, counted from 1 */
+    int64_t total;        /* total steps (linear, cosine) */
+    int64_t warmup;       /* warmup steps, 0 <= warmup < total (linear, cosine) */
+    int32_t schedule;     /* psk_schedule */
+    double grad_clip;     /* c > 0: clip by the global norm; <= 0: no clipping */
+} psk_adamw_config;
+
+/* The step of psk_adamw_step under a full configuration: with clipping,
+ * three launches on the stream -- the tree-wide sum of squares (a partial
+ * sum per chunk), a one-workgroup pass that combines the partials in a fixed
+ * order and forms the factor in device memory owned by the tree, and the
+ * step, which reads the factor; no host synchronisation.  Refuses t < 1, t > total or
+ * warmup >= total for the decaying schedules, non-finite values. */
+psk_status psk_adamw_step_config(const psk_tree* tree, const psk_adamw_config* cfg, void* hip_stream);
+
+/* Host-only: the schedule's learning rate at cfg->t (before rounding). */
+psk_status psk_adamw_lr(const psk_adamw_config* cfg, double* lr);
+
+/* The squared global norm and the f32 factor of the last clipped step on
+ * this tree (synchronises the device).  For checks and reporting. */
+psk_status psk_tree_clip_result(const psk_tree* tree, double* sumsq, float* factor);
+
 /* --------------------------------------------------------------- partition */
 /* Partition a function body (a let-list of n nodes, leaves included) into
  * fusion groups (PSK-Realize, "What a group is").  types[i] is node i's

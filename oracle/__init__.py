@@ -71,6 +71,16 @@ def lib() -> ctypes.CDLL:
         L.orc_adamw.argtypes = [i64, ctypes.c_int, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp,
                                 ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                 ctypes.c_double, i64, vp, vp, vp]
+        L.orc_lr_schedule.argtypes = [ctypes.c_int, ctypes.c_double, i64, i64, i64]
+        L.orc_lr_schedule.restype = ctypes.c_double
+        L.orc_sumsq.argtypes = [i64, ctypes.c_int, vp, ctypes.POINTER(ctypes.c_double),
+                                ctypes.POINTER(ctypes.c_double)]
+        L.orc_sumsq.restype = None
+        L.orc_clip_factor.argtypes = [ctypes.c_double, ctypes.c_double]
+        L.orc_clip_factor.restype = ctypes.c_float
+        L.orc_adamw_scaled.argtypes = [i64, ctypes.c_int, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp,
+                                       ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                       ctypes.c_double, i64, ctypes.c_float, vp, vp, vp]
         L.orc_softmax_causal.argtypes = [i64, i64, i64, ctypes.c_float, vp, vp, i64, i64]
         L.orc_rmsnorm_gelu.argtypes = [i64, i64, vp, vp, vp, ctypes.c_float, vp, i64, i64]
         L.orc_partition.argtypes = [ctypes.c_int, vp, vp, vp, vp, ctypes.c_int, vp, vp]
@@ -165,6 +175,38 @@ def adamw(theta: np.ndarray, grad: np.ndarray, m: np.ndarray, v: np.ndarray,
     lib().orc_adamw(theta.size, _dtype_code(theta), _ptr(theta), _dtype_code(grad), _ptr(grad),
                     _dtype_code(m), _ptr(m), _ptr(v), lr, beta1, beta2, eps, weight_decay, int(t),
                     _ptr(to), _ptr(mo), _ptr(vo))
+    return to, mo, vo
+
+
+SCHEDULES = {"constant": 0, "linear": 1, "cosine": 2}
+
+
+def lr_schedule(kind: str, lr: float, t: int, total: int = 0, warmup: int = 0) -> float:
+    return lib().orc_lr_schedule(SCHEDULES[kind], lr, int(t), int(total), int(warmup))
+
+
+def tree_sumsq(grads: Sequence[np.ndarray]) -> float:
+    """Squared global norm of a gradient tree: squares exact in f64, summed
+    with compensation (exact to about one f64 rounding)."""
+    s, c = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    for g in grads:
+        g = np.ascontiguousarray(g)
+        lib().orc_sumsq(g.size, _dtype_code(g), _ptr(g), ctypes.byref(s), ctypes.byref(c))
+    return s.value + c.value
+
+
+def clip_factor(sumsq: float, c: float) -> np.float32:
+    return np.float32(lib().orc_clip_factor(sumsq, c))
+
+
+def adamw_scaled(theta, grad, m, v, lr, beta1, beta2, eps, weight_decay, t, gscale):
+    """AdamW with the gradient scaled by the f32 factor gscale first; lr is
+    the schedule's value at t."""
+    theta, grad, m, v = (np.ascontiguousarray(a) for a in (theta, grad, m, v))
+    to, mo, vo = np.empty_like(theta), np.empty_like(m), np.empty_like(v)
+    lib().orc_adamw_scaled(theta.size, _dtype_code(theta), _ptr(theta), _dtype_code(grad), _ptr(grad),
+                           _dtype_code(m), _ptr(m), _ptr(v), lr, beta1, beta2, eps, weight_decay, int(t),
+                           float(gscale), _ptr(to), _ptr(mo), _ptr(vo))
     return to, mo, vo
 
 

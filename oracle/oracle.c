@@ -323,6 +323,87 @@ void orc_adamw(int64_t n, int theta_dt, const void *theta, int grad_dt, const vo
     }
 }
 
+/*
+ * Learning-rate schedule lr(t, total) (presk language reference, section
+ * "Configuration blocks", the optimizer): constant: lr; linear(warmup w):
+ * lr*t/w for t <= w, then lr*(total - t)/(total - w); cosine(warmup w):
+ * lr*t/w for t <= w, then lr * 1/2 * (1 + cos(pi (t - w)/(total - w))).
+ * Scalar arithmetic, in f64.  kind: 0 constant, 1 linear, 2 cosine.
+ */
+double orc_lr_schedule(int kind, double lr, int64_t t, int64_t total, int64_t warmup)
+{
+    if (kind == 0)
+        return lr;
+    if (t <= warmup)
+        return lr * (double)t / (double)warmup;
+    if (kind == 1)
+        return lr * (double)(total - t) / (double)(total - warmup);
+    const double pi = 3.14159265358979323846;
+    return lr * 0.5 * (1.0 + cos(pi * (double)(t - warmup) / (double)(total - warmup)));
+}
+
+/* Sum of squares of a gradient leaf, added to a running (sum, compensation)
+ * pair (the squared norm of a tree is the sum over its leaves).  Squares of
+ * f32 values are exact in f64; the sum is compensated (Neumaier's variant of
+ * Kahan summation), so the result is the exact sum to about one f64
+ * rounding, whatever the length: the norm is a scalar definition, not a
+ * bracketing of the tree's elements. */
+void orc_sumsq(int64_t n, int dtype, const void *g, double *sum, double *comp)
+{
+    double s = *sum, c = *comp;
+    for (int64_t i = 0; i < n; ++i) {
+        double x = (double)load_elem(g, dtype, i);
+        double y = x * x;
+        double t = s + y;
+        if (fabs(s) >= fabs(y))
+            c += (s - t) + y;
+        else
+            c += (y - t) + s;
+        s = t;
+    }
+    *sum = s;
+    *comp = c;
+}
+
+/* Global-norm clipping factor min(1, c / (sqrt(sumsq) + 1e-6)) in f64,
+ * rounded once to f32 (as clip_grad_norm_ scales the gradient). */
+float orc_clip_factor(double sumsq, double c)
+{
+    double f = c / (sqrt(sumsq) + 1e-6);
+    return (float)(f < 1.0 ? f : 1.0);
+}
+
+/* One AdamW step with the gradient first scaled by an f32 factor:
+ * g_c = g * gscale (one f32 multiply), then the step of orc_adamw with lr
+ * taken as given (the schedule's value). */
+void orc_adamw_scaled(int64_t n, int theta_dt, const void *theta, int grad_dt, const void *grad,
+                      int mv_dt, const void *m, const void *v,
+                      double lr, double beta1, double beta2, double eps, double wd, int64_t t, float gscale,
+                      void *theta_out, void *m_out, void *v_out)
+{
+    float s[9];
+    orc_adamw_scalars(lr, beta1, beta2, eps, wd, t, s);
+    const float b1 = s[0], b2 = s[1], c1 = s[2], c2 = s[3], bc1 = s[4], bc2 = s[5];
+    const float lr_f = s[6], eps_f = s[7], wd_f = s[8];
+    for (int64_t i = 0; i < n; ++i) {
+        float th = load_elem(theta, theta_dt, i);
+        float g = load_elem(grad, grad_dt, i) * gscale;
+        float mm = load_elem(m, mv_dt, i);
+        float vv = load_elem(v, mv_dt, i);
+        float m2 = b1 * mm + c1 * g;
+        float v2 = b2 * vv + c2 * (g * g);
+        m2 = through_storage(mv_dt, m2);
+        v2 = through_storage(mv_dt, v2);
+        float mh = m2 / bc1;
+        float vh = v2 / bc2;
+        float u = mh / (sqrtf(vh) + eps_f) + wd_f * th;
+        float th2 = th - lr_f * u;
+        store_elem(theta_out, theta_dt, i, th2);
+        store_elem(m_out, mv_dt, i, m2);
+        store_elem(v_out, mv_dt, i, v2);
+    }
+}
+
 /* ------------------------------------------------------ causal softmax */
 /*
  * Masked softmax over each row of x [R, C], mask causal with period T:

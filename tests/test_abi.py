@@ -240,3 +240,15 @@ def test_emitted_source_structure(lib):
     assert src.count("__syncthreads") == 2          # two waves per 1024-wide row: one LDS exchange per phase
     src = P.psk_group_source(_workload_descs()["rmsnorm"])
     assert src.count("__syncthreads") == 1          # 256 lanes per row: one cross-wave exchange
+
+
+def test_schedule_lr_matches_oracle(lib, orc):
+    for kind in ("constant", "linear", "cosine"):
+        for t in (1, 5, 10, 11, 37, 99, 100):
+            cfg = P.adamw_config(3e-4, 0.9, 0.999, 1e-8, 0.01, t, total=100, warmup=10, schedule=kind)
+            assert P.psk_adamw_lr(cfg) == orc.lr_schedule(kind, 3e-4, t, 100, 10)
+    for bad in (dict(t=0, total=100, warmup=10), dict(t=101, total=100, warmup=10),
+                dict(t=5, total=100, warmup=100)):
+        with pytest.raises(P.PskError) as ei:
+            P.psk_adamw_lr(P.adamw_config(3e-4, 0.9, 0.999, 1e-8, 0.01, schedule="cosine", **bad))
+        assert ei.value.status == P.PSK_E_SHAPE

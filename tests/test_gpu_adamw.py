@@ -164,3 +164,78 @@ def test_llama_tree_full_size_sampled():
         assert_bits(to_np(outs[leaf][0][i]), rt, f"leaf {leaf} theta'")
         assert_bits(to_np(outs[leaf][1][i]), rm, f"leaf {leaf} m'")
         assert_bits(to_np(outs[leaf][2][i]), rv, f"leaf {leaf} v'")
+
+
+# ------------------------------------------------------ clipping, schedules
+# The device sums exact f64 squares in a fixed tree: sequentially over each
+# thread's 16 elements, a 64-lane butterfly, 4 waves, then up to ~850 chunk
+# partials per thread of the last workgroup and another butterfly: at most
+# about 900 f64 additions on any path, so relative error below 900 * 2^-53
+# (1e-13) of the exact sum; the test allows 1e-12.
+GPU_SUMSQ_REL = 1e-12
+def _run_config(state, **cfg):
+    tree = P.Tree([[s["theta"], s["grad"], s["m"], s["v"]] for s in state])
+    hp = hp_args()
+    tree.adamw_step(*hp[:5], cfg.pop("t", hp[5]), **cfg)
+    torch.cuda.synchronize()
+    return tree
+
+
+@pytest.mark.parametrize("clip,schedule", [(0.05, "cosine"), (1e6, "linear"), (0.05, "constant")])
+def test_clip_and_schedule_tiny_bit_exact(clip, schedule):
+    shapes = [s for _, s in configs.tiny_gpt_leaves()]
+    state = configs.adamw_state(shapes, device=DEV, seed=31)
+    before = snapshot(state)
+    t, total, warmup = 37, 200, 20
+    tree = _run_config(state, t=t, total=total, warmup=warmup, schedule=schedule, grad_clip=clip)
+    lr = oracle.lr_schedule(schedule, HP["lr"], t, total, warmup)
+    ss = oracle.tree_sumsq([b["grad"] for b in before])
+    f = oracle.clip_factor(ss, clip)
+    gss, gf = tree.clip_result()
+    assert abs(gss - ss) <= GPU_SUMSQ_REL * ss
+    assert np.float32(gf) == f
+    assert (f < 1.0) == (clip < 1.0)
+    for i, (s, b) in enumerate(zip(state, before)):
+        rt, rm, rv = oracle.adamw_scaled(b["theta"], b["grad"], b["m"], b["v"], lr, HP["beta1"], HP["beta2"],
+                                         HP["eps"], HP["weight_decay"], t, f)
+        assert_bits(to_np(s["theta"]), rt, f"leaf {i} theta'")
+        assert_bits(to_np(s["m"]), rm, f"leaf {i} m'")
+        assert_bits(to_np(s["v"]), rv, f"leaf {i} v'")
+
+
+def test_clip_is_deterministic_and_repeatable():
+    shapes = [(4097,), (65536,), (3,), (1 << 20,)]
+    state = configs.adamw_state(shapes, device=DEV, seed=32)
+    tree = P.Tree([[s["theta"], s["grad"], s["m"], s["v"]] for s in state])
+    results = []
+    for _ in range(3):   # the gradient is not updated by the step, so the norm repeats
+        tree.adamw_step(*hp_args(), grad_clip=0.1)
+        torch.cuda.synchronize()
+        results.append(tree.clip_result())
+    assert results[0] == results[1] == results[2]
+
+
+def test_llama_tree_clipped_cosine_sampled():
+    shapes = [s for _, s in configs.llama_leaves()]
+    state = configs.adamw_state(shapes, theta_dtype=torch.bfloat16, grad_dtype=torch.bfloat16,
+                                mv_dtype=torch.float32, device=DEV, seed=configs.SEED_BASE + 2)
+    ss = oracle.tree_sumsq([to_np(s["grad"]) for s in state])       # every gradient element, f64
+    gen = torch.Generator(device="cpu").manual_seed(98)
+    idx = []
+    for s in state:
+        n = s["theta"].numel()
+        r = torch.randint(0, n, (2048,), generator=gen)
+        idx.append(torch.unique(torch.cat([torch.arange(32), torch.arange(n - 32, n), r])).to(DEV))
+    before = [{k: to_np(s[k][i]) for k in s} for s, i in zip(state, idx)]
+    t, total, warmup, clip = 10, 1000, 100, 1.0
+    tree = _run_config(state, t=t, total=total, warmup=warmup, schedule="cosine", grad_clip=clip)
+    gss, gf = tree.clip_result()
+    f = oracle.clip_factor(ss, clip)
+    assert abs(gss - ss) <= GPU_SUMSQ_REL * ss and np.float32(gf) == f and f < 1.0
+    lr = oracle.lr_schedule("cosine", HP["lr"], t, total, warmup)
+    for leaf, (s, i, b) in enumerate(zip(state, idx, before)):
+        rt, rm, rv = oracle.adamw_scaled(b["theta"], b["grad"], b["m"], b["v"], lr, HP["beta1"], HP["beta2"],
+                                         HP["eps"], HP["weight_decay"], t, f)
+        assert_bits(to_np(s["theta"][i]), rt, f"leaf {leaf} theta'")
+        assert_bits(to_np(s["m"][i]), rm, f"leaf {leaf} m'")
+        assert_bits(to_np(s["v"][i]), rv, f"leaf {leaf} v'")

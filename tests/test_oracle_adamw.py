@@ -135,3 +135,74 @@ def test_bf16_moments_are_rounded_before_theta_reads_them(orc):
     vh = vw / s[5]
     ref = th - s[6] * (mh / (np.sqrt(vh) + s[7]) + s[8] * th)
     np.testing.assert_array_equal(to.view(np.uint32), ref.astype(np.float32).view(np.uint32))
+
+
+# ------------------------------------------------- schedules and clipping
+def test_schedules_closed_forms(orc):
+    lr = 3e-4
+    assert orc.lr_schedule("constant", lr, 7, 100, 10) == lr
+    # warmup ramps linearly to lr at t = w, then decays to 0 at total
+    for kind in ("linear", "cosine"):
+        assert orc.lr_schedule(kind, lr, 5, 100, 10) == lr * 5 / 10
+        assert orc.lr_schedule(kind, lr, 10, 100, 10) == lr
+        assert abs(orc.lr_schedule(kind, lr, 100, 100, 10)) <= 1e-20
+    # linear: halfway through the decay is half of lr
+    assert abs(orc.lr_schedule("linear", lr, 55, 100, 10) - lr / 2) <= 1e-18
+    # cosine: halfway is lr/2; at t = 32, lr (1 + cos(pi 22/90))/2
+    assert abs(orc.lr_schedule("cosine", lr, 55, 100, 10) - lr / 2) <= 1e-18
+    assert abs(orc.lr_schedule("cosine", lr, 32, 100, 10) -
+               lr * 0.5 * (1 + math.cos(math.pi * 22 / 90))) <= 1e-18
+    # no warmup: the decay starts at t = 0
+    assert abs(orc.lr_schedule("linear", lr, 25, 100, 0) - lr * 0.75) <= 1e-18
+
+
+def test_tree_sumsq_and_clip(orc):
+    r = np.random.default_rng(8)
+    leaves = [(r.standard_normal(n) * 0.01).astype(np.float32) for n in (1000, 17, 4096)]
+    ss = orc.tree_sumsq(leaves)
+    # math.fsum is the correctly rounded sum of the exact squares
+    ref = math.fsum(float(x) ** 2 for g in leaves for x in g.astype(np.float64))
+    assert abs(ss - ref) <= 2 * 2.0 ** -53 * ref
+    # a long sum of small terms onto a large one, where plain summation stalls
+    big = [np.array([4096.0], np.float32), np.full(1 << 16, 2.0 ** -20, np.float32)]
+    assert orc.tree_sumsq(big) == 4096.0 ** 2 + (1 << 16) * 2.0 ** -40
+    # bf16 leaves are widened exactly
+    b = orc.bf16_round(leaves[0])
+    assert orc.tree_sumsq([b]) == pytest.approx(float(np.sum(orc.bf16_widen(b).astype(np.float64) ** 2)), rel=1e-13)
+    norm = math.sqrt(ref)
+    assert orc.clip_factor(ref, 1e9) == np.float32(1.0)               # no clipping needed
+    assert orc.clip_factor(ref, 0.5 * norm) == np.float32(0.5 * norm / (norm + 1e-6))
+
+
+def test_clipped_step_vs_torch(orc):
+    # clip_grad_norm_ over the whole tree, then AdamW: the pages define the
+    # step as PyTorch does (within tolerance: different operation order)
+    r = np.random.default_rng(9)
+    shapes = (3000, 257)
+    th = [(r.standard_normal(n) * 0.02).astype(np.float32) for n in shapes]
+    g = [(r.standard_normal(n) * 0.5).astype(np.float32) for n in shapes]
+    z = [np.zeros(n, np.float32) for n in shapes]
+    c, lr = 1.0, 1e-3
+    ss = orc.tree_sumsq(g)
+    f = orc.clip_factor(ss, c)
+    assert f < 1.0
+    outs = [orc.adamw_scaled(a, b, m, v, lr, 0.9, 0.999, 1e-8, 0.01, 1, f) for a, b, m, v in zip(th, g, z, z)]
+    ps = [torch.nn.Parameter(torch.from_numpy(a.copy())) for a in th]
+    for p, gg in zip(ps, g):
+        p.grad = torch.from_numpy(gg.copy())
+    torch.nn.utils.clip_grad_norm_(ps, c)
+    opt = torch.optim.AdamW(ps, lr=lr, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, foreach=False)
+    opt.step()
+    for (to, mo, vo), p in zip(outs, ps):
+        assert np.all(close(to, p.detach().numpy()))
+        assert np.all(close(mo, opt.state[p]["exp_avg"].numpy()))
+        assert np.all(close(vo, opt.state[p]["exp_avg_sq"].numpy()))
+
+
+def test_scale_one_is_the_plain_step(orc):
+    th, g, m, v = _state(5000, seed=10)
+    args = (HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["weight_decay"], HP["t"])
+    a = orc.adamw(th, g, m, v, *args)
+    b = orc.adamw_scaled(th, g, m, v, *args, 1.0)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x.view(np.uint32), y.view(np.uint32))
