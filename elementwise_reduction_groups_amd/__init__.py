@@ -24,6 +24,7 @@ for _i, _n in enumerate(STATUS_NAMES):
     globals()[_n] = _i
 
 PSK_F32, PSK_BF16 = 0, 1
+PSK_GROUP_TREE = 1
 PSK_MAX_RANK = 4
 PSK_MAX_SLOTS = 8
 PSK_TREE_CHUNK = 4096
@@ -104,7 +105,7 @@ _lib = None
 EXPORTED = ["psk_group_create", "psk_group_run", "psk_group_destroy", "psk_group_get_info", "psk_group_source",
             "psk_group_code_object", "psk_tree_create", "psk_tree_destroy", "psk_tree_get_info",
             "psk_tree_get_tables", "psk_tree_plan", "psk_adamw_step", "psk_adamw_step_config", "psk_adamw_lr",
-            "psk_tree_clip_result", "psk_partition", "psk_last_error",
+            "psk_tree_clip_result", "psk_group_run_tree", "psk_partition", "psk_last_error",
             "psk_status_str", "psk_version", "psk_get_stats"]
 
 
@@ -134,6 +135,7 @@ def lib() -> ctypes.CDLL:
     L.psk_adamw_step_config.argtypes = [vp, ctypes.POINTER(psk_adamw_config), vp]
     L.psk_adamw_lr.argtypes = [ctypes.POINTER(psk_adamw_config), ctypes.POINTER(ctypes.c_double)]
     L.psk_tree_clip_result.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_float)]
+    L.psk_group_run_tree.argtypes = [vp, vp, ctypes.POINTER(i32), i32, ctypes.POINTER(vp), vp]
     L.psk_partition.argtypes = [i32, ctypes.POINTER(psk_node), ctypes.POINTER(psk_tensor_desc),
                                 ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(i32), ctypes.POINTER(i32),
                                 ctypes.POINTER(i32)]
@@ -248,6 +250,17 @@ def psk_group_code_object(desc: GroupDesc) -> bytes:
     buf = ctypes.create_string_buffer(n.value)
     _check(lib().psk_group_code_object(ctypes.byref(desc.desc), buf, n.value, ctypes.byref(n)))
     return buf.raw[:n.value]
+
+
+def psk_group_run_tree(group: int, tree: int, in_slots: Sequence[int], out_slot: int,
+                       scalars: Sequence[int] = (), stream: Optional[int] = None):
+    """in_slots[k]: the tree slot of rank-1 input k; scalars[k]: the device
+    address of rank-0 input k (0 for rank-1 inputs)."""
+    n = max(len(in_slots), len(scalars), 1)
+    sl = (ctypes.c_int32 * n)(*[int(x) for x in list(in_slots) + [0] * (n - len(in_slots))])
+    sc = (ctypes.c_void_p * n)(*[ctypes.c_void_p(int(p)) for p in list(scalars) + [0] * (n - len(scalars))])
+    _check(lib().psk_group_run_tree(ctypes.c_void_p(group), ctypes.c_void_p(tree), sl, int(out_slot), sc,
+                                    ctypes.c_void_p(stream or 0)))
 
 
 def psk_tree_create(leaves: Sequence[Tuple[int, Sequence[int]]], slot_dtypes: Sequence) -> int:
@@ -370,8 +383,8 @@ def _stream_handle(stream) -> int:
 class Group:
     """A compiled fusion group, run on torch tensors."""
 
-    def __init__(self, nodes, inputs, out_shape, out_dtype, root=None):
-        self.desc = GroupDesc(nodes, inputs, out_shape, out_dtype, root=root)
+    def __init__(self, nodes, inputs, out_shape, out_dtype, root=None, tree=False):
+        self.desc = GroupDesc(nodes, inputs, out_shape, out_dtype, root=root, flags=PSK_GROUP_TREE if tree else 0)
         self.handle = psk_group_create(self.desc)
         self.out_shape = tuple(out_shape)
         self.out_dtype = out_dtype
@@ -387,6 +400,12 @@ class Group:
         psk_group_run(self.handle, [t.data_ptr() for t in inputs], out.data_ptr(), _stream_handle(stream))
         return out
 
+    def run_tree(self, tree: "Tree", in_slots, out_slot, scalars=(), stream=None):
+        """Map the group over every leaf of `tree` (one launch); scalars are
+        0-d device tensors (or None for per-element inputs)."""
+        ptrs = [0 if t is None else t.data_ptr() for t in scalars]
+        psk_group_run_tree(self.handle, tree.handle, in_slots, out_slot, ptrs, _stream_handle(stream))
+
     def __del__(self):
         h = getattr(self, "handle", None)
         if h and _lib is not None:
@@ -398,9 +417,10 @@ class Tree:
     """A parameter tree over torch tensors: slots theta, g, m, v (in place) or
     theta, g, m, v, theta', m', v'."""
 
-    def __init__(self, slots: Sequence[Sequence]):
+    def __init__(self, slots: Sequence[Sequence], n_slots: Optional[int] = None):
         self._keep = [list(s) for s in slots]       # keep the tensors alive
-        n_slots = len(self._keep[0]) if self._keep else 4
+        if n_slots is None:
+            n_slots = len(self._keep[0]) if self._keep else 4
         dts = [self._dt(t) for t in self._keep[0]] if self._keep else [PSK_F32] * n_slots
         leaves = []
         for s in self._keep:

@@ -43,44 +43,58 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b)
     return __builtin_bit_cast(unsigned, __builtin_convertvector(f, b2v));
 }
 
+// Slot addresses come out of a device-side table, so the compiler cannot
+// tell that they point to global memory and would use generic (flat)
+// accesses.  Every data access goes through these casts to the global
+// address space instead, which gives global loads and stores.
+#define PSK_GLOBAL __attribute__((address_space(1)))
+template <typename T> __device__ __forceinline__ const PSK_GLOBAL T* gbl(const void* p, int64_t e)
+{
+    return (const PSK_GLOBAL T*)p + e;   // address-space casts take the C form
+}
+template <typename T> __device__ __forceinline__ PSK_GLOBAL T* gbl(void* p, int64_t e)
+{
+    return (PSK_GLOBAL T*)p + e;
+}
+
 template <typename T> struct Io;
 
 template <> struct Io<float> {
     static __device__ __forceinline__ void load4(const void* p, int64_t e, float* x)
     {
-        u4v w = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(static_cast<const float*>(p) + e));
+        u4v w = __builtin_nontemporal_load((const PSK_GLOBAL u4v*)gbl<float>(p, e));
         x[0] = __uint_as_float(w[0]); x[1] = __uint_as_float(w[1]);
         x[2] = __uint_as_float(w[2]); x[3] = __uint_as_float(w[3]);
     }
-    static __device__ __forceinline__ float load1(const void* p, int64_t e) { return static_cast<const float*>(p)[e]; }
+    static __device__ __forceinline__ float load1(const void* p, int64_t e) { return *gbl<float>(p, e); }
     static __device__ __forceinline__ void store4(void* p, int64_t e, const float* x)
     {
         u4v w = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
-        __builtin_nontemporal_store(w, reinterpret_cast<u4v*>(static_cast<float*>(p) + e));
+        __builtin_nontemporal_store(w, (PSK_GLOBAL u4v*)gbl<float>(p, e));
     }
-    static __device__ __forceinline__ void store1(void* p, int64_t e, float x) { static_cast<float*>(p)[e] = x; }
+    static __device__ __forceinline__ void store1(void* p, int64_t e, float x) { *gbl<float>(p, e) = x; }
     static __device__ __forceinline__ float through(float x) { return x; }
 };
 
 template <> struct Io<__bf16> {
     static __device__ __forceinline__ void load4(const void* p, int64_t e, float* x)
     {
-        u2v w = __builtin_nontemporal_load(reinterpret_cast<const u2v*>(static_cast<const unsigned short*>(p) + e));
+        u2v w = __builtin_nontemporal_load((const PSK_GLOBAL u2v*)gbl<unsigned short>(p, e));
         x[0] = __uint_as_float(w[0] << 16); x[1] = __uint_as_float(w[0] & 0xffff0000u);
         x[2] = __uint_as_float(w[1] << 16); x[3] = __uint_as_float(w[1] & 0xffff0000u);
     }
     static __device__ __forceinline__ float load1(const void* p, int64_t e)
     {
-        return __uint_as_float(((unsigned)static_cast<const unsigned short*>(p)[e]) << 16);
+        return __uint_as_float(((unsigned)*gbl<unsigned short>(p, e)) << 16);
     }
     static __device__ __forceinline__ void store4(void* p, int64_t e, const float* x)
     {
         u2v w = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
-        __builtin_nontemporal_store(w, reinterpret_cast<u2v*>(static_cast<unsigned short*>(p) + e));
+        __builtin_nontemporal_store(w, (PSK_GLOBAL u2v*)gbl<unsigned short>(p, e));
     }
     static __device__ __forceinline__ void store1(void* p, int64_t e, float x)
     {
-        static_cast<unsigned short*>(p)[e] = (unsigned short)(pack_bf16(x, 0.0f) & 0xffffu);
+        *gbl<unsigned short>(p, e) = (unsigned short)(pack_bf16(x, 0.0f) & 0xffffu);
     }
     // the value a store leaves behind, read back
     static __device__ __forceinline__ float through(float x)

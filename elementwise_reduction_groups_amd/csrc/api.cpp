@@ -136,7 +136,7 @@ extern "C" psk_status psk_group_create(const psk_group_desc* desc, psk_group** o
     psk_status st = analyse(desc, g->an);
     if (st != PSK_OK) return st;
     KernelPlan p = plan_kernel(g->an, true);
-    if (p.grid > 0x7fffffffLL) return fail(PSK_E_UNSUPPORTED, "output too large for one launch");
+    if (!g->an.tree && p.grid > 0x7fffffffLL) return fail(PSK_E_UNSUPPORTED, "output too large for one launch");
     st = get_kernel(g->an, true, g->vec);
     if (st != PSK_OK) return st;
     if (g->vec->plan.vec == 1) g->scalar = g->vec;
@@ -174,6 +174,7 @@ extern "C" psk_status psk_group_run(const psk_group* group, const void* const* i
     clear_error();
     if (!group) return fail(PSK_E_NULL, "group is NULL");
     const Analysis& an = group->an;
+    if (an.tree) return fail(PSK_E_UNSUPPORTED, "a tree-mapped group runs with psk_group_run_tree");
     if (an.numel == 0) return PSK_OK;
     if (!out) return fail(PSK_E_NULL, "out is NULL");
     if (!an.inputs.empty() && !inputs) return fail(PSK_E_NULL, "inputs is NULL");
@@ -260,6 +261,14 @@ extern "C" psk_status psk_group_code_object(const psk_group_desc* desc, void* bu
 }
 
 // ------------------------------------------------------------------- trees
+namespace {
+// one slot buffer of one leaf: [b, e)
+struct Range {
+    uintptr_t b, e;
+    int32_t leaf, slot;
+};
+}  // namespace
+
 struct psk_tree {
     int32_t n_leaves = 0, n_slots = 0;
     int32_t dt[PSK_MAX_SLOTS] = {};
@@ -267,26 +276,22 @@ struct psk_tree {
     std::vector<LeafDev> leaves;
     std::vector<ChunkDev> chunks;
     LeafDev* d_leaves = nullptr;
+    GenLeafDev* d_gleaves = nullptr;  // every slot's address, for tree-mapped groups
     ChunkDev* d_chunks = nullptr;
     double* d_partials = nullptr;   // clipping: one partial sum of squares per chunk
     ClipOut* d_clip = nullptr;      // clipping: squared norm and factor
+    std::vector<Range> ranges;      // every slot buffer, sorted by start; equal ranges are adjacent
     int device = 0;
     int32_t vector_leaves = 0;
     ~psk_tree()
     {
         if (d_leaves) (void)hipFree(d_leaves);
+        if (d_gleaves) (void)hipFree(d_gleaves);
         if (d_chunks) (void)hipFree(d_chunks);
         if (d_partials) (void)hipFree(d_partials);
         if (d_clip) (void)hipFree(d_clip);
     }
 };
-
-namespace {
-struct Range {
-    uintptr_t b, e;
-    int32_t leaf, slot;
-};
-}  // namespace
 
 extern "C" psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, int32_t n_slots,
                                       const int32_t* slot_dtypes, psk_tree** out)
@@ -296,8 +301,8 @@ extern "C" psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, 
     *out = nullptr;
     if (n_leaves < 0) return fail(PSK_E_SHAPE, "negative leaf count");
     if (n_leaves > 0 && !leaves) return fail(PSK_E_NULL, "leaves is NULL");
-    if (n_slots != 4 && n_slots != 7)
-        return fail(PSK_E_SHAPE, "a tree has 4 slots (theta, g, m, v; in place) or 7 (plus theta', m', v')");
+    if (n_slots < 1 || n_slots > PSK_MAX_SLOTS) return fail(PSK_E_SHAPE, "a tree has 1 to 8 slots");
+    const bool adamw_roles = n_slots == 4 || n_slots == 7;
     if (!slot_dtypes) return fail(PSK_E_NULL, "slot_dtypes is NULL");
     auto t = std::make_unique<psk_tree>();
     t->n_leaves = n_leaves;
@@ -307,7 +312,7 @@ extern "C" psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, 
             return fail(PSK_E_TYPE, "slot " + std::to_string(s) + ": storage type must be f32 or bf16");
         t->dt[s] = slot_dtypes[s];
     }
-    if (t->dt[2] != t->dt[3]) return fail(PSK_E_TYPE, "m and v must share a storage type");
+    if (adamw_roles && t->dt[2] != t->dt[3]) return fail(PSK_E_TYPE, "m and v must share a storage type");
     if (n_slots == 7 && (t->dt[4] != t->dt[0] || t->dt[5] != t->dt[2] || t->dt[6] != t->dt[3]))
         return fail(PSK_E_TYPE, "an output slot must have its input's storage type");
     std::vector<int64_t> numel(n_leaves);
@@ -318,10 +323,12 @@ extern "C" psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, 
     const int out_slot[3] = {n_slots == 7 ? 4 : 0, n_slots == 7 ? 5 : 2, n_slots == 7 ? 6 : 3};
     std::vector<Range> ranges;
     t->leaves.resize(n_leaves);
+    std::vector<GenLeafDev> gleaves(n_leaves);
     for (int32_t l = 0; l < n_leaves; ++l) {
         const psk_leaf& lf = leaves[l];
         LeafDev& d = t->leaves[l];
         std::memset(&d, 0, sizeof d);
+        std::memset(&gleaves[l], 0, sizeof gleaves[l]);
         if (lf.numel == 0) continue;
         bool v16 = true;
         for (int s = 0; s < n_slots; ++s) {
@@ -333,9 +340,13 @@ extern "C" psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, 
             if (p % 16) v16 = false;
             ranges.push_back({p, p + (uintptr_t)lf.numel * esize(t->dt[s]), l, s});
         }
-        for (int s = 0; s < 4; ++s) d.in[s] = lf.slot[s];
-        for (int s = 0; s < 3; ++s) d.out[s] = lf.slot[out_slot[s]];
+        if (adamw_roles) {
+            for (int s = 0; s < 4; ++s) d.in[s] = lf.slot[s];
+            for (int s = 0; s < 3; ++s) d.out[s] = lf.slot[out_slot[s]];
+        }
         d.flags = v16 ? 1 : 0;
+        for (int s = 0; s < n_slots; ++s) gleaves[l].slot[s] = lf.slot[s];
+        gleaves[l].flags = v16 ? 1 : 0;
         t->vector_leaves += v16;
     }
     // aliasing: identical ranges are allowed only for an input and its own
@@ -346,6 +357,7 @@ extern "C" psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, 
     auto pair_ok = [&](const Range& x, const Range& y) {
         if (x.leaf != y.leaf) return false;
         int a = std::min(x.slot, y.slot), b = std::max(x.slot, y.slot);
+        if (!adamw_roles) return t->dt[a] == t->dt[b];   // one buffer in two slots of a leaf
         if (n_slots == 4) return false;   // in place: every slot is its own buffer
         return (a == 0 && b == 4) || (a == 2 && b == 5) || (a == 3 && b == 6);
     };
@@ -362,6 +374,7 @@ extern "C" psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, 
         }
         if (r.e > max_end) { max_end = r.e; prev = i; }
     }
+    t->ranges = ranges;
     const size_t nc = t->plan.chunk_leaf.size();
     t->chunks.resize(nc);
     for (size_t c = 0; c < nc; ++c)
@@ -372,6 +385,11 @@ extern "C" psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, 
         e = hipMalloc(&t->d_leaves, sizeof(LeafDev) * (size_t)n_leaves);
         if (e == hipSuccess)
             e = hipMemcpy(t->d_leaves, t->leaves.data(), sizeof(LeafDev) * (size_t)n_leaves, hipMemcpyHostToDevice);
+    }
+    if (e == hipSuccess && n_leaves > 0) {
+        e = hipMalloc(&t->d_gleaves, sizeof(GenLeafDev) * (size_t)n_leaves);
+        if (e == hipSuccess)
+            e = hipMemcpy(t->d_gleaves, gleaves.data(), sizeof(GenLeafDev) * (size_t)n_leaves, hipMemcpyHostToDevice);
     }
     if (e == hipSuccess && nc > 0) {
         e = hipMalloc(&t->d_chunks, sizeof(ChunkDev) * nc);
@@ -440,6 +458,8 @@ extern "C" psk_status psk_adamw_step(const psk_tree* tree, const psk_adamw_hp* h
     const double v[5] = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
     for (double x : v)
         if (!std::isfinite(x)) return fail(PSK_E_SHAPE, "hyperparameters must be finite");
+    if (tree->n_slots != 4 && tree->n_slots != 7)
+        return fail(PSK_E_SHAPE, "an AdamW tree has 4 slots (theta, g, m, v) or 7 (plus theta', m', v')");
     if (tree->chunks.empty()) return PSK_OK;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != tree->device)
@@ -484,6 +504,8 @@ extern "C" psk_status psk_adamw_step_config(const psk_tree* tree, const psk_adam
     double lr = 0.0;
     psk_status st = schedule_lr(cfg, &lr);
     if (st != PSK_OK) return st;
+    if (tree->n_slots != 4 && tree->n_slots != 7)
+        return fail(PSK_E_SHAPE, "an AdamW tree has 4 slots (theta, g, m, v) or 7 (plus theta', m', v')");
     if (tree->chunks.empty()) return PSK_OK;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != tree->device)
@@ -513,6 +535,73 @@ extern "C" psk_status psk_tree_clip_result(const psk_tree* tree, double* sumsq, 
     }
     if (sumsq) *sumsq = h.sumsq;
     if (factor) *factor = h.factor;
+    return PSK_OK;
+}
+
+// ------------------------------------------------------- tree-mapped groups
+extern "C" psk_status psk_group_run_tree(const psk_group* group, const psk_tree* tree, const int32_t* in_slot,
+                                         int32_t out_slot, const void* const* scalars, void* hip_stream)
+{
+    clear_error();
+    if (!group || !tree) return fail(PSK_E_NULL, "group or tree is NULL");
+    const Analysis& an = group->an;
+    if (!an.tree) return fail(PSK_E_UNSUPPORTED, "the group was not created with PSK_GROUP_TREE");
+    const int n_in = (int)an.inputs.size();
+    if (n_in > 0 && !in_slot) return fail(PSK_E_NULL, "in_slot is NULL");
+    if (out_slot < 0 || out_slot >= tree->n_slots) return fail(PSK_E_SHAPE, "out_slot out of range");
+    if (tree->dt[out_slot] != an.out_dtype)
+        return fail(PSK_E_TYPE, "the output slot's storage type is not the group's");
+    std::vector<int> slot_args(n_in + 1, 0);
+    std::vector<const void*> sc(n_in, nullptr);
+    for (int k = 0; k < n_in; ++k) {
+        const InputInfo& in = an.inputs[k];
+        if (!in.used) continue;
+        if (in.kind == InKind::Scalar) {
+            if (!scalars || !scalars[k]) return fail(PSK_E_NULL, "scalar input " + std::to_string(k) + " is NULL");
+            const uintptr_t a = reinterpret_cast<uintptr_t>(scalars[k]);
+            if (a % esize(in.dtype)) return fail(PSK_E_ALIGN, "scalar input " + std::to_string(k) + " is misaligned");
+            // every thread reads the scalar: it may not lie in a buffer the launch writes.  Ranges
+            // that hold a are identical (partial overlaps were refused), so they sit side by side
+            // just before the first range that starts after a.
+            auto it = std::upper_bound(tree->ranges.begin(), tree->ranges.end(), a,
+                                       [](uintptr_t x, const Range& r) { return x < r.b; });
+            while (it != tree->ranges.begin()) {
+                --it;
+                if (a >= it->e) break;
+                if (it->slot == out_slot)
+                    return fail(PSK_E_ALIAS, "scalar input " + std::to_string(k) + " lies in leaf " +
+                                                 std::to_string(it->leaf) + "'s output slot");
+            }
+            sc[k] = scalars[k];
+        } else {
+            const int s = in_slot[k];
+            if (s < 0 || s >= tree->n_slots) return fail(PSK_E_SHAPE, "in_slot out of range");
+            if (tree->dt[s] != in.dtype)
+                return fail(PSK_E_TYPE, "input " + std::to_string(k) + ": the slot's storage type is not the group's");
+            slot_args[k] = s;
+        }
+    }
+    slot_args[n_in] = out_slot;
+    if (tree->chunks.empty()) return PSK_OK;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != tree->device)
+        return fail(PSK_E_HIP, "the current device is not the device the tree was created on");
+    const int64_t n_virtual = (int64_t)tree->chunks.size() * kTreeSub;
+    const int64_t per = (n_virtual + 7) / 8;
+    if (per * 8 > 0x7fffffffLL) return fail(PSK_E_UNSUPPORTED, "tree too large for one launch");
+    hipFunction_t fn = nullptr;
+    psk_status st = kernel_function(*group->vec, fn);
+    if (st != PSK_OK) return st;
+    const void* lp = tree->d_gleaves;
+    const void* cp = tree->d_chunks;
+    unsigned nv = (unsigned)n_virtual, pv = (unsigned)per;
+    std::vector<void*> args = {&lp, &cp, &nv, &pv};
+    for (int k = 0; k <= n_in; ++k) args.push_back(&slot_args[k]);
+    for (int k = 0; k < n_in; ++k) args.push_back(&sc[k]);
+    hipError_t e = hipModuleLaunchKernel(fn, (unsigned)(per * 8), 1, 1, kTreeBlock, 1, 1, 0,
+                                         static_cast<hipStream_t>(hip_stream), args.data(), nullptr);
+    if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipModuleLaunchKernel: ") + hipGetErrorString(e));
+    count_launch();
     return PSK_OK;
 }
 

@@ -112,6 +112,16 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
     const int V = an.out_dtype == PSK_BF16 ? 8 : 4;
     p.vec = (allow_vector && an.cols % V == 0) ? V : 1;
     p.nt = layout_value("nt", 1) != 0;
+    if (an.tree) {
+        // one launch shape for every tree (the AdamW kernel's): workgroups of
+        // kTreeBlock threads, kTreePer elements each, XCD-contiguous mapping
+        p.kind = 2;
+        p.vec = kTreePer;
+        p.block = kTreeBlock;
+        p.nt = layout_value("nt", 1) != 0;
+        p.xcd = true;
+        return p;
+    }
     p.xcd = layout_value("xcd", an.row_kind ? 0 : 1) != 0;
     int block = layout_value("block", 256);
     if (block < 64 || block > 1024 || (block & (block - 1))) block = 256;
@@ -168,6 +178,23 @@ template <typename T> __device__ __forceinline__ T psk_ld(const T* p) {
 #endif
 }
 template <typename T> __device__ __forceinline__ void psk_st(T* p, T v) {
+#if PSK_NT
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+// the same for pointers named as global memory (addresses read from a
+// device table would otherwise be accessed through generic instructions)
+#define PSK_G __attribute__((address_space(1)))
+template <typename T> __device__ __forceinline__ T psk_ld(const PSK_G T* p) {
+#if PSK_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+template <typename T> __device__ __forceinline__ void psk_st(PSK_G T* p, T v) {
 #if PSK_NT
   __builtin_nontemporal_store(v, p);
 #else
@@ -260,7 +287,7 @@ struct Emitter {
 
     Emitter(const Analysis& a, const KernelPlan& p) : an(a), pl(p)
     {
-        NE = (pl.kind == 1 ? pl.nv : 1) * pl.vec;
+        NE = (pl.kind == 1 ? pl.nv : 1) * pl.vec;   // tree: kTreePer
         big = an.numel >= (int64_t(1) << 31) - 4096;
         for (auto& nd : an.nodes)
             if (nd.op == PSK_OP_CAUSAL_MASK) period = nd.iparam;
@@ -656,6 +683,84 @@ struct Emitter {
         return o.str();
     }
 
+    // ----------------------------------------------------------------- tree
+    // One workgroup per 512 elements of a chunk of the tree's chunk table;
+    // per-element inputs come from the leaf's slots, per-tree inputs from
+    // device scalars; the root goes to the output slot.
+    std::string tree(const std::string& name)
+    {
+        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n" << kPrelude;
+        o << "struct psk_leaf_dev { void* slot[" << PSK_MAX_SLOTS << "]; long long flags; };\n";
+        o << "struct psk_chunk_dev { int leaf; int count; long long start; };\n";
+        o << "extern \"C\" __global__ void __launch_bounds__(" << kTreeBlock << ") " << name
+          << "(const psk_leaf_dev* __restrict__ leaves, const psk_chunk_dev* __restrict__ chunks, "
+             "unsigned n_virtual, unsigned per_xcd";
+        for (size_t k = 0; k <= an.inputs.size(); ++k) o << ", int slot" << k;   // last: the output's
+        for (size_t k = 0; k < an.inputs.size(); ++k) o << ", const void* s" << k;
+        o << ")\n{\n";
+        o << "  const unsigned vb = (blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;\n";
+        o << "  if (vb >= n_virtual) return;\n";
+        o << "  const psk_chunk_dev ch = chunks[vb / " << kTreeSub << "u];\n";
+        o << "  const psk_leaf_dev* L = leaves + ch.leaf;\n";
+        o << "  const int i0 = ((int)(vb % " << kTreeSub << "u) * " << kTreeBlock << " + (int)threadIdx.x) * "
+          << kTreePer << ";\n";
+        o << "  const int cnt = ch.count - i0;\n";
+        o << "  if (cnt <= 0) return;\n";
+        o << "  const long long e0 = ch.start + i0;\n";
+        o << "  const bool full = (L->flags & 1) != 0 && cnt >= " << kTreePer << ";\n";
+        o << "  {\n";
+        // per-tree scalars and per-element inputs
+        for (size_t k = 0; k < an.inputs.size(); ++k) {
+            const InputInfo& in = an.inputs[k];
+            if (!in.used) continue;
+            std::string T = ptype(in.dtype);
+            if (in.kind == InKind::Scalar) {
+                std::string p = "(const " + T + "*)s" + std::to_string(k);
+                o << "    const float xr" << k << " = "
+                  << (in.dtype == PSK_BF16 ? "psk_h(*" + p + ")" : "*" + p) << ";\n";
+                continue;
+            }
+            o << "    const PSK_G " << T << "* in" << k << " = (const PSK_G " << T << "*)L->slot[slot" << k << "] + e0;\n";
+            const int nw = kTreePer * esize(in.dtype) / 4;   // 32-bit words of a full vector
+            std::string w = "w" + std::to_string(k);
+            o << "    unsigned " << w << "[" << nw << "];\n";
+            o << "    if (full) {\n";
+            if (nw == 4)
+                o << "      const psk_u4v t = psk_ld((const PSK_G psk_u4v*)in" << k << ");\n";
+            else
+                o << "      const psk_u2v t = psk_ld((const PSK_G psk_u2v*)in" << k << ");\n";
+            for (int q = 0; q < nw; ++q) o << "      " << w << "[" << q << "] = t[" << q << "];\n";
+            o << "    }\n";
+            for (int j = 0; j < kTreePer; ++j) {
+                o << "    const float x" << k << "_" << j << " = full ? ";
+                if (in.dtype == PSK_F32) o << "__uint_as_float(" << w << "[" << j << "])";
+                else o << (j % 2 == 0 ? "psk_lo(" : "psk_hi(") << w << "[" << j / 2 << "])";
+                o << " : (" << j << " < cnt ? " << (in.dtype == PSK_BF16 ? "psk_h(in" : "(in") << k << "[" << j
+                  << "]) : 0.0f);\n";
+            }
+        }
+        leaves();
+        members_at(0);
+        std::string T = ptype(an.out_dtype);
+        o << "    PSK_G " << T << "* out = (PSK_G " << T << "*)L->slot[slot" << an.inputs.size() << "] + e0;\n";
+        o << "    if (full) {\n";
+        if (an.out_dtype == PSK_F32) {
+            o << "      psk_st((PSK_G psk_u4v*)out, (psk_u4v){";
+            for (int j = 0; j < 4; ++j) o << (j ? ", " : "") << "__float_as_uint(" << val(an.root, j) << ")";
+            o << "});\n";
+        } else {
+            o << "      psk_st((PSK_G psk_u2v*)out, (psk_u2v){psk_pack2(" << val(an.root, 0) << ", " << val(an.root, 1)
+              << "), psk_pack2(" << val(an.root, 2) << ", " << val(an.root, 3) << ")});\n";
+        }
+        o << "    } else {\n";
+        for (int j = 0; j < kTreePer; ++j)
+            o << "      if (" << j << " < cnt) out[" << j << "] = "
+              << (an.out_dtype == PSK_BF16 ? "psk_r1(" + val(an.root, j) + ")" : val(an.root, j)) << ";\n";
+        o << "    }\n";
+        o << "  }\n}\n";
+        return o.str();
+    }
+
     // ------------------------------------------------------------------ row
     void reductions_at(int p)
     {
@@ -766,6 +871,7 @@ std::string emit_source(const Analysis& an, const KernelPlan& plan, const std::s
     std::string line;
     while (std::getline(ct, line)) hdr << "//   " << line << "\n";
     hdr << "// plan: " << plan.key() << "\n";
+    if (plan.kind == 2) return hdr.str() + em.tree(kernel_name);
     return hdr.str() + (plan.kind == 1 ? em.row(kernel_name) : em.pointwise(kernel_name));
 }
 

@@ -55,6 +55,7 @@ struct Analysis {
     int64_t out_shape4[PSK_MAX_RANK] = {1, 1, 1, 1};  // output right-aligned to 4 axes
     int64_t rows = 0, cols = 0, numel = 0;
     bool row_kind = false;              // has at least one row reduction
+    bool tree = false;                  // PSK_GROUP_TREE: mapped over tree leaves
     uint32_t flags = 0;
 };
 
@@ -70,7 +71,7 @@ const char* op_name(int op);
 
 // ------------------------------------------------------------------- emit
 struct KernelPlan {
-    int kind = 0;            // 0 pointwise, 1 row
+    int kind = 0;            // 0 pointwise, 1 row, 2 tree-mapped
     int vec = 1;             // elements per vector access
     int block = 256;         // threads per workgroup
     int lanes = 64;          // row kernel: lanes per row
@@ -130,7 +131,18 @@ struct ChunkDev {
     int32_t count;
     int64_t start;
 };
+// Device-side leaf descriptor of any tree: every slot's address.
+struct GenLeafDev {
+    void* slot[PSK_MAX_SLOTS];
+    int64_t flags;      // bit 0: every slot 16-byte aligned
+};
 static_assert(sizeof(LeafDev) == 64, "LeafDev layout");
+static_assert(sizeof(GenLeafDev) == 72, "GenLeafDev layout");
+// Launch shape of tree-mapped kernels (AdamW's): 128 threads, 4 elements each,
+// PSK_TREE_CHUNK / 512 workgroups per chunk.
+constexpr int kTreeBlock = 128;
+constexpr int kTreePer = 4;
+constexpr int kTreeSub = PSK_TREE_CHUNK / (kTreeBlock * kTreePer);
 static_assert(sizeof(ChunkDev) == 16, "ChunkDev layout");
 
 // Result of a tree-wide clipping pass, in device memory owned by the tree.

@@ -87,8 +87,8 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
         return fail(PSK_E_NULL, "inputs is NULL");
     if (desc->arith != PSK_F32)
         return fail(PSK_E_TYPE, "the arithmetic type must be f32 (bf16 is storage only)");
-    if (desc->flags != 0)
-        return fail(PSK_E_UNSUPPORTED, "flags must be 0");
+    if (desc->flags & ~PSK_GROUP_TREE)
+        return fail(PSK_E_UNSUPPORTED, "unknown flags");
 
     // ---- output
     const psk_tensor_desc& o = desc->out;
@@ -117,6 +117,9 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
         InputInfo& in = an.inputs[k];
         if (t.rank < 0 || t.rank > PSK_MAX_RANK)
             return fail(PSK_E_SHAPE, "input " + std::to_string(k) + ": rank must be in 0..4");
+        if ((desc->flags & PSK_GROUP_TREE) && (t.rank > 1 || o.rank != 1))
+            return fail(PSK_E_SHAPE, "a tree-mapped group has a rank-1 output and inputs of rank 1 (per "
+                                     "element) or 0 (per tree)");
         if (t.rank > o.rank)
             return fail(PSK_E_BROADCAST, "input " + std::to_string(k) + ": rank above the output's");
         if (!dtype_ok(t.dtype))
@@ -130,6 +133,14 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
             in.shape[d] = t.shape[d];
             in.aligned[PSK_MAX_RANK - t.rank + d] = t.shape[d];
             in.numel *= t.shape[d];
+        }
+        if (desc->flags & PSK_GROUP_TREE) {
+            // leaf-mapped: rank 1 is one element per leaf element, rank 0 one
+            // value for the whole tree; lengths are the leaves'
+            if (t.rank > 1)
+                return fail(PSK_E_SHAPE, "a tree-mapped group's inputs have rank 1 (per element) or 0 (per tree)");
+            in.kind = t.rank == 0 ? InKind::Scalar : InKind::Full;
+            continue;
         }
         bool all1 = true, lead1 = true, same = true;
         for (int d = 0; d < PSK_MAX_RANK; ++d) {
@@ -248,6 +259,18 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
         an.depth[i] = dep;
     }
     an.row_kind = an.n_reductions > 0;
+    an.flags = desc->flags;
+    an.tree = (desc->flags & PSK_GROUP_TREE) != 0;
+    if (an.tree) {
+        if (an.out_rank != 1) return fail(PSK_E_SHAPE, "a tree-mapped group has a rank-1 output");
+        for (int k = 0; k < desc->n_inputs; ++k)
+            if (desc->inputs[k].rank > 1)
+                return fail(PSK_E_SHAPE, "a tree-mapped group's inputs have rank 1 (per element) or 0 (per tree)");
+        if (an.row_kind) return fail(PSK_E_ROW, "a tree-mapped group has no row reduction");
+        for (int i = 0; i < n; ++i)
+            if (an.nodes[i].op == PSK_OP_CAUSAL_MASK)
+                return fail(PSK_E_OP, at(i) + "a tree-mapped group has no rows for a causal mask");
+    }
     an.phases = an.depth[an.root];
     if (an.is_row[an.root] && an.cols > 1)
         return fail(PSK_E_ROW, "the root is one value per row but the output has " + std::to_string(an.cols) +

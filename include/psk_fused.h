@@ -150,8 +150,14 @@ typedef struct psk_group_desc {
     const psk_tensor_desc* inputs;
     psk_tensor_desc out;             /* the root's storage type and shape */
     int32_t arith;                   /* arithmetic type: must be PSK_F32 */
-    uint32_t flags;                  /* reserved, must be 0 */
+    uint32_t flags;                  /* 0, or PSK_GROUP_TREE */
 } psk_group_desc;
+
+/* A group mapped over the leaves of a parameter tree (psk_group_run_tree):
+ * output rank 1, every input rank 1 (one element per leaf element) or rank 0
+ * (one value for the whole tree); shape lengths are not used, each leaf has
+ * its own; no row reductions and no causal mask. */
+#define PSK_GROUP_TREE 1u
 
 typedef struct psk_group psk_group;
 typedef struct psk_tree psk_tree;
@@ -178,7 +184,7 @@ void psk_group_destroy(psk_group* group);
 
 /* Kernel shape chosen for a group (for tests and measurement). */
 typedef struct psk_group_info {
-    int32_t kind;            /* 0 pointwise, 1 row */
+    int32_t kind;            /* 0 pointwise, 1 row, 2 tree-mapped */
     int32_t members;         /* member count */
     int32_t n_reductions;    /* row reductions */
     int32_t phases;          /* reduction phases (longest chain of dependent reductions) */
@@ -214,9 +220,13 @@ typedef struct psk_leaf {
  * into chunks of PSK_TREE_CHUNK elements (the last one shorter); chunk
  * starts are multiples of 8 elements within a leaf, so 16-byte vector
  * accesses stay inside one leaf.  The tables are uploaded to the current
- * device once.  Slot dtypes apply to every leaf.  Refuses: NULL pointers of
- * non-empty leaves, negative numel, misaligned pointers, outputs partially
- * overlapping inputs or other leaves' outputs (PSK_E_ALIAS). */
+ * device once.  Slot dtypes apply to every leaf; 1 to 8 slots.  A tree of 4
+ * or 7 slots has AdamW's slot roles (theta, g, m, v [, theta', m', v']): its
+ * slots are distinct buffers, except that an output may be the same buffer as
+ * its own input.  Other trees may repeat a buffer across slots of one leaf
+ * (same storage type) but never overlap partly.  Refuses: NULL pointers of
+ * non-empty leaves, negative numel, misaligned pointers, overlaps as above
+ * (PSK_E_ALIAS). */
 #define PSK_TREE_CHUNK 4096
 psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, int32_t n_slots,
                            const int32_t* slot_dtypes, psk_tree** out);
@@ -295,6 +305,23 @@ psk_status psk_adamw_lr(const psk_adamw_config* cfg, double* lr);
 /* The squared global norm and the f32 factor of the last clipped step on
  * this tree (synchronises the device).  For checks and reporting. */
 psk_status psk_tree_clip_result(const psk_tree* tree, double* sumsq, float* factor);
+
+/* Run a PSK_GROUP_TREE group over every leaf of a tree in one launch
+ * (PSK-Realize, "What a group is", parameter trees: the chain is mapped over
+ * the leaves).  Input k of rank 1 reads slot in_slot[k] of each leaf; input
+ * k of rank 0 reads the device address scalars[k] (one f32 or bf16 value
+ * shared by every leaf; in_slot[k] is ignored).  The root is written, rounded
+ * to the output storage type, to slot out_slot of each leaf.  Slot storage
+ * types must equal the group's (PSK_E_TYPE); slots out of range give
+ * PSK_E_SHAPE, a NULL or misaligned scalar PSK_E_NULL / PSK_E_ALIGN, and a
+ * scalar that lies inside an output-slot buffer PSK_E_ALIAS.  out_slot may
+ * equal an input's slot (in place: each element is read before it is
+ * written, by the same thread); other overlaps were refused when the tree
+ * was created.  The tree must have been created on the current device.
+ * Leaves whose slots are all 16-byte aligned take 8/16-byte accesses; a
+ * tree with no elements launches nothing.  Buffers stay the caller's. */
+psk_status psk_group_run_tree(const psk_group* group, const psk_tree* tree, const int32_t* in_slot, int32_t out_slot,
+                              const void* const* scalars, void* hip_stream);
 
 /* --------------------------------------------------------------- partition */
 /* Partition a function body (a let-list of n nodes, leaves included) into

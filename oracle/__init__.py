@@ -158,6 +158,24 @@ def eval_group(nodes, inputs: Sequence[np.ndarray], out_shape: Sequence[int], ou
     return out
 
 
+# ---------------------------------------------------- tree-mapped groups
+def tree_map_group(nodes, leaves: Sequence[Sequence[Optional[np.ndarray]]],
+                   scalars: Sequence[Optional[np.ndarray]], out_dtype: int = F32,
+                   root: Optional[int] = None) -> List[np.ndarray]:
+    """A group mapped over the leaves of a parameter tree (PSK-Realize, "What
+    a group is", parameter trees): each leaf's result is the group evaluated
+    on that leaf alone, its rank-1 inputs taken from the leaf and its rank-0
+    inputs shared by every leaf.  ``leaves[l][k]`` is input k of leaf l (1-D;
+    ignored where ``scalars[k]`` is given), ``scalars[k]`` a 0-d array."""
+    outs = []
+    for leaf in leaves:
+        ins = [np.asarray(scalars[k]) if scalars[k] is not None else leaf[k] for k in range(len(scalars))]
+        n = next(x.size for k, x in enumerate(leaf) if scalars[k] is None)
+        outs.append(eval_group(nodes, ins, (n,), out_dtype, root=root) if n else
+                    np.zeros(0, np.float32 if out_dtype == F32 else np.uint16))
+    return outs
+
+
 # ----------------------------------------------------------------- AdamW
 def adamw_scalars(lr, beta1, beta2, eps, weight_decay, t) -> np.ndarray:
     s = np.zeros(9, np.float32)

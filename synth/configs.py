@@ -172,3 +172,45 @@ def chain64_dag() -> List[Node]:
     """The accepted 64-node chain (written by tests/golden/make_chain64_dag.py)."""
     with open(CHAIN64_PATH) as f:
         return parse_dag(f.read())
+
+
+# ---------------------------------------------------------------------------
+# Groups mapped over a parameter tree (one value per leaf element; rank-0
+# inputs are one value for the whole tree).
+def tree_sgd_dag() -> List[Node]:
+    """theta' = theta - lr * g; input 2 (lr) is rank 0."""
+    return parse_dag("""
+        %0 = input 0
+        %1 = input 1
+        %2 = input 2
+        %3 = mul %2 %1
+        %4 = sub %0 %3
+    """)
+
+
+def tree_mixed_dag() -> List[Node]:
+    """tanh(x) * exp(-|y|) + gelu(x) * s, with s rank 0: transcendental
+    members, a bf16 and an f32 per-element input."""
+    return parse_dag("""
+        %0 = input 0
+        %1 = input 1
+        %2 = input 2
+        %3 = tanh %0
+        %4 = abs %1
+        %5 = neg %4
+        %6 = exp %5
+        %7 = mul %3 %6
+        %8 = gelu %0
+        %9 = mul %8 %2
+        %10 = add %7 %9
+    """)
+
+
+def tree_leaf_values(shapes: Sequence[Sequence[int]], dtype, device="cpu", seed: int = SEED_BASE + 5,
+                     std: float = 1.0) -> List[torch.Tensor]:
+    """One normal(0, std) tensor per leaf shape, in the given storage type."""
+    out = []
+    for i, s in enumerate(shapes):
+        g = _gen("cpu", seed, i)
+        out.append((torch.randn(numel(s), generator=g) * std).to(dtype).to(device))
+    return out

@@ -99,7 +99,46 @@ def test_refusals(lib):
     # negative sizes, rank out of range
     _refused(_desc("%0 = input 0\n%1 = exp %0\n", [((8, 16), "f32")], (8, -16)), P.PSK_E_SHAPE)
     # reserved flags
-    _refused(_desc("%0 = input 0\n%1 = exp %0\n", F, (8, 16), flags=1), P.PSK_E_UNSUPPORTED)
+    _refused(_desc("%0 = input 0\n%1 = exp %0\n", F, (8, 16), flags=2), P.PSK_E_UNSUPPORTED)
+
+
+T1 = [((1,), "f32")]
+
+
+def test_tree_group_refusals(lib):
+    tree = dict(flags=P.PSK_GROUP_TREE)
+    # the output and every input are per element (rank 1) or per tree (rank 0)
+    _refused(_desc("%0 = input 0\n%1 = exp %0\n", T1, (8, 16), **tree), P.PSK_E_SHAPE)
+    _refused(_desc("%0 = input 0\n%1 = exp %0\n", [((8, 16), "f32")], (1,), **tree), P.PSK_E_SHAPE)
+    # no rows: no row reduction, no causal mask
+    _refused(_desc("%0 = input 0\n%1 = row_max %0\n%2 = sub %0 %1\n", T1, (1,), **tree), P.PSK_E_ROW)
+    _refused(_desc("%0 = input 0\n%1 = causal_mask %0 4\n", T1, (1,), **tree), P.PSK_E_OP)
+    # the usual group rules still hold
+    chain = "%0 = input 0\n" + "".join(f"%{i + 1} = exp %{i}\n" for i in range(65))
+    _refused(_desc(chain, T1, (1,), **tree), P.PSK_E_CAP)
+    _refused(_desc("%0 = input 0\n%1 = exp %0\n", T1, (1,), arith=P.PSK_BF16, **tree), P.PSK_E_TYPE)
+    # accepted: rank-1 output, rank-1 and rank-0 inputs of either storage type
+    g = P.psk_group_create(_desc("%0 = input 0\n%1 = input 1\n%2 = mul %0 %1\n",
+                                 [((1,), "bf16"), ((), "f32")], (1,), "bf16", **tree))
+    info = P.psk_group_get_info(g)
+    assert info.kind == 2 and info.members == 1
+    P.psk_group_destroy(g)
+
+
+def test_tree_group_kernel_compiles(lib, tmp_path):
+    from synth import configs as C
+    desc = P.GroupDesc(C.tree_mixed_dag(), [((1,), "f32"), ((1,), "bf16"), ((), "f32")], (1,), "bf16",
+                       flags=P.PSK_GROUP_TREE)
+    src = P.psk_group_source(desc)
+    # slot addresses are read from the leaf table and named as global memory
+    assert "L->slot[slot0]" in src and "L->slot[slot1]" in src and "L->slot[slot3]" in src
+    assert "L->slot[slot2]" not in src and "PSK_G" in src   # input 2 is a rank-0 scalar
+    asm, notes = _isa(P.psk_group_code_object(desc), tmp_path, "tree")
+    assert not re.search(r"v_pk_(fma|mul|add)_f32", asm)
+    assert re.search(r"\.private_segment_fixed_size:\s+0\b", notes)
+    # global (not generic) accesses: 16-byte f32 and 8-byte bf16 vectors
+    assert "global_load_dwordx4" in asm and "global_load_dwordx2" in asm and "global_store_dwordx2" in asm
+    assert not re.search(r"\bflat_(load|store)", asm)
 
 
 def test_group_create_needs_no_gpu(lib):
@@ -179,9 +218,18 @@ def test_tree_plan(lib):
 
 def test_tree_refusals_without_device(lib):
     # refusals are decided before any device call
+    for n_slots in (0, 9):   # 1 to 8 slots
+        with pytest.raises(P.PskError) as ei:
+            P.psk_tree_create([(8, [16 * (k + 1) for k in range(min(n_slots, 8))])], ["f32"] * n_slots)
+        assert ei.value.status == P.PSK_E_SHAPE
+    # slots of a generic tree: partial overlaps are refused, and so is one
+    # buffer in two slots of different storage types
     with pytest.raises(P.PskError) as ei:
         P.psk_tree_create([(8, [16, 32, 48])], ["f32"] * 3)
-    assert ei.value.status == P.PSK_E_SHAPE
+    assert ei.value.status == P.PSK_E_ALIAS
+    with pytest.raises(P.PskError) as ei:
+        P.psk_tree_create([(8, [1024, 1024, 4096])], ["f32", "bf16", "f32"])
+    assert ei.value.status == P.PSK_E_ALIAS
     with pytest.raises(P.PskError) as ei:
         P.psk_tree_create([(8, [16, 0, 64, 96])], ["f32"] * 4)
     assert ei.value.status == P.PSK_E_NULL
