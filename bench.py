@@ -170,14 +170,14 @@ def main():
         result["roofline"]["traffic"] = traffic
     if args.profile_step:
         if args.profile_all:
-            profile_others(P, configs, torch, dev, stream, hp)
+            profile_others(P, configs, torch, dev, stream, hp, state)
         print(json.dumps(result), flush=True)
         return
 
     # ----------------------------------------------------- per-group timing
     if not args.no_groups:
         result["groups"] = time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, probs,
-                                       adamw_bytes, softmax_bytes, hp)
+                                       adamw_bytes, softmax_bytes, hp, state)
 
     # ------------------------------------------------------------ CPU leg
     if not args.no_cpu_baseline:
@@ -218,7 +218,15 @@ def committed_traffic():
         return None
 
 
-def profile_others(P, configs, torch, dev, stream, hp):
+def tree_sgd(P, configs, torch, dev, state):
+    """theta' = theta - lr * g as a generic tree-mapped group over the theta
+    and g buffers of the Llama tree (in place; 6 bytes per parameter)."""
+    tree = P.Tree([[s["theta"], s["grad"]] for s in state])
+    group = P.Group(configs.tree_sgd_dag(), [((1,), "bf16"), ((1,), "bf16"), ((), "f32")], (1,), "bf16", tree=True)
+    return tree, group, torch.tensor(1e-4, dtype=torch.float32, device=dev)
+
+
+def profile_others(P, configs, torch, dev, stream, hp, state):
     tiny_shapes = [s for _, s in configs.tiny_gpt_leaves()]
     tiny = configs.adamw_state(tiny_shapes, device=dev, seed=configs.SEED_BASE)
     tiny_tree = P.Tree([[s["theta"], s["grad"], s["m"], s["v"]] for s in tiny])
@@ -230,15 +238,18 @@ def profile_others(P, configs, torch, dev, stream, hp):
     Z = torch.empty_like(A)
     chain = P.Group(configs.chain64_dag(), [((16384, 16384), "f32"), ((16384, 1), "f32"), ((1, 16384), "f32")],
                     (16384, 16384), "f32")
+    sgd_tree, sgd, lr = tree_sgd(P, configs, torch, dev, state)
     torch.cuda.synchronize()
     for _ in range(2):
+        sgd.run_tree(sgd_tree, [0, 1, -1], 0, [None, None, lr], stream=stream)
         tiny_tree.adamw_step(*hp, stream=stream)
         rms.run([x, r, g], y, stream=stream)
         chain.run([A, B, Cc], Z, stream=stream)
     torch.cuda.synchronize()
 
 
-def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, probs, adamw_bytes, softmax_bytes, hp):
+def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, probs, adamw_bytes, softmax_bytes, hp,
+                state):
     """Each workload alone: a 1 GiB write between calls evicts the 256 MB
     last-level cache; HIP events around each call; median of --reps."""
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -275,6 +286,12 @@ def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, pro
     add("adamw_llama_bf16_clip_cosine", adamw_bytes + 2 * n_params,
         lambda: tree.adamw_step(*hp, stream=stream, total=1000, warmup=100, schedule="cosine", grad_clip=1.0),
         note="three launches: per-chunk sums of squares (f64), a one-workgroup combine, the clipped step")
+
+    # a generic group mapped over the same tree: plain SGD on theta (bf16)
+    sgd_tree, sgd, lr = tree_sgd(P, configs, torch, dev, state)
+    add("tree_sgd_llama_bf16", 6 * n_params, lambda: sgd.run_tree(sgd_tree, [0, 1, -1], 0, [None, None, lr],
+                                                                   stream=stream),
+        note="emitted tree-mapped group: theta' = theta - lr * g, lr a device scalar")
 
     # tiny GPT tree, f32
     tiny_shapes = [s for _, s in configs.tiny_gpt_leaves()]

@@ -83,7 +83,8 @@ static psk_status get_kernel(const Analysis& an, bool vector, std::shared_ptr<Ke
     auto k = std::make_shared<Kernel>();
     k->plan = plan;
     char nm[64];
-    std::snprintf(nm, sizeof nm, "psk_%s_%016llx", plan.kind ? "row" : "pw", (unsigned long long)fnv1a(key));
+    static const char* const kind_name[3] = {"pw", "row", "tree"};
+    std::snprintf(nm, sizeof nm, "psk_%s_%016llx", kind_name[plan.kind], (unsigned long long)fnv1a(key));
     k->name = nm;
     std::string src = emit_source(an, plan, k->name);
     psk_status st = jit_compile(src, k->name, k->code);
@@ -586,7 +587,8 @@ extern "C" psk_status psk_group_run_tree(const psk_group* group, const psk_tree*
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != tree->device)
         return fail(PSK_E_HIP, "the current device is not the device the tree was created on");
-    const int64_t n_virtual = (int64_t)tree->chunks.size() * kTreeSub;
+    const KernelPlan& kp = group->vec->plan;   // kp.blocks workgroups of kp.block threads per chunk
+    const int64_t n_virtual = (int64_t)tree->chunks.size() * kp.blocks;
     const int64_t per = (n_virtual + 7) / 8;
     if (per * 8 > 0x7fffffffLL) return fail(PSK_E_UNSUPPORTED, "tree too large for one launch");
     hipFunction_t fn = nullptr;
@@ -598,7 +600,7 @@ extern "C" psk_status psk_group_run_tree(const psk_group* group, const psk_tree*
     std::vector<void*> args = {&lp, &cp, &nv, &pv};
     for (int k = 0; k <= n_in; ++k) args.push_back(&slot_args[k]);
     for (int k = 0; k < n_in; ++k) args.push_back(&sc[k]);
-    hipError_t e = hipModuleLaunchKernel(fn, (unsigned)(per * 8), 1, 1, kTreeBlock, 1, 1, 0,
+    hipError_t e = hipModuleLaunchKernel(fn, (unsigned)(per * 8), 1, 1, (unsigned)kp.block, 1, 1, 0,
                                          static_cast<hipStream_t>(hip_stream), args.data(), nullptr);
     if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipModuleLaunchKernel: ") + hipGetErrorString(e));
     count_launch();

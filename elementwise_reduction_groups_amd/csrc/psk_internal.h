@@ -138,8 +138,9 @@ struct GenLeafDev {
 };
 static_assert(sizeof(LeafDev) == 64, "LeafDev layout");
 static_assert(sizeof(GenLeafDev) == 72, "GenLeafDev layout");
-// Launch shape of tree-mapped kernels (AdamW's): 128 threads, 4 elements each,
-// PSK_TREE_CHUNK / 512 workgroups per chunk.
+// Launch shape of the AdamW tree kernel: 128 threads, 4 elements each,
+// PSK_TREE_CHUNK / 512 workgroups per chunk.  Emitted tree-mapped groups
+// choose their own (KernelPlan: block threads, vec elements per thread).
 constexpr int kTreeBlock = 128;
 constexpr int kTreePer = 4;
 constexpr int kTreeSub = PSK_TREE_CHUNK / (kTreeBlock * kTreePer);

@@ -136,9 +136,18 @@ def test_tree_group_kernel_compiles(lib, tmp_path):
     asm, notes = _isa(P.psk_group_code_object(desc), tmp_path, "tree")
     assert not re.search(r"v_pk_(fma|mul|add)_f32", asm)
     assert re.search(r"\.private_segment_fixed_size:\s+0\b", notes)
-    # global (not generic) accesses: 16-byte f32 and 8-byte bf16 vectors
-    assert "global_load_dwordx4" in asm and "global_load_dwordx2" in asm and "global_store_dwordx2" in asm
+    # global (not generic) accesses, 16-byte vectors: 10 bytes per element
+    # gives 8 elements per thread (two f32 vectors, one bf16 vector each)
+    assert "global_load_dwordx4" in asm and "global_store_dwordx4" in asm
     assert not re.search(r"\bflat_(load|store)", asm)
+    g = P.psk_group_create(desc)
+    assert P.psk_group_get_info(g).vec == 8
+    P.psk_group_destroy(g)
+    # an SGD step moves 6 bytes per element: 8 elements per thread
+    g = P.psk_group_create(P.GroupDesc(C.tree_sgd_dag(), [((1,), "bf16"), ((1,), "bf16"), ((), "f32")], (1,),
+                                       "bf16", flags=P.PSK_GROUP_TREE))
+    assert P.psk_group_get_info(g).vec == 8
+    P.psk_group_destroy(g)
 
 
 def test_group_create_needs_no_gpu(lib):
