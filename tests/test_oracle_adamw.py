@@ -206,3 +206,14 @@ def test_scale_one_is_the_plain_step(orc):
     b = orc.adamw_scaled(th, g, m, v, *args, 1.0)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+def test_scaled_step_is_the_plain_step_on_the_scaled_gradient(orc):
+    # the factor multiplies each gradient element once, in f32, before the moments
+    th, g, m, v = _state(5000, seed=11)
+    args = (HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["weight_decay"], HP["t"])
+    f = np.float32(0.3713)
+    a = orc.adamw_scaled(th, g, m, v, *args, f)
+    b = orc.adamw(th, (g * f).astype(np.float32), m, v, *args)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x.view(np.uint32), y.view(np.uint32))
