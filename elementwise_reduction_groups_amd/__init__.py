@@ -60,7 +60,9 @@ class psk_tensor_desc(ctypes.Structure):
 class psk_group_desc(ctypes.Structure):
     _fields_ = [("n_nodes", ctypes.c_int32), ("nodes", ctypes.POINTER(psk_node)), ("root", ctypes.c_int32),
                 ("n_inputs", ctypes.c_int32), ("inputs", ctypes.POINTER(psk_tensor_desc)),
-                ("out", psk_tensor_desc), ("arith", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("out", psk_tensor_desc), ("arith", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("n_extra", ctypes.c_int32), ("extra_root", ctypes.POINTER(ctypes.c_int32)),
+                ("extra_out", ctypes.POINTER(psk_tensor_desc))]
 
 
 class psk_group_info(ctypes.Structure):
@@ -105,7 +107,8 @@ _lib = None
 EXPORTED = ["psk_group_create", "psk_group_run", "psk_group_destroy", "psk_group_get_info", "psk_group_source",
             "psk_group_code_object", "psk_tree_create", "psk_tree_destroy", "psk_tree_get_info",
             "psk_tree_get_tables", "psk_tree_plan", "psk_adamw_step", "psk_adamw_step_config", "psk_adamw_lr",
-            "psk_tree_clip_result", "psk_group_run_tree", "psk_partition", "psk_last_error",
+            "psk_tree_clip_result", "psk_group_run_tree", "psk_group_run_multi", "psk_group_run_tree_multi",
+            "psk_partition", "psk_last_error",
             "psk_status_str", "psk_version", "psk_get_stats"]
 
 
@@ -136,6 +139,8 @@ def lib() -> ctypes.CDLL:
     L.psk_adamw_lr.argtypes = [ctypes.POINTER(psk_adamw_config), ctypes.POINTER(ctypes.c_double)]
     L.psk_tree_clip_result.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_float)]
     L.psk_group_run_tree.argtypes = [vp, vp, ctypes.POINTER(i32), i32, ctypes.POINTER(vp), vp]
+    L.psk_group_run_multi.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp]
+    L.psk_group_run_tree_multi.argtypes = [vp, vp, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(vp), vp]
     L.psk_partition.argtypes = [i32, ctypes.POINTER(psk_node), ctypes.POINTER(psk_tensor_desc),
                                 ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(i32), ctypes.POINTER(i32),
                                 ctypes.POINTER(i32)]
@@ -199,7 +204,9 @@ class GroupDesc:
     """Keeps a psk_group_desc and the arrays it points to alive."""
 
     def __init__(self, nodes, inputs: Sequence[Tuple[Sequence[int], object]], out_shape: Sequence[int], out_dtype,
-                 root: Optional[int] = None, arith=PSK_F32, flags: int = 0):
+                 root: Optional[int] = None, arith=PSK_F32, flags: int = 0,
+                 extras: Sequence[Tuple[int, Sequence[int], object]] = ()):
+        """extras: (node index, shape, storage type) of each further stored value."""
         self._nodes = node_array(nodes)
         self._inputs = (psk_tensor_desc * max(1, len(inputs)))(*[tensor_desc(s, d) for s, d in inputs])
         self.desc = psk_group_desc()
@@ -211,6 +218,11 @@ class GroupDesc:
         self.desc.out = tensor_desc(out_shape, out_dtype)
         self.desc.arith = _dtype_code(arith)
         self.desc.flags = flags
+        self._extra_root = (ctypes.c_int32 * max(1, len(extras)))(*[int(n) for n, _, _ in extras])
+        self._extra_out = (psk_tensor_desc * max(1, len(extras)))(*[tensor_desc(sh, d) for _, sh, d in extras])
+        self.desc.n_extra = len(extras)
+        self.desc.extra_root = self._extra_root
+        self.desc.extra_out = self._extra_out
 
 
 # ------------------------------------------------------------ C functions
@@ -224,6 +236,13 @@ def psk_group_run(group: int, inputs: Sequence[int], out: int, stream: Optional[
     """inputs/out are device addresses (ints)."""
     arr = (ctypes.c_void_p * max(1, len(inputs)))(*[ctypes.c_void_p(p) for p in inputs])
     _check(lib().psk_group_run(ctypes.c_void_p(group), arr, ctypes.c_void_p(out), ctypes.c_void_p(stream or 0)))
+
+
+def psk_group_run_multi(group: int, inputs: Sequence[int], outs: Sequence[int], stream: Optional[int] = None):
+    """outs[0]: the root's output, outs[1 + k]: extra output k (device addresses)."""
+    arr = (ctypes.c_void_p * max(1, len(inputs)))(*[ctypes.c_void_p(p) for p in inputs])
+    oa = (ctypes.c_void_p * len(outs))(*[ctypes.c_void_p(p) for p in outs])
+    _check(lib().psk_group_run_multi(ctypes.c_void_p(group), arr, oa, ctypes.c_void_p(stream or 0)))
 
 
 def psk_group_destroy(group: int):
@@ -261,6 +280,17 @@ def psk_group_run_tree(group: int, tree: int, in_slots: Sequence[int], out_slot:
     sc = (ctypes.c_void_p * n)(*[ctypes.c_void_p(int(p)) for p in list(scalars) + [0] * (n - len(scalars))])
     _check(lib().psk_group_run_tree(ctypes.c_void_p(group), ctypes.c_void_p(tree), sl, int(out_slot), sc,
                                     ctypes.c_void_p(stream or 0)))
+
+
+def psk_group_run_tree_multi(group: int, tree: int, in_slots: Sequence[int], out_slots: Sequence[int],
+                             scalars: Sequence[int] = (), stream: Optional[int] = None):
+    """out_slots[0]: the root's slot, out_slots[1 + k]: extra output k's."""
+    n = max(len(in_slots), len(scalars), 1)
+    sl = (ctypes.c_int32 * n)(*[int(x) for x in list(in_slots) + [0] * (n - len(in_slots))])
+    sc = (ctypes.c_void_p * n)(*[ctypes.c_void_p(int(p)) for p in list(scalars) + [0] * (n - len(scalars))])
+    os_ = (ctypes.c_int32 * max(1, len(out_slots)))(*[int(x) for x in out_slots])
+    _check(lib().psk_group_run_tree_multi(ctypes.c_void_p(group), ctypes.c_void_p(tree), sl, os_, sc,
+                                          ctypes.c_void_p(stream or 0)))
 
 
 def psk_tree_create(leaves: Sequence[Tuple[int, Sequence[int]]], slot_dtypes: Sequence) -> int:
@@ -383,8 +413,10 @@ def _stream_handle(stream) -> int:
 class Group:
     """A compiled fusion group, run on torch tensors."""
 
-    def __init__(self, nodes, inputs, out_shape, out_dtype, root=None, tree=False):
-        self.desc = GroupDesc(nodes, inputs, out_shape, out_dtype, root=root, flags=PSK_GROUP_TREE if tree else 0)
+    def __init__(self, nodes, inputs, out_shape, out_dtype, root=None, tree=False, extras=()):
+        self.desc = GroupDesc(nodes, inputs, out_shape, out_dtype, root=root, flags=PSK_GROUP_TREE if tree else 0,
+                              extras=extras)
+        self.n_extra = len(extras)
         self.handle = psk_group_create(self.desc)
         self.out_shape = tuple(out_shape)
         self.out_dtype = out_dtype
@@ -393,18 +425,28 @@ class Group:
     def info(self) -> psk_group_info:
         return psk_group_get_info(self.handle)
 
-    def run(self, inputs, out, stream=None):
-        for t in list(inputs) + [out]:
+    def run(self, inputs, out, stream=None, extra_outs=None):
+        """extra_outs: one tensor per extra output (a group with extra outputs
+        runs through psk_group_run_multi)."""
+        outs = [out] + list(extra_outs or [])
+        for t in list(inputs) + outs:
             if not t.is_cuda or not t.is_contiguous():
                 raise ValueError("group buffers must be contiguous device tensors")
-        psk_group_run(self.handle, [t.data_ptr() for t in inputs], out.data_ptr(), _stream_handle(stream))
+        if extra_outs is None:
+            psk_group_run(self.handle, [t.data_ptr() for t in inputs], out.data_ptr(), _stream_handle(stream))
+        else:
+            psk_group_run_multi(self.handle, [t.data_ptr() for t in inputs], [t.data_ptr() for t in outs],
+                                _stream_handle(stream))
         return out
 
     def run_tree(self, tree: "Tree", in_slots, out_slot, scalars=(), stream=None):
         """Map the group over every leaf of `tree` (one launch); scalars are
         0-d device tensors (or None for per-element inputs)."""
         ptrs = [0 if t is None else t.data_ptr() for t in scalars]
-        psk_group_run_tree(self.handle, tree.handle, in_slots, out_slot, ptrs, _stream_handle(stream))
+        if isinstance(out_slot, int):
+            psk_group_run_tree(self.handle, tree.handle, in_slots, out_slot, ptrs, _stream_handle(stream))
+        else:
+            psk_group_run_tree_multi(self.handle, tree.handle, in_slots, out_slot, ptrs, _stream_handle(stream))
 
     def __del__(self):
         h = getattr(self, "handle", None)

@@ -159,30 +159,48 @@ extern "C" psk_status psk_group_get_info(const psk_group* group, psk_group_info*
     info->phases = an.phases;
     info->rows = an.rows;
     info->cols = an.cols;
-    info->lanes_per_row = p.kind ? p.lanes : 1;
+    info->lanes_per_row = p.kind == 1 ? p.lanes : 1;
     info->vec = p.vec;
     info->block = p.block;
-    info->rows_per_block = p.kind ? p.rows_per_block : 0;
+    info->rows_per_block = p.kind == 1 ? p.rows_per_block : 0;
     int64_t bytes = an.numel * esize(an.out_dtype);
     for (const InputInfo& in : an.inputs)
         if (in.used) bytes += in.numel * esize(in.dtype);
+    for (const auto& x : an.extras) bytes += (x.per_row ? an.rows : an.numel) * esize(x.dtype);
     info->algorithmic_bytes = bytes;
     return PSK_OK;
 }
 
-extern "C" psk_status psk_group_run(const psk_group* group, const void* const* inputs, void* out, void* hip_stream)
+// One launch of a group: outs[0] is the root's output, outs[1 + k] extra output k's.
+static psk_status run_group(const psk_group* group, const void* const* inputs, void* const* outs, void* hip_stream)
 {
-    clear_error();
-    if (!group) return fail(PSK_E_NULL, "group is NULL");
     const Analysis& an = group->an;
     if (an.tree) return fail(PSK_E_UNSUPPORTED, "a tree-mapped group runs with psk_group_run_tree");
     if (an.numel == 0) return PSK_OK;
-    if (!out) return fail(PSK_E_NULL, "out is NULL");
     if (!an.inputs.empty() && !inputs) return fail(PSK_E_NULL, "inputs is NULL");
-    const uintptr_t ob = reinterpret_cast<uintptr_t>(out);
-    const uintptr_t oe = ob + (uintptr_t)an.numel * esize(an.out_dtype);
-    bool aligned16 = (ob % 16) == 0;
-    if (ob % esize(an.out_dtype)) return fail(PSK_E_ALIGN, "out is not aligned to its element size");
+    // every output: [b, e), element size, per row or per element
+    struct Out {
+        uintptr_t b, e;
+        int size;
+        bool per_row;
+        psk_dtype dt;
+    };
+    const int n_out = 1 + (int)an.extras.size();
+    std::vector<Out> ov(n_out);
+    bool aligned16 = true;
+    for (int k = 0; k < n_out; ++k) {
+        const std::string name = k == 0 ? "out" : "extra output " + std::to_string(k - 1);
+        if (!outs[k]) return fail(PSK_E_NULL, name + " is NULL");
+        const psk_dtype dt = k == 0 ? an.out_dtype : an.extras[k - 1].dtype;
+        const bool per_row = k > 0 && an.extras[k - 1].per_row;
+        const uintptr_t b = reinterpret_cast<uintptr_t>(outs[k]);
+        if (b % esize(dt)) return fail(PSK_E_ALIGN, name + " is not aligned to its element size");
+        if (!per_row && b % 16) aligned16 = false;
+        ov[k] = {b, b + (uintptr_t)(per_row ? an.rows : an.numel) * esize(dt), esize(dt), per_row, dt};
+        for (int j = 0; j < k; ++j)
+            if (ov[j].b < ov[k].e && ov[k].b < ov[j].e)
+                return fail(PSK_E_ALIAS, name + " overlaps another output");
+    }
     for (size_t k = 0; k < an.inputs.size(); ++k) {
         const InputInfo& in = an.inputs[k];
         if (!in.used) continue;
@@ -192,10 +210,12 @@ extern "C" psk_status psk_group_run(const psk_group* group, const void* const* i
         if (b % esize(in.dtype)) return fail(PSK_E_ALIGN, "input " + std::to_string(k) + " is not aligned to its element size");
         if (b % 16) aligned16 = false;
         const uintptr_t e = b + (uintptr_t)in.numel * esize(in.dtype);
-        if (b < oe && ob < e) {
-            bool same = b == ob && in.kind == InKind::Full && in.dtype == an.out_dtype;
+        for (const Out& o : ov) {
+            if (!(b < o.e && o.b < e)) continue;
+            // in place: an element output over a same-shape, same-type input
+            bool same = b == o.b && !o.per_row && in.kind == InKind::Full && in.dtype == o.dt;
             if (!same)
-                return fail(PSK_E_ALIAS, "out overlaps input " + std::to_string(k) +
+                return fail(PSK_E_ALIAS, "an output overlaps input " + std::to_string(k) +
                                              " (only an in-place update of a same-shape, same-type input is allowed)");
         }
     }
@@ -219,8 +239,8 @@ extern "C" psk_status psk_group_run(const psk_group* group, const void* const* i
     for (size_t i = 0; i < an.inputs.size(); ++i) ptrs[i] = inputs ? inputs[i] : nullptr;
     long long n_total = k->plan.kind == 1 ? (long long)an.rows : (long long)an.numel;
     for (size_t i = 0; i < ptrs.size(); ++i) args.push_back(&ptrs[i]);
-    void* outp = out;
-    args.push_back(&outp);
+    std::vector<void*> optr(outs, outs + n_out);
+    for (int i = 0; i < n_out; ++i) args.push_back(&optr[i]);
     args.push_back(&n_total);
     const KernelPlan& p = k->plan;
     hipError_t e = hipModuleLaunchKernel(fn, (unsigned)p.grid, 1, 1, (unsigned)p.block, 1, 1, 0,
@@ -228,6 +248,25 @@ extern "C" psk_status psk_group_run(const psk_group* group, const void* const* i
     if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipModuleLaunchKernel: ") + hipGetErrorString(e));
     count_launch();
     return PSK_OK;
+}
+
+extern "C" psk_status psk_group_run(const psk_group* group, const void* const* inputs, void* out, void* hip_stream)
+{
+    clear_error();
+    if (!group) return fail(PSK_E_NULL, "group is NULL");
+    if (!group->an.extras.empty())
+        return fail(PSK_E_UNSUPPORTED, "the group has extra outputs: run it with psk_group_run_multi");
+    void* outs[1] = {out};
+    return run_group(group, inputs, outs, hip_stream);
+}
+
+extern "C" psk_status psk_group_run_multi(const psk_group* group, const void* const* inputs, void* const* outs,
+                                          void* hip_stream)
+{
+    clear_error();
+    if (!group) return fail(PSK_E_NULL, "group is NULL");
+    if (!outs) return fail(PSK_E_NULL, "outs is NULL");
+    return run_group(group, inputs, outs, hip_stream);
 }
 
 extern "C" psk_status psk_group_source(const psk_group_desc* desc, char* buf, size_t cap, size_t* len)
@@ -282,6 +321,7 @@ struct psk_tree {
     double* d_partials = nullptr;   // clipping: one partial sum of squares per chunk
     ClipOut* d_clip = nullptr;      // clipping: squared norm and factor
     std::vector<Range> ranges;      // every slot buffer, sorted by start; equal ranges are adjacent
+    uint8_t shared[PSK_MAX_SLOTS][PSK_MAX_SLOTS] = {};   // some leaf has one buffer in both slots
     int device = 0;
     int32_t vector_leaves = 0;
     ~psk_tree()
@@ -376,6 +416,13 @@ extern "C" psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, 
         if (r.e > max_end) { max_end = r.e; prev = i; }
     }
     t->ranges = ranges;
+    for (size_t i = 0; i < ranges.size();) {
+        size_t j = i + 1;
+        while (j < ranges.size() && ranges[j].b == ranges[i].b && ranges[j].e == ranges[i].e) ++j;
+        for (size_t a = i; a < j; ++a)
+            for (size_t b = i; b < j; ++b) t->shared[ranges[a].slot][ranges[b].slot] = 1;
+        i = j;
+    }
     const size_t nc = t->plan.chunk_leaf.size();
     t->chunks.resize(nc);
     for (size_t c = 0; c < nc; ++c)
@@ -540,19 +587,26 @@ extern "C" psk_status psk_tree_clip_result(const psk_tree* tree, double* sumsq, 
 }
 
 // ------------------------------------------------------- tree-mapped groups
-extern "C" psk_status psk_group_run_tree(const psk_group* group, const psk_tree* tree, const int32_t* in_slot,
-                                         int32_t out_slot, const void* const* scalars, void* hip_stream)
+static psk_status run_tree(const psk_group* group, const psk_tree* tree, const int32_t* in_slot,
+                           const int32_t* out_slot, const void* const* scalars, void* hip_stream)
 {
-    clear_error();
-    if (!group || !tree) return fail(PSK_E_NULL, "group or tree is NULL");
     const Analysis& an = group->an;
     if (!an.tree) return fail(PSK_E_UNSUPPORTED, "the group was not created with PSK_GROUP_TREE");
     const int n_in = (int)an.inputs.size();
+    const int n_out = 1 + (int)an.extras.size();
     if (n_in > 0 && !in_slot) return fail(PSK_E_NULL, "in_slot is NULL");
-    if (out_slot < 0 || out_slot >= tree->n_slots) return fail(PSK_E_SHAPE, "out_slot out of range");
-    if (tree->dt[out_slot] != an.out_dtype)
-        return fail(PSK_E_TYPE, "the output slot's storage type is not the group's");
-    std::vector<int> slot_args(n_in + 1, 0);
+    std::vector<int> slot_args(n_in + n_out, 0);
+    for (int k = 0; k < n_out; ++k) {
+        const int s = out_slot[k];
+        if (s < 0 || s >= tree->n_slots) return fail(PSK_E_SHAPE, "output slot out of range");
+        if (tree->dt[s] != (k == 0 ? an.out_dtype : an.extras[k - 1].dtype))
+            return fail(PSK_E_TYPE, "output " + std::to_string(k) + ": the slot's storage type is not the group's");
+        for (int j = 0; j < k; ++j)
+            if (tree->shared[out_slot[j]][s] || out_slot[j] == s)
+                return fail(PSK_E_ALIAS, "outputs " + std::to_string(j) + " and " + std::to_string(k) +
+                                             " would write the same buffer");
+        slot_args[n_in + k] = s;
+    }
     std::vector<const void*> sc(n_in, nullptr);
     for (int k = 0; k < n_in; ++k) {
         const InputInfo& in = an.inputs[k];
@@ -569,9 +623,11 @@ extern "C" psk_status psk_group_run_tree(const psk_group* group, const psk_tree*
             while (it != tree->ranges.begin()) {
                 --it;
                 if (a >= it->e) break;
-                if (it->slot == out_slot)
-                    return fail(PSK_E_ALIAS, "scalar input " + std::to_string(k) + " lies in leaf " +
-                                                 std::to_string(it->leaf) + "'s output slot");
+                for (int j = 0; j < n_out; ++j)
+                    if (it->slot == out_slot[j])
+                        return fail(PSK_E_ALIAS, "scalar input " + std::to_string(k) + " lies in leaf " +
+                                                     std::to_string(it->leaf) + "'s output slot " +
+                                                     std::to_string(it->slot));
             }
             sc[k] = scalars[k];
         } else {
@@ -582,7 +638,6 @@ extern "C" psk_status psk_group_run_tree(const psk_group* group, const psk_tree*
             slot_args[k] = s;
         }
     }
-    slot_args[n_in] = out_slot;
     if (tree->chunks.empty()) return PSK_OK;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != tree->device)
@@ -598,13 +653,33 @@ extern "C" psk_status psk_group_run_tree(const psk_group* group, const psk_tree*
     const void* cp = tree->d_chunks;
     unsigned nv = (unsigned)n_virtual, pv = (unsigned)per;
     std::vector<void*> args = {&lp, &cp, &nv, &pv};
-    for (int k = 0; k <= n_in; ++k) args.push_back(&slot_args[k]);
+    for (int k = 0; k < n_in + n_out; ++k) args.push_back(&slot_args[k]);
     for (int k = 0; k < n_in; ++k) args.push_back(&sc[k]);
     hipError_t e = hipModuleLaunchKernel(fn, (unsigned)(per * 8), 1, 1, (unsigned)kp.block, 1, 1, 0,
                                          static_cast<hipStream_t>(hip_stream), args.data(), nullptr);
     if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipModuleLaunchKernel: ") + hipGetErrorString(e));
     count_launch();
     return PSK_OK;
+}
+
+extern "C" psk_status psk_group_run_tree(const psk_group* group, const psk_tree* tree, const int32_t* in_slot,
+                                         int32_t out_slot, const void* const* scalars, void* hip_stream)
+{
+    clear_error();
+    if (!group || !tree) return fail(PSK_E_NULL, "group or tree is NULL");
+    if (!group->an.extras.empty())
+        return fail(PSK_E_UNSUPPORTED, "the group has extra outputs: run it with psk_group_run_tree_multi");
+    const int32_t outs[1] = {out_slot};
+    return run_tree(group, tree, in_slot, outs, scalars, hip_stream);
+}
+
+extern "C" psk_status psk_group_run_tree_multi(const psk_group* group, const psk_tree* tree, const int32_t* in_slot,
+                                               const int32_t* out_slot, const void* const* scalars, void* hip_stream)
+{
+    clear_error();
+    if (!group || !tree) return fail(PSK_E_NULL, "group or tree is NULL");
+    if (!out_slot) return fail(PSK_E_NULL, "out_slot is NULL");
+    return run_tree(group, tree, in_slot, out_slot, scalars, hip_stream);
 }
 
 // --------------------------------------------------------------- partition

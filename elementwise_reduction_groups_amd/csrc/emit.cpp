@@ -72,6 +72,8 @@ std::string canonical_text(const Analysis& an)
         s << i << " " << nd.op << " " << nd.a << " " << nd.b << " " << nd.c << " " << nd.iparam << " "
           << (nd.op == PSK_OP_CONST ? bits : 0u) << "\n";
     }
+    for (const auto& x : an.extras) s << "extra " << x.node << " " << x.dtype << " " << (x.per_row ? 1 : 0) << "\n";
+    s << "flags " << an.flags << "\n";
     return s.str();
 }
 
@@ -124,6 +126,7 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
         int bytes = size_of(an.out_dtype);
         for (const InputInfo& in : an.inputs)
             if (in.used && in.kind != InKind::Scalar) bytes += size_of(in.dtype);
+        for (const auto& x : an.extras) bytes += size_of(x.dtype);
         int per = 4;
         while (per < 16 && per * bytes < 48) per *= 2;
         per = layout_value("tper", per);
@@ -225,6 +228,8 @@ __device__ __forceinline__ psk_u32 psk_pack2(float a, float b) {
   return __builtin_bit_cast(psk_u32, __builtin_convertvector(f, psk_b2));
 }
 __device__ __forceinline__ psk_u16 psk_r1(float a) { return (psk_u16)(psk_pack2(a, 0.0f) & 0xffffu); }
+// a value as stored to bf16 and read back (members read stored values so)
+__device__ __forceinline__ float psk_rt(float a) { return psk_h(psk_r1(a)); }
 // gelu(x) = x * Phi(x) with Phi(x) = erfc(-x/sqrt 2) / 2.  erfc(w), w >= 0,
 // is the Chebyshev-fitted form of Press, Teukolsky, Vetterling and Flannery,
 // Numerical Recipes (2nd ed.), section 6.2: erfc(w) = t exp(-w^2 + P(t)),
@@ -349,6 +354,15 @@ struct Emitter {
 
     bool use_refused = false;
     bool divr_ok = true;          // row-value divisors use psk_divr
+
+    // node i's defining expression as its readers see it: a value stored as
+    // bf16 (an extra output) is read back rounded
+    std::string rt(int i, const std::string& e) const { return an.rounded(i) ? "psk_rt(" + e + ")" : e; }
+    void round_elems(int i, const std::vector<int>& elems, const char* indent)
+    {
+        if (!an.rounded(i)) return;
+        for (int e : elems) o << indent << "v" << i << "_" << e << " = psk_rt(v" << i << "_" << e << ");\n";
+    }
 
     // a row value that divides element values: its reciprocal, once per row
     void row_reciprocal(int i)
@@ -495,21 +509,34 @@ struct Emitter {
 
     void store_vec(const std::string& off, int e0, const std::string& cond)
     {
+        store_node(an.root, "out", an.out_dtype, off, e0, cond);
+    }
+
+    // store element values of node i (elements e0 .. e0+vec-1) to `ptr`
+    void store_node(int i, const std::string& ptr, psk_dtype dt, const std::string& off, int e0,
+                    const std::string& cond)
+    {
         const int V = pl.vec;
-        std::string p = "(out + " + off + ")";
-        auto src = [&](int j) { return val(an.root, e0 + j); };
+        std::string p = "(" + ptr + " + " + off + ")";
+        auto src = [&](int j) { return val(i, e0 + j); };
         if (V == 1) {
             o << "    if (" << cond << ") psk_st(" << p << ", "
-              << (an.out_dtype == PSK_BF16 ? "psk_r1(" + src(0) + ")" : src(0)) << ");\n";
+              << (dt == PSK_BF16 ? "psk_r1(" + src(0) + ")" : src(0)) << ");\n";
             return;
         }
-        if (an.out_dtype == PSK_F32) {
-            o << "    if (" << cond << ") psk_st((psk_u4v*)" << p << ", (psk_u4v){";
-            for (int j = 0; j < 4; ++j) o << (j ? ", " : "") << "__float_as_uint(" << src(j) << ")";
-            o << "});\n";
-        } else {
-            o << "    if (" << cond << ") psk_st((psk_u4v*)" << p << ", (psk_u4v){";
-            for (int j = 0; j < 4; ++j) o << (j ? ", " : "") << "psk_pack2(" << src(2 * j) << ", " << src(2 * j + 1) << ")";
+        // 32-bit words of the V elements, written as 16-byte pieces (one
+        // 8-byte piece when only two words are left: four bf16 values)
+        std::vector<std::string> words;
+        if (dt == PSK_F32)
+            for (int j = 0; j < V; ++j) words.push_back("__float_as_uint(" + src(j) + ")");
+        else
+            for (int j = 0; j < V; j += 2) words.push_back("psk_pack2(" + src(j) + ", " + src(j + 1) + ")");
+        const int epw = dt == PSK_F32 ? 1 : 2;   // elements per word
+        for (size_t w = 0; w < words.size(); w += 4) {
+            const size_t cnt = std::min<size_t>(4, words.size() - w);
+            const char* vt = cnt == 4 ? "psk_u4v" : "psk_u2v";
+            o << "    if (" << cond << ") psk_st((" << vt << "*)(" << p << " + " << w * epw << "), (" << vt << "){";
+            for (size_t q = 0; q < cnt; ++q) o << (q ? ", " : "") << words[w + q];
             o << "});\n";
         }
     }
@@ -535,11 +562,16 @@ struct Emitter {
         // (in place); every load of an element precedes its store
         for (size_t k = 0; k < an.inputs.size(); ++k)
             o << "const void* in" << k << "_, ";
-        o << "void* out_, long long n_total)\n{\n";
+        o << "void* out_, ";
+        for (size_t k = 0; k < an.extras.size(); ++k) o << "void* xo" << k << "_, ";
+        o << "long long n_total)\n{\n";
         for (size_t k = 0; k < an.inputs.size(); ++k)
             o << "  const " << ptype(an.inputs[k].dtype) << "* in" << k << " = (const "
               << ptype(an.inputs[k].dtype) << "*)in" << k << "_;\n";
         o << "  " << ptype(an.out_dtype) << "* out = (" << ptype(an.out_dtype) << "*)out_;\n";
+        for (size_t k = 0; k < an.extras.size(); ++k)
+            o << "  " << ptype(an.extras[k].dtype) << "* xo" << k << " = (" << ptype(an.extras[k].dtype) << "*)xo" << k
+              << "_;\n";
     }
 
     // Row kernel with a causal mask: a lane's vector k whose first column
@@ -563,14 +595,14 @@ struct Emitter {
             const psk_node& nd = an.nodes[i];
             if (op_is_leaf(nd.op) || op_is_row(nd.op) || an.depth[i] != p) continue;
             if (an.is_row[i]) {
-                o << "    const float r" << i << " = " << expr(i, 0) << ";\n";
+                o << "    const float r" << i << " = " << rt(i, expr(i, 0)) << ";\n";
                 row_reciprocal(i);
             } else {
                 elems.push_back(i);
             }
         }
         for (int i : elems)
-            if (an.uniform[i]) o << "    const float u" << i << " = " << refused_expr(i) << ";\n";
+            if (an.uniform[i]) o << "    const float u" << i << " = " << rt(i, refused_expr(i)) << ";\n";
         for (int k = 0; k < pl.nv; ++k) {
             for (int i : elems)
                 for (int j = 0; j < pl.vec; ++j) o << "    float v" << i << "_" << k * pl.vec + j << ";\n";
@@ -597,6 +629,16 @@ struct Emitter {
                     o << ";\n";
                 }
             o << "    }\n";
+            for (int i : elems) {
+                std::vector<int> es;
+                for (int j = 0; j < pl.vec; ++j) es.push_back(k * pl.vec + j);
+                if (!an.uniform[i]) round_elems(i, es, "    ");   // u is rounded already
+                else if (an.rounded(i)) {
+                    o << "    if (c" << k << " <= q) {\n";
+                    round_elems(i, es, "      ");
+                    o << "    }\n";
+                }
+            }
         }
     }
 
@@ -608,7 +650,7 @@ struct Emitter {
             const psk_node& nd = an.nodes[i];
             if (op_is_leaf(nd.op) || op_is_row(nd.op) || an.depth[i] != p) continue;
             if (an.is_row[i]) {
-                o << "    const float r" << i << " = " << expr((int)i, 0) << ";\n";
+                o << "    const float r" << i << " = " << rt((int)i, expr((int)i, 0)) << ";\n";
                 row_reciprocal((int)i);
             } else if (divr_node((int)i)) {
                 divr_open((int)i);
@@ -618,9 +660,10 @@ struct Emitter {
                     es.push_back(e);
                 }
                 divr_close((int)i, es, "    ");
+                round_elems((int)i, es, "    ");
             } else {
                 for (int e = 0; e < NE; ++e)
-                    o << "    const float v" << i << "_" << e << " = " << expr((int)i, e) << ";\n";
+                    o << "    const float v" << i << "_" << e << " = " << rt((int)i, expr((int)i, e)) << ";\n";
             }
         }
     }
@@ -692,9 +735,23 @@ struct Emitter {
         }
         leaves();
         members_at(0);
+        for (size_t k = 0; k < an.extras.size(); ++k) {
+            const Analysis::Extra& x = an.extras[k];
+            std::string xo = "xo" + std::to_string(k);
+            if (x.per_row)
+                o << "    if (c0 == 0) " << xo << "[row] = " << scalar_store(x.node, x.dtype) << ";\n";
+            else
+                store_node(x.node, xo, x.dtype, "e0", 0, "true");
+        }
         store_vec("e0", 0, "true");
         o << "  }\n}\n";
         return o.str();
+    }
+
+    // a row value of node i as stored to `dt`
+    std::string scalar_store(int i, psk_dtype dt) const
+    {
+        return dt == PSK_BF16 ? "psk_r1(r" + std::to_string(i) + ")" : "r" + std::to_string(i);
     }
 
     // ----------------------------------------------------------------- tree
@@ -713,7 +770,8 @@ struct Emitter {
         o << "extern \"C\" __global__ void __launch_bounds__(" << TB << ") " << name
           << "(const psk_leaf_dev* __restrict__ leaves, const psk_chunk_dev* __restrict__ chunks, "
              "unsigned n_virtual, unsigned per_xcd";
-        for (size_t k = 0; k <= an.inputs.size(); ++k) o << ", int slot" << k;   // last: the output's
+        // inputs' slots, then the outputs' (root first, then the extra outputs)
+        for (size_t k = 0; k <= an.inputs.size() + an.extras.size(); ++k) o << ", int slot" << k;
         for (size_t k = 0; k < an.inputs.size(); ++k) o << ", const void* s" << k;
         o << ")\n{\n";
         o << "  const unsigned vb = (blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;\n";
@@ -763,34 +821,45 @@ struct Emitter {
         }
         leaves();
         members_at(0);
-        std::string T = ptype(an.out_dtype);
-        o << "    PSK_G " << T << "* out = (PSK_G " << T << "*)L->slot[slot" << an.inputs.size() << "] + e0;\n";
+        for (size_t k = 0; k < an.extras.size(); ++k)
+            tree_store(an.extras[k].node, an.extras[k].dtype, (int)(an.inputs.size() + 1 + k), "xo" + std::to_string(k));
+        tree_store(an.root, an.out_dtype, (int)an.inputs.size(), "out");
+        o << "  }\n}\n";
+        return o.str();
+    }
+
+    // tree kernel: node i's elements to slot `slot_arg` of the leaf
+    void tree_store(int root, psk_dtype dt, int slot_arg, const std::string& name)
+    {
+        std::string T = ptype(dt);
+        o << "    {\n";
+        o << "    PSK_G " << T << "* " << name << " = (PSK_G " << T << "*)L->slot[slot" << slot_arg << "] + e0;\n";
+        const std::string out = name;
         o << "    if (full) {\n";
-        if (an.out_dtype == PSK_F32) {
+        if (dt == PSK_F32) {
             for (int q = 0; q < NE / 4; ++q) {
-                o << "      psk_st((PSK_G psk_u4v*)out + " << q << ", (psk_u4v){";
-                for (int j = 0; j < 4; ++j) o << (j ? ", " : "") << "__float_as_uint(" << val(an.root, 4 * q + j) << ")";
+                o << "      psk_st((PSK_G psk_u4v*)" << out << " + " << q << ", (psk_u4v){";
+                for (int j = 0; j < 4; ++j) o << (j ? ", " : "") << "__float_as_uint(" << val(root, 4 * q + j) << ")";
                 o << "});\n";
             }
         } else if (NE == 4) {
-            o << "      psk_st((PSK_G psk_u2v*)out, (psk_u2v){psk_pack2(" << val(an.root, 0) << ", " << val(an.root, 1)
-              << "), psk_pack2(" << val(an.root, 2) << ", " << val(an.root, 3) << ")});\n";
+            o << "      psk_st((PSK_G psk_u2v*)" << out << ", (psk_u2v){psk_pack2(" << val(root, 0) << ", " << val(root, 1)
+              << "), psk_pack2(" << val(root, 2) << ", " << val(root, 3) << ")});\n";
         } else {
             for (int q = 0; q < NE / 8; ++q) {
-                o << "      psk_st((PSK_G psk_u4v*)out + " << q << ", (psk_u4v){";
+                o << "      psk_st((PSK_G psk_u4v*)" << out << " + " << q << ", (psk_u4v){";
                 for (int j = 0; j < 4; ++j)
-                    o << (j ? ", " : "") << "psk_pack2(" << val(an.root, 8 * q + 2 * j) << ", "
-                      << val(an.root, 8 * q + 2 * j + 1) << ")";
+                    o << (j ? ", " : "") << "psk_pack2(" << val(root, 8 * q + 2 * j) << ", "
+                      << val(root, 8 * q + 2 * j + 1) << ")";
                 o << "});\n";
             }
         }
         o << "    } else {\n";
         for (int j = 0; j < NE; ++j)
-            o << "      if (" << j << " < cnt) out[" << j << "] = "
-              << (an.out_dtype == PSK_BF16 ? "psk_r1(" + val(an.root, j) + ")" : val(an.root, j)) << ";\n";
+            o << "      if (" << j << " < cnt) " << out << "[" << j << "] = "
+              << (dt == PSK_BF16 ? "psk_r1(" + val(root, j) + ")" : val(root, j)) << ";\n";
         o << "    }\n";
-        o << "  }\n}\n";
-        return o.str();
+        o << "    }\n";
     }
 
     // ------------------------------------------------------------------ row
@@ -843,9 +912,10 @@ struct Emitter {
         }
         for (int i : reds) {
             if (an.nodes[i].op == PSK_OP_ROW_MEAN)
-                o << "    const float r" << i << " = p" << i << " / " << flit((float)an.cols) << ";\n";
+                o << "    const float r" << i << " = " << rt(i, "p" + std::to_string(i) + " / " + flit((float)an.cols))
+                  << ";\n";
             else
-                o << "    const float r" << i << " = p" << i << ";\n";
+                o << "    const float r" << i << " = " << rt(i, "p" + std::to_string(i)) << ";\n";
             row_reciprocal(i);
         }
     }
@@ -879,6 +949,23 @@ struct Emitter {
         leaves();
         for (int p = 0; p <= an.phases; ++p) {
             members_at(p);
+            // extra outputs computed by now: stored at once
+            for (size_t k = 0; k < an.extras.size(); ++k) {
+                const Analysis::Extra& x = an.extras[k];
+                if (an.depth[x.node] != p) continue;
+                std::string xo = "xo" + std::to_string(k);
+                if (x.per_row) {
+                    o << "    if (rok && lane == 0) " << xo << "[row] = " << scalar_store(x.node, x.dtype) << ";\n";
+                    continue;
+                }
+                for (int v = 0; v < pl.nv; ++v) {
+                    std::string c = "c" + std::to_string(v);
+                    std::string cond = "rok";
+                    if ((int64_t)(v + 1) * L * V > an.cols) cond += " && " + c + " < " + std::to_string(an.cols);
+                    store_node(x.node, xo, x.dtype, "row * (" + std::string(I()) + ")" + std::to_string(an.cols) + " + " + c,
+                               v * V, cond);
+                }
+            }
             if (p < an.phases) reductions_at(p);
         }
         for (int v = 0; v < pl.nv; ++v) {

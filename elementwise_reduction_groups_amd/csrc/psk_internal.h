@@ -57,6 +57,16 @@ struct Analysis {
     bool row_kind = false;              // has at least one row reduction
     bool tree = false;                  // PSK_GROUP_TREE: mapped over tree leaves
     uint32_t flags = 0;
+    // extra outputs: node, storage type, one per row (stored [rows, 1])
+    struct Extra {
+        int node;
+        psk_dtype dtype;
+        bool per_row;
+    };
+    std::vector<Extra> extras;
+    std::vector<int> stored;            // node -> 1 + extra index, or 0
+    // members that read node i read it rounded to bf16 (a bf16 extra output)
+    bool rounded(int i) const { return stored[i] > 0 && extras[stored[i] - 1].dtype == PSK_BF16; }
 };
 
 // Validates the descriptor; on success fills `an`.

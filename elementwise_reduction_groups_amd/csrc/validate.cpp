@@ -208,13 +208,34 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
         return fail(PSK_E_ROOT, "the root must be a member, not an input or a constant");
     if (an.n_readers[an.root] != 0)
         return fail(PSK_E_ROOT, "the root is read by another node");
+    // ---- extra outputs: members stored besides the root
+    if (desc->n_extra < 0 || desc->n_extra > PSK_MAX_EXTRA)
+        return fail(PSK_E_CAP, "n_extra must be in 0.." + std::to_string(PSK_MAX_EXTRA));
+    if (desc->n_extra > 0 && (!desc->extra_root || !desc->extra_out))
+        return fail(PSK_E_NULL, "extra_root or extra_out is NULL");
+    an.stored.assign(n, 0);
+    for (int k = 0; k < desc->n_extra; ++k) {
+        const int i = desc->extra_root[k];
+        if (i < 0 || i >= n) return fail(PSK_E_ROOT, "extra output " + std::to_string(k) + ": node out of range");
+        if (op_is_leaf(an.nodes[i].op))
+            return fail(PSK_E_ROOT, "extra output " + std::to_string(k) + ": an input or a constant is not stored");
+        if (i == an.root || an.stored[i])
+            return fail(PSK_E_ROOT, "extra output " + std::to_string(k) + ": node " + std::to_string(i) +
+                                        " is already an output");
+        if (!dtype_ok(desc->extra_out[k].dtype))
+            return fail(PSK_E_TYPE, "extra output " + std::to_string(k) + ": storage type must be f32 or bf16");
+        an.stored[i] = k + 1;
+        an.extras.push_back({i, (psk_dtype)desc->extra_out[k].dtype, false});
+    }
     for (int i = 0; i < n; ++i)
-        if (i != an.root && an.n_readers[i] == 0 && !op_is_leaf(an.nodes[i].op))
-            return fail(PSK_E_ROOT, at(i) + "a second unread member: a group has exactly one root");
-    // reachability from the root
+        if (i != an.root && !an.stored[i] && an.n_readers[i] == 0 && !op_is_leaf(an.nodes[i].op))
+            return fail(PSK_E_ROOT, at(i) + "a second unread member: a group has one root (store it as an "
+                                            "extra output to keep it)");
+    // reachability from the root and the extra outputs
     an.needed.assign(n, 0);
     an.needed[an.root] = 1;
-    for (int i = an.root; i >= 0; --i) {
+    for (auto& x : an.extras) an.needed[x.node] = 1;
+    for (int i = n - 1; i >= 0; --i) {
         if (!an.needed[i]) continue;
         const psk_node& nd = an.nodes[i];
         int ar = op_arity(nd.op);
@@ -223,7 +244,7 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
     }
     for (int i = 0; i < n; ++i)
         if (!an.needed[i])
-            return fail(PSK_E_DEAD, at(i) + "not read on any path to the root (dead code)");
+            return fail(PSK_E_DEAD, at(i) + "not read on any path to the root or a stored value (dead code)");
     for (int i = 0; i < n; ++i)
         if (an.nodes[i].op == PSK_OP_POWN && an.nodes[i].iparam > 2 && an.members > 1)
             return fail(PSK_E_OP, at(i) + "pow n with n > 2 never joins a group");
@@ -258,6 +279,25 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
         }
         an.depth[i] = dep;
     }
+    // extra outputs' shapes: the output's (element value) or the output's
+    // with a last axis of 1 (one value per row)
+    for (int k = 0; k < (int)an.extras.size(); ++k) {
+        Analysis::Extra& x = an.extras[k];
+        const psk_tensor_desc& t = desc->extra_out[k];
+        x.per_row = an.is_row[x.node] != 0;
+        bool ok = t.rank == desc->out.rank;
+        for (int d = 0; ok && d < t.rank; ++d) {
+            int64_t want = (x.per_row && d == t.rank - 1) ? 1 : desc->out.shape[d];
+            ok = t.shape[d] == want;
+        }
+        if (!ok)
+            return fail(PSK_E_SHAPE, "extra output " + std::to_string(k) + ": shape must be the output's" +
+                                         std::string(x.per_row ? " with a last axis of 1 (the node is one value "
+                                                                 "per row)" : " (the node is an element value)"));
+        if (x.per_row && (desc->flags & PSK_GROUP_TREE))
+            return fail(PSK_E_SHAPE, "extra output " + std::to_string(k) + ": a tree-mapped group stores element "
+                                         "values only");
+    }
     an.row_kind = an.n_reductions > 0;
     an.flags = desc->flags;
     an.tree = (desc->flags & PSK_GROUP_TREE) != 0;
@@ -272,6 +312,7 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
                 return fail(PSK_E_OP, at(i) + "a tree-mapped group has no rows for a causal mask");
     }
     an.phases = an.depth[an.root];
+    for (auto& x : an.extras) an.phases = std::max(an.phases, an.depth[x.node]);
     if (an.is_row[an.root] && an.cols > 1)
         return fail(PSK_E_ROW, "the root is one value per row but the output has " + std::to_string(an.cols) +
                                    " columns: a reduction cannot be the stored value here");
@@ -301,7 +342,8 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
         std::vector<char>& irrelevant = an.irrelevant;
         irrelevant.assign(n, 0);
         for (int i = n - 1; i >= 0; --i) {
-            if (i == an.root || readers[i].empty() || an.is_row[i]) continue;
+            // stored values are written everywhere, refused positions included
+            if (i == an.root || an.stored[i] || readers[i].empty() || an.is_row[i]) continue;
             bool irr = true;
             for (int r : readers[i]) {
                 const psk_node& rd = an.nodes[r];

@@ -54,6 +54,7 @@ extern "C" {
 #define PSK_MAX_INPUTS 16
 #define PSK_MAX_RANK 4
 #define PSK_MAX_SLOTS 8
+#define PSK_MAX_EXTRA 7         /* stored values besides the root */
 
 typedef enum psk_status {
     PSK_OK = 0,
@@ -151,12 +152,27 @@ typedef struct psk_group_desc {
     psk_tensor_desc out;             /* the root's storage type and shape */
     int32_t arith;                   /* arithmetic type: must be PSK_F32 */
     uint32_t flags;                  /* 0, or PSK_GROUP_TREE */
+    /* Further stored values (multi-output groups; 0 for a single root).
+     * PSK-Realize, "Not in this version", names multi-output kernels as what
+     * keeps a value read both inside and outside a group from splitting it,
+     * and "What it buys, measured" the layer normalization that splits for
+     * want of it.  extra_root[k] is a member other than the root, each
+     * named once; extra_out[k] its storage: an element value has the
+     * output's shape, a value that is one per row (a reduction, or a member
+     * of row values) the output's shape with a last axis of 1.  Members that
+     * read a stored value read it as stored (rounded to its storage type),
+     * so the group computes what the partitioned program would: the stored
+     * value ends one group and the next reads it from memory. */
+    int32_t n_extra;                 /* 0..PSK_MAX_EXTRA */
+    const int32_t* extra_root;
+    const psk_tensor_desc* extra_out;
 } psk_group_desc;
 
 /* A group mapped over the leaves of a parameter tree (psk_group_run_tree):
  * output rank 1, every input rank 1 (one element per leaf element) or rank 0
  * (one value for the whole tree); shape lengths are not used, each leaf has
- * its own; no row reductions and no causal mask. */
+ * its own; no row reductions and no causal mask.  Extra outputs are element
+ * values stored to further slots. */
 #define PSK_GROUP_TREE 1u
 
 typedef struct psk_group psk_group;
@@ -179,6 +195,15 @@ psk_status psk_group_create(const psk_group_desc* desc, psk_group** out);
  * (PSK_E_ALIGN); 16-byte alignment takes the vector path.  Empty outputs
  * launch nothing. */
 psk_status psk_group_run(const psk_group* group, const void* const* inputs, void* out, void* hip_stream);
+
+/* The same for a group with extra outputs: outs[0] is the root's output,
+ * outs[1 + k] extra output k's (laid out as desc.extra_out[k]).  An element
+ * output may be the same buffer as an input of its shape and storage type
+ * (in place); outputs never overlap one another, and a per-row output
+ * overlaps nothing (PSK_E_ALIAS).  psk_group_run refuses a group with extra
+ * outputs (PSK_E_UNSUPPORTED). */
+psk_status psk_group_run_multi(const psk_group* group, const void* const* inputs, void* const* outs,
+                               void* hip_stream);
 
 void psk_group_destroy(psk_group* group);
 
@@ -322,6 +347,13 @@ psk_status psk_tree_clip_result(const psk_tree* tree, double* sumsq, float* fact
  * tree with no elements launches nothing.  Buffers stay the caller's. */
 psk_status psk_group_run_tree(const psk_group* group, const psk_tree* tree, const int32_t* in_slot, int32_t out_slot,
                               const void* const* scalars, void* hip_stream);
+
+/* The same for a tree-mapped group with extra outputs: out_slot[0] receives
+ * the root, out_slot[1 + k] extra output k; output slots are distinct
+ * (PSK_E_ALIAS otherwise), and a scalar may lie in none of them.
+ * psk_group_run_tree refuses a group with extra outputs. */
+psk_status psk_group_run_tree_multi(const psk_group* group, const psk_tree* tree, const int32_t* in_slot,
+                                    const int32_t* out_slot, const void* const* scalars, void* hip_stream);
 
 /* --------------------------------------------------------------- partition */
 /* Partition a function body (a let-list of n nodes, leaves included) into

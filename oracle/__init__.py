@@ -67,6 +67,10 @@ def lib() -> ctypes.CDLL:
                                      ctypes.POINTER(vp), vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp,
                                      i64, i64]
         L.orc_eval_group.restype = ctypes.c_int
+        L.orc_eval_group_multi.argtypes = [ctypes.c_int, ctypes.POINTER(_orc_node), ctypes.c_int, ctypes.c_int,
+                                           ctypes.POINTER(vp), vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp,
+                                           ctypes.c_int, vp, vp, vp, ctypes.POINTER(vp), i64, i64]
+        L.orc_eval_group_multi.restype = ctypes.c_int
         L.orc_adamw_scalars.argtypes = [ctypes.c_double] * 5 + [i64, vp]
         L.orc_adamw.argtypes = [i64, ctypes.c_int, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp,
                                 ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double,
@@ -120,13 +124,18 @@ def _dtype_code(a: np.ndarray) -> int:
 # ------------------------------------------------------------ group evaluator
 def eval_group(nodes, inputs: Sequence[np.ndarray], out_shape: Sequence[int], out_dtype: int = F32,
                rows: Optional[Tuple[int, int]] = None, out: Optional[np.ndarray] = None,
-               root: Optional[int] = None) -> np.ndarray:
+               root: Optional[int] = None, extras: Sequence[Tuple[int, np.ndarray]] = ()) -> np.ndarray:
     """Evaluate a let-list (``synth.Node`` sequence) over broadcast inputs.
 
     Inputs are float32 arrays or uint16 arrays holding bf16 bits.  Returns the
     output as float32 (f32) or uint16 (bf16 bits); with ``rows=(r0, r1)``
     only those rows of the [R, C] view are computed (others are left as
-    they are in ``out``, zero if ``out`` is not given)."""
+    they are in ``out``, zero if ``out`` is not given).
+
+    ``extras``: (node, array) pairs, further stored values of a multi-output
+    group; the array (float32 or uint16 bf16 bits) has the output's shape,
+    or the output's shape with a last axis of 1 for a value that is one per
+    row.  A bf16 stored value is read rounded by later nodes."""
     n = len(nodes)
     arr = (_orc_node * n)()
     for i, nd in enumerate(nodes):
@@ -151,8 +160,16 @@ def eval_group(nodes, inputs: Sequence[np.ndarray], out_shape: Sequence[int], ou
     if out is None:
         out = np.zeros(out_shape, np.float32 if out_dtype == F32 else np.uint16)
     r0, r1 = rows if rows is not None else (0, R)
-    rc = lib().orc_eval_group(n, arr, n - 1 if root is None else root, k, ptrs, _ptr(dts), _ptr(ranks),
-                              _ptr(shapes), len(out_shape), _ptr(oshape), out_dtype, _ptr(out), r0, r1)
+    ne = len(extras)
+    for _, a in extras:
+        assert a.flags["C_CONTIGUOUS"] and a.size in (R * C, R)
+    xroot = np.array([int(nd) for nd, _ in extras] or [0], np.int32)
+    xdt = np.array([_dtype_code(a) for _, a in extras] or [0], np.int32)
+    xrow = np.array([int(a.shape[-1] == 1 and C != 1) for _, a in extras] or [0], np.int32)
+    xout = (ctypes.c_void_p * max(ne, 1))(*[_ptr(a) for _, a in extras])
+    rc = lib().orc_eval_group_multi(n, arr, n - 1 if root is None else root, k, ptrs, _ptr(dts), _ptr(ranks),
+                                    _ptr(shapes), len(out_shape), _ptr(oshape), out_dtype, _ptr(out),
+                                    ne, _ptr(xroot), _ptr(xdt), _ptr(xrow), xout, r0, r1)
     if rc != 0:
         raise ValueError("oracle refused the node list")
     return out

@@ -161,16 +161,29 @@ static int64_t bcast_offset(int out_rank, const int64_t *out_shape, int64_t r, i
  * causal_mask is true where seq2 <= seq), which gives the bits of the
  * softmax over the allowed positions (presk manual, "Native execution").
  *
+ * Extra stored values (orc_eval_group_multi): node extra_root[k] is stored
+ * to extra_out[k] as well, rounded to extra_dtype[k]: at [r, c] for an
+ * element value, at [r] when extra_per_row[k] (a value that is one per row).
+ * A stored value is what its readers read: a bf16 one is rounded before any
+ * later node uses it, as in the partitioned program where the stored value
+ * ends one group and the next group loads it (PSK-Realize, "What a group
+ * is": the root is the only value that reaches memory, rounded once).
+ *
  * Returns 0, or -1 on a malformed node list.
  */
-int orc_eval_group(int n_nodes, const orc_node *nodes, int root,
-                   int n_inputs, const void *const *inputs, const int32_t *in_dtype,
-                   const int32_t *in_rank, const int64_t *in_shape /* n_inputs x 8 */,
-                   int out_rank, const int64_t *out_shape, int out_dtype, void *out,
-                   int64_t row_begin, int64_t row_end)
+int orc_eval_group_multi(int n_nodes, const orc_node *nodes, int root,
+                         int n_inputs, const void *const *inputs, const int32_t *in_dtype,
+                         const int32_t *in_rank, const int64_t *in_shape /* n_inputs x 8 */,
+                         int out_rank, const int64_t *out_shape, int out_dtype, void *out,
+                         int n_extra, const int32_t *extra_root, const int32_t *extra_dtype,
+                         const int32_t *extra_per_row, void *const *extra_out,
+                         int64_t row_begin, int64_t row_end)
 {
-    if (out_rank < 1 || out_rank > 8 || root < 0 || root >= n_nodes)
+    if (out_rank < 1 || out_rank > 8 || root < 0 || root >= n_nodes || n_extra < 0)
         return -1;
+    for (int k = 0; k < n_extra; ++k)
+        if (extra_root[k] < 0 || extra_root[k] >= n_nodes)
+            return -1;
     int64_t C = out_shape[out_rank - 1];
     if (C <= 0)
         return 0;
@@ -257,15 +270,38 @@ int orc_eval_group(int n_nodes, const orc_node *nodes, int root,
             default:
                 rc = -1;
             }
+            /* a value stored as bf16 is read back rounded */
+            for (int k = 0; k < n_extra && rc == 0; ++k)
+                if (extra_root[k] == i && extra_dtype[k] == ORC_BF16)
+                    for (int64_t c = 0; c < C; ++c)
+                        v[c] = orc_bf16_widen(orc_bf16_round(v[c]));
         }
         if (rc == 0) {
             const float *res = val + (size_t)root * C;
             for (int64_t c = 0; c < C; ++c)
                 store_elem(out, out_dtype, r * C + c, res[c]);
+            for (int k = 0; k < n_extra; ++k) {
+                const float *x = val + (size_t)extra_root[k] * C;
+                if (extra_per_row[k])
+                    store_elem(extra_out[k], extra_dtype[k], r, x[0]);
+                else
+                    for (int64_t c = 0; c < C; ++c)
+                        store_elem(extra_out[k], extra_dtype[k], r * C + c, x[c]);
+            }
         }
     }
     free(val);
     return rc;
+}
+
+int orc_eval_group(int n_nodes, const orc_node *nodes, int root,
+                   int n_inputs, const void *const *inputs, const int32_t *in_dtype,
+                   const int32_t *in_rank, const int64_t *in_shape /* n_inputs x 8 */,
+                   int out_rank, const int64_t *out_shape, int out_dtype, void *out,
+                   int64_t row_begin, int64_t row_end)
+{
+    return orc_eval_group_multi(n_nodes, nodes, root, n_inputs, inputs, in_dtype, in_rank, in_shape, out_rank,
+                                out_shape, out_dtype, out, 0, NULL, NULL, NULL, NULL, row_begin, row_end);
 }
 
 /* ---------------------------------------------------------------- AdamW */

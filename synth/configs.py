@@ -214,3 +214,83 @@ def tree_leaf_values(shapes: Sequence[Sequence[int]], dtype, device="cpu", seed:
         g = _gen("cpu", seed, i)
         out.append((torch.randn(numel(s), generator=g) * std).to(dtype).to(device))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Multi-output groups.
+def layernorm_dag(eps_f32: float) -> List[Node]:
+    """(x - mean) / sqrt(mean((x - mean)^2) + eps) * gamma + beta, plus
+    rstd = 1 / sqrt(var + eps).  Node 12 is the normalised output (the
+    root), node 3 the row mean, node 14 rstd (both one value per row)."""
+    return parse_dag(f"""
+        %0 = input 0
+        %1 = input 1
+        %2 = input 2
+        %3 = row_mean %0
+        %4 = sub %0 %3
+        %5 = pow2 %4
+        %6 = row_mean %5
+        %7 = const {float(eps_f32).hex()}
+        %8 = add %6 %7
+        %9 = sqrt %8
+        %10 = div %4 %9
+        %11 = mul %10 %1
+        %12 = add %11 %2
+        %13 = const 1.0
+        %14 = div %13 %9
+    """)
+
+
+LAYERNORM_ROOT, LAYERNORM_MEAN, LAYERNORM_RSTD = 12, 3, 14
+RMSNORM_H = 3   # h = x + res in rmsnorm_gelu_dag
+
+
+def layernorm_inputs(rows: int, cols: int, device="cpu", seed: int = SEED_BASE + 6):
+    """x ~ N(1, 2) (rows with a non-zero mean), gamma ~ N(1, 0.1), beta ~
+    N(0, 0.1), all bf16."""
+    g = _gen("cpu", seed, 0)
+    x = (torch.randn(rows, cols, generator=g) * 2.0 + 1.0).to(torch.bfloat16)
+    gamma = (torch.randn(cols, generator=g) * 0.1 + 1.0).to(torch.bfloat16)
+    beta = (torch.randn(cols, generator=g) * 0.1).to(torch.bfloat16)
+    return x.to(device), gamma.to(device), beta.to(device)
+
+
+def adamw_group_dag() -> List[Node]:
+    """The AdamW step as a group over a parameter tree: inputs 0..3 are
+    theta, g, m, v (per element), 4..12 the f32 step scalars b1, b2, 1-b1,
+    1-b2, 1-b1^t, 1-b2^t, lr, eps, wd (per tree).  Node 15 is m', node 19
+    v' (stored: extra outputs), node 28 theta' (the root)."""
+    return parse_dag("""
+        %0 = input 0
+        %1 = input 1
+        %2 = input 2
+        %3 = input 3
+        %4 = input 4
+        %5 = input 5
+        %6 = input 6
+        %7 = input 7
+        %8 = input 8
+        %9 = input 9
+        %10 = input 10
+        %11 = input 11
+        %12 = input 12
+        %13 = mul %4 %2
+        %14 = mul %6 %1
+        %15 = add %13 %14
+        %16 = mul %5 %3
+        %17 = mul %1 %1
+        %18 = mul %7 %17
+        %19 = add %16 %18
+        %20 = div %15 %8
+        %21 = div %19 %9
+        %22 = sqrt %21
+        %23 = add %22 %11
+        %24 = div %20 %23
+        %25 = mul %12 %0
+        %26 = add %24 %25
+        %27 = mul %10 %26
+        %28 = sub %0 %27
+    """)
+
+
+ADAMW_GROUP_M, ADAMW_GROUP_V, ADAMW_GROUP_THETA = 15, 19, 28

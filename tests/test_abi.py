@@ -309,3 +309,61 @@ def test_schedule_lr_matches_oracle(lib, orc):
         with pytest.raises(P.PskError) as ei:
             P.psk_adamw_lr(P.adamw_config(3e-4, 0.9, 0.999, 1e-8, 0.01, schedule="cosine", **bad))
         assert ei.value.status == P.PSK_E_SHAPE
+
+
+def test_extra_output_refusals(lib):
+    from synth import configs as C
+    pw = "%0 = input 0\n%1 = exp %0\n%2 = tanh %1\n"
+    ok = _desc(pw, F, (8, 16), extras=[(1, (8, 16), "bf16")])
+    assert "xo0" in P.psk_group_source(ok)
+    _refused(_desc(pw, F, (8, 16), extras=[(0, (8, 16), "f32")]), P.PSK_E_ROOT)       # an input
+    _refused(_desc(pw, F, (8, 16), extras=[(2, (8, 16), "f32")]), P.PSK_E_ROOT)       # the root
+    _refused(_desc(pw, F, (8, 16), extras=[(1, (8, 16), "f32"), (1, (8, 16), "f32")]), P.PSK_E_ROOT)
+    _refused(_desc(pw, F, (8, 16), extras=[(7, (8, 16), "f32")]), P.PSK_E_ROOT)       # out of range
+    _refused(_desc(pw, F, (8, 16), extras=[(1, (8, 1), "f32")]), P.PSK_E_SHAPE)       # element value, row shape
+    _refused(_desc(pw, F, (8, 16), extras=[(1, (8, 16), 7)]), P.PSK_E_TYPE)
+    _refused(_desc(pw, F, (8, 16), extras=[(1, (8, 16), "f32")] * 8), P.PSK_E_CAP)
+    # a second unread member is kept only as a stored value
+    two = "%0 = input 0\n%1 = exp %0\n%2 = tanh %0\n"
+    _refused(_desc(two, F, (8, 16), root=2), P.PSK_E_ROOT)
+    assert P.psk_group_source(_desc(two, F, (8, 16), root=2, extras=[(1, (8, 16), "f32")]))
+    # a row value is stored per row
+    rows = "%0 = input 0\n%1 = row_max %0\n%2 = sub %0 %1\n"
+    _refused(_desc(rows, F, (8, 16), extras=[(1, (8, 16), "f32")]), P.PSK_E_SHAPE)
+    assert "xo0[row]" in P.psk_group_source(_desc(rows, F, (8, 16), extras=[(1, (8, 1), "f32")]))
+    # tree-mapped groups store element values only
+    tree = dict(flags=P.PSK_GROUP_TREE)
+    _refused(_desc("%0 = input 0\n%1 = input 1\n%2 = mul %1 %1\n%3 = mul %0 %2\n", [((1,), "f32"), ((), "f32")],
+                   (1,), extras=[(2, (1,), "f32")], **tree), P.PSK_E_SHAPE)
+
+
+def test_multi_output_kernels_compile(lib, tmp_path):
+    from synth import configs as C
+    eps = C.f32(1e-5)
+    R, N = 16384, 4096
+    descs = {
+        "layernorm": P.GroupDesc(C.layernorm_dag(eps), [((R, N), "bf16"), ((N,), "bf16"), ((N,), "bf16")], (R, N),
+                                 "bf16", root=C.LAYERNORM_ROOT,
+                                 extras=[(C.LAYERNORM_MEAN, (R, 1), "f32"), (C.LAYERNORM_RSTD, (R, 1), "f32")]),
+        "add_rmsnorm_h": P.GroupDesc(C.rmsnorm_gelu_dag(eps), [((R, N), "bf16"), ((R, N), "bf16"), ((N,), "bf16")],
+                                     (R, N), "bf16", extras=[(C.RMSNORM_H, (R, N), "bf16")]),
+        "adamw_tree": P.GroupDesc(C.adamw_group_dag(), [((1,), "bf16"), ((1,), "bf16"), ((1,), "f32"), ((1,), "f32")]
+                                  + [((), "f32")] * 9, (1,), "bf16", flags=P.PSK_GROUP_TREE,
+                                  extras=[(C.ADAMW_GROUP_M, (1,), "f32"), (C.ADAMW_GROUP_V, (1,), "f32")]),
+    }
+    for name, d in descs.items():
+        asm, notes = _isa(P.psk_group_code_object(d), tmp_path, name)
+        assert not re.search(r"v_pk_(fma|mul|add)_f32", asm), name
+        assert re.search(r"\.private_segment_fixed_size:\s+0\b", notes), name
+        g = P.psk_group_create(d)
+        info = P.psk_group_get_info(g)
+        P.psk_group_destroy(g)
+        if name == "layernorm":
+            # mean then variance: two reduction phases in one kernel; the
+            # algorithmic bytes count the two per-row statistics
+            assert info.kind == 1 and info.phases == 2 and info.n_reductions == 2
+            assert info.algorithmic_bytes == R * N * 2 * 2 + 2 * N * 2 + 2 * R * 4
+        if name == "add_rmsnorm_h":
+            assert info.algorithmic_bytes == R * N * 2 * 4 + N * 2
+        if name == "adamw_tree":
+            assert info.kind == 2 and info.vec == 4
