@@ -226,6 +226,30 @@ def tree_sgd(P, configs, torch, dev, state):
     return tree, group, torch.tensor(1e-4, dtype=torch.float32, device=dev)
 
 
+def layernorm_group(P, configs):
+    R, C = 16384, 4096
+    return P.Group(configs.layernorm_dag(configs.f32(1e-5)), [((R, C), "bf16"), ((C,), "bf16"), ((C,), "bf16")],
+                   (R, C), "bf16", root=configs.LAYERNORM_ROOT,
+                   extras=[(configs.LAYERNORM_MEAN, (R, 1), "f32"), (configs.LAYERNORM_RSTD, (R, 1), "f32")])
+
+
+def adamw_group(P, configs, torch, dev, state, hp):
+    """The AdamW step written as a group (m', v' stored, theta' the root),
+    mapped over the Llama tree in place; the nine f32 step scalars are
+    formed on the host in f64 and rounded once, as the library does."""
+    import numpy as np
+    b1, b2, t = hp[1], hp[2], hp[5]
+    sc = np.array([b1, b2, 1 - b1, 1 - b2, 1 - b1 ** t, 1 - b2 ** t, hp[0], hp[3], hp[4]], np.float64)
+    scal = torch.from_numpy(sc.astype(np.float32)).to(dev)
+    grp = P.Group(configs.adamw_group_dag(), [((1,), "bf16"), ((1,), "bf16"), ((1,), "f32"), ((1,), "f32")] +
+                  [((), "f32")] * 9, (1,), "bf16", tree=True,
+                  extras=[(configs.ADAMW_GROUP_M, (1,), "f32"), (configs.ADAMW_GROUP_V, (1,), "f32")])
+    tree = P.Tree([[s["theta"], s["grad"], s["m"], s["v"]] for s in state])
+    args = (tree, [0, 1, 2, 3] + [-1] * 9, [0, 2, 3], [None] * 4 + [scal[i] for i in range(9)])
+    grp._keep = (tree, scal)
+    return grp, args
+
+
 def profile_others(P, configs, torch, dev, stream, hp, state):
     tiny_shapes = [s for _, s in configs.tiny_gpt_leaves()]
     tiny = configs.adamw_state(tiny_shapes, device=dev, seed=configs.SEED_BASE)
@@ -239,9 +263,17 @@ def profile_others(P, configs, torch, dev, stream, hp, state):
     chain = P.Group(configs.chain64_dag(), [((16384, 16384), "f32"), ((16384, 1), "f32"), ((1, 16384), "f32")],
                     (16384, 16384), "f32")
     sgd_tree, sgd, lr = tree_sgd(P, configs, torch, dev, state)
+    xl, gl, bl = configs.layernorm_inputs(16384, 4096, device=dev)
+    yl = torch.empty_like(xl)
+    ml = torch.empty((16384, 1), device=dev)
+    rl = torch.empty((16384, 1), device=dev)
+    ln = layernorm_group(P, configs)
+    adamw_g, adamw_args = adamw_group(P, configs, torch, dev, state, hp)
     torch.cuda.synchronize()
     for _ in range(2):
         sgd.run_tree(sgd_tree, [0, 1, -1], 0, [None, None, lr], stream=stream)
+        ln.run([xl, gl, bl], yl, stream=stream, extra_outs=[ml, rl])
+        adamw_g.run_tree(*adamw_args, stream=stream)
         tiny_tree.adamw_step(*hp, stream=stream)
         rms.run([x, r, g], y, stream=stream)
         chain.run([A, B, Cc], Z, stream=stream)
@@ -307,6 +339,29 @@ def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, pro
     rms = P.Group(configs.rmsnorm_gelu_dag(configs.f32(1e-5)),
                   [((16384, 4096), "bf16"), ((16384, 4096), "bf16"), ((4096,), "bf16")], (16384, 4096), "bf16")
     add("rmsnorm_gelu_bf16", rms.info.algorithmic_bytes, lambda: rms.run([x, r, g], y, stream=stream))
+
+    # layer normalization with its row statistics, bf16 [16384, 4096]: one
+    # kernel, two reduction phases, three outputs
+    xl, gl, bl = configs.layernorm_inputs(16384, 4096, device=dev)
+    yl = torch.empty_like(xl)
+    ml = torch.empty((16384, 1), device=dev)
+    rl = torch.empty((16384, 1), device=dev)
+    ln = layernorm_group(P, configs)
+    add("layernorm_stats_bf16", ln.info.algorithmic_bytes,
+        lambda: ln.run([xl, gl, bl], yl, stream=stream, extra_outs=[ml, rl]),
+        note="mean, x - mean read twice, variance, normalise; mean and rstd stored per row")
+
+    # add + RMSNorm + gamma + GELU that also stores h = x + res in place over res
+    rms_h = P.Group(configs.rmsnorm_gelu_dag(configs.f32(1e-5)),
+                    [((16384, 4096), "bf16"), ((16384, 4096), "bf16"), ((4096,), "bf16")], (16384, 4096), "bf16",
+                    extras=[(configs.RMSNORM_H, (16384, 4096), "bf16")])
+    add("add_rmsnorm_gelu_store_h_bf16", rms_h.info.algorithmic_bytes,
+        lambda: rms_h.run([x, r, g], y, stream=stream, extra_outs=[r]), note="h written in place over the residual")
+
+    # the AdamW step as an emitted three-output tree-mapped group
+    adamw_g, adamw_args = adamw_group(P, configs, torch, dev, state, hp)
+    add("adamw_llama_bf16_emitted_group", adamw_bytes, lambda: adamw_g.run_tree(*adamw_args, stream=stream),
+        note="the generic tree-mapped group path; bit-identical to the hand-written kernel")
 
     # 64-node chain over [16384, 16384]
     A, B, Cc = configs.chain_inputs(16384, 16384, device=dev)

@@ -69,7 +69,8 @@ class psk_group_info(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("members", ctypes.c_int32), ("n_reductions", ctypes.c_int32),
                 ("phases", ctypes.c_int32), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("lanes_per_row", ctypes.c_int32), ("vec", ctypes.c_int32), ("block", ctypes.c_int32),
-                ("rows_per_block", ctypes.c_int32), ("algorithmic_bytes", ctypes.c_int64)]
+                ("rows_per_block", ctypes.c_int32), ("algorithmic_bytes", ctypes.c_int64),
+                ("kernel", ctypes.c_char * 48)]
 
 
 class psk_leaf(ctypes.Structure):

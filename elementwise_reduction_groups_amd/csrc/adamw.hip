@@ -117,59 +117,64 @@ adamw_tree_kernel(const LeafDev* __restrict__ leaves, const ChunkDev* __restrict
     const unsigned vb = xcd_block(blockIdx.x, per_xcd);
     if (vb >= n_virtual) return;
     const ChunkDev ch = chunks[vb / kSub];
-    const LeafDev L = leaves[ch.leaf];
+    const LeafDev* L = leaves + ch.leaf;   // only the slots used are read
     const int i0 = ((int)(vb % kSub) * kBlock + (int)threadIdx.x) * kPer;   // offset within the chunk
     const int cnt = ch.count - i0;
     if (cnt <= 0) return;
     const int64_t e0 = ch.start + i0;
-    const bool full = (L.flags & 1) != 0 && cnt >= kPer;
+    const bool full = (L->flags & 1) != 0 && cnt >= kPer;
 
     float th[kPer], g[kPer], m[kPer], v[kPer];
     if (full) {
-        Io<TP>::load4(L.in[0], e0, th);
-        Io<TG>::load4(L.in[1], e0, g);
-        Io<TM>::load4(L.in[2], e0, m);
-        Io<TM>::load4(L.in[3], e0, v);
+        Io<TP>::load4(L->in[0], e0, th);
+        Io<TG>::load4(L->in[1], e0, g);
+        Io<TM>::load4(L->in[2], e0, m);
+        Io<TM>::load4(L->in[3], e0, v);
     } else {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             th[j] = g[j] = m[j] = v[j] = 0.0f;
             if (j < cnt) {
-                th[j] = Io<TP>::load1(L.in[0], e0 + j);
-                g[j] = Io<TG>::load1(L.in[1], e0 + j);
-                m[j] = Io<TM>::load1(L.in[2], e0 + j);
-                v[j] = Io<TM>::load1(L.in[3], e0 + j);
+                th[j] = Io<TP>::load1(L->in[0], e0 + j);
+                g[j] = Io<TG>::load1(L->in[1], e0 + j);
+                m[j] = Io<TM>::load1(L->in[2], e0 + j);
+                v[j] = Io<TM>::load1(L->in[3], e0 + j);
             }
         }
     }
+    // the moments first: their stores leave while theta' is computed
     float to[kPer], mo[kPer], vo[kPer];
     const float gs = SCALE ? *gscale : 1.0f;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const float gj = SCALE ? g[j] * gs : g[j];
-        float m2 = s.b1 * m[j] + s.c1 * gj;
-        float v2 = s.b2 * v[j] + s.c2 * (gj * gj);
-        m2 = Io<TM>::through(m2);
-        v2 = Io<TM>::through(v2);
-        const float mh = m2 / s.bc1;
-        const float vh = v2 / s.bc2;
-        const float upd = mh / (sqrtf(vh) + s.eps) + s.wd * th[j];
-        to[j] = th[j] - s.lr * upd;
-        mo[j] = m2;
-        vo[j] = v2;
+        mo[j] = Io<TM>::through(s.b1 * m[j] + s.c1 * gj);
+        vo[j] = Io<TM>::through(s.b2 * v[j] + s.c2 * (gj * gj));
     }
     if (full) {
-        Io<TP>::store4(L.out[0], e0, to);
-        Io<TM>::store4(L.out[1], e0, mo);
-        Io<TM>::store4(L.out[2], e0, vo);
+        Io<TM>::store4(L->out[1], e0, mo);
+        Io<TM>::store4(L->out[2], e0, vo);
     } else {
 #pragma unroll
         for (int j = 0; j < kPer; ++j)
             if (j < cnt) {
-                Io<TP>::store1(L.out[0], e0 + j, to[j]);
-                Io<TM>::store1(L.out[1], e0 + j, mo[j]);
-                Io<TM>::store1(L.out[2], e0 + j, vo[j]);
+                Io<TM>::store1(L->out[1], e0 + j, mo[j]);
+                Io<TM>::store1(L->out[2], e0 + j, vo[j]);
             }
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const float mh = mo[j] / s.bc1;
+        const float vh = vo[j] / s.bc2;
+        const float upd = mh / (sqrtf(vh) + s.eps) + s.wd * th[j];
+        to[j] = th[j] - s.lr * upd;
+    }
+    if (full) {
+        Io<TP>::store4(L->out[0], e0, to);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (j < cnt) Io<TP>::store1(L->out[0], e0 + j, to[j]);
     }
 }
 

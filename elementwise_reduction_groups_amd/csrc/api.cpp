@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <cstdio>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -168,6 +169,7 @@ extern "C" psk_status psk_group_get_info(const psk_group* group, psk_group_info*
         if (in.used) bytes += in.numel * esize(in.dtype);
     for (const auto& x : an.extras) bytes += (x.per_row ? an.rows : an.numel) * esize(x.dtype);
     info->algorithmic_bytes = bytes;
+    std::snprintf(info->kernel, sizeof info->kernel, "%s", group->vec->name.c_str());
     return PSK_OK;
 }
 

@@ -218,7 +218,8 @@ typedef struct psk_group_info {
     int32_t vec;             /* elements per vector access */
     int32_t block;           /* threads per workgroup */
     int32_t rows_per_block;  /* row kernel */
-    int64_t algorithmic_bytes; /* inputs read once at their own size + output written once */
+    int64_t algorithmic_bytes; /* inputs read once at their own size + outputs written once */
+    char kernel[48];         /* the emitted kernel's name (as profilers show it), NUL-terminated */
 } psk_group_info;
 psk_status psk_group_get_info(const psk_group* group, psk_group_info* info);
 
