@@ -23,7 +23,7 @@ STATUS_NAMES = ["PSK_OK", "PSK_E_NULL", "PSK_E_CAP", "PSK_E_ORDER", "PSK_E_ROOT"
 for _i, _n in enumerate(STATUS_NAMES):
     globals()[_n] = _i
 
-PSK_F32, PSK_BF16 = 0, 1
+PSK_F32, PSK_BF16, PSK_U8 = 0, 1, 2
 PSK_GROUP_TREE = 1
 PSK_MAX_RANK = 4
 PSK_MAX_SLOTS = 8
@@ -34,7 +34,7 @@ OPCODES = {
     "add": 10, "sub": 11, "mul": 12, "div": 13, "max": 14, "min": 15,
     "neg": 20, "abs": 21, "exp": 22, "log": 23, "sqrt": 24, "tanh": 25, "erf": 26, "gelu": 27,
     "sqrtabs": 28, "pow2": 29, "pown": 30,
-    "select": 40, "causal_mask": 41,
+    "select": 40, "causal_mask": 41, "where": 42,
     "row_max": 50, "row_sum": 51, "row_mean": 52,
     "reduce": 60, "contract": 61, "matmul": 61, "cast": 62, "opaque": 63,
 }
@@ -173,6 +173,8 @@ def _dtype_code(dt) -> int:
         return PSK_F32
     if s in ("bf16", "bfloat16", "torch.bfloat16"):
         return PSK_BF16
+    if s in ("u8", "uint8", "bool", "torch.uint8", "torch.bool"):
+        return PSK_U8
     raise ValueError(f"unsupported storage type {dt!r}")
 
 

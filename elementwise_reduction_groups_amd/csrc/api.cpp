@@ -115,7 +115,7 @@ static psk_status kernel_function(Kernel& k, hipFunction_t& fn)
     return PSK_OK;
 }
 
-static int esize(int dt) { return dt == PSK_BF16 ? 2 : 4; }
+static int esize(int dt) { return dt == PSK_BF16 ? 2 : dt == PSK_U8 ? 1 : 4; }
 
 }  // namespace psk
 

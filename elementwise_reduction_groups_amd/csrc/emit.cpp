@@ -181,6 +181,7 @@ namespace {
 const char* kPrelude = R"PSK(
 typedef unsigned int psk_u32;
 typedef unsigned short psk_u16;
+typedef unsigned char psk_u8;
 typedef float psk_f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 psk_b2 __attribute__((ext_vector_type(2)));
 typedef unsigned psk_u4v __attribute__((ext_vector_type(4)));
@@ -432,14 +433,23 @@ struct Emitter {
             return s;
         }
         case PSK_OP_SELECT: return "((" + A() + " != 0.0f) ? " + B() + " : " + C() + ")";
+        case PSK_OP_WHERE: return "((" + A() + " != 0.0f) ? " + B() + " : " + flit(nd.imm) + ")";
         case PSK_OP_CAUSAL_MASK: return "((" + col(e) + " <= q) ? " + A() + " : (-__builtin_inff()))";
         default: return "0.0f";
         }
     }
 
-    static int esize(psk_dtype d) { return d == PSK_BF16 ? 2 : 4; }
+    static int esize(psk_dtype d) { return d == PSK_BF16 ? 2 : d == PSK_U8 ? 1 : 4; }
 
-    std::string ptype(psk_dtype d) const { return d == PSK_BF16 ? "psk_u16" : "float"; }
+    std::string ptype(psk_dtype d) const { return d == PSK_BF16 ? "psk_u16" : d == PSK_U8 ? "psk_u8" : "float"; }
+
+    // a loaded element as f32: bf16 widened, a mask byte as 0.0 or its value
+    static std::string widen(psk_dtype d, const std::string& x)
+    {
+        if (d == PSK_BF16) return "psk_h(" + x + ")";
+        if (d == PSK_U8) return "(float)(" + x + ")";
+        return x;
+    }
 
     // offset expression of input k's row part for the current row variable `rv`
     std::string row_offset(const InputInfo& in, const std::string& rv) const
@@ -476,8 +486,20 @@ struct Emitter {
         auto dst = [&](int j) { return "x" + ks + "_" + std::to_string(e0 + j); };
         if (V == 1) {
             o << "    float " << dst(0) << " = 0.0f;\n";
-            o << "    if (" << cond << ") " << dst(0) << " = "
-              << (in.dtype == PSK_BF16 ? "psk_h(psk_ld(" + p + "))" : "psk_ld(" + p + ")") << ";\n";
+            o << "    if (" << cond << ") " << dst(0) << " = " << widen(in.dtype, "psk_ld(" + p + ")") << ";\n";
+            return;
+        }
+        if (in.dtype == PSK_U8) {
+            // V mask bytes: one 4-, 8- or 16-byte load
+            const int nw = std::max(1, V / 4);
+            std::string wn = "w" + ks + "_" + std::to_string(e0);
+            const char* vt = nw == 1 ? "psk_u32" : nw == 2 ? "psk_u2v" : "psk_u4v";
+            o << "    " << vt << " " << wn << " = {};\n";
+            o << "    if (" << cond << ") " << wn << " = psk_ld((const " << vt << "*)(" << p << "));\n";
+            for (int j = 0; j < V; ++j) {
+                std::string w = nw == 1 ? wn : wn + "[" + std::to_string(j / 4) + "]";
+                o << "    const float " << dst(j) << " = (float)((" << w << " >> " << 8 * (j % 4) << ") & 255u);\n";
+            }
             return;
         }
         int nwords = bytes / 4;
@@ -697,8 +719,7 @@ struct Emitter {
             if (!in.used || !(in.kind == InKind::Scalar || in.kind == InKind::RowConst)) continue;
             std::string off = in.kind == InKind::Scalar ? "0" : row_offset(in, rv);
             std::string p = "(in" + std::to_string(k) + " + " + off + ")";
-            o << "    const float xr" << k << " = (" << cond << ") ? "
-              << (in.dtype == PSK_BF16 ? "psk_h(*" + p + ")" : "*" + p) << " : 0.0f;\n";
+            o << "    const float xr" << k << " = (" << cond << ") ? " << widen(in.dtype, "*" + p) << " : 0.0f;\n";
         }
     }
 

@@ -31,7 +31,7 @@ bool op_is_elementwise(int op)
     case PSK_OP_ADD: case PSK_OP_SUB: case PSK_OP_MUL: case PSK_OP_DIV: case PSK_OP_MAX: case PSK_OP_MIN:
     case PSK_OP_NEG: case PSK_OP_ABS: case PSK_OP_EXP: case PSK_OP_LOG: case PSK_OP_SQRT: case PSK_OP_TANH:
     case PSK_OP_ERF: case PSK_OP_GELU: case PSK_OP_SQRTABS: case PSK_OP_POW2: case PSK_OP_POWN:
-    case PSK_OP_SELECT: case PSK_OP_CAUSAL_MASK:
+    case PSK_OP_SELECT: case PSK_OP_CAUSAL_MASK: case PSK_OP_WHERE:
         return true;
     default:
         return false;
@@ -43,7 +43,7 @@ int op_arity(int op)
     switch (op) {
     case PSK_OP_INPUT: case PSK_OP_CONST: return 0;
     case PSK_OP_ADD: case PSK_OP_SUB: case PSK_OP_MUL: case PSK_OP_DIV: case PSK_OP_MAX: case PSK_OP_MIN:
-    case PSK_OP_CONTRACT:
+    case PSK_OP_CONTRACT: case PSK_OP_WHERE:
         return 2;
     case PSK_OP_SELECT: return 3;
     case PSK_OP_OPAQUE: return -1;  // any number of operands
@@ -61,7 +61,8 @@ const char* op_name(int op)
     case PSK_OP_LOG: return "log"; case PSK_OP_SQRT: return "sqrt"; case PSK_OP_TANH: return "tanh";
     case PSK_OP_ERF: return "erf"; case PSK_OP_GELU: return "gelu"; case PSK_OP_SQRTABS: return "sqrtabs";
     case PSK_OP_POW2: return "pow2"; case PSK_OP_POWN: return "pown"; case PSK_OP_SELECT: return "select";
-    case PSK_OP_CAUSAL_MASK: return "causal_mask"; case PSK_OP_ROW_MAX: return "row_max";
+    case PSK_OP_CAUSAL_MASK: return "causal_mask"; case PSK_OP_WHERE: return "where";
+    case PSK_OP_ROW_MAX: return "row_max";
     case PSK_OP_ROW_SUM: return "row_sum"; case PSK_OP_ROW_MEAN: return "row_mean";
     case PSK_OP_REDUCE: return "reduce"; case PSK_OP_CONTRACT: return "contract"; case PSK_OP_CAST: return "cast";
     case PSK_OP_OPAQUE: return "opaque";
@@ -70,6 +71,7 @@ const char* op_name(int op)
 }
 
 static bool dtype_ok(int32_t d) { return d == PSK_F32 || d == PSK_BF16; }
+static bool input_dtype_ok(int32_t d) { return dtype_ok(d) || d == PSK_U8; }
 
 static std::string at(int i) { return "node " + std::to_string(i) + ": "; }
 
@@ -122,8 +124,10 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
                                      "element) or 0 (per tree)");
         if (t.rank > o.rank)
             return fail(PSK_E_BROADCAST, "input " + std::to_string(k) + ": rank above the output's");
-        if (!dtype_ok(t.dtype))
-            return fail(PSK_E_TYPE, "input " + std::to_string(k) + ": storage type must be f32 or bf16");
+        if (!input_dtype_ok(t.dtype))
+            return fail(PSK_E_TYPE, "input " + std::to_string(k) + ": storage type must be f32, bf16 or u8 (a mask)");
+        if (t.dtype == PSK_U8 && (desc->flags & PSK_GROUP_TREE))
+            return fail(PSK_E_TYPE, "input " + std::to_string(k) + ": a tree-mapped group has no mask inputs");
         in.dtype = (psk_dtype)t.dtype;
         in.rank = t.rank;
         in.numel = 1;
@@ -197,6 +201,22 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
             return fail(PSK_E_OP, at(i) + "causal_mask period must be >= 1");
         if (!op_is_leaf(nd.op))
             an.members++;
+    }
+    // a mask (u8 input) is read only as the mask of a WHERE, and a WHERE's
+    // mask is a mask input
+    for (int i = 0; i < n; ++i) {
+        const psk_node& nd = an.nodes[i];
+        auto is_mask = [&](int j) {
+            return an.nodes[j].op == PSK_OP_INPUT && desc->inputs[an.nodes[j].iparam].dtype == PSK_U8;
+        };
+        const int ar = op_arity(nd.op);
+        const int32_t opnd[3] = {nd.a, nd.b, nd.c};
+        for (int k = 0; k < ar; ++k) {
+            const bool mask_slot = nd.op == PSK_OP_WHERE && k == 0;
+            if (is_mask(opnd[k]) != mask_slot)
+                return fail(PSK_E_TYPE, at(i) + (mask_slot ? "the first operand of where must be a mask (u8) input"
+                                                           : "a mask (u8 input) enters no arithmetic; only where reads it"));
+        }
     }
     if (an.members > PSK_MAX_MEMBERS)
         return fail(PSK_E_CAP, "group has " + std::to_string(an.members) +

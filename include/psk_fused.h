@@ -78,7 +78,11 @@ typedef enum psk_status {
 /* Storage types.  bf16 is storage only: a load widens exactly (a 16-bit
  * shift), a store rounds to nearest even (presk manual, "Native execution",
  * section "The realization"). */
-typedef enum psk_dtype { PSK_F32 = 0, PSK_BF16 = 1 } psk_dtype;
+/* Storage types.  PSK_U8 is an input-only mask: one byte per element, 0
+ * refuses and any other value allows (presk language reference, "Typing",
+ * builtins: a bool mask is an index buffer of 0 and 1 that enters no
+ * arithmetic).  torch.bool and torch.uint8 buffers are such masks. */
+typedef enum psk_dtype { PSK_F32 = 0, PSK_BF16 = 1, PSK_U8 = 2 } psk_dtype;
 
 /* Node ops.  Elementwise set after poot "Fusion and Planning" (binary ops;
  * Neg, Exp, Log, Sqrt, Tanh, Erf; Select) and the presk builtins (gelu,
@@ -105,6 +109,14 @@ typedef enum psk_dtype { PSK_F32 = 0, PSK_BF16 = 1 } psk_dtype;
  *                            flattened index over all axes but the last
  *                            (causal_mask: allowed where seq2 <= seq, presk
  *                            language reference, section "Typing", builtins)
+ *   WHERE (imm = fill)       b where the mask a allows (a != 0), else imm: a
+ *                            is a PSK_U8 input, the only op that may read one.
+ *                            With fill -inf before a row max and 0 after the
+ *                            division it gives the masked softmax of the
+ *                            presk manual ("Native execution", "The
+ *                            realization"): maximum and sum over the allowed
+ *                            positions, 0 where refused, a row the mask
+ *                            empties giving zeros
  *   ROW_MAX ROW_SUM ROW_MEAN reduction over the last axis, keepdim; the
  *                            result broadcasts back along the row.  ROW_MEAN
  *                            is ROW_SUM divided by the row length.
@@ -118,7 +130,7 @@ typedef enum psk_op {
     PSK_OP_ADD = 10, PSK_OP_SUB = 11, PSK_OP_MUL = 12, PSK_OP_DIV = 13, PSK_OP_MAX = 14, PSK_OP_MIN = 15,
     PSK_OP_NEG = 20, PSK_OP_ABS = 21, PSK_OP_EXP = 22, PSK_OP_LOG = 23, PSK_OP_SQRT = 24, PSK_OP_TANH = 25,
     PSK_OP_ERF = 26, PSK_OP_GELU = 27, PSK_OP_SQRTABS = 28, PSK_OP_POW2 = 29, PSK_OP_POWN = 30,
-    PSK_OP_SELECT = 40, PSK_OP_CAUSAL_MASK = 41,
+    PSK_OP_SELECT = 40, PSK_OP_CAUSAL_MASK = 41, PSK_OP_WHERE = 42,
     PSK_OP_ROW_MAX = 50, PSK_OP_ROW_SUM = 51, PSK_OP_ROW_MEAN = 52,
     PSK_OP_REDUCE = 60, PSK_OP_CONTRACT = 61, PSK_OP_CAST = 62, PSK_OP_OPAQUE = 63
 } psk_op;

@@ -27,7 +27,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 CFLAGS = ["-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math",
           "-fPIC", "-shared"]
 
-F32, BF16 = 0, 1
+F32, BF16, U8 = 0, 1, 2
 
 # this oracle's own op numbering (mirrors the enum in oracle.c)
 _OPCODE = {name: i for i, name in enumerate([
@@ -36,6 +36,7 @@ _OPCODE = {name: i for i, name in enumerate([
     "neg", "abs", "exp", "log", "sqrt", "tanh", "erf", "gelu", "sqrtabs",
     "pow2", "pown", "select", "causal_mask",
     "row_max", "row_sum", "row_mean",
+    "where",
 ])}
 
 
@@ -118,7 +119,9 @@ def _dtype_code(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:
         return BF16
-    raise TypeError(f"oracle arrays are float32 or uint16 (bf16 bits), got {a.dtype}")
+    if a.dtype in (np.uint8, np.bool_):
+        return U8
+    raise TypeError(f"oracle arrays are float32, uint16 (bf16 bits) or uint8/bool (a mask), got {a.dtype}")
 
 
 # ------------------------------------------------------------ group evaluator

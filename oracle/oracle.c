@@ -63,12 +63,15 @@ void orc_bf16_round_array(int64_t n, const float *in, uint16_t *out)
         out[i] = orc_bf16_round(in[i]);
 }
 
-enum { ORC_F32 = 0, ORC_BF16 = 1 };
+/* storage types; ORC_U8 is a mask (one byte per element, read as its value) */
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_U8 = 2 };
 
 static float load_elem(const void *base, int dtype, int64_t i)
 {
     if (dtype == ORC_BF16)
         return orc_bf16_widen(((const uint16_t *)base)[i]);
+    if (dtype == ORC_U8)
+        return (float)((const uint8_t *)base)[i];
     return ((const float *)base)[i];
 }
 
@@ -113,6 +116,7 @@ enum {
     O_NEG, O_ABS, O_EXP, O_LOG, O_SQRT, O_TANH, O_ERF, O_GELU, O_SQRTABS,
     O_POW2, O_POWN, O_SELECT, O_CAUSAL_MASK,
     O_ROW_MAX, O_ROW_SUM, O_ROW_MEAN,
+    O_WHERE,
     O_NUM_OPS
 };
 
@@ -244,6 +248,11 @@ int orc_eval_group_multi(int n_nodes, const orc_node *nodes, int root,
             case O_SELECT:
                 /* bit-moving select: the branch not picked is never read */
                 for (int64_t c = 0; c < C; ++c) v[c] = (A[c] != 0.0f) ? B[c] : Cc[c];
+                break;
+            case O_WHERE:
+                /* a mask selects: b where it allows, the fill value where it refuses
+                 * (presk language reference, "Typing": softmax(..., where = m)) */
+                for (int64_t c = 0; c < C; ++c) v[c] = (A[c] != 0.0f) ? B[c] : nd->imm;
                 break;
             case O_CAUSAL_MASK: {
                 int64_t T = nd->iparam;

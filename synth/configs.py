@@ -294,3 +294,47 @@ def adamw_group_dag() -> List[Node]:
 
 
 ADAMW_GROUP_M, ADAMW_GROUP_V, ADAMW_GROUP_THETA = 15, 19, 28
+
+
+# ---------------------------------------------------------------------------
+# Softmax variants: a mask read from a byte buffer, wide rows, bf16 storage.
+def softmax_masked_dag(scale: float = 0.125) -> List[Node]:
+    """Input 0 the scores, input 1 a mask (u8, broadcast into the scores):
+    scale, -inf where the mask refuses, row max, subtract, exp, row sum,
+    divide, then 0 where the mask refuses (so a row it empties is zeros)."""
+    return parse_dag(f"""
+        %0 = input 0
+        %1 = input 1
+        %2 = const {float(scale).hex()}
+        %3 = mul %0 %2
+        %4 = where %1 %3 -inf
+        %5 = row_max %4
+        %6 = sub %4 %5
+        %7 = exp %6
+        %8 = row_sum %7
+        %9 = div %7 %8
+        %10 = where %1 %9 0.0
+    """)
+
+
+def causal_mask_bytes(T: int, device="cpu") -> torch.Tensor:
+    """[T, T] bool, true where column <= row (the causal_mask op's pattern)."""
+    return torch.ones(T, T, dtype=torch.bool, device=device).tril()
+
+
+def padding_mask(lengths: Sequence[int], T: int, device="cpu") -> torch.Tensor:
+    """[B, 1, 1, T] bool key-padding mask: row b allows its first lengths[b]
+    columns (broadcast over heads and query positions)."""
+    m = torch.arange(T)[None, :] < torch.tensor(list(lengths))[:, None]
+    return m[:, None, None, :].to(device)
+
+
+def random_mask(rows: int, cols: int, p_keep: float = 0.5, empty_rows: Sequence[int] = (), device="cpu",
+                seed: int = SEED_BASE + 7) -> torch.Tensor:
+    """[rows, cols] bool, each position allowed with probability p_keep; the
+    listed rows refuse everything."""
+    g = _gen("cpu", seed, 0)
+    m = torch.rand(rows, cols, generator=g) < p_keep
+    for r in empty_rows:
+        m[r] = False
+    return m.to(device)

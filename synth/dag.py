@@ -30,7 +30,7 @@ OPS = {
     "neg": (1, "ew"), "abs": (1, "ew"), "exp": (1, "ew"), "log": (1, "ew"),
     "sqrt": (1, "ew"), "tanh": (1, "ew"), "erf": (1, "ew"), "gelu": (1, "ew"),
     "sqrtabs": (1, "ew"), "pow2": (1, "ew"), "pown": (1, "ew"),
-    "select": (3, "ew"), "causal_mask": (1, "ew"),
+    "select": (3, "ew"), "causal_mask": (1, "ew"), "where": (2, "ew"),
     "row_max": (1, "row"), "row_sum": (1, "row"), "row_mean": (1, "row"),
     # boundaries, only meaningful to the partition
     "reduce": (1, "nonew"), "matmul": (2, "nonew"), "cast": (1, "nonew"),
@@ -39,13 +39,15 @@ OPS = {
 
 # ops that carry an integer parameter after their operands
 _IPARAM_OPS = {"input", "pown", "causal_mask"}
+# ops that carry a float immediate after their operands
+_IMM_OPS = {"const", "where"}
 
 
 @dataclasses.dataclass(frozen=True)
 class Node:
     op: str
     args: Tuple[int, ...] = ()
-    imm: Optional[float] = None      # const value (already an f32 value)
+    imm: Optional[float] = None      # const value (already an f32 value); where's fill value
     iparam: Optional[int] = None     # input slot, pown exponent, causal period
 
     def __post_init__(self):
@@ -65,7 +67,7 @@ def format_dag(nodes: Sequence[Node]) -> str:
     for i, n in enumerate(nodes):
         parts = [f"%{i} =", n.op]
         parts += [f"%{a}" for a in n.args]
-        if n.op == "const":
+        if n.op in _IMM_OPS:
             parts.append(_fmt_imm(n.imm))
         if n.op in _IPARAM_OPS:
             parts.append(str(int(n.iparam)))
@@ -87,7 +89,7 @@ def parse_dag(text: str) -> List[Node]:
         args = tuple(int(t[1:]) for t in rest if t.startswith("%"))
         extra = [t for t in rest if not t.startswith("%")]
         imm = iparam = None
-        if op == "const":
+        if op in _IMM_OPS:
             s = extra.pop(0)
             imm = float.fromhex(s) if "0x" in s.lower() else float(s)
         if op in _IPARAM_OPS:

@@ -367,3 +367,22 @@ def test_multi_output_kernels_compile(lib, tmp_path):
             assert info.algorithmic_bytes == R * N * 2 * 4 + N * 2
         if name == "adamw_tree":
             assert info.kind == 2 and info.vec == 4
+
+
+def test_mask_refusals(lib):
+    from synth.dag import parse_dag
+
+    def refused(status, nodes, inputs, shape, dt="f32"):
+        with pytest.raises(P.PskError) as ei:
+            P.Group(parse_dag(nodes), inputs, shape, dt)
+        assert ei.value.status == status, ei.value.name
+
+    # a mask in arithmetic; a where whose mask is not a mask input; a mask output
+    refused(P.PSK_E_TYPE, "%0 = input 0\n%1 = input 1\n%2 = add %0 %1\n", [((4, 8), "f32"), ((4, 8), "u8")], (4, 8))
+    refused(P.PSK_E_TYPE, "%0 = input 0\n%1 = input 1\n%2 = where %0 %1 0.0\n", [((4, 8), "f32"), ((4, 8), "f32")],
+            (4, 8))
+    refused(P.PSK_E_TYPE, "%0 = input 0\n%1 = input 1\n%2 = where %1 %0 0.0\n", [((4, 8), "f32"), ((4, 8), "u8")],
+            (4, 8), "u8")
+    # a mask may not widen the scores
+    refused(P.PSK_E_BROADCAST, "%0 = input 0\n%1 = input 1\n%2 = where %1 %0 0.0\n",
+            [((4, 8), "f32"), ((2, 4, 8), "u8")], (4, 8))
