@@ -70,7 +70,7 @@ class psk_group_info(ctypes.Structure):
                 ("phases", ctypes.c_int32), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("lanes_per_row", ctypes.c_int32), ("vec", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("rows_per_block", ctypes.c_int32), ("algorithmic_bytes", ctypes.c_int64),
-                ("kernel", ctypes.c_char * 48)]
+                ("kernel", ctypes.c_char * 48), ("tiles", ctypes.c_int32)]
 
 
 class psk_leaf(ctypes.Structure):

@@ -84,7 +84,7 @@ static psk_status get_kernel(const Analysis& an, bool vector, std::shared_ptr<Ke
     auto k = std::make_shared<Kernel>();
     k->plan = plan;
     char nm[64];
-    static const char* const kind_name[3] = {"pw", "row", "tree"};
+    static const char* const kind_name[4] = {"pw", "row", "tree", "rowt"};
     std::snprintf(nm, sizeof nm, "psk_%s_%016llx", kind_name[plan.kind], (unsigned long long)fnv1a(key));
     k->name = nm;
     std::string src = emit_source(an, plan, k->name);
@@ -160,10 +160,11 @@ extern "C" psk_status psk_group_get_info(const psk_group* group, psk_group_info*
     info->phases = an.phases;
     info->rows = an.rows;
     info->cols = an.cols;
-    info->lanes_per_row = p.kind == 1 ? p.lanes : 1;
+    info->lanes_per_row = (p.kind == 1 || p.kind == 3) ? p.lanes : 1;
     info->vec = p.vec;
     info->block = p.block;
-    info->rows_per_block = p.kind == 1 ? p.rows_per_block : 0;
+    info->rows_per_block = (p.kind == 1 || p.kind == 3) ? p.rows_per_block : 0;
+    info->tiles = p.tiles;
     int64_t bytes = an.numel * esize(an.out_dtype);
     for (const InputInfo& in : an.inputs)
         if (in.used) bytes += in.numel * esize(in.dtype);
@@ -239,7 +240,7 @@ static psk_status run_group(const psk_group* group, const void* const* inputs, v
     std::vector<void*> args;
     std::vector<const void*> ptrs(an.inputs.size());
     for (size_t i = 0; i < an.inputs.size(); ++i) ptrs[i] = inputs ? inputs[i] : nullptr;
-    long long n_total = k->plan.kind == 1 ? (long long)an.rows : (long long)an.numel;
+    long long n_total = (k->plan.kind == 1 || k->plan.kind == 3) ? (long long)an.rows : (long long)an.numel;
     for (size_t i = 0; i < ptrs.size(); ++i) args.push_back(&ptrs[i]);
     std::vector<void*> optr(outs, outs + n_out);
     for (int i = 0; i < n_out; ++i) args.push_back(&optr[i]);

@@ -103,8 +103,8 @@ static int layout_value(const char* key, int dflt)
 std::string KernelPlan::key() const
 {
     char b[160];
-    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld", kind, vec, block, lanes, nv, (int)nt, (int)xcd,
-                  (long long)blocks);
+    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d", kind, vec, block, lanes, nv, (int)nt, (int)xcd,
+                  (long long)blocks, tiles);
     return b;
 }
 
@@ -165,6 +165,23 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
         p.block = L > block ? L : block;
         p.rows_per_block = p.block / L;
         p.blocks = ceil_div(an.rows, p.rows_per_block);
+        // Wide rows: past 32 elements per lane the row no longer lives in
+        // registers.  The tiled kernel gives a row one workgroup, walks it in
+        // tiles of lanes * tn vectors, and re-reads it in every phase (the
+        // re-reads of a row come from the caches).
+        if ((int64_t)p.nv * p.vec > 32 || layout_value("tiled", 0)) {
+            p.kind = 3;
+            int Lt = layout_value("lanes", 1024);
+            if (!(Lt >= 64 && Lt <= 1024 && !(Lt & (Lt - 1)))) Lt = 1024;
+            int tn = layout_value("tn", 2);
+            if (tn < 1 || tn > 8) tn = 2;
+            p.lanes = Lt;
+            p.nv = tn;
+            p.tiles = (int)ceil_div(an.cols, (int64_t)Lt * tn * p.vec);
+            p.block = Lt;
+            p.rows_per_block = 1;
+            p.blocks = an.rows;
+        }
     }
     if (p.xcd) {
         p.per_xcd = ceil_div(p.blocks, 8);
@@ -307,12 +324,14 @@ struct Emitter {
 
     Emitter(const Analysis& a, const KernelPlan& p) : an(a), pl(p)
     {
-        NE = (pl.kind == 1 ? pl.nv : 1) * pl.vec;   // tree: elements per thread
+        NE = (pl.kind == 1 || pl.kind == 3 ? pl.nv : 1) * pl.vec;   // tree: elements per thread
         big = an.numel >= (int64_t(1) << 31) - 4096;
         for (auto& nd : an.nodes)
             if (nd.op == PSK_OP_CAUSAL_MASK) period = nd.iparam;
         if (pl.kind == 1)
             ragged = (int64_t)pl.nv * pl.lanes * pl.vec != an.cols;
+        if (pl.kind == 3)
+            ragged = an.cols % ((int64_t)pl.nv * pl.lanes * pl.vec) != 0;
     }
 
     const char* I() const { return big ? "long long" : "int"; }
@@ -321,7 +340,7 @@ struct Emitter {
     std::string col(int e) const
     {
         int k = e / pl.vec, j = e % pl.vec;
-        if (pl.kind == 1)
+        if (pl.kind == 1 || pl.kind == 3)
             return "(c" + std::to_string(k) + " + " + std::to_string(j) + ")";
         return "(c0 + " + std::to_string(j) + ")";
     }
@@ -603,7 +622,7 @@ struct Emitter {
     // are computed as usual.
     bool skip_refused() const
     {
-        if (pl.kind != 1 || an.mask_period <= 0) return false;
+        if (pl.kind != 1 || an.mask_period <= 0) return false;   // not in the tiled kernel
         for (size_t i = 0; i < an.nodes.size(); ++i)
             if (an.uniform[i] && an.nodes[i].op != PSK_OP_CAUSAL_MASK) return true;
         return false;
@@ -665,12 +684,16 @@ struct Emitter {
     }
 
     // element members of the given depth, and row members of that depth
-    void members_at(int p)
+    // mode 0: element and row members, 1: element members only, 2: row
+    // members only; `only`, when given, selects the members emitted
+    void members_at(int p, int mode = 0, const std::vector<char>* only = nullptr)
     {
-        if (skip_refused()) { members_at_skipping(p); return; }
+        if (mode == 0 && skip_refused()) { members_at_skipping(p); return; }
         for (size_t i = 0; i < an.nodes.size(); ++i) {
             const psk_node& nd = an.nodes[i];
             if (op_is_leaf(nd.op) || op_is_row(nd.op) || an.depth[i] != p) continue;
+            if ((mode == 1 && an.is_row[i]) || (mode == 2 && !an.is_row[i])) continue;
+            if (only && !(*only)[i]) continue;
             if (an.is_row[i]) {
                 o << "    const float r" << i << " = " << rt((int)i, expr((int)i, 0)) << ";\n";
                 row_reciprocal((int)i);
@@ -690,10 +713,15 @@ struct Emitter {
         }
     }
 
-    void leaves()
+    // mode 0: every leaf, 1: constants and row-valued inputs, 2: element
+    // inputs (those in `only`, when given)
+    void leaves(int mode = 0, const std::vector<char>* only = nullptr)
     {
         for (size_t i = 0; i < an.nodes.size(); ++i) {
             const psk_node& nd = an.nodes[i];
+            const bool elem = nd.op == PSK_OP_INPUT && !an.is_row[i];
+            if ((mode == 1 && elem) || (mode == 2 && !elem)) continue;
+            if (only && !(*only)[i]) continue;
             if (nd.op == PSK_OP_CONST) {
                 o << "    const float r" << i << " = " << flit(nd.imm) << ";\n";
                 row_reciprocal((int)i);
@@ -884,27 +912,46 @@ struct Emitter {
     }
 
     // ------------------------------------------------------------------ row
-    void reductions_at(int p)
+    // reductions whose operand has depth p
+    std::vector<int> reductions_of(int p) const
     {
-        // reductions whose operand has depth p
         std::vector<int> reds;
         for (size_t i = 0; i < an.nodes.size(); ++i)
             if (op_is_row(an.nodes[i].op) && an.depth[i] == p + 1) reds.push_back((int)i);
-        if (reds.empty()) return;
-        const int W = pl.lanes / 64;
+        return reds;
+    }
+
+    void reduce_declare(const std::vector<int>& reds)
+    {
+        for (int i : reds)
+            o << "    float p" << i << " = " << (an.nodes[i].op == PSK_OP_ROW_MAX ? "(-__builtin_inff())" : "0.0f")
+              << ";\n";
+    }
+
+    // this lane's elements folded into its partials, in element order
+    void reduce_accumulate(const std::vector<int>& reds, const char* indent = "    ")
+    {
         for (int i : reds) {
             const psk_node& nd = an.nodes[i];
             bool mx = nd.op == PSK_OP_ROW_MAX;
-            o << "    float p" << i << " = " << (mx ? "(-__builtin_inff())" : "0.0f") << ";\n";
             for (int e = 0; e < NE; ++e) {
                 std::string v = val(nd.a, e);
                 std::string acc = mx ? "psk_max(p" + std::to_string(i) + ", " + v + ")"
                                      : "(p" + std::to_string(i) + " + " + v + ")";
                 if (ragged)
-                    o << "    if (" << col(e) << " < " << an.cols << ") p" << i << " = " << acc << ";\n";
+                    o << indent << "if (" << col(e) << " < " << an.cols << ") p" << i << " = " << acc << ";\n";
                 else
-                    o << "    p" << i << " = " << acc << ";\n";
+                    o << indent << "p" << i << " = " << acc << ";\n";
             }
+        }
+    }
+
+    // lanes of a wave (DPP), then waves (LDS), then the row values
+    void reduce_finish(const std::vector<int>& reds, int p)
+    {
+        const int W = pl.lanes / 64;
+        for (int i : reds) {
+            bool mx = an.nodes[i].op == PSK_OP_ROW_MAX;
             if (pl.lanes == 16)
                 o << "    p" << i << " = " << (mx ? "psk_max16" : "psk_sum16") << "(p" << i << ");\n";
             else
@@ -939,6 +986,125 @@ struct Emitter {
                 o << "    const float r" << i << " = " << rt(i, "p" + std::to_string(i)) << ";\n";
             row_reciprocal(i);
         }
+    }
+
+    void reductions_at(int p)
+    {
+        std::vector<int> reds = reductions_of(p);
+        if (reds.empty()) return;
+        reduce_declare(reds);
+        reduce_accumulate(reds);
+        reduce_finish(reds, p);
+    }
+
+    // element nodes the targets read, through element values only (row
+    // values are known by the phase that reads them)
+    std::vector<char> needed_for(const std::vector<int>& targets) const
+    {
+        std::vector<char> need(an.nodes.size(), 0);
+        std::vector<int> st;
+        for (int t : targets)
+            if (!an.is_row[t]) st.push_back(t);
+        while (!st.empty()) {
+            int i = st.back();
+            st.pop_back();
+            if (need[i]) continue;
+            need[i] = 1;
+            const psk_node& nd = an.nodes[i];
+            const int32_t opnd[3] = {nd.a, nd.b, nd.c};
+            for (int k = 0; k < op_arity(nd.op); ++k)
+                if (!an.is_row[opnd[k]]) st.push_back(opnd[k]);
+        }
+        return need;
+    }
+
+    void store_row_extras(int depth)
+    {
+        for (size_t k = 0; k < an.extras.size(); ++k) {
+            const Analysis::Extra& x = an.extras[k];
+            if (x.per_row && an.depth[x.node] == depth)
+                o << "    if (rok && lane == 0) xo" << k << "[row] = " << scalar_store(x.node, x.dtype) << ";\n";
+        }
+    }
+
+    // Wide rows: one workgroup per row; every phase walks the row in tiles
+    // of lanes x nv vectors, re-reading the inputs it needs and recomputing
+    // the element members it needs; partial reductions stay in registers
+    // until the phase ends.  The last phase stores the root and the element
+    // extra outputs.
+    std::string row_tiled(const std::string& name)
+    {
+        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n" << kPrelude;
+        signature(name);
+        const int L = pl.lanes, V = pl.vec, TN = pl.nv;
+        const int64_t tile = (int64_t)L * TN * V;
+        o << "  {\n";
+        o << "    const int slot = 0;\n";
+        o << "    const int lane = (int)threadIdx.x;\n";
+        block_index();
+        o << "    const " << I() << " row = (" << I() << ")vb;\n";
+        o << "    const bool rok = row < (" << I() << ")n_total;\n";
+        if (period > 0) o << "    const int q = (int)(row % (" << I() << ")" << period << ");\n";
+        row_inputs("row", "rok");
+        leaves(1);
+        members_at(0, 2);
+        store_row_extras(0);
+        for (int p = 0; p <= an.phases; ++p) {
+            std::vector<int> reds = p < an.phases ? reductions_of(p) : std::vector<int>();
+            std::vector<int> targets;
+            for (int r : reds) targets.push_back(an.nodes[r].a);
+            if (p == an.phases) {
+                targets.push_back(an.root);
+                for (const auto& x : an.extras)
+                    if (!x.per_row) targets.push_back(x.node);
+            }
+            std::vector<char> need = needed_for(targets);
+            reduce_declare(reds);
+            o << "    #pragma unroll 1\n";
+            o << "    for (int t = 0; t < " << pl.tiles << "; ++t) {\n";
+            o << "    const int cb = t * " << tile << ";\n";
+            for (int k = 0; k < TN; ++k)
+                o << "    const int c" << k << " = cb + (" << k * L << " + lane) * " << V << ";\n";
+            for (size_t k = 0; k < an.inputs.size(); ++k) {
+                const InputInfo& in = an.inputs[k];
+                if (!in.used || in.kind == InKind::Scalar || in.kind == InKind::RowConst) continue;
+                bool used_here = false;
+                for (size_t i = 0; i < an.nodes.size(); ++i)
+                    if (need[i] && an.nodes[i].op == PSK_OP_INPUT && an.nodes[i].iparam == (int)k) used_here = true;
+                if (!used_here) continue;
+                for (int v = 0; v < TN; ++v) {
+                    std::string c = "c" + std::to_string(v);
+                    std::string cond = "rok";
+                    if (ragged) cond += " && " + c + " < " + std::to_string(an.cols);
+                    if (in.mask_guarded) cond += " && " + c + " <= q";
+                    load_vec((int)k, elem_offset(in, "row", c), v * V, cond);
+                }
+            }
+            leaves(2, &need);
+            for (int d = 0; d <= p; ++d) members_at(d, 1, &need);
+            if (p < an.phases) {
+                reduce_accumulate(reds);
+            } else {
+                for (int v = 0; v < TN; ++v) {
+                    std::string c = "c" + std::to_string(v);
+                    std::string cond = "rok";
+                    if (ragged) cond += " && " + c + " < " + std::to_string(an.cols);
+                    std::string off = "row * (" + std::string(I()) + ")" + std::to_string(an.cols) + " + " + c;
+                    for (size_t k = 0; k < an.extras.size(); ++k)
+                        if (!an.extras[k].per_row)
+                            store_node(an.extras[k].node, "xo" + std::to_string(k), an.extras[k].dtype, off, v * V, cond);
+                    store_vec(off, v * V, cond);
+                }
+            }
+            o << "    }\n";
+            if (p < an.phases) {
+                reduce_finish(reds, p);
+                members_at(p + 1, 2);
+                store_row_extras(p + 1);
+            }
+        }
+        o << "  }\n}\n";
+        return o.str();
     }
 
     std::string row(const std::string& name)
@@ -1012,6 +1178,7 @@ std::string emit_source(const Analysis& an, const KernelPlan& plan, const std::s
     while (std::getline(ct, line)) hdr << "//   " << line << "\n";
     hdr << "// plan: " << plan.key() << "\n";
     if (plan.kind == 2) return hdr.str() + em.tree(kernel_name);
+    if (plan.kind == 3) return hdr.str() + em.row_tiled(kernel_name);
     return hdr.str() + (plan.kind == 1 ? em.row(kernel_name) : em.pointwise(kernel_name));
 }
 

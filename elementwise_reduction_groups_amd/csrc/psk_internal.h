@@ -81,12 +81,13 @@ const char* op_name(int op);
 
 // ------------------------------------------------------------------- emit
 struct KernelPlan {
-    int kind = 0;            // 0 pointwise, 1 row, 2 tree-mapped
+    int kind = 0;            // 0 pointwise, 1 row, 2 tree-mapped, 3 row tiled (wide rows)
     int vec = 1;             // elements per vector access
     int block = 256;         // threads per workgroup
     int lanes = 64;          // row kernel: lanes per row
     int rows_per_block = 1;  // row kernel
-    int nv = 1;              // row kernel: vectors per lane
+    int nv = 1;              // row kernel: vectors per lane (tiled: per lane per tile)
+    int tiles = 0;           // tiled row kernel (kind 3): tiles per row, each phase re-reads the row
     bool nt = true;          // nontemporal loads and stores
     bool xcd = true;         // each XCD takes a contiguous eighth of the blocks
     int64_t blocks = 0;      // workgroups that carry work

@@ -336,8 +336,8 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
     if (an.is_row[an.root] && an.cols > 1)
         return fail(PSK_E_ROW, "the root is one value per row but the output has " + std::to_string(an.cols) +
                                    " columns: a reduction cannot be the stored value here");
-    if (an.row_kind && an.cols > 65536)
-        return fail(PSK_E_UNSUPPORTED, "row groups over rows longer than 65536 are not implemented");
+    if (an.row_kind && an.cols > (int64_t(1) << 30))
+        return fail(PSK_E_UNSUPPORTED, "row groups over rows longer than 2^30 are not implemented");
 
     // ---- inputs read only where a causal mask allows them
     // A value is irrelevant at refused positions when every reader is a

@@ -221,7 +221,7 @@ void psk_group_destroy(psk_group* group);
 
 /* Kernel shape chosen for a group (for tests and measurement). */
 typedef struct psk_group_info {
-    int32_t kind;            /* 0 pointwise, 1 row, 2 tree-mapped */
+    int32_t kind;            /* 0 pointwise, 1 row, 2 tree-mapped, 3 row tiled */
     int32_t members;         /* member count */
     int32_t n_reductions;    /* row reductions */
     int32_t phases;          /* reduction phases (longest chain of dependent reductions) */
@@ -232,6 +232,8 @@ typedef struct psk_group_info {
     int32_t rows_per_block;  /* row kernel */
     int64_t algorithmic_bytes; /* inputs read once at their own size + outputs written once */
     char kernel[48];         /* the emitted kernel's name (as profilers show it), NUL-terminated */
+    int32_t tiles;           /* tiled row kernel (kind 3, rows too wide for registers): tiles per
+                                row; each reduction phase re-reads the row.  0 otherwise */
 } psk_group_info;
 psk_status psk_group_get_info(const psk_group* group, psk_group_info* info);
 

@@ -386,3 +386,24 @@ def test_mask_refusals(lib):
     # a mask may not widen the scores
     refused(P.PSK_E_BROADCAST, "%0 = input 0\n%1 = input 1\n%2 = where %1 %0 0.0\n",
             [((4, 8), "f32"), ((2, 4, 8), "u8")], (4, 8))
+
+
+def test_wide_rows_take_the_tiled_kernel(lib, tmp_path):
+    from synth import configs as C
+    # up to 32 elements per lane at 1024 lanes the row stays in registers
+    g = P.psk_group_create(P.GroupDesc(C.softmax_causal_dag(0.125, 32768), [((4, 32768), "f32")], (4, 32768), "f32"))
+    assert P.psk_group_get_info(g).kind == 1
+    P.psk_group_destroy(g)
+    for cols, dt in [(32772, "f32"), (65536, "f32"), (131072, "bf16"), (1 << 20, "f32")]:
+        d = P.GroupDesc(C.softmax_causal_dag(0.125, cols), [((4, cols), dt)], (4, cols), dt)
+        g = P.psk_group_create(d)
+        info = P.psk_group_get_info(g)
+        P.psk_group_destroy(g)
+        assert info.kind == 3 and info.lanes_per_row == 1024 and info.rows_per_block == 1
+        assert info.tiles == -(-cols // (1024 * 2 * info.vec))
+        asm, notes = _isa(P.psk_group_code_object(d), tmp_path, f"wide{cols}")
+        assert re.search(r"\.private_segment_fixed_size:\s+0\b", notes)    # no spills
+        assert not re.search(r"v_pk_(fma|mul|add)_f32", asm)
+    # rows past 2^30 columns are refused
+    _refused(_desc("%0 = input 0\n%1 = row_max %0\n%2 = sub %0 %1\n", [((1, (1 << 30) + 8), "f32")],
+                   (1, (1 << 30) + 8)), P.PSK_E_UNSUPPORTED)

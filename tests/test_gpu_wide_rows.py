@@ -1,0 +1,104 @@
+"""GPU parity of the tiled row kernel (rows too wide to live in registers:
+more than 32 elements per lane at 1024 lanes) against the oracle: each
+reduction phase walks the row in tiles and re-reads what it needs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import configs
+from tests.gpu_util import assert_bf16_close, assert_f32_close, to_np
+
+P = pytest.importorskip("elementwise_reduction_groups_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+F32, BF16 = P.PSK_F32, P.PSK_BF16
+EPS = configs.f32(1e-5)
+
+
+@pytest.mark.parametrize("R,C,dt", [(8, 40000, "f32"), (4, 65536, "f32"), (3, 131072, "bf16"), (5, 33333, "f32"),
+                                    (2, 300000, "f32")])
+def test_wide_softmax(R, C, dt):
+    x = configs.softmax_scores(R, C, device=DEV, seed=C)
+    if dt == "bf16":
+        x = x.to(torch.bfloat16)
+    # a causal period shorter than the row count, so rows keep various prefixes;
+    # and the unmasked softmax (period larger than every column index)
+    for period in (3, C):
+        g = P.Group(configs.softmax_causal_dag(0.125, period), [((R, C), dt)], (R, C), dt)
+        info = g.info
+        assert info.kind == 3 and info.tiles >= 2
+        out = torch.full_like(x, float("nan"))
+        g.run([x], out)
+        torch.cuda.synchronize()
+        ref = oracle.eval_group(configs.softmax_causal_dag(0.125, period), [to_np(x)], (R, C), F32 if dt == "f32"
+                                else BF16)
+        if dt == "f32":
+            assert_f32_close(to_np(out), ref, f"wide softmax {R}x{C} period {period}")
+        else:
+            assert_bf16_close(to_np(out), ref, f"wide softmax {R}x{C} period {period}")
+
+
+def test_wide_masked_softmax_with_emptied_rows():
+    R, C = 6, 70000
+    x = configs.softmax_scores(R, C, device=DEV, seed=5)
+    m = configs.random_mask(R, C, 0.2, empty_rows=[2], device=DEV, seed=6)
+    g = P.Group(configs.softmax_masked_dag(0.125), [((R, C), "f32"), ((R, C), "u8")], (R, C), "f32")
+    assert g.info.kind == 3
+    out = torch.full_like(x, float("nan"))
+    g.run([x, m], out)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    ref = oracle.eval_group(configs.softmax_masked_dag(0.125), [to_np(x), m.cpu().numpy().view(np.uint8)], (R, C),
+                            F32)
+    assert_f32_close(got, ref, "wide masked softmax")
+    assert np.all(got[2].view(np.uint32) == 0)
+
+
+def test_wide_layernorm_with_statistics():
+    R, C = 8, 50000
+    x, gm, bt = configs.layernorm_inputs(R, C, device=DEV, seed=9)
+    g = P.Group(configs.layernorm_dag(EPS), [((R, C), "bf16"), ((C,), "bf16"), ((C,), "bf16")], (R, C), "bf16",
+                root=configs.LAYERNORM_ROOT,
+                extras=[(configs.LAYERNORM_MEAN, (R, 1), "f32"), (configs.LAYERNORM_RSTD, (R, 1), "f32")])
+    assert g.info.kind == 3
+    out = torch.full((R, C), float("nan"), dtype=torch.bfloat16, device=DEV)
+    mean = torch.full((R, 1), float("nan"), device=DEV)
+    rstd = torch.full((R, 1), float("nan"), device=DEV)
+    g.run([x, gm, bt], out, extra_outs=[mean, rstd])
+    torch.cuda.synchronize()
+    rm, rr = np.zeros((R, 1), np.float32), np.zeros((R, 1), np.float32)
+    ref = oracle.eval_group(configs.layernorm_dag(EPS), [to_np(x), to_np(gm), to_np(bt)], (R, C), BF16,
+                            root=configs.LAYERNORM_ROOT,
+                            extras=[(configs.LAYERNORM_MEAN, rm), (configs.LAYERNORM_RSTD, rr)])
+    # statistics: a lane sums its elements over the tiles in order (tiles x vectors x vec per lane),
+    # then the wave butterfly and the 16 waves; against float64 within that path's bound
+    U = 2.0 ** -24
+    k = g.info.tiles * 2 * g.info.vec + 6 + 15
+    x64 = x.double().cpu()
+    m64 = x64.mean(dim=1)
+    assert torch.all((mean.double().cpu()[:, 0] - m64).abs() <= k * U * x64.abs().mean(dim=1) + U * m64.abs())
+    r64 = 1.0 / torch.sqrt(x64.var(dim=1, unbiased=False) + EPS)
+    assert ((rstd.double().cpu()[:, 0] - r64).abs() / r64).max() <= (k + 8) * U
+    d = np.abs(to_np(out).astype(np.int32) - ref.astype(np.int32))
+    # away from cancellations the outputs are within one bf16 ulp
+    big = np.abs((ref.astype(np.uint32) << 16).view(np.float32)) > 0.05
+    assert d[big].max() <= 1
+
+
+def test_wide_rms_norm_storing_h_in_place():
+    R, C = 4, 45000
+    x, res, gm = configs.rmsnorm_inputs(R, C, device=DEV, seed=10)
+    xn, rn, gn = to_np(x), to_np(res), to_np(gm)
+    g = P.Group(configs.rmsnorm_gelu_dag(EPS), [((R, C), "bf16"), ((R, C), "bf16"), ((C,), "bf16")], (R, C), "bf16",
+                extras=[(configs.RMSNORM_H, (R, C), "bf16")])
+    assert g.info.kind == 3
+    out = torch.full((R, C), float("nan"), dtype=torch.bfloat16, device=DEV)
+    g.run([x, res, gm], out, extra_outs=[res])
+    torch.cuda.synchronize()
+    rh = np.zeros((R, C), np.uint16)
+    ref = oracle.eval_group(configs.rmsnorm_gelu_dag(EPS), [xn, rn, gn], (R, C), BF16,
+                            extras=[(configs.RMSNORM_H, rh)])
+    np.testing.assert_array_equal(to_np(res), rh)
+    assert_bf16_close(to_np(out), ref, "wide rmsnorm")
