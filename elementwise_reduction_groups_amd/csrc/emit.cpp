@@ -103,8 +103,8 @@ static int layout_value(const char* key, int dflt)
 std::string KernelPlan::key() const
 {
     char b[160];
-    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d", kind, vec, block, lanes, nv, (int)nt, (int)xcd,
-                  (long long)blocks, tiles);
+    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d c%d w%d", kind, vec, block, lanes, nv, (int)nt,
+                  (int)xcd, (long long)blocks, tiles, (int)tcache, wpe);
     return b;
 }
 
@@ -181,6 +181,8 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
             p.block = Lt;
             p.rows_per_block = 1;
             p.blocks = an.rows;
+            p.tcache = layout_value("tcache", 1) != 0;
+            p.wpe = layout_value("wpe", 0);
         }
     }
     if (p.xcd) {
@@ -219,6 +221,8 @@ template <typename T> __device__ __forceinline__ void psk_st(T* p, T v) {
   *p = v;
 #endif
 }
+// a load whose data is read again (an early phase of the tiled row kernel)
+template <typename T> __device__ __forceinline__ T psk_ldc(const T* p) { return *p; }
 // the same for pointers named as global memory (addresses read from a
 // device table would otherwise be accessed through generic instructions)
 #define PSK_G __attribute__((address_space(1)))
@@ -374,6 +378,8 @@ struct Emitter {
 
     bool use_refused = false;
     bool divr_ok = true;          // row-value divisors use psk_divr
+    bool cached_loads = false;    // loads whose data a later phase reads again
+    std::string ld_fn() const { return cached_loads ? "psk_ldc" : "psk_ld"; }
 
     // node i's defining expression as its readers see it: a value stored as
     // bf16 (an extra output) is read back rounded
@@ -505,7 +511,7 @@ struct Emitter {
         auto dst = [&](int j) { return "x" + ks + "_" + std::to_string(e0 + j); };
         if (V == 1) {
             o << "    float " << dst(0) << " = 0.0f;\n";
-            o << "    if (" << cond << ") " << dst(0) << " = " << widen(in.dtype, "psk_ld(" + p + ")") << ";\n";
+            o << "    if (" << cond << ") " << dst(0) << " = " << widen(in.dtype, ld_fn() + "(" + p + ")") << ";\n";
             return;
         }
         if (in.dtype == PSK_U8) {
@@ -514,7 +520,7 @@ struct Emitter {
             std::string wn = "w" + ks + "_" + std::to_string(e0);
             const char* vt = nw == 1 ? "psk_u32" : nw == 2 ? "psk_u2v" : "psk_u4v";
             o << "    " << vt << " " << wn << " = {};\n";
-            o << "    if (" << cond << ") " << wn << " = psk_ld((const " << vt << "*)(" << p << "));\n";
+            o << "    if (" << cond << ") " << wn << " = " << ld_fn() << "((const " << vt << "*)(" << p << "));\n";
             for (int j = 0; j < V; ++j) {
                 std::string w = nw == 1 ? wn : wn + "[" + std::to_string(j / 4) + "]";
                 o << "    const float " << dst(j) << " = (float)((" << w << " >> " << 8 * (j % 4) << ") & 255u);\n";
@@ -532,11 +538,11 @@ struct Emitter {
             int eoff = w * elems_per_word;
             if (cnt == 4) {
                 o << "    psk_u4v " << wn << " = {0u, 0u, 0u, 0u};\n";
-                o << "    if (" << cond << ") " << wn << " = psk_ld((const psk_u4v*)(" << p << " + " << eoff << "));\n";
+                o << "    if (" << cond << ") " << wn << " = " << ld_fn() << "((const psk_u4v*)(" << p << " + " << eoff << "));\n";
                 for (int q = 0; q < 4; ++q) words.push_back(wn + "[" + std::to_string(q) + "]");
             } else {
                 o << "    psk_u2v " << wn << " = {0u, 0u};\n";
-                o << "    if (" << cond << ") " << wn << " = psk_ld((const psk_u2v*)(" << p << " + " << eoff << "));\n";
+                o << "    if (" << cond << ") " << wn << " = " << ld_fn() << "((const psk_u2v*)(" << p << " + " << eoff << "));\n";
                 for (int q = 0; q < 2; ++q) words.push_back(wn + "[" + std::to_string(q) + "]");
             }
         }
@@ -598,7 +604,9 @@ struct Emitter {
 
     void signature(const std::string& name)
     {
-        o << "extern \"C\" __global__ void __launch_bounds__(" << pl.block << ") " << name << "(";
+        o << "extern \"C\" __global__ void __launch_bounds__(" << pl.block << ") ";
+        if (pl.wpe > 0) o << "__attribute__((amdgpu_waves_per_eu(1, " << pl.wpe << "))) ";
+        o << name << "(";
         // no __restrict__: the output may be the same buffer as an input
         // (in place); every load of an element precedes its store
         for (size_t k = 0; k < an.inputs.size(); ++k)
@@ -1059,6 +1067,9 @@ struct Emitter {
                     if (!x.per_row) targets.push_back(x.node);
             }
             std::vector<char> need = needed_for(targets);
+            // data read again by a later phase stays in the caches: plain
+            // loads before the last phase, nontemporal ones in it
+            cached_loads = p < an.phases && pl.tcache;
             reduce_declare(reds);
             o << "    #pragma unroll 1\n";
             o << "    for (int t = 0; t < " << pl.tiles << "; ++t) {\n";

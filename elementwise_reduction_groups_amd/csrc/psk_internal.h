@@ -88,6 +88,8 @@ struct KernelPlan {
     int rows_per_block = 1;  // row kernel
     int nv = 1;              // row kernel: vectors per lane (tiled: per lane per tile)
     int tiles = 0;           // tiled row kernel (kind 3): tiles per row, each phase re-reads the row
+    bool tcache = true;      // tiled row kernel: cached (plain) loads before the last phase
+    int wpe = 0;             // tiled row kernel: at most this many waves per SIMD (0: no limit)
     bool nt = true;          // nontemporal loads and stores
     bool xcd = true;         // each XCD takes a contiguous eighth of the blocks
     int64_t blocks = 0;      // workgroups that carry work

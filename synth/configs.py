@@ -338,3 +338,18 @@ def random_mask(rows: int, cols: int, p_keep: float = 0.5, empty_rows: Sequence[
     for r in empty_rows:
         m[r] = False
     return m.to(device)
+
+
+def softmax_dag(scale: float = 0.125) -> List[Node]:
+    """The plain row softmax (no mask): scale, row max, subtract, exp, row
+    sum, divide."""
+    return parse_dag(f"""
+        %0 = input 0
+        %1 = const {float(scale).hex()}
+        %2 = mul %0 %1
+        %3 = row_max %2
+        %4 = sub %2 %3
+        %5 = exp %4
+        %6 = row_sum %5
+        %7 = div %5 %6
+    """)
