@@ -179,6 +179,9 @@ def main():
         result["groups"] = time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, probs,
                                        adamw_bytes, softmax_bytes, hp, state)
 
+    # ------------------------------------------------ static dispatch counts
+    result["dispatch"] = dispatch_report(P, configs)
+
     # ------------------------------------------------------------ CPU leg
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, configs, n_params, shapes, R, C, step_bytes)
@@ -224,6 +227,24 @@ def tree_sgd(P, configs, torch, dev, state):
     tree = P.Tree([[s["theta"], s["grad"]] for s in state])
     group = P.Group(configs.tree_sgd_dag(), [((1,), "bf16"), ((1,), "bf16"), ((), "f32")], (1,), "bf16", tree=True)
     return tree, group, torch.tensor(1e-4, dtype=torch.float32, device=dev)
+
+
+def dispatch_report(P, configs):
+    """Launches and bytes of a synthetic GPT forward (the corpus GPT's sizes)
+    before and after the partition, with reductions ending groups and with
+    rows fused; and of the AdamW step over the tiny GPT's tree."""
+    from synth.body import gpt_forward
+    b = gpt_forward(V=92, D=64, H=2, L=2, B=2, T=32)
+    out = {"gpt_forward_V92_D64_H2_L2_B2_T32": {
+        "reductions_end_groups": P.psk_dispatch_count(b.nodes, b.types, b.outputs),
+        "rows_fused": P.psk_dispatch_count(b.nodes, b.types, b.outputs, rows=True)}}
+    dag = configs.adamw_group_dag()
+    lets = sum(1 for n in dag if n.op not in ("input", "const"))
+    leaves = len(configs.tiny_gpt_leaves())
+    out["adamw_tiny_gpt_tree"] = {"leaves": leaves, "lets_per_leaf": lets,
+                                  "launches_unfused": lets * leaves, "launches_one_per_leaf": leaves,
+                                  "launches_one_per_tree": 1}
+    return out
 
 
 def layernorm_group(P, configs):

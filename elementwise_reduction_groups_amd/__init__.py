@@ -25,6 +25,7 @@ for _i, _n in enumerate(STATUS_NAMES):
 
 PSK_F32, PSK_BF16, PSK_U8 = 0, 1, 2
 PSK_GROUP_TREE = 1
+PSK_PARTITION_ROWS = 1
 PSK_MAX_RANK = 4
 PSK_MAX_SLOTS = 8
 PSK_TREE_CHUNK = 4096
@@ -63,6 +64,11 @@ class psk_group_desc(ctypes.Structure):
                 ("out", psk_tensor_desc), ("arith", ctypes.c_int32), ("flags", ctypes.c_uint32),
                 ("n_extra", ctypes.c_int32), ("extra_root", ctypes.POINTER(ctypes.c_int32)),
                 ("extra_out", ctypes.POINTER(psk_tensor_desc))]
+
+
+class psk_dispatch_report(ctypes.Structure):
+    _fields_ = [("lets", ctypes.c_int32), ("launches_unfused", ctypes.c_int32), ("launches_fused", ctypes.c_int32),
+                ("fused_groups", ctypes.c_int32), ("bytes_unfused", ctypes.c_int64), ("bytes_fused", ctypes.c_int64)]
 
 
 class psk_group_info(ctypes.Structure):
@@ -109,7 +115,7 @@ EXPORTED = ["psk_group_create", "psk_group_run", "psk_group_destroy", "psk_group
             "psk_group_code_object", "psk_tree_create", "psk_tree_destroy", "psk_tree_get_info",
             "psk_tree_get_tables", "psk_tree_plan", "psk_adamw_step", "psk_adamw_step_config", "psk_adamw_lr",
             "psk_tree_clip_result", "psk_group_run_tree", "psk_group_run_multi", "psk_group_run_tree_multi",
-            "psk_partition", "psk_last_error",
+            "psk_partition", "psk_partition_ex", "psk_dispatch_count", "psk_last_error",
             "psk_status_str", "psk_version", "psk_get_stats"]
 
 
@@ -145,6 +151,11 @@ def lib() -> ctypes.CDLL:
     L.psk_partition.argtypes = [i32, ctypes.POINTER(psk_node), ctypes.POINTER(psk_tensor_desc),
                                 ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(i32), ctypes.POINTER(i32),
                                 ctypes.POINTER(i32)]
+    L.psk_partition_ex.argtypes = [i32, ctypes.POINTER(psk_node), ctypes.POINTER(psk_tensor_desc),
+                                   ctypes.POINTER(ctypes.c_uint8), ctypes.c_uint32, ctypes.POINTER(i32),
+                                   ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.psk_dispatch_count.argtypes = [i32, ctypes.POINTER(psk_node), ctypes.POINTER(psk_tensor_desc),
+                                     ctypes.POINTER(ctypes.c_uint8), ctypes.c_uint32, ctypes.POINTER(psk_dispatch_report)]
     L.psk_last_error.restype = ctypes.c_char_p
     L.psk_status_str.restype = ctypes.c_char_p
     L.psk_status_str.argtypes = [ctypes.c_int]
@@ -374,17 +385,34 @@ def psk_tree_clip_result(tree: int):
     return ss.value, f.value
 
 
-def psk_partition(nodes, types: Sequence[Tuple[Sequence[int], object]], is_output: Sequence[bool]):
-    import numpy as np
+def _body_arrays(nodes, types, is_output):
     n = len(nodes)
-    arr = node_array(nodes)
+    arr = node_array(nodes) if n else (psk_node * 1)()
     tys = (psk_tensor_desc * max(1, n))(*[tensor_desc(s, d) for s, d in types])
     outs = (ctypes.c_uint8 * max(1, n))(*[1 if o else 0 for o in is_output])
+    return n, arr, tys, outs
+
+
+def psk_partition(nodes, types: Sequence[Tuple[Sequence[int], object]], is_output: Sequence[bool], rows=False):
+    """(group_of, is_root, n_groups); rows=True fuses last-axis row
+    reductions (psk_partition_ex with PSK_PARTITION_ROWS)."""
+    import numpy as np
+    n, arr, tys, outs = _body_arrays(nodes, types, is_output)
     g = (ctypes.c_int32 * max(1, n))()
     r = (ctypes.c_int32 * max(1, n))()
     ng = ctypes.c_int32()
-    _check(lib().psk_partition(n, arr, tys, outs, g, r, ctypes.byref(ng)))
+    if rows:
+        _check(lib().psk_partition_ex(n, arr, tys, outs, PSK_PARTITION_ROWS, g, r, ctypes.byref(ng)))
+    else:
+        _check(lib().psk_partition(n, arr, tys, outs, g, r, ctypes.byref(ng)))
     return np.array(g[:n], np.int32), np.array(r[:n], np.int32), ng.value
+
+
+def psk_dispatch_count(nodes, types, is_output, rows=False) -> dict:
+    n, arr, tys, outs = _body_arrays(nodes, types, is_output)
+    rep = psk_dispatch_report()
+    _check(lib().psk_dispatch_count(n, arr, tys, outs, PSK_PARTITION_ROWS if rows else 0, ctypes.byref(rep)))
+    return {k: getattr(rep, k) for k, _ in psk_dispatch_report._fields_}
 
 
 def psk_last_error() -> str:

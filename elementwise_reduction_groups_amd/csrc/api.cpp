@@ -690,7 +690,22 @@ extern "C" psk_status psk_partition(int32_t n, const psk_node* body, const psk_t
                                     const uint8_t* is_output, int32_t* group_of, int32_t* is_root, int32_t* n_groups)
 {
     clear_error();
-    return partition(n, body, types, is_output, group_of, is_root, n_groups);
+    return partition(n, body, types, is_output, 0u, group_of, is_root, n_groups);
+}
+
+extern "C" psk_status psk_partition_ex(int32_t n, const psk_node* body, const psk_tensor_desc* types,
+                                       const uint8_t* is_output, uint32_t flags, int32_t* group_of, int32_t* is_root,
+                                       int32_t* n_groups)
+{
+    clear_error();
+    return partition(n, body, types, is_output, flags, group_of, is_root, n_groups);
+}
+
+extern "C" psk_status psk_dispatch_count(int32_t n, const psk_node* body, const psk_tensor_desc* types,
+                                         const uint8_t* is_output, uint32_t flags, psk_dispatch_report* report)
+{
+    clear_error();
+    return dispatch_count(n, body, types, is_output, flags, report);
 }
 
 // -------------------------------------------------------------------- misc

@@ -113,7 +113,9 @@ extern const int kJitOptionCount;
 
 // -------------------------------------------------------------- partition
 psk_status partition(int32_t n, const psk_node* body, const psk_tensor_desc* types, const uint8_t* is_output,
-                     int32_t* group_of, int32_t* is_root, int32_t* n_groups);
+                     uint32_t flags, int32_t* group_of, int32_t* is_root, int32_t* n_groups);
+psk_status dispatch_count(int32_t n, const psk_node* body, const psk_tensor_desc* types, const uint8_t* is_output,
+                          uint32_t flags, psk_dispatch_report* rep);
 
 // ------------------------------------------------------------------ trees
 struct TreePlan {

@@ -385,6 +385,35 @@ psk_status psk_group_run_tree_multi(const psk_group* group, const psk_tree* tree
 psk_status psk_partition(int32_t n, const psk_node* body, const psk_tensor_desc* types,
                          const uint8_t* is_output, int32_t* group_of, int32_t* is_root, int32_t* n_groups);
 
+/* The same with options.  PSK_PARTITION_ROWS fuses reductions as the row
+ * kernels run them (poot, "Fusion and Planning", "Reduction-rooted
+ * regions"; PSK-Realize, "Not in this version", reduction fusion): a
+ * last-axis row reduction is a member candidate, and a let whose shape is
+ * the group root's with a last axis of 1 (a value one per row, whatever its
+ * storage type) joins under the same reader rule.  flags 0 is psk_partition.
+ * Unknown flags: PSK_E_UNSUPPORTED. */
+#define PSK_PARTITION_ROWS 1u
+psk_status psk_partition_ex(int32_t n, const psk_node* body, const psk_tensor_desc* types,
+                            const uint8_t* is_output, uint32_t flags, int32_t* group_of, int32_t* is_root,
+                            int32_t* n_groups);
+
+/* Static launch count and traffic of a body before and after the partition
+ * (what poot's dispatch_count reports, "What fusion reports"; PSK-Realize,
+ * "What it removes").  Unfused, every non-leaf let is a launch that reads
+ * each operand and writes its value; fused, every group is one launch that
+ * reads each value from outside it once and writes its root.  Bytes are
+ * tensor sizes at their storage types (f32 4, bf16 2, u8 1). */
+typedef struct psk_dispatch_report {
+    int32_t lets;               /* non-leaf lets */
+    int32_t launches_unfused;   /* = lets */
+    int32_t launches_fused;     /* groups */
+    int32_t fused_groups;       /* groups with more than one member */
+    int64_t bytes_unfused;
+    int64_t bytes_fused;
+} psk_dispatch_report;
+psk_status psk_dispatch_count(int32_t n, const psk_node* body, const psk_tensor_desc* types,
+                              const uint8_t* is_output, uint32_t flags, psk_dispatch_report* report);
+
 /* ------------------------------------------------------------------ misc */
 const char* psk_last_error(void);
 const char* psk_status_str(psk_status status);

@@ -88,7 +88,7 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_double, i64, ctypes.c_float, vp, vp, vp]
         L.orc_softmax_causal.argtypes = [i64, i64, i64, ctypes.c_float, vp, vp, i64, i64]
         L.orc_rmsnorm_gelu.argtypes = [i64, i64, vp, vp, vp, ctypes.c_float, vp, i64, i64]
-        L.orc_partition.argtypes = [ctypes.c_int, vp, vp, vp, vp, ctypes.c_int, vp, vp]
+        L.orc_partition.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp, vp]
         L.orc_partition.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -280,9 +280,11 @@ def rmsnorm_gelu(x: np.ndarray, res: np.ndarray, gamma: np.ndarray, eps: float, 
 _CLASS = {"leaf": 0, "ew": 1, "row": 2, "nonew": 2}
 
 
-def partition(nodes, type_ids: Sequence[int], is_output: Sequence[bool], cap: int = 64):
+def partition(nodes, types, is_output: Sequence[bool], cap: int = 64, rows: bool = False):
     """Greedy fusion-group partition; returns (group_of, is_root) as int32
-    arrays.  ``pown`` with an exponent above 2 is a boundary."""
+    arrays.  ``types[i]`` is node i's (shape, storage type) or an integer
+    type id (then rows must be False).  ``pown`` with an exponent above 2 is
+    a boundary; with ``rows`` last-axis row reductions fuse."""
     from synth.dag import OPS
     n = len(nodes)
     cls = np.zeros(n, np.int32)
@@ -291,14 +293,30 @@ def partition(nodes, type_ids: Sequence[int], is_output: Sequence[bool], cap: in
         c = _CLASS[OPS[nd.op][1]]
         if nd.op == "pown" and (nd.iparam or 0) > 2:
             c = 2
+        if rows and OPS[nd.op][1] == "row":
+            c = 3
         cls[i] = c
         a = list(nd.args)[:3]
         args[i, :len(a)] = a
-    tid = np.ascontiguousarray(type_ids, np.int32)
+    ids, shape_ids = {}, {}
+    tid = np.zeros(n, np.int32)
+    sid = np.zeros(n, np.int32)
+    rsid = np.full(n, -1, np.int32)
+    for i, t in enumerate(types):
+        if isinstance(t, (int, np.integer)):
+            assert not rows, "row fusion needs shapes"
+            tid[i] = int(t)
+            continue
+        shape, dt = tuple(int(x) for x in t[0]), str(t[1])
+        tid[i] = ids.setdefault((shape, dt), len(ids))
+        sid[i] = shape_ids.setdefault(shape, len(shape_ids))
+        if shape and shape[-1] > 1:
+            rsid[i] = shape_ids.setdefault(shape[:-1] + (1,), len(shape_ids))
     outp = np.ascontiguousarray([1 if o else 0 for o in is_output], np.uint8)
     g = np.zeros(n, np.int32)
     r = np.zeros(n, np.int32)
-    rc = lib().orc_partition(n, _ptr(cls), _ptr(args), _ptr(tid), _ptr(outp), cap, _ptr(g), _ptr(r))
+    rc = lib().orc_partition(n, _ptr(cls), _ptr(args), _ptr(tid), _ptr(sid), _ptr(rsid), _ptr(outp), cap,
+                             1 if rows else 0, _ptr(g), _ptr(r))
     if rc < 0:
         raise ValueError("oracle refused the node list")
     return g, r

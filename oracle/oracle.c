@@ -543,11 +543,22 @@ void orc_rmsnorm_gelu(int64_t R, int64_t C, const uint16_t *x, const uint16_t *r
  * contraction, cast, pow n>2) is a group of its own that nothing joins.
  * Groups are numbered in increasing order of their root's position.
  *
- * op_class: 0 leaf, 1 elementwise, 2 boundary.
+ * With `rows` set, reductions fuse as the row kernels run them (poot,
+ * "Fusion and Planning", reduction-rooted regions): a last-axis row
+ * reduction (op_class 3) is a member candidate like an elementwise let, and
+ * a candidate whose shape is the group root's with a last axis of 1 (a
+ * value that is one per row: shape_id[i] equals rowshape_id of the root)
+ * joins as well as one of the root's type; a reduction joins only so,
+ * and only when it reduces a value of the root's shape.
+ *
+ * op_class: 0 leaf, 1 elementwise, 2 boundary, 3 row reduction.
  * args: n x 3 operand indices (-1 unused).
+ * type_id: shape and storage type; shape_id: shape alone; rowshape_id: the
+ * shape with its last axis set to 1 (-1 when the last axis is already 1).
  */
 int orc_partition(int n, const int32_t *op_class, const int32_t *args, const int32_t *type_id,
-                  const uint8_t *is_output, int cap, int32_t *group_of, int32_t *is_root)
+                  const int32_t *shape_id, const int32_t *rowshape_id, const uint8_t *is_output, int cap, int rows,
+                  int32_t *group_of, int32_t *is_root)
 {
     int32_t *nread = (int32_t *)calloc((size_t)n + 1, sizeof(int32_t));
     int32_t *gsize = (int32_t *)calloc((size_t)n + 1, sizeof(int32_t));
@@ -572,16 +583,25 @@ int orc_partition(int n, const int32_t *op_class, const int32_t *args, const int
         if (op_class[i] == 0)
             continue;
         int join = -1;
-        if (op_class[i] == 1 && !is_output[i] && nread[i] > 0) {
+        int cand = op_class[i] == 1 || (rows && op_class[i] == 3);
+        if (cand && !is_output[i] && nread[i] > 0) {
             int G = -2, ok = 1;
             for (int j = i + 1; j < n && ok; ++j)
                 for (int k = 0; k < 3; ++k)
                     if (args[3 * j + k] == i) {
-                        if (op_class[j] != 1) { ok = 0; break; }
+                        int member = op_class[j] == 1 || (rows && op_class[j] == 3);
+                        if (!member) { ok = 0; break; }
                         if (G == -2) G = group_of[j];
                         else if (group_of[j] != G) { ok = 0; break; }
                     }
-            if (ok && G >= 0 && gtype[G] == type_id[i] && gsize[G] < cap)
+            /* a row value joins when its shape is the root's with a last
+             * axis of 1; a reduction only when it reduces a value of the
+             * root's shape */
+            int typed = ok && G >= 0 &&
+                        ((op_class[i] == 1 && gtype[G] == type_id[i]) ||
+                         (rows && rowshape_id[groot[G]] >= 0 && shape_id[i] == rowshape_id[groot[G]] &&
+                          (op_class[i] == 1 || shape_id[args[3 * i]] == shape_id[groot[G]])));
+            if (typed && gsize[G] < cap)
                 join = G;
         }
         if (join >= 0) {
