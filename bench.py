@@ -290,11 +290,25 @@ def profile_others(P, configs, torch, dev, stream, hp, state):
     rl = torch.empty((16384, 1), device=dev)
     ln = layernorm_group(P, configs)
     adamw_g, adamw_args = adamw_group(P, configs, torch, dev, state, hp)
+    xs = configs.softmax_scores(131072, 1024, device=dev)
+    ys = torch.empty_like(xs)
+    mask = configs.causal_mask_bytes(1024, device=dev)
+    masked = P.Group(configs.softmax_masked_dag(0.125), [((8, 16, 1024, 1024), "f32"), ((1024, 1024), "u8")],
+                     (8, 16, 1024, 1024), "f32")
+    sb = xs.to(torch.bfloat16)
+    pb = torch.empty_like(sb)
+    soft_bf16 = P.Group(configs.softmax_causal_dag(0.125, 1024), [((131072, 1024), "bf16")], (131072, 1024), "bf16")
+    xw = configs.softmax_scores(8192, 131072, device=dev)
+    yw = torch.empty_like(xw)
+    wide = P.Group(configs.softmax_dag(0.125), [((8192, 131072), "f32")], (8192, 131072), "f32")
     torch.cuda.synchronize()
     for _ in range(2):
         sgd.run_tree(sgd_tree, [0, 1, -1], 0, [None, None, lr], stream=stream)
         ln.run([xl, gl, bl], yl, stream=stream, extra_outs=[ml, rl])
         adamw_g.run_tree(*adamw_args, stream=stream)
+        masked.run([xs.view(8, 16, 1024, 1024), mask], ys.view(8, 16, 1024, 1024), stream=stream)
+        soft_bf16.run([sb], pb, stream=stream)
+        wide.run([xw], yw, stream=stream)
         tiny_tree.adamw_step(*hp, stream=stream)
         rms.run([x, r, g], y, stream=stream)
         chain.run([A, B, Cc], Z, stream=stream)
@@ -303,6 +317,8 @@ def profile_others(P, configs, torch, dev, stream, hp, state):
 
 def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, probs, adamw_bytes, softmax_bytes, hp,
                 state):
+    R, C = scores.shape
+    allowed = sum(min(r % 1024, C - 1) + 1 for r in range(1024)) * (R // 1024)
     """Each workload alone: a 1 GiB write between calls evicts the 256 MB
     last-level cache; HIP events around each call; median of --reps."""
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -360,6 +376,28 @@ def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, pro
     rms = P.Group(configs.rmsnorm_gelu_dag(configs.f32(1e-5)),
                   [((16384, 4096), "bf16"), ((16384, 4096), "bf16"), ((4096,), "bf16")], (16384, 4096), "bf16")
     add("rmsnorm_gelu_bf16", rms.info.algorithmic_bytes, lambda: rms.run([x, r, g], y, stream=stream))
+
+    # softmax variants over [8, 16, 1024, 1024] scores: a [1024, 1024] byte
+    # mask (causal pattern) read from memory, and bf16 scores and probabilities
+    xs4 = scores.view(8, 16, 1024, 1024)
+    mask = configs.causal_mask_bytes(1024, device=dev)
+    masked = P.Group(configs.softmax_masked_dag(0.125), [((8, 16, 1024, 1024), "f32"), ((1024, 1024), "u8")],
+                     (8, 16, 1024, 1024), "f32")
+    add("softmax_mask_buffer_f32", R * C * 4 * 2 + 1024 * 1024,
+        lambda: masked.run([xs4, mask], probs.view(8, 16, 1024, 1024), stream=stream),
+        note="every score read (the mask is data), mask bytes once, probabilities written")
+    sb = scores.to(torch.bfloat16)
+    pb = torch.empty_like(sb)
+    soft_bf16 = P.Group(configs.softmax_causal_dag(0.125, 1024), [((R, C), "bf16")], (R, C), "bf16")
+    add("softmax_causal_bf16", allowed * 2 + R * C * 2, lambda: soft_bf16.run([sb], pb, stream=stream))
+    del sb, pb
+    # wide rows: the tiled kernel re-reads the row in each phase
+    xw = configs.softmax_scores(8192, 131072, device=dev)
+    yw = torch.empty_like(xw)
+    wide = P.Group(configs.softmax_dag(0.125), [((8192, 131072), "f32")], (8192, 131072), "f32")
+    add("softmax_wide_8192x131072_f32", 2 * xw.numel() * 4, lambda: wide.run([xw], yw, stream=stream),
+        note="tiled kernel: 3 phases read the row, bytes counted once")
+    del xw, yw
 
     # layer normalization with its row statistics, bf16 [16384, 4096]: one
     # kernel, two reduction phases, three outputs
