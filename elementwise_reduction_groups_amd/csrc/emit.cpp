@@ -256,12 +256,13 @@ __device__ __forceinline__ float psk_rt(float a) { return psk_h(psk_r1(a)); }
 // is the Chebyshev-fitted form of Press, Teukolsky, Vetterling and Flannery,
 // Numerical Recipes (2nd ed.), section 6.2: erfc(w) = t exp(-w^2 + P(t)),
 // t = 1/(1 + w/2), fractional error below 1.2e-7 for all w >= 0.  The
-// exponential takes -w^2 as the exact pair hi + lo (an fma gives the
-// rounding error of w*w) and reduces it Cody-Waite style with the
-// 15-significant-bit split of ln 2, so the large term never rounds; the
-// reduced argument (|r| < 0.35) goes through the hardware 2^x.  For x > 0,
-// Phi = 1 - erfc(w)/2.  w is clamped at 10, where erfc(w) < 2^-149: Phi is
-// then 0 or 1, also for infinite x (a NaN x stays NaN through x * Phi).
+// exponent z = P(t) - w^2 is formed with one rounding (an fma) and taken to
+// base 2, split into an integer k and |r| <= 1/2 for the hardware 2^x, and
+// scaled back by 2^k (so tiny results come out subnormal, not zero).  The
+// rounding of z costs a relative error of about w^2 2^-24 in erfc, below
+// 6e-7 where |x| < 4.3 and negligible beside gelu's size beyond.  For
+// x > 0, Phi = 1 - erfc(w)/2.  w is clamped at 10, where erfc(w) < 2^-149:
+// Phi is then 0 or 1, also for infinite x (a NaN x stays NaN).
 __device__ __forceinline__ float psk_gelu(float x) {
   const float w = fminf(fabsf(x) * 0.70710678118654752440f, 10.0f);
   const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, w, 1.0f));
@@ -269,13 +270,9 @@ __device__ __forceinline__ float psk_gelu(float x) {
   p = fmaf(p, t, -0.82215223f); p = fmaf(p, t, 1.48851587f); p = fmaf(p, t, -1.13520398f);
   p = fmaf(p, t, 0.27886807f);  p = fmaf(p, t, -0.18628806f); p = fmaf(p, t, 0.09678418f);
   p = fmaf(p, t, 0.37409196f);  p = fmaf(p, t, 1.00002368f);  p = fmaf(p, t, -1.26551223f);
-  const float hi = w * w;
-  const float lo = fmaf(w, w, -hi);
-  const float k = __builtin_rintf(hi * -1.44269504088896341f);
-  float r = fmaf(k, -0.693145751953125f, -hi);
-  r = fmaf(k, -1.42860682030941723212e-6f, r);
-  r = r + (p - lo);
-  const float ec = t * __builtin_ldexpf(__builtin_amdgcn_exp2f(r * 1.44269504088896341f), (int)k);
+  const float z2 = fmaf(-w, w, p) * 1.44269504088896341f;
+  const float k = __builtin_rintf(z2);
+  const float ec = t * __builtin_ldexpf(__builtin_amdgcn_exp2f(z2 - k), (int)k);
   const float phi = (x > 0.0f) ? fmaf(-0.5f, ec, 1.0f) : 0.5f * ec;
   return x * phi;
 }
@@ -286,11 +283,13 @@ __device__ __forceinline__ float psk_gelu(float x) {
 // b lies in [2^-40, 2^40] and a is zero or in [2^-86, 2^87] (no underflow of
 // the remainder, no overflow of q); `bad` records a lane where it may not,
 // and the caller then redoes that member's elements with IEEE division.
+// A zero a gives q itself: the correction would turn -0 into +0.
 __device__ __forceinline__ float psk_divr(float a, float b, float y, bool& bad) {
   const float q = a * y;
   const float rem = fmaf(-q, b, a);
-  bad |= !((fabsf(a) >= 0x1p-86f || a == 0.0f) && fabsf(a) <= 0x1p87f);
-  return fmaf(rem, y, q);
+  const bool zero = a == 0.0f;
+  bad |= !((fabsf(a) >= 0x1p-86f || zero) && fabsf(a) <= 0x1p87f);
+  return zero ? q : fmaf(rem, y, q);
 }
 __device__ __forceinline__ float psk_max(float a, float b) { return (a > b) ? a : b; }
 __device__ __forceinline__ float psk_min(float a, float b) { return (a < b) ? a : b; }

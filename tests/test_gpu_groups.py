@@ -223,3 +223,35 @@ def test_row_group_two_phase_max_sum_mean():
     _, out = run_group(nodes, [x, s, k], (150, 777), "f32")
     ref = oracle.eval_group(nodes, [to_np(x), to_np(s), to_np(k)], (150, 777))
     assert_f32_close(to_np(out), ref, "two-phase row group")
+
+
+@pytest.mark.parametrize("C", [256, 1000, 40000])
+def test_division_by_a_row_value_is_ieee_bit_exact(C):
+    """x / row_max(|x| + d): the maximum is exact in any order, so the
+    quotients must be IEEE's bit for bit: signed zeros, tiny and huge
+    numerators (the path that falls back to IEEE division), negative and
+    huge divisors (rows scaled by d), in the register and the tiled kernel."""
+    R = 12
+    gen = torch.Generator(device="cpu").manual_seed(C)
+    x = torch.randn(R, C, generator=gen)
+    x[0, ::3] = -0.0
+    x[1, ::5] = 0.0
+    x[2, ::7] = 1e-30                       # below 2^-86: the IEEE fallback
+    x[3, ::11] = -3e38
+    x[4] = x[4] * 1e-38                     # subnormal-range numerators
+    d = torch.ones(R, 1)
+    d[5] = -2.0                             # negative divisors after the negation below
+    d[6] = 1e30
+    d[7] = 1e-35
+    nodes = parse_dag("""%0 = input 0
+%1 = input 1
+%2 = abs %0
+%3 = add %2 %1
+%4 = row_max %3
+%5 = mul %4 %1
+%6 = div %0 %5
+""")
+    _, out = run_group(nodes, [x.to(DEV), d.to(DEV)], (R, C), "f32")
+    ref = oracle.eval_group(nodes, [x.numpy(), d.numpy()], (R, C))
+    assert_bits(to_np(out), ref, f"x / row value, {C} columns")
+    assert (to_np(out)[0, ::3].view(np.uint32) == 0x80000000).all()   # -0 / positive = -0
