@@ -103,8 +103,8 @@ static int layout_value(const char* key, int dflt)
 std::string KernelPlan::key() const
 {
     char b[160];
-    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d c%d w%d", kind, vec, block, lanes, nv, (int)nt,
-                  (int)xcd, (long long)blocks, tiles, (int)tcache, wpe);
+    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d c%d w%d p%d", kind, vec, block, lanes, nv,
+                  (int)nt, (int)xcd, (long long)blocks, tiles, (int)tcache, wpe, persist);
     return b;
 }
 
@@ -151,7 +151,7 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
         // about 32 bytes of output per lane (8 f32 or 16 bf16 elements); a
         // row is 16 lanes (one DPP row) or whole waves; a workgroup of at
         // least 128 threads, one row per workgroup once a row has 128 lanes
-        const int epl = an.out_dtype == PSK_BF16 ? 16 : 8;
+        const int epl = layout_value("epl", an.out_dtype == PSK_BF16 ? 16 : 8);
         int64_t want = ceil_div(an.cols, epl);
         int L = 16;
         while (L < want && L < 1024) L <<= 1;
@@ -169,7 +169,17 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
         // registers.  The tiled kernel gives a row one workgroup, walks it in
         // tiles of lanes * tn vectors, and re-reads it in every phase (the
         // re-reads of a row come from the caches).
+        // Persistent rows: a few workgroups per CU walk the rows, loading the
+        // next row while the current one is computed (one row per workgroup
+        // of at least 128 lanes).
+        const int persist = layout_value("persist", 0);
+        if (persist > 0 && p.rows_per_block == 1) {
+            p.persist = persist;
+            p.blocks = std::min<int64_t>(an.rows, (int64_t)256 * persist);
+            p.xcd = false;
+        }
         if ((int64_t)p.nv * p.vec > 32 || layout_value("tiled", 0)) {
+            p.persist = 0;
             p.kind = 3;
             int Lt = layout_value("lanes", 1024);
             if (!(Lt >= 64 && Lt <= 1024 && !(Lt & (Lt - 1)))) Lt = 1024;
@@ -270,6 +280,24 @@ __device__ __forceinline__ float psk_gelu(float x) {
   p = fmaf(p, t, -0.82215223f); p = fmaf(p, t, 1.48851587f); p = fmaf(p, t, -1.13520398f);
   p = fmaf(p, t, 0.27886807f);  p = fmaf(p, t, -0.18628806f); p = fmaf(p, t, 0.09678418f);
   p = fmaf(p, t, 0.37409196f);  p = fmaf(p, t, 1.00002368f);  p = fmaf(p, t, -1.26551223f);
+  const float z2 = fmaf(-w, w, p) * 1.44269504088896341f;
+  const float k = __builtin_rintf(z2);
+  const float ec = t * __builtin_ldexpf(__builtin_amdgcn_exp2f(z2 - k), (int)k);
+  const float phi = (x > 0.0f) ? fmaf(-0.5f, ec, 1.0f) : 0.5f * ec;
+  return x * phi;
+}
+// gelu whose value is only rounded to bf16 (the root of a group whose
+// results are all bf16): the same form with a degree-5 exponent polynomial,
+// fitted here (weighted least squares towards minimax on t in [1/6, 1],
+// w in [0, 10]); its relative error in erfc is below 8e-6, far inside a
+// bf16 half-ulp (2^-9), so the rounded result is the exact one's or its
+// neighbour.
+__device__ __forceinline__ float psk_gelu_b(float x) {
+  const float w = fminf(fabsf(x) * 0.70710678118654752440f, 10.0f);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, w, 1.0f));
+  float p = 0.228792509f;
+  p = fmaf(p, t, -0.709197821f); p = fmaf(p, t, 0.474501494f); p = fmaf(p, t, 0.254438582f);
+  p = fmaf(p, t, 1.01801471f);   p = fmaf(p, t, -1.26654186f);
   const float z2 = fmaf(-w, w, p) * 1.44269504088896341f;
   const float k = __builtin_rintf(z2);
   const float ec = t * __builtin_ldexpf(__builtin_amdgcn_exp2f(z2 - k), (int)k);
@@ -405,7 +433,33 @@ struct Emitter {
     bool divr_node(int i) const
     {
         const psk_node& nd = an.nodes[i];
-        return !use_refused && divr_ok && nd.op == PSK_OP_DIV && !an.is_row[i] && an.is_row[nd.b];
+        return !use_refused && divr_ok && !bf16_results() && nd.op == PSK_OP_DIV && !an.is_row[i] && an.is_row[nd.b];
+    }
+
+    // every value the group stores is bf16: interior f32 values only reach
+    // memory through a rounding to 8 significant bits
+    bool bf16_results() const
+    {
+        if (an.out_dtype != PSK_BF16) return false;
+        for (const auto& x : an.extras)
+            if (x.dtype != PSK_BF16) return false;
+        return true;
+    }
+
+    // node i's value is rounded to bf16 and read by no member
+    bool bf16_terminal(int i) const
+    {
+        if (!bf16_results() || an.n_readers[i] != 0) return false;
+        return i == an.root || an.stored[i] > 0;
+    }
+
+    // element / row value in a bf16-results group: the row's reciprocal
+    // (correctly rounded) times the element, within 1.5 f32 ulps of the
+    // quotient
+    bool recip_node(int i) const
+    {
+        const psk_node& nd = an.nodes[i];
+        return !use_refused && divr_ok && bf16_results() && nd.op == PSK_OP_DIV && !an.is_row[i] && an.is_row[nd.b];
     }
 
     // elements of member i (given as element indices) written through
@@ -435,6 +489,7 @@ struct Emitter {
         case PSK_OP_SUB: return "(" + A() + " - " + B() + ")";
         case PSK_OP_MUL: return "(" + A() + " * " + B() + ")";
         case PSK_OP_DIV:
+            if (recip_node(i)) return "(" + A() + " * y" + std::to_string(nd.b) + ")";
             if (divr_node(i))
                 return "psk_divr(" + A() + ", " + B() + ", y" + std::to_string(nd.b) + ", bad" + std::to_string(i) + ")";
             return "(" + A() + " / " + B() + ")";
@@ -447,7 +502,7 @@ struct Emitter {
         case PSK_OP_SQRT: return "sqrtf(" + A() + ")";
         case PSK_OP_TANH: return "tanhf(" + A() + ")";
         case PSK_OP_ERF: return "erff(" + A() + ")";
-        case PSK_OP_GELU: return "psk_gelu(" + A() + ")";
+        case PSK_OP_GELU: return (bf16_terminal(i) ? "psk_gelu_b(" : "psk_gelu(") + A() + ")";
         case PSK_OP_SQRTABS: return "sqrtf(fabsf(" + A() + "))";
         case PSK_OP_POW2: return "(" + A() + " * " + A() + ")";
         case PSK_OP_POWN: {
@@ -549,6 +604,75 @@ struct Emitter {
             std::string v;
             if (in.dtype == PSK_F32) v = "__uint_as_float(" + words[j] + ")";
             else v = (j % 2 == 0 ? "psk_lo(" : "psk_hi(") + words[j / 2] + ")";
+            o << "    const float " << dst(j) << " = " << v << ";\n";
+        }
+    }
+
+    // The pieces input k's vector at element e0 arrives in: (type, name
+    // suffix, element offset); V == 1 arrives as one widened float.
+    struct Piece {
+        std::string type, name;
+        int eoff;
+    };
+    std::vector<Piece> pieces(int k, int e0) const
+    {
+        const InputInfo& in = an.inputs[k];
+        const int V = pl.vec;
+        const std::string base = std::to_string(k) + "_" + std::to_string(e0);
+        if (V == 1) return {{"float", base, 0}};
+        if (in.dtype == PSK_U8) {
+            const int nw = std::max(1, V / 4);
+            return {{nw == 1 ? "psk_u32" : nw == 2 ? "psk_u2v" : "psk_u4v", base, 0}};
+        }
+        std::vector<Piece> ps;
+        const int nwords = V * esize(in.dtype) / 4, epw = 4 / esize(in.dtype);
+        for (int w = 0, piece = 0; w < nwords; w += 4, ++piece)
+            ps.push_back({nwords - w >= 4 ? "psk_u4v" : "psk_u2v", base + "_" + std::to_string(piece), w * epw});
+        return ps;
+    }
+
+    // declare input k's pieces as `pfx`<name> and load them (zero when cond fails)
+    void load_pieces(int k, const std::string& off, int e0, const std::string& cond, const std::string& pfx)
+    {
+        const InputInfo& in = an.inputs[k];
+        const std::string p = "(in" + std::to_string(k) + " + " + off + ")";
+        for (const Piece& pc : pieces(k, e0)) {
+            o << "    " << pc.type << " " << pfx << pc.name << " = {};\n";
+            if (pc.type == "float")
+                o << "    if (" << cond << ") " << pfx << pc.name << " = " << widen(in.dtype, ld_fn() + "(" + p + ")")
+                  << ";\n";
+            else
+                o << "    if (" << cond << ") " << pfx << pc.name << " = " << ld_fn() << "((const " << pc.type << "*)("
+                  << p << " + " << pc.eoff << "));\n";
+        }
+    }
+
+    // the f32 values x<k>_<e> of input k's vector at e0 from pieces `pfx`<name>
+    void decode_pieces(int k, int e0, const std::string& pfx)
+    {
+        const InputInfo& in = an.inputs[k];
+        const int V = pl.vec;
+        const std::vector<Piece> ps = pieces(k, e0);
+        auto dst = [&](int j) { return "x" + std::to_string(k) + "_" + std::to_string(e0 + j); };
+        if (V == 1) {
+            o << "    const float " << dst(0) << " = " << pfx << ps[0].name << ";\n";
+            return;
+        }
+        if (in.dtype == PSK_U8) {
+            const int nw = std::max(1, V / 4);
+            for (int j = 0; j < V; ++j) {
+                std::string w = pfx + ps[0].name + (nw == 1 ? "" : "[" + std::to_string(j / 4) + "]");
+                o << "    const float " << dst(j) << " = (float)((" << w << " >> " << 8 * (j % 4) << ") & 255u);\n";
+            }
+            return;
+        }
+        std::vector<std::string> words;
+        for (const Piece& pc : ps)
+            for (int q = 0; q < (pc.type == "psk_u4v" ? 4 : 2); ++q)
+                words.push_back(pfx + pc.name + "[" + std::to_string(q) + "]");
+        for (int j = 0; j < V; ++j) {
+            std::string v = in.dtype == PSK_F32 ? "__uint_as_float(" + words[j] + ")"
+                                                : (j % 2 == 0 ? "psk_lo(" : "psk_hi(") + words[j / 2] + ")";
             o << "    const float " << dst(j) << " = " << v << ";\n";
         }
     }
@@ -966,20 +1090,24 @@ struct Emitter {
         }
         if (W > 1) {
             const int NR = (int)reds.size();
+            const int size = pl.rows_per_block * W * NR;
+            // a persistent workgroup alternates two halves, so a wave that is
+            // one row ahead never overwrites values another wave still reads
+            const std::string base = pl.persist ? "par * " + std::to_string(size) + " + " : "";
             std::string arr = "psk_red" + std::to_string(p);
-            o << "    __shared__ float " << arr << "[" << pl.rows_per_block * W * NR << "];\n";
+            o << "    __shared__ float " << arr << "[" << (pl.persist ? 2 : 1) * size << "];\n";
             o << "    if ((lane & 63) == 0) {\n";
             for (int r = 0; r < NR; ++r)
-                o << "      " << arr << "[(slot * " << W << " + (lane >> 6)) * " << NR << " + " << r << "] = p"
-                  << reds[r] << ";\n";
+                o << "      " << arr << "[" << base << "(slot * " << W << " + (lane >> 6)) * " << NR << " + " << r
+                  << "] = p" << reds[r] << ";\n";
             o << "    }\n    __syncthreads();\n";
             for (int r = 0; r < NR; ++r) {
                 int i = reds[r];
                 bool mx = an.nodes[i].op == PSK_OP_ROW_MAX;
-                o << "    p" << i << " = " << arr << "[(slot * " << W << ") * " << NR << " + " << r << "];\n";
+                o << "    p" << i << " = " << arr << "[" << base << "(slot * " << W << ") * " << NR << " + " << r << "];\n";
                 for (int w = 1; w < W; ++w) {
-                    std::string el = arr + "[(slot * " + std::to_string(W) + " + " + std::to_string(w) + ") * " +
-                                     std::to_string(NR) + " + " + std::to_string(r) + "]";
+                    std::string el = arr + "[" + base + "(slot * " + std::to_string(W) + " + " + std::to_string(w) +
+                                     ") * " + std::to_string(NR) + " + " + std::to_string(r) + "]";
                     if (mx) o << "    p" << i << " = psk_max(p" << i << ", " << el << ");\n";
                     else o << "    p" << i << " = p" << i << " + " << el << ";\n";
                 }
@@ -1117,8 +1245,123 @@ struct Emitter {
         return o.str();
     }
 
+    // the phases of one row and its stores (rows of the register kernel)
+    void row_body()
+    {
+        const int L = pl.lanes, V = pl.vec;
+        leaves();
+        for (int p = 0; p <= an.phases; ++p) {
+            members_at(p);
+            for (size_t k = 0; k < an.extras.size(); ++k) {
+                const Analysis::Extra& x = an.extras[k];
+                if (an.depth[x.node] != p) continue;
+                std::string xo = "xo" + std::to_string(k);
+                if (x.per_row) {
+                    o << "    if (rok && lane == 0) " << xo << "[row] = " << scalar_store(x.node, x.dtype) << ";\n";
+                    continue;
+                }
+                for (int v = 0; v < pl.nv; ++v) {
+                    std::string c = "c" + std::to_string(v);
+                    std::string cond = "rok";
+                    if ((int64_t)(v + 1) * L * V > an.cols) cond += " && " + c + " < " + std::to_string(an.cols);
+                    store_node(x.node, xo, x.dtype, "row * (" + std::string(I()) + ")" + std::to_string(an.cols) + " + " + c,
+                               v * V, cond);
+                }
+            }
+            if (p < an.phases) reductions_at(p);
+        }
+        for (int v = 0; v < pl.nv; ++v) {
+            std::string c = "c" + std::to_string(v);
+            std::string cond = "rok";
+            if ((int64_t)(v + 1) * L * V > an.cols) cond += " && " + c + " < " + std::to_string(an.cols);
+            store_vec("row * (" + std::string(I()) + ")" + std::to_string(an.cols) + " + " + c, v * V, cond);
+        }
+    }
+
+    // Persistent rows: gridDim.x workgroups walk the rows (row, row + G,
+    // ...); the next row's element inputs are loaded before the current row
+    // is computed, so its loads are in flight during the arithmetic.  Column
+    // vectors (gamma) are loaded and widened once per workgroup.
+    std::string row_persistent(const std::string& name)
+    {
+        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n" << kPrelude;
+        signature(name);
+        const int L = pl.lanes, V = pl.vec;
+        auto streamed = [&](const InputInfo& in) {
+            return in.used && in.kind != InKind::Scalar && in.kind != InKind::RowConst && in.kind != InKind::ColVec;
+        };
+        auto vcond = [&](int v, const std::string& ok, const std::string& qv, const InputInfo& in) {
+            std::string c = "c" + std::to_string(v);
+            std::string cond = ok;
+            if ((int64_t)(v + 1) * L * V > an.cols) cond += " && " + c + " < " + std::to_string(an.cols);
+            if (in.mask_guarded) cond += " && " + c + " <= " + qv;
+            return cond;
+        };
+        o << "  {\n";
+        o << "    const int slot = 0;\n";
+        o << "    const int lane = (int)threadIdx.x;\n";
+        for (int k = 0; k < pl.nv; ++k)
+            o << "    const int c" << k << " = (" << k * L << " + lane) * " << V << ";\n";
+        // column vectors: once
+        for (size_t k = 0; k < an.inputs.size(); ++k) {
+            const InputInfo& in = an.inputs[k];
+            if (!in.used || in.kind != InKind::ColVec) continue;
+            for (int v = 0; v < pl.nv; ++v) {
+                std::string c = "c" + std::to_string(v);
+                std::string cond = "true";
+                if ((int64_t)(v + 1) * L * V > an.cols) cond = c + " < " + std::to_string(an.cols);
+                load_vec((int)k, c, v * V, cond);
+            }
+        }
+        o << "    " << I() << " row = (" << I() << ")blockIdx.x;\n";
+        o << "    const " << I() << " G = (" << I() << ")gridDim.x;\n";
+        o << "    int par = 0;\n";
+        if (period > 0) o << "    int q0 = (int)(row % (" << I() << ")" << period << ");\n";
+        // the first row's element inputs
+        for (size_t k = 0; k < an.inputs.size(); ++k) {
+            const InputInfo& in = an.inputs[k];
+            if (!streamed(in)) continue;
+            for (int v = 0; v < pl.nv; ++v)
+                load_pieces((int)k, elem_offset(in, "row", "c" + std::to_string(v)), v * V,
+                            vcond(v, "row < (" + std::string(I()) + ")n_total", "q0", in), "cw");
+        }
+        o << "    for (; row < (" << I() << ")n_total; row += G) {\n";
+        o << "    const " << I() << " nrow = row + G;\n";
+        o << "    const bool nok = nrow < (" << I() << ")n_total;\n";
+        if (period > 0) o << "    const int qn = (int)(nrow % (" << I() << ")" << period << ");\n";
+        for (size_t k = 0; k < an.inputs.size(); ++k) {
+            const InputInfo& in = an.inputs[k];
+            if (!streamed(in)) continue;
+            for (int v = 0; v < pl.nv; ++v)
+                load_pieces((int)k, elem_offset(in, "nrow", "c" + std::to_string(v)), v * V, vcond(v, "nok", "qn", in),
+                            "nw");
+        }
+        o << "    {\n";
+        o << "    const bool rok = true;\n";
+        if (period > 0) o << "    const int q = (int)(row % (" << I() << ")" << period << ");\n";
+        row_inputs("row", "rok");
+        for (size_t k = 0; k < an.inputs.size(); ++k) {
+            const InputInfo& in = an.inputs[k];
+            if (!streamed(in)) continue;
+            for (int v = 0; v < pl.nv; ++v) decode_pieces((int)k, v * V, "cw");
+        }
+        row_body();
+        o << "    }\n";
+        for (size_t k = 0; k < an.inputs.size(); ++k) {
+            const InputInfo& in = an.inputs[k];
+            if (!streamed(in)) continue;
+            for (int v = 0; v < pl.nv; ++v)
+                for (const Piece& pc : pieces((int)k, v * V)) o << "    cw" << pc.name << " = nw" << pc.name << ";\n";
+        }
+        o << "    par ^= 1;\n";
+        o << "    }\n";
+        o << "  }\n}\n";
+        return o.str();
+    }
+
     std::string row(const std::string& name)
     {
+        if (pl.persist) return row_persistent(name);
         o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n" << kPrelude;
         signature(name);
         const int L = pl.lanes, V = pl.vec;

@@ -90,6 +90,7 @@ struct KernelPlan {
     int tiles = 0;           // tiled row kernel (kind 3): tiles per row, each phase re-reads the row
     bool tcache = true;      // tiled row kernel: cached (plain) loads before the last phase
     int wpe = 0;             // tiled row kernel: at most this many waves per SIMD (0: no limit)
+    int persist = 0;         // row kernel: persistent workgroups per CU (0: one workgroup per row)
     bool nt = true;          // nontemporal loads and stores
     bool xcd = true;         // each XCD takes a contiguous eighth of the blocks
     int64_t blocks = 0;      // workgroups that carry work

@@ -407,3 +407,28 @@ def test_wide_rows_take_the_tiled_kernel(lib, tmp_path):
     # rows past 2^30 columns are refused
     _refused(_desc("%0 = input 0\n%1 = row_max %0\n%2 = sub %0 %1\n", [((1, (1 << 30) + 8), "f32")],
                    (1, (1 << 30) + 8)), P.PSK_E_UNSUPPORTED)
+
+
+def test_precision_follows_what_is_stored(lib):
+    from synth import configs as C
+    eps = C.f32(1e-5)
+    R, N = 64, 4096
+    # every result bf16: the gelu root takes the bf16 form, the division by
+    # the row value the row's reciprocal
+    rms = P.psk_group_source(P.GroupDesc(C.rmsnorm_gelu_dag(eps), [((R, N), "bf16"), ((R, N), "bf16"),
+                                                                    ((N,), "bf16")], (R, N), "bf16"))
+    body = rms[rms.index('extern "C"'):]
+    assert "psk_gelu_b(" in body and "psk_divr(" not in body and "* y8)" in body
+    # an f32 result (or an f32 stored statistic) keeps the f32 forms
+    rms32 = P.psk_group_source(P.GroupDesc(C.rmsnorm_gelu_dag(eps), [((R, N), "bf16"), ((R, N), "bf16"),
+                                                                      ((N,), "bf16")], (R, N), "f32"))
+    body = rms32[rms32.index('extern "C"'):]
+    assert "psk_gelu(" in body and "psk_gelu_b(" not in body and "psk_divr(" in body
+    ln = P.psk_group_source(P.GroupDesc(C.layernorm_dag(eps), [((R, N), "bf16"), ((N,), "bf16"), ((N,), "bf16")],
+                                        (R, N), "bf16", root=C.LAYERNORM_ROOT,
+                                        extras=[(C.LAYERNORM_MEAN, (R, 1), "f32"), (C.LAYERNORM_RSTD, (R, 1), "f32")]))
+    assert "psk_divr(" in ln[ln.index('extern "C"'):]
+    # a gelu that other members read is not the bf16 form
+    tree = P.psk_group_source(P.GroupDesc(C.tree_mixed_dag(), [((1,), "f32"), ((1,), "bf16"), ((), "f32")], (1,),
+                                          "bf16", flags=P.PSK_GROUP_TREE))
+    assert "psk_gelu(" in tree[tree.index('extern "C"'):] and "psk_gelu_b(" not in tree[tree.index('extern "C"'):]
