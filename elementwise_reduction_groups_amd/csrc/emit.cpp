@@ -608,6 +608,38 @@ struct Emitter {
         }
     }
 
+    // Extra load condition for a vector of `in` at element e0 (columns from
+    // c): under a causal mask, the vector's first column is allowed; under a
+    // byte mask read by every WHERE, some mask byte under the vector allows
+    // (the mask's own vector at e0 is loaded first).
+    std::string guard(const InputInfo& in, int e0, const std::string& c) const
+    {
+        if (!in.mask_guarded) return "";
+        if (an.mask_period > 0) return " && " + c + " <= q";
+        if (an.where_mask < 0) return "";
+        const InputInfo& m = an.inputs[an.where_mask];
+        const std::string mk = std::to_string(an.where_mask);
+        if (m.kind == InKind::Scalar || m.kind == InKind::RowConst) return " && xr" + mk + " != 0.0f";
+        const int V = pl.vec;
+        if (V == 1) return " && x" + mk + "_" + std::to_string(e0) + " != 0.0f";
+        const std::string w = "w" + mk + "_" + std::to_string(e0);
+        const int nw = std::max(1, V / 4);
+        if (nw == 1) return " && " + w + " != 0u";
+        std::string any = w + "[0]";
+        for (int q = 1; q < nw; ++q) any += " | " + w + "[" + std::to_string(q) + "]";
+        return " && (" + any + ") != 0u";
+    }
+
+    // input indices in load order: the unguarded first (the mask among them)
+    std::vector<int> load_order() const
+    {
+        std::vector<int> ks;
+        for (int pass = 0; pass < 2; ++pass)
+            for (size_t k = 0; k < an.inputs.size(); ++k)
+                if (an.inputs[k].mask_guarded == (pass == 1)) ks.push_back((int)k);
+        return ks;
+    }
+
     // The pieces input k's vector at element e0 arrives in: (type, name
     // suffix, element offset); V == 1 arrives as one widened float.
     struct Piece {
@@ -906,12 +938,10 @@ struct Emitter {
         o << "    const " << I() << " c0 = e0 - row * (" << I() << ")" << an.cols << ";\n";
         if (period > 0) o << "    const " << I() << " q = row % (" << I() << ")" << period << ";\n";
         row_inputs("row", "true");
-        for (size_t k = 0; k < an.inputs.size(); ++k) {
+        for (int k : load_order()) {
             const InputInfo& in = an.inputs[k];
             if (!in.used || in.kind == InKind::Scalar || in.kind == InKind::RowConst) continue;
-            std::string cond = V == 1 ? "true" : "true";
-            if (in.mask_guarded) cond = "c0 <= q";
-            load_vec((int)k, elem_offset(in, "row", "c0"), 0, cond);
+            load_vec(k, elem_offset(in, "row", "c0"), 0, "true" + guard(in, 0, "c0"));
         }
         leaves();
         members_at(0);
@@ -1203,19 +1233,18 @@ struct Emitter {
             o << "    const int cb = t * " << tile << ";\n";
             for (int k = 0; k < TN; ++k)
                 o << "    const int c" << k << " = cb + (" << k * L << " + lane) * " << V << ";\n";
-            for (size_t k = 0; k < an.inputs.size(); ++k) {
+            for (int k : load_order()) {
                 const InputInfo& in = an.inputs[k];
                 if (!in.used || in.kind == InKind::Scalar || in.kind == InKind::RowConst) continue;
                 bool used_here = false;
                 for (size_t i = 0; i < an.nodes.size(); ++i)
-                    if (need[i] && an.nodes[i].op == PSK_OP_INPUT && an.nodes[i].iparam == (int)k) used_here = true;
+                    if (need[i] && an.nodes[i].op == PSK_OP_INPUT && an.nodes[i].iparam == k) used_here = true;
                 if (!used_here) continue;
                 for (int v = 0; v < TN; ++v) {
                     std::string c = "c" + std::to_string(v);
                     std::string cond = "rok";
                     if (ragged) cond += " && " + c + " < " + std::to_string(an.cols);
-                    if (in.mask_guarded) cond += " && " + c + " <= q";
-                    load_vec((int)k, elem_offset(in, "row", c), v * V, cond);
+                    load_vec(k, elem_offset(in, "row", c), v * V, cond + guard(in, v * V, c));
                 }
             }
             leaves(2, &need);
@@ -1294,7 +1323,7 @@ struct Emitter {
             std::string c = "c" + std::to_string(v);
             std::string cond = ok;
             if ((int64_t)(v + 1) * L * V > an.cols) cond += " && " + c + " < " + std::to_string(an.cols);
-            if (in.mask_guarded) cond += " && " + c + " <= " + qv;
+            if (in.mask_guarded && an.mask_period > 0) cond += " && " + c + " <= " + qv;   // byte masks: no skip here
             return cond;
         };
         o << "  {\n";
@@ -1375,15 +1404,14 @@ struct Emitter {
         for (int k = 0; k < pl.nv; ++k)
             o << "    const int c" << k << " = (" << k * L << " + lane) * " << V << ";\n";
         row_inputs("row", "rok");
-        for (size_t k = 0; k < an.inputs.size(); ++k) {
+        for (int k : load_order()) {
             const InputInfo& in = an.inputs[k];
             if (!in.used || in.kind == InKind::Scalar || in.kind == InKind::RowConst) continue;
             for (int v = 0; v < pl.nv; ++v) {
                 std::string c = "c" + std::to_string(v);
                 std::string cond = "rok";
                 if ((int64_t)(v + 1) * L * V > an.cols) cond += " && " + c + " < " + std::to_string(an.cols);
-                if (in.mask_guarded) cond += " && " + c + " <= q";
-                load_vec((int)k, elem_offset(in, "row", c), v * V, cond);
+                load_vec(k, elem_offset(in, "row", c), v * V, cond + guard(in, v * V, c));
             }
         }
         leaves();

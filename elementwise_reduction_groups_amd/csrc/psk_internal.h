@@ -31,7 +31,7 @@ struct InputInfo {
     int64_t numel = 0;
     InKind kind = InKind::Scalar;
     bool used = false;
-    bool mask_guarded = false;   // read only where a causal mask allows
+    bool mask_guarded = false;   // read only where the group's mask (causal or WHERE) allows
 };
 
 // Everything the emitter needs to know about a validated group.
@@ -47,6 +47,8 @@ struct Analysis {
     std::vector<char> needed;           // reachable from the root
     // causal masks (one period): values at refused positions
     int mask_period = 0;                // 0: no causal mask, or masks of different periods
+    int where_mask = -1;                // the input every WHERE reads as its mask (or -1): inputs
+                                        // marked mask_guarded are then read only where it allows
     std::vector<char> irrelevant;       // element value never used at a refused position
     std::vector<char> uniform;          // element value at refused positions is one value per row
     std::vector<InputInfo> inputs;

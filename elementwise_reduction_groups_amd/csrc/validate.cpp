@@ -394,6 +394,56 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
                     in.mask_guarded = false;
             }
     }
+
+    // ---- inputs read only where a byte mask allows them
+    // The same analysis for WHERE, when there is no causal mask and every
+    // WHERE reads one mask input: a value read only as a WHERE's value (or
+    // by members themselves irrelevant there) is not needed where the mask
+    // refuses, and its vector is loaded only when a mask byte under it
+    // allows.
+    if (period < 0) {
+        int mask_slot = -1;
+        bool one_mask = true;
+        for (int i = 0; i < n; ++i)
+            if (an.nodes[i].op == PSK_OP_WHERE) {
+                const int slot = an.nodes[an.nodes[i].a].iparam;
+                if (mask_slot < 0) mask_slot = slot;
+                else if (mask_slot != slot) one_mask = false;
+            }
+        if (mask_slot >= 0 && one_mask) {
+            std::vector<std::vector<int>> readers(n);
+            for (int i = 0; i < n; ++i) {
+                const psk_node& nd = an.nodes[i];
+                int ar = op_arity(nd.op);
+                const int32_t opnd[3] = {nd.a, nd.b, nd.c};
+                for (int k = 0; k < ar; ++k) readers[opnd[k]].push_back(i);
+            }
+            std::vector<char> irrelevant(n, 0);
+            for (int i = n - 1; i >= 0; --i) {
+                if (i == an.root || an.stored[i] || readers[i].empty() || an.is_row[i]) continue;
+                if (an.nodes[i].op == PSK_OP_INPUT && an.nodes[i].iparam == mask_slot) continue;
+                bool irr = true;
+                for (int r : readers[i]) {
+                    const psk_node& rd = an.nodes[r];
+                    if (rd.op == PSK_OP_WHERE && rd.b == i) continue;
+                    if (op_is_row(rd.op) || an.is_row[r] || !irrelevant[r]) { irr = false; break; }
+                }
+                irrelevant[i] = irr;
+            }
+            bool any = false;
+            for (auto& in : an.inputs) in.mask_guarded = in.used;
+            for (int i = 0; i < n; ++i)
+                if (an.nodes[i].op == PSK_OP_INPUT) {
+                    InputInfo& in = an.inputs[an.nodes[i].iparam];
+                    if (!irrelevant[i] || in.kind == InKind::Scalar || in.kind == InKind::RowConst)
+                        in.mask_guarded = false;
+                }
+            for (auto& in : an.inputs) any = any || in.mask_guarded;
+            if (any) an.where_mask = mask_slot;
+            else
+                for (auto& in : an.inputs) in.mask_guarded = false;
+        }
+    }
     return PSK_OK;
 }
 

@@ -255,3 +255,36 @@ def test_division_by_a_row_value_is_ieee_bit_exact(C):
     ref = oracle.eval_group(nodes, [x.numpy(), d.numpy()], (R, C))
     assert_bits(to_np(out), ref, f"x / row value, {C} columns")
     assert (to_np(out)[0, ::3].view(np.uint32) == 0x80000000).all()   # -0 / positive = -0
+
+
+def test_persistent_row_layout_is_bit_identical(monkeypatch):
+    """The persistent row kernel (a layout switch: a few workgroups per CU
+    walk the rows and prefetch the next one) gives the one-row-per-workgroup
+    kernel's bits: same reduction order, LDS halves alternating by row."""
+    R, C = 3000, 4096
+    x, r, g = configs.rmsnorm_inputs(R, C, device=DEV, seed=5)
+    xl, gl, bl = configs.layernorm_inputs(R, C, device=DEV, seed=6)
+    s = configs.softmax_scores(2048, 1024, device=DEV, seed=7)
+    m = configs.random_mask(1024, 1024, 0.5, empty_rows=[3], device=DEV, seed=8)
+    cases = [
+        (configs.rmsnorm_gelu_dag(EPS), [((R, C), "bf16"), ((R, C), "bf16"), ((C,), "bf16")], (R, C), "bf16", {},
+         [x, r, g], []),
+        (configs.layernorm_dag(EPS), [((R, C), "bf16"), ((C,), "bf16"), ((C,), "bf16")], (R, C), "bf16",
+         dict(root=configs.LAYERNORM_ROOT, extras=[(configs.LAYERNORM_MEAN, (R, 1), "f32"),
+                                                  (configs.LAYERNORM_RSTD, (R, 1), "f32")]), [xl, gl, bl], [(R, 1), (R, 1)]),
+        (configs.softmax_causal_dag(0.125, 1024), [((2048, 1024), "f32")], (2048, 1024), "f32", {}, [s], []),
+        (configs.softmax_masked_dag(0.125), [((2, 1024, 1024), "f32"), ((1024, 1024), "u8")], (2, 1024, 1024), "f32",
+         {}, [s.view(2, 1024, 1024), m], []),
+    ]
+    for nodes, ins, shape, dt, kw, tensors, xs in cases:
+        outs = []
+        for layout in ("", "persist=4"):
+            monkeypatch.setenv("PSK_LAYOUT", layout)
+            grp = P.Group(nodes, ins, shape, dt, **kw)
+            out = torch.full(shape, float("nan"), dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device=DEV)
+            ex = [torch.full(sh, float("nan"), device=DEV) for sh in xs]
+            grp.run(tensors, out, extra_outs=ex or None)
+            torch.cuda.synchronize()
+            outs.append([to_np(out)] + [to_np(e) for e in ex])
+        for a, b in zip(*outs):
+            assert_bits(a, b, f"persistent layout, {shape}")
