@@ -383,9 +383,10 @@ def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, pro
     mask = configs.causal_mask_bytes(1024, device=dev)
     masked = P.Group(configs.softmax_masked_dag(0.125), [((8, 16, 1024, 1024), "f32"), ((1024, 1024), "u8")],
                      (8, 16, 1024, 1024), "f32")
-    add("softmax_mask_buffer_f32", R * C * 4 * 2 + 1024 * 1024,
+    add("softmax_mask_buffer_f32", allowed * 4 + R * C * 4 + 1024 * 1024,
         lambda: masked.run([xs4, mask], probs.view(8, 16, 1024, 1024), stream=stream),
-        note="every score read (the mask is data), mask bytes once, probabilities written")
+        note="the scores the mask allows read (vectors it refuses are not loaded), the mask once, "
+             "probabilities written")
     sb = scores.to(torch.bfloat16)
     pb = torch.empty_like(sb)
     soft_bf16 = P.Group(configs.softmax_causal_dag(0.125, 1024), [((R, C), "bf16")], (R, C), "bf16")

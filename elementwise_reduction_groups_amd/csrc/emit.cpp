@@ -395,6 +395,7 @@ struct Emitter {
     {
         const psk_node& nd = an.nodes[i];
         if (nd.op == PSK_OP_CAUSAL_MASK) return "(-__builtin_inff())";
+        if (nd.op == PSK_OP_WHERE) return flit(nd.imm);      // the group's one mask refuses here
         // the member's own expression with every operand at its refused value
         Emitter& self = const_cast<Emitter&>(*this);
         self.use_refused = true;
@@ -630,6 +631,17 @@ struct Emitter {
         return " && (" + any + ") != 0u";
     }
 
+    // lane vector k has an allowed position: its first column under a causal
+    // mask, a nonzero byte of the group's mask under a WHERE mask
+    std::string allowed_vec(int k) const
+    {
+        if (an.mask_period > 0) return "c" + std::to_string(k) + " <= q";
+        InputInfo probe;
+        probe.mask_guarded = true;
+        std::string g = guard(probe, k * pl.vec, "c" + std::to_string(k));   // " && <cond>"
+        return g.empty() ? "true" : g.substr(4);
+    }
+
     // input indices in load order: the unguarded first (the mask among them)
     std::vector<int> load_order() const
     {
@@ -785,7 +797,7 @@ struct Emitter {
     // are computed as usual.
     bool skip_refused() const
     {
-        if (pl.kind != 1 || an.mask_period <= 0) return false;   // not in the tiled kernel
+        if (pl.kind != 1 || pl.persist || (an.mask_period <= 0 && an.where_mask < 0)) return false;
         for (size_t i = 0; i < an.nodes.size(); ++i)
             if (an.uniform[i] && an.nodes[i].op != PSK_OP_CAUSAL_MASK) return true;
         return false;
@@ -810,7 +822,7 @@ struct Emitter {
         for (int k = 0; k < pl.nv; ++k) {
             for (int i : elems)
                 for (int j = 0; j < pl.vec; ++j) o << "    float v" << i << "_" << k * pl.vec + j << ";\n";
-            o << "    if (c" << k << " <= q) {\n";
+            o << "    if (" << allowed_vec(k) << ") {\n";
             for (int i : elems) {
                 divr_open(i);
                 std::vector<int> es;
@@ -838,7 +850,7 @@ struct Emitter {
                 for (int j = 0; j < pl.vec; ++j) es.push_back(k * pl.vec + j);
                 if (!an.uniform[i]) round_elems(i, es, "    ");   // u is rounded already
                 else if (an.rounded(i)) {
-                    o << "    if (c" << k << " <= q) {\n";
+                    o << "    if (" << allowed_vec(k) << ") {\n";
                     round_elems(i, es, "      ");
                     o << "    }\n";
                 }

@@ -430,6 +430,20 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
                 }
                 irrelevant[i] = irr;
             }
+            an.irrelevant = irrelevant;
+            // uniform where the mask refuses: a WHERE (its fill value), and
+            // members whose operands are uniform there or one value per row
+            an.uniform.assign(n, 0);
+            for (int i = 0; i < n; ++i) {
+                const psk_node& nd = an.nodes[i];
+                if (an.is_row[i] || op_is_leaf(nd.op) || op_is_row(nd.op)) continue;
+                if (nd.op == PSK_OP_WHERE) { an.uniform[i] = 1; continue; }
+                int ar = op_arity(nd.op);
+                const int32_t opnd[3] = {nd.a, nd.b, nd.c};
+                bool u = true;
+                for (int k = 0; k < ar; ++k) u = u && (an.is_row[opnd[k]] || an.uniform[opnd[k]]);
+                an.uniform[i] = u;
+            }
             bool any = false;
             for (auto& in : an.inputs) in.mask_guarded = in.used;
             for (int i = 0; i < n; ++i)
@@ -439,9 +453,8 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
                         in.mask_guarded = false;
                 }
             for (auto& in : an.inputs) any = any || in.mask_guarded;
-            if (any) an.where_mask = mask_slot;
-            else
-                for (auto& in : an.inputs) in.mask_guarded = false;
+            an.where_mask = mask_slot;
+            (void)any;
         }
     }
     return PSK_OK;
