@@ -286,11 +286,15 @@ __device__ __forceinline__ float psk_gelu(float x) {
   const float phi = (x > 0.0f) ? fmaf(-0.5f, ec, 1.0f) : 0.5f * ec;
   return x * phi;
 }
-// gelu whose value is only rounded to bf16 (the root of a group whose
-// results are all bf16): the same form with a degree-5 exponent polynomial,
-// fitted here (weighted least squares towards minimax on t in [1/6, 1],
-// w in [0, 10]); its relative error in erfc is below 8e-6, far inside a
-// bf16 half-ulp (2^-9), so the rounded result is the exact one's or its
+// gelu whose value is only rounded to bf16 (a stored result of a group
+// whose results are all bf16, read by no member): the same form with a
+// degree-5 exponent polynomial, fitted here (weighted least squares towards
+// minimax on t in [1/6, 1], w in [0, 10]); its relative error in erfc is
+// below 8e-6.  erfc(w)/2 = t 2^(z - 1) is taken as 2^(z + 63) 2^-64: the
+// shifted argument keeps the hardware 2^x in its normal range and the exact
+// scaling by 2^-64 makes the tiny results subnormal, at the price of one
+// more rounding of the exponent (relative error below 3e-6).  All far inside
+// a bf16 half-ulp (2^-9): the rounded result is the exact one's or its
 // neighbour.
 __device__ __forceinline__ float psk_gelu_b(float x) {
   const float w = fminf(fabsf(x) * 0.70710678118654752440f, 10.0f);
@@ -298,10 +302,9 @@ __device__ __forceinline__ float psk_gelu_b(float x) {
   float p = 0.228792509f;
   p = fmaf(p, t, -0.709197821f); p = fmaf(p, t, 0.474501494f); p = fmaf(p, t, 0.254438582f);
   p = fmaf(p, t, 1.01801471f);   p = fmaf(p, t, -1.26654186f);
-  const float z2 = fmaf(-w, w, p) * 1.44269504088896341f;
-  const float k = __builtin_rintf(z2);
-  const float ec = t * __builtin_ldexpf(__builtin_amdgcn_exp2f(z2 - k), (int)k);
-  const float phi = (x > 0.0f) ? fmaf(-0.5f, ec, 1.0f) : 0.5f * ec;
+  const float z = fmaf(fmaf(-w, w, p), 1.44269504088896341f, 63.0f);
+  const float half_ec = t * (__builtin_amdgcn_exp2f(z) * 0x1p-64f);
+  const float phi = (x > 0.0f) ? 1.0f - half_ec : half_ec;
   return x * phi;
 }
 // a / b for a value b shared by the whole row, given y = 1/b correctly
