@@ -195,12 +195,20 @@ ADAMW_SOURCES = ["elementwise_reduction_groups_amd/csrc/adamw.hip", "elementwise
 
 
 def kernel_source_sha(paths):
+    """SHA-256 of the AdamW kernel's source: adamw.hip whole, and of the
+    shared header only its AdamW section (the structures the kernel reads)."""
     import hashlib
     h = hashlib.sha256()
     root = os.path.dirname(os.path.abspath(__file__))
     for rel in paths:
         with open(os.path.join(root, rel), "rb") as f:
-            h.update(f.read())
+            data = f.read()
+        if rel.endswith(".h"):
+            text = data.decode()
+            a = text.index("// ------------------------------------------------------------------ AdamW")
+            b = text.index("// --------------------------------------------------------------- counters")
+            data = text[a:b].encode()
+        h.update(data)
     return h.hexdigest()
 
 
