@@ -405,7 +405,7 @@ def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, pro
     yw = torch.empty_like(xw)
     wide = P.Group(configs.softmax_dag(0.125), [((8192, 131072), "f32")], (8192, 131072), "f32")
     add("softmax_wide_8192x131072_f32", 2 * xw.numel() * 4, lambda: wide.run([xw], yw, stream=stream),
-        note="tiled kernel: 3 phases read the row, bytes counted once")
+        note="tiled kernel, 512 lanes a row: 3 phases walk it, the leading tiles from registers, the rest re-read; bytes counted once")
     del xw, yw
 
     # layer normalization with its row statistics, bf16 [16384, 4096]: one

@@ -103,8 +103,8 @@ static int layout_value(const char* key, int dflt)
 std::string KernelPlan::key() const
 {
     char b[160];
-    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d c%d w%d p%d", kind, vec, block, lanes, nv,
-                  (int)nt, (int)xcd, (long long)blocks, tiles, (int)tcache, wpe, persist);
+    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d c%d w%d p%d r%d", kind, vec, block, lanes, nv,
+                  (int)nt, (int)xcd, (long long)blocks, tiles, (int)tcache, wpe, persist, rcache);
     return b;
 }
 
@@ -167,8 +167,9 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
         p.blocks = ceil_div(an.rows, p.rows_per_block);
         // Wide rows: past 32 elements per lane the row no longer lives in
         // registers.  The tiled kernel gives a row one workgroup, walks it in
-        // tiles of lanes * tn vectors, and re-reads it in every phase (the
-        // re-reads of a row come from the caches).
+        // tiles of lanes * tn vectors, and every phase walks the row again:
+        // the leading tiles from registers, the rest re-read (from the caches
+        // where they still hold it).
         // Persistent rows: a few workgroups per CU walk the rows, loading the
         // next row while the current one is computed (one row per workgroup
         // of at least 128 lanes).
@@ -181,8 +182,10 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
         if ((int64_t)p.nv * p.vec > 32 || layout_value("tiled", 0)) {
             p.persist = 0;
             p.kind = 3;
-            int Lt = layout_value("lanes", 1024);
-            if (!(Lt >= 64 && Lt <= 1024 && !(Lt & (Lt - 1)))) Lt = 1024;
+            // 512 lanes: two workgroups share a CU, so one loads while the
+            // other reduces (measured faster than 1024 lanes on wide rows)
+            int Lt = layout_value("lanes", 512);
+            if (!(Lt >= 64 && Lt <= 1024 && !(Lt & (Lt - 1)))) Lt = 512;
             int tn = layout_value("tn", 2);
             if (tn < 1 || tn > 8) tn = 2;
             p.lanes = Lt;
@@ -193,6 +196,17 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
             p.blocks = an.rows;
             p.tcache = layout_value("tcache", 1) != 0;
             p.wpe = layout_value("wpe", 0);
+            // the per-row inputs of the leading tiles stay in registers from
+            // the phase that first loads them to the last: about 64 words a
+            // lane, about half of what a wave may hold when two 512-lane
+            // workgroups share a CU, the rest left for the arithmetic
+            int words = 0;
+            for (const InputInfo& in : an.inputs)
+                if (in.used && (in.kind == InKind::General || in.kind == InKind::Full))
+                    words += tn * std::max(1, p.vec * (in.dtype == PSK_BF16 ? 2 : in.dtype == PSK_U8 ? 1 : 4) / 4);
+            int rc = (words > 0 && an.phases > 0) ? 64 / words : 0;
+            rc = layout_value("rc", rc);
+            p.rcache = std::max(0, std::min(rc, p.tiles));
         }
     }
     if (p.xcd) {
@@ -557,53 +571,73 @@ struct Emitter {
         return s;
     }
 
+    // The variables a vector load of input k at element e0 fills before
+    // widening: type, name, zero value, and the loaded expression's type and
+    // element offset (one 4-, 8- or 16-byte load each; V == 1 loads a float).
+    struct RawVar { std::string type, name, zero; int eoff; };
+    std::vector<RawVar> raw_vars(int k, int e0) const
+    {
+        const InputInfo& in = an.inputs[k];
+        const int V = pl.vec;
+        const std::string ks = std::to_string(k), es = std::to_string(e0);
+        if (V == 1) return {{"float", "x" + ks + "_" + es, "0.0f", 0}};
+        if (in.dtype == PSK_U8) {
+            const int nw = std::max(1, V / 4);
+            return {{nw == 1 ? "psk_u32" : nw == 2 ? "psk_u2v" : "psk_u4v", "w" + ks + "_" + es, "{}", 0}};
+        }
+        std::vector<RawVar> r;
+        const int nwords = V * esize(in.dtype) / 4, epw = 4 / esize(in.dtype);
+        int piece = 0;
+        for (int w = 0; w < nwords; w += 4, ++piece) {
+            const bool four = nwords - w >= 4;
+            r.push_back({four ? "psk_u4v" : "psk_u2v", "w" + ks + "_" + es + "_" + std::to_string(piece),
+                         four ? "{0u, 0u, 0u, 0u}" : "{0u, 0u}", w * epw});
+        }
+        return r;
+    }
+
+    // How load_vec fills its raw variables: 0 loads, 1 loads and keeps a copy
+    // in the register cache slot `cache_slot`, 2 takes them from that slot
+    int cache_mode = 0;
+    std::string cache_slot = "t";
+
     // emit loading of a vector of input k at element offset `off` into x{k}_{e0..}
     void load_vec(int k, const std::string& off, int e0, const std::string& cond)
     {
         const InputInfo& in = an.inputs[k];
         const int V = pl.vec;
-        const int bytes = V * esize(in.dtype);
-        std::string base = "in" + std::to_string(k);
         std::string ks = std::to_string(k);
-        std::string p = "(" + base + " + " + off + ")";
+        std::string p = "(in" + ks + " + " + off + ")";
         auto dst = [&](int j) { return "x" + ks + "_" + std::to_string(e0 + j); };
-        if (V == 1) {
-            o << "    float " << dst(0) << " = 0.0f;\n";
-            o << "    if (" << cond << ") " << dst(0) << " = " << widen(in.dtype, ld_fn() + "(" + p + ")") << ";\n";
-            return;
+        std::vector<RawVar> raw = raw_vars(k, e0);
+        for (const RawVar& r : raw) {
+            if (cache_mode == 2) {
+                // the empty asm makes the words a new value, so the compiler
+                // widens them again instead of keeping an earlier phase's
+                // widened copies alive (twice the registers for bf16 and masks)
+                o << "    " << r.type << " " << r.name << " = k" << r.name << "[" << cache_slot << "];\n";
+                o << "    __asm__ volatile(\"\" : \"+v\"(" << r.name << "));\n";
+                continue;
+            }
+            o << "    " << r.type << " " << r.name << " = " << r.zero << ";\n";
+            std::string ld;
+            if (V == 1) ld = widen(in.dtype, ld_fn() + "(" + p + ")");
+            else ld = ld_fn() + "((const " + r.type + "*)(" + p + (r.eoff ? " + " + std::to_string(r.eoff) : "") + "))";
+            o << "    if (" << cond << ") " << r.name << " = " << ld << ";\n";
+            if (cache_mode == 1) o << "    k" << r.name << "[" << cache_slot << "] = " << r.name << ";\n";
         }
+        if (V == 1) return;
         if (in.dtype == PSK_U8) {
-            // V mask bytes: one 4-, 8- or 16-byte load
             const int nw = std::max(1, V / 4);
-            std::string wn = "w" + ks + "_" + std::to_string(e0);
-            const char* vt = nw == 1 ? "psk_u32" : nw == 2 ? "psk_u2v" : "psk_u4v";
-            o << "    " << vt << " " << wn << " = {};\n";
-            o << "    if (" << cond << ") " << wn << " = " << ld_fn() << "((const " << vt << "*)(" << p << "));\n";
             for (int j = 0; j < V; ++j) {
-                std::string w = nw == 1 ? wn : wn + "[" + std::to_string(j / 4) + "]";
+                std::string w = nw == 1 ? raw[0].name : raw[0].name + "[" + std::to_string(j / 4) + "]";
                 o << "    const float " << dst(j) << " = (float)((" << w << " >> " << 8 * (j % 4) << ") & 255u);\n";
             }
             return;
         }
-        int nwords = bytes / 4;
-        // 16-byte pieces (or one 8-byte piece for 4 bf16)
         std::vector<std::string> words;
-        int piece = 0;
-        for (int w = 0; w < nwords; w += 4, ++piece) {
-            int cnt = std::min(4, nwords - w);
-            std::string wn = "w" + ks + "_" + std::to_string(e0) + "_" + std::to_string(piece);
-            int elems_per_word = 4 / esize(in.dtype);
-            int eoff = w * elems_per_word;
-            if (cnt == 4) {
-                o << "    psk_u4v " << wn << " = {0u, 0u, 0u, 0u};\n";
-                o << "    if (" << cond << ") " << wn << " = " << ld_fn() << "((const psk_u4v*)(" << p << " + " << eoff << "));\n";
-                for (int q = 0; q < 4; ++q) words.push_back(wn + "[" + std::to_string(q) + "]");
-            } else {
-                o << "    psk_u2v " << wn << " = {0u, 0u};\n";
-                o << "    if (" << cond << ") " << wn << " = " << ld_fn() << "((const psk_u2v*)(" << p << " + " << eoff << "));\n";
-                for (int q = 0; q < 2; ++q) words.push_back(wn + "[" + std::to_string(q) + "]");
-            }
-        }
+        for (const RawVar& r : raw)
+            for (int q = 0; q < (r.type == "psk_u4v" ? 4 : 2); ++q) words.push_back(r.name + "[" + std::to_string(q) + "]");
         for (int j = 0; j < V; ++j) {
             std::string v;
             if (in.dtype == PSK_F32) v = "__uint_as_float(" + words[j] + ")";
@@ -1229,43 +1263,68 @@ struct Emitter {
         leaves(1);
         members_at(0, 2);
         store_row_extras(0);
+        // what each phase computes and which inputs it loads
+        std::vector<std::vector<char>> need(an.phases + 1);
+        std::vector<std::vector<char>> loads(an.phases + 1, std::vector<char>(an.inputs.size(), 0));
         for (int p = 0; p <= an.phases; ++p) {
-            std::vector<int> reds = p < an.phases ? reductions_of(p) : std::vector<int>();
             std::vector<int> targets;
-            for (int r : reds) targets.push_back(an.nodes[r].a);
-            if (p == an.phases) {
+            if (p < an.phases) {
+                for (int r : reductions_of(p)) targets.push_back(an.nodes[r].a);
+            } else {
                 targets.push_back(an.root);
                 for (const auto& x : an.extras)
                     if (!x.per_row) targets.push_back(x.node);
             }
-            std::vector<char> need = needed_for(targets);
-            // data read again by a later phase stays in the caches: plain
-            // loads before the last phase, nontemporal ones in it
-            cached_loads = p < an.phases && pl.tcache;
-            reduce_declare(reds);
-            o << "    #pragma unroll 1\n";
-            o << "    for (int t = 0; t < " << pl.tiles << "; ++t) {\n";
+            need[p] = needed_for(targets);
+            for (size_t i = 0; i < an.nodes.size(); ++i)
+                if (need[p][i] && an.nodes[i].op == PSK_OP_INPUT) loads[p][an.nodes[i].iparam] = 1;
+        }
+        // Register cache: a per-row input that two or more phases load keeps
+        // the raw words of the leading pl.rcache tiles from the phase that
+        // first loads them; later phases take them from there instead of
+        // memory.  The arithmetic and its order do not change.
+        const int RC = pl.rcache;
+        std::vector<int> first(an.inputs.size(), -1);
+        for (size_t k = 0; k < an.inputs.size(); ++k) {
+            const InputInfo& in = an.inputs[k];
+            if (RC <= 0 || !in.used || !(in.kind == InKind::General || in.kind == InKind::Full)) continue;
+            int n = 0;
+            for (int p = 0; p <= an.phases; ++p)
+                if (loads[p][k]) {
+                    if (first[k] < 0) first[k] = p;
+                    ++n;
+                }
+            if (n < 2) first[k] = -1;
+            if (first[k] < 0) continue;
+            for (int v = 0; v < TN; ++v)
+                for (const RawVar& r : raw_vars((int)k, v * V))
+                    o << "    " << r.type << " k" << r.name << "[" << RC << "];\n";
+        }
+        auto tile_body = [&](int p, bool cached) {
             o << "    const int cb = t * " << tile << ";\n";
             for (int k = 0; k < TN; ++k)
                 o << "    const int c" << k << " = cb + (" << k * L << " + lane) * " << V << ";\n";
             for (int k : load_order()) {
                 const InputInfo& in = an.inputs[k];
                 if (!in.used || in.kind == InKind::Scalar || in.kind == InKind::RowConst) continue;
-                bool used_here = false;
-                for (size_t i = 0; i < an.nodes.size(); ++i)
-                    if (need[i] && an.nodes[i].op == PSK_OP_INPUT && an.nodes[i].iparam == k) used_here = true;
-                if (!used_here) continue;
+                if (!loads[p][k]) continue;
+                cache_mode = (cached && first[k] >= 0) ? (first[k] == p ? 1 : 2) : 0;
+                // what the register cache keeps is not read from memory again
+                const bool keep = cached_loads;
+                if (cache_mode == 1) cached_loads = false;
                 for (int v = 0; v < TN; ++v) {
                     std::string c = "c" + std::to_string(v);
                     std::string cond = "rok";
                     if (ragged) cond += " && " + c + " < " + std::to_string(an.cols);
                     load_vec(k, elem_offset(in, "row", c), v * V, cond + guard(in, v * V, c));
                 }
+                cache_mode = 0;
+                cached_loads = keep;
             }
-            leaves(2, &need);
-            for (int d = 0; d <= p; ++d) members_at(d, 1, &need);
+            leaves(2, &need[p]);
+            for (int d = 0; d <= p; ++d) members_at(d, 1, &need[p]);
             if (p < an.phases) {
-                reduce_accumulate(reds);
+                reduce_accumulate(reductions_of(p));
             } else {
                 for (int v = 0; v < TN; ++v) {
                     std::string c = "c" + std::to_string(v);
@@ -1278,7 +1337,25 @@ struct Emitter {
                     store_vec(off, v * V, cond);
                 }
             }
-            o << "    }\n";
+        };
+        for (int p = 0; p <= an.phases; ++p) {
+            std::vector<int> reds = p < an.phases ? reductions_of(p) : std::vector<int>();
+            // data read again by a later phase stays in the caches: plain
+            // loads before the last phase, nontemporal ones in it
+            cached_loads = p < an.phases && pl.tcache;
+            reduce_declare(reds);
+            if (RC > 0) {
+                o << "    #pragma unroll\n";
+                o << "    for (int t = 0; t < " << RC << "; ++t) {\n";
+                tile_body(p, true);
+                o << "    }\n";
+            }
+            if (RC < pl.tiles) {
+                o << "    #pragma unroll 1\n";
+                o << "    for (int t = " << RC << "; t < " << pl.tiles << "; ++t) {\n";
+                tile_body(p, false);
+                o << "    }\n";
+            }
             if (p < an.phases) {
                 reduce_finish(reds, p);
                 members_at(p + 1, 2);

@@ -91,6 +91,7 @@ struct KernelPlan {
     int nv = 1;              // row kernel: vectors per lane (tiled: per lane per tile)
     int tiles = 0;           // tiled row kernel (kind 3): tiles per row, each phase re-reads the row
     bool tcache = true;      // tiled row kernel: cached (plain) loads before the last phase
+    int rcache = 0;          // tiled row kernel: leading tiles whose per-row inputs stay in registers
     int wpe = 0;             // tiled row kernel: at most this many waves per SIMD (0: no limit)
     int persist = 0;         // row kernel: persistent workgroups per CU (0: one workgroup per row)
     bool nt = true;          // nontemporal loads and stores

@@ -102,3 +102,52 @@ def test_wide_rms_norm_storing_h_in_place():
                             extras=[(configs.RMSNORM_H, rh)])
     np.testing.assert_array_equal(to_np(res), rh)
     assert_bf16_close(to_np(out), ref, "wide rmsnorm")
+
+
+@pytest.mark.parametrize("case", ["softmax_f32", "softmax_bf16_ragged", "masked", "layernorm", "rmsnorm_h"])
+def test_register_cache_changes_no_bit(case, monkeypatch):
+    """Per-row inputs of the leading tiles kept in registers between phases
+    (none, a few, every tile): the same arithmetic in the same order, so the
+    same bits as re-reading them."""
+    if case == "softmax_f32":
+        R, C = 3, 131072
+        ins = [configs.softmax_scores(R, C, device=DEV, seed=31)]
+        args = (configs.softmax_dag(0.125), [((R, C), "f32")], (R, C), "f32")
+        kw, xs = {}, []
+    elif case == "softmax_bf16_ragged":
+        R, C = 4, 70001
+        ins = [configs.softmax_scores(R, C, device=DEV, seed=32).to(torch.bfloat16)]
+        args = (configs.softmax_causal_dag(0.125, 50000), [((R, C), "bf16")], (R, C), "bf16")
+        kw, xs = {}, []
+    elif case == "masked":
+        R, C = 4, 70000
+        ins = [configs.softmax_scores(R, C, device=DEV, seed=33),
+               configs.random_mask(R, C, 0.4, empty_rows=[1], device=DEV, seed=34)]
+        args = (configs.softmax_masked_dag(0.125), [((R, C), "f32"), ((R, C), "u8")], (R, C), "f32")
+        kw, xs = {}, []
+    elif case == "layernorm":
+        R, C = 4, 50000
+        ins = list(configs.layernorm_inputs(R, C, device=DEV, seed=35))
+        args = (configs.layernorm_dag(EPS), [((R, C), "bf16"), ((C,), "bf16"), ((C,), "bf16")], (R, C), "bf16")
+        kw = dict(root=configs.LAYERNORM_ROOT,
+                  extras=[(configs.LAYERNORM_MEAN, (R, 1), "f32"), (configs.LAYERNORM_RSTD, (R, 1), "f32")])
+        xs = [((R, 1), torch.float32), ((R, 1), torch.float32)]
+    else:
+        R, C = 3, 45000
+        ins = list(configs.rmsnorm_inputs(R, C, device=DEV, seed=36))
+        args = (configs.rmsnorm_gelu_dag(EPS), [((R, C), "bf16"), ((R, C), "bf16"), ((C,), "bf16")], (R, C), "bf16")
+        kw = dict(extras=[(configs.RMSNORM_H, (R, C), "bf16")])
+        xs = [((R, C), torch.bfloat16)]
+    runs = []
+    for layout in ("rc=0", "rc=1", "rc=3", ""):
+        monkeypatch.setenv("PSK_LAYOUT", layout)
+        g = P.Group(*args, **kw)
+        assert g.info.kind == 3
+        out = torch.full((R, C), float("nan"), dtype=ins[0].dtype, device=DEV)
+        ex = [torch.full(sh, float("nan"), dtype=dt, device=DEV) for sh, dt in xs]
+        g.run(ins, out, extra_outs=ex or None)
+        torch.cuda.synchronize()
+        runs.append([to_np(out)] + [to_np(e) for e in ex])
+    for other in runs[1:]:
+        for a, b in zip(runs[0], other):
+            np.testing.assert_array_equal(a.view(np.uint8), b.view(np.uint8), f"register cache, {case}")
