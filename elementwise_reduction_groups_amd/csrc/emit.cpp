@@ -157,7 +157,7 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
         while (L < want && L < 1024) L <<= 1;
         if (L > 16 && L < 64) L = 64;
         int Lo = layout_value("lanes", L);
-        if (Lo == 16 || (Lo >= 64 && Lo <= 1024 && !(Lo & (Lo - 1)))) L = Lo;
+        if (Lo == 16 || Lo == 32 || (Lo >= 64 && Lo <= 1024 && !(Lo & (Lo - 1)))) L = Lo;
         p.lanes = L;
         p.nv = (int)ceil_div(an.cols, (int64_t)L * p.vec);
         if (L >= 128) block = layout_value("block", 128);
@@ -179,7 +179,7 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
             p.blocks = std::min<int64_t>(an.rows, (int64_t)256 * persist);
             p.xcd = false;
         }
-        if ((int64_t)p.nv * p.vec > 32 || layout_value("tiled", 0)) {
+        if ((int64_t)p.nv * p.vec > layout_value("epmax", 32) || layout_value("tiled", 0)) {
             p.persist = 0;
             p.kind = 3;
             // 512 lanes: two workgroups share a CU, so one loads while the
@@ -350,6 +350,20 @@ __device__ __forceinline__ float psk_max16(float x) {
   x = psk_max(x, PSK_DPP(x, 0xB1)); x = psk_max(x, PSK_DPP(x, 0x4E));
   x = psk_max(x, PSK_DPP(x, 0x141)); x = psk_max(x, PSK_DPP(x, 0x140)); return x;
 }
+// 32 lanes: the 16-lane results of the two halves combined, the lower
+// half's first (ds_swizzle in bit mode, xor 16, exchanges them within each
+// 32-lane group); `upper`: the lane is in the upper half
+#define PSK_SWZ16(x) __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, (x)), 0x401F))
+__device__ __forceinline__ float psk_sum32(float x, bool upper) {
+  x = psk_sum16(x);
+  const float y = PSK_SWZ16(x);
+  return upper ? y + x : x + y;
+}
+__device__ __forceinline__ float psk_max32(float x, bool upper) {
+  x = psk_max16(x);
+  const float y = PSK_SWZ16(x);
+  return upper ? psk_max(y, x) : psk_max(x, y);
+}
 // whole wave: the four row results combined in lane order 0, 16, 32, 48
 __device__ __forceinline__ float psk_sum64(float x) {
   x = psk_sum16(x);
@@ -370,8 +384,22 @@ struct Emitter {
     int period = 0;         // causal mask period (0: none)
     bool ragged = false;    // some lane columns fall past the row end
 
+    // node -> some f32 stored value depends on it (through any members)
+    std::vector<char> f32_reach;
+
     Emitter(const Analysis& a, const KernelPlan& p) : an(a), pl(p)
     {
+        const int n = (int)an.nodes.size();
+        f32_reach.assign(n, 0);
+        for (int i = n - 1; i >= 0; --i) {
+            const bool f32_store = (i == an.root && an.out_dtype != PSK_BF16) ||
+                                   (an.stored[i] > 0 && an.extras[an.stored[i] - 1].dtype != PSK_BF16);
+            if (f32_store) f32_reach[i] = 1;
+            if (!f32_reach[i]) continue;
+            const psk_node& nd = an.nodes[i];
+            const int32_t opnd[3] = {nd.a, nd.b, nd.c};
+            for (int k = 0; k < op_arity(nd.op); ++k) f32_reach[opnd[k]] = 1;
+        }
         NE = (pl.kind == 1 || pl.kind == 3 ? pl.nv : 1) * pl.vec;   // tree: elements per thread
         big = an.numel >= (int64_t(1) << 31) - 4096;
         for (auto& nd : an.nodes)
@@ -447,37 +475,31 @@ struct Emitter {
         o << "    const bool yok" << i << " = fabsf(r" << i << ") >= 0x1p-40f && fabsf(r" << i << ") <= 0x1p40f;\n";
     }
 
-    // element division by a row value: Markstein's correction
-    bool divr_node(int i) const
+    // element divided by a row value (a reduction's result, or a scalar)
+    bool row_div(int i) const
     {
         const psk_node& nd = an.nodes[i];
-        return !use_refused && divr_ok && !bf16_results() && nd.op == PSK_OP_DIV && !an.is_row[i] && an.is_row[nd.b];
+        return !use_refused && divr_ok && nd.op == PSK_OP_DIV && !an.is_row[i] && an.is_row[nd.b];
     }
 
-    // every value the group stores is bf16: interior f32 values only reach
-    // memory through a rounding to 8 significant bits
-    bool bf16_results() const
-    {
-        if (an.out_dtype != PSK_BF16) return false;
-        for (const auto& x : an.extras)
-            if (x.dtype != PSK_BF16) return false;
-        return true;
-    }
+    // the other element divisions by a row value: Markstein's correction
+    bool divr_node(int i) const { return row_div(i) && !recip_node(i); }
 
-    // node i's value is rounded to bf16 and read by no member
+    // node i's value is stored only as bf16 and read by no member: it
+    // reaches memory only through a rounding to 8 significant bits
     bool bf16_terminal(int i) const
     {
-        if (!bf16_results() || an.n_readers[i] != 0) return false;
+        if (f32_reach[i] || an.n_readers[i] != 0) return false;
         return i == an.root || an.stored[i] > 0;
     }
 
-    // element / row value in a bf16-results group: the row's reciprocal
-    // (correctly rounded) times the element, within 1.5 f32 ulps of the
-    // quotient
+    // element / row statistic (a value computed from a reduction) that only
+    // bf16 results depend on: the row's reciprocal (correctly rounded) times
+    // the element, within 1.5 f32 ulps of the quotient.  A division by a
+    // scalar input stays correctly rounded.
     bool recip_node(int i) const
     {
-        const psk_node& nd = an.nodes[i];
-        return !use_refused && divr_ok && bf16_results() && nd.op == PSK_OP_DIV && !an.is_row[i] && an.is_row[nd.b];
+        return row_div(i) && !f32_reach[i] && an.depth[an.nodes[i].b] > 0;
     }
 
     // elements of member i (given as element indices) written through
@@ -1164,6 +1186,8 @@ struct Emitter {
             bool mx = an.nodes[i].op == PSK_OP_ROW_MAX;
             if (pl.lanes == 16)
                 o << "    p" << i << " = " << (mx ? "psk_max16" : "psk_sum16") << "(p" << i << ");\n";
+            else if (pl.lanes == 32)
+                o << "    p" << i << " = " << (mx ? "psk_max32" : "psk_sum32") << "(p" << i << ", (lane & 16) != 0);\n";
             else
                 o << "    p" << i << " = " << (mx ? "psk_max64" : "psk_sum64") << "(p" << i << ");\n";
         }

@@ -399,8 +399,8 @@ def test_wide_rows_take_the_tiled_kernel(lib, tmp_path):
         g = P.psk_group_create(d)
         info = P.psk_group_get_info(g)
         P.psk_group_destroy(g)
-        assert info.kind == 3 and info.lanes_per_row == 1024 and info.rows_per_block == 1
-        assert info.tiles == -(-cols // (1024 * 2 * info.vec))
+        assert info.kind == 3 and info.lanes_per_row == 512 and info.rows_per_block == 1
+        assert info.tiles == -(-cols // (512 * 2 * info.vec))
         asm, notes = _isa(P.psk_group_code_object(d), tmp_path, f"wide{cols}")
         assert re.search(r"\.private_segment_fixed_size:\s+0\b", notes)    # no spills
         assert not re.search(r"v_pk_(fma|mul|add)_f32", asm)
@@ -427,7 +427,21 @@ def test_precision_follows_what_is_stored(lib):
     ln = P.psk_group_source(P.GroupDesc(C.layernorm_dag(eps), [((R, N), "bf16"), ((N,), "bf16"), ((N,), "bf16")],
                                         (R, N), "bf16", root=C.LAYERNORM_ROOT,
                                         extras=[(C.LAYERNORM_MEAN, (R, 1), "f32"), (C.LAYERNORM_RSTD, (R, 1), "f32")]))
-    assert "psk_divr(" in ln[ln.index('extern "C"'):]
+    # f32 statistics that the normalized value does not reach: the division
+    # feeding only the bf16 result takes the reciprocal form
+    body = ln[ln.index('extern "C"'):]
+    assert "psk_divr(" not in body and "* y9)" in body
+    # ... but an f32 extra that depends on it keeps the correctly rounded one
+    ln32 = P.psk_group_source(P.GroupDesc(C.layernorm_dag(eps), [((R, N), "bf16"), ((N,), "bf16"), ((N,), "bf16")],
+                                          (R, N), "bf16", root=C.LAYERNORM_ROOT, extras=[(11, (R, N), "f32"), (C.LAYERNORM_RSTD, (R, 1), "f32")]))
+    assert "psk_divr(" in ln32[ln32.index('extern "C"'):]
+    # h = x + r stored in f32 comes before the division and the gelu: both
+    # keep their bf16-result forms
+    rmsh = P.psk_group_source(P.GroupDesc(C.rmsnorm_gelu_dag(eps), [((R, N), "bf16"), ((R, N), "bf16"),
+                                                                      ((N,), "bf16")], (R, N), "bf16",
+                                          extras=[(C.RMSNORM_H, (R, N), "f32")]))
+    body = rmsh[rmsh.index('extern "C"'):]
+    assert "psk_gelu_b(" in body and "psk_divr(" not in body and "* y8)" in body
     # a gelu that other members read is not the bf16 form
     tree = P.psk_group_source(P.GroupDesc(C.tree_mixed_dag(), [((1,), "f32"), ((1,), "bf16"), ((), "f32")], (1,),
                                           "bf16", flags=P.PSK_GROUP_TREE))
