@@ -309,8 +309,13 @@ def profile_others(P, configs, torch, dev, stream, hp, state):
     xw = configs.softmax_scores(8192, 131072, device=dev)
     yw = torch.empty_like(xw)
     wide = P.Group(configs.softmax_dag(0.125), [((8192, 131072), "f32")], (8192, 131072), "f32")
+    rms_h = P.Group(configs.rmsnorm_gelu_dag(configs.f32(1e-5)),
+                    [((16384, 4096), "bf16"), ((16384, 4096), "bf16"), ((4096,), "bf16")], (16384, 4096), "bf16",
+                    extras=[(configs.RMSNORM_H, (16384, 4096), "bf16")])
+    rh = r.clone()
     torch.cuda.synchronize()
     for _ in range(2):
+        rms_h.run([x, rh, g], y, stream=stream, extra_outs=[rh])
         sgd.run_tree(sgd_tree, [0, 1, -1], 0, [None, None, lr], stream=stream)
         ln.run([xl, gl, bl], yl, stream=stream, extra_outs=[ml, rl])
         adamw_g.run_tree(*adamw_args, stream=stream)
