@@ -220,6 +220,13 @@ def test_tree_plan(lib):
     shapes = [s for _, s in configs.llama_leaves()]
     off, *_ = P.psk_tree_plan([int(np.prod(s)) for s in shapes])
     assert len(shapes) == 145 and off[-1] == 887685120
+    # a leaf past 2^31 elements: 64-bit starts, consecutive whole chunks
+    big = (1 << 31) + 100
+    off, cl, cs, cc = P.psk_tree_plan([5, big, 3])
+    assert off.tolist() == [0, 5, 5 + big, 8 + big]
+    sel = cl == 1
+    assert cs[sel][0] == 0 and np.all(np.diff(cs[sel]) == P.PSK_TREE_CHUNK)
+    assert cs[sel][-1] + cc[sel][-1] == big and int(cc[sel].sum()) == big and cs[sel][-1] >= (1 << 31)
     with pytest.raises(P.PskError) as ei:
         P.psk_tree_plan([4, -1])
     assert ei.value.status == P.PSK_E_SHAPE
