@@ -103,8 +103,8 @@ static int layout_value(const char* key, int dflt)
 std::string KernelPlan::key() const
 {
     char b[160];
-    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d c%d w%d p%d r%d", kind, vec, block, lanes, nv,
-                  (int)nt, (int)xcd, (long long)blocks, tiles, (int)tcache, wpe, persist, rcache);
+    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d c%d w%d m%d p%d r%d s%d", kind, vec, block,
+                  lanes, nv, (int)nt, (int)xcd, (long long)blocks, tiles, (int)tcache, wpe, wmin, persist, rcache, lcache);
     return b;
 }
 
@@ -196,6 +196,10 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
             p.blocks = an.rows;
             p.tcache = layout_value("tcache", 1) != 0;
             p.wpe = layout_value("wpe", 0);
+            // registers for two workgroups a CU: at least 2 * Lt / 256 waves
+            // a SIMD (at most 128 registers a lane at 512 lanes)
+            p.wmin = layout_value("wmin", std::min(8, 2 * Lt / 256));
+            if (p.wmin < 0 || p.wmin > 8) p.wmin = 0;
             // the per-row inputs of the leading tiles stay in registers from
             // the phase that first loads them to the last: about 64 words a
             // lane, about half of what a wave may hold when two 512-lane
@@ -207,6 +211,12 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
             int rc = (words > 0 && an.phases > 0) ? 64 / words : 0;
             rc = layout_value("rc", rc);
             p.rcache = std::max(0, std::min(rc, p.tiles));
+            // the next tiles' words in LDS: 64 KiB a workgroup, so two
+            // workgroups (and their reduction scratch) share a CU's 160 KiB
+            int lc = (words > 0 && an.phases > 0) ? (64 << 10) / (words * 4 * Lt) : 0;
+            lc = layout_value("lc", lc);
+            if ((int64_t)lc * words * 4 * Lt > (96 << 10)) lc = (96 << 10) / (words * 4 * Lt);
+            p.lcache = std::max(0, std::min(lc, p.tiles - p.rcache));
         }
     }
     if (p.xcd) {
@@ -619,7 +629,9 @@ struct Emitter {
     }
 
     // How load_vec fills its raw variables: 0 loads, 1 loads and keeps a copy
-    // in the register cache slot `cache_slot`, 2 takes them from that slot
+    // in the register cache slot `cache_slot`, 2 takes them from that slot;
+    // 3 loads and keeps a copy in this lane's LDS cache slot, 4 takes them
+    // from there (each lane reads back only what it wrote itself)
     int cache_mode = 0;
     std::string cache_slot = "t";
 
@@ -633,6 +645,11 @@ struct Emitter {
         auto dst = [&](int j) { return "x" + ks + "_" + std::to_string(e0 + j); };
         std::vector<RawVar> raw = raw_vars(k, e0);
         for (const RawVar& r : raw) {
+            const std::string lds = "l" + r.name + "[" + cache_slot + "][lane]";
+            if (cache_mode == 4) {
+                o << "    " << r.type << " " << r.name << " = " << lds << ";\n";
+                continue;
+            }
             if (cache_mode == 2) {
                 // the empty asm makes the words a new value, so the compiler
                 // widens them again instead of keeping an earlier phase's
@@ -647,6 +664,7 @@ struct Emitter {
             else ld = ld_fn() + "((const " + r.type + "*)(" + p + (r.eoff ? " + " + std::to_string(r.eoff) : "") + "))";
             o << "    if (" << cond << ") " << r.name << " = " << ld << ";\n";
             if (cache_mode == 1) o << "    k" << r.name << "[" << cache_slot << "] = " << r.name << ";\n";
+            if (cache_mode == 3) o << "    " << lds << " = " << r.name << ";\n";
         }
         if (V == 1) return;
         if (in.dtype == PSK_U8) {
@@ -831,7 +849,11 @@ struct Emitter {
     void signature(const std::string& name)
     {
         o << "extern \"C\" __global__ void __launch_bounds__(" << pl.block << ") ";
-        if (pl.wpe > 0) o << "__attribute__((amdgpu_waves_per_eu(1, " << pl.wpe << "))) ";
+        if (pl.wmin > 0)
+            o << "__attribute__((amdgpu_waves_per_eu(" << pl.wmin << ", " << std::max(pl.wmin, pl.wpe > 0 ? pl.wpe : 8)
+              << "))) ";
+        else if (pl.wpe > 0)
+            o << "__attribute__((amdgpu_waves_per_eu(1, " << pl.wpe << "))) ";
         o << name << "(";
         // no __restrict__: the output may be the same buffer as an input
         // (in place); every load of an element precedes its store
@@ -1307,11 +1329,11 @@ struct Emitter {
         // the raw words of the leading pl.rcache tiles from the phase that
         // first loads them; later phases take them from there instead of
         // memory.  The arithmetic and its order do not change.
-        const int RC = pl.rcache;
+        const int RC = pl.rcache, LC = pl.lcache;
         std::vector<int> first(an.inputs.size(), -1);
         for (size_t k = 0; k < an.inputs.size(); ++k) {
             const InputInfo& in = an.inputs[k];
-            if (RC <= 0 || !in.used || !(in.kind == InKind::General || in.kind == InKind::Full)) continue;
+            if (RC + LC <= 0 || !in.used || !(in.kind == InKind::General || in.kind == InKind::Full)) continue;
             int n = 0;
             for (int p = 0; p <= an.phases; ++p)
                 if (loads[p][k]) {
@@ -1321,10 +1343,13 @@ struct Emitter {
             if (n < 2) first[k] = -1;
             if (first[k] < 0) continue;
             for (int v = 0; v < TN; ++v)
-                for (const RawVar& r : raw_vars((int)k, v * V))
-                    o << "    " << r.type << " k" << r.name << "[" << RC << "];\n";
+                for (const RawVar& r : raw_vars((int)k, v * V)) {
+                    if (RC > 0) o << "    " << r.type << " k" << r.name << "[" << RC << "];\n";
+                    if (LC > 0) o << "    __shared__ " << r.type << " l" << r.name << "[" << LC << "][" << L << "];\n";
+                }
         }
-        auto tile_body = [&](int p, bool cached) {
+        // cached: 0 memory, 1 registers, 2 LDS
+        auto tile_body = [&](int p, int cached) {
             o << "    const int cb = t * " << tile << ";\n";
             for (int k = 0; k < TN; ++k)
                 o << "    const int c" << k << " = cb + (" << k * L << " + lane) * " << V << ";\n";
@@ -1332,10 +1357,12 @@ struct Emitter {
                 const InputInfo& in = an.inputs[k];
                 if (!in.used || in.kind == InKind::Scalar || in.kind == InKind::RowConst) continue;
                 if (!loads[p][k]) continue;
-                cache_mode = (cached && first[k] >= 0) ? (first[k] == p ? 1 : 2) : 0;
-                // what the register cache keeps is not read from memory again
+                cache_mode = 0;
+                if (cached && first[k] >= 0) cache_mode = (first[k] == p ? 1 : 2) + (cached == 2 ? 2 : 0);
+                cache_slot = cached == 2 ? "t - " + std::to_string(RC) : "t";
+                // what a cache keeps is not read from memory again
                 const bool keep = cached_loads;
-                if (cache_mode == 1) cached_loads = false;
+                if (cache_mode == 1 || cache_mode == 3) cached_loads = false;
                 for (int v = 0; v < TN; ++v) {
                     std::string c = "c" + std::to_string(v);
                     std::string cond = "rok";
@@ -1371,13 +1398,19 @@ struct Emitter {
             if (RC > 0) {
                 o << "    #pragma unroll\n";
                 o << "    for (int t = 0; t < " << RC << "; ++t) {\n";
-                tile_body(p, true);
+                tile_body(p, 1);
                 o << "    }\n";
             }
-            if (RC < pl.tiles) {
+            if (LC > 0) {
                 o << "    #pragma unroll 1\n";
-                o << "    for (int t = " << RC << "; t < " << pl.tiles << "; ++t) {\n";
-                tile_body(p, false);
+                o << "    for (int t = " << RC << "; t < " << RC + LC << "; ++t) {\n";
+                tile_body(p, 2);
+                o << "    }\n";
+            }
+            if (RC + LC < pl.tiles) {
+                o << "    #pragma unroll 1\n";
+                o << "    for (int t = " << RC + LC << "; t < " << pl.tiles << "; ++t) {\n";
+                tile_body(p, 0);
                 o << "    }\n";
             }
             if (p < an.phases) {

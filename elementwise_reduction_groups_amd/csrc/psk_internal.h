@@ -92,7 +92,9 @@ struct KernelPlan {
     int tiles = 0;           // tiled row kernel (kind 3): tiles per row, each phase re-reads the row
     bool tcache = true;      // tiled row kernel: cached (plain) loads before the last phase
     int rcache = 0;          // tiled row kernel: leading tiles whose per-row inputs stay in registers
+    int lcache = 0;          // tiled row kernel: the tiles after those whose per-row inputs stay in LDS
     int wpe = 0;             // tiled row kernel: at most this many waves per SIMD (0: no limit)
+    int wmin = 0;            // tiled row kernel: registers for at least this many waves per SIMD (0: any)
     int persist = 0;         // row kernel: persistent workgroups per CU (0: one workgroup per row)
     bool nt = true;          // nontemporal loads and stores
     bool xcd = true;         // each XCD takes a contiguous eighth of the blocks

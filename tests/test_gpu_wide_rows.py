@@ -106,9 +106,9 @@ def test_wide_rms_norm_storing_h_in_place():
 
 @pytest.mark.parametrize("case", ["softmax_f32", "softmax_bf16_ragged", "masked", "layernorm", "rmsnorm_h"])
 def test_register_cache_changes_no_bit(case, monkeypatch):
-    """Per-row inputs of the leading tiles kept in registers between phases
-    (none, a few, every tile): the same arithmetic in the same order, so the
-    same bits as re-reading them."""
+    """Per-row inputs of the leading tiles kept in registers and of the next
+    ones in LDS between phases (none, a few, every tile): the same
+    arithmetic in the same order, so the same bits as re-reading them."""
     if case == "softmax_f32":
         R, C = 3, 131072
         ins = [configs.softmax_scores(R, C, device=DEV, seed=31)]
@@ -139,7 +139,7 @@ def test_register_cache_changes_no_bit(case, monkeypatch):
         kw = dict(extras=[(configs.RMSNORM_H, (R, C), "bf16")])
         xs = [((R, C), torch.bfloat16)]
     runs = []
-    for layout in ("rc=0", "rc=1", "rc=3", ""):
+    for layout in ("rc=0,lc=0", "rc=1,lc=0", "rc=0,lc=2", "rc=3,lc=1", "rc=1,lc=64", ""):
         monkeypatch.setenv("PSK_LAYOUT", layout)
         g = P.Group(*args, **kw)
         assert g.info.kind == 3
