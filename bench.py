@@ -309,6 +309,7 @@ def profile_others(P, configs, torch, dev, stream, hp, state):
     xw = configs.softmax_scores(8192, 131072, device=dev)
     yw = torch.empty_like(xw)
     wide = P.Group(configs.softmax_dag(0.125), [((8192, 131072), "f32")], (8192, 131072), "f32")
+    wide_online = P.Group(configs.softmax_dag(0.125), [((8192, 131072), "f32")], (8192, 131072), "f32", online=True)
     rms_h = P.Group(configs.rmsnorm_gelu_dag(configs.f32(1e-5)),
                     [((16384, 4096), "bf16"), ((16384, 4096), "bf16"), ((4096,), "bf16")], (16384, 4096), "bf16",
                     extras=[(configs.RMSNORM_H, (16384, 4096), "bf16")])
@@ -322,6 +323,7 @@ def profile_others(P, configs, torch, dev, stream, hp, state):
         masked.run([xs.view(8, 16, 1024, 1024), mask], ys.view(8, 16, 1024, 1024), stream=stream)
         soft_bf16.run([sb], pb, stream=stream)
         wide.run([xw], yw, stream=stream)
+        wide_online.run([xw], yw, stream=stream)
         tiny_tree.adamw_step(*hp, stream=stream)
         rms.run([x, r, g], y, stream=stream)
         chain.run([A, B, Cc], Z, stream=stream)
@@ -411,6 +413,10 @@ def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, pro
     wide = P.Group(configs.softmax_dag(0.125), [((8192, 131072), "f32")], (8192, 131072), "f32")
     add("softmax_wide_8192x131072_f32", 2 * xw.numel() * 4, lambda: wide.run([xw], yw, stream=stream),
         note="tiled kernel, 512 lanes a row: 3 phases walk it, the leading tiles from registers, the rest re-read; bytes counted once")
+    wide_online = P.Group(configs.softmax_dag(0.125), [((8192, 131072), "f32")], (8192, 131072), "f32", online=True)
+    add("softmax_wide_8192x131072_f32_online", 2 * xw.numel() * 4, lambda: wide_online.run([xw], yw, stream=stream),
+        note="PSK_GROUP_ONLINE: the sum taken in the maximum's pass (2 phases); its rounding differs from the exact "
+             "sum (declared differs, within the f32 tolerance)")
     del xw, yw
 
     # layer normalization with its row statistics, bf16 [16384, 4096]: one

@@ -25,6 +25,7 @@ for _i, _n in enumerate(STATUS_NAMES):
 
 PSK_F32, PSK_BF16, PSK_U8 = 0, 1, 2
 PSK_GROUP_TREE = 1
+PSK_GROUP_ONLINE = 2
 PSK_PARTITION_ROWS = 1
 PSK_MAX_RANK = 4
 PSK_MAX_SLOTS = 8
@@ -444,9 +445,11 @@ def _stream_handle(stream) -> int:
 class Group:
     """A compiled fusion group, run on torch tensors."""
 
-    def __init__(self, nodes, inputs, out_shape, out_dtype, root=None, tree=False, extras=()):
-        self.desc = GroupDesc(nodes, inputs, out_shape, out_dtype, root=root, flags=PSK_GROUP_TREE if tree else 0,
-                              extras=extras)
+    def __init__(self, nodes, inputs, out_shape, out_dtype, root=None, tree=False, extras=(), online=False):
+        """online: take a row sum of exp(y - row_max(y)) in the maximum's pass
+        (PSK_GROUP_ONLINE)."""
+        flags = (PSK_GROUP_TREE if tree else 0) | (PSK_GROUP_ONLINE if online else 0)
+        self.desc = GroupDesc(nodes, inputs, out_shape, out_dtype, root=root, flags=flags, extras=extras)
         self.n_extra = len(extras)
         self.handle = psk_group_create(self.desc)
         self.out_shape = tuple(out_shape)

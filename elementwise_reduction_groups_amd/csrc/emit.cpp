@@ -30,6 +30,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <sstream>
 
 #include "psk_internal.h"
@@ -173,7 +174,9 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
         // Persistent rows: a few workgroups per CU walk the rows, loading the
         // next row while the current one is computed (one row per workgroup
         // of at least 128 lanes).
-        const int persist = layout_value("persist", 0);
+        bool online = false;
+        for (int m : an.online_max) online = online || m >= 0;
+        const int persist = online ? 0 : layout_value("persist", 0);
         if (persist > 0 && p.rows_per_block == 1) {
             p.persist = persist;
             p.blocks = std::min<int64_t>(an.rows, (int64_t)256 * persist);
@@ -1188,6 +1191,11 @@ struct Emitter {
         for (int i : reds) {
             const psk_node& nd = an.nodes[i];
             bool mx = nd.op == PSK_OP_ROW_MAX;
+            if (an.online_max[i] >= 0) continue;      // taken with its maximum
+            if (an.online_sum[i] >= 0) {
+                online_accumulate(i, an.online_sum[i], indent);
+                continue;
+            }
             for (int e = 0; e < NE; ++e) {
                 std::string v = val(nd.a, e);
                 std::string acc = mx ? "psk_max(p" + std::to_string(i) + ", " + v + ")"
@@ -1200,11 +1208,38 @@ struct Emitter {
         }
     }
 
+    // Online normalizer: this lane's elements of y (the maximum's operand)
+    // update the running maximum p<mx> once for the group of elements and
+    // the sum p<sm> of exp(y - running maximum), rescaled by
+    // exp(old - new) when the maximum grows.  While the maximum is still
+    // -inf every y so far is -inf, and the exponentials are taken against 0
+    // (giving exp(-inf) = 0 rather than exp(NaN)).
+    void online_accumulate(int mx, int sm, const char* indent)
+    {
+        const int y = an.nodes[mx].a;
+        const std::string P = "p" + std::to_string(mx), S = "p" + std::to_string(sm);
+        o << indent << "{\n" << indent << "  float tm = (-__builtin_inff());\n";
+        for (int e = 0; e < NE; ++e) {
+            std::string acc = "tm = psk_max(tm, " + val(y, e) + ");";
+            if (ragged) o << indent << "  if (" << col(e) << " < " << an.cols << ") " << acc << "\n";
+            else o << indent << "  " << acc << "\n";
+        }
+        o << indent << "  if (tm > " << P << ") { " << S << " = " << S << " * expf(" << P << " - tm); " << P
+          << " = tm; }\n";
+        o << indent << "  const float mref = " << P << " == (-__builtin_inff()) ? 0.0f : " << P << ";\n";
+        for (int e = 0; e < NE; ++e) {
+            std::string acc = S + " = (" + S + " + expf(" + val(y, e) + " - mref));";
+            if (ragged) o << indent << "  if (" << col(e) << " < " << an.cols << ") " << acc << "\n";
+            else o << indent << "  " << acc << "\n";
+        }
+        o << indent << "}\n";
+    }
+
     // lanes of a wave (DPP), then waves (LDS), then the row values
     void reduce_finish(const std::vector<int>& reds, int p)
     {
         const int W = pl.lanes / 64;
-        for (int i : reds) {
+        auto lane_reduce = [&](int i) {
             bool mx = an.nodes[i].op == PSK_OP_ROW_MAX;
             if (pl.lanes == 16)
                 o << "    p" << i << " = " << (mx ? "psk_max16" : "psk_sum16") << "(p" << i << ");\n";
@@ -1212,6 +1247,20 @@ struct Emitter {
                 o << "    p" << i << " = " << (mx ? "psk_max32" : "psk_sum32") << "(p" << i << ", (lane & 16) != 0);\n";
             else
                 o << "    p" << i << " = " << (mx ? "psk_max64" : "psk_sum64") << "(p" << i << ");\n";
+        };
+        for (int i : reds) {
+            if (an.online_max[i] >= 0) continue;
+            if (an.online_sum[i] >= 0) o << "    const float q" << i << " = p" << i << ";\n";
+            lane_reduce(i);
+        }
+        // an online sum: each lane's part rescaled to the maximum of its
+        // wave (or row part) before the lanes add up
+        for (int i : reds) {
+            const int m = an.online_max[i];
+            if (m < 0) continue;
+            o << "    p" << i << " = (q" << m << " == p" << m << ") ? p" << i << " : p" << i << " * expf(q" << m
+              << " - p" << m << ");\n";
+            lane_reduce(i);
         }
         if (W > 1) {
             const int NR = (int)reds.size();
@@ -1226,13 +1275,30 @@ struct Emitter {
                 o << "      " << arr << "[" << base << "(slot * " << W << " + (lane >> 6)) * " << NR << " + " << r
                   << "] = p" << reds[r] << ";\n";
             o << "    }\n    __syncthreads();\n";
+            auto slot_of = [&](int w, int r) {
+                return arr + "[" + base + "(slot * " + std::to_string(W) + " + " + std::to_string(w) + ") * " +
+                       std::to_string(NR) + " + " + std::to_string(r) + "]";
+            };
             for (int r = 0; r < NR; ++r) {
                 int i = reds[r];
                 bool mx = an.nodes[i].op == PSK_OP_ROW_MAX;
-                o << "    p" << i << " = " << arr << "[" << base << "(slot * " << W << ") * " << NR << " + " << r << "];\n";
+                const int m = an.online_max[i];
+                if (m >= 0) {
+                    // the waves' sums, each rescaled from its wave's maximum to
+                    // the row's (already combined: the maximum precedes)
+                    const int rm = (int)(std::find(reds.begin(), reds.end(), m) - reds.begin());
+                    for (int w = 0; w < W; ++w) {
+                        std::string mw = slot_of(w, rm), sw = slot_of(w, r);
+                        std::string t = "((" + mw + " == p" + std::to_string(m) + ") ? " + sw + " : " + sw +
+                                        " * expf(" + mw + " - p" + std::to_string(m) + "))";
+                        if (w == 0) o << "    p" << i << " = " << t << ";\n";
+                        else o << "    p" << i << " = p" << i << " + " << t << ";\n";
+                    }
+                    continue;
+                }
+                o << "    p" << i << " = " << slot_of(0, r) << ";\n";
                 for (int w = 1; w < W; ++w) {
-                    std::string el = arr + "[" + base + "(slot * " + std::to_string(W) + " + " + std::to_string(w) +
-                                     ") * " + std::to_string(NR) + " + " + std::to_string(r) + "]";
+                    std::string el = slot_of(w, r);
                     if (mx) o << "    p" << i << " = psk_max(p" << i << ", " << el << ");\n";
                     else o << "    p" << i << " = p" << i << " + " << el << ";\n";
                 }
@@ -1315,7 +1381,8 @@ struct Emitter {
         for (int p = 0; p <= an.phases; ++p) {
             std::vector<int> targets;
             if (p < an.phases) {
-                for (int r : reductions_of(p)) targets.push_back(an.nodes[r].a);
+                for (int r : reductions_of(p))
+                    if (an.online_max[r] < 0) targets.push_back(an.nodes[r].a);
             } else {
                 targets.push_back(an.root);
                 for (const auto& x : an.extras)

@@ -43,6 +43,10 @@ struct Analysis {
     int phases = 0;                     // max reduction depth of the root
     std::vector<char> is_row;           // node value is one per row
     std::vector<int> depth;             // reduction phases that precede the node
+    // online normalizer (PSK_GROUP_ONLINE): node -> the ROW_MAX whose pass
+    // also takes this ROW_SUM of exp(y - max) (-1: none); and for a ROW_MAX,
+    // the ROW_SUM it carries (-1: none)
+    std::vector<int> online_max, online_sum;
     std::vector<int> n_readers;
     std::vector<char> needed;           // reachable from the root
     // causal masks (one period): values at refused positions

@@ -89,7 +89,7 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
         return fail(PSK_E_NULL, "inputs is NULL");
     if (desc->arith != PSK_F32)
         return fail(PSK_E_TYPE, "the arithmetic type must be f32 (bf16 is storage only)");
-    if (desc->flags & ~PSK_GROUP_TREE)
+    if (desc->flags & ~(PSK_GROUP_TREE | PSK_GROUP_ONLINE))
         return fail(PSK_E_UNSUPPORTED, "unknown flags");
 
     // ---- output
@@ -269,6 +269,31 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
         if (an.nodes[i].op == PSK_OP_POWN && an.nodes[i].iparam > 2 && an.members > 1)
             return fail(PSK_E_OP, at(i) + "pow n with n > 2 never joins a group");
 
+    // ---- online normalizer: ROW_SUM(EXP(SUB(y, ROW_MAX(y)))), y an element
+    // value read through exactly these nodes' operands
+    an.online_max.assign(n, -1);
+    an.online_sum.assign(n, -1);
+    if (desc->flags & PSK_GROUP_ONLINE) {
+        if (desc->flags & PSK_GROUP_TREE)
+            return fail(PSK_E_UNSUPPORTED, "the online normalizer needs row reductions; a tree-mapped group has none");
+        for (int i = 0; i < n; ++i) {
+            const psk_node& s = an.nodes[i];
+            if (s.op != PSK_OP_ROW_SUM) continue;
+            const psk_node& e = an.nodes[s.a];
+            if (e.op != PSK_OP_EXP) continue;
+            const psk_node& d = an.nodes[e.a];
+            if (d.op != PSK_OP_SUB) continue;
+            const psk_node& m = an.nodes[d.b];
+            if (m.op != PSK_OP_ROW_MAX || m.a != d.a || an.online_sum[d.b] >= 0) continue;
+            an.online_max[i] = d.b;
+            an.online_sum[d.b] = i;
+        }
+        bool any = false;
+        for (int i = 0; i < n; ++i) any = any || an.online_max[i] >= 0;
+        if (!any)
+            return fail(PSK_E_UNSUPPORTED, "PSK_GROUP_ONLINE: no row sum of exp(y - row_max(y)) in the group");
+    }
+
     // ---- row-level values and reduction depth
     an.is_row.assign(n, 0);
     an.depth.assign(n, 0);
@@ -288,7 +313,8 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
             if (an.is_row[nd.a])
                 return fail(PSK_E_ROW, at(i) + "a row reduction must reduce an element value, not a row value");
             an.is_row[i] = 1;
-            dep = an.depth[nd.a] + 1;
+            // an online sum finishes with its maximum, in the pass over y
+            dep = an.online_max[i] >= 0 ? an.depth[an.online_max[i]] : an.depth[nd.a] + 1;
             an.n_reductions++;
         } else if (nd.op == PSK_OP_CAUSAL_MASK) {
             an.is_row[i] = 0;

@@ -163,7 +163,7 @@ typedef struct psk_group_desc {
     const psk_tensor_desc* inputs;
     psk_tensor_desc out;             /* the root's storage type and shape */
     int32_t arith;                   /* arithmetic type: must be PSK_F32 */
-    uint32_t flags;                  /* 0, or PSK_GROUP_TREE */
+    uint32_t flags;                  /* 0, PSK_GROUP_TREE or PSK_GROUP_ONLINE */
     /* Further stored values (multi-output groups; 0 for a single root).
      * PSK-Realize, "Not in this version", names multi-output kernels as what
      * keeps a value read both inside and outside a group from splitting it,
@@ -186,6 +186,17 @@ typedef struct psk_group_desc {
  * its own; no row reductions and no causal mask.  Extra outputs are element
  * values stored to further slots. */
 #define PSK_GROUP_TREE 1u
+
+/* The online normalizer (poot, "Flash attention rewrite": the planner's
+ * online-softmax generator).  A row sum of exp(y - m) where m is the row
+ * maximum of the same y is taken in the maximum's pass: each lane keeps a
+ * running maximum and a sum of exponentials relative to it, rescaled by
+ * exp(old - new) when the maximum grows, and lanes and waves combine their
+ * pairs the same way.  One pass over the row fewer, so wide rows are read
+ * once less; the sum's rounding differs from the exact two-pass sum (a few
+ * f32 ulps: declared differs, tested within the f32 tolerance).  Refused
+ * (PSK_E_UNSUPPORTED) unless the group holds such a sum, and for trees. */
+#define PSK_GROUP_ONLINE 2u
 
 typedef struct psk_group psk_group;
 typedef struct psk_tree psk_tree;

@@ -99,7 +99,7 @@ def test_refusals(lib):
     # negative sizes, rank out of range
     _refused(_desc("%0 = input 0\n%1 = exp %0\n", [((8, 16), "f32")], (8, -16)), P.PSK_E_SHAPE)
     # reserved flags
-    _refused(_desc("%0 = input 0\n%1 = exp %0\n", F, (8, 16), flags=2), P.PSK_E_UNSUPPORTED)
+    _refused(_desc("%0 = input 0\n%1 = exp %0\n", F, (8, 16), flags=4), P.PSK_E_UNSUPPORTED)
 
 
 T1 = [((1,), "f32")]
@@ -453,3 +453,31 @@ def test_precision_follows_what_is_stored(lib):
     tree = P.psk_group_source(P.GroupDesc(C.tree_mixed_dag(), [((1,), "f32"), ((1,), "bf16"), ((), "f32")], (1,),
                                           "bf16", flags=P.PSK_GROUP_TREE))
     assert "psk_gelu(" in tree[tree.index('extern "C"'):] and "psk_gelu_b(" not in tree[tree.index('extern "C"'):]
+
+
+def test_online_normalizer_flag(lib):
+    from synth import configs as C
+    O = P.PSK_GROUP_ONLINE
+    # a softmax: its sum moves into the maximum's pass (one reduction phase)
+    src = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((8, 64), "f32")], (8, 64), "f32", flags=O))
+    body = src[src.index('extern "C"'):]
+    assert "float tm = " in body and "expf(q" in body
+    wide = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((4, 70000), "f32")], (4, 70000), "f32",
+                                          flags=O))
+    plain = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((4, 70000), "f32")], (4, 70000), "f32"))
+    # tiled: two walks of the row (register, LDS and memory tile loops each) instead of three
+    assert wide.count("for (int t = ") * 3 == plain.count("for (int t = ") * 2
+    # masked and causal softmax take it too
+    P.psk_group_source(P.GroupDesc(C.softmax_masked_dag(0.125), [((8, 64), "f32"), ((8, 64), "u8")], (8, 64), "f32",
+                                   flags=O))
+    P.psk_group_source(P.GroupDesc(C.softmax_causal_dag(0.125, 64), [((8, 64), "bf16")], (8, 64), "bf16", flags=O))
+    # refused without such a sum, and for trees
+    _refused(P.GroupDesc(C.rmsnorm_gelu_dag(C.f32(1e-5)), [((8, 64), "bf16"), ((8, 64), "bf16"), ((64,), "bf16")],
+                         (8, 64), "bf16", flags=O), P.PSK_E_UNSUPPORTED)
+    _refused(_desc("%0 = input 0\n%1 = row_max %0\n%2 = sub %0 %1\n%3 = exp %2\n%4 = row_max %3\n%5 = div %3 %4\n",
+                   F, (8, 16), flags=O), P.PSK_E_UNSUPPORTED)
+    # exp(y - max(z)) with z != y is not the normalizer
+    _refused(_desc("%0 = input 0\n%1 = input 1\n%2 = row_max %1\n%3 = sub %0 %2\n%4 = exp %3\n%5 = row_sum %4\n"
+                   "%6 = div %4 %5\n", F + F, (8, 16), flags=O), P.PSK_E_UNSUPPORTED)
+    _refused(P.GroupDesc(C.tree_sgd_dag(), [((1,), "f32"), ((1,), "f32"), ((), "f32")], (1,), "f32",
+                         flags=P.PSK_GROUP_TREE | O), P.PSK_E_UNSUPPORTED)
