@@ -81,10 +81,20 @@ std::string canonical_text(const Analysis& an)
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Layout overrides for measurement, "key=value" pairs separated by commas in
-// PSK_LAYOUT: nt=0|1, xcd=0|1, block=64..1024 (pointwise, and row kernels
-// whose rows are narrower than a block), lanes=16|64|128|...|1024 (row
-// kernel; changes the reduction tree).  A layout never changes which
-// elements are computed.
+// PSK_LAYOUT (an unknown or out-of-range value falls back to the default):
+//   every kernel: nt=0|1 (nontemporal accesses), xcd=0|1 (XCD-contiguous
+//     block mapping), block=64..1024 (threads per workgroup);
+//   tree kernels: tper=4|8|16 (elements per thread);
+//   row kernels: epl (elements of output a lane aims for), lanes=16|32|
+//     64..1024, epmax (most elements a lane holds before the tiled kernel
+//     takes over, default 32), persist=k (k persistent workgroups a CU),
+//     tiled=1 (force the tiled kernel);
+//   tiled kernel: lanes=64..1024, tn (vectors a lane per tile), tcache=0|1
+//     (cached loads before the last phase), rc / lc (tiles kept in
+//     registers / LDS), wpe / wmin (most / fewest waves a SIMD).
+// A layout never changes which elements are computed; lanes, epl, epmax,
+// tiled and tn change a reduction's bracketing (within tolerance), the
+// others change no bit.
 static int layout_value(const char* key, int dflt)
 {
     const char* env = std::getenv("PSK_LAYOUT");

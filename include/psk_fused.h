@@ -207,7 +207,11 @@ typedef struct psk_tree psk_tree;
  * operand counts, a single root, no dead node, the member cap, one result
  * type for the element members, broadcast legality, row-reduction use (a
  * reduction's operand is an element value; the root is an element value),
- * storage types.  Does not need a GPU: the kernel is loaded on first run. */
+ * storage types.  Does not need a GPU: the kernel is loaded on first run.
+ * The launch layout (lanes a row, workgroup size, tiling, caches) follows
+ * from the shapes; the environment variable PSK_LAYOUT ("key=value,...")
+ * overrides it at create time, for measurement: it never changes which
+ * elements are computed, only, for some keys, a reduction's bracketing. */
 psk_status psk_group_create(const psk_group_desc* desc, psk_group** out);
 
 /* Run the group as one kernel launch.  inputs[k] is the device address of
