@@ -35,7 +35,10 @@
  *     the launch.  Device faults surface at the caller's next synchronisation.
  *   - Kernels never write their inputs unless an output is the same buffer
  *     (in-place).  Outputs are not zeroed beforehand.
- *   - The library allocates no device memory in *_run / *_step.
+ *   - The library allocates no device memory for data in *_run / *_step
+ *     (tree tables and the clipping pass's partials are allocated by
+ *     psk_tree_create).  The first run of a group on a device loads its
+ *     code object there (hipModuleLoadData); later runs only launch.
  *   - All functions are thread-safe.
  */
 #ifndef PSK_FUSED_H
