@@ -159,6 +159,9 @@ def main():
             "avg_ms": round(adamw_avg, 4),
             "bytes_per_launch": adamw_bytes,
         },
+        "env": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+                "numpy": __import__("numpy").__version__, "device": torch.cuda.get_device_name(dev),
+                "library_version": P.psk_version()},
         "kernels": {
             "adamw_ms_median": round(statistics.median(adamw_ms), 4),
             "softmax_ms_median": round(statistics.median(softmax_ms), 4),
@@ -332,10 +335,10 @@ def profile_others(P, configs, torch, dev, stream, hp, state):
 
 def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, probs, adamw_bytes, softmax_bytes, hp,
                 state):
-    R, C = scores.shape
-    allowed = sum(min(r % 1024, C - 1) + 1 for r in range(1024)) * (R // 1024)
     """Each workload alone: a 1 GiB write between calls evicts the 256 MB
     last-level cache; HIP events around each call; median of --reps."""
+    R, C = scores.shape
+    allowed = sum(min(r % 1024, C - 1) + 1 for r in range(1024)) * (R // 1024)
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
 
     def timed(fn, reps):
@@ -383,7 +386,18 @@ def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, pro
     tiny_tree = P.Tree([[s["theta"], s["grad"], s["m"], s["v"]] for s in tiny])
     n_tiny = sum(math.prod(s) for s in tiny_shapes)
     add("adamw_tiny_gpt_f32", n_tiny * 28, lambda: tiny_tree.adamw_step(*hp, stream=stream),
-        note="3 MB: launch-latency bound, no HBM target")
+        note="3 MB: launch-latency bound, no HBM target; ms_* cold (cache flushed), us_warm_median back to back")
+    warm = []
+    for k in range(args.reps + 2):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        tiny_tree.adamw_step(*hp, stream=stream)
+        b.record(stream)
+        b.synchronize()
+        if k >= 2:
+            warm.append(a.elapsed_time(b))
+    out["adamw_tiny_gpt_f32"]["us_warm_median"] = round(statistics.median(warm) * 1e3, 2)
 
     # add + RMSNorm + gamma + GELU, bf16 [16384, 4096]
     x, r, g = configs.rmsnorm_inputs(16384, 4096, device=dev)
