@@ -344,6 +344,16 @@ __device__ __forceinline__ float psk_gelu_b(float x) {
   const float phi = (x > 0.0f) ? 1.0f - half_ec : half_ec;
   return x * phi;
 }
+// exp(x) for an argument known to be <= 0 (an element minus its row's
+// maximum) whose value only reaches bf16 results: 2^(x log2 e + 64) 2^-64,
+// the hardware 2^x kept in its normal range by the shift and the exact
+// power-of-two scaling making tiny results subnormal (or 0).  The rounding
+// of log2 e and of the fused multiply-add cost a relative error below
+// about 6e-6 for x >= -88 (far inside a bf16 half-ulp, 2^-9); -inf gives 0
+// and NaN stays NaN.
+__device__ __forceinline__ float psk_exp_np_b(float x) {
+  return __builtin_amdgcn_exp2f(fmaf(x, 1.44269504088896341f, 64.0f)) * 0x1p-64f;
+}
 // a / b for a value b shared by the whole row, given y = 1/b correctly
 // rounded: q = a*y is within an ulp of a/b; the fma gives the exact
 // remainder a - b*q, and one more fma rounds q + remainder*y to the
@@ -516,6 +526,18 @@ struct Emitter {
         return i == an.root || an.stored[i] > 0;
     }
 
+    // exp(y - row_max(y)): an argument that is <= 0 (or NaN)
+    bool exp_nonpos(int i) const
+    {
+        const psk_node& nd = an.nodes[i];
+        if (nd.op != PSK_OP_EXP) return false;
+        const psk_node& d = an.nodes[nd.a];
+        return d.op == PSK_OP_SUB && an.nodes[d.b].op == PSK_OP_ROW_MAX && an.nodes[d.b].a == d.a;
+    }
+
+    // ... whose value only bf16 results depend on: the short exponential
+    bool cheap_exp(int i) const { return exp_nonpos(i) && !f32_reach[i]; }
+
     // element / row statistic (a value computed from a reduction) that only
     // bf16 results depend on: the row's reciprocal (correctly rounded) times
     // the element, within 1.5 f32 ulps of the quotient.  A division by a
@@ -560,7 +582,7 @@ struct Emitter {
         case PSK_OP_MIN: return "psk_min(" + A() + ", " + B() + ")";
         case PSK_OP_NEG: return "(-" + A() + ")";
         case PSK_OP_ABS: return "fabsf(" + A() + ")";
-        case PSK_OP_EXP: return "expf(" + A() + ")";
+        case PSK_OP_EXP: return (cheap_exp(i) ? "psk_exp_np_b(" : "expf(") + A() + ")";
         case PSK_OP_LOG: return "logf(" + A() + ")";
         case PSK_OP_SQRT: return "sqrtf(" + A() + ")";
         case PSK_OP_TANH: return "tanhf(" + A() + ")";
@@ -1218,6 +1240,10 @@ struct Emitter {
         }
     }
 
+    // the exponential an online sum uses: its exp node's form (every
+    // argument here is <= 0 as well)
+    std::string online_exp(int sm) const { return cheap_exp(an.nodes[sm].a) ? "psk_exp_np_b" : "expf"; }
+
     // Online normalizer: this lane's elements of y (the maximum's operand)
     // update the running maximum p<mx> once for the group of elements and
     // the sum p<sm> of exp(y - running maximum), rescaled by
@@ -1228,17 +1254,18 @@ struct Emitter {
     {
         const int y = an.nodes[mx].a;
         const std::string P = "p" + std::to_string(mx), S = "p" + std::to_string(sm);
+        const std::string ex = online_exp(sm);
         o << indent << "{\n" << indent << "  float tm = (-__builtin_inff());\n";
         for (int e = 0; e < NE; ++e) {
             std::string acc = "tm = psk_max(tm, " + val(y, e) + ");";
             if (ragged) o << indent << "  if (" << col(e) << " < " << an.cols << ") " << acc << "\n";
             else o << indent << "  " << acc << "\n";
         }
-        o << indent << "  if (tm > " << P << ") { " << S << " = " << S << " * expf(" << P << " - tm); " << P
+        o << indent << "  if (tm > " << P << ") { " << S << " = " << S << " * " << ex << "(" << P << " - tm); " << P
           << " = tm; }\n";
         o << indent << "  const float mref = " << P << " == (-__builtin_inff()) ? 0.0f : " << P << ";\n";
         for (int e = 0; e < NE; ++e) {
-            std::string acc = S + " = (" + S + " + expf(" + val(y, e) + " - mref));";
+            std::string acc = S + " = (" + S + " + " + ex + "(" + val(y, e) + " - mref));";
             if (ragged) o << indent << "  if (" << col(e) << " < " << an.cols << ") " << acc << "\n";
             else o << indent << "  " << acc << "\n";
         }
@@ -1268,8 +1295,8 @@ struct Emitter {
         for (int i : reds) {
             const int m = an.online_max[i];
             if (m < 0) continue;
-            o << "    p" << i << " = (q" << m << " == p" << m << ") ? p" << i << " : p" << i << " * expf(q" << m
-              << " - p" << m << ");\n";
+            o << "    p" << i << " = (q" << m << " == p" << m << ") ? p" << i << " : p" << i << " * " << online_exp(i)
+              << "(q" << m << " - p" << m << ");\n";
             lane_reduce(i);
         }
         if (W > 1) {
@@ -1299,8 +1326,8 @@ struct Emitter {
                     const int rm = (int)(std::find(reds.begin(), reds.end(), m) - reds.begin());
                     for (int w = 0; w < W; ++w) {
                         std::string mw = slot_of(w, rm), sw = slot_of(w, r);
-                        std::string t = "((" + mw + " == p" + std::to_string(m) + ") ? " + sw + " : " + sw +
-                                        " * expf(" + mw + " - p" + std::to_string(m) + "))";
+                        std::string t = "((" + mw + " == p" + std::to_string(m) + ") ? " + sw + " : " + sw + " * " +
+                                        online_exp(i) + "(" + mw + " - p" + std::to_string(m) + "))";
                         if (w == 0) o << "    p" << i << " = " << t << ";\n";
                         else o << "    p" << i << " = p" << i << " + " << t << ";\n";
                     }

@@ -449,6 +449,11 @@ def test_precision_follows_what_is_stored(lib):
                                           extras=[(C.RMSNORM_H, (R, N), "f32")]))
     body = rmsh[rmsh.index('extern "C"'):]
     assert "psk_gelu_b(" in body and "psk_divr(" not in body and "* y8)" in body
+    # softmax's exp(y - max y): the short exponential only for bf16 results
+    for dt, short in (("bf16", True), ("f32", False)):
+        sm = P.psk_group_source(P.GroupDesc(C.softmax_causal_dag(0.125, N), [((R, N), dt)], (R, N), dt))
+        body = sm[sm.index('extern "C"'):]
+        assert ("psk_exp_np_b(" in body) == short and ("expf(" in body) != short
     # a gelu that other members read is not the bf16 form
     tree = P.psk_group_source(P.GroupDesc(C.tree_mixed_dag(), [((1,), "f32"), ((1,), "bf16"), ((), "f32")], (1,),
                                           "bf16", flags=P.PSK_GROUP_TREE))
