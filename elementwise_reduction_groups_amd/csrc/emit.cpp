@@ -419,6 +419,12 @@ struct Emitter {
 
     // node -> some f32 stored value depends on it (through any members)
     std::vector<char> f32_reach;
+    // node -> every path from it to a stored value keeps a small relative
+    // error small: products, quotients, selections, sign and magnitude
+    // operations, square roots, squares, maxima and minima, and the row sum
+    // of a never-negative exponential (no sum or difference that can cancel,
+    // no logarithm)
+    std::vector<char> conditioned;
 
     Emitter(const Analysis& a, const KernelPlan& p) : an(a), pl(p)
     {
@@ -432,6 +438,24 @@ struct Emitter {
             const psk_node& nd = an.nodes[i];
             const int32_t opnd[3] = {nd.a, nd.b, nd.c};
             for (int k = 0; k < op_arity(nd.op); ++k) f32_reach[opnd[k]] = 1;
+        }
+        conditioned.assign(n, 1);
+        for (int j = n - 1; j >= 0; --j) {
+            const psk_node& nd = an.nodes[j];
+            const int32_t opnd[3] = {nd.a, nd.b, nd.c};
+            for (int k = 0; k < op_arity(nd.op); ++k) {
+                bool ok = conditioned[j];
+                switch (nd.op) {
+                case PSK_OP_MUL: case PSK_OP_DIV: case PSK_OP_NEG: case PSK_OP_ABS: case PSK_OP_SQRT:
+                case PSK_OP_POW2: case PSK_OP_MAX: case PSK_OP_MIN: case PSK_OP_CAUSAL_MASK: case PSK_OP_ROW_MAX:
+                    break;
+                case PSK_OP_WHERE: ok = ok && k == 1; break;            // the value, not the mask
+                case PSK_OP_SELECT: ok = ok && k != 0; break;           // a chosen value, not the condition
+                case PSK_OP_ROW_SUM: ok = ok && an.nodes[opnd[k]].op == PSK_OP_EXP; break;
+                default: ok = false;
+                }
+                if (!ok) conditioned[opnd[k]] = 0;
+            }
         }
         NE = (pl.kind == 1 || pl.kind == 3 ? pl.nv : 1) * pl.vec;   // tree: elements per thread
         big = an.numel >= (int64_t(1) << 31) - 4096;
@@ -535,8 +559,9 @@ struct Emitter {
         return d.op == PSK_OP_SUB && an.nodes[d.b].op == PSK_OP_ROW_MAX && an.nodes[d.b].a == d.a;
     }
 
-    // ... whose value only bf16 results depend on: the short exponential
-    bool cheap_exp(int i) const { return exp_nonpos(i) && !f32_reach[i]; }
+    // ... whose value only bf16 results depend on, through well-conditioned
+    // operations: the short exponential
+    bool cheap_exp(int i) const { return exp_nonpos(i) && !f32_reach[i] && conditioned[i]; }
 
     // element / row statistic (a value computed from a reduction) that only
     // bf16 results depend on: the row's reciprocal (correctly rounded) times

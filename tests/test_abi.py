@@ -454,6 +454,11 @@ def test_precision_follows_what_is_stored(lib):
         sm = P.psk_group_source(P.GroupDesc(C.softmax_causal_dag(0.125, N), [((R, N), dt)], (R, N), dt))
         body = sm[sm.index('extern "C"'):]
         assert ("psk_exp_np_b(" in body) == short and ("expf(" in body) != short
+    # ... but not where a difference could cancel its error (1 - exp(y - max y))
+    one = P.psk_group_source(_desc("%0 = input 0\n%1 = row_max %0\n%2 = sub %0 %1\n%3 = exp %2\n"
+                                   "%4 = const 1.0\n%5 = sub %4 %3\n", [((R, N), "bf16")], (R, N), "bf16"))
+    body = one[one.index('extern "C"'):]
+    assert "psk_exp_np_b(" not in body and "expf(" in body
     # a gelu that other members read is not the bf16 form
     tree = P.psk_group_source(P.GroupDesc(C.tree_mixed_dag(), [((1,), "f32"), ((1,), "bf16"), ((), "f32")], (1,),
                                           "bf16", flags=P.PSK_GROUP_TREE))
