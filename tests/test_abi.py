@@ -491,3 +491,21 @@ def test_online_normalizer_flag(lib):
                    "%6 = div %4 %5\n", F + F, (8, 16), flags=O), P.PSK_E_UNSUPPORTED)
     _refused(P.GroupDesc(C.tree_sgd_dag(), [((1,), "f32"), ((1,), "f32"), ((), "f32")], (1,), "f32",
                          flags=P.PSK_GROUP_TREE | O), P.PSK_E_UNSUPPORTED)
+
+
+def test_persistent_rows_where_column_vectors_weigh(lib):
+    """LayerNorm's γ and β weigh as much as its rows: persistent workgroups
+    that load them once; softmax (no column vectors) and RMSNorm (one,
+    beside two row inputs) keep one row per workgroup."""
+    from synth import configs as C
+    eps = C.f32(1e-5)
+    R, N = 64, 4096
+    persistent = "for (; row < "
+    ln = P.psk_group_source(P.GroupDesc(C.layernorm_dag(eps), [((R, N), "bf16"), ((N,), "bf16"), ((N,), "bf16")],
+                                        (R, N), "bf16", root=C.LAYERNORM_ROOT,
+                                        extras=[(C.LAYERNORM_MEAN, (R, 1), "f32"), (C.LAYERNORM_RSTD, (R, 1), "f32")]))
+    assert persistent in ln
+    sm = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((R, N), "f32")], (R, N), "f32"))
+    rms = P.psk_group_source(P.GroupDesc(C.rmsnorm_gelu_dag(eps), [((R, N), "bf16"), ((R, N), "bf16"), ((N,), "bf16")],
+                                         (R, N), "bf16"))
+    assert persistent not in sm and persistent not in rms

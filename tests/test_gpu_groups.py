@@ -278,7 +278,7 @@ def test_persistent_row_layout_is_bit_identical(monkeypatch):
     ]
     for nodes, ins, shape, dt, kw, tensors, xs in cases:
         outs = []
-        for layout in ("", "persist=4"):
+        for layout in ("persist=0", "persist=4", "persist=2", ""):
             monkeypatch.setenv("PSK_LAYOUT", layout)
             grp = P.Group(nodes, ins, shape, dt, **kw)
             out = torch.full(shape, float("nan"), dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device=DEV)
@@ -286,5 +286,6 @@ def test_persistent_row_layout_is_bit_identical(monkeypatch):
             grp.run(tensors, out, extra_outs=ex or None)
             torch.cuda.synchronize()
             outs.append([to_np(out)] + [to_np(e) for e in ex])
-        for a, b in zip(*outs):
-            assert_bits(a, b, f"persistent layout, {shape}")
+        for other in outs[1:]:
+            for a, b in zip(outs[0], other):
+                assert_bits(a, b, f"persistent layout, {shape}")
