@@ -1,0 +1,96 @@
+/* The C ABI used from plain C99 (no C++ and no Python): the header compiles
+ * as C, the library links, and the host-side calls behave as documented.
+ * No GPU is touched: groups are created and emitted (hipRTC compiles without
+ * a device), bodies partitioned, tree plans built.  Prints "ok" and exits 0
+ * on success; prints the failing check and exits 1 otherwise. */
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "psk_fused.h"
+
+#define CHECK(c) do { if (!(c)) { printf("check failed: %s (line %d): %s\n", #c, __LINE__, psk_last_error()); \
+                                  return 1; } } while (0)
+
+static psk_node node(int op, int a, int b, float imm, int iparam)
+{
+    psk_node n;
+    memset(&n, 0, sizeof n);
+    n.op = op; n.a = a; n.b = b; n.c = -1; n.imm = imm; n.iparam = iparam;
+    return n;
+}
+
+static psk_tensor_desc tensor(int rank, int64_t d0, int64_t d1, int dtype)
+{
+    psk_tensor_desc t;
+    memset(&t, 0, sizeof t);
+    t.rank = rank; t.shape[0] = d0; t.shape[1] = d1; t.dtype = dtype;
+    return t;
+}
+
+int main(void)
+{
+    CHECK(psk_version() == PSK_VERSION);
+    CHECK(strcmp(psk_status_str(PSK_OK), "PSK_OK") == 0);
+
+    /* softmax over [8, 64] f32: x*s, row max, subtract, exp, row sum, divide */
+    psk_node nodes[8];
+    nodes[0] = node(PSK_OP_INPUT, -1, -1, 0.0f, 0);
+    nodes[1] = node(PSK_OP_CONST, -1, -1, 0.125f, 0);
+    nodes[2] = node(PSK_OP_MUL, 0, 1, 0.0f, 0);
+    nodes[3] = node(PSK_OP_ROW_MAX, 2, -1, 0.0f, 0);
+    nodes[4] = node(PSK_OP_SUB, 2, 3, 0.0f, 0);
+    nodes[5] = node(PSK_OP_EXP, 4, -1, 0.0f, 0);
+    nodes[6] = node(PSK_OP_ROW_SUM, 5, -1, 0.0f, 0);
+    nodes[7] = node(PSK_OP_DIV, 5, 6, 0.0f, 0);
+    psk_tensor_desc in = tensor(2, 8, 64, PSK_F32);
+    psk_group_desc d;
+    memset(&d, 0, sizeof d);
+    d.n_nodes = 8; d.nodes = nodes; d.root = 7; d.n_inputs = 1; d.inputs = &in;
+    d.out = tensor(2, 8, 64, PSK_F32); d.arith = PSK_F32;
+
+    size_t len = 0;
+    CHECK(psk_group_source(&d, NULL, 0, &len) == PSK_OK && len > 0);
+    char* src = (char*)malloc(len + 1);
+    CHECK(src && psk_group_source(&d, src, len + 1, &len) == PSK_OK);
+    CHECK(strstr(src, "extern \"C\" __global__") != NULL);
+    free(src);
+
+    psk_group* g = NULL;
+    CHECK(psk_group_create(&d, &g) == PSK_OK && g != NULL);
+    psk_group_info info;
+    CHECK(psk_group_get_info(g, &info) == PSK_OK && info.kind == 1);
+    psk_group_destroy(g);
+
+    /* the online normalizer takes the same group; refusals leave no object */
+    d.flags = PSK_GROUP_ONLINE;
+    g = NULL;
+    CHECK(psk_group_create(&d, &g) == PSK_OK);
+    psk_group_destroy(g);
+    d.flags = 0;
+    d.root = 3;                       /* node 7 would be dead */
+    g = (psk_group*)&d;
+    CHECK(psk_group_create(&d, &g) != PSK_OK && g == NULL && strlen(psk_last_error()) > 0);
+    CHECK(psk_group_create(NULL, &g) == PSK_E_NULL);
+
+    /* partition: the chain x -> exp -> tanh is one group, with rows fused the
+     * whole softmax is one group too */
+    psk_tensor_desc types[8];
+    for (int i = 0; i < 8; ++i) types[i] = tensor(2, 8, 64, PSK_F32);
+    types[1] = tensor(0, 0, 0, PSK_F32);
+    types[3] = tensor(2, 8, 1, PSK_F32);
+    types[6] = tensor(2, 8, 1, PSK_F32);
+    uint8_t out[8] = {0, 0, 0, 0, 0, 0, 0, 1};
+    int32_t group_of[8], is_root[8], n_groups = 0;
+    CHECK(psk_partition(8, nodes, types, out, group_of, is_root, &n_groups) == PSK_OK && n_groups == 5);
+    CHECK(psk_partition_ex(8, nodes, types, out, PSK_PARTITION_ROWS, group_of, is_root, &n_groups) == PSK_OK);
+    CHECK(n_groups == 1 && is_root[7] == 1 && group_of[0] == -1 && group_of[2] == group_of[7]);
+
+    /* tree plan: prefix offsets and whole chunks */
+    int64_t numel[3] = {5, 4096 * 3 + 1, 0}, n_chunks = 0, off[4];
+    CHECK(psk_tree_plan(numel, 3, &n_chunks, off, NULL, NULL, NULL) == PSK_OK);
+    CHECK(n_chunks == 5 && off[0] == 0 && off[1] == 5 && off[2] == 5 + 4096 * 3 + 1 && off[3] == off[2]);
+
+    printf("ok\n");
+    return 0;
+}
