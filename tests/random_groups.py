@@ -1,0 +1,99 @@
+"""Seeded random pointwise groups made of IEEE-exact operations (add, sub,
+mul, div, max, min, neg, abs, sqrt, pow2, select, where): any output rank,
+broadcast inputs of every kind, bf16 and f32 storage, byte masks, extra
+stored values.  Both the GPU path and the oracle compute such a group
+exactly (one rounding per op, the same rounding of stored values), so the
+two must agree bit for bit.  Test infrastructure only: it builds
+descriptions and inputs, it evaluates nothing."""
+import math
+import random
+from typing import List, Tuple
+
+from synth.dag import Node
+
+BINARY = ["add", "sub", "mul", "div", "max", "min"]
+UNARY = ["neg", "abs", "sqrt", "pow2"]
+
+
+def _input_shape(rng, out_shape):
+    kind = rng.choice(["full", "full", "bcast", "scalar", "col", "rowconst"])
+    r = len(out_shape)
+    if kind == "full":
+        return tuple(out_shape)
+    if kind == "scalar":
+        return ()
+    if kind == "col":
+        return (out_shape[-1],)
+    if kind == "rowconst":
+        return tuple(out_shape[:-1]) + (1,) if r > 1 else (1,)
+    k = rng.randint(1, r)                      # right-aligned, some axes broadcast
+    return tuple(d if rng.random() < 0.6 else 1 for d in out_shape[r - k:])
+
+
+def random_group(rng: random.Random):
+    """(nodes, inputs [(shape, dtype)], out_shape, out_dtype, extras [(node, dtype)])"""
+    rank = rng.randint(1, 4)
+    lead = [rng.choice([1, 2, 3, 5, 7, 16, 33]) for _ in range(rank - 1)]
+    out_shape = tuple(lead + [rng.choice([1, 3, 8, 12, 64, 100, 129, 256, 1000])])
+    out_dtype = rng.choice(["f32", "bf16"])
+    inputs, nodes, is_row = [], [], []
+    for k in range(rng.randint(1, 4)):
+        shape = _input_shape(rng, out_shape) if k else tuple(out_shape)   # input 0 spans the output
+        inputs.append((shape, rng.choice(["f32", "bf16"])))
+        nodes.append(Node("input", (), None, k))
+        is_row.append(len(shape) == 0 or shape[-1] == 1)       # one value per row (or per tensor)
+    mask = None
+    if rng.random() < 0.35:
+        mask = len(nodes)
+        mshape = _input_shape(rng, out_shape) or (1,)
+        inputs.append((mshape, "u8"))
+        nodes.append(Node("input", (), None, len(inputs) - 1))
+        is_row.append(mshape[-1] == 1)
+    if rng.random() < 0.5:
+        nodes.append(Node("const", (), float(rng.choice([0.5, -3.0, 1.25, 0.0, 7.0]))))
+        is_row.append(True)
+    values = [i for i in range(len(nodes)) if i != mask]
+    unread = set(values)
+    members = []
+
+    def pick():
+        if unread and rng.random() < 0.6:
+            return rng.choice(sorted(unread))
+        return rng.choice(values)
+
+    def add(op, args, imm=None):
+        idx = len(nodes)
+        nodes.append(Node(op, tuple(args), imm))
+        is_row.append(all(is_row[a] for a in args))
+        for a in args:
+            unread.discard(a)
+        unread.add(idx)
+        values.append(idx)
+        members.append(idx)
+        return idx
+
+    for _ in range(rng.randint(1, 14)):
+        r = rng.random()
+        if mask is not None and r < 0.15:
+            add("where", [mask, pick()], float(rng.choice([0.0, -math.inf, 2.5])))
+        elif r < 0.25:
+            add("select", [pick(), pick(), pick()])
+        elif r < 0.5:
+            add(rng.choice(UNARY), [pick()])
+        else:
+            add(rng.choice(BINARY), [pick(), pick()])
+    if mask is not None and not any(nodes[m].op == "where" for m in members):
+        add("where", [mask, members[-1]], 0.0)
+    # every value read: fold what is unread into the root
+    while len(unread) > 1:
+        a, b = sorted(unread)[:2]
+        add(rng.choice(["add", "mul", "max"]), [a, b])
+    root = len(nodes) - 1
+    if root not in members or is_row[root]:
+        root = add("add", [root, 0])            # input 0 spans the output
+    extras = []
+    cand = [m for m in members if m != root and not is_row[m]]
+    rng.shuffle(cand)
+    for m in cand[:rng.randint(0, 2)]:
+        extras.append((m, rng.choice(["f32", "bf16"])))
+    return nodes, inputs, out_shape, out_dtype, extras

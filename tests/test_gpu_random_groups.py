@@ -1,0 +1,73 @@
+"""GPU parity of seeded random pointwise groups of IEEE-exact operations
+(tests/random_groups.py: every output rank, broadcast inputs of every kind,
+bf16/f32 storage, byte masks, extra stored values, some inputs misaligned
+so the element path runs) against the oracle, bit for bit: both sides round
+once per operation and store the same roundings.  NaN compares as NaN (any
+payload)."""
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import to_np
+from tests.random_groups import random_group
+
+P = pytest.importorskip("elementwise_reduction_groups_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+OD = {"f32": P.PSK_F32, "bf16": P.PSK_BF16}
+
+
+def same_bits(got, ref):
+    if got.dtype == np.float32:
+        g, r = got.view(np.uint32), ref.view(np.uint32)
+        gn, rn = np.isnan(got), np.isnan(ref)
+    else:
+        g, r = got, ref
+        gn = ((g & 0x7F80) == 0x7F80) & ((g & 0x7F) != 0)
+        rn = ((r & 0x7F80) == 0x7F80) & ((r & 0x7F) != 0)
+    ok = (gn & rn) | (~gn & ~rn & (g == r))
+    return ok
+
+
+def make_input(shape, dt, gen, misaligned):
+    if dt == "u8":
+        v = torch.randint(0, 3, shape, generator=gen, device="cpu").to(torch.uint8) * 3   # 0, 3, 6
+        return v.to(DEV)
+    x = (torch.rand(shape, generator=gen) * 4.0 - 2.0)
+    x[torch.rand(shape, generator=gen) < 0.05] = 0.0                                  # exact zeros
+    x = x.to(TD[dt])
+    if misaligned and x.numel() > 0:
+        buf = torch.empty(x.numel() + 1, dtype=x.dtype, device=DEV)
+        v = buf[1:].view(shape)
+        v.copy_(x.to(DEV))
+        return v
+    return x.to(DEV)
+
+
+@pytest.mark.parametrize("chunk", range(5))
+def test_random_exact_groups_bit_for_bit(chunk):
+    rng = random.Random(1000 + chunk)
+    gen = torch.Generator().manual_seed(77 + chunk)
+    for trial in range(12):
+        nodes, inputs, shape, dt, extras = random_group(rng)
+        mis = rng.random() < 0.25
+        tensors = [make_input(s, t, gen, mis and k == 0) for k, (s, t) in enumerate(inputs)]
+        g = P.Group(nodes, inputs, shape, dt, root=len(nodes) - 1, extras=[(m, shape, xdt) for m, xdt in extras])
+        out = torch.full(shape, float("nan"), dtype=TD[dt], device=DEV)
+        xs = [torch.full(shape, float("nan"), dtype=TD[xdt], device=DEV) for _, xdt in extras]
+        g.run(tensors, out, extra_outs=xs or None)
+        torch.cuda.synchronize()
+        ins_np = [t.cpu().numpy().view(np.uint8) if t.dtype == torch.uint8 else to_np(t) for t in tensors]
+        refx = [(m, np.zeros(shape, np.float32 if xdt == "f32" else np.uint16)) for m, xdt in extras]
+        ref = oracle.eval_group(nodes, ins_np, shape, OD[dt], root=len(nodes) - 1, extras=refx)
+        what = f"chunk {chunk} trial {trial}: shape {shape} {dt} inputs {inputs} extras {extras} misaligned {mis}"
+        ok = same_bits(to_np(out), ref)
+        assert ok.all(), f"{what}: root differs at {int((~ok).sum())} of {ok.size}"
+        for (m, r), x in zip(refx, xs):
+            ok = same_bits(to_np(x), r)
+            assert ok.all(), f"{what}: extra {m} differs at {int((~ok).sum())} of {ok.size}"
