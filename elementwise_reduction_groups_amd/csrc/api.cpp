@@ -327,6 +327,10 @@ struct psk_tree {
     uint8_t shared[PSK_MAX_SLOTS][PSK_MAX_SLOTS] = {};   // some leaf has one buffer in both slots
     int device = 0;
     int32_t vector_leaves = 0;
+    // AdamW's slot roles (theta, g, m, v [, theta', m', v']): PSK_OK when
+    // the tree can take an AdamW step, else why not (checked at the step)
+    psk_status adamw_status = PSK_OK;
+    std::string adamw_refusal;
     ~psk_tree()
     {
         if (d_leaves) (void)hipFree(d_leaves);
@@ -356,9 +360,18 @@ extern "C" psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, 
             return fail(PSK_E_TYPE, "slot " + std::to_string(s) + ": storage type must be f32 or bf16");
         t->dt[s] = slot_dtypes[s];
     }
-    if (adamw_roles && t->dt[2] != t->dt[3]) return fail(PSK_E_TYPE, "m and v must share a storage type");
+    // what an AdamW step needs beyond a valid tree (refused at the step)
+    auto no_adamw = [&](psk_status st, const std::string& why) {
+        if (t->adamw_status == PSK_OK) {
+            t->adamw_status = st;
+            t->adamw_refusal = why;
+        }
+    };
+    if (!adamw_roles)
+        no_adamw(PSK_E_SHAPE, "an AdamW tree has 4 slots (theta, g, m, v) or 7 (plus theta', m', v')");
+    if (adamw_roles && t->dt[2] != t->dt[3]) no_adamw(PSK_E_TYPE, "m and v must share a storage type");
     if (n_slots == 7 && (t->dt[4] != t->dt[0] || t->dt[5] != t->dt[2] || t->dt[6] != t->dt[3]))
-        return fail(PSK_E_TYPE, "an output slot must have its input's storage type");
+        no_adamw(PSK_E_TYPE, "an output slot must have its input's storage type");
     std::vector<int64_t> numel(n_leaves);
     for (int32_t l = 0; l < n_leaves; ++l) numel[l] = leaves[l].numel;
     psk_status st = plan_tree(numel.data(), n_leaves, PSK_TREE_CHUNK, t->plan);
@@ -393,15 +406,17 @@ extern "C" psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, 
         gleaves[l].flags = v16 ? 1 : 0;
         t->vector_leaves += v16;
     }
-    // aliasing: identical ranges are allowed only for an input and its own
-    // output in one leaf; any other overlap is refused
+    // aliasing: one buffer may fill two slots of a leaf that share a storage
+    // type; any other overlap is refused.  AdamW's roles allow less: only an
+    // input and its own output (7 slots) share a buffer.
     std::sort(ranges.begin(), ranges.end(), [](const Range& x, const Range& y) {
         return x.b != y.b ? x.b < y.b : x.e < y.e;
     });
     auto pair_ok = [&](const Range& x, const Range& y) {
-        if (x.leaf != y.leaf) return false;
+        return x.leaf == y.leaf && t->dt[x.slot] == t->dt[y.slot];
+    };
+    auto adamw_pair_ok = [&](const Range& x, const Range& y) {
         int a = std::min(x.slot, y.slot), b = std::max(x.slot, y.slot);
-        if (!adamw_roles) return t->dt[a] == t->dt[b];   // one buffer in two slots of a leaf
         if (n_slots == 4) return false;   // in place: every slot is its own buffer
         return (a == 0 && b == 4) || (a == 2 && b == 5) || (a == 3 && b == 6);
     };
@@ -411,10 +426,10 @@ extern "C" psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, 
         const Range& r = ranges[i];
         if (i > 0 && r.b < max_end) {
             const Range& q = ranges[prev];
-            if (!(q.b == r.b && q.e == r.e && pair_ok(q, r)))
-                return fail(PSK_E_ALIAS, "leaf " + std::to_string(r.leaf) + " slot " + std::to_string(r.slot) +
-                                             " overlaps leaf " + std::to_string(q.leaf) + " slot " +
-                                             std::to_string(q.slot));
+            const std::string what = "leaf " + std::to_string(r.leaf) + " slot " + std::to_string(r.slot) +
+                                     " overlaps leaf " + std::to_string(q.leaf) + " slot " + std::to_string(q.slot);
+            if (!(q.b == r.b && q.e == r.e && pair_ok(q, r))) return fail(PSK_E_ALIAS, what);
+            if (adamw_roles && !adamw_pair_ok(q, r)) no_adamw(PSK_E_ALIAS, what + " (AdamW's slots are distinct)");
         }
         if (r.e > max_end) { max_end = r.e; prev = i; }
     }
@@ -509,8 +524,7 @@ extern "C" psk_status psk_adamw_step(const psk_tree* tree, const psk_adamw_hp* h
     const double v[5] = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
     for (double x : v)
         if (!std::isfinite(x)) return fail(PSK_E_SHAPE, "hyperparameters must be finite");
-    if (tree->n_slots != 4 && tree->n_slots != 7)
-        return fail(PSK_E_SHAPE, "an AdamW tree has 4 slots (theta, g, m, v) or 7 (plus theta', m', v')");
+    if (tree->adamw_status != PSK_OK) return fail(tree->adamw_status, tree->adamw_refusal);
     if (tree->chunks.empty()) return PSK_OK;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != tree->device)
@@ -555,8 +569,7 @@ extern "C" psk_status psk_adamw_step_config(const psk_tree* tree, const psk_adam
     double lr = 0.0;
     psk_status st = schedule_lr(cfg, &lr);
     if (st != PSK_OK) return st;
-    if (tree->n_slots != 4 && tree->n_slots != 7)
-        return fail(PSK_E_SHAPE, "an AdamW tree has 4 slots (theta, g, m, v) or 7 (plus theta', m', v')");
+    if (tree->adamw_status != PSK_OK) return fail(tree->adamw_status, tree->adamw_refusal);
     if (tree->chunks.empty()) return PSK_OK;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != tree->device)

@@ -278,13 +278,15 @@ typedef struct psk_leaf {
  * into chunks of PSK_TREE_CHUNK elements (the last one shorter); chunk
  * starts are multiples of 8 elements within a leaf, so 16-byte vector
  * accesses stay inside one leaf.  The tables are uploaded to the current
- * device once.  Slot dtypes apply to every leaf; 1 to 8 slots.  A tree of 4
- * or 7 slots has AdamW's slot roles (theta, g, m, v [, theta', m', v']): its
- * slots are distinct buffers, except that an output may be the same buffer as
- * its own input.  Other trees may repeat a buffer across slots of one leaf
- * (same storage type) but never overlap partly.  Refuses: NULL pointers of
- * non-empty leaves, negative numel, misaligned pointers, overlaps as above
- * (PSK_E_ALIAS). */
+ * device once.  Slot dtypes apply to every leaf; 1 to 8 slots.  A leaf may
+ * repeat a buffer across its slots when they share a storage type; buffers
+ * never overlap partly, and leaves never share memory.  Refuses: NULL
+ * pointers of non-empty leaves, negative numel, misaligned pointers,
+ * overlaps as above (PSK_E_ALIAS).  AdamW's slot roles (theta, g, m, v
+ * [, theta', m', v']: 4 or 7 slots, m and v of one storage type, each output
+ * of its input's type, every slot its own buffer except an output over its
+ * own input) are not required here: psk_adamw_step refuses a tree without
+ * them, with the reason. */
 #define PSK_TREE_CHUNK 4096
 psk_status psk_tree_create(const psk_leaf* leaves, int32_t n_leaves, int32_t n_slots,
                            const int32_t* slot_dtypes, psk_tree** out);
@@ -325,7 +327,10 @@ typedef struct psk_adamw_hp {
  * Slot dtypes: theta and g each f32 or bf16; m and v the same type, f32 or
  * bf16; outputs the type of their input.  Arithmetic is f32; theta' is
  * rounded once to theta's storage; m' and v' are stored, and theta' reads
- * the stored values.  Refuses t < 1, non-finite hyperparameters. */
+ * the stored values.  Refuses t < 1, non-finite hyperparameters, and a
+ * tree without AdamW's slot roles (see psk_tree_create): PSK_E_SHAPE for a
+ * slot count other than 4 or 7, PSK_E_TYPE for storage types, PSK_E_ALIAS
+ * for a buffer in two slots other than an output over its own input. */
 psk_status psk_adamw_step(const psk_tree* tree, const psk_adamw_hp* hp, void* hip_stream);
 
 /* Learning-rate schedules (presk language reference, section "Configuration

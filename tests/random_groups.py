@@ -97,3 +97,52 @@ def random_group(rng: random.Random):
     for m in cand[:rng.randint(0, 2)]:
         extras.append((m, rng.choice(["f32", "bf16"])))
     return nodes, inputs, out_shape, out_dtype, extras
+
+
+def random_tree_group(rng: random.Random):
+    """A random group of the same operations to map over a parameter tree:
+    rank-1 inputs (one element per leaf element, f32 or bf16) and rank-0
+    inputs (one value for the tree, f32).  (nodes, inputs, out_dtype,
+    extras [(node, dtype)])"""
+    inputs, nodes = [], []
+    n_el = rng.randint(1, 3)
+    for k in range(n_el + rng.randint(0, 2)):
+        inputs.append(((1,), rng.choice(["f32", "bf16"])) if k < n_el else ((), "f32"))
+        nodes.append(Node("input", (), None, k))
+    values = list(range(len(nodes)))
+    unread = set(values)
+    members = []
+
+    def pick():
+        if unread and rng.random() < 0.6:
+            return rng.choice(sorted(unread))
+        return rng.choice(values)
+
+    def add(op, args):
+        idx = len(nodes)
+        nodes.append(Node(op, tuple(args)))
+        for a in args:
+            unread.discard(a)
+        unread.add(idx)
+        values.append(idx)
+        members.append(idx)
+        return idx
+
+    for _ in range(rng.randint(1, 12)):
+        r = rng.random()
+        if r < 0.1:
+            add("select", [pick(), pick(), pick()])
+        elif r < 0.4:
+            add(rng.choice(UNARY), [pick()])
+        else:
+            add(rng.choice(BINARY), [pick(), pick()])
+    while len(unread) > 1:
+        a, b = sorted(unread)[:2]
+        add(rng.choice(["add", "mul", "max"]), [a, b])
+    if len(nodes) - 1 not in members or all(nodes[a].op == "input" and inputs[nodes[a].iparam][0] == ()
+                                            for a in nodes[-1].args):
+        add("add", [len(nodes) - 1, 0])         # input 0 is per element
+    cand = [m for m in members if m != len(nodes) - 1]
+    rng.shuffle(cand)
+    extras = [(m, rng.choice(["f32", "bf16"])) for m in cand[:rng.randint(0, 2)]]
+    return nodes, inputs, rng.choice(["f32", "bf16"]), extras

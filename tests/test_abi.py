@@ -258,9 +258,9 @@ def test_tree_refusals_without_device(lib):
     with pytest.raises(P.PskError) as ei:   # two leaves overlap
         P.psk_tree_create([(8, [1024, 2048, 3072, 4096]), (8, [1040, 8192, 9216, 10240])], ["f32"] * 4)
     assert ei.value.status == P.PSK_E_ALIAS
-    with pytest.raises(P.PskError) as ei:
-        P.psk_tree_create([(8, [1024, 2048, 3072, 4096])], ["f32", "f32", "f32", "bf16"])
-    assert ei.value.status == P.PSK_E_TYPE
+    with pytest.raises(P.PskError) as ei:   # one buffer in two slots of different storage types
+        P.psk_tree_create([(8, [1024, 2048, 1024, 4096])], ["f32", "f32", "bf16", "f32"])
+    assert ei.value.status == P.PSK_E_ALIAS
 
 
 def _isa(code: bytes, tmp_path, name):

@@ -130,9 +130,19 @@ def test_empty_leaves_and_empty_tree():
 
 def test_refusals_on_device():
     state = configs.adamw_state([(16,)], device=DEV, seed=4)[0]
-    with pytest.raises(P.PskError) as ei:
-        P.Tree([[state["theta"], state["grad"], state["m"], state["theta"]]])   # v is theta
-    assert ei.value.status == P.PSK_E_ALIAS
+    # trees are generic: AdamW's slot roles are checked by the step, which
+    # refuses before any launch and leaves every buffer as it was
+    before = snapshot([state])
+    for slots, status in [([state["theta"], state["grad"], state["m"], state["theta"]], P.PSK_E_ALIAS),  # v is theta
+                          ([state["theta"], state["grad"], state["m"], state["v"].to(torch.bfloat16)], P.PSK_E_TYPE),
+                          ([state["theta"], state["grad"], state["m"]], P.PSK_E_SHAPE)]:
+        t = P.Tree([slots])
+        with pytest.raises(P.PskError) as ei:
+            t.adamw_step(*hp_args())
+        assert ei.value.status == status
+    torch.cuda.synchronize()
+    for k in ("theta", "grad", "m", "v"):
+        assert_bits(to_np(state[k]), before[0][k], f"{k} after a refused step")
     tree = P.Tree([[state["theta"], state["grad"], state["m"], state["v"]]])
     with pytest.raises(P.PskError) as ei:
         tree.adamw_step(*hp_args(t=0))

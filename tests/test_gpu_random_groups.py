@@ -71,3 +71,42 @@ def test_random_exact_groups_bit_for_bit(chunk):
         for (m, r), x in zip(refx, xs):
             ok = same_bits(to_np(x), r)
             assert ok.all(), f"{what}: extra {m} differs at {int((~ok).sum())} of {ok.size}"
+
+
+@pytest.mark.parametrize("chunk", range(3))
+def test_random_exact_tree_groups_bit_for_bit(chunk):
+    """The same operations mapped over random trees (ragged leaves, one
+    launch): every leaf's outputs equal the oracle's evaluation of that
+    leaf, bit for bit."""
+    from tests.random_groups import random_tree_group
+    rng = random.Random(2000 + chunk)
+    gen = torch.Generator().manual_seed(99 + chunk)
+    for trial in range(10):
+        nodes, inputs, dt, extras = random_tree_group(rng)
+        n_el = sum(1 for s, _ in inputs if s == (1,))
+        sizes = [rng.choice([1, 3, 7, 8, 100, 4095, 4096, 4097, 20000]) for _ in range(rng.randint(1, 6))]
+        leaves = []
+        for n in sizes:
+            slots = [make_input((n,), t, gen, False) for s, t in inputs if s == (1,)]
+            slots.append(torch.full((n,), float("nan"), dtype=TD[dt], device=DEV))
+            slots += [torch.full((n,), float("nan"), dtype=TD[xdt], device=DEV) for _, xdt in extras]
+            leaves.append(slots)
+        scalars = [None if s == (1,) else make_input((), t, gen, False) for s, t in inputs]
+        g = P.Group(nodes, inputs, (1,), dt, root=len(nodes) - 1, tree=True,
+                    extras=[(m, (1,), xdt) for m, xdt in extras])
+        tree = P.Tree(leaves)
+        in_slots = [k if s == (1,) else -1 for k, (s, _) in enumerate(inputs)]
+        outs = [n_el + j for j in range(1 + len(extras))]
+        g.run_tree(tree, in_slots, outs[0] if not extras else outs, scalars)
+        torch.cuda.synchronize()
+        sc_np = [None if t is None else to_np(t) for t in scalars]
+        for li, (n, slots) in enumerate(zip(sizes, leaves)):
+            ins = [sc_np[k] if s == () else to_np(slots[k]) for k, (s, _) in enumerate(inputs)]
+            refx = [(m, np.zeros((n,), np.float32 if xdt == "f32" else np.uint16)) for m, xdt in extras]
+            ref = oracle.eval_group(nodes, ins, (n,), OD[dt], root=len(nodes) - 1, extras=refx)
+            what = f"chunk {chunk} trial {trial} leaf {li} (n={n}): inputs {inputs} extras {extras}"
+            ok = same_bits(to_np(slots[n_el]), ref)
+            assert ok.all(), f"{what}: root differs at {int((~ok).sum())} of {ok.size}"
+            for j, (m, r) in enumerate(refx):
+                ok = same_bits(to_np(slots[n_el + 1 + j]), r)
+                assert ok.all(), f"{what}: extra {m} differs at {int((~ok).sum())} of {ok.size}"
