@@ -146,3 +146,74 @@ def random_tree_group(rng: random.Random):
     rng.shuffle(cand)
     extras = [(m, rng.choice(["f32", "bf16"])) for m in cand[:rng.randint(0, 2)]]
     return nodes, inputs, rng.choice(["f32", "bf16"]), extras
+
+
+def random_row_group(rng: random.Random):
+    """A random row group: the exact element operations (sqrt of a magnitude
+    instead of sqrt, no difference of a value with itself, so that no NaN
+    and no signed zero decides a maximum) and row maxima, whose result does
+    not depend on the order the lanes combine in.  Row values feed later
+    members (one or more reduction phases); stored extras may be element
+    values or row values.  (nodes, inputs, out_shape, out_dtype, extras
+    [(node, shape, dtype)])"""
+    rank = rng.randint(1, 3)
+    cols = rng.choice([3, 64, 100, 129, 1000, 4096, 40000])
+    lead = [rng.choice([1, 2, 5, 17]) for _ in range(rank - 1)]
+    out_shape = tuple(lead + [cols])
+    row_shape = tuple(lead + [1])
+    out_dtype = rng.choice(["f32", "bf16"])
+    inputs, nodes, is_row = [], [], []
+    for k in range(rng.randint(1, 3)):
+        shape = _input_shape(rng, out_shape) if k else tuple(out_shape)
+        inputs.append((shape, rng.choice(["f32", "bf16"])))
+        nodes.append(Node("input", (), None, k))
+        is_row.append(len(shape) == 0 or shape[-1] == 1)
+    if rng.random() < 0.5:
+        nodes.append(Node("const", (), float(rng.choice([0.5, -3.0, 1.25, 7.0]))))
+        is_row.append(True)
+    values = list(range(len(nodes)))
+    unread = set(values)
+    members = []
+
+    def pick(elem=False):
+        pool = [v for v in (sorted(unread) if unread and rng.random() < 0.6 else values) if not elem or not is_row[v]]
+        return rng.choice(pool or [0])
+
+    def add(op, args):
+        idx = len(nodes)
+        nodes.append(Node(op, tuple(args)))
+        is_row.append(op == "row_max" or all(is_row[a] for a in args))
+        for a in args:
+            unread.discard(a)
+        unread.add(idx)
+        values.append(idx)
+        members.append(idx)
+        return idx
+
+    for _ in range(rng.randint(2, 14)):
+        r = rng.random()
+        if r < 0.2:
+            add("row_max", [pick(elem=True)])
+        elif r < 0.3:
+            add("select", [pick(), pick(), pick()])
+        elif r < 0.5:
+            add(rng.choice(["neg", "abs", "sqrtabs", "pow2"]), [pick()])
+        else:
+            a = pick()
+            b = pick()
+            op = rng.choice(BINARY)
+            if a == b and op == "sub":
+                op = "add"
+            add(op, [a, b])
+    while len(unread) > 1:
+        a, b = sorted(unread)[:2]
+        add(rng.choice(["add", "mul", "max"]), [a, b])
+    root = len(nodes) - 1
+    if root not in members or is_row[root]:
+        root = add("add", [root, 0])
+    extras = []
+    cand = [m for m in members if m != root]
+    rng.shuffle(cand)
+    for m in cand[:rng.randint(0, 2)]:
+        extras.append((m, row_shape if is_row[m] else out_shape, rng.choice(["f32", "bf16"])))
+    return nodes, inputs, out_shape, out_dtype, extras

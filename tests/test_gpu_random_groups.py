@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_util import to_np
+from tests.gpu_util import assert_bf16_close, to_np
 from tests.random_groups import random_group
 
 P = pytest.importorskip("elementwise_reduction_groups_amd")
@@ -110,3 +110,37 @@ def test_random_exact_tree_groups_bit_for_bit(chunk):
             for j, (m, r) in enumerate(refx):
                 ok = same_bits(to_np(slots[n_el + 1 + j]), r)
                 assert ok.all(), f"{what}: extra {m} differs at {int((~ok).sum())} of {ok.size}"
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_random_exact_row_groups_bit_for_bit(chunk):
+    """Random row groups of the exact operations and row maxima (register,
+    tiled and persistent row kernels, one or more reduction phases, row
+    values stored at [rows, 1]): a maximum does not depend on the order the
+    lanes combine in, so the GPU and the oracle agree bit for bit (bf16
+    results within one ulp: a quotient by a row statistic that only bf16
+    results read is the row's reciprocal times the element)."""
+    from tests.random_groups import random_row_group
+    rng = random.Random(3000 + chunk)
+    gen = torch.Generator().manual_seed(55 + chunk)
+    for trial in range(10):
+        nodes, inputs, shape, dt, extras = random_row_group(rng)
+        tensors = []
+        for s, t in inputs:
+            x = make_input(s, t, gen, False)
+            tensors.append(torch.where(x == 0, torch.ones_like(x), x))        # no exact zeros
+        g = P.Group(nodes, inputs, shape, dt, root=len(nodes) - 1, extras=extras)
+        out = torch.full(shape, float("nan"), dtype=TD[dt], device=DEV)
+        xs = [torch.full(xsh, float("nan"), dtype=TD[xdt], device=DEV) for _, xsh, xdt in extras]
+        g.run(tensors, out, extra_outs=xs or None)
+        torch.cuda.synchronize()
+        refx = [(m, np.zeros(xsh, np.float32 if xdt == "f32" else np.uint16)) for m, xsh, xdt in extras]
+        ref = oracle.eval_group(nodes, [to_np(t) for t in tensors], shape, OD[dt], root=len(nodes) - 1, extras=refx)
+        what = (f"chunk {chunk} trial {trial}: kind {g.info.kind} shape {shape} {dt} inputs {inputs} "
+                f"extras {extras} ops {[n.op for n in nodes]}")
+        for name, got, r in [("root", to_np(out), ref)] + [(f"extra {m}", to_np(x), r) for (m, r), x in zip(refx, xs)]:
+            if got.dtype == np.uint16:
+                assert_bf16_close(got, r, f"{what}: {name}")
+            else:
+                ok = same_bits(got, r)
+                assert ok.all(), f"{what}: {name} differs at {int((~ok).sum())} of {ok.size}"
