@@ -86,6 +86,55 @@ int main(void)
     CHECK(psk_partition_ex(8, nodes, types, out, PSK_PARTITION_ROWS, group_of, is_root, &n_groups) == PSK_OK);
     CHECK(n_groups == 1 && is_root[7] == 1 && group_of[0] == -1 && group_of[2] == group_of[7]);
 
+    /* random damage to a valid descriptor: every request is either accepted
+     * or refused with a status and a message; nothing else happens */
+    {
+        uint32_t seed = 12345u;
+        psk_node pool[32];
+        psk_tensor_desc ins[4], xout[2];
+        int32_t xroot[2];
+        int accepted = 0, refused = 0;
+        for (int trial = 0; trial < 3000; ++trial) {
+            memcpy(pool, nodes, sizeof nodes);
+            for (int i = 8; i < 32; ++i) pool[i] = node(PSK_OP_ADD, i - 1, 0, 0.0f, 0);
+            ins[0] = in; ins[1] = tensor(1, 64, 0, PSK_BF16); ins[2] = tensor(0, 0, 0, PSK_F32);
+            ins[3] = tensor(2, 8, 64, PSK_U8);
+            psk_group_desc q = d;
+            q.nodes = pool; q.inputs = ins; q.n_inputs = 1; q.root = 7; q.n_nodes = 8; q.flags = 0;
+            int n_damage = 1 + (int)((seed >> 8) % 3);
+            for (int k = 0; k < n_damage; ++k) {
+                seed = seed * 1664525u + 1013904223u;
+                int i = (int)((seed >> 4) % 32);
+                int what = (int)((seed >> 16) % 10);
+                int v = (int)((seed >> 20) % 70) - 5;
+                switch (what) {
+                case 0: pool[i].op = v; break;
+                case 1: pool[i].a = v; break;
+                case 2: pool[i].b = v; break;
+                case 3: q.root = v % 40; break;
+                case 4: q.n_nodes = 1 + (int)((seed >> 9) % 32); q.root = q.n_nodes - 1; break;
+                case 5: q.n_inputs = (int)((seed >> 9) % 5); break;
+                case 6: ins[(seed >> 9) % 4].rank = v % 7; break;
+                case 7: ins[(seed >> 9) % 4].shape[(seed >> 12) % 2] = v * 13; break;
+                case 8: q.flags = (uint32_t)((seed >> 9) % 4); break;
+                default:
+                    xroot[0] = v % 10; xroot[1] = (v + 3) % 10;
+                    xout[0] = tensor(2, 8, 64, (int)((seed >> 9) % 3)); xout[1] = tensor(2, 8, 1, PSK_F32);
+                    q.n_extra = 1 + (int)((seed >> 11) % 2); q.extra_root = xroot; q.extra_out = xout;
+                }
+            }
+            char buf[64];
+            size_t n = 0;
+            psk_status st = psk_group_source(&q, buf, sizeof buf, &n);
+            if (st == PSK_OK) { CHECK(n > sizeof buf && strlen(buf) == sizeof buf - 1); ++accepted; }
+            else {
+                CHECK(st > PSK_OK && strlen(psk_last_error()) > 0);
+                ++refused;
+            }
+        }
+        CHECK(accepted > 100 && refused > 1000);
+    }
+
     /* tree plan: prefix offsets and whole chunks */
     int64_t numel[3] = {5, 4096 * 3 + 1, 0}, n_chunks = 0, off[4];
     CHECK(psk_tree_plan(numel, 3, &n_chunks, off, NULL, NULL, NULL) == PSK_OK);
