@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libpsk_fused.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
-HOST_SOURCES = ["api.cpp", "validate.cpp", "emit.cpp", "jit.cpp", "partition.cpp"]
+HOST_SOURCES = ["api.cpp", "validate.cpp", "plan.cpp", "emit.cpp", "jit.cpp", "partition.cpp"]
 HIP_SOURCES = ["adamw.hip"]
 
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",

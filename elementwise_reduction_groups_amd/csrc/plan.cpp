@@ -1,0 +1,198 @@
+// Launch planning: which kernel shape a validated group gets (pointwise,
+// register rows, tiled rows, tree-mapped) and its launch layout (vector
+// width, lanes a row, workgroup size, tiles and caches, persistent rows,
+// XCD mapping), from the shapes alone unless PSK_LAYOUT overrides a choice.
+// Every choice here changes no element that is computed; the ones that
+// change a reduction's bracketing are listed with the override keys below.
+//
+// Host-only: nothing here calls HIP.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "psk_internal.h"
+
+namespace psk {
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Layout overrides for measurement, "key=value" pairs separated by commas in
+// PSK_LAYOUT (an unknown or out-of-range value falls back to the default):
+//   every kernel: nt=0|1 (nontemporal accesses), xcd=0|1 (XCD-contiguous
+//     block mapping), block=64..1024 (threads per workgroup);
+//   tree kernels: tper=4|8|16 (elements per thread);
+//   row kernels: epl (elements of output a lane aims for), lanes=16|32|
+//     64..1024, epmax (most elements a lane holds before the tiled kernel
+//     takes over, default 32), persist=k (k persistent workgroups a CU),
+//     tiled=1 (force the tiled kernel);
+//   tiled kernel: lanes=64..1024, tn (vectors a lane per tile), tcache=0|1
+//     (cached loads before the last phase), rc / lc (tiles kept in
+//     registers / LDS), wpe / wmin (most / fewest waves a SIMD).
+// A layout never changes which elements are computed; lanes, epl, epmax,
+// tiled and tn change a reduction's bracketing (within tolerance), the
+// others change no bit.
+static int layout_value(const char* key, int dflt)
+{
+    const char* env = std::getenv("PSK_LAYOUT");
+    if (!env) return dflt;
+    std::string s(env), k = std::string(key) + "=";
+    size_t pos = 0;
+    while (pos < s.size()) {
+        size_t end = s.find(',', pos);
+        if (end == std::string::npos) end = s.size();
+        std::string item = s.substr(pos, end - pos);
+        if (item.compare(0, k.size(), k) == 0) return std::atoi(item.c_str() + k.size());
+        pos = end + 1;
+    }
+    return dflt;
+}
+
+std::string KernelPlan::key() const
+{
+    char b[160];
+    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d c%d w%d m%d p%d r%d s%d", kind, vec, block,
+                  lanes, nv, (int)nt, (int)xcd, (long long)blocks, tiles, (int)tcache, wpe, wmin, persist, rcache, lcache);
+    return b;
+}
+
+KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
+{
+    KernelPlan p;
+    const int V = an.out_dtype == PSK_BF16 ? 8 : 4;
+    p.vec = (allow_vector && an.cols % V == 0) ? V : 1;
+    p.nt = layout_value("nt", 1) != 0;
+    if (an.tree) {
+        // Workgroups of 128 threads; each thread takes `vec` consecutive
+        // elements, the fewest of 4, 8, 16 that move at least 48 bytes.
+        // Measured on the 887M-element Llama tree: an SGD step (6 bytes per
+        // element) runs at 4.6 / 6.4 / 5.3 TB/s with 4 / 8 / 16, AdamW (22
+        // bytes) is fastest with 4.  A chunk splits into whole workgroups;
+        // XCD-contiguous mapping.
+        p.kind = 2;
+        auto size_of = [](psk_dtype d) { return d == PSK_BF16 ? 2 : 4; };
+        int bytes = size_of(an.out_dtype);
+        for (const InputInfo& in : an.inputs)
+            if (in.used && in.kind != InKind::Scalar) bytes += size_of(in.dtype);
+        for (const auto& x : an.extras) bytes += size_of(x.dtype);
+        int per = 4;
+        while (per < 16 && per * bytes < 48) per *= 2;
+        per = layout_value("tper", per);
+        if (per != 4 && per != 8 && per != 16) per = 4;
+        int block = layout_value("block", 128);
+        if (block < 64 || block > 256 || (block & (block - 1))) block = 128;
+        p.vec = per;
+        p.block = block;
+        p.blocks = PSK_TREE_CHUNK / (block * per);   // workgroups per chunk
+        p.xcd = true;
+        return p;
+    }
+    p.xcd = layout_value("xcd", an.row_kind ? 0 : 1) != 0;
+    int block = layout_value("block", 256);
+    if (block < 64 || block > 1024 || (block & (block - 1))) block = 256;
+    if (!an.row_kind) {
+        p.kind = 0;
+        p.block = block;
+        p.blocks = ceil_div(ceil_div(an.numel, p.vec), p.block);
+    } else {
+        p.kind = 1;
+        // about 32 bytes of output per lane (8 f32 or 16 bf16 elements); a
+        // row is 16 lanes (one DPP row) or whole waves; a workgroup of at
+        // least 128 threads, one row per workgroup once a row has 128 lanes
+        const int epl = layout_value("epl", an.out_dtype == PSK_BF16 ? 16 : 8);
+        int64_t want = ceil_div(an.cols, epl);
+        int L = 16;
+        while (L < want && L < 1024) L <<= 1;
+        if (L > 16 && L < 64) L = 64;
+        int Lo = layout_value("lanes", L);
+        if (Lo == 16 || Lo == 32 || (Lo >= 64 && Lo <= 1024 && !(Lo & (Lo - 1)))) L = Lo;
+        p.lanes = L;
+        p.nv = (int)ceil_div(an.cols, (int64_t)L * p.vec);
+        if (L >= 128) block = layout_value("block", 128);
+        if (block < 64 || block > 1024 || (block & (block - 1))) block = 128;
+        p.block = L > block ? L : block;
+        p.rows_per_block = p.block / L;
+        p.blocks = ceil_div(an.rows, p.rows_per_block);
+        // Wide rows: past 32 elements per lane the row no longer lives in
+        // registers.  The tiled kernel gives a row one workgroup, walks it in
+        // tiles of lanes * tn vectors, and every phase walks the row again:
+        // the leading tiles from registers, the rest re-read (from the caches
+        // where they still hold it).
+        // Persistent rows: a few workgroups per CU walk the rows, loading the
+        // next row while the current one is computed (one row per workgroup
+        // of at least 128 lanes).
+        bool online = false;
+        for (int m : an.online_max) online = online || m >= 0;
+        // Persistent rows by default where the column vectors (γ, β: the
+        // same for every row) weigh at least as much as a row's own traffic:
+        // a persistent workgroup loads them once instead of once per row
+        // (LayerNorm with γ and β: 9-14% faster; groups without column
+        // vectors, or with one beside heavier rows, run faster one row per
+        // workgroup).  Enough workgroups for about 16 waves a CU, at least 2.
+        auto esz = [](psk_dtype d) { return d == PSK_BF16 ? 2 : d == PSK_U8 ? 1 : 4; };
+        int64_t colvec = 0, streamed = esz(an.out_dtype);
+        for (const InputInfo& in : an.inputs) {
+            if (!in.used) continue;
+            if (in.kind == InKind::ColVec) colvec += esz(in.dtype);
+            else if (in.kind == InKind::General || in.kind == InKind::Full) streamed += esz(in.dtype);
+        }
+        for (const auto& x : an.extras)
+            if (!x.per_row) streamed += esz(x.dtype);
+        const int persist_dflt = (colvec >= streamed && L >= 256 && p.vec > 1) ? std::max(2, 1024 / L) : 0;
+        const int persist = online ? 0 : layout_value("persist", persist_dflt);
+        if (persist > 0 && p.rows_per_block == 1) {
+            p.persist = persist;
+            p.blocks = std::min<int64_t>(an.rows, (int64_t)256 * persist);
+            p.xcd = false;
+        }
+        if ((int64_t)p.nv * p.vec > layout_value("epmax", 32) || layout_value("tiled", 0)) {
+            p.persist = 0;
+            p.kind = 3;
+            // 512 lanes: two workgroups share a CU, so one loads while the
+            // other reduces (measured faster than 1024 lanes on wide rows)
+            int Lt = layout_value("lanes", 512);
+            if (!(Lt >= 64 && Lt <= 1024 && !(Lt & (Lt - 1)))) Lt = 512;
+            int tn = layout_value("tn", 2);
+            if (tn < 1 || tn > 8) tn = 2;
+            p.lanes = Lt;
+            p.nv = tn;
+            p.tiles = (int)ceil_div(an.cols, (int64_t)Lt * tn * p.vec);
+            p.block = Lt;
+            p.rows_per_block = 1;
+            p.blocks = an.rows;
+            p.tcache = layout_value("tcache", 1) != 0;
+            p.wpe = layout_value("wpe", 0);
+            // registers for two workgroups a CU: at least 2 * Lt / 256 waves
+            // a SIMD (at most 128 registers a lane at 512 lanes)
+            p.wmin = layout_value("wmin", std::min(8, 2 * Lt / 256));
+            if (p.wmin < 0 || p.wmin > 8) p.wmin = 0;
+            // the per-row inputs of the leading tiles stay in registers from
+            // the phase that first loads them to the last: about 64 words a
+            // lane, about half of what a wave may hold when two 512-lane
+            // workgroups share a CU, the rest left for the arithmetic
+            int words = 0;
+            for (const InputInfo& in : an.inputs)
+                if (in.used && (in.kind == InKind::General || in.kind == InKind::Full))
+                    words += tn * std::max(1, p.vec * (in.dtype == PSK_BF16 ? 2 : in.dtype == PSK_U8 ? 1 : 4) / 4);
+            int rc = (words > 0 && an.phases > 0) ? 64 / words : 0;
+            rc = layout_value("rc", rc);
+            p.rcache = std::max(0, std::min(rc, p.tiles));
+            // the next tiles' words in LDS: 64 KiB a workgroup, so two
+            // workgroups (and their reduction scratch) share a CU's 160 KiB
+            int lc = (words > 0 && an.phases > 0) ? (64 << 10) / (words * 4 * Lt) : 0;
+            lc = layout_value("lc", lc);
+            if ((int64_t)lc * words * 4 * Lt > (96 << 10)) lc = (96 << 10) / (words * 4 * Lt);
+            p.lcache = std::max(0, std::min(lc, p.tiles - p.rcache));
+        }
+    }
+    if (p.xcd) {
+        p.per_xcd = ceil_div(p.blocks, 8);
+        p.grid = p.per_xcd * 8;
+    } else {
+        p.per_xcd = p.blocks;
+        p.grid = p.blocks;
+    }
+    return p;
+}
+
+}  // namespace psk
