@@ -252,6 +252,8 @@ clip_finalize_kernel(const double* __restrict__ partials, unsigned n, ClipOut* o
 {
     __shared__ double red[kFinalBlock / 64];
     double s = 0.0;
+    // loads issued ahead, additions in increasing i as before
+#pragma unroll 8
     for (unsigned i = threadIdx.x; i < n; i += kFinalBlock) s += partials[i];
     s = wave_sum(s);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
