@@ -104,11 +104,12 @@ def random_tree_group(rng: random.Random):
     rank-1 inputs (one element per leaf element, f32 or bf16) and rank-0
     inputs (one value for the tree, f32).  (nodes, inputs, out_dtype,
     extras [(node, dtype)])"""
-    inputs, nodes = [], []
+    inputs, nodes, per_tree = [], [], []
     n_el = rng.randint(1, 3)
     for k in range(n_el + rng.randint(0, 2)):
         inputs.append(((1,), rng.choice(["f32", "bf16"])) if k < n_el else ((), "f32"))
         nodes.append(Node("input", (), None, k))
+        per_tree.append(k >= n_el)              # one value for the whole tree
     values = list(range(len(nodes)))
     unread = set(values)
     members = []
@@ -121,6 +122,7 @@ def random_tree_group(rng: random.Random):
     def add(op, args):
         idx = len(nodes)
         nodes.append(Node(op, tuple(args)))
+        per_tree.append(all(per_tree[a] for a in args))
         for a in args:
             unread.discard(a)
         unread.add(idx)
@@ -139,10 +141,9 @@ def random_tree_group(rng: random.Random):
     while len(unread) > 1:
         a, b = sorted(unread)[:2]
         add(rng.choice(["add", "mul", "max"]), [a, b])
-    if len(nodes) - 1 not in members or all(nodes[a].op == "input" and inputs[nodes[a].iparam][0] == ()
-                                            for a in nodes[-1].args):
+    if len(nodes) - 1 not in members or per_tree[-1]:
         add("add", [len(nodes) - 1, 0])         # input 0 is per element
-    cand = [m for m in members if m != len(nodes) - 1]
+    cand = [m for m in members if m != len(nodes) - 1 and not per_tree[m]]
     rng.shuffle(cand)
     extras = [(m, rng.choice(["f32", "bf16"])) for m in cand[:rng.randint(0, 2)]]
     return nodes, inputs, rng.choice(["f32", "bf16"]), extras
