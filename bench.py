@@ -59,8 +59,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; the fused groups shard without "
-                                   "communication (see DESIGN.md), so no multi-GPU figure is produced",
+        print(json.dumps({"error": "this benchmark runs on one GPU only: each GPU would run the same kernels on "
+                                   "its own share of rows, elements or leaves, with no exchange inside the step, "
+                                   "so no multi-GPU figure is produced",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

@@ -73,7 +73,7 @@ typedef enum psk_status {
     PSK_E_ALIGN = 10,        /* a pointer not aligned to its element size */
     PSK_E_ALIAS = 11,        /* an output overlapping an input it may not overlap */
     PSK_E_SHAPE = 12,        /* a negative size, a rank out of range, sizes that disagree */
-    PSK_E_UNSUPPORTED = 13,  /* valid, but outside what this build implements */
+    PSK_E_UNSUPPORTED = 13,  /* valid, but outside what this library implements */
     PSK_E_JIT = 14,          /* hipRTC could not compile the emitted kernel */
     PSK_E_HIP = 15           /* a HIP runtime call failed */
 } psk_status;
