@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=16, help="Llama-style tree depth (16: the explicit leaf list)")
-    ap.add_argument("--reps", type=int, default=11, help="calls per workload in the per-group timing")
+    ap.add_argument("--reps", type=int, default=21, help="calls per workload in the per-group timing")
     ap.add_argument("--no-groups", action="store_true", help="skip the per-group timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=float, default=1.0, help="fraction of the step the oracle times")
