@@ -387,7 +387,8 @@ def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, pro
     tiny_tree = P.Tree([[s["theta"], s["grad"], s["m"], s["v"]] for s in tiny])
     n_tiny = sum(math.prod(s) for s in tiny_shapes)
     add("adamw_tiny_gpt_f32", n_tiny * 28, lambda: tiny_tree.adamw_step(*hp, stream=stream),
-        note="3 MB: launch-latency bound, no HBM target; ms_* cold (cache flushed), us_warm_median back to back")
+        note="3 MB: launch-latency bound, no HBM target; ms_* cold (cache flushed), us_warm_median back to back, "
+             "us_per_step_graph_of_20: 20 steps captured in one HIP graph")
     warm = []
     for k in range(args.reps + 2):
         a = torch.cuda.Event(enable_timing=True)
@@ -399,6 +400,23 @@ def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, pro
         if k >= 2:
             warm.append(a.elapsed_time(b))
     out["adamw_tiny_gpt_f32"]["us_warm_median"] = round(statistics.median(warm) * 1e3, 2)
+    # launch-bound: 20 steps captured in one HIP graph, replayed back to back
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(20):
+            tiny_tree.adamw_step(*hp)
+    torch.cuda.synchronize()
+    per_step = []
+    for k in range(args.reps + 2):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        b.synchronize()
+        if k >= 2:
+            per_step.append(a.elapsed_time(b) / 20)
+    out["adamw_tiny_gpt_f32"]["us_per_step_graph_of_20"] = round(statistics.median(per_step) * 1e3, 2)
 
     # add + RMSNorm + gamma + GELU, bf16 [16384, 4096]
     x, r, g = configs.rmsnorm_inputs(16384, 4096, device=dev)
