@@ -79,6 +79,16 @@ template <> struct Io<float> {
 };
 
 template <> struct Io<__bf16> {
+    // 8 elements, one 16-byte access
+    static __device__ __forceinline__ void load8(const void* p, int64_t e, float* x)
+    {
+        u4v w = __builtin_nontemporal_load((const PSK_GLOBAL u4v*)gbl<unsigned short>(p, e));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            x[2 * q] = __uint_as_float(w[q] << 16);
+            x[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+        }
+    }
     static __device__ __forceinline__ void load4(const void* p, int64_t e, float* x)
     {
         u2v w = __builtin_nontemporal_load((const PSK_GLOBAL u2v*)gbl<unsigned short>(p, e));
@@ -220,20 +230,25 @@ sumsq_kernel(const LeafDev* __restrict__ leaves, const ChunkDev* __restrict__ ch
     const bool vec = (L.flags & 1) != 0;
     double acc = 0.0;
     // squares of f32 values are exact in f64; the sum runs in f64
+    // 16-byte accesses: 4 f32 or 8 bf16 elements
+    constexpr int kW = sizeof(TG) == 2 ? 8 : 4;
 #pragma unroll
-    for (int k = 0; k < kClipPer / 4; ++k) {
-        const int i0 = (k * kClipBlock + (int)threadIdx.x) * 4;
+    for (int k = 0; k < kClipPer / kW; ++k) {
+        const int i0 = (k * kClipBlock + (int)threadIdx.x) * kW;
         const int cnt = ch.count - i0;
-        float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (vec && cnt >= 4) {
-            Io<TG>::load4(L.in[1], ch.start + i0, x);
+        float x[kW];
+#pragma unroll
+        for (int j = 0; j < kW; ++j) x[j] = 0.0f;
+        if (vec && cnt >= kW) {
+            if constexpr (kW == 8) Io<TG>::load8(L.in[1], ch.start + i0, x);
+            else Io<TG>::load4(L.in[1], ch.start + i0, x);
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < kW; ++j)
                 if (j < cnt) x[j] = Io<TG>::load1(L.in[1], ch.start + i0 + j);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc += (double)x[j] * (double)x[j];
+        for (int j = 0; j < kW; ++j) acc += (double)x[j] * (double)x[j];
     }
     acc = wave_sum(acc);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
