@@ -299,3 +299,22 @@ def test_tree_multi_output_refusals_on_device():
     # two slots of one leaf holding one buffer cannot both be outputs
     tree2 = P.Tree([[s["theta"], s["grad"], s["m"], s["v"], s["m"]]])
     refused(P.PSK_E_ALIAS, lambda: grp.run_tree(tree2, [0, 1, 2, 3] + [-1] * 9, [0, 2, 4], scal))
+
+
+def test_add_rmsnorm_gelu_storing_h_in_place_full_size_sampled_rows():
+    """[16384, 4096] bf16, h written in place over the residual, as timed."""
+    R, C = 16384, 4096
+    x, res, gm = configs.rmsnorm_inputs(R, C, device=DEV, seed=91)
+    rows = np.unique(np.concatenate([[0, 1, R - 1], np.random.default_rng(92).integers(0, R, 300)]))
+    idx = torch.from_numpy(rows).to(DEV)
+    xs, rs, gn = to_np(x[idx]), to_np(res[idx]), to_np(gm)
+    g = P.Group(configs.rmsnorm_gelu_dag(EPS), [((R, C), "bf16"), ((R, C), "bf16"), ((C,), "bf16")], (R, C), "bf16",
+                extras=[(configs.RMSNORM_H, (R, C), "bf16")])
+    out = torch.full((R, C), float("nan"), dtype=torch.bfloat16, device=DEV)
+    g.run([x, res, gm], out, extra_outs=[res])
+    torch.cuda.synchronize()
+    rh = np.zeros((len(rows), C), np.uint16)
+    ref = oracle.eval_group(configs.rmsnorm_gelu_dag(EPS), [xs, rs, gn], (len(rows), C), BF16,
+                            extras=[(configs.RMSNORM_H, rh)])
+    assert_bits(to_np(res[idx]), rh, "h full size")
+    assert_bf16_close(to_np(out[idx]), ref, "out full size")

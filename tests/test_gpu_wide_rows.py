@@ -151,3 +151,19 @@ def test_register_cache_changes_no_bit(case, monkeypatch):
     for other in runs[1:]:
         for a, b in zip(runs[0], other):
             np.testing.assert_array_equal(a.view(np.uint8), b.view(np.uint8), f"register cache, {case}")
+
+
+def test_wide_softmax_full_size_sampled_rows():
+    """[8192, 131072] f32 in the layout that is timed (512 lanes, registers
+    and LDS caches)."""
+    R, C = 8192, 131072
+    x = configs.softmax_scores(R, C, device=DEV)
+    g = P.Group(configs.softmax_dag(0.125), [((R, C), "f32")], (R, C), "f32")
+    assert g.info.kind == 3 and g.info.lanes_per_row == 512
+    out = torch.empty_like(x)
+    g.run([x], out)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, R - 1], np.random.default_rng(93).integers(0, R, 40)]))
+    ri = torch.from_numpy(rows).to(DEV)
+    ref = oracle.eval_group(configs.softmax_dag(0.125), [to_np(x[ri])], (len(rows), C), F32)
+    assert_f32_close(to_np(out[ri]), ref, "wide softmax full size")
