@@ -12,10 +12,14 @@ before timing starts.
 softmax: allowed scores read once + every output written once) divided by
 the measured time per step, in GB/s.  The roofline object is for the
 dominant kernel (AdamW), timed with HIP events on the stream it runs on.
-The other three workloads (tiny-GPT AdamW, add+RMSNorm+GELU, 64-node
-chain) are timed one by one with the cache flushed between calls and
-reported under "groups".  The CPU baseline runs the oracle single-threaded
-on the same step (inputs drawn on the host).
+Every other workload (the step's two kernels alone, the clipped cosine
+AdamW, a 22-layer tree, the tiny-GPT tree cold, warm and graph-replayed,
+the tree-mapped SGD and AdamW groups, RMSNorm+GELU with and without h
+stored, LayerNorm with its statistics, the byte-mask, bf16 and wide
+softmaxes (exact and online), the 64-node chain and a device copy) is timed
+on its own with the cache flushed between calls and reported under
+"groups" (median, min, max of --reps calls).  The CPU baseline runs the
+oracle single-threaded on the same step (inputs drawn on the host).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -367,6 +371,17 @@ def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, pro
             out[name]["note"] = note
 
     add("adamw_llama_bf16", adamw_bytes, lambda: tree.adamw_step(*hp, stream=stream))
+    # depth sensitivity: the same architecture at 22 layers (199 leaves, 1 195 991 040 params)
+    if args.layers != 22:
+        shapes22 = [s for _, s in configs.llama_leaves(L=22)]
+        n22 = sum(math.prod(s) for s in shapes22)
+        st22 = configs.adamw_state(shapes22, theta_dtype=torch.bfloat16, grad_dtype=torch.bfloat16,
+                                   mv_dtype=torch.float32, device=dev, seed=configs.SEED_BASE + 12)
+        tree22 = P.Tree([[s["theta"], s["grad"], s["m"], s["v"]] for s in st22])
+        add("adamw_llama22_bf16", 22 * n22, lambda: tree22.adamw_step(*hp, stream=stream),
+            note=f"22 layers: {len(shapes22)} leaves, {n22} params")
+        del tree22, st22
+        torch.cuda.empty_cache()
     add("softmax_causal_f32", softmax_bytes, lambda: softmax.run([scores], probs, stream=stream))
     # the same tree with global-norm clipping and a cosine schedule: a
     # sum-of-squares pass over g (2 B/param more) and the step
