@@ -60,8 +60,12 @@ uint64_t fnv1a(const std::string& s)
     return h;
 }
 
+// A literal f32 operand.  +0.0 is emitted as psk_pz(), a zero the compiler
+// cannot see through: the backend folds 0 - x, when another instruction
+// reads it, into a negation of x, which gives -0 where 0 - (+0) is +0.
 static std::string flit(float x)
 {
+    if (x == 0.0f && !std::signbit(x)) return "psk_pz()";
     if (std::isnan(x)) return "__builtin_nanf(\"\")";
     if (std::isinf(x)) return x > 0 ? "__builtin_inff()" : "(-__builtin_inff())";
     char buf[64];
@@ -218,6 +222,8 @@ __device__ __forceinline__ float psk_divr(float a, float b, float y, bool& bad) 
   bad |= !((fabsf(a) >= 0x1p-86f || zero) && fabsf(a) <= 0x1p87f);
   return zero ? q : fmaf(rem, y, q);
 }
+// +0.0 as an opaque register value (see the emitter's literals)
+__device__ __forceinline__ float psk_pz() { float z = 0.0f; __asm__("" : "+v"(z)); return z; }
 __device__ __forceinline__ float psk_max(float a, float b) { return (a > b) ? a : b; }
 __device__ __forceinline__ float psk_min(float a, float b) { return (a < b) ? a : b; }
 #define PSK_DPP(x, ctl) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (x)), (ctl), 0xF, 0xF, false))

@@ -289,3 +289,40 @@ def test_persistent_row_layout_is_bit_identical(monkeypatch):
         for other in outs[1:]:
             for a, b in zip(outs[0], other):
                 assert_bits(a, b, f"persistent layout, {shape}")
+
+
+def test_signed_zeros_through_fused_expressions():
+    """0 - x is +0 for x = +0 also when another member reads it (the compiler
+    must not turn it into -x), x + 0 is +0 for x = -0: every sign of zero the
+    oracle gives, bit for bit, on both the vector and the element path."""
+    nodes = parse_dag("""
+        %0 = input 0
+        %1 = input 1
+        %2 = const 0x0p+0
+        %3 = sub %2 %0
+        %4 = mul %3 %1
+        %5 = add %3 %1
+        %6 = add %0 %2
+        %7 = mul %6 %1
+        %8 = sub %2 %1
+        %9 = mul %8 %6
+    """)
+    vals = np.array([0.0, -0.0, 1.0, -1.0, 2.5], np.float32)
+    xs, ys = np.meshgrid(vals, np.array([0.0, -0.0, 1.0, -1.0], np.float32))
+    x = np.tile(xs.ravel(), 13)[:256].astype(np.float32)
+    y = np.tile(ys.ravel(), 13)[:256].astype(np.float32)
+    for offset in (0, 1):                       # aligned: vector path; offset by one element: element path
+        bx = torch.zeros(257, device=DEV); by = torch.zeros(257, device=DEV)
+        tx, ty = bx[offset:offset + 256], by[offset:offset + 256]
+        tx.copy_(torch.from_numpy(x)); ty.copy_(torch.from_numpy(y))
+        g = P.Group(nodes, [((256,), "f32"), ((256,), "f32")], (256,), "f32",
+                    extras=[(4, (256,), "f32"), (5, (256,), "f32"), (7, (256,), "f32")])
+        out = torch.full((256,), float("nan"), device=DEV)
+        xo = [torch.full((256,), float("nan"), device=DEV) for _ in range(3)]
+        g.run([tx, ty], out, extra_outs=xo)
+        torch.cuda.synchronize()
+        refx = [(m, np.zeros(256, np.float32)) for m in (4, 5, 7)]
+        ref = oracle.eval_group(nodes, [x, y], (256,), P.PSK_F32, extras=refx)
+        assert_bits(to_np(out), ref, f"(0 - y)(x + 0), offset {offset}")
+        for (m, r), t in zip(refx, xo):
+            assert_bits(to_np(t), r, f"member {m}, offset {offset}")
