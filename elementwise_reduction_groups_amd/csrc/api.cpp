@@ -594,7 +594,13 @@ extern "C" psk_status psk_tree_clip_result(const psk_tree* tree, double* sumsq, 
     if (!tree) return fail(PSK_E_NULL, "tree is NULL");
     ClipOut h = {0.0, 0.0f, 0.0f};
     if (tree->d_clip) {
-        hipError_t e = hipMemcpy(&h, tree->d_clip, sizeof h, hipMemcpyDeviceToHost);
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess || dev != tree->device)
+            return fail(PSK_E_HIP, "the current device is not the device the tree was created on");
+        // the step may have run on a non-blocking stream: wait for the whole device
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipDeviceSynchronize: ") + hipGetErrorString(e));
+        e = hipMemcpy(&h, tree->d_clip, sizeof h, hipMemcpyDeviceToHost);
         if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipMemcpy: ") + hipGetErrorString(e));
     }
     if (sumsq) *sumsq = h.sumsq;

@@ -368,7 +368,9 @@ psk_status psk_adamw_step_config(const psk_tree* tree, const psk_adamw_config* c
 psk_status psk_adamw_lr(const psk_adamw_config* cfg, double* lr);
 
 /* The squared global norm and the f32 factor of the last clipped step on
- * this tree (synchronises the device).  For checks and reporting. */
+ * this tree: waits for the whole device (every stream), then copies them
+ * back.  The current device must be the tree's (else PSK_E_HIP).  Zeros
+ * before any clipped step.  For checks and reporting. */
 psk_status psk_tree_clip_result(const psk_tree* tree, double* sumsq, float* factor);
 
 /* Run a PSK_GROUP_TREE group over every leaf of a tree in one launch
