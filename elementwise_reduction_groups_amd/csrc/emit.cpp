@@ -1379,23 +1379,29 @@ struct Emitter {
             // loads before the last phase, nontemporal ones in it
             cached_loads = p < an.phases && pl.tcache;
             reduce_declare(reds);
-            if (RC > 0) {
-                o << "    #pragma unroll\n";
-                o << "    for (int t = 0; t < " << RC << "; ++t) {\n";
-                tile_body(p, 1);
+            // Odd phases walk the tiles from last to first, so they begin on
+            // the tiles the phase before read last.  The order depends on
+            // the phase alone (the caches hold leading tiles), not on what
+            // is cached.
+            const bool back = pl.alt && p % 2 == 1;
+            auto walk = [&](int lo, int hi, int cached, const char* unroll) {
+                if (lo >= hi) return;
+                o << "    #pragma " << unroll << "\n";
+                if (back)
+                    o << "    for (int t = " << hi - 1 << "; t >= " << lo << "; --t) {\n";
+                else
+                    o << "    for (int t = " << lo << "; t < " << hi << "; ++t) {\n";
+                tile_body(p, cached);
                 o << "    }\n";
-            }
-            if (LC > 0) {
-                o << "    #pragma unroll 1\n";
-                o << "    for (int t = " << RC << "; t < " << RC + LC << "; ++t) {\n";
-                tile_body(p, 2);
-                o << "    }\n";
-            }
-            if (RC + LC < pl.tiles) {
-                o << "    #pragma unroll 1\n";
-                o << "    for (int t = " << RC + LC << "; t < " << pl.tiles << "; ++t) {\n";
-                tile_body(p, 0);
-                o << "    }\n";
+            };
+            if (back) {
+                walk(RC + LC, pl.tiles, 0, "unroll 1");
+                walk(RC, RC + LC, 2, "unroll 1");
+                walk(0, RC, 1, "unroll");
+            } else {
+                walk(0, RC, 1, "unroll");
+                walk(RC, RC + LC, 2, "unroll 1");
+                walk(RC + LC, pl.tiles, 0, "unroll 1");
             }
             if (p < an.phases) {
                 reduce_finish(reds, p);

@@ -28,9 +28,10 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //     tiled=1 (force the tiled kernel);
 //   tiled kernel: lanes=64..1024, tn (vectors a lane per tile), tcache=0|1
 //     (cached loads before the last phase), rc / lc (tiles kept in
-//     registers / LDS), wpe / wmin (most / fewest waves a SIMD).
+//     registers / LDS), wpe / wmin (most / fewest waves a SIMD), alt=0|1
+//     (odd phases walk the tiles last to first).
 // A layout never changes which elements are computed; lanes, epl, epmax,
-// tiled and tn change a reduction's bracketing (within tolerance), the
+// tiled, tn and alt change a reduction's bracketing (within tolerance), the
 // others change no bit.
 static int layout_value(const char* key, int dflt)
 {
@@ -53,7 +54,7 @@ std::string KernelPlan::key() const
     char b[160];
     std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d c%d w%d m%d p%d r%d s%d", kind, vec, block,
                   lanes, nv, (int)nt, (int)xcd, (long long)blocks, tiles, (int)tcache, wpe, wmin, persist, rcache, lcache);
-    return b;
+    return kind == 3 ? std::string(b) + (alt ? " a1" : " a0") : std::string(b);
 }
 
 KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
@@ -161,6 +162,9 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
             p.rows_per_block = 1;
             p.blocks = an.rows;
             p.tcache = layout_value("tcache", 1) != 0;
+            // a phase that walks the row backwards starts on the tiles the
+            // previous phase read last, which the caches still hold
+            p.alt = layout_value("alt", 1) != 0;
             p.wpe = layout_value("wpe", 0);
             // registers for two workgroups a CU: at least 2 * Lt / 256 waves
             // a SIMD (at most 128 registers a lane at 512 lanes)
