@@ -1394,14 +1394,16 @@ struct Emitter {
                 tile_body(p, cached);
                 o << "    }\n";
             };
+            const std::string mu = "unroll " + std::to_string(pl.munroll);
+            const std::string lu = "unroll " + std::to_string(pl.lunroll);
             if (back) {
-                walk(RC + LC, pl.tiles, 0, "unroll 1");
-                walk(RC, RC + LC, 2, "unroll 1");
+                walk(RC + LC, pl.tiles, 0, mu.c_str());
+                walk(RC, RC + LC, 2, lu.c_str());
                 walk(0, RC, 1, "unroll");
             } else {
                 walk(0, RC, 1, "unroll");
-                walk(RC, RC + LC, 2, "unroll 1");
-                walk(RC + LC, pl.tiles, 0, "unroll 1");
+                walk(RC, RC + LC, 2, lu.c_str());
+                walk(RC + LC, pl.tiles, 0, mu.c_str());
             }
             if (p < an.phases) {
                 reduce_finish(reds, p);

@@ -29,7 +29,8 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //   tiled kernel: lanes=64..1024, tn (vectors a lane per tile), tcache=0|1
 //     (cached loads before the last phase), rc / lc (tiles kept in
 //     registers / LDS), wpe / wmin (most / fewest waves a SIMD), alt=0|1
-//     (odd phases walk the tiles last to first).
+//     (odd phases walk the tiles last to first), mu / lu (unroll of the
+//     loops over tiles read from memory / kept in LDS).
 // A layout never changes which elements are computed; lanes, epl, epmax,
 // tiled, tn and alt change a reduction's bracketing (within tolerance), the
 // others change no bit.
@@ -54,7 +55,9 @@ std::string KernelPlan::key() const
     char b[160];
     std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d c%d w%d m%d p%d r%d s%d", kind, vec, block,
                   lanes, nv, (int)nt, (int)xcd, (long long)blocks, tiles, (int)tcache, wpe, wmin, persist, rcache, lcache);
-    return kind == 3 ? std::string(b) + (alt ? " a1" : " a0") : std::string(b);
+    return kind == 3 ? std::string(b) + (alt ? " a1" : " a0") + " u" + std::to_string(munroll) + " y" +
+                           std::to_string(lunroll)
+                     : std::string(b);
 }
 
 KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
@@ -165,6 +168,12 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
             // a phase that walks the row backwards starts on the tiles the
             // previous phase read last, which the caches still hold
             p.alt = layout_value("alt", 1) != 0;
+            // two memory tiles a loop iteration: the second tile's loads are
+            // issued before the first tile's arithmetic
+            p.munroll = layout_value("mu", 2);
+            if (p.munroll < 1 || p.munroll > 8) p.munroll = 2;
+            p.lunroll = layout_value("lu", 1);
+            if (p.lunroll < 1 || p.lunroll > 8) p.lunroll = 1;
             p.wpe = layout_value("wpe", 0);
             // registers for two workgroups a CU: at least 2 * Lt / 256 waves
             // a SIMD (at most 128 registers a lane at 512 lanes)
