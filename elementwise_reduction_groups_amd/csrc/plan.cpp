@@ -168,10 +168,12 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
             // a phase that walks the row backwards starts on the tiles the
             // previous phase read last, which the caches still hold
             p.alt = layout_value("alt", 1) != 0;
-            // two memory tiles a loop iteration: the second tile's loads are
-            // issued before the first tile's arithmetic
-            p.munroll = layout_value("mu", 2);
-            if (p.munroll < 1 || p.munroll > 8) p.munroll = 2;
+            // two memory tiles a loop iteration for f32 rows: the second
+            // tile's loads are issued before the first tile's arithmetic
+            // (bf16 rows, whose widening takes more registers, would spill)
+            const int mu_dflt = an.out_dtype == PSK_F32 ? 2 : 1;
+            p.munroll = layout_value("mu", mu_dflt);
+            if (p.munroll < 1 || p.munroll > 8) p.munroll = mu_dflt;
             p.lunroll = layout_value("lu", 1);
             if (p.lunroll < 1 || p.lunroll > 8) p.lunroll = 1;
             p.wpe = layout_value("wpe", 0);

@@ -98,7 +98,7 @@ struct KernelPlan {
     int rcache = 0;          // tiled row kernel: leading tiles whose per-row inputs stay in registers
     int lcache = 0;          // tiled row kernel: the tiles after those whose per-row inputs stay in LDS
     bool alt = true;         // tiled row kernel: odd phases walk the tiles last to first
-    int munroll = 2;         // tiled row kernel: unroll of the loop over tiles read from memory
+    int munroll = 1;         // tiled row kernel: unroll of the loop over tiles read from memory
     int lunroll = 1;         // tiled row kernel: unroll of the loop over tiles kept in LDS
     int wpe = 0;             // tiled row kernel: at most this many waves per SIMD (0: no limit)
     int wmin = 0;            // tiled row kernel: registers for at least this many waves per SIMD (0: any)

@@ -411,6 +411,27 @@ def test_wide_rows_take_the_tiled_kernel(lib, tmp_path):
         asm, notes = _isa(P.psk_group_code_object(d), tmp_path, f"wide{cols}")
         assert re.search(r"\.private_segment_fixed_size:\s+0\b", notes)    # no spills
         assert not re.search(r"v_pk_(fma|mul|add)_f32", asm)
+    # the other wide row groups (several inputs, byte masks, extra outputs,
+    # the online normalizer) keep their register caches without spilling
+    eps, W = C.f32(1e-5), 70000
+    others = {
+        "ln": P.GroupDesc(C.layernorm_dag(eps), [((4, W), "bf16"), ((W,), "bf16"), ((W,), "bf16")], (4, W), "bf16",
+                          root=C.LAYERNORM_ROOT,
+                          extras=[(C.LAYERNORM_MEAN, (4, 1), "f32"), (C.LAYERNORM_RSTD, (4, 1), "f32")]),
+        "rms_f32": P.GroupDesc(C.rmsnorm_gelu_dag(eps), [((4, W), "f32"), ((4, W), "f32"), ((W,), "f32")], (4, W), "f32"),
+        "rms_h": P.GroupDesc(C.rmsnorm_gelu_dag(eps), [((4, W), "bf16"), ((4, W), "bf16"), ((W,), "bf16")], (4, W),
+                             "bf16", extras=[(C.RMSNORM_H, (4, W), "bf16")]),
+        "masked_f32": P.GroupDesc(C.softmax_masked_dag(0.125), [((4, W), "f32"), ((4, W), "u8")], (4, W), "f32"),
+        "masked_bf16": P.GroupDesc(C.softmax_masked_dag(0.125), [((4, W), "bf16"), ((4, W), "u8")], (4, W), "bf16"),
+        "online_bf16": P.GroupDesc(C.softmax_dag(0.125), [((4, 131072), "bf16")], (4, 131072), "bf16",
+                                   flags=P.PSK_GROUP_ONLINE),
+    }
+    for name, d in others.items():
+        g = P.psk_group_create(d)
+        assert P.psk_group_get_info(g).kind == 3, name
+        P.psk_group_destroy(g)
+        _, notes = _isa(P.psk_group_code_object(d), tmp_path, f"wide_{name}")
+        assert re.search(r"\.private_segment_fixed_size:\s+0\b", notes), name
     # rows past 2^30 columns are refused
     _refused(_desc("%0 = input 0\n%1 = row_max %0\n%2 = sub %0 %1\n", [((1, (1 << 30) + 8), "f32")],
                    (1, (1 << 30) + 8)), P.PSK_E_UNSUPPORTED)
