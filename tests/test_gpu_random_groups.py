@@ -159,3 +159,18 @@ def test_random_exact_row_groups_bit_for_bit(chunk):
             else:
                 ok = same_bits(got, r)
                 assert ok.all(), f"{what}: {name} differs at {int((~ok).sum())} of {ok.size}"
+
+
+@pytest.mark.parametrize("layout,chunk", [
+    ("tiled=1,lanes=128,tn=1,rc=1,lc=1", 10),          # registers, LDS and memory tiles; unrolled memory loop
+    ("tiled=1,lanes=256,tn=2,rc=2,lc=2,mu=3", 11),     # an unroll that leaves a remainder
+    ("tiled=1,lanes=128,tn=1,rc=0,lc=0,alt=0", 12),    # every tile from memory, every phase forwards
+])
+def test_random_exact_row_groups_through_the_tiled_kernel(layout, chunk, monkeypatch):
+    """The same random exact row groups, every one forced through the tiled
+    wide-row kernel with small tiles, so that rows of a few hundred columns
+    already span several tiles, the three loops (register, LDS and memory
+    tiles) and the walks in both directions: bit for bit against the
+    oracle, as above."""
+    monkeypatch.setenv("PSK_LAYOUT", layout)
+    test_random_exact_row_groups_bit_for_bit(chunk)
