@@ -530,3 +530,15 @@ def test_persistent_rows_where_column_vectors_weigh(lib):
     rms = P.psk_group_source(P.GroupDesc(C.rmsnorm_gelu_dag(eps), [((R, N), "bf16"), ((R, N), "bf16"), ((N,), "bf16")],
                                          (R, N), "bf16"))
     assert persistent not in sm and persistent not in rms
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every call raises; nothing falls back to
+    another implementation."""
+    monkeypatch.setattr(P, "_lib", None)
+    monkeypatch.setattr(P, "LIB_PATH", str(tmp_path / "libpsk_fused.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        P.lib()
+    from synth import configs as C
+    with pytest.raises(RuntimeError, match="not built"):
+        P.Group(C.softmax_dag(0.125), [((4, 8), "f32")], (4, 8), "f32")
