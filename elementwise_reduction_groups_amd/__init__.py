@@ -442,6 +442,28 @@ def _stream_handle(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _numel(shape) -> int:
+    n = 1
+    for d in shape:
+        n *= int(d)
+    return n
+
+
+def _check_buffer(t, numel: int, code: int, what: str, dev: int):
+    """A tensor for one of a group's buffers: its element count and storage
+    type, on the current device."""
+    if t.numel() != numel:
+        raise ValueError(f"{what}: {t.numel()} elements where the group's buffer has {numel}")
+    try:
+        tcode = _dtype_code(str(t.dtype))
+    except ValueError:
+        tcode = None
+    if tcode != code:
+        raise ValueError(f"{what}: {t.dtype} does not hold the group's storage type {('f32', 'bf16', 'u8')[code]}")
+    if t.device.index != dev:
+        raise ValueError(f"{what}: on {t.device}, the current device is cuda:{dev}")
+
+
 class Group:
     """A compiled fusion group, run on torch tensors."""
 
@@ -454,6 +476,13 @@ class Group:
         self.handle = psk_group_create(self.desc)
         self.out_shape = tuple(out_shape)
         self.out_dtype = out_dtype
+        # what each buffer must hold: the kernel reads and writes exactly
+        # these extents, so a smaller or differently typed tensor is refused
+        # here, before the launch
+        self.tree = tree
+        self._in_specs = [(_numel(s), _dtype_code(d)) for s, d in inputs]
+        self._out_specs = [(_numel(out_shape), _dtype_code(out_dtype))] + [
+            (_numel(sh), _dtype_code(d)) for _, sh, d in extras]
 
     @property
     def info(self) -> psk_group_info:
@@ -466,6 +495,19 @@ class Group:
         for t in list(inputs) + outs:
             if not t.is_cuda or not t.is_contiguous():
                 raise ValueError("group buffers must be contiguous device tensors")
+        # Each tensor against the group's buffer: without extra_outs only the
+        # root's (the library refuses the call if the group has extra
+        # outputs); none for a tree-mapped group, which the library refuses
+        # here since its buffers are a tree's leaves.
+        if not self.tree:
+            out_specs = self._out_specs if extra_outs is not None else self._out_specs[:1]
+            if len(inputs) != len(self._in_specs) or len(outs) != len(out_specs):
+                raise ValueError(f"the group takes {len(self._in_specs)} inputs and {len(self._out_specs)} outputs")
+            import torch
+            dev = torch.cuda.current_device()
+            for what, ts, specs in (("input", inputs, self._in_specs), ("output", outs, out_specs)):
+                for k, (t, (n, code)) in enumerate(zip(ts, specs)):
+                    _check_buffer(t, n, code, f"{what} {k}", dev)
         if extra_outs is None:
             psk_group_run(self.handle, [t.data_ptr() for t in inputs], out.data_ptr(), _stream_handle(stream))
         else:
@@ -476,6 +518,13 @@ class Group:
     def run_tree(self, tree: "Tree", in_slots, out_slot, scalars=(), stream=None):
         """Map the group over every leaf of `tree` (one launch); scalars are
         0-d device tensors (or None for per-element inputs)."""
+        if len(scalars) > len(self._in_specs):
+            raise ValueError(f"the group takes {len(self._in_specs)} inputs")
+        for k, t in enumerate(scalars):
+            if t is not None:
+                if not t.is_cuda:
+                    raise ValueError(f"scalar input {k} must be a device tensor")
+                _check_buffer(t, 1, self._in_specs[k][1], f"scalar input {k}", t.device.index)
         ptrs = [0 if t is None else t.data_ptr() for t in scalars]
         if isinstance(out_slot, int):
             psk_group_run_tree(self.handle, tree.handle, in_slots, out_slot, ptrs, _stream_handle(stream))

@@ -195,6 +195,29 @@ def test_in_place_and_alias_refusal():
     assert ei.value.status == P.PSK_E_ALIAS
 
 
+def test_binding_refuses_tensors_that_do_not_match_the_group():
+    """The binding checks every tensor against the group's buffers (element
+    count, storage type, device) before the launch: a short or mistyped
+    tensor would otherwise be read or written past its end."""
+    g = P.Group(parse_dag("%0 = input 0\n%1 = input 1\n%2 = add %0 %1\n"), [((64, 4), "f32"), ((64, 1), "f32")],
+                (64, 4), "f32")
+    x, y, out = torch.randn(64, 4, device=DEV), torch.randn(64, 1, device=DEV), torch.empty(64, 4, device=DEV)
+    before = P.psk_get_stats().launches
+    for ins, o, what in [([x, torch.randn(32, 1, device=DEV)], out, "elements"),
+                         ([x, y], torch.empty(64, 3, device=DEV), "elements"),
+                         ([x, y.to(torch.bfloat16)], out, "storage type"),
+                         ([x, y], out.to(torch.bfloat16), "storage type"),
+                         ([x], out, "inputs")]:
+        with pytest.raises(ValueError, match=what):
+            g.run(ins, o)
+    with pytest.raises(ValueError, match="outputs"):
+        g.run([x, y], out, extra_outs=[torch.empty(64, 4, device=DEV)])
+    assert P.psk_get_stats().launches == before
+    g.run([x.view(256), y.view(64)], out.view(16, 16))      # any view with the right count and type
+    torch.cuda.synchronize()
+    assert torch.equal(out, x + y)
+
+
 def test_empty_output_launches_nothing():
     g = P.Group(parse_dag("%0 = input 0\n%1 = exp %0\n"), [((0, 16), "f32")], (0, 16), "f32")
     before = P.psk_get_stats().launches
