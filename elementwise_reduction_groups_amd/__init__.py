@@ -548,11 +548,24 @@ class Tree:
             n_slots = len(self._keep[0]) if self._keep else 4
         dts = [self._dt(t) for t in self._keep[0]] if self._keep else [PSK_F32] * n_slots
         leaves = []
-        for s in self._keep:
+        dev = None
+        for i, s in enumerate(self._keep):
+            if len(s) != n_slots:
+                raise ValueError(f"leaf {i} has {len(s)} slots, the tree {n_slots}")
             n = s[0].numel()
-            for t in s:
+            for k, t in enumerate(s):
                 if t.numel() != n or (n and (not t.is_cuda or not t.is_contiguous())):
                     raise ValueError("leaf slots must be contiguous device tensors of equal numel")
+                # a slot has one storage type over every leaf: the kernels
+                # read and write each leaf's buffer at that type's size
+                if self._dt(t) != dts[k]:
+                    raise ValueError(f"leaf {i} slot {k}: {t.dtype}, where slot {k} of leaf 0 has another type")
+                if n:
+                    if dev is None:
+                        import torch
+                        dev = torch.cuda.current_device()
+                    if t.device.index != dev:
+                        raise ValueError(f"leaf {i} slot {k}: on {t.device}, the current device is cuda:{dev}")
             leaves.append((n, [t.data_ptr() for t in s]))
         self.handle = psk_tree_create(leaves, dts)
 

@@ -218,6 +218,17 @@ def test_binding_refuses_tensors_that_do_not_match_the_group():
     assert torch.equal(out, x + y)
 
 
+def test_tree_binding_refuses_mixed_slot_types():
+    """Every leaf's tensor in a slot must have that slot's storage type (the
+    kernels size each leaf's accesses by it) and each leaf all the slots."""
+    a = [torch.zeros(8, device=DEV) for _ in range(4)]
+    b = [torch.zeros(8, device=DEV, dtype=torch.bfloat16)] + [torch.zeros(8, device=DEV) for _ in range(3)]
+    with pytest.raises(ValueError, match="slot 0"):
+        P.Tree([a, b])
+    with pytest.raises(ValueError, match="slots"):
+        P.Tree([a, a[:3]])
+
+
 def test_empty_output_launches_nothing():
     g = P.Group(parse_dag("%0 = input 0\n%1 = exp %0\n"), [((0, 16), "f32")], (0, 16), "f32")
     before = P.psk_get_stats().launches
