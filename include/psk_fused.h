@@ -33,6 +33,10 @@
  *   - *_run / *_step calls are asynchronous on the given HIP stream (NULL =
  *     the null stream); buffers must stay alive until the stream has reached
  *     the launch.  Device faults surface at the caller's next synchronisation.
+ *   - A launch goes to the calling thread's current HIP device: the stream
+ *     and every buffer must belong to it (a tree also checks that it is the
+ *     device it was created on).  Buffer extents are the caller's to
+ *     guarantee: the library sees addresses, not sizes.
  *   - Kernels never write their inputs unless an output is the same buffer
  *     (in-place).  Outputs are not zeroed beforehand.
  *   - The library allocates no device memory for data in *_run / *_step
