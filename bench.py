@@ -68,6 +68,10 @@ def main():
                                    "so no multi-GPU figure is produced",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0 or args.reps < 1 or not (0.0 < args.cpu_sample <= 1.0):
+        print(json.dumps({"error": "--steps and --reps must be at least 1, --warmup at least 0, "
+                                   "--cpu-sample in (0, 1]"}))
+        sys.exit(2)
 
     import torch
     import elementwise_reduction_groups_amd as P
