@@ -16,8 +16,8 @@ Every other workload (the step's two kernels alone, the clipped cosine
 AdamW, a 22-layer tree, the tiny-GPT tree cold, warm and graph-replayed,
 the tree-mapped SGD and AdamW groups, RMSNorm+GELU with and without h
 stored, LayerNorm with its statistics, the byte-mask, bf16 and wide
-softmaxes (exact and online), the 64-node chain and a device copy) is timed
-on its own with the cache flushed between calls and reported under
+softmaxes (exact and online), the 64-node chain, torch's device copy and
+an emitted copy) is timed on its own with the cache flushed between calls and reported under
 "groups" (median, min, max of --reps calls).  The CPU baseline runs the
 oracle single-threaded on the same step (inputs drawn on the host).
 
@@ -503,10 +503,17 @@ def time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, pro
         note="ALU-bound: 64 node evaluations per element")
     out["chain64_f32"]["node_evals_per_s"] = round(64 * 16384 * 16384 / (out["chain64_f32"]["ms_median"] * 1e-3), 1)
 
-    # device copy of 2 GiB (read + write) as the practical streaming ceiling
+    # streaming copies of 1 GiB read + 1 GiB written: torch's device copy, and
+    # the emitted pointwise kernel of y = -(-x) (bit-exact copy; nontemporal
+    # 16-byte accesses), the plain r1:w1 stream of this library's kernels
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     add("copy_ceiling", 2 * src.numel() * 4, lambda: dst.copy_(src), note="torch device copy, read+write")
+    from synth.dag import parse_dag
+    copy = P.Group(parse_dag("%0 = input 0\n%1 = neg %0\n%2 = neg %1\n"), [((src.numel(),), "f32")],
+                   (src.numel(),), "f32")
+    add("copy_emitted", 2 * src.numel() * 4, lambda: copy.run([src], dst, stream=stream),
+        note="emitted pointwise y = -(-x): the r1:w1 streaming rate of an emitted kernel")
     del flush, src, dst
     return out
 
