@@ -165,12 +165,15 @@ def test_random_exact_row_groups_bit_for_bit(chunk):
     ("tiled=1,lanes=128,tn=1,rc=1,lc=1", 10),          # registers, LDS and memory tiles; unrolled memory loop
     ("tiled=1,lanes=256,tn=2,rc=2,lc=2,mu=3", 11),     # an unroll that leaves a remainder
     ("tiled=1,lanes=128,tn=1,rc=0,lc=0,alt=0", 12),    # every tile from memory, every phase forwards
+    ("persist=2", 13),                                 # persistent rows (next row loaded during this one)
+    ("lanes=32", 14),                                  # half-wave rows (the 32-lane join)
 ])
-def test_random_exact_row_groups_through_the_tiled_kernel(layout, chunk, monkeypatch):
-    """The same random exact row groups, every one forced through the tiled
-    wide-row kernel with small tiles, so that rows of a few hundred columns
-    already span several tiles, the three loops (register, LDS and memory
-    tiles) and the walks in both directions: bit for bit against the
-    oracle, as above."""
+def test_random_exact_row_groups_through_other_layouts(layout, chunk, monkeypatch):
+    """The same random exact row groups under other launch layouts: forced
+    through the tiled wide-row kernel with small tiles (rows of a few
+    hundred columns already span several tiles, the three loops over
+    register, LDS and memory tiles, the walks in both directions), through
+    persistent rows, and with 32-lane rows: bit for bit against the oracle,
+    as above."""
     monkeypatch.setenv("PSK_LAYOUT", layout)
     test_random_exact_row_groups_bit_for_bit(chunk)
