@@ -22,7 +22,8 @@
 //
 //  * tiled row: rows too wide for registers are walked in tiles by every
 //    phase, the leading tiles' inputs kept in registers and the next ones in
-//    LDS, the rest re-read;
+//    LDS, the rest re-read; odd phases walk from the last tile to the first,
+//    so they begin where the phase before ended (in L2);
 //
 //  * tree-mapped: the group over every leaf of a parameter tree, one launch,
 //    chunks of leaves from a device table.
