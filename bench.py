@@ -190,6 +190,13 @@ def main():
     if not args.no_groups:
         result["groups"] = time_groups(args, P, configs, torch, dev, stream, tree, softmax, scores, probs,
                                        adamw_bytes, softmax_bytes, hp, state)
+        # each HBM-bound group against the emitted r1:w1 copy measured in the
+        # same run (a practical streaming rate, not the published peak)
+        ref = result["groups"].get("copy_emitted", {}).get("GBps")
+        if ref:
+            for name, g in result["groups"].items():
+                if name not in ("copy_emitted", "copy_ceiling", "chain64_f32", "adamw_tiny_gpt_f32"):
+                    g["frac_of_emitted_copy"] = round(g["GBps"] / ref, 3)
 
     # ------------------------------------------------ static dispatch counts
     result["dispatch"] = dispatch_report(P, configs)
