@@ -74,6 +74,10 @@ static std::string flit(float x)
     return std::string("(") + buf + ")";
 }
 
+// ops whose value depends on the node's imm field: a constant's value and
+// WHERE's fill; the kernel cache key must carry its bits for both
+static bool op_reads_imm(int op) { return op == PSK_OP_CONST || op == PSK_OP_WHERE; }
+
 std::string canonical_text(const Analysis& an)
 {
     std::ostringstream s;
@@ -89,7 +93,7 @@ std::string canonical_text(const Analysis& an)
         uint32_t bits;
         std::memcpy(&bits, &nd.imm, 4);
         s << i << " " << nd.op << " " << nd.a << " " << nd.b << " " << nd.c << " " << nd.iparam << " "
-          << (nd.op == PSK_OP_CONST ? bits : 0u) << "\n";
+          << (op_reads_imm(nd.op) ? bits : 0u) << "\n";
     }
     for (const auto& x : an.extras) s << "extra " << x.node << " " << x.dtype << " " << (x.per_row ? 1 : 0) << "\n";
     s << "flags " << an.flags << "\n";
@@ -227,6 +231,10 @@ __device__ __forceinline__ float psk_divr(float a, float b, float y, bool& bad) 
 __device__ __forceinline__ float psk_pz() { float z = 0.0f; __asm__("" : "+v"(z)); return z; }
 __device__ __forceinline__ float psk_max(float a, float b) { return (a > b) ? a : b; }
 __device__ __forceinline__ float psk_min(float a, float b) { return (a < b) ? a : b; }
+// one step of a row maximum: a NaN on either side gives NaN, so the row's
+// maximum does not depend on the order lanes and waves combine in; a tie
+// gives the second operand, as for max
+__device__ __forceinline__ float psk_rmax(float a, float b) { return (a > b || a != a) ? a : b; }
 #define PSK_DPP(x, ctl) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (x)), (ctl), 0xF, 0xF, false))
 #define PSK_RL(x, l) __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, (x)), (l)))
 // all-reduce within each 16-lane row: xor 1, xor 2 (quad_perm), then the
@@ -236,8 +244,8 @@ __device__ __forceinline__ float psk_sum16(float x) {
   x = x + PSK_DPP(x, 0x141); x = x + PSK_DPP(x, 0x140); return x;
 }
 __device__ __forceinline__ float psk_max16(float x) {
-  x = psk_max(x, PSK_DPP(x, 0xB1)); x = psk_max(x, PSK_DPP(x, 0x4E));
-  x = psk_max(x, PSK_DPP(x, 0x141)); x = psk_max(x, PSK_DPP(x, 0x140)); return x;
+  x = psk_rmax(x, PSK_DPP(x, 0xB1)); x = psk_rmax(x, PSK_DPP(x, 0x4E));
+  x = psk_rmax(x, PSK_DPP(x, 0x141)); x = psk_rmax(x, PSK_DPP(x, 0x140)); return x;
 }
 // 32 lanes: the 16-lane results of the two halves combined, the lower
 // half's first (ds_swizzle in bit mode, xor 16, exchanges them within each
@@ -251,7 +259,7 @@ __device__ __forceinline__ float psk_sum32(float x, bool upper) {
 __device__ __forceinline__ float psk_max32(float x, bool upper) {
   x = psk_max16(x);
   const float y = PSK_SWZ16(x);
-  return upper ? psk_max(y, x) : psk_max(x, y);
+  return upper ? psk_rmax(y, x) : psk_rmax(x, y);
 }
 // whole wave: the four row results combined in lane order 0, 16, 32, 48
 __device__ __forceinline__ float psk_sum64(float x) {
@@ -260,7 +268,7 @@ __device__ __forceinline__ float psk_sum64(float x) {
 }
 __device__ __forceinline__ float psk_max64(float x) {
   x = psk_max16(x);
-  return psk_max(psk_max(psk_max(PSK_RL(x, 0), PSK_RL(x, 16)), PSK_RL(x, 32)), PSK_RL(x, 48));
+  return psk_rmax(psk_rmax(psk_rmax(PSK_RL(x, 0), PSK_RL(x, 16)), PSK_RL(x, 32)), PSK_RL(x, 48));
 }
 )PSK";
 
@@ -281,6 +289,14 @@ struct Emitter {
     // of a never-negative exponential (no sum or difference that can cancel,
     // no logarithm)
     std::vector<char> conditioned;
+    // node -> the most gelus on any path from it to a stored value whose
+    // other steps are all well-conditioned as above (kUncond: some path
+    // passes an operation that may cancel).  gelu's relative condition
+    // number 1 + x phi(x)/Phi(x) stays below about 170 wherever its result
+    // is a normal f32 (x > -13), so one gelu turns a relative error of 1.5
+    // f32 ulps (2e-7) into at most 3e-5, far inside a bf16 half-ulp (2^-9)
+    std::vector<int> gelu_path;
+    static constexpr int kUncond = 1 << 20;
 
     Emitter(const Analysis& a, const KernelPlan& p) : an(a), pl(p)
     {
@@ -311,6 +327,25 @@ struct Emitter {
                 default: ok = false;
                 }
                 if (!ok) conditioned[opnd[k]] = 0;
+            }
+        }
+        gelu_path.assign(n, 0);
+        for (int j = n - 1; j >= 0; --j) {
+            const psk_node& nd = an.nodes[j];
+            const int32_t opnd[3] = {nd.a, nd.b, nd.c};
+            for (int k = 0; k < op_arity(nd.op); ++k) {
+                int via = gelu_path[j];
+                switch (nd.op) {
+                case PSK_OP_MUL: case PSK_OP_DIV: case PSK_OP_NEG: case PSK_OP_ABS: case PSK_OP_SQRT:
+                case PSK_OP_POW2: case PSK_OP_MAX: case PSK_OP_MIN: case PSK_OP_CAUSAL_MASK: case PSK_OP_ROW_MAX:
+                    break;
+                case PSK_OP_GELU: via = std::min(kUncond, via + 1); break;
+                case PSK_OP_WHERE: if (k != 1) via = kUncond; break;
+                case PSK_OP_SELECT: if (k == 0) via = kUncond; break;
+                case PSK_OP_ROW_SUM: if (an.nodes[opnd[k]].op != PSK_OP_EXP) via = kUncond; break;
+                default: via = kUncond;
+                }
+                gelu_path[opnd[k]] = std::max(gelu_path[opnd[k]], via);
             }
         }
         NE = (pl.kind == 1 || pl.kind == 3 ? pl.nv : 1) * pl.vec;   // tree: elements per thread
@@ -420,12 +455,14 @@ struct Emitter {
     bool cheap_exp(int i) const { return exp_nonpos(i) && !f32_reach[i] && conditioned[i]; }
 
     // element / row statistic (a value computed from a reduction) that only
-    // bf16 results depend on: the row's reciprocal (correctly rounded) times
-    // the element, within 1.5 f32 ulps of the quotient.  A division by a
-    // scalar input stays correctly rounded.
+    // bf16 results depend on, through well-conditioned operations and at
+    // most one gelu: the row's reciprocal (correctly rounded) times the
+    // element, within 1.5 f32 ulps of the quotient.  A division by a scalar
+    // input, or one whose error a later sum or difference could magnify
+    // (LayerNorm's + beta), stays correctly rounded.
     bool recip_node(int i) const
     {
-        return row_div(i) && !f32_reach[i] && an.depth[an.nodes[i].b] > 0;
+        return row_div(i) && !f32_reach[i] && an.depth[an.nodes[i].b] > 0 && gelu_path[i] <= 1;
     }
 
     // elements of member i (given as element indices) written through
@@ -1111,7 +1148,7 @@ struct Emitter {
             }
             for (int e = 0; e < NE; ++e) {
                 std::string v = val(nd.a, e);
-                std::string acc = mx ? "psk_max(p" + std::to_string(i) + ", " + v + ")"
+                std::string acc = mx ? "psk_rmax(p" + std::to_string(i) + ", " + v + ")"
                                      : "(p" + std::to_string(i) + " + " + v + ")";
                 if (ragged)
                     o << indent << "if (" << col(e) << " < " << an.cols << ") p" << i << " = " << acc << ";\n";
@@ -1138,12 +1175,13 @@ struct Emitter {
         const std::string ex = online_exp(sm);
         o << indent << "{\n" << indent << "  float tm = (-__builtin_inff());\n";
         for (int e = 0; e < NE; ++e) {
-            std::string acc = "tm = psk_max(tm, " + val(y, e) + ");";
+            std::string acc = "tm = psk_rmax(tm, " + val(y, e) + ");";
             if (ragged) o << indent << "  if (" << col(e) << " < " << an.cols << ") " << acc << "\n";
             else o << indent << "  " << acc << "\n";
         }
-        o << indent << "  if (tm > " << P << ") { " << S << " = " << S << " * " << ex << "(" << P << " - tm); " << P
-          << " = tm; }\n";
+        // a NaN maximum replaces the running one (and makes the sum NaN)
+        o << indent << "  if (tm > " << P << " || tm != tm) { " << S << " = " << S << " * " << ex << "(" << P
+          << " - tm); " << P << " = tm; }\n";
         o << indent << "  const float mref = " << P << " == (-__builtin_inff()) ? 0.0f : " << P << ";\n";
         for (int e = 0; e < NE; ++e) {
             std::string acc = S + " = (" + S + " + " + ex + "(" + val(y, e) + " - mref));";
@@ -1217,7 +1255,7 @@ struct Emitter {
                 o << "    p" << i << " = " << slot_of(0, r) << ";\n";
                 for (int w = 1; w < W; ++w) {
                     std::string el = slot_of(w, r);
-                    if (mx) o << "    p" << i << " = psk_max(p" << i << ", " << el << ");\n";
+                    if (mx) o << "    p" << i << " = psk_rmax(p" << i << ", " << el << ");\n";
                     else o << "    p" << i << " = p" << i << " + " << el << ";\n";
                 }
             }

@@ -1,8 +1,9 @@
 // hipRTC compilation of emitted kernels for gfx950.
 //
 // Flags: -O3; -ffp-contract=off so no multiply-add is fused (the oracle and
-// the pages' kernels round every operation: "Fusion reassociates nothing",
-// PSK-Realize); correctly rounded f32 division and square root; packed-FP32
+// the pages' kernels round every operation, and fusion keeps the operation
+// order: PSK-Realize, "What it buys, measured"); correctly rounded f32
+// division and square root; packed-FP32
 // instructions disabled.  hipRTC needs no GPU, so kernels also compile in a
 // host-only process.
 #include <hip/hiprtc.h>

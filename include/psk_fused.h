@@ -128,7 +128,9 @@ typedef enum psk_dtype { PSK_F32 = 0, PSK_BF16 = 1, PSK_U8 = 2 } psk_dtype;
  *                            empties giving zeros
  *   ROW_MAX ROW_SUM ROW_MEAN reduction over the last axis, keepdim; the
  *                            result broadcasts back along the row.  ROW_MEAN
- *                            is ROW_SUM divided by the row length.
+ *                            is ROW_SUM divided by the row length.  ROW_MAX
+ *                            over a row holding a NaN is NaN, whatever the
+ *                            combining order (ties: the later element).
  * Leaves: INPUT (iparam = input slot), CONST (imm = an f32 value).
  * Boundary ops (REDUCE, CONTRACT, CAST, OPAQUE) are accepted by
  * psk_partition only: a reduction ends a group, contractions and casts are

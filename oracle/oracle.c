@@ -14,8 +14,8 @@
  *     round to nearest even;
  *   - each operation is one IEEE-754 binary32 operation in program order:
  *     this file must be compiled with -ffp-contract=off and without any
- *     fast-math flag, so nothing is fused or reassociated ("Fusion
- *     reassociates nothing", PSK-Realize, section "What it buys, measured");
+ *     fast-math flag, so nothing is fused or reassociated (fusion keeps the
+ *     order of operations: PSK-Realize, section "What it buys, measured");
  *   - exp, log, tanh, erf are the C library's f32 functions; their last bits
  *     are the library's, not a specification (presk manual, "Native
  *     execution", section "Conformance").
@@ -107,6 +107,14 @@ static float orc_gelu(float x)
  * section "Typing", builtins). */
 static float orc_max(float x, float y) { return (x > y) ? x : y; }
 static float orc_min(float x, float y) { return (x < y) ? x : y; }
+
+/* One step of a row maximum folded left to right: the running maximum m
+ * against the next element y.  The pages give max's tie rule (the second
+ * operand) but no rule for NaN; a reduction's result must not depend on the
+ * order its elements are combined in, so a NaN anywhere in the row makes the
+ * row maximum NaN (as IEEE 754-2019 maximum does), and ties still go to the
+ * later element. */
+static float orc_row_max_step(float m, float y) { return (m != m) ? m : ((m > y) ? m : y); }
 
 /* -------------------------------------------------- generic group evaluator */
 /* Op codes of this oracle (its own numbering). */
@@ -263,7 +271,7 @@ int orc_eval_group_multi(int n_nodes, const orc_node *nodes, int root,
             }
             case O_ROW_MAX: {
                 float m = A[0];
-                for (int64_t c = 1; c < C; ++c) m = orc_max(m, A[c]);
+                for (int64_t c = 1; c < C; ++c) m = orc_row_max_step(m, A[c]);
                 for (int64_t c = 0; c < C; ++c) v[c] = m;
                 break;
             }
@@ -474,7 +482,7 @@ void orc_softmax_causal(int64_t R, int64_t C, int64_t T, float scale, const floa
         for (int64_t c = 0; c <= last; ++c) {
             float y = xr[c] * scale;
             if (first < 0) { m = y; first = c; }
-            else m = orc_max(m, y);
+            else m = orc_row_max_step(m, y);
         }
         if (first < 0) {
             for (int64_t c = 0; c < C; ++c) o[c] = 0.0f;

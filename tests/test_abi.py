@@ -455,10 +455,24 @@ def test_precision_follows_what_is_stored(lib):
     ln = P.psk_group_source(P.GroupDesc(C.layernorm_dag(eps), [((R, N), "bf16"), ((N,), "bf16"), ((N,), "bf16")],
                                         (R, N), "bf16", root=C.LAYERNORM_ROOT,
                                         extras=[(C.LAYERNORM_MEAN, (R, 1), "f32"), (C.LAYERNORM_RSTD, (R, 1), "f32")]))
-    # f32 statistics that the normalized value does not reach: the division
-    # feeding only the bf16 result takes the reciprocal form
+    # the division feeds only the bf16 result, but through + beta, a sum
+    # that could cancel its error: it stays correctly rounded
     body = ln[ln.index('extern "C"'):]
-    assert "psk_divr(" not in body and "* y9)" in body
+    assert "psk_divr(" in body and "* y9)" not in body
+    # without beta (the normalized value times gamma, then a gelu) the path
+    # is well-conditioned and the division takes the reciprocal form
+    lng = P.psk_group_source(_desc("%0 = input 0\n%1 = input 1\n%2 = row_mean %0\n%3 = sub %0 %2\n"
+                                   "%4 = pow2 %3\n%5 = row_mean %4\n%6 = sqrt %5\n%7 = div %3 %6\n"
+                                   "%8 = mul %7 %1\n%9 = gelu %8\n", [((R, N), "bf16"), ((N,), "bf16")], (R, N),
+                                   "bf16"))
+    body = lng[lng.index('extern "C"'):]
+    assert "psk_divr(" not in body and "* y6)" in body
+    # two gelus after the division: their condition numbers compound, so
+    # the division stays correctly rounded
+    lng2 = P.psk_group_source(_desc("%0 = input 0\n%1 = row_mean %0\n%2 = sub %0 %1\n%3 = pow2 %2\n"
+                                    "%4 = row_mean %3\n%5 = sqrt %4\n%6 = div %2 %5\n%7 = gelu %6\n"
+                                    "%8 = gelu %7\n", [((R, N), "bf16")], (R, N), "bf16"))
+    assert "psk_divr(" in lng2[lng2.index('extern "C"'):]
     # ... but an f32 extra that depends on it keeps the correctly rounded one
     ln32 = P.psk_group_source(P.GroupDesc(C.layernorm_dag(eps), [((R, N), "bf16"), ((N,), "bf16"), ((N,), "bf16")],
                                           (R, N), "bf16", root=C.LAYERNORM_ROOT, extras=[(11, (R, N), "f32"), (C.LAYERNORM_RSTD, (R, 1), "f32")]))
@@ -542,3 +556,21 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     from synth import configs as C
     with pytest.raises(RuntimeError, match="not built"):
         P.Group(C.softmax_dag(0.125), [((4, 8), "f32")], (4, 8), "f32")
+
+
+def test_kernel_cache_keys_on_every_immediate(lib):
+    """Two groups that differ only in a WHERE's fill value (or a constant)
+    get different kernels: the cache key carries every immediate a kernel
+    reads."""
+    def where(fill):
+        nd = parse_dag(f"%0 = input 0\n%1 = input 1\n%2 = where %1 %0 {fill}\n%3 = neg %2\n")
+        return P.GroupDesc(nd, [((8, 16), "f32"), ((8, 16), "u8")], (8, 16), "f32")
+    a, b = where("-inf"), where("0.0")
+    assert P.psk_group_source(a) != P.psk_group_source(b)
+    ca, cb = P.psk_group_code_object(a), P.psk_group_code_object(b)
+    assert ca != cb
+    assert P.psk_group_code_object(where("-inf")) == ca
+    # constants: the same
+    c1 = _desc("%0 = input 0\n%1 = const 2.0\n%2 = mul %0 %1\n", F, (8, 16))
+    c2 = _desc("%0 = input 0\n%1 = const 3.0\n%2 = mul %0 %1\n", F, (8, 16))
+    assert P.psk_group_code_object(c1) != P.psk_group_code_object(c2)

@@ -119,3 +119,21 @@ def test_causal_softmax_bf16_full_size_sampled_rows():
         refs.append(oracle.eval_group(configs.softmax_causal_dag(0.125, 1024), [block], (1024, C), BF16,
                                       rows=(q, q + 1))[q])
     assert_bf16_close(to_np(out[torch.from_numpy(rows).to(DEV)]), np.stack(refs), "bf16 softmax full size")
+
+
+def test_groups_differing_only_in_where_fill():
+    """Two groups that differ only in a WHERE's fill value, created and run
+    in one process: each gets its own kernel and its own fill, bit for bit
+    against the oracle."""
+    from synth.dag import parse_dag
+    x = configs.softmax_scores(64, 96, device=DEV, seed=17)
+    m = configs.random_mask(64, 96, p_keep=0.5, device=DEV)
+    ins = [to_np(x), mask_np(m)]
+    for fill in ("-inf", "0.0", "-2.5", "inf"):
+        nodes = parse_dag(f"%0 = input 0\n%1 = input 1\n%2 = where %1 %0 {fill}\n%3 = neg %2\n")
+        g = P.Group(nodes, [((64, 96), "f32"), ((64, 96), "u8")], (64, 96), "f32")
+        out = torch.full_like(x, float("nan"))
+        g.run([x, m], out)
+        torch.cuda.synchronize()
+        ref = oracle.eval_group(nodes, ins, (64, 96))
+        assert_bits(to_np(out), ref, f"where fill {fill}")

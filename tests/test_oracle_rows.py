@@ -145,3 +145,40 @@ def test_rmsnorm_vs_f64(orc):
     ref = orc.eval_group_f64(configs.rmsnorm_gelu_dag(eps), [_bf16(x), _bf16(r), _bf16(g)], (16, 1024))
     ref_bf16 = _bf16(torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16))
     assert bf16_ulp_distance(out, ref_bf16).max() <= 1
+
+
+# ------------------------------------------------------------ row maximum
+def test_row_max_nan_and_ties(orc):
+    """The row maximum against numpy's maximum, which returns NaN for a row
+    holding a NaN wherever it stands; and at a tie of signed zeros the later
+    element (max's tie rule), checked on its sign bit."""
+    from synth.dag import parse_dag
+    nodes = parse_dag("%0 = input 0\n%1 = row_max %0\n%2 = sub %0 %1\n")
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((64, 37)).astype(np.float32)
+    for r in range(0, 64, 3):                      # NaN at the first, last or an inner position
+        x[r, [0, 36, r % 37][r % 3]] = np.nan
+    x[5, :] = np.nan
+    mx = np.zeros((64, 1), np.float32)
+    orc.eval_group(nodes, [x], x.shape, extras=[(1, mx)])
+    want = x.max(axis=1, keepdims=True)
+    assert np.array_equal(np.isnan(mx), np.isnan(want))
+    assert np.array_equal(mx[~np.isnan(want)], want[~np.isnan(want)])
+    z = np.array([[-0.0, 0.0], [0.0, -0.0], [-1.0, -0.0], [-0.0, -1.0]], np.float32)
+    mz = np.zeros((4, 1), np.float32)
+    orc.eval_group(nodes, [z], z.shape, extras=[(1, mz)])
+    assert list(np.signbit(mz[:, 0])) == [False, True, True, True]
+
+
+def test_softmax_row_with_nan_is_nan(orc):
+    """The dedicated causal softmax over a row holding a NaN among its
+    allowed scores: every allowed output is NaN (the maximum is NaN); a
+    NaN only in refused columns changes nothing."""
+    T = 8
+    x = np.random.default_rng(2).standard_normal((T, T)).astype(np.float32)
+    y = x.copy()
+    y[5, 2] = np.nan            # allowed in row 5 (columns 0..5)
+    y[3, 6] = np.nan            # refused in row 3 (columns 0..3)
+    a, b = orc.softmax_causal(x, T, 0.125), orc.softmax_causal(y, T, 0.125)
+    assert np.isnan(b[5, :6]).all() and np.all(b[5, 6:] == 0)
+    assert np.array_equal(a[3], b[3])
