@@ -97,8 +97,13 @@ psk_status partition(int32_t n, const psk_node* body, const psk_tensor_desc* typ
             }
             // an element member has the group's type; with rows fused, a
             // value one per row of the group's rows joins as well: a member
-            // of row values, or a reduction of a value of the group's shape
+            // of row values, or a reduction of a value of the group's shape.
+            // A group rooted at a reduction takes no member: the reduction
+            // reduces an element value, and its own value is one per row
+            // (with a last axis of length 1 the types would agree, but the
+            // group the row kernels run would not)
             const psk_tensor_desc& rt = types[groot[g]];
+            if (ok && node_class(body[groot[g]], rows) == 3) ok = false;
             bool typed = ok && ((cls == 1 && same_type(types[i], rt)) ||
                                 (rows && row_shape_of(types[i], rt) &&
                                  (cls == 1 || same_shape(types[body[i].a], rt))));

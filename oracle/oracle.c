@@ -604,7 +604,11 @@ int orc_partition(int n, const int32_t *op_class, const int32_t *args, const int
                     }
             /* a row value joins when its shape is the root's with a last
              * axis of 1; a reduction only when it reduces a value of the
-             * root's shape */
+             * root's shape; a group whose root is a reduction takes no
+             * member (the reduction reads an element value and is itself
+             * one value per row) */
+            if (ok && G >= 0 && op_class[groot[G]] == 3)
+                ok = 0;
             int typed = ok && G >= 0 &&
                         ((op_class[i] == 1 && gtype[G] == type_id[i]) ||
                          (rows && rowshape_id[groot[G]] >= 0 && shape_id[i] == rowshape_id[groot[G]] &&
