@@ -204,12 +204,17 @@ def adamw_scalars(lr, beta1, beta2, eps, weight_decay, t) -> np.ndarray:
 
 
 def adamw(theta: np.ndarray, grad: np.ndarray, m: np.ndarray, v: np.ndarray,
-          lr, beta1, beta2, eps, weight_decay, t):
+          lr, beta1, beta2, eps, weight_decay, t, out=None):
     """One AdamW step (out of place).  Arrays are float32 or uint16 (bf16
-    bits); m and v share a dtype.  Returns (theta', m', v')."""
+    bits); m and v share a dtype.  Returns (theta', m', v'), written into
+    ``out`` (three contiguous arrays like theta, m, v) when given."""
     theta, grad, m, v = (np.ascontiguousarray(a) for a in (theta, grad, m, v))
     assert m.dtype == v.dtype and theta.size == grad.size == m.size == v.size
-    to, mo, vo = np.empty_like(theta), np.empty_like(m), np.empty_like(v)
+    if out is None:
+        to, mo, vo = np.empty_like(theta), np.empty_like(m), np.empty_like(v)
+    else:
+        to, mo, vo = out
+        assert to.dtype == theta.dtype and mo.dtype == vo.dtype == m.dtype and to.size == mo.size == vo.size == m.size
     lib().orc_adamw(theta.size, _dtype_code(theta), _ptr(theta), _dtype_code(grad), _ptr(grad),
                     _dtype_code(m), _ptr(m), _ptr(v), lr, beta1, beta2, eps, weight_decay, int(t),
                     _ptr(to), _ptr(mo), _ptr(vo))

@@ -67,3 +67,18 @@ def assert_bits(got, ref, what=""):
         i = np.argwhere(gb != rb)[0]
         raise AssertionError(f"{what}: {bad} of {gb.size} elements differ in bits; first at {tuple(i)}: "
                              f"gpu {got[tuple(i)]!r} ref {ref[tuple(i)]!r}")
+
+
+def compare_all(got: np.ndarray, ref: np.ndarray, rule: str, what: str = "", chunk: int = 1 << 24) -> int:
+    """Compare every element of two large arrays chunk by chunk under one of
+    the rules above ("f32", "bf16" or "bits"); raises on the first chunk
+    with a mismatch and returns the number of elements compared."""
+    g, r = got.reshape(-1), ref.reshape(-1)
+    assert g.size == r.size and g.dtype == r.dtype, f"{what}: {g.shape} {g.dtype} vs {r.shape} {r.dtype}"
+    check = {"f32": assert_f32_close, "bf16": assert_bf16_close, "bits": assert_bits}[rule]
+    n = 0
+    for a in range(0, g.size, chunk):
+        b = min(g.size, a + chunk)
+        check(g[a:b], r[a:b], f"{what} (elements {a}..{b})")
+        n += b - a
+    return n

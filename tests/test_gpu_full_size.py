@@ -1,0 +1,101 @@
+"""Every output element of the full-size workloads against the oracle, in
+the launch layouts the benchmark times.
+
+The GPU's inputs are copied to the host and the oracle runs over them on
+the host's threads (oracle.parallel: blocks of rows, leaves or elements;
+bit for bit the single-threaded oracle).  Each test asserts that the count
+of elements compared equals the output's size:
+
+  * AdamW over the Llama-style tree (145 leaves, 887 685 120 parameters,
+    bf16 theta and g, f32 m and v): theta', m', v' of every leaf bit for bit;
+  * causal softmax, f32 [131072, 1024]: all 134M outputs within
+    1e-7 + 2e-6 |ref|;
+  * add + RMSNorm + gamma + GELU, bf16 [16384, 4096]: all 67M outputs within
+    one bf16 ulp;
+  * the 64-node chain, f32 [16384, 16384]: all 268M outputs within
+    1e-7 + 2e-6 |ref|.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.parallel as OP
+from synth import configs
+from tests.gpu_util import compare_all, to_np
+
+P = pytest.importorskip("elementwise_reduction_groups_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+THREADS = OP.host_threads(16)
+EPS = configs.f32(1e-5)
+
+
+def say(msg):
+    print(f"[full size] {msg}", file=sys.stderr, flush=True)
+
+
+def test_adamw_llama_tree_every_element():
+    shapes = [s for _, s in configs.llama_leaves()]
+    state = configs.adamw_state(shapes, theta_dtype=torch.bfloat16, grad_dtype=torch.bfloat16,
+                                mv_dtype=torch.float32, device=DEV, seed=configs.SEED_BASE + 2)
+    n = sum(math.prod(s) for s in shapes)
+    assert len(shapes) == 145 and n == 887685120
+    say("AdamW Llama tree: inputs to host")
+    host = [tuple(to_np(s[k]).reshape(-1) for k in ("theta", "grad", "m", "v")) for s in state]
+    tree = P.Tree([[s["theta"], s["grad"], s["m"], s["v"]] for s in state])
+    HP = configs.ADAMW_HP
+    hp = (HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["weight_decay"], HP["t"])
+    say("AdamW Llama tree: one step on the GPU")
+    tree.adamw_step(*hp)
+    torch.cuda.synchronize()
+    say(f"AdamW Llama tree: oracle on {THREADS} host threads")
+    ref = OP.adamw_leaves(host, hp, THREADS)
+    compared = 0
+    for leaf, (s, r) in enumerate(zip(state, ref)):
+        for k, name, rr in zip(("theta", "m", "v"), ("theta'", "m'", "v'"), r):
+            compared += compare_all(to_np(s[k]), rr, "bits", f"leaf {leaf} {name}")
+    assert compared == 3 * n
+
+
+def test_causal_softmax_every_element():
+    R, C = 131072, 1024
+    x = configs.softmax_scores(R, C, device=DEV)
+    g = P.Group(configs.softmax_causal_dag(0.125, 1024), [((R, C), "f32")], (R, C), "f32")
+    out = torch.full_like(x, float("nan"))
+    say("causal softmax [131072, 1024] f32 on the GPU")
+    g.run([x], out)
+    torch.cuda.synchronize()
+    say(f"causal softmax: oracle on {THREADS} host threads")
+    ref = OP.softmax_causal(to_np(x), 1024, 0.125, THREADS)
+    assert compare_all(to_np(out), ref, "f32", "causal softmax") == R * C
+
+
+def test_rmsnorm_gelu_every_element():
+    R, C = 16384, 4096
+    x, r, gm = configs.rmsnorm_inputs(R, C, device=DEV)
+    g = P.Group(configs.rmsnorm_gelu_dag(EPS), [((R, C), "bf16"), ((R, C), "bf16"), ((C,), "bf16")], (R, C), "bf16")
+    out = torch.full_like(x, float("nan"))
+    say("add + RMSNorm + gamma + GELU [16384, 4096] bf16 on the GPU")
+    g.run([x, r, gm], out)
+    torch.cuda.synchronize()
+    say(f"RMSNorm + GELU: oracle on {THREADS} host threads")
+    ref = OP.rmsnorm_gelu(to_np(x), to_np(r), to_np(gm), EPS, THREADS)
+    assert compare_all(to_np(out), ref, "bf16", "RMSNorm + GELU") == R * C
+
+
+def test_chain64_every_element():
+    N = 16384
+    nodes = configs.chain64_dag()
+    A, B, C = configs.chain_inputs(N, N, device=DEV)
+    g = P.Group(nodes, [((N, N), "f32"), ((N, 1), "f32"), ((1, N), "f32")], (N, N), "f32")
+    out = torch.full_like(A, float("nan"))
+    say("64-node chain [16384, 16384] f32 on the GPU")
+    g.run([A, B, C], out)
+    torch.cuda.synchronize()
+    say(f"64-node chain: oracle on {THREADS} host threads")
+    ref = OP.eval_group(nodes, [to_np(A), to_np(B), to_np(C)], (N, N), 0, THREADS)
+    assert compare_all(to_np(out), ref, "f32", "chain64") == N * N
