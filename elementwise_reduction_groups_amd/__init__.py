@@ -114,7 +114,8 @@ _lib = None
 
 EXPORTED = ["psk_group_create", "psk_group_run", "psk_group_destroy", "psk_group_get_info", "psk_group_source",
             "psk_group_code_object", "psk_tree_create", "psk_tree_destroy", "psk_tree_get_info",
-            "psk_tree_get_tables", "psk_tree_plan", "psk_adamw_step", "psk_adamw_step_config", "psk_adamw_lr",
+            "psk_tree_get_tables", "psk_tree_plan", "psk_adamw_step", "psk_adamw_step_config",
+            "psk_adamw_step_config_noalloc", "psk_adamw_lr",
             "psk_tree_clip_result", "psk_group_run_tree", "psk_group_run_multi", "psk_group_run_tree_multi",
             "psk_partition", "psk_partition_ex", "psk_dispatch_count", "psk_last_error",
             "psk_status_str", "psk_version", "psk_get_stats"]
@@ -144,6 +145,7 @@ def lib() -> ctypes.CDLL:
     L.psk_tree_plan.argtypes = [vp, i32, ctypes.POINTER(i64), vp, vp, vp, vp]
     L.psk_adamw_step.argtypes = [vp, ctypes.POINTER(psk_adamw_hp), vp]
     L.psk_adamw_step_config.argtypes = [vp, ctypes.POINTER(psk_adamw_config), vp]
+    L.psk_adamw_step_config_noalloc.argtypes = [vp, ctypes.POINTER(psk_adamw_config), vp]
     L.psk_adamw_lr.argtypes = [ctypes.POINTER(psk_adamw_config), ctypes.POINTER(ctypes.c_double)]
     L.psk_tree_clip_result.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_float)]
     L.psk_group_run_tree.argtypes = [vp, vp, ctypes.POINTER(i32), i32, ctypes.POINTER(vp), vp]
@@ -374,6 +376,11 @@ def psk_adamw_step_config(tree: int, cfg: psk_adamw_config, stream: Optional[int
     _check(lib().psk_adamw_step_config(ctypes.c_void_p(tree), ctypes.byref(cfg), ctypes.c_void_p(stream or 0)))
 
 
+def psk_adamw_step_config_noalloc(tree: int, cfg: psk_adamw_config, stream: Optional[int] = None):
+    _check(lib().psk_adamw_step_config_noalloc(ctypes.c_void_p(tree), ctypes.byref(cfg),
+                                               ctypes.c_void_p(stream or 0)))
+
+
 def psk_adamw_lr(cfg: psk_adamw_config) -> float:
     x = ctypes.c_double()
     _check(lib().psk_adamw_lr(ctypes.byref(cfg), ctypes.byref(x)))
@@ -590,6 +597,12 @@ class Tree:
             psk_adamw_step_config(self.handle, cfg, _stream_handle(stream))
         else:
             psk_adamw_step(self.handle, lr, beta1, beta2, eps, weight_decay, t, _stream_handle(stream))
+
+    def adamw_step_noalloc(self, lr, beta1, beta2, eps, weight_decay, t, stream=None, **config):
+        """The configured step through psk_adamw_step_config_noalloc (the
+        clipping pass's scratch in the library's static device array)."""
+        cfg = adamw_config(lr, beta1, beta2, eps, weight_decay, t, **config)
+        psk_adamw_step_config_noalloc(self.handle, cfg, _stream_handle(stream))
 
     def clip_result(self):
         return psk_tree_clip_result(self.handle)

@@ -17,9 +17,47 @@
 // evaluation bit for bit.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "psk_internal.h"
 
 namespace psk {
+
+// ------------------------------------------- static scratch (no allocation)
+// The clipping pass's per-chunk partial sums and its result (ClipOut) for
+// psk_adamw_step_config_noalloc, the entry point for callers that cannot
+// allocate: a file-scope device array, one copy on every GPU the library
+// runs on, alive until the process ends.  kStaticChunks partials followed
+// by one ClipOut (two doubles' room); trees of up to 2^20 chunks (2^32
+// elements).  Nothing here must start at zero: the sum-of-squares kernel
+// writes every partial it covers and the combine writes the result.
+static __device__ __align__(256) double scratch[kStaticChunks + 2];
+
+static std::mutex g_scratch_mu;
+static double* g_scratch[kMaxScratchDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current.  Host code never passes the array's own
+// name to a kernel: on the host it is a stand-in, not a device address.
+psk_status static_scratch(double** partials, ClipOut** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices) return fail(PSK_E_HIP, "device index out of range");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(PSK_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+        g_scratch[dev] = static_cast<double*>(p);
+    }
+    *partials = g_scratch[dev];
+    *out = reinterpret_cast<ClipOut*>(g_scratch[dev] + kStaticChunks);
+    return PSK_OK;
+}
+
 namespace {
 
 // Launch shape, chosen by measurement on MI355X over the 145-leaf tree:

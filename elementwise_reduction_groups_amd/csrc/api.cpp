@@ -559,9 +559,11 @@ extern "C" psk_status psk_adamw_lr(const psk_adamw_config* cfg, double* lr)
     return schedule_lr(cfg, lr);
 }
 
-extern "C" psk_status psk_adamw_step_config(const psk_tree* tree, const psk_adamw_config* cfg, void* hip_stream)
+// The configured step; the clipping pass keeps its partials and result in
+// the tree's device memory, or (no_alloc) in the library's static scratch.
+static psk_status adamw_config_step(const psk_tree* tree, const psk_adamw_config* cfg, void* hip_stream,
+                                    bool no_alloc)
 {
-    clear_error();
     if (!tree || !cfg) return fail(PSK_E_NULL, "tree or cfg is NULL");
     const double v[6] = {cfg->lr, cfg->beta1, cfg->beta2, cfg->eps, cfg->weight_decay, cfg->grad_clip};
     for (double x : v)
@@ -579,13 +581,35 @@ extern "C" psk_status psk_adamw_step_config(const psk_tree* tree, const psk_adam
     const int64_t nc = (int64_t)tree->chunks.size();
     const float* gscale = nullptr;
     if (cfg->grad_clip > 0.0) {
-        st = launch_clip(tree->d_leaves, tree->d_chunks, nc, tree->dt[1], tree->d_partials, tree->d_clip,
-                         cfg->grad_clip, hip_stream);
+        double* partials = tree->d_partials;
+        ClipOut* clip = tree->d_clip;
+        if (no_alloc) {
+            if (nc > kStaticChunks)
+                return fail(PSK_E_UNSUPPORTED, "the tree has " + std::to_string(nc) + " chunks; the static scratch of "
+                                               "the clipping pass holds " + std::to_string(kStaticChunks) +
+                                               " (trees of up to 2^32 elements)");
+            st = static_scratch(&partials, &clip);
+            if (st != PSK_OK) return st;
+        }
+        st = launch_clip(tree->d_leaves, tree->d_chunks, nc, tree->dt[1], partials, clip, cfg->grad_clip, hip_stream);
         if (st != PSK_OK) return st;
-        gscale = &tree->d_clip->factor;
+        gscale = &clip->factor;
     }
     return launch_adamw(tree->d_leaves, tree->d_chunks, nc, tree->dt[0], tree->dt[1], tree->dt[2], s, gscale,
                         hip_stream);
+}
+
+extern "C" psk_status psk_adamw_step_config(const psk_tree* tree, const psk_adamw_config* cfg, void* hip_stream)
+{
+    clear_error();
+    return adamw_config_step(tree, cfg, hip_stream, false);
+}
+
+extern "C" psk_status psk_adamw_step_config_noalloc(const psk_tree* tree, const psk_adamw_config* cfg,
+                                                    void* hip_stream)
+{
+    clear_error();
+    return adamw_config_step(tree, cfg, hip_stream, true);
 }
 
 extern "C" psk_status psk_tree_clip_result(const psk_tree* tree, double* sumsq, float* factor)

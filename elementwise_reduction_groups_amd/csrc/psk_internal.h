@@ -193,6 +193,13 @@ psk_status launch_adamw(const LeafDev* d_leaves, const ChunkDev* d_chunks, int64
 psk_status launch_clip(const LeafDev* d_leaves, const ChunkDev* d_chunks, int64_t n_chunks, int grad_dt,
                        double* partials, ClipOut* out, double c, void* stream);
 
+// Library-static device scratch of the clipping pass (defined in adamw.hip):
+// room for kStaticChunks partials and one ClipOut on every device; the
+// addresses on the current device (looked up once per device).
+constexpr int64_t kStaticChunks = int64_t(1) << 20;
+constexpr int kMaxScratchDevices = 64;
+psk_status static_scratch(double** partials, ClipOut** out);
+
 // --------------------------------------------------------------- counters
 void count_launch();
 void count_jit(bool hit);

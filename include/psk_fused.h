@@ -370,6 +370,20 @@ typedef struct psk_adamw_config {
  * warmup >= total for the decaying schedules, non-finite values. */
 psk_status psk_adamw_step_config(const psk_tree* tree, const psk_adamw_config* cfg, void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the step
+ * of psk_adamw_step_config, bit for bit, whose clipping pass keeps its
+ * per-chunk partial sums and its result in a library-static device array
+ * (one per GPU, 8 MiB, held until the process ends) instead of the tree's
+ * memory.  The call allocates nothing (no hipMalloc, no allocating library
+ * routine); the tree and its tables were created beforehand.  Every such
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams, or from several threads without ordering) race.
+ * With clipping, a tree of more than 2^20 chunks (2^32 elements) is refused
+ * (PSK_E_UNSUPPORTED) before any launch.  psk_tree_clip_result does not see
+ * the result of a step taken here.  Other refusals as psk_adamw_step_config. */
+psk_status psk_adamw_step_config_noalloc(const psk_tree* tree, const psk_adamw_config* cfg, void* hip_stream);
+
 /* Host-only: the schedule's learning rate at cfg->t (before rounding). */
 psk_status psk_adamw_lr(const psk_adamw_config* cfg, double* lr);
 
