@@ -28,6 +28,7 @@ PSK_GROUP_TREE = 1
 PSK_GROUP_ONLINE = 2
 PSK_PARTITION_ROWS = 1
 PSK_MAX_RANK = 4
+PSK_VERSION = 200            # the C ABI this binding marshals (psk_tensor_desc with strides)
 PSK_MAX_SLOTS = 8
 PSK_TREE_CHUNK = 4096
 
@@ -56,7 +57,8 @@ class psk_node(ctypes.Structure):
 
 
 class psk_tensor_desc(ctypes.Structure):
-    _fields_ = [("rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("shape", ctypes.c_int64 * PSK_MAX_RANK)]
+    _fields_ = [("rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("shape", ctypes.c_int64 * PSK_MAX_RANK),
+                ("stride", ctypes.c_int64 * PSK_MAX_RANK)]
 
 
 class psk_group_desc(ctypes.Structure):
@@ -129,6 +131,8 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
     L = ctypes.CDLL(LIB_PATH)
+    if L.psk_version() != PSK_VERSION:
+        raise RuntimeError(f"{LIB_PATH} is version {L.psk_version()}, this binding {PSK_VERSION}: rebuild it")
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.psk_group_create.argtypes = [ctypes.POINTER(psk_group_desc), ctypes.POINTER(vp)]
     L.psk_group_run.argtypes = [vp, ctypes.POINTER(vp), vp, vp]
@@ -192,11 +196,25 @@ def _dtype_code(dt) -> int:
     raise ValueError(f"unsupported storage type {dt!r}")
 
 
-def tensor_desc(shape: Sequence[int], dtype) -> psk_tensor_desc:
+def tensor_desc(shape: Sequence[int], dtype, strides: Optional[Sequence[int]] = None) -> psk_tensor_desc:
+    """strides: each axis's step in elements (None: dense row-major); a
+    stride of 0 broadcasts that axis."""
     d = psk_tensor_desc()
     shape = tuple(int(s) for s in shape)
     if len(shape) > PSK_MAX_RANK:
         raise ValueError("rank above 4")
+    if strides is not None:
+        strides = tuple(int(x) for x in strides)
+        if len(strides) != len(shape):
+            raise ValueError("one stride per axis")
+        if any(x < 0 for x in strides):
+            raise ValueError("negative strides are not supported")
+        # all-zero strides mean dense to the library: a view expanded from one
+        # element along every axis is one value, described by sizes of 1
+        if not any(strides) and any(n > 1 for n in shape):
+            raise ValueError("a tensor expanded from one element: give it with shape of 1s")
+        for i, x in enumerate(strides):
+            d.stride[i] = x
     d.rank = len(shape)
     d.dtype = _dtype_code(dtype)
     for i, s in enumerate(shape):
@@ -223,9 +241,11 @@ class GroupDesc:
     def __init__(self, nodes, inputs: Sequence[Tuple[Sequence[int], object]], out_shape: Sequence[int], out_dtype,
                  root: Optional[int] = None, arith=PSK_F32, flags: int = 0,
                  extras: Sequence[Tuple[int, Sequence[int], object]] = ()):
-        """extras: (node index, shape, storage type) of each further stored value."""
+        """inputs: (shape, storage type) of each dense input, or (shape,
+        storage type, strides) of a strided one; extras: (node index, shape,
+        storage type) of each further stored value."""
         self._nodes = node_array(nodes)
-        self._inputs = (psk_tensor_desc * max(1, len(inputs)))(*[tensor_desc(s, d) for s, d in inputs])
+        self._inputs = (psk_tensor_desc * max(1, len(inputs)))(*[tensor_desc(*spec) for spec in inputs])
         self.desc = psk_group_desc()
         self.desc.n_nodes = len(nodes)
         self.desc.nodes = self._nodes
@@ -487,7 +507,10 @@ class Group:
         # these extents, so a smaller or differently typed tensor is refused
         # here, before the launch
         self.tree = tree
-        self._in_specs = [(_numel(s), _dtype_code(d)) for s, d in inputs]
+        self._in_specs = [(_numel(spec[0]), _dtype_code(spec[1])) for spec in inputs]
+        # strided inputs: the shape and strides a tensor must have
+        self._in_layout = [(tuple(int(x) for x in spec[0]), tuple(int(x) for x in spec[2]))
+                           if len(spec) > 2 and spec[2] is not None else None for spec in inputs]
         self._out_specs = [(_numel(out_shape), _dtype_code(out_dtype))] + [
             (_numel(sh), _dtype_code(d)) for _, sh, d in extras]
 
@@ -499,9 +522,24 @@ class Group:
         """extra_outs: one tensor per extra output (a group with extra outputs
         runs through psk_group_run_multi)."""
         outs = [out] + list(extra_outs or [])
-        for t in list(inputs) + outs:
+        for t in outs:
             if not t.is_cuda or not t.is_contiguous():
-                raise ValueError("group buffers must be contiguous device tensors")
+                raise ValueError("group outputs must be contiguous device tensors")
+        for k, t in enumerate(inputs):
+            layout = self._in_layout[k] if k < len(self._in_layout) else None
+            if not t.is_cuda:
+                raise ValueError(f"input {k} must be a device tensor")
+            if layout is None:
+                if not t.is_contiguous():
+                    raise ValueError(f"input {k}: the group was created for a dense input; create it with this "
+                                     f"tensor's strides {tuple(t.stride())} to read the view in place")
+            else:
+                shape, strides = layout
+                got = tuple(x if n > 1 else 0 for n, x in zip(t.shape, t.stride()))
+                want = tuple(x if n > 1 else 0 for n, x in zip(shape, strides))
+                if tuple(t.shape) != shape or got != want:
+                    raise ValueError(f"input {k}: shape {tuple(t.shape)} strides {tuple(t.stride())}, where the "
+                                     f"group reads shape {shape} strides {strides}")
         # Each tensor against the group's buffer: without extra_outs only the
         # root's (the library refuses the call if the group has extra
         # outputs); none for a tree-mapped group, which the library refuses

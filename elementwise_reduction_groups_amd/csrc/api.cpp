@@ -212,7 +212,8 @@ static psk_status run_group(const psk_group* group, const void* const* inputs, v
         if (!b) return fail(PSK_E_NULL, "input " + std::to_string(k) + " is NULL");
         if (b % esize(in.dtype)) return fail(PSK_E_ALIGN, "input " + std::to_string(k) + " is not aligned to its element size");
         if (b % 16) aligned16 = false;
-        const uintptr_t e = b + (uintptr_t)in.numel * esize(in.dtype);
+        // the bytes the input's layout reaches: first element to last offset
+        const uintptr_t e = b + (uintptr_t)in.span * esize(in.dtype);
         for (const Out& o : ov) {
             if (!(b < o.e && o.b < e)) continue;
             // in place: an element output over a same-shape, same-type input

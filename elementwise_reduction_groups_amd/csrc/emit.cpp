@@ -86,7 +86,8 @@ std::string canonical_text(const Analysis& an)
     for (size_t k = 0; k < an.inputs.size(); ++k) {
         const InputInfo& in = an.inputs[k];
         s << "in" << k << " " << in.dtype << " [" << in.aligned[0] << "," << in.aligned[1] << "," << in.aligned[2]
-          << "," << in.aligned[3] << "]\n";
+          << "," << in.aligned[3] << "] step [" << in.stride4[0] << "," << in.stride4[1] << "," << in.stride4[2]
+          << "," << in.stride4[3] << "]\n";
     }
     for (size_t i = 0; i < an.nodes.size(); ++i) {
         const psk_node& nd = an.nodes[i];
@@ -231,10 +232,10 @@ __device__ __forceinline__ float psk_divr(float a, float b, float y, bool& bad) 
 __device__ __forceinline__ float psk_pz() { float z = 0.0f; __asm__("" : "+v"(z)); return z; }
 __device__ __forceinline__ float psk_max(float a, float b) { return (a > b) ? a : b; }
 __device__ __forceinline__ float psk_min(float a, float b) { return (a < b) ? a : b; }
-// one step of a row maximum: a NaN on either side gives NaN, so the row's
-// maximum does not depend on the order lanes and waves combine in; a tie
-// gives the second operand, as for max
-__device__ __forceinline__ float psk_rmax(float a, float b) { return (a > b || a != a) ? a : b; }
+// one step of a row maximum: IEEE 754-2019 maximum (NaN on either side
+// gives NaN; +0 above -0), so the row's maximum does not depend on the order
+// lanes and waves combine in; v_maximum3_f32 takes two elements a step
+__device__ __forceinline__ float psk_rmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 #define PSK_DPP(x, ctl) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (x)), (ctl), 0xF, 0xF, false))
 #define PSK_RL(x, l) __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, (x)), (l)))
 // all-reduce within each 16-lane row: xor 1, xor 2 (quad_perm), then the
@@ -349,7 +350,7 @@ struct Emitter {
             }
         }
         NE = (pl.kind == 1 || pl.kind == 3 ? pl.nv : 1) * pl.vec;   // tree: elements per thread
-        big = an.numel >= (int64_t(1) << 31) - 4096;
+        big = an.numel >= (int64_t(1) << 31) - 4096 || an.max_span >= (int64_t(1) << 31) - 4096;
         for (auto& nd : an.nodes)
             if (nd.op == PSK_OP_CAUSAL_MASK) period = nd.iparam;
         if (pl.kind == 1)
@@ -533,18 +534,16 @@ struct Emitter {
         return x;
     }
 
-    // offset expression of input k's row part for the current row variable `rv`
+    // offset expression of input k's row part for the current row variable
+    // `rv`: each leading output axis's index times the input's step along it
     std::string row_offset(const InputInfo& in, const std::string& rv) const
     {
         // output leading axes O0,O1,O2 (right-aligned), row = (i0*O1 + i1)*O2 + i2
         const int64_t* O = an.out_shape4;
-        const int64_t* A = in.aligned;
-        int64_t st[4];
-        st[3] = 1;
-        for (int d = 2; d >= 0; --d) st[d] = st[d + 1] * A[d + 1];
+        const int64_t* st = in.stride4;
         std::string s = "0";
         for (int d = 0; d < 3; ++d) {
-            if (A[d] == 1) continue;
+            if (st[d] == 0) continue;
             int64_t inner = 1;
             for (int dd = d + 1; dd < 3; ++dd) inner *= O[dd];
             std::string idx = "(" + rv;
@@ -960,12 +959,19 @@ struct Emitter {
         }
     }
 
+    // the column part: the column index times the input's last-axis step
+    std::string col_offset(const InputInfo& in, const std::string& cexpr) const
+    {
+        if (in.stride4[3] == 1) return cexpr;
+        return "(" + std::string(I()) + ")(" + cexpr + ") * (" + std::string(I()) + ")" + std::to_string(in.stride4[3]);
+    }
+
     std::string elem_offset(const InputInfo& in, const std::string& rv, const std::string& cexpr)
     {
         switch (in.kind) {
         case InKind::Full: return "(" + rv + ") * (" + std::string(I()) + ")" + std::to_string(an.cols) + " + " + cexpr;
-        case InKind::ColVec: return cexpr;
-        default: return "(" + row_offset(in, rv) + ") + " + cexpr;
+        case InKind::ColVec: return col_offset(in, cexpr);
+        default: return "(" + row_offset(in, rv) + ") + " + col_offset(in, cexpr);
         }
     }
 
@@ -1179,9 +1185,10 @@ struct Emitter {
             if (ragged) o << indent << "  if (" << col(e) << " < " << an.cols << ") " << acc << "\n";
             else o << indent << "  " << acc << "\n";
         }
-        // a NaN maximum replaces the running one (and makes the sum NaN)
-        o << indent << "  if (tm > " << P << " || tm != tm) { " << S << " = " << S << " * " << ex << "(" << P
-          << " - tm); " << P << " = tm; }\n";
+        // the running maximum becomes the maximum with this group's; the sum
+        // is rescaled when it changes (a NaN maximum makes the sum NaN)
+        o << indent << "  { const float pn = psk_rmax(" << P << ", tm); if (!(pn == " << P << ")) " << S << " = " << S
+          << " * " << ex << "(" << P << " - pn); " << P << " = pn; }\n";
         o << indent << "  const float mref = " << P << " == (-__builtin_inff()) ? 0.0f : " << P << ";\n";
         for (int e = 0; e < NE; ++e) {
             std::string acc = S + " = (" + S + " + " + ex + "(" + val(y, e) + " - mref));";

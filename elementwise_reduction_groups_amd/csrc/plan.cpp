@@ -64,7 +64,9 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
 {
     KernelPlan p;
     const int V = an.out_dtype == PSK_BF16 ? 8 : 4;
-    p.vec = (allow_vector && an.cols % V == 0) ? V : 1;
+    // 16-byte accesses where every per-element input allows them: a
+    // last-axis step of 1 and row starts at whole vectors
+    p.vec = (allow_vector && an.cols % V == 0 && inputs_vector_ok(an, V)) ? V : 1;
     p.nt = layout_value("nt", 1) != 0;
     if (an.tree) {
         // Workgroups of 128 threads; each thread takes `vec` consecutive

@@ -19,8 +19,8 @@ enum class InKind : int {
     Scalar = 0,     // every axis broadcast: one value for the whole output
     RowConst = 1,   // last axis broadcast: one value per row
     ColVec = 2,     // only the last axis varies: the same row vector for every row
-    General = 3,    // last axis contiguous, leading axes by their strides
-    Full = 4        // same shape as the output: flat index
+    General = 3,    // leading axes and the last axis by their strides
+    Full = 4        // dense, the output's shape: flat index
 };
 
 struct InputInfo {
@@ -28,7 +28,12 @@ struct InputInfo {
     int rank = 0;
     int64_t shape[PSK_MAX_RANK] = {0, 0, 0, 0};
     int64_t aligned[PSK_MAX_RANK] = {1, 1, 1, 1};  // shape right-aligned to the output's 4 axes
-    int64_t numel = 0;
+    // step of each of the output's 4 axes in elements: 0 where the input
+    // broadcasts (a size-1 axis, a stride-0 axis, an axis it does not have)
+    int64_t stride4[PSK_MAX_RANK] = {0, 0, 0, 0};
+    bool strided = false;        // the descriptor gave strides other than the dense ones
+    int64_t numel = 0;           // distinct elements read (the extents of the non-broadcast axes)
+    int64_t span = 0;            // 1 + the largest element offset read (0 when empty)
     InKind kind = InKind::Scalar;
     bool used = false;
     bool mask_guarded = false;   // read only where the group's mask (causal or WHERE) allows
@@ -60,6 +65,7 @@ struct Analysis {
     int out_rank = 1;
     int64_t out_shape4[PSK_MAX_RANK] = {1, 1, 1, 1};  // output right-aligned to 4 axes
     int64_t rows = 0, cols = 0, numel = 0;
+    int64_t max_span = 0;               // the largest input span (64-bit indexing beyond 2^31)
     bool row_kind = false;              // has at least one row reduction
     bool tree = false;                  // PSK_GROUP_TREE: mapped over tree leaves
     uint32_t flags = 0;
@@ -77,6 +83,9 @@ struct Analysis {
 
 // Validates the descriptor; on success fills `an`.
 psk_status analyse(const psk_group_desc* desc, Analysis& an);
+// Every input the kernel loads per element takes V-element vector accesses:
+// last-axis stride 1 and the other strides multiples of V.
+bool inputs_vector_ok(const Analysis& an, int V);
 
 bool op_is_leaf(int op);
 bool op_is_elementwise(int op);

@@ -8,6 +8,7 @@
 // with n > 2 never joining a group.  Row reductions are last-axis keepdim
 // reductions whose value feeds an elementwise epilogue (poot, "Fusion and
 // Planning", section "Reduction-rooted regions").
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <sstream>
@@ -75,6 +76,59 @@ static bool input_dtype_ok(int32_t d) { return dtype_ok(d) || d == PSK_U8; }
 
 static std::string at(int i) { return "node " + std::to_string(i) + ": "; }
 
+// The descriptor's rank where it can index its arrays (callers check the
+// rank itself where it matters).
+static int rank_of(const psk_tensor_desc& t) { return std::max(0, std::min<int>(t.rank, PSK_MAX_RANK)); }
+
+// Row-major strides of a shape (elements).
+static void dense_strides(const psk_tensor_desc& t, int64_t* st)
+{
+    int64_t s = 1;
+    for (int d = rank_of(t) - 1; d >= 0; --d) {
+        st[d] = s;
+        s *= t.shape[d] > 0 ? t.shape[d] : 1;
+    }
+}
+
+// Strides were given (some entry within the rank is nonzero) and differ
+// from the dense ones on an axis longer than 1.
+static bool strides_given(const psk_tensor_desc& t)
+{
+    for (int d = 0; d < rank_of(t); ++d)
+        if (t.stride[d] != 0) return true;
+    return false;
+}
+
+static bool strides_dense(const psk_tensor_desc& t)
+{
+    if (!strides_given(t)) return true;
+    int64_t st[PSK_MAX_RANK];
+    dense_strides(t, st);
+    for (int d = 0; d < rank_of(t); ++d)
+        if (t.shape[d] > 1 && t.stride[d] != st[d]) return false;
+    return true;
+}
+
+// Outputs (and tree-mapped inputs) are dense: zero or the dense strides.
+static psk_status dense_only(const psk_tensor_desc& t, const std::string& what)
+{
+    for (int d = 0; d < rank_of(t); ++d)
+        if (t.stride[d] < 0) return fail(PSK_E_SHAPE, what + ": negative stride");
+    if (!strides_dense(t)) return fail(PSK_E_UNSUPPORTED, what + " must be dense (row-major strides)");
+    return PSK_OK;
+}
+
+bool inputs_vector_ok(const Analysis& an, int V)
+{
+    for (const InputInfo& in : an.inputs) {
+        if (!in.used || in.kind == InKind::Scalar || in.kind == InKind::RowConst) continue;
+        if (in.stride4[3] != 1) return false;
+        for (int d = 0; d < 3; ++d)
+            if (in.stride4[d] % V != 0) return false;
+    }
+    return true;
+}
+
 psk_status analyse(const psk_group_desc* desc, Analysis& an)
 {
     if (!desc)
@@ -96,6 +150,10 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
     const psk_tensor_desc& o = desc->out;
     if (o.rank < 1 || o.rank > PSK_MAX_RANK)
         return fail(PSK_E_SHAPE, "output rank must be in 1..4");
+    {
+        psk_status st = dense_only(o, "the output");
+        if (st != PSK_OK) return st;
+    }
     if (!dtype_ok(o.dtype))
         return fail(PSK_E_TYPE, "output storage type must be f32 or bf16");
     an = Analysis();
@@ -130,40 +188,61 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
             return fail(PSK_E_TYPE, "input " + std::to_string(k) + ": a tree-mapped group has no mask inputs");
         in.dtype = (psk_dtype)t.dtype;
         in.rank = t.rank;
-        in.numel = 1;
         for (int d = 0; d < t.rank; ++d) {
             if (t.shape[d] < 0)
                 return fail(PSK_E_SHAPE, "input " + std::to_string(k) + ": negative size");
+            if (t.stride[d] < 0)
+                return fail(PSK_E_SHAPE, "input " + std::to_string(k) + ": negative stride");
             in.shape[d] = t.shape[d];
             in.aligned[PSK_MAX_RANK - t.rank + d] = t.shape[d];
-            in.numel *= t.shape[d];
         }
+        // each output axis's step in this input: the given strides (all zero
+        // means dense), 0 where the input broadcasts
+        int64_t dense[PSK_MAX_RANK] = {0, 0, 0, 0};
+        dense_strides(t, dense);
+        const bool given = strides_given(t);
+        in.strided = !strides_dense(t);
+        for (int d = 0; d < t.rank; ++d)
+            in.stride4[PSK_MAX_RANK - t.rank + d] = t.shape[d] == 1 ? 0 : (given ? t.stride[d] : dense[d]);
+        in.numel = 1;
+        in.span = 1;
+        for (int d = 0; d < PSK_MAX_RANK; ++d) {
+            if (in.aligned[d] == 0) in.numel = in.span = 0;
+            if (in.stride4[d] != 0) {
+                in.numel *= in.aligned[d];
+                in.span += (in.aligned[d] - 1) * in.stride4[d];
+            }
+        }
+        if (in.numel == 0) in.span = 0;
+        an.max_span = std::max(an.max_span, in.span);
         if (desc->flags & PSK_GROUP_TREE) {
             // leaf-mapped: rank 1 is one element per leaf element, rank 0 one
             // value for the whole tree; lengths are the leaves'
             if (t.rank > 1)
                 return fail(PSK_E_SHAPE, "a tree-mapped group's inputs have rank 1 (per element) or 0 (per tree)");
+            if (given && t.rank == 1 && t.stride[0] != 1)
+                return fail(PSK_E_UNSUPPORTED, "input " + std::to_string(k) + ": a tree-mapped group reads its "
+                                               "leaves densely");
             in.kind = t.rank == 0 ? InKind::Scalar : InKind::Full;
             continue;
         }
-        bool all1 = true, lead1 = true, same = true;
+        bool same = true;
         for (int d = 0; d < PSK_MAX_RANK; ++d) {
             int64_t a = in.aligned[d], od = an.out_shape4[d];
             if (a != od && a != 1)
                 return fail(PSK_E_BROADCAST, "input " + std::to_string(k) + ": axis " + std::to_string(d) +
                                                  " of length " + std::to_string(a) + " does not broadcast to " +
                                                  std::to_string(od) + " (an input may not widen the output)");
-            if (a != 1) all1 = false;
-            if (d < 3 && a != 1) lead1 = false;
             if (a != od) same = false;
         }
-        if (all1)
+        const bool lead0 = in.stride4[0] == 0 && in.stride4[1] == 0 && in.stride4[2] == 0;
+        if (lead0 && in.stride4[3] == 0)
             in.kind = InKind::Scalar;
-        else if (in.aligned[3] == 1)
+        else if (in.stride4[3] == 0)
             in.kind = InKind::RowConst;
-        else if (same)
+        else if (same && !in.strided)
             in.kind = InKind::Full;
-        else if (lead1)
+        else if (lead0)
             in.kind = InKind::ColVec;
         else
             in.kind = InKind::General;
@@ -244,6 +323,10 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
                                         " is already an output");
         if (!dtype_ok(desc->extra_out[k].dtype))
             return fail(PSK_E_TYPE, "extra output " + std::to_string(k) + ": storage type must be f32 or bf16");
+        {
+            psk_status st = dense_only(desc->extra_out[k], "extra output " + std::to_string(k));
+            if (st != PSK_OK) return st;
+        }
         an.stored[i] = k + 1;
         an.extras.push_back({i, (psk_dtype)desc->extra_out[k].dtype, false});
     }

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define PSK_VERSION 100
+#define PSK_VERSION 200
 #define PSK_MAX_MEMBERS 64      /* member (non-leaf) nodes per group */
 #define PSK_MAX_NODES 256       /* total nodes, leaves included */
 #define PSK_MAX_INPUTS 16
@@ -129,8 +129,9 @@ typedef enum psk_dtype { PSK_F32 = 0, PSK_BF16 = 1, PSK_U8 = 2 } psk_dtype;
  *   ROW_MAX ROW_SUM ROW_MEAN reduction over the last axis, keepdim; the
  *                            result broadcasts back along the row.  ROW_MEAN
  *                            is ROW_SUM divided by the row length.  ROW_MAX
- *                            over a row holding a NaN is NaN, whatever the
- *                            combining order (ties: the later element).
+ *                            is IEEE 754-2019 maximum over the row: NaN if
+ *                            any element is NaN, +0 above -0 (the same bits
+ *                            whatever the combining order).
  * Leaves: INPUT (iparam = input slot), CONST (imm = an f32 value).
  * Boundary ops (REDUCE, CONTRACT, CAST, OPAQUE) are accepted by
  * psk_partition only: a reduction ends a group, contractions and casts are
@@ -156,14 +157,31 @@ typedef struct psk_node {
     int32_t iparam;    /* PSK_OP_INPUT: slot; PSK_OP_POWN: n; PSK_OP_CAUSAL_MASK: T */
 } psk_node;
 
-/* A dense row-major tensor.  Inputs align with the output from the last
- * axis; an input axis of length 1 broadcasts (numpy's rule, which the
- * configs' [N,1] and [1,N] inputs use); an input may never widen the output
- * (PSK-Realize, "What a group is": inputs may be smaller and broadcast). */
+/* A tensor: shape, storage type and the step of each axis in elements.
+ * Inputs align with the output from the last axis; an input axis of length
+ * 1 broadcasts (numpy's rule, which the configs' [N,1] and [1,N] inputs
+ * use); an input may never widen the output (PSK-Realize, "What a group
+ * is": inputs may be smaller and broadcast).  One compiled kernel serves
+ * the layout the descriptor states (poot, "Fusion and Planning", "Launch
+ * metadata": the metadata a kernel is specialised on).
+ *
+ * Strides: all zero (over the rank) means dense row-major, so a descriptor
+ * filled with zeros but for rank, dtype and shape is dense.  Otherwise
+ * stride[d] is axis d's step in elements, >= 0, and 0 broadcasts the axis
+ * (a view expanded along it): a transposed or sliced view is read in place,
+ * with no copy.  An input whose last-axis stride is 1 and whose other
+ * strides are multiples of the vector width (4 elements for an f32 output,
+ * 8 for bf16) takes 16-byte accesses; any other layout the element path.
+ * A tensor expanded from one element along every axis is given as rank 0
+ * (or with sizes 1), since all-zero strides mean dense.  Outputs, extra
+ * outputs and the inputs of tree-mapped groups are dense (their strides
+ * must be zero or the dense ones: PSK_E_UNSUPPORTED otherwise); negative
+ * strides are refused (PSK_E_SHAPE). */
 typedef struct psk_tensor_desc {
     int32_t rank;                    /* 0..PSK_MAX_RANK (output: 1..PSK_MAX_RANK) */
     int32_t dtype;                   /* psk_dtype */
     int64_t shape[PSK_MAX_RANK];     /* entries at and beyond rank are ignored */
+    int64_t stride[PSK_MAX_RANK];    /* elements; all zero: dense row-major */
 } psk_tensor_desc;
 
 typedef struct psk_group_desc {
@@ -226,8 +244,8 @@ typedef struct psk_tree psk_tree;
 psk_status psk_group_create(const psk_group_desc* desc, psk_group** out);
 
 /* Run the group as one kernel launch.  inputs[k] is the device address of
- * input slot k laid out as desc.inputs[k]; out is the device address of the
- * output.  The output may be the same buffer as an input of the same shape
+ * input slot k's first element, laid out as desc.inputs[k] (shape and
+ * strides); out is the device address of the (dense) output.  The output may be the same buffer as an input of the same shape
  * and storage type (in place); any other overlap with an input is refused
  * (PSK_E_ALIAS).  Pointers must be aligned to their element size
  * (PSK_E_ALIGN); 16-byte alignment takes the vector path.  Empty outputs

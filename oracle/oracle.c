@@ -109,12 +109,21 @@ static float orc_max(float x, float y) { return (x > y) ? x : y; }
 static float orc_min(float x, float y) { return (x < y) ? x : y; }
 
 /* One step of a row maximum folded left to right: the running maximum m
- * against the next element y.  The pages give max's tie rule (the second
- * operand) but no rule for NaN; a reduction's result must not depend on the
- * order its elements are combined in, so a NaN anywhere in the row makes the
- * row maximum NaN (as IEEE 754-2019 maximum does), and ties still go to the
- * later element. */
-static float orc_row_max_step(float m, float y) { return (m != m) ? m : ((m > y) ? m : y); }
+ * against the next element y.  The pages give elementwise max's tie rule
+ * (the second operand) but nothing a reduction could keep independent of
+ * the order its elements are combined in; the row maximum is IEEE 754-2019
+ * maximum folded over the row: NaN if any element is NaN, otherwise the
+ * largest element, +0 counting above -0. */
+static float orc_row_max_step(float m, float y)
+{
+    if (m != m)
+        return m;
+    if (y != y)
+        return y;
+    if (m == y)                 /* equal: the same bits, or zeros of both signs (+0 wins) */
+        return signbit(m) ? y : m;
+    return (m > y) ? m : y;
+}
 
 /* -------------------------------------------------- generic group evaluator */
 /* Op codes of this oracle (its own numbering). */

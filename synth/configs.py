@@ -353,3 +353,45 @@ def softmax_dag(scale: float = 0.125) -> List[Node]:
         %6 = row_sum %5
         %7 = div %5 %6
     """)
+
+
+# ---------------------------------------------------------------------------
+# A measurement workload: the VALU rate an emitted pointwise kernel sustains.
+def valu_ceiling_dag(chains: int = 8, depth: int = 7) -> List[Node]:
+    """64 members of add and mul only: x = B + C over a [R, 1] and a [1, N]
+    input (so the output's 4 bytes are the only HBM traffic an element
+    costs), then `chains` independent chains of `depth` alternating
+    multiplications and additions by constants starting from x (values stay
+    within a few units: each chain contracts towards a fixed point), summed
+    pairwise at the end.  Every member is one f32 operation, so it is one
+    vector instruction of the emitted kernel."""
+    lines = ["%0 = input 0", "%1 = input 1", "%2 = add %0 %1"]
+    consts = {}
+
+    def const(v):
+        if v not in consts:
+            consts[v] = len(lines)
+            lines.append(f"%{len(lines)} = const {float(v).hex()}")
+        return consts[v]
+
+    ends = []
+    for c in range(chains):
+        cur = 2
+        for d in range(depth):
+            if d % 2 == 0:
+                k = const(0.5 + 0.0625 * ((c + d) % 7))
+                lines.append(f"%{len(lines)} = mul %{cur} %{k}")
+            else:
+                k = const(-0.375 + 0.125 * ((c * 3 + d) % 7))
+                lines.append(f"%{len(lines)} = add %{cur} %{k}")
+            cur = len(lines) - 1
+        ends.append(cur)
+    while len(ends) > 1:
+        nxt = []
+        for a, b in zip(ends[0::2], ends[1::2]):
+            lines.append(f"%{len(lines)} = add %{a} %{b}")
+            nxt.append(len(lines) - 1)
+        if len(ends) % 2:
+            nxt.append(ends[-1])
+        ends = nxt
+    return parse_dag("\n".join(lines) + "\n")

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
     missing = [n for n in names if n not in exported]
     assert not missing, missing
     assert set(P.EXPORTED) <= exported
-    assert P.psk_version() == 100
+    assert P.psk_version() == P.PSK_VERSION == 200
 
 
 def test_status_strings(lib):
@@ -574,3 +574,60 @@ def test_kernel_cache_keys_on_every_immediate(lib):
     c1 = _desc("%0 = input 0\n%1 = const 2.0\n%2 = mul %0 %1\n", F, (8, 16))
     c2 = _desc("%0 = input 0\n%1 = const 3.0\n%2 = mul %0 %1\n", F, (8, 16))
     assert P.psk_group_code_object(c1) != P.psk_group_code_object(c2)
+
+
+def test_strided_inputs_host(lib):
+    """Strided input descriptors: a transposed or sliced view is described in
+    place; vector accesses only where every per-element input has a unit
+    last-axis step and vector-aligned rows; dense strides given explicitly
+    are the dense layout; the strides are part of the kernel's key."""
+    from synth import configs as C
+    R, N = 64, 512
+    soft = C.softmax_dag(0.125)
+    dense = P.Group(soft, [((R, N), "f32")], (R, N), "f32")
+    given = P.Group(soft, [((R, N), "f32", (N, 1))], (R, N), "f32")
+    assert dense.info.kernel == given.info.kernel and dense.info.vec == 4
+    sliced = P.Group(soft, [((R, N), "f32", (2 * N, 1))], (R, N), "f32")
+    assert sliced.info.vec == 4 and sliced.info.kernel != dense.info.kernel
+    odd = P.Group(soft, [((R, N), "f32", (N + 2, 1))], (R, N), "f32")        # rows not at whole vectors
+    transposed = P.Group(soft, [((R, N), "f32", (1, R))], (R, N), "f32")
+    assert odd.info.vec == 1 and transposed.info.vec == 1
+    # an expanded [R, 1] input (stride 0 along the row) is one value a row
+    d = _desc("%0 = input 0\n%1 = input 1\n%2 = add %0 %1\n", [((R, N), "f32"), ((R, N), "f32", (1, 0))], (R, N))
+    src = P.psk_group_source(d)
+    assert "xr1" in src
+    # refusals: negative strides, strided outputs and extra outputs, tree leaves read with a step
+    neg = _desc("%0 = input 0\n%1 = neg %0\n", [((R, N), "f32", (N, 1))], (R, N))
+    neg.desc.inputs[0].stride[1] = -1
+    _refused(neg, P.PSK_E_SHAPE)
+    with pytest.raises(ValueError):
+        P.tensor_desc((R, N), "f32", (N, -1))
+    nd = parse_dag("%0 = input 0\n%1 = neg %0\n")
+    bad_out = P.GroupDesc(nd, F, (8, 16), "f32")
+    bad_out.desc.out.stride[0], bad_out.desc.out.stride[1] = 32, 1
+    _refused(bad_out, P.PSK_E_UNSUPPORTED)
+    extra = P.GroupDesc(parse_dag("%0 = input 0\n%1 = neg %0\n%2 = neg %1\n"), F, (8, 16), "f32",
+                        extras=[(1, (8, 16), "f32")])
+    extra.desc.extra_out[0].stride[0], extra.desc.extra_out[0].stride[1] = 16, 2
+    _refused(extra, P.PSK_E_UNSUPPORTED)
+    tree = P.GroupDesc(C.tree_sgd_dag(), [((1,), "f32", (2,)), ((1,), "f32"), ((), "f32")], (1,), "f32",
+                       flags=P.PSK_GROUP_TREE)
+    _refused(tree, P.PSK_E_UNSUPPORTED)
+    # the binding refuses all-zero strides of a tensor larger than one element
+    with pytest.raises(ValueError):
+        P.tensor_desc((4, 8), "f32", (0, 0))
+
+
+def test_strided_inputs_compile(lib, tmp_path):
+    """Element-path and vector-path strided kernels, and a 64-bit offset when
+    a view's span passes 2^31 elements, compile for gfx950."""
+    from synth import configs as C
+    for name, spec, out in [("transposed", ((512, 384), "bf16", (1, 512)), (512, 384)),
+                            ("sliced", ((512, 384), "bf16", (1024, 1)), (512, 384)),
+                            ("huge_span", ((2, 8), "f32", (1 << 31, 1)), (2, 8))]:
+        d = P.GroupDesc(C.softmax_dag(0.125), [spec], out, spec[1])
+        src = P.psk_group_source(d)
+        if name == "huge_span":
+            assert "long long" in src[src.index('extern "C"'):]
+        asm, _ = _isa(P.psk_group_code_object(d), tmp_path, name)
+        assert "scratch_" not in asm

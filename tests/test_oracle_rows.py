@@ -150,8 +150,9 @@ def test_rmsnorm_vs_f64(orc):
 # ------------------------------------------------------------ row maximum
 def test_row_max_nan_and_ties(orc):
     """The row maximum against numpy's maximum, which returns NaN for a row
-    holding a NaN wherever it stands; and at a tie of signed zeros the later
-    element (max's tie rule), checked on its sign bit."""
+    holding a NaN wherever it stands; and signed zeros as IEEE 754-2019
+    maximum orders them (+0 above -0, whatever the order in the row),
+    checked on the sign bit."""
     from synth.dag import parse_dag
     nodes = parse_dag("%0 = input 0\n%1 = row_max %0\n%2 = sub %0 %1\n")
     rng = np.random.default_rng(11)
@@ -164,10 +165,21 @@ def test_row_max_nan_and_ties(orc):
     want = x.max(axis=1, keepdims=True)
     assert np.array_equal(np.isnan(mx), np.isnan(want))
     assert np.array_equal(mx[~np.isnan(want)], want[~np.isnan(want)])
-    z = np.array([[-0.0, 0.0], [0.0, -0.0], [-1.0, -0.0], [-0.0, -1.0]], np.float32)
-    mz = np.zeros((4, 1), np.float32)
+    z = np.array([[-0.0, 0.0, -1.0], [0.0, -0.0, -1.0], [-1.0, -0.0, -0.0], [-0.0, -1.0, -2.0],
+                  [-0.0, 0.0, -0.0]], np.float32)
+    mz = np.zeros((5, 1), np.float32)
     orc.eval_group(nodes, [z], z.shape, extras=[(1, mz)])
-    assert list(np.signbit(mz[:, 0])) == [False, True, True, True]
+    assert np.all(mz == 0) and list(np.signbit(mz[:, 0])) == [False, False, True, True, False]
+    # any order of a row gives the same bits
+    rng2 = np.random.default_rng(12)
+    w = rng2.choice(np.array([-0.0, 0.0, -3.0, 2.0, np.nan, -np.inf], np.float32), size=(200, 6))
+    m1 = np.zeros((200, 1), np.float32)
+    m2 = np.zeros((200, 1), np.float32)
+    orc.eval_group(nodes, [w], w.shape, extras=[(1, m1)])
+    orc.eval_group(nodes, [np.ascontiguousarray(w[:, ::-1])], w.shape, extras=[(1, m2)])
+    assert np.array_equal(np.isnan(m1), np.isnan(m2))
+    fin = ~np.isnan(m1)
+    assert np.array_equal(m1[fin].view(np.uint32), m2[fin].view(np.uint32))
 
 
 def test_softmax_row_with_nan_is_nan(orc):
