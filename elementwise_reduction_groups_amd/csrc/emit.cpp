@@ -236,6 +236,15 @@ __device__ __forceinline__ float psk_min(float a, float b) { return (a < b) ? a 
 // gives NaN; +0 above -0), so the row's maximum does not depend on the order
 // lanes and waves combine in; v_maximum3_f32 takes two elements a step
 __device__ __forceinline__ float psk_rmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+// the same step by compares and selects, for kernels at their register cap
+// (the tiled row kernel): there the compiler's scheduling around the
+// maximum instructions spilled registers.  A NaN on either side gives NaN;
+// of two equal values the bitwise AND is that value, and +0 for zeros of
+// both signs
+__device__ __forceinline__ float psk_rmax_s(float a, float b) {
+  const float r = (a > b || a != a) ? a : b;
+  return (a == b) ? __uint_as_float(__float_as_uint(a) & __float_as_uint(b)) : r;
+}
 #define PSK_DPP(x, ctl) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (x)), (ctl), 0xF, 0xF, false))
 #define PSK_RL(x, l) __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, (x)), (l)))
 // all-reduce within each 16-lane row: xor 1, xor 2 (quad_perm), then the
@@ -1154,7 +1163,8 @@ struct Emitter {
             }
             for (int e = 0; e < NE; ++e) {
                 std::string v = val(nd.a, e);
-                std::string acc = mx ? "psk_rmax(p" + std::to_string(i) + ", " + v + ")"
+                std::string acc = mx ? std::string(pl.kind == 3 ? "psk_rmax_s(p" : "psk_rmax(p") + std::to_string(i) +
+                                           ", " + v + ")"
                                      : "(p" + std::to_string(i) + " + " + v + ")";
                 if (ragged)
                     o << indent << "if (" << col(e) << " < " << an.cols << ") p" << i << " = " << acc << ";\n";
@@ -1181,7 +1191,8 @@ struct Emitter {
         const std::string ex = online_exp(sm);
         o << indent << "{\n" << indent << "  float tm = (-__builtin_inff());\n";
         for (int e = 0; e < NE; ++e) {
-            std::string acc = "tm = psk_rmax(tm, " + val(y, e) + ");";
+            std::string acc = std::string("tm = ") + (pl.kind == 3 ? "psk_rmax_s" : "psk_rmax") + "(tm, " +
+                              val(y, e) + ");";
             if (ragged) o << indent << "  if (" << col(e) << " < " << an.cols << ") " << acc << "\n";
             else o << indent << "  " << acc << "\n";
         }

@@ -360,3 +360,39 @@ def test_signed_zeros_through_fused_expressions():
         assert_bits(to_np(out), ref, f"(0 - y)(x + 0), offset {offset}")
         for (m, r), t in zip(refx, xo):
             assert_bits(to_np(t), r, f"member {m}, offset {offset}")
+
+
+@pytest.mark.parametrize("layout", ["", "tiled=1,lanes=128,tn=1,rc=1,lc=1", "persist=2", "lanes=32"])
+def test_row_max_signed_zeros_and_nan(layout, monkeypatch):
+    """The row maximum over rows of signed zeros, NaNs, -inf and a few
+    values, stored per row and subtracted from the row: IEEE 754-2019
+    maximum (+0 above -0, NaN anywhere gives NaN) whatever the kernel's
+    combining order, bit for bit against the oracle's sequential fold
+    (NaN compared as NaN)."""
+    if layout:
+        monkeypatch.setenv("PSK_LAYOUT", layout)
+    from synth.dag import parse_dag
+    nodes = parse_dag("%0 = input 0\n%1 = row_max %0\n%2 = sub %0 %1\n")
+    R, C = 96, 1000
+    vals = np.array([-0.0, 0.0, -1.0, -2.5, -np.inf, np.nan, 3.5], np.float32)
+    rng = np.random.default_rng(21)
+    x = np.empty((R, C), np.float32)
+    for r in range(R):
+        pool = vals[: 2 + r % 5] if r % 7 else vals          # rows of only zeros, of zeros and negatives, ...
+        x[r] = rng.choice(pool, size=C)
+    x[3, :] = -0.0
+    x[4, :] = 0.0
+    x[5, ::2], x[5, 1::2] = -0.0, 0.0
+    xt = torch.from_numpy(x).to(DEV)
+    g = P.Group(nodes, [((R, C), "f32")], (R, C), "f32", extras=[(1, (R, 1), "f32")])
+    out = torch.full((R, C), float("nan"), device=DEV)
+    mx = torch.full((R, 1), float("nan"), device=DEV)
+    g.run([xt], out, extra_outs=[mx])
+    torch.cuda.synchronize()
+    rmx = np.zeros((R, 1), np.float32)
+    ref = oracle.eval_group(nodes, [x], (R, C), extras=[(1, rmx)])
+    for name, got, r in (("row max", to_np(mx), rmx), ("x - row max", to_np(out), ref)):
+        nan = np.isnan(r)
+        assert np.array_equal(np.isnan(got), nan), f"{layout}: {name} NaN positions differ"
+        assert_bits(got[~nan], r[~nan], f"{layout}: {name}")
+    assert np.signbit(rmx[3, 0]) and not np.signbit(rmx[4, 0]) and not np.signbit(rmx[5, 0])
