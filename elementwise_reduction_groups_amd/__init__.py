@@ -79,7 +79,7 @@ class psk_group_info(ctypes.Structure):
                 ("phases", ctypes.c_int32), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("lanes_per_row", ctypes.c_int32), ("vec", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("rows_per_block", ctypes.c_int32), ("algorithmic_bytes", ctypes.c_int64),
-                ("kernel", ctypes.c_char * 48), ("tiles", ctypes.c_int32)]
+                ("kernel", ctypes.c_char * 48), ("tiles", ctypes.c_int32), ("split", ctypes.c_int32)]
 
 
 class psk_leaf(ctypes.Structure):
@@ -120,7 +120,7 @@ EXPORTED = ["psk_group_create", "psk_group_run", "psk_group_destroy", "psk_group
             "psk_adamw_step_config_noalloc", "psk_adamw_lr",
             "psk_tree_clip_result", "psk_group_run_tree", "psk_group_run_multi", "psk_group_run_tree_multi",
             "psk_partition", "psk_partition_ex", "psk_dispatch_count", "psk_last_error",
-            "psk_status_str", "psk_version", "psk_get_stats"]
+            "psk_status_str", "psk_version", "psk_get_stats", "psk_group_check"]
 
 
 def lib() -> ctypes.CDLL:
@@ -138,6 +138,7 @@ def lib() -> ctypes.CDLL:
     L.psk_group_run.argtypes = [vp, ctypes.POINTER(vp), vp, vp]
     L.psk_group_destroy.argtypes = [vp]
     L.psk_group_destroy.restype = None
+    L.psk_group_check.argtypes = [vp]
     L.psk_group_get_info.argtypes = [vp, ctypes.POINTER(psk_group_info)]
     L.psk_group_source.argtypes = [ctypes.POINTER(psk_group_desc), ctypes.c_char_p, sz, ctypes.POINTER(sz)]
     L.psk_group_code_object.argtypes = [ctypes.POINTER(psk_group_desc), vp, sz, ctypes.POINTER(sz)]
@@ -280,6 +281,12 @@ def psk_group_run_multi(group: int, inputs: Sequence[int], outs: Sequence[int], 
     arr = (ctypes.c_void_p * max(1, len(inputs)))(*[ctypes.c_void_p(p) for p in inputs])
     oa = (ctypes.c_void_p * len(outs))(*[ctypes.c_void_p(p) for p in outs])
     _check(lib().psk_group_run_multi(ctypes.c_void_p(group), arr, oa, ctypes.c_void_p(stream or 0)))
+
+
+def psk_group_check(group: int):
+    """Raises PskError (PSK_E_HIP) when a bounded wait of the group's split
+    rows ran out since the last check (waits for the device first)."""
+    _check(lib().psk_group_check(ctypes.c_void_p(group)))
 
 
 def psk_group_destroy(group: int):
@@ -517,6 +524,10 @@ class Group:
     @property
     def info(self) -> psk_group_info:
         return psk_group_get_info(self.handle)
+
+    def check(self):
+        """psk_group_check: raises if a split-row wait of this group ran out."""
+        psk_group_check(self.handle)
 
     def run(self, inputs, out, stream=None, extra_outs=None):
         """extra_outs: one tensor per extra output (a group with extra outputs

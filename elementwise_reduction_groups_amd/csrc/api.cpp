@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -58,6 +59,7 @@ struct Kernel {
     std::mutex mu;
     hipModule_t mod[kMaxDevices] = {};
     hipFunction_t fn[kMaxDevices] = {};
+    int capacity[kMaxDevices] = {};   // split rows: workgroups the device holds at once (0: not yet asked)
 };
 
 static std::mutex g_cache_mu;
@@ -67,9 +69,33 @@ static std::map<std::string, std::shared_ptr<Kernel>>& cache()
     return *m;
 }
 
+static psk_status get_kernel_plan(const Analysis& an, const KernelPlan& plan, std::shared_ptr<Kernel>& out);
+
+// A split-rows kernel holds its segment in registers: the planned width is
+// compiled first and, if the compiled kernel spills registers, narrower
+// segments (more workgroups a row) are tried; if every width spills, the
+// tiled kernel takes the group.  Other plans compile as planned.
 static psk_status get_kernel(const Analysis& an, bool vector, std::shared_ptr<Kernel>& out)
 {
     KernelPlan plan = plan_kernel(an, vector);
+    if (plan.kind != 4) return get_kernel_plan(an, plan, out);
+    const int first = plan.nv * plan.vec;
+    const int widths[] = {first, 48, 32, 16};
+    for (int i = 0; i < 4; ++i) {
+        const int ept = widths[i];
+        if (i > 0 && ept >= first) continue;
+        KernelPlan p = plan_kernel(an, vector, ept);
+        if (p.kind != 4) break;
+        psk_status st = get_kernel_plan(an, p, out);
+        if (st != PSK_OK) return st;
+        if (code_scratch_bytes(out->code) == 0) return PSK_OK;
+        if (std::getenv("PSK_LAYOUT") && std::strstr(std::getenv("PSK_LAYOUT"), "sept=")) return PSK_OK;
+    }
+    return get_kernel_plan(an, plan_kernel(an, vector, 0), out);
+}
+
+static psk_status get_kernel_plan(const Analysis& an, const KernelPlan& plan, std::shared_ptr<Kernel>& out)
+{
     std::string canon = canonical_text(an);
     std::string key = canon + plan.key();
     {
@@ -84,7 +110,7 @@ static psk_status get_kernel(const Analysis& an, bool vector, std::shared_ptr<Ke
     auto k = std::make_shared<Kernel>();
     k->plan = plan;
     char nm[64];
-    static const char* const kind_name[4] = {"pw", "row", "tree", "rowt"};
+    static const char* const kind_name[5] = {"pw", "row", "tree", "rowt", "rows"};
     std::snprintf(nm, sizeof nm, "psk_%s_%016llx", kind_name[plan.kind], (unsigned long long)fnv1a(key));
     k->name = nm;
     std::string src = emit_source(an, plan, k->name);
@@ -122,12 +148,82 @@ static int esize(int dt) { return dt == PSK_BF16 ? 2 : dt == PSK_U8 ? 1 : 4; }
 using namespace psk;
 
 // ------------------------------------------------------------------ groups
+// Device state of a split-rows kernel on one device: the generation counter,
+// the count of finished workgroups, the status word of the bounded waits,
+// then the teams' partial slots (teams x exchanged values x K, 8 bytes each).
+struct SplitState {
+    void* mem = nullptr;
+    int64_t teams = 0;
+};
+
 struct psk_group {
     Analysis an;
     std::shared_ptr<Kernel> vec;      // 16-byte accesses
     std::shared_ptr<Kernel> scalar;   // element accesses (compiled on first need)
     std::mutex mu;
+    SplitState split[kMaxDevices][2];   // [device][vector, element kernel]
+    int wait_limit = 1 << 20;           // tries a bounded wait makes (PSK_SPLIT_WAIT overrides)
+    ~psk_group()
+    {
+        for (auto& d : split)
+            for (auto& st : d)
+                if (st.mem) (void)hipFree(st.mem);
+    }
 };
+
+// The launch shape of a split-rows kernel on the current device: teams of K
+// workgroups, the whole grid no larger than what the device holds at once
+// (so every member of a team runs while the others wait for it); teams of
+// one XCD when the grid is a multiple of 8 K.  Allocates the device state on
+// the first run on a device (zeroed: generation 0, no tags).
+static psk_status split_launch(psk_group* g, Kernel& k, int which, hipFunction_t fn, int64_t rows, int64_t& teams,
+                               int& xmap, void*& mem)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    const int K = k.plan.split;
+    std::lock_guard<std::mutex> lk(g->mu);
+    {
+        std::lock_guard<std::mutex> lk2(k.mu);
+        if (!k.capacity[dev]) {
+            int per_cu = 0, cus = 0;
+            e = hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, k.plan.block, 0);
+            if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            if (e != hipSuccess) return fail(PSK_E_HIP, std::string("occupancy query: ") + hipGetErrorString(e));
+            k.capacity[dev] = per_cu * cus;
+        }
+    }
+    const int64_t cap = k.capacity[dev];
+    if (cap < K)
+        return fail(PSK_E_UNSUPPORTED, "the device holds " + std::to_string(cap) + " of these workgroups at once; a "
+                                       "row needs " + std::to_string(K));
+    teams = cap / K;
+    xmap = 0;
+    if (cap >= 8 * K) {
+        teams = (cap / (8 * K)) * 8;
+        xmap = 1;
+    }
+    SplitState& st = g->split[dev][which];
+    if (!st.mem) {
+        const size_t bytes = 16 + (size_t)teams * k.plan.exch * K * 8;
+        e = hipMalloc(&st.mem, bytes);
+        if (e == hipSuccess) e = hipMemset(st.mem, 0, bytes);
+        if (e != hipSuccess) {
+            if (st.mem) (void)hipFree(st.mem);
+            st.mem = nullptr;
+            return fail(PSK_E_HIP, std::string("split-row state: ") + hipGetErrorString(e));
+        }
+        st.teams = teams;
+    }
+    teams = std::min(teams, st.teams);
+    if (teams > rows) {
+        teams = rows;
+        xmap = 0;
+    }
+    mem = st.mem;
+    return PSK_OK;
+}
 
 extern "C" psk_status psk_group_create(const psk_group_desc* desc, psk_group** out)
 {
@@ -142,6 +238,7 @@ extern "C" psk_status psk_group_create(const psk_group_desc* desc, psk_group** o
     st = get_kernel(g->an, true, g->vec);
     if (st != PSK_OK) return st;
     if (g->vec->plan.vec == 1) g->scalar = g->vec;
+    if (const char* w = std::getenv("PSK_SPLIT_WAIT")) g->wait_limit = std::max(0, std::atoi(w));
     *out = g.release();
     return PSK_OK;
 }
@@ -160,11 +257,12 @@ extern "C" psk_status psk_group_get_info(const psk_group* group, psk_group_info*
     info->phases = an.phases;
     info->rows = an.rows;
     info->cols = an.cols;
-    info->lanes_per_row = (p.kind == 1 || p.kind == 3) ? p.lanes : 1;
+    info->lanes_per_row = (p.kind == 1 || p.kind == 3) ? p.lanes : p.kind == 4 ? p.lanes * p.split : 1;
     info->vec = p.vec;
     info->block = p.block;
-    info->rows_per_block = (p.kind == 1 || p.kind == 3) ? p.rows_per_block : 0;
+    info->rows_per_block = (p.kind == 1 || p.kind == 3 || p.kind == 4) ? p.rows_per_block : 0;
     info->tiles = p.tiles;
+    info->split = p.split;
     int64_t bytes = an.numel * esize(an.out_dtype);
     for (const InputInfo& in : an.inputs)
         if (in.used) bytes += in.numel * esize(in.dtype);
@@ -241,13 +339,33 @@ static psk_status run_group(const psk_group* group, const void* const* inputs, v
     std::vector<void*> args;
     std::vector<const void*> ptrs(an.inputs.size());
     for (size_t i = 0; i < an.inputs.size(); ++i) ptrs[i] = inputs ? inputs[i] : nullptr;
-    long long n_total = (k->plan.kind == 1 || k->plan.kind == 3) ? (long long)an.rows : (long long)an.numel;
+    const KernelPlan& p = k->plan;
+    long long n_total = (p.kind == 1 || p.kind == 3 || p.kind == 4) ? (long long)an.rows : (long long)an.numel;
     for (size_t i = 0; i < ptrs.size(); ++i) args.push_back(&ptrs[i]);
     std::vector<void*> optr(outs, outs + n_out);
     for (int i = 0; i < n_out; ++i) args.push_back(&optr[i]);
     args.push_back(&n_total);
-    const KernelPlan& p = k->plan;
-    hipError_t e = hipModuleLaunchKernel(fn, (unsigned)p.grid, 1, 1, (unsigned)p.block, 1, 1, 0,
+    int64_t grid = p.grid;
+    void* xslots = nullptr;
+    unsigned* xstate = nullptr;
+    unsigned teams = 0;
+    int xmap = 0, limit = group->wait_limit;
+    if (p.kind == 4) {
+        int64_t t = 0;
+        void* mem = nullptr;
+        st = split_launch(const_cast<psk_group*>(group), *k, k == group->vec ? 0 : 1, fn, an.rows, t, xmap, mem);
+        if (st != PSK_OK) return st;
+        xstate = static_cast<unsigned*>(mem);
+        xslots = static_cast<char*>(mem) + 16;
+        teams = (unsigned)t;
+        grid = t * p.split;
+        args.push_back(&xslots);
+        args.push_back(&xstate);
+        args.push_back(&teams);
+        args.push_back(&xmap);
+        args.push_back(&limit);
+    }
+    hipError_t e = hipModuleLaunchKernel(fn, (unsigned)grid, 1, 1, (unsigned)p.block, 1, 1, 0,
                                          static_cast<hipStream_t>(hip_stream), args.data(), nullptr);
     if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipModuleLaunchKernel: ") + hipGetErrorString(e));
     count_launch();
@@ -262,6 +380,36 @@ extern "C" psk_status psk_group_run(const psk_group* group, const void* const* i
         return fail(PSK_E_UNSUPPORTED, "the group has extra outputs: run it with psk_group_run_multi");
     void* outs[1] = {out};
     return run_group(group, inputs, outs, hip_stream);
+}
+
+extern "C" psk_status psk_group_check(const psk_group* group)
+{
+    clear_error();
+    if (!group) return fail(PSK_E_NULL, "group is NULL");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) return fail(PSK_E_HIP, "hipGetDevice failed");
+    psk_group* g = const_cast<psk_group*>(group);
+    std::lock_guard<std::mutex> lk(g->mu);
+    bool any = false;
+    for (auto& st : g->split[dev]) any = any || st.mem;
+    if (!any) return PSK_OK;
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail(PSK_E_HIP, std::string("hipDeviceSynchronize: ") + hipGetErrorString(e));
+    unsigned timed_out = 0;
+    for (auto& st : g->split[dev]) {
+        if (!st.mem) continue;
+        unsigned w = 0;
+        e = hipMemcpy(&w, static_cast<unsigned*>(st.mem) + 2, sizeof w, hipMemcpyDeviceToHost);
+        if (e == hipSuccess && w) e = hipMemset(static_cast<unsigned*>(st.mem) + 2, 0, sizeof w);
+        if (e != hipSuccess) return fail(PSK_E_HIP, std::string("reading the wait status: ") + hipGetErrorString(e));
+        timed_out |= w;
+    }
+    if (timed_out)
+        return fail(PSK_E_HIP, "a run's workgroups sharing a row waited past their bound for one another (the "
+                               "device was shared, or its workgroups did not all run at once): that run's "
+                               "results are not valid");
+    return PSK_OK;
 }
 
 extern "C" psk_status psk_group_run_multi(const psk_group* group, const void* const* inputs, void* const* outs,

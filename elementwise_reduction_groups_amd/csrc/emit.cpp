@@ -282,6 +282,33 @@ __device__ __forceinline__ float psk_max64(float x) {
 }
 )PSK";
 
+// Split rows: the workgroups that share a row exchange their partial row
+// values through device memory.  A partial travels with its tag in one
+// 64-bit word, stored and loaded as a relaxed atomic at device scope: a
+// reader that sees the tag sees that value, so no fence is needed.  Waits
+// are bounded: a wait that runs out of tries (or finds that another wait
+// of the launch already has) records it in *status and goes on with what
+// it holds (the host reports it; the row's results are then not to be
+// used).  Nothing is stored through the scalar cache.
+const char* kSplitPrelude = R"PSK(
+__device__ __forceinline__ void psk_put(unsigned long long* p, unsigned tag, float v) {
+  __hip_atomic_store(p, ((unsigned long long)tag << 32) | (unsigned long long)__float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float psk_take(unsigned long long* p, unsigned tag, int limit, unsigned* status) {
+  unsigned long long w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int n = 0; (unsigned)(w >> 32) != tag; ++n) {
+    if (n >= limit || __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+      __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return __uint_as_float((unsigned)w);
+}
+)PSK";
+
 struct Emitter {
     const Analysis& an;
     const KernelPlan& pl;
@@ -358,7 +385,7 @@ struct Emitter {
                 gelu_path[opnd[k]] = std::max(gelu_path[opnd[k]], via);
             }
         }
-        NE = (pl.kind == 1 || pl.kind == 3 ? pl.nv : 1) * pl.vec;   // tree: elements per thread
+        NE = (pl.kind == 1 || pl.kind == 3 || pl.kind == 4 ? pl.nv : 1) * pl.vec;   // tree: elements per thread
         big = an.numel >= (int64_t(1) << 31) - 4096 || an.max_span >= (int64_t(1) << 31) - 4096;
         for (auto& nd : an.nodes)
             if (nd.op == PSK_OP_CAUSAL_MASK) period = nd.iparam;
@@ -366,6 +393,8 @@ struct Emitter {
             ragged = (int64_t)pl.nv * pl.lanes * pl.vec != an.cols;
         if (pl.kind == 3)
             ragged = an.cols % ((int64_t)pl.nv * pl.lanes * pl.vec) != 0;
+        if (pl.kind == 4)
+            ragged = (int64_t)pl.split * pl.nv * pl.lanes * pl.vec != an.cols;
     }
 
     const char* I() const { return big ? "long long" : "int"; }
@@ -374,7 +403,7 @@ struct Emitter {
     std::string col(int e) const
     {
         int k = e / pl.vec, j = e % pl.vec;
-        if (pl.kind == 1 || pl.kind == 3)
+        if (pl.kind == 1 || pl.kind == 3 || pl.kind == 4)
             return "(c" + std::to_string(k) + " + " + std::to_string(j) + ")";
         return "(c0 + " + std::to_string(j) + ")";
     }
@@ -822,7 +851,11 @@ struct Emitter {
             o << "const void* in" << k << "_, ";
         o << "void* out_, ";
         for (size_t k = 0; k < an.extras.size(); ++k) o << "void* xo" << k << "_, ";
-        o << "long long n_total)\n{\n";
+        o << "long long n_total";
+        if (pl.kind == 4)
+            o << ", unsigned long long* psk_xslots, unsigned* psk_xstate, unsigned psk_teams, int psk_xmap, "
+                 "int psk_limit";
+        o << ")\n{\n";
         for (size_t k = 0; k < an.inputs.size(); ++k)
             o << "  const " << ptype(an.inputs[k].dtype) << "* in" << k << " = (const "
               << ptype(an.inputs[k].dtype) << "*)in" << k << "_;\n";
@@ -915,14 +948,22 @@ struct Emitter {
                 o << "    const float r" << i << " = " << rt((int)i, expr((int)i, 0)) << ";\n";
                 row_reciprocal((int)i);
             } else if (divr_node((int)i)) {
-                divr_open((int)i);
-                std::vector<int> es;
-                for (int e = 0; e < NE; ++e) {
-                    o << "    float v" << i << "_" << e << " = " << expr((int)i, e) << ";\n";
-                    es.push_back(e);
+                // one vector at a time, each with its own fallback: a vector's
+                // numerators are dead once its quotients are checked (all of a
+                // lane's numerators live at once would double the registers)
+                for (int e = 0; e < NE; ++e) o << "    float v" << i << "_" << e << ";\n";
+                for (int e0 = 0; e0 < NE; e0 += pl.vec) {
+                    o << "    {\n";
+                    divr_open((int)i);
+                    std::vector<int> es;
+                    for (int e = e0; e < std::min(NE, e0 + pl.vec); ++e) {
+                        o << "    v" << i << "_" << e << " = " << expr((int)i, e) << ";\n";
+                        es.push_back(e);
+                    }
+                    divr_close((int)i, es, "    ");
+                    round_elems((int)i, es, "    ");
+                    o << "    }\n";
                 }
-                divr_close((int)i, es, "    ");
-                round_elems((int)i, es, "    ");
             } else {
                 for (int e = 0; e < NE; ++e)
                     o << "    const float v" << i << "_" << e << " = " << rt((int)i, expr((int)i, e)) << ";\n";
@@ -1278,6 +1319,7 @@ struct Emitter {
                 }
             }
         }
+        if (pl.kind == 4) exchange(reds, p);
         for (int i : reds) {
             if (an.nodes[i].op == PSK_OP_ROW_MEAN)
                 o << "    const float r" << i << " = " << rt(i, "p" + std::to_string(i) + " / " + flit((float)an.cols))
@@ -1286,6 +1328,45 @@ struct Emitter {
                 o << "    const float r" << i << " = " << rt(i, "p" + std::to_string(i)) << ";\n";
             row_reciprocal(i);
         }
+    }
+
+    // Split rows: this workgroup's partials of phase p go to its member slot
+    // of the team's slot block, tagged; lanes r*K + m of the first wave take
+    // member m's partial of reduction r (waiting, bounded, for its tag) and
+    // every one of them combines the K partials of each reduction in member
+    // order, so every member of the team holds the same row values.
+    void exchange(const std::vector<int>& reds, int p)
+    {
+        const int K = pl.split, NR = (int)reds.size();
+        int off = 0;
+        for (int q = 0; q < p; ++q) off += (int)reductions_of(q).size();
+        const std::string arr = "psk_xv" + std::to_string(p);
+        o << "    {\n";
+        o << "      const unsigned psk_tag = psk_gen * psk_stride + psk_it * " << std::max(1, an.phases) << "u + "
+          << p + 1 << "u;\n";
+        o << "      unsigned long long* psk_s = psk_xslots + ((unsigned long long)psk_t * " << pl.exch << "u + " << off
+          << "u) * " << K << "u;\n";
+        o << "      if (lane == 0) {\n";
+        for (int r = 0; r < NR; ++r)
+            o << "        psk_put(psk_s + " << r * K << "u + psk_j, psk_tag, p" << reds[r] << ");\n";
+        o << "      }\n";
+        o << "      __shared__ float " << arr << "[" << NR << "];\n";
+        o << "      if (lane < " << NR * K << ") {\n";
+        o << "        const float v = psk_take(psk_s + lane, psk_tag, psk_limit, psk_xstate + 2);\n";
+        for (int r = 0; r < NR; ++r) {
+            const bool mx = an.nodes[reds[r]].op == PSK_OP_ROW_MAX;
+            o << "        float a" << r << " = PSK_RL(v, " << r * K << ");\n";
+            for (int m = 1; m < K; ++m) {
+                const std::string b = "PSK_RL(v, " + std::to_string(r * K + m) + ")";
+                if (mx) o << "        a" << r << " = psk_rmax(a" << r << ", " << b << ");\n";
+                else o << "        a" << r << " = a" << r << " + " << b << ";\n";
+            }
+            o << "        if (lane == 0) " << arr << "[" << r << "] = a" << r << ";\n";
+        }
+        o << "      }\n";
+        o << "      __syncthreads();\n";
+        for (int r = 0; r < NR; ++r) o << "      p" << reds[r] << " = " << arr << "[" << r << "];\n";
+        o << "    }\n";
     }
 
     void reductions_at(int p)
@@ -1586,6 +1667,86 @@ struct Emitter {
         return o.str();
     }
 
+    // Split rows: the grid is the device's resident capacity (every
+    // workgroup runs at once); K consecutive members form a team (on one
+    // XCD when the grid is a multiple of 8 K: workgroups reach the XCDs
+    // round robin), and team t takes rows t, t + teams, ...  Member j holds
+    // columns [j S, (j + 1) S) of the row in registers (S = lanes * nv *
+    // vec), reduces them as the register row kernel does, and exchanges
+    // each phase's partials with the other members (exchange above).  The
+    // tags of a launch come from a generation counter in device memory that
+    // the last workgroup to finish advances, so they never repeat from one
+    // launch (or graph replay) to the next.
+    std::string row_split(const std::string& name)
+    {
+        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n" << kPrelude << kSplitPrelude;
+        signature(name);
+        const int L = pl.lanes, V = pl.vec, K = pl.split;
+        const int64_t S = (int64_t)L * pl.nv * V;
+        o << "  {\n";
+        o << "    const int slot = 0;\n";
+        o << "    const int lane = (int)threadIdx.x;\n";
+        o << "    const unsigned psk_b = blockIdx.x;\n";
+        o << "    unsigned psk_t, psk_j;\n";
+        o << "    if (psk_xmap) { const unsigned idx = psk_b / 8u; psk_t = (idx / " << K << "u) * 8u + psk_b % 8u; psk_j = "
+             "idx % " << K << "u; }\n";
+        o << "    else { psk_t = psk_b / " << K << "u; psk_j = psk_b % " << K << "u; }\n";
+        o << "    const unsigned psk_gen = __hip_atomic_load(psk_xstate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n";
+        o << "    const unsigned psk_stride = (unsigned)(" << std::max(1, an.phases)
+          << "LL * ((n_total + psk_teams - 1) / psk_teams) + 1);\n";
+        o << "    unsigned psk_it = 0;\n";
+        o << "    for (" << I() << " row = (" << I() << ")psk_t; row < (" << I() << ")n_total; row += ("
+          << I() << ")psk_teams, ++psk_it) {\n";
+        o << "    const bool rok = true;\n";
+        if (period > 0) o << "    const int q = (int)(row % (" << I() << ")" << period << ");\n";
+        for (int k = 0; k < pl.nv; ++k)
+            o << "    const int c" << k << " = (int)psk_j * " << S << " + (" << k * L << " + lane) * " << V << ";\n";
+        row_inputs("row", "rok");
+        auto cond_of = [&](int v) {
+            std::string c = "c" + std::to_string(v);
+            return ragged ? "rok && " + c + " < " + std::to_string(an.cols) : std::string("rok");
+        };
+        for (int k : load_order()) {
+            const InputInfo& in = an.inputs[k];
+            if (!in.used || in.kind == InKind::Scalar || in.kind == InKind::RowConst) continue;
+            for (int v = 0; v < pl.nv; ++v)
+                load_vec(k, elem_offset(in, "row", "c" + std::to_string(v)), v * V,
+                         cond_of(v) + guard(in, v * V, "c" + std::to_string(v)));
+        }
+        leaves();
+        const std::string roff = "row * (" + std::string(I()) + ")" + std::to_string(an.cols) + " + ";
+        for (int p = 0; p <= an.phases; ++p) {
+            members_at(p);
+            for (size_t k = 0; k < an.extras.size(); ++k) {
+                const Analysis::Extra& x = an.extras[k];
+                if (an.depth[x.node] != p) continue;
+                std::string xo = "xo" + std::to_string(k);
+                if (x.per_row) {
+                    o << "    if (lane == 0 && psk_j == 0u) " << xo << "[row] = " << scalar_store(x.node, x.dtype)
+                      << ";\n";
+                    continue;
+                }
+                for (int v = 0; v < pl.nv; ++v)
+                    store_node(x.node, xo, x.dtype, roff + "c" + std::to_string(v), v * V, cond_of(v));
+            }
+            if (p < an.phases) reductions_at(p);
+        }
+        for (int v = 0; v < pl.nv; ++v) store_vec(roff + "c" + std::to_string(v), v * V, cond_of(v));
+        o << "    __syncthreads();\n";
+        o << "    }\n";
+        // the last workgroup to finish advances the generation
+        o << "    if (threadIdx.x == 0) {\n";
+        o << "      const unsigned d = __hip_atomic_fetch_add(psk_xstate + 1, 1u, __ATOMIC_RELAXED, "
+             "__HIP_MEMORY_SCOPE_AGENT);\n";
+        o << "      if (d == gridDim.x - 1u) {\n";
+        o << "        __hip_atomic_store(psk_xstate + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n";
+        o << "        __hip_atomic_fetch_add(psk_xstate, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n";
+        o << "      }\n";
+        o << "    }\n";
+        o << "  }\n}\n";
+        return o.str();
+    }
+
     std::string row(const std::string& name)
     {
         if (pl.persist) return row_persistent(name);
@@ -1658,6 +1819,7 @@ std::string emit_source(const Analysis& an, const KernelPlan& plan, const std::s
     hdr << "// plan: " << plan.key() << "\n";
     if (plan.kind == 2) return hdr.str() + em.tree(kernel_name);
     if (plan.kind == 3) return hdr.str() + em.row_tiled(kernel_name);
+    if (plan.kind == 4) return hdr.str() + em.row_split(kernel_name);
     return hdr.str() + (plan.kind == 1 ? em.row(kernel_name) : em.pointwise(kernel_name));
 }
 

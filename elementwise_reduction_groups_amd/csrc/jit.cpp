@@ -39,6 +39,27 @@ static std::string cache_path(const std::string& source)
     return std::string(dir) + name;
 }
 
+// The code object's metadata is a MessagePack map in an ELF note; the kernel
+// descriptor's ".private_segment_fixed_size" key is followed by an unsigned
+// integer (positive fixint, or uint8/16/32/64 with their markers).
+int64_t code_scratch_bytes(const std::vector<char>& code)
+{
+    static const char key[] = ".private_segment_fixed_size";
+    const size_t kl = sizeof key - 1;
+    for (size_t i = 0; i + kl + 9 < code.size(); ++i) {
+        if (std::memcmp(code.data() + i, key, kl) != 0) continue;
+        const unsigned char* p = reinterpret_cast<const unsigned char*>(code.data() + i + kl);
+        const unsigned m = p[0];
+        if (m <= 0x7f) return m;
+        int n = m == 0xcc ? 1 : m == 0xcd ? 2 : m == 0xce ? 4 : m == 0xcf ? 8 : 0;
+        if (!n) return -1;
+        int64_t v = 0;
+        for (int k = 1; k <= n; ++k) v = (v << 8) | p[k];   // MessagePack integers are big-endian
+        return v;
+    }
+    return -1;
+}
+
 psk_status jit_compile(const std::string& source, const std::string& name, std::vector<char>& code)
 {
     std::string cpath = cache_path(source);

@@ -55,12 +55,13 @@ std::string KernelPlan::key() const
     char b[160];
     std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d c%d w%d m%d p%d r%d s%d", kind, vec, block,
                   lanes, nv, (int)nt, (int)xcd, (long long)blocks, tiles, (int)tcache, wpe, wmin, persist, rcache, lcache);
+    if (kind == 4) return std::string(b) + " K" + std::to_string(split);
     return kind == 3 ? std::string(b) + (alt ? " a1" : " a0") + " u" + std::to_string(munroll) + " y" +
                            std::to_string(lunroll)
                      : std::string(b);
 }
 
-KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
+KernelPlan plan_kernel(const Analysis& an, bool allow_vector, int split_ept)
 {
     KernelPlan p;
     const int V = an.out_dtype == PSK_BF16 ? 8 : 4;
@@ -151,7 +152,53 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector)
             p.blocks = std::min<int64_t>(an.rows, (int64_t)256 * persist);
             p.xcd = false;
         }
-        if ((int64_t)p.nv * p.vec > layout_value("epmax", 32) || layout_value("tiled", 0)) {
+        // Split rows: a row too wide for one workgroup's registers is shared
+        // by K workgroups of 512 lanes (two a CU), each holding a segment in
+        // registers: 64 elements a lane where the group streams one input of
+        // at most 4 bytes an element and has no mask (the softmax: 128 KiB a
+        // workgroup, 110 registers a lane), else 32 (a causal mask's selects
+        // and guarded loads spill at 64).  The row is read once; the workgroups exchange their
+        // partial row values.  Measured on a [8192, 131072] f32 softmax:
+        // K = 4 at 64 elements a lane 1.51 ms, K = 8 at 32 elements 1.57 ms,
+        // against 1.95 ms for one workgroup a row (the tiled kernel, which
+        // re-reads what its registers and LDS cannot hold).  Not for the
+        // online normalizer (its partials are pairs rescaled on combining);
+        // at most 32 workgroups a row (the first wave takes every member's
+        // partial of every reduction of a phase: at most 64).
+        int streamed_inputs = 0, streamed_bytes = 0;
+        for (const InputInfo& in : an.inputs)
+            if (in.used && (in.kind == InKind::General || in.kind == InKind::Full)) {
+                ++streamed_inputs;
+                streamed_bytes = std::max(streamed_bytes, (int)esz(in.dtype));
+            }
+        const bool wide = (int64_t)p.nv * p.vec > layout_value("epmax", 32);
+        if (wide && !online && split_ept != 0 && !layout_value("tiled", 0) && layout_value("split", 1)) {
+            const int Ls = 512;
+            const bool lean = streamed_inputs <= 1 && streamed_bytes <= 4 && an.mask_period == 0 && an.where_mask < 0;
+            const int ept = split_ept > 0 ? split_ept : layout_value("sept", lean ? 64 : 32);
+            const int nvs = std::max(1, ept / p.vec);
+            const int64_t seg = (int64_t)Ls * nvs * p.vec;
+            const int64_t K = ceil_div(an.cols, seg);
+            int exch = 0;
+            for (size_t i = 0; i < an.nodes.size(); ++i)
+                if (op_is_row(an.nodes[i].op)) ++exch;
+            if (K >= 2 && K <= 32 && exch * K <= 64) {
+                p.kind = 4;
+                p.persist = 0;
+                p.lanes = Ls;
+                p.block = Ls;
+                p.nv = nvs;
+                p.rows_per_block = 1;
+                p.split = (int)K;
+                p.exch = exch;
+                p.blocks = 0;        // persistent: the grid is the device's resident capacity, set at launch
+                p.xcd = false;
+                p.wmin = std::min(8, 2 * Ls / 256);
+                p.per_xcd = p.grid = 0;
+                return p;
+            }
+        }
+        if (wide || layout_value("tiled", 0)) {
             p.persist = 0;
             p.kind = 3;
             // 512 lanes: two workgroups share a CU, so one loads while the

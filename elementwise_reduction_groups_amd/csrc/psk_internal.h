@@ -96,7 +96,7 @@ const char* op_name(int op);
 
 // ------------------------------------------------------------------- emit
 struct KernelPlan {
-    int kind = 0;            // 0 pointwise, 1 row, 2 tree-mapped, 3 row tiled (wide rows)
+    int kind = 0;            // 0 pointwise, 1 row, 2 tree-mapped, 3 row tiled (wide rows), 4 split rows
     int vec = 1;             // elements per vector access
     int block = 256;         // threads per workgroup
     int lanes = 64;          // row kernel: lanes per row
@@ -112,6 +112,9 @@ struct KernelPlan {
     int wpe = 0;             // tiled row kernel: at most this many waves per SIMD (0: no limit)
     int wmin = 0;            // tiled row kernel: registers for at least this many waves per SIMD (0: any)
     int persist = 0;         // row kernel: persistent workgroups per CU (0: one workgroup per row)
+    int split = 0;           // split rows (kind 4): workgroups that share one row, each a segment of
+                             // lanes * nv * vec columns kept in registers
+    int exch = 0;            // split rows: row values exchanged per row (one per reduction)
     bool nt = true;          // nontemporal loads and stores
     bool xcd = true;         // each XCD takes a contiguous eighth of the blocks
     int64_t blocks = 0;      // workgroups that carry work
@@ -120,7 +123,12 @@ struct KernelPlan {
     std::string key() const;
 };
 
-KernelPlan plan_kernel(const Analysis& an, bool allow_vector);
+// split_ept: elements a lane holds in a split-rows kernel (-1: the default
+// rule, 0: no split rows, > 0: that many)
+KernelPlan plan_kernel(const Analysis& an, bool allow_vector, int split_ept = -1);
+// Bytes of scratch (register spills) a compiled code object's kernel uses,
+// from its metadata; -1 when the metadata does not say.
+int64_t code_scratch_bytes(const std::vector<char>& code);
 // HIP source for the group under `plan`, entry point named `kernel_name`.
 std::string emit_source(const Analysis& an, const KernelPlan& plan, const std::string& kernel_name);
 // Canonical text of the group (what the kernel cache is keyed by).

@@ -263,9 +263,23 @@ psk_status psk_group_run_multi(const psk_group* group, const void* const* inputs
 
 void psk_group_destroy(psk_group* group);
 
+/* Rows too wide for one workgroup's registers are shared by several
+ * workgroups (kind 4), which exchange partial row values (a maximum, a sum)
+ * through the group's device memory: launches of the group are persistent,
+ * with no more workgroups than the device holds at once, so all of them run
+ * together, and every wait is bounded.  The group's first run on a device
+ * allocates that memory (like loading the code object); runs of one group
+ * on one device must follow one another (one stream, or ordered streams):
+ * two at once would share it.  A wait that ran out (the device was shared
+ * with other work long enough, for instance) leaves that run's results
+ * invalid; psk_group_check waits for the device and returns PSK_E_HIP if any
+ * wait of the group on the current device ran out since the last check
+ * (PSK_OK at once for groups without split rows). */
+psk_status psk_group_check(const psk_group* group);
+
 /* Kernel shape chosen for a group (for tests and measurement). */
 typedef struct psk_group_info {
-    int32_t kind;            /* 0 pointwise, 1 row, 2 tree-mapped, 3 row tiled */
+    int32_t kind;            /* 0 pointwise, 1 row, 2 tree-mapped, 3 row tiled, 4 split rows */
     int32_t members;         /* member count */
     int32_t n_reductions;    /* row reductions */
     int32_t phases;          /* reduction phases (longest chain of dependent reductions) */
@@ -278,6 +292,9 @@ typedef struct psk_group_info {
     char kernel[48];         /* the emitted kernel's name (as profilers show it), NUL-terminated */
     int32_t tiles;           /* tiled row kernel (kind 3, rows too wide for registers): tiles per
                                 row; each reduction phase re-reads the row.  0 otherwise */
+    int32_t split;           /* split rows (kind 4): workgroups that share one row, each holding
+                                a segment in registers and exchanging partial row values with
+                                the others.  0 otherwise */
 } psk_group_info;
 psk_status psk_group_get_info(const psk_group* group, psk_group_info* info);
 

@@ -5,13 +5,15 @@
  *
  *   - softmax (scale, row max, subtract, exp, row sum, divide) on a
  *     stream: causal over [300, 1000] f32 (register row kernel) and plain
- *     over [3, 40000] f32 (tiled wide-row kernel), within 1e-7 + 2e-6 |ref|
- *     of the oracle;
+ *     over [6, 40000] f32 (rows split over workgroups, then the bounded
+ *     waits checked) and [3, 40000] (the tiled kernel, forced through the
+ *     PSK_LAYOUT variable), within 1e-7 + 2e-6 |ref| of the oracle;
  *   - one AdamW step over a 3-leaf f32 tree (1, 1000 and 4097 elements, in
  *     place): bit for bit against the oracle.
  *
  * Inputs come from a xorshift generator of this file.  Prints "ok" and
  * exits 0 on success; prints the failing check and exits 1 otherwise. */
+#define _POSIX_C_SOURCE 200112L   /* setenv */
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -111,6 +113,7 @@ static int softmax_case(int64_t R, int64_t C, int64_t T, int want_kind, hipStrea
     const void *ins[1] = {dx};
     CHECK(psk_group_run(g, ins, dy, (void *)stream) == PSK_OK);
     HIP(hipStreamSynchronize(stream));
+    CHECK(psk_group_check(g) == PSK_OK);
     HIP(hipMemcpy(y, dy, bytes, hipMemcpyDeviceToHost));
     if (T > 0) {
         orc_softmax_causal(R, C, T, scale, x, ref, 0, R);
@@ -210,7 +213,10 @@ int main(void)
     hipStream_t stream;
     HIP(hipStreamCreate(&stream));
     if (softmax_case(300, 1000, 1000, 1, stream)) return 1;    /* register row kernel */
-    if (softmax_case(3, 40000, 0, 3, stream)) return 1;        /* tiled wide-row kernel */
+    if (softmax_case(6, 40000, 0, 4, stream)) return 1;        /* rows split over workgroups */
+    setenv("PSK_LAYOUT", "tiled=1", 1);                          /* the tiled wide-row kernel */
+    if (softmax_case(3, 40000, 0, 3, stream)) return 1;
+    unsetenv("PSK_LAYOUT");
     if (adamw_case(stream)) return 1;
     HIP(hipStreamDestroy(stream));
     printf("ok\n");

@@ -395,22 +395,40 @@ def test_mask_refusals(lib):
             [((4, 8), "f32"), ((2, 4, 8), "u8")], (4, 8))
 
 
-def test_wide_rows_take_the_tiled_kernel(lib, tmp_path):
+def test_wide_rows_take_split_or_tiled_kernels(lib, tmp_path, monkeypatch):
+    """Rows too wide for one workgroup's registers: split over workgroups
+    (kind 4) by default, at the widest segment that compiles without
+    spilling registers; the tiled kernel (kind 3) when forced, for the online
+    normalizer, and for rows a split would need more than 32 workgroups for."""
     from synth import configs as C
     # up to 32 elements per lane at 1024 lanes the row stays in registers
     g = P.psk_group_create(P.GroupDesc(C.softmax_causal_dag(0.125, 32768), [((4, 32768), "f32")], (4, 32768), "f32"))
     assert P.psk_group_get_info(g).kind == 1
     P.psk_group_destroy(g)
-    for cols, dt in [(32772, "f32"), (65536, "f32"), (131072, "bf16"), (1 << 20, "f32")]:
+    plain = P.GroupDesc(C.softmax_dag(0.125), [((4, 131072), "f32")], (4, 131072), "f32")
+    g = P.psk_group_create(plain)
+    info = P.psk_group_get_info(g)
+    P.psk_group_destroy(g)
+    assert info.kind == 4 and info.split == 4 and info.block == 512 and info.lanes_per_row == 2048
+    for cols, dt, kind in [(32772, "f32", 4), (65536, "f32", 4), (131072, "bf16", 4), (1 << 20, "f32", 3)]:
         d = P.GroupDesc(C.softmax_causal_dag(0.125, cols), [((4, cols), dt)], (4, cols), dt)
-        g = P.psk_group_create(d)
-        info = P.psk_group_get_info(g)
-        P.psk_group_destroy(g)
-        assert info.kind == 3 and info.lanes_per_row == 512 and info.rows_per_block == 1
-        assert info.tiles == -(-cols // (512 * 2 * info.vec))
-        asm, notes = _isa(P.psk_group_code_object(d), tmp_path, f"wide{cols}")
-        assert re.search(r"\.private_segment_fixed_size:\s+0\b", notes)    # no spills
-        assert not re.search(r"v_pk_(fma|mul|add)_f32", asm)
+        for forced in (False, True):
+            if forced:
+                monkeypatch.setenv("PSK_LAYOUT", "tiled=1")
+            g = P.psk_group_create(d)
+            info = P.psk_group_get_info(g)
+            P.psk_group_destroy(g)
+            k = 3 if forced else kind
+            assert info.kind == k, (cols, dt, forced)
+            if k == 3:
+                assert info.lanes_per_row == 512 and info.rows_per_block == 1
+                assert info.tiles == -(-cols // (512 * 2 * info.vec))
+            else:
+                assert 2 <= info.split <= 32 and info.split * 512 * info.vec * 16 >= cols
+            asm, notes = _isa(P.psk_group_code_object(d), tmp_path, f"wide{cols}{forced}")
+            assert re.search(r"\.private_segment_fixed_size:\s+0\b", notes)    # no spills
+            assert not re.search(r"v_pk_(fma|mul|add)_f32", asm)
+            monkeypatch.delenv("PSK_LAYOUT", raising=False)
     # the other wide row groups (several inputs, byte masks, extra outputs,
     # the online normalizer) keep their register caches without spilling
     eps, W = C.f32(1e-5), 70000
@@ -427,11 +445,15 @@ def test_wide_rows_take_the_tiled_kernel(lib, tmp_path):
                                    flags=P.PSK_GROUP_ONLINE),
     }
     for name, d in others.items():
-        g = P.psk_group_create(d)
-        assert P.psk_group_get_info(g).kind == 3, name
-        P.psk_group_destroy(g)
-        _, notes = _isa(P.psk_group_code_object(d), tmp_path, f"wide_{name}")
-        assert re.search(r"\.private_segment_fixed_size:\s+0\b", notes), name
+        for forced in (False, True):
+            if forced:
+                monkeypatch.setenv("PSK_LAYOUT", "tiled=1")
+            g = P.psk_group_create(d)
+            assert P.psk_group_get_info(g).kind == (3 if forced or name.startswith("online") else 4), name
+            P.psk_group_destroy(g)
+            _, notes = _isa(P.psk_group_code_object(d), tmp_path, f"wide_{name}{forced}")
+            assert re.search(r"\.private_segment_fixed_size:\s+0\b", notes), name
+            monkeypatch.delenv("PSK_LAYOUT", raising=False)
     # rows past 2^30 columns are refused
     _refused(_desc("%0 = input 0\n%1 = row_max %0\n%2 = sub %0 %1\n", [((1, (1 << 30) + 8), "f32")],
                    (1, (1 << 30) + 8)), P.PSK_E_UNSUPPORTED)
@@ -500,7 +522,7 @@ def test_precision_follows_what_is_stored(lib):
     assert "psk_gelu(" in tree[tree.index('extern "C"'):] and "psk_gelu_b(" not in tree[tree.index('extern "C"'):]
 
 
-def test_online_normalizer_flag(lib):
+def test_online_normalizer_flag(lib, monkeypatch):
     from synth import configs as C
     O = P.PSK_GROUP_ONLINE
     # a softmax: its sum moves into the maximum's pass (one reduction phase)
@@ -509,7 +531,9 @@ def test_online_normalizer_flag(lib):
     assert "float tm = " in body and "expf(q" in body
     wide = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((4, 70000), "f32")], (4, 70000), "f32",
                                           flags=O))
+    monkeypatch.setenv("PSK_LAYOUT", "tiled=1")      # the exact sum through the tiled kernel, for comparison
     plain = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((4, 70000), "f32")], (4, 70000), "f32"))
+    monkeypatch.delenv("PSK_LAYOUT")
     # tiled: two walks of the row (register, LDS and memory tile loops each) instead of three
     assert wide.count("for (int t = ") * 3 == plain.count("for (int t = ") * 2
     # masked and causal softmax take it too

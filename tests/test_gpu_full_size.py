@@ -99,3 +99,19 @@ def test_chain64_every_element():
     say(f"64-node chain: oracle on {THREADS} host threads")
     ref = OP.eval_group(nodes, [to_np(A), to_np(B), to_np(C)], (N, N), 0, THREADS)
     assert compare_all(to_np(out), ref, "f32", "chain64") == N * N
+
+
+def test_wide_softmax_every_element():
+    """The [8192, 131072] f32 softmax (rows split over workgroups): all 1.07e9
+    outputs within 1e-7 + 2e-6 |ref|."""
+    R, C = 8192, 131072
+    x = configs.softmax_scores(R, C, device=DEV)
+    g = P.Group(configs.softmax_dag(0.125), [((R, C), "f32")], (R, C), "f32")
+    out = torch.full_like(x, float("nan"))
+    say("wide softmax [8192, 131072] f32 on the GPU")
+    g.run([x], out)
+    torch.cuda.synchronize()
+    g.check()
+    say(f"wide softmax: oracle on {THREADS} host threads")
+    ref = OP.eval_group(configs.softmax_dag(0.125), [to_np(x)], (R, C), 0, THREADS)
+    assert compare_all(to_np(out), ref, "f32", "wide softmax") == R * C

@@ -69,14 +69,20 @@ def test_softmax_rows_past_2_31():
     free()
 
 
-def test_tiled_rows_past_2_31():
+@pytest.mark.parametrize("layout,kind", [("", 4), ("tiled=1", 3)])
+def test_wide_rows_past_2_31(layout, kind, monkeypatch):
+    """Rows split over workgroups (the default) and the tiled kernel (forced)
+    over 2^31 + elements: 64-bit offsets."""
+    if layout:
+        monkeypatch.setenv("PSK_LAYOUT", layout)
     R, C = 16385, 131072                     # 2 147 614 720 elements, bf16
     x = configs.softmax_scores(R, C, device=DEV, seed=7).to(torch.bfloat16)
     out = torch.empty_like(x)
     g = P.Group(configs.softmax_dag(0.125), [((R, C), "bf16")], (R, C), "bf16")
-    assert g.info.kind == 3
+    assert g.info.kind == kind
     g.run([x], out)
     torch.cuda.synchronize()
+    g.check()
     rows = np.array([0, 1, 16382, 16383, 16384])
     ri = torch.from_numpy(rows).to(DEV)
     ref = oracle.eval_group(configs.softmax_dag(0.125), [to_np(x[ri])], (len(rows), C), BF16)

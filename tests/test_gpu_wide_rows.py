@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from synth import configs
-from tests.gpu_util import assert_bf16_close, assert_f32_close, to_np
+from tests.gpu_util import assert_bf16_close, assert_bits, assert_f32_close, to_np
 
 P = pytest.importorskip("elementwise_reduction_groups_amd")
 
@@ -17,9 +17,24 @@ F32, BF16 = P.PSK_F32, P.PSK_BF16
 EPS = configs.f32(1e-5)
 
 
+# every wide-row test runs through both kernels for rows too wide for one
+# workgroup's registers: rows split over workgroups (the default, kind 4)
+# and the tiled kernel (kind 3, forced)
+WIDE = pytest.mark.parametrize("layout,kind", [("", 4), ("tiled=1", 3)])
+
+
+def _layout(monkeypatch, layout):
+    if layout:
+        monkeypatch.setenv("PSK_LAYOUT", layout)
+    else:
+        monkeypatch.delenv("PSK_LAYOUT", raising=False)
+
+
+@WIDE
 @pytest.mark.parametrize("R,C,dt", [(8, 40000, "f32"), (4, 65536, "f32"), (3, 131072, "bf16"), (5, 33333, "f32"),
                                     (2, 300000, "f32")])
-def test_wide_softmax(R, C, dt):
+def test_wide_softmax(R, C, dt, layout, kind, monkeypatch):
+    _layout(monkeypatch, layout)
     x = configs.softmax_scores(R, C, device=DEV, seed=C)
     if dt == "bf16":
         x = x.to(torch.bfloat16)
@@ -28,10 +43,11 @@ def test_wide_softmax(R, C, dt):
     for period in (3, C):
         g = P.Group(configs.softmax_causal_dag(0.125, period), [((R, C), dt)], (R, C), dt)
         info = g.info
-        assert info.kind == 3 and info.tiles >= 2
+        assert info.kind == kind and (info.tiles >= 2 or info.split >= 2)
         out = torch.full_like(x, float("nan"))
         g.run([x], out)
         torch.cuda.synchronize()
+        g.check()
         ref = oracle.eval_group(configs.softmax_causal_dag(0.125, period), [to_np(x)], (R, C), F32 if dt == "f32"
                                 else BF16)
         if dt == "f32":
@@ -40,12 +56,14 @@ def test_wide_softmax(R, C, dt):
             assert_bf16_close(to_np(out), ref, f"wide softmax {R}x{C} period {period}")
 
 
-def test_wide_masked_softmax_with_emptied_rows():
+@WIDE
+def test_wide_masked_softmax_with_emptied_rows(layout, kind, monkeypatch):
+    _layout(monkeypatch, layout)
     R, C = 6, 70000
     x = configs.softmax_scores(R, C, device=DEV, seed=5)
     m = configs.random_mask(R, C, 0.2, empty_rows=[2], device=DEV, seed=6)
     g = P.Group(configs.softmax_masked_dag(0.125), [((R, C), "f32"), ((R, C), "u8")], (R, C), "f32")
-    assert g.info.kind == 3
+    assert g.info.kind == kind
     out = torch.full_like(x, float("nan"))
     g.run([x, m], out)
     torch.cuda.synchronize()
@@ -56,13 +74,15 @@ def test_wide_masked_softmax_with_emptied_rows():
     assert np.all(got[2].view(np.uint32) == 0)
 
 
-def test_wide_layernorm_with_statistics():
+@WIDE
+def test_wide_layernorm_with_statistics(layout, kind, monkeypatch):
+    _layout(monkeypatch, layout)
     R, C = 8, 50000
     x, gm, bt = configs.layernorm_inputs(R, C, device=DEV, seed=9)
     g = P.Group(configs.layernorm_dag(EPS), [((R, C), "bf16"), ((C,), "bf16"), ((C,), "bf16")], (R, C), "bf16",
                 root=configs.LAYERNORM_ROOT,
                 extras=[(configs.LAYERNORM_MEAN, (R, 1), "f32"), (configs.LAYERNORM_RSTD, (R, 1), "f32")])
-    assert g.info.kind == 3
+    assert g.info.kind == kind
     out = torch.full((R, C), float("nan"), dtype=torch.bfloat16, device=DEV)
     mean = torch.full((R, 1), float("nan"), device=DEV)
     rstd = torch.full((R, 1), float("nan"), device=DEV)
@@ -72,10 +92,14 @@ def test_wide_layernorm_with_statistics():
     ref = oracle.eval_group(configs.layernorm_dag(EPS), [to_np(x), to_np(gm), to_np(bt)], (R, C), BF16,
                             root=configs.LAYERNORM_ROOT,
                             extras=[(configs.LAYERNORM_MEAN, rm), (configs.LAYERNORM_RSTD, rr)])
-    # statistics: a lane sums its elements over the tiles in order (tiles x vectors x vec per lane),
-    # then the wave butterfly and the 16 waves; against float64 within that path's bound
+    # statistics: a lane sums its elements in order (tiled: tiles x vectors x vec per lane; split: its
+    # segment's elements), then the wave butterfly, the waves, and (split) the workgroups of the row;
+    # against float64 within that path's bound
     U = 2.0 ** -24
-    k = g.info.tiles * 2 * g.info.vec + 6 + 15
+    if kind == 3:
+        k = g.info.tiles * 2 * g.info.vec + 6 + 15
+    else:
+        k = -(-C // (g.info.split * g.info.block)) + g.info.vec + 6 + 7 + g.info.split
     x64 = x.double().cpu()
     m64 = x64.mean(dim=1)
     assert torch.all((mean.double().cpu()[:, 0] - m64).abs() <= k * U * x64.abs().mean(dim=1) + U * m64.abs())
@@ -87,13 +111,15 @@ def test_wide_layernorm_with_statistics():
     assert d[big].max() <= 1
 
 
-def test_wide_rms_norm_storing_h_in_place():
+@WIDE
+def test_wide_rms_norm_storing_h_in_place(layout, kind, monkeypatch):
+    _layout(monkeypatch, layout)
     R, C = 4, 45000
     x, res, gm = configs.rmsnorm_inputs(R, C, device=DEV, seed=10)
     xn, rn, gn = to_np(x), to_np(res), to_np(gm)
     g = P.Group(configs.rmsnorm_gelu_dag(EPS), [((R, C), "bf16"), ((R, C), "bf16"), ((C,), "bf16")], (R, C), "bf16",
                 extras=[(configs.RMSNORM_H, (R, C), "bf16")])
-    assert g.info.kind == 3
+    assert g.info.kind == kind
     out = torch.full((R, C), float("nan"), dtype=torch.bfloat16, device=DEV)
     g.run([x, res, gm], out, extra_outs=[res])
     torch.cuda.synchronize()
@@ -140,7 +166,7 @@ def test_register_cache_changes_no_bit(case, monkeypatch):
         xs = [((R, C), torch.bfloat16)]
     runs = []
     for layout in ("rc=0,lc=0", "rc=1,lc=0", "rc=0,lc=2", "rc=3,lc=1", "rc=1,lc=64", ""):
-        monkeypatch.setenv("PSK_LAYOUT", layout)
+        monkeypatch.setenv("PSK_LAYOUT", "tiled=1" + ("," + layout if layout else ""))
         g = P.Group(*args, **kw)
         assert g.info.kind == 3
         out = torch.full((R, C), float("nan"), dtype=ins[0].dtype, device=DEV)
@@ -154,12 +180,12 @@ def test_register_cache_changes_no_bit(case, monkeypatch):
 
 
 def test_wide_softmax_full_size_sampled_rows():
-    """[8192, 131072] f32 in the layout that is timed (512 lanes, registers
-    and LDS caches)."""
+    """[8192, 131072] f32 in the layout that is timed (each row split over 4
+    workgroups of 512 lanes)."""
     R, C = 8192, 131072
     x = configs.softmax_scores(R, C, device=DEV)
     g = P.Group(configs.softmax_dag(0.125), [((R, C), "f32")], (R, C), "f32")
-    assert g.info.kind == 3 and g.info.lanes_per_row == 512
+    assert g.info.kind == 4 and g.info.split == 4 and g.info.block == 512
     out = torch.empty_like(x)
     g.run([x], out)
     torch.cuda.synchronize()
@@ -167,3 +193,88 @@ def test_wide_softmax_full_size_sampled_rows():
     ri = torch.from_numpy(rows).to(DEV)
     ref = oracle.eval_group(configs.softmax_dag(0.125), [to_np(x[ri])], (len(rows), C), F32)
     assert_f32_close(to_np(out[ri]), ref, "wide softmax full size")
+    g.check()
+
+
+# ------------------------------------------------------------- split rows
+def _split_softmax(R, C, **kw):
+    return P.Group(configs.softmax_dag(0.125), [((R, C), "f32")], (R, C), "f32", **kw)
+
+
+def test_split_rows_same_bits_across_runs_and_graph_replays():
+    """A split-rows group gives the same bits on every run: eager runs, and
+    replays of a captured HIP graph with eager work in between (the tags of
+    the exchange come from a device-side generation counter, not from the
+    launch arguments a graph freezes)."""
+    R, C = 300, 131072
+    x = configs.softmax_scores(R, C, device=DEV, seed=41)
+    g = _split_softmax(R, C)
+    assert g.info.kind == 4
+    ref = torch.full_like(x, float("nan"))
+    g.run([x], ref)                                   # first run: loads the kernel, allocates the state
+    torch.cuda.synchronize()
+    want = to_np(ref)
+    oref = oracle.eval_group(configs.softmax_dag(0.125), [to_np(x[:7])], (7, C), F32)
+    assert_f32_close(want[:7], oref, "split softmax")
+    for k in range(3):
+        out = torch.full_like(x, float("nan"))
+        g.run([x], out)
+        torch.cuda.synchronize()
+        assert_bits(to_np(out), want, f"eager run {k}")
+    out = torch.full_like(x, float("nan"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        g.run([x], out)
+    torch.cuda.synchronize()
+    for k in range(4):
+        out.fill_(float("nan"))
+        other = torch.full_like(x, 0.0)
+        g.run([x], other)                             # eager work between the replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_bits(to_np(out), want, f"graph replay {k}")
+        assert_bits(to_np(other), want, f"eager run between replays {k}")
+    g.check()
+
+
+def test_split_rows_fewer_rows_than_teams():
+    for R in (1, 3, 9):
+        C = 70000
+        x = configs.softmax_scores(R, C, device=DEV, seed=R)
+        g = _split_softmax(R, C)
+        assert g.info.kind == 4
+        out = torch.full_like(x, float("nan"))
+        g.run([x], out)
+        torch.cuda.synchronize()
+        ref = oracle.eval_group(configs.softmax_dag(0.125), [to_np(x)], (R, C), F32)
+        assert_f32_close(to_np(out), ref, f"split softmax, {R} rows")
+        g.check()
+
+
+def test_split_rows_bounded_wait_is_reported(monkeypatch):
+    """A wait that runs out is reported, not hung on: with the bound set to
+    no tries at all (from the host, at the group's creation), a wait that
+    does not find its partial at once gives up, the launch still finishes,
+    and psk_group_check reports PSK_E_HIP once; the same group shape with
+    the default bound then gives the oracle's result."""
+    R, C = 2048, 131072
+    x = configs.softmax_scores(R, C, device=DEV, seed=43)
+    monkeypatch.setenv("PSK_SPLIT_WAIT", "0")
+    g = _split_softmax(R, C)
+    monkeypatch.delenv("PSK_SPLIT_WAIT")
+    out = torch.full_like(x, float("nan"))
+    g.run([x], out)
+    with pytest.raises(P.PskError) as ei:
+        g.check()
+    assert ei.value.status == P.PSK_E_HIP
+    g.check()                                          # reported once
+    ok = _split_softmax(R, C)
+    out.fill_(float("nan"))
+    ok.run([x], out)
+    torch.cuda.synchronize()
+    ok.check()
+    rows = torch.tensor([0, 1, R // 2, R - 1], device=DEV)
+    ref = oracle.eval_group(configs.softmax_dag(0.125), [to_np(x[rows])], (4, C), F32)
+    assert_f32_close(to_np(out[rows]), ref, "after a reported timeout")
