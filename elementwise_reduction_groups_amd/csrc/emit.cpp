@@ -213,6 +213,20 @@ __device__ __forceinline__ float psk_gelu_b(float x) {
 __device__ __forceinline__ float psk_exp_np_b(float x) {
   return __builtin_amdgcn_exp2f(fmaf(x, 1.44269504088896341f, 64.0f)) * 0x1p-64f;
 }
+// exp(x) for an argument known to be <= 0 whose results reach f32 values
+// through well-conditioned operations: x log2 e split into t = fl(x L) and
+// its remainder r = x L - t, formed with two fmas (L + L_lo is log2 e to
+// about 2^-48), then exp(x) = 2^t (1 + r ln 2): the hardware 2^t (within an
+// ulp), one multiply-add, r^2 terms below 2^-34.  Within about two f32 ulps,
+// in eight instructions (the library's expf takes fourteen).  Results below
+// 2^-126 may be flushed to 0 (far below the f32 tolerance's absolute
+// part); -inf gives 0 and NaN stays NaN.
+__device__ __forceinline__ float psk_exp_np(float x) {
+  const float t = x * 1.44269504088896341f;
+  const float r = fmaf(x, 1.925963033500e-8f, fmaf(x, 1.44269504088896341f, -t));
+  const float p = __builtin_amdgcn_exp2f(t);
+  return (t > -128.0f) ? fmaf(p, r * 0.693147180559945309f, p) : p;
+}
 // a / b for a value b shared by the whole row, given y = 1/b correctly
 // rounded: q = a*y is within an ulp of a/b; the fma gives the exact
 // remainder a - b*q, and one more fma rounds q + remainder*y to the
@@ -493,6 +507,10 @@ struct Emitter {
     // operations: the short exponential
     bool cheap_exp(int i) const { return exp_nonpos(i) && !f32_reach[i] && conditioned[i]; }
 
+    // ... whose value f32 results depend on, through well-conditioned
+    // operations: the split-product exponential (about two ulps)
+    bool split_exp(int i) const { return pl.fexp && exp_nonpos(i) && f32_reach[i] && conditioned[i]; }
+
     // element / row statistic (a value computed from a reduction) that only
     // bf16 results depend on, through well-conditioned operations and at
     // most one gelu: the row's reciprocal (correctly rounded) times the
@@ -539,7 +557,8 @@ struct Emitter {
         case PSK_OP_MIN: return "psk_min(" + A() + ", " + B() + ")";
         case PSK_OP_NEG: return "(-" + A() + ")";
         case PSK_OP_ABS: return "fabsf(" + A() + ")";
-        case PSK_OP_EXP: return (cheap_exp(i) ? "psk_exp_np_b(" : "expf(") + A() + ")";
+        case PSK_OP_EXP: return std::string(cheap_exp(i) ? "psk_exp_np_b(" : split_exp(i) ? "psk_exp_np(" : "expf(") +
+                                A() + ")";
         case PSK_OP_LOG: return "logf(" + A() + ")";
         case PSK_OP_SQRT: return "sqrtf(" + A() + ")";
         case PSK_OP_TANH: return "tanhf(" + A() + ")";
@@ -650,8 +669,11 @@ struct Emitter {
             }
             o << "    " << r.type << " " << r.name << " = " << r.zero << ";\n";
             std::string ld;
-            if (V == 1) ld = widen(in.dtype, ld_fn() + "(" + p + ")");
-            else ld = ld_fn() + "((const " + r.type + "*)(" + p + (r.eoff ? " + " + std::to_string(r.eoff) : "") + "))";
+            // an input other rows read again (it broadcasts over some axis of
+            // the output) is loaded through the caches
+            const std::string fn = (in.numel < an.numel && !pl.bnt) ? "psk_ldc" : ld_fn();
+            if (V == 1) ld = widen(in.dtype, fn + "(" + p + ")");
+            else ld = fn + "((const " + r.type + "*)(" + p + (r.eoff ? " + " + std::to_string(r.eoff) : "") + "))";
             o << "    if (" << cond << ") " << r.name << " = " << ld << ";\n";
             if (cache_mode == 1) o << "    k" << r.name << "[" << cache_slot << "] = " << r.name << ";\n";
             if (cache_mode == 3) o << "    " << lds << " = " << r.name << ";\n";
@@ -747,13 +769,14 @@ struct Emitter {
     {
         const InputInfo& in = an.inputs[k];
         const std::string p = "(in" + std::to_string(k) + " + " + off + ")";
+        const std::string fn = (in.numel < an.numel && !pl.bnt) ? "psk_ldc" : ld_fn();   // read again by other rows
         for (const Piece& pc : pieces(k, e0)) {
             o << "    " << pc.type << " " << pfx << pc.name << " = {};\n";
             if (pc.type == "float")
-                o << "    if (" << cond << ") " << pfx << pc.name << " = " << widen(in.dtype, ld_fn() + "(" + p + ")")
+                o << "    if (" << cond << ") " << pfx << pc.name << " = " << widen(in.dtype, fn + "(" + p + ")")
                   << ";\n";
             else
-                o << "    if (" << cond << ") " << pfx << pc.name << " = " << ld_fn() << "((const " << pc.type << "*)("
+                o << "    if (" << cond << ") " << pfx << pc.name << " = " << fn << "((const " << pc.type << "*)("
                   << p << " + " << pc.eoff << "));\n";
         }
     }
@@ -1217,7 +1240,11 @@ struct Emitter {
 
     // the exponential an online sum uses: its exp node's form (every
     // argument here is <= 0 as well)
-    std::string online_exp(int sm) const { return cheap_exp(an.nodes[sm].a) ? "psk_exp_np_b" : "expf"; }
+    std::string online_exp(int sm) const
+    {
+        const int e = an.nodes[sm].a;
+        return cheap_exp(e) ? "psk_exp_np_b" : split_exp(e) ? "psk_exp_np" : "expf";
+    }
 
     // Online normalizer: this lane's elements of y (the maximum's operand)
     // update the running maximum p<mx> once for the group of elements and

@@ -19,8 +19,11 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Layout overrides for measurement, "key=value" pairs separated by commas in
 // PSK_LAYOUT (an unknown or out-of-range value falls back to the default):
-//   every kernel: nt=0|1 (nontemporal accesses), xcd=0|1 (XCD-contiguous
-//     block mapping), block=64..1024 (threads per workgroup);
+//   every kernel: nt=0|1 (nontemporal accesses), bnt=0|1 (nontemporal loads
+//     also for broadcast inputs, which other rows read again), fexp=0|1
+//     (the split-product exponential for a softmax's f32 exp, else the
+//     library's), xcd=0|1 (XCD-contiguous block mapping), block=64..1024
+//     (threads per workgroup);
 //   tree kernels: tper=4|8|16 (elements per thread);
 //   row kernels: epl (elements of output a lane aims for), lanes=16|32|
 //     64..1024, epmax (most elements a lane holds before the tiled kernel
@@ -32,8 +35,8 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //     (odd phases walk the tiles last to first), mu / lu (unroll of the
 //     loops over tiles read from memory / kept in LDS).
 // A layout never changes which elements are computed; lanes, epl, epmax,
-// tiled, tn and alt change a reduction's bracketing (within tolerance), the
-// others change no bit.
+// tiled, tn and alt change a reduction's bracketing (within tolerance), fexp
+// an exponential's last bits (within tolerance), the others change no bit.
 static int layout_value(const char* key, int dflt)
 {
     const char* env = std::getenv("PSK_LAYOUT");
@@ -52,9 +55,10 @@ static int layout_value(const char* key, int dflt)
 
 std::string KernelPlan::key() const
 {
-    char b[160];
-    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d c%d w%d m%d p%d r%d s%d", kind, vec, block,
-                  lanes, nv, (int)nt, (int)xcd, (long long)blocks, tiles, (int)tcache, wpe, wmin, persist, rcache, lcache);
+    char b[200];
+    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d c%d w%d m%d p%d r%d s%d bn%d fe%d", kind, vec,
+                  block, lanes, nv, (int)nt, (int)xcd, (long long)blocks, tiles, (int)tcache, wpe, wmin, persist, rcache,
+                  lcache, (int)bnt, (int)fexp);
     if (kind == 4) return std::string(b) + " K" + std::to_string(split);
     return kind == 3 ? std::string(b) + (alt ? " a1" : " a0") + " u" + std::to_string(munroll) + " y" +
                            std::to_string(lunroll)
@@ -69,6 +73,8 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector, int split_ept)
     // last-axis step of 1 and row starts at whole vectors
     p.vec = (allow_vector && an.cols % V == 0 && inputs_vector_ok(an, V)) ? V : 1;
     p.nt = layout_value("nt", 1) != 0;
+    p.bnt = layout_value("bnt", 0) != 0;
+    p.fexp = layout_value("fexp", 1) != 0;
     if (an.tree) {
         // Workgroups of 128 threads; each thread takes `vec` consecutive
         // elements, the fewest of 4, 8, 16 that move at least 48 bytes.

@@ -116,6 +116,8 @@ struct KernelPlan {
                              // lanes * nv * vec columns kept in registers
     int exch = 0;            // split rows: row values exchanged per row (one per reduction)
     bool nt = true;          // nontemporal loads and stores
+    bool bnt = false;        // nontemporal loads also for inputs read again by other rows (broadcast)
+    bool fexp = true;        // exp(y - max y) with f32 results by the split-product exponential
     bool xcd = true;         // each XCD takes a contiguous eighth of the blocks
     int64_t blocks = 0;      // workgroups that carry work
     int64_t per_xcd = 0;     // blocks per XCD (xcd layout)

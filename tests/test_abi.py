@@ -506,16 +506,26 @@ def test_precision_follows_what_is_stored(lib):
                                           extras=[(C.RMSNORM_H, (R, N), "f32")]))
     body = rmsh[rmsh.index('extern "C"'):]
     assert "psk_gelu_b(" in body and "psk_divr(" not in body and "* y8)" in body
-    # softmax's exp(y - max y): the short exponential only for bf16 results
-    for dt, short in (("bf16", True), ("f32", False)):
+    # softmax's exp(y - max y): the short exponential for bf16 results, the
+    # split-product one (about two ulps) for f32 results, the library's when
+    # the layout asks for it
+    for dt, fn in (("bf16", "psk_exp_np_b("), ("f32", "psk_exp_np(")):
         sm = P.psk_group_source(P.GroupDesc(C.softmax_causal_dag(0.125, N), [((R, N), dt)], (R, N), dt))
         body = sm[sm.index('extern "C"'):]
-        assert ("psk_exp_np_b(" in body) == short and ("expf(" in body) != short
+        assert fn in body and "expf(" not in body, dt
+    import os
+    os.environ["PSK_LAYOUT"] = "fexp=0"
+    try:
+        sm = P.psk_group_source(P.GroupDesc(C.softmax_causal_dag(0.125, N), [((R, N), "f32")], (R, N), "f32"))
+    finally:
+        del os.environ["PSK_LAYOUT"]
+    body = sm[sm.index('extern "C"'):]
+    assert "expf(" in body and "psk_exp_np(" not in body
     # ... but not where a difference could cancel its error (1 - exp(y - max y))
     one = P.psk_group_source(_desc("%0 = input 0\n%1 = row_max %0\n%2 = sub %0 %1\n%3 = exp %2\n"
                                    "%4 = const 1.0\n%5 = sub %4 %3\n", [((R, N), "bf16")], (R, N), "bf16"))
     body = one[one.index('extern "C"'):]
-    assert "psk_exp_np_b(" not in body and "expf(" in body
+    assert "psk_exp_np_b(" not in body and "psk_exp_np(" not in body and "expf(" in body
     # a gelu that other members read is not the bf16 form
     tree = P.psk_group_source(P.GroupDesc(C.tree_mixed_dag(), [((1,), "f32"), ((1,), "bf16"), ((), "f32")], (1,),
                                           "bf16", flags=P.PSK_GROUP_TREE))
@@ -528,7 +538,7 @@ def test_online_normalizer_flag(lib, monkeypatch):
     # a softmax: its sum moves into the maximum's pass (one reduction phase)
     src = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((8, 64), "f32")], (8, 64), "f32", flags=O))
     body = src[src.index('extern "C"'):]
-    assert "float tm = " in body and "expf(q" in body
+    assert "float tm = " in body and "psk_exp_np(q" in body
     wide = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((4, 70000), "f32")], (4, 70000), "f32",
                                           flags=O))
     monkeypatch.setenv("PSK_LAYOUT", "tiled=1")      # the exact sum through the tiled kernel, for comparison

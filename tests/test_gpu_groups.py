@@ -396,3 +396,31 @@ def test_row_max_signed_zeros_and_nan(layout, monkeypatch):
         assert np.array_equal(np.isnan(got), nan), f"{layout}: {name} NaN positions differ"
         assert_bits(got[~nan], r[~nan], f"{layout}: {name}")
     assert np.signbit(rmx[3, 0]) and not np.signbit(rmx[4, 0]) and not np.signbit(rmx[5, 0])
+
+
+def test_split_product_exponential_within_three_ulps():
+    """exp(x - max x) with f32 results takes the split-product exponential
+    (2^t (1 + r ln 2), t = fl((x - m) log2 e)): against float64 exp of the
+    same f32 differences, within 3 f32 ulps wherever the result is normal,
+    and below 2^-126 where it is not; -inf gives 0."""
+    from synth.dag import parse_dag
+    nodes = parse_dag("%0 = input 0\n%1 = row_max %0\n%2 = sub %0 %1\n%3 = exp %2\n")
+    R, C = 256, 4096
+    rng = np.random.default_rng(31)
+    x = (-rng.random((R, C)) * 104.0).astype(np.float32)
+    x[:, 0] = 0.0                                            # the row maximum is 0: x - m is x
+    x[:, 1] = -np.inf
+    x[:, 2:40] = -(np.arange(38, dtype=np.float32) * 2.0 ** -20)   # tiny arguments
+    g = P.Group(nodes, [((R, C), "f32")], (R, C), "f32")
+    assert "psk_exp_np(" in P.psk_group_source(g.desc)
+    out = torch.full((R, C), float("nan"), device=DEV)
+    g.run([torch.from_numpy(x).to(DEV)], out)
+    torch.cuda.synchronize()
+    got = to_np(out).astype(np.float64)
+    ref = np.exp(x.astype(np.float64))
+    normal = ref >= 2.0 ** -126
+    ulp = np.spacing(ref[normal].astype(np.float32)).astype(np.float64)
+    err = np.abs(got[normal] - ref[normal]) / ulp
+    assert err.max() <= 3.0, f"split-product exponential: {err.max():.2f} ulps"
+    assert np.all(np.abs(got[~normal] - ref[~normal]) <= 2.0 ** -126)
+    assert np.all(got[:, 1] == 0.0)
