@@ -1651,17 +1651,27 @@ struct Emitter {
         o << "    " << I() << " row = (" << I() << ")blockIdx.x;\n";
         o << "    const " << I() << " G = (" << I() << ")gridDim.x;\n";
         o << "    int par = 0;\n";
-        if (period > 0) o << "    int q0 = (int)(row % (" << I() << ")" << period << ");\n";
-        // the first row's element inputs
-        for (size_t k = 0; k < an.inputs.size(); ++k) {
-            const InputInfo& in = an.inputs[k];
-            if (!streamed(in)) continue;
-            for (int v = 0; v < pl.nv; ++v)
-                load_pieces((int)k, elem_offset(in, "row", "c" + std::to_string(v)), v * V,
-                            vcond(v, "row < (" + std::string(I()) + ")n_total", "q0", in), "cw");
+        // Prefetch depth D: when a row starts, the element inputs of rows
+        // row, row + G, ..., row + (D - 1) G are in registers (buffers cw,
+        // w1 .. w(D-1)); the row's iteration loads row + D G (buffer nw),
+        // and the buffers shift by one at its end.
+        const int D = std::max(1, std::min(4, pl.pf));
+        auto bufname = [&](int d) { return d == 0 ? std::string("cw") : "w" + std::to_string(d); };
+        for (int d = 0; d < D; ++d) {
+            const std::string pr = "pr" + std::to_string(d);
+            o << "    const " << I() << " " << pr << " = row + (" << I() << ")" << d << " * G;\n";
+            if (period > 0)
+                o << "    const int q" << pr << " = (int)(" << pr << " % (" << I() << ")" << period << ");\n";
+            for (size_t k = 0; k < an.inputs.size(); ++k) {
+                const InputInfo& in = an.inputs[k];
+                if (!streamed(in)) continue;
+                for (int v = 0; v < pl.nv; ++v)
+                    load_pieces((int)k, elem_offset(in, pr, "c" + std::to_string(v)), v * V,
+                                vcond(v, pr + " < (" + std::string(I()) + ")n_total", "q" + pr, in), bufname(d));
+            }
         }
         o << "    for (; row < (" << I() << ")n_total; row += G) {\n";
-        o << "    const " << I() << " nrow = row + G;\n";
+        o << "    const " << I() << " nrow = row + (" << I() << ")" << D << " * G;\n";
         o << "    const bool nok = nrow < (" << I() << ")n_total;\n";
         if (period > 0) o << "    const int qn = (int)(nrow % (" << I() << ")" << period << ");\n";
         for (size_t k = 0; k < an.inputs.size(); ++k) {
@@ -1686,7 +1696,10 @@ struct Emitter {
             const InputInfo& in = an.inputs[k];
             if (!streamed(in)) continue;
             for (int v = 0; v < pl.nv; ++v)
-                for (const Piece& pc : pieces((int)k, v * V)) o << "    cw" << pc.name << " = nw" << pc.name << ";\n";
+                for (const Piece& pc : pieces((int)k, v * V))
+                    for (int d = 0; d < D; ++d)
+                        o << "    " << bufname(d) << pc.name << " = " << (d + 1 < D ? bufname(d + 1) : std::string("nw"))
+                          << pc.name << ";\n";
         }
         o << "    par ^= 1;\n";
         o << "    }\n";

@@ -28,7 +28,9 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //   row kernels: epl (elements of output a lane aims for), lanes=16|32|
 //     64..1024, epmax (most elements a lane holds before the tiled kernel
 //     takes over, default 32), persist=k (k persistent workgroups a CU),
-//     tiled=1 (force the tiled kernel);
+//     pf=1..4 (rows a persistent workgroup loads ahead), tiled=1 (force the
+//     tiled kernel), split=0 (no split rows), sept (elements a lane of a
+//     split row holds);
 //   tiled kernel: lanes=64..1024, tn (vectors a lane per tile), tcache=0|1
 //     (cached loads before the last phase), rc / lc (tiles kept in
 //     registers / LDS), wpe / wmin (most / fewest waves a SIMD), alt=0|1
@@ -60,6 +62,7 @@ std::string KernelPlan::key() const
                   block, lanes, nv, (int)nt, (int)xcd, (long long)blocks, tiles, (int)tcache, wpe, wmin, persist, rcache,
                   lcache, (int)bnt, (int)fexp);
     if (kind == 4) return std::string(b) + " K" + std::to_string(split);
+    if (persist) return std::string(b) + " pf" + std::to_string(pf);
     return kind == 3 ? std::string(b) + (alt ? " a1" : " a0") + " u" + std::to_string(munroll) + " y" +
                            std::to_string(lunroll)
                      : std::string(b);
@@ -155,6 +158,8 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector, int split_ept)
         const int persist = online ? 0 : layout_value("persist", persist_dflt);
         if (persist > 0 && p.rows_per_block == 1) {
             p.persist = persist;
+            p.pf = layout_value("pf", 1);
+            if (p.pf < 1 || p.pf > 4) p.pf = 1;
             p.blocks = std::min<int64_t>(an.rows, (int64_t)256 * persist);
             p.xcd = false;
         }

@@ -112,6 +112,7 @@ struct KernelPlan {
     int wpe = 0;             // tiled row kernel: at most this many waves per SIMD (0: no limit)
     int wmin = 0;            // tiled row kernel: registers for at least this many waves per SIMD (0: any)
     int persist = 0;         // row kernel: persistent workgroups per CU (0: one workgroup per row)
+    int pf = 1;              // persistent rows: rows whose inputs are loaded ahead of the current one
     int split = 0;           // split rows (kind 4): workgroups that share one row, each a segment of
                              // lanes * nv * vec columns kept in registers
     int exch = 0;            // split rows: row values exchanged per row (one per reduction)

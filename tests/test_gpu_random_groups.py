@@ -156,6 +156,7 @@ def test_random_exact_row_groups_bit_for_bit(chunk):
     ("tiled=1,lanes=256,tn=2,rc=2,lc=2,mu=3", 11),     # an unroll that leaves a remainder
     ("tiled=1,lanes=128,tn=1,rc=0,lc=0,alt=0", 12),    # every tile from memory, every phase forwards
     ("persist=2", 13),                                 # persistent rows (next row loaded during this one)
+    ("persist=3,pf=3", 15),                            # persistent rows loading three rows ahead
     ("lanes=32", 14),                                  # half-wave rows (the 32-lane join)
 ])
 def test_random_exact_row_groups_through_other_layouts(layout, chunk, monkeypatch):
