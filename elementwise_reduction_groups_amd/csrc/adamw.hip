@@ -60,14 +60,17 @@ psk_status static_scratch(double** partials, ClipOut** out)
 
 namespace {
 
-// Launch shape, chosen by measurement on MI355X over the 145-leaf tree:
-// small workgroups of 128 threads, 4 elements per thread (8-byte bf16 and
-// 16-byte f32 accesses, one per stream), nontemporal loads and stores (every
-// byte is touched once), and each XCD given one contiguous eighth of the
-// chunks: 5.96 TB/s, against 5.17 with 8 elements x 2 steps x 256 threads
-// and plain accesses, 5.47 nontemporal, 5.83 with 256-thread workgroups.
+// Launch shape, chosen by measurement on MI355X over the 145-leaf tree
+// (bf16 theta and g, f32 m and v; medians of 12 runs): workgroups of 128
+// threads, 2 elements per thread (4-byte bf16 and 8-byte f32 accesses, one
+// per stream), nontemporal loads and stores (every byte is touched once),
+// and each XCD given one contiguous eighth of the chunks: 6.14 TB/s,
+// against 5.99 with 4 elements per thread, 6.03 with 2 elements and
+// 64-thread workgroups, 6.09 with 512-thread workgroups.  Storing theta'
+// first, loading the moments first or reading the leaf pointers from the
+// chunk table change nothing measurable.
 constexpr int kBlock = 128;
-constexpr int kPer = 4;                                   // elements per thread
+constexpr int kPer = 2;                                   // elements per thread
 constexpr int kSub = PSK_TREE_CHUNK / (kBlock * kPer);   // workgroups per chunk
 static_assert(kSub * kBlock * kPer == PSK_TREE_CHUNK, "a chunk must split into whole workgroups");
 constexpr int kXcds = 8;
@@ -106,11 +109,16 @@ template <> struct Io<float> {
         x[0] = __uint_as_float(w[0]); x[1] = __uint_as_float(w[1]);
         x[2] = __uint_as_float(w[2]); x[3] = __uint_as_float(w[3]);
     }
-    static __device__ __forceinline__ float load1(const void* p, int64_t e) { return *gbl<float>(p, e); }
-    static __device__ __forceinline__ void store4(void* p, int64_t e, const float* x)
+    static __device__ __forceinline__ void load2(const void* p, int64_t e, float* x)
     {
-        u4v w = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
-        __builtin_nontemporal_store(w, (PSK_GLOBAL u4v*)gbl<float>(p, e));
+        u2v w = __builtin_nontemporal_load((const PSK_GLOBAL u2v*)gbl<float>(p, e));
+        x[0] = __uint_as_float(w[0]); x[1] = __uint_as_float(w[1]);
+    }
+    static __device__ __forceinline__ float load1(const void* p, int64_t e) { return *gbl<float>(p, e); }
+    static __device__ __forceinline__ void store2(void* p, int64_t e, const float* x)
+    {
+        u2v w = {__float_as_uint(x[0]), __float_as_uint(x[1])};
+        __builtin_nontemporal_store(w, (PSK_GLOBAL u2v*)gbl<float>(p, e));
     }
     static __device__ __forceinline__ void store1(void* p, int64_t e, float x) { *gbl<float>(p, e) = x; }
     static __device__ __forceinline__ float through(float x) { return x; }
@@ -127,20 +135,18 @@ template <> struct Io<__bf16> {
             x[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
         }
     }
-    static __device__ __forceinline__ void load4(const void* p, int64_t e, float* x)
+    static __device__ __forceinline__ void load2(const void* p, int64_t e, float* x)
     {
-        u2v w = __builtin_nontemporal_load((const PSK_GLOBAL u2v*)gbl<unsigned short>(p, e));
-        x[0] = __uint_as_float(w[0] << 16); x[1] = __uint_as_float(w[0] & 0xffff0000u);
-        x[2] = __uint_as_float(w[1] << 16); x[3] = __uint_as_float(w[1] & 0xffff0000u);
+        unsigned w = __builtin_nontemporal_load((const PSK_GLOBAL unsigned*)gbl<unsigned short>(p, e));
+        x[0] = __uint_as_float(w << 16); x[1] = __uint_as_float(w & 0xffff0000u);
     }
     static __device__ __forceinline__ float load1(const void* p, int64_t e)
     {
         return __uint_as_float(((unsigned)*gbl<unsigned short>(p, e)) << 16);
     }
-    static __device__ __forceinline__ void store4(void* p, int64_t e, const float* x)
+    static __device__ __forceinline__ void store2(void* p, int64_t e, const float* x)
     {
-        u2v w = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
-        __builtin_nontemporal_store(w, (PSK_GLOBAL u2v*)gbl<unsigned short>(p, e));
+        __builtin_nontemporal_store(pack_bf16(x[0], x[1]), (PSK_GLOBAL unsigned*)gbl<unsigned short>(p, e));
     }
     static __device__ __forceinline__ void store1(void* p, int64_t e, float x)
     {
@@ -159,6 +165,22 @@ template <> struct Io<__bf16> {
 // [x * per, (x + 1) * per); virtual blocks past the end exit.
 __device__ __forceinline__ unsigned xcd_block(unsigned b, unsigned per) { return (b % kXcds) * per + b / kXcds; }
 
+// a / b for a divisor b in [2^-40, 2^40] shared by every element, given y,
+// the correctly rounded 1/b: q = a*y is within an ulp of a/b, the fma gives
+// the exact remainder a - b*q, and a second fma rounds q + remainder*y to
+// the correctly rounded quotient (Markstein).  That needs a zero or in
+// [2^-86, 2^87] (no underflow of the remainder, no overflow of q); `bad`
+// records a lane where it is not.  A zero a returns q itself, which keeps
+// the sign of -0.
+__device__ __forceinline__ float div_shared(float a, float b, float y, bool& bad)
+{
+    const float q = a * y;
+    const float rem = fmaf(-q, b, a);
+    const bool zero = a == 0.0f;
+    bad |= !((fabsf(a) >= 0x1p-86f || zero) && fabsf(a) <= 0x1p87f);
+    return zero ? q : fmaf(rem, y, q);
+}
+
 template <typename TP, typename TG, typename TM, bool SCALE>
 __global__ void __launch_bounds__(kBlock)
 adamw_tree_kernel(const LeafDev* __restrict__ leaves, const ChunkDev* __restrict__ chunks, unsigned n_virtual,
@@ -167,28 +189,28 @@ adamw_tree_kernel(const LeafDev* __restrict__ leaves, const ChunkDev* __restrict
     const unsigned vb = xcd_block(blockIdx.x, per_xcd);
     if (vb >= n_virtual) return;
     const ChunkDev ch = chunks[vb / kSub];
-    const LeafDev* L = leaves + ch.leaf;   // only the slots used are read
+    const LeafDev L = leaves[ch.leaf];     // the seven slots and the flags, read together
     const int i0 = ((int)(vb % kSub) * kBlock + (int)threadIdx.x) * kPer;   // offset within the chunk
     const int cnt = ch.count - i0;
     if (cnt <= 0) return;
     const int64_t e0 = ch.start + i0;
-    const bool full = (L->flags & 1) != 0 && cnt >= kPer;
+    const bool full = (L.flags & 1) != 0 && cnt >= kPer;
 
     float th[kPer], g[kPer], m[kPer], v[kPer];
     if (full) {
-        Io<TP>::load4(L->in[0], e0, th);
-        Io<TG>::load4(L->in[1], e0, g);
-        Io<TM>::load4(L->in[2], e0, m);
-        Io<TM>::load4(L->in[3], e0, v);
+        Io<TP>::load2(L.in[0], e0, th);
+        Io<TG>::load2(L.in[1], e0, g);
+        Io<TM>::load2(L.in[2], e0, m);
+        Io<TM>::load2(L.in[3], e0, v);
     } else {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             th[j] = g[j] = m[j] = v[j] = 0.0f;
             if (j < cnt) {
-                th[j] = Io<TP>::load1(L->in[0], e0 + j);
-                g[j] = Io<TG>::load1(L->in[1], e0 + j);
-                m[j] = Io<TM>::load1(L->in[2], e0 + j);
-                v[j] = Io<TM>::load1(L->in[3], e0 + j);
+                th[j] = Io<TP>::load1(L.in[0], e0 + j);
+                g[j] = Io<TG>::load1(L.in[1], e0 + j);
+                m[j] = Io<TM>::load1(L.in[2], e0 + j);
+                v[j] = Io<TM>::load1(L.in[3], e0 + j);
             }
         }
     }
@@ -202,29 +224,46 @@ adamw_tree_kernel(const LeafDev* __restrict__ leaves, const ChunkDev* __restrict
         vo[j] = Io<TM>::through(s.b2 * v[j] + s.c2 * (gj * gj));
     }
     if (full) {
-        Io<TM>::store4(L->out[1], e0, mo);
-        Io<TM>::store4(L->out[2], e0, vo);
+        Io<TM>::store2(L.out[1], e0, mo);
+        Io<TM>::store2(L.out[2], e0, vo);
     } else {
 #pragma unroll
         for (int j = 0; j < kPer; ++j)
             if (j < cnt) {
-                Io<TM>::store1(L->out[1], e0 + j, mo[j]);
-                Io<TM>::store1(L->out[2], e0 + j, vo[j]);
+                Io<TM>::store1(L.out[1], e0 + j, mo[j]);
+                Io<TM>::store1(L.out[2], e0 + j, vo[j]);
             }
+    }
+    // the bias corrections: by the reciprocals where the host gave them and
+    // every dividend lies in range, else by division, which gives the same
+    // bits
+    float mh[kPer], vh[kPer];
+    bool bad = s.rc1 == 0.0f;
+    if (!bad) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            mh[j] = div_shared(mo[j], s.bc1, s.rc1, bad);
+            vh[j] = div_shared(vo[j], s.bc2, s.rc2, bad);
+        }
+    }
+    if (bad) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            mh[j] = mo[j] / s.bc1;
+            vh[j] = vo[j] / s.bc2;
+        }
     }
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-        const float mh = mo[j] / s.bc1;
-        const float vh = vo[j] / s.bc2;
-        const float upd = mh / (sqrtf(vh) + s.eps) + s.wd * th[j];
+        const float upd = mh[j] / (sqrtf(vh[j]) + s.eps) + s.wd * th[j];
         to[j] = th[j] - s.lr * upd;
     }
     if (full) {
-        Io<TP>::store4(L->out[0], e0, to);
+        Io<TP>::store2(L.out[0], e0, to);
     } else {
 #pragma unroll
         for (int j = 0; j < kPer; ++j)
-            if (j < cnt) Io<TP>::store1(L->out[0], e0 + j, to[j]);
+            if (j < cnt) Io<TP>::store1(L.out[0], e0 + j, to[j]);
     }
 }
 

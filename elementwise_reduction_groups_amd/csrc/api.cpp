@@ -46,6 +46,13 @@ AdamwScalars adamw_scalars(const psk_adamw_hp& hp)
     s.lr = (float)hp.lr;
     s.eps = (float)hp.eps;
     s.wd = (float)hp.weight_decay;
+    // 1/bc in f64 rounded to f32 is the correctly rounded f32 reciprocal:
+    // rounding twice is harmless for a quotient when the first rounding keeps
+    // at least 2*24+2 bits (Figueroa's condition; f64 keeps 53)
+    auto in_range = [](float b) { return b >= 0x1p-40f && b <= 0x1p40f; };
+    const bool rec = in_range(s.bc1) && in_range(s.bc2);
+    s.rc1 = rec ? (float)(1.0 / (double)s.bc1) : 0.0f;
+    s.rc2 = rec ? (float)(1.0 / (double)s.bc2) : 0.0f;
     return s;
 }
 

@@ -1094,8 +1094,9 @@ struct Emitter {
     // tree's chunk table; per-element inputs come from the leaf's slots,
     // per-tree inputs from device scalars; the root goes to the output slot.
     // A thread whose NE elements are all present in a leaf whose slots are
-    // 16-byte aligned moves them as 16-byte (or, for 4 bf16, 8-byte)
-    // vectors; the last thread of a ragged leaf goes element by element.
+    // 16-byte aligned moves them as vectors of up to 16 bytes (NE of 2: 4
+    // bytes of bf16, 8 of f32); the last thread of a ragged leaf goes
+    // element by element.
     std::string tree(const std::string& name)
     {
         const int TB = pl.block, TS = (int)pl.blocks;
@@ -1119,7 +1120,10 @@ struct Emitter {
         o << "  const long long e0 = ch.start + i0;\n";
         o << "  const bool full = (L->flags & 1) != 0 && cnt >= " << NE << ";\n";
         o << "  {\n";
-        // per-tree scalars and per-element inputs
+        // per-tree scalars and per-element inputs: every input's vector
+        // loads in one branch, issued before any of them is waited for, the
+        // element-by-element loads of a ragged thread in the other
+        std::vector<size_t> vin;
         for (size_t k = 0; k < an.inputs.size(); ++k) {
             const InputInfo& in = an.inputs[k];
             if (!in.used) continue;
@@ -1130,30 +1134,48 @@ struct Emitter {
                   << (in.dtype == PSK_BF16 ? "psk_h(*" + p + ")" : "*" + p) << ";\n";
                 continue;
             }
+            vin.push_back(k);
             o << "    const PSK_G " << T << "* in" << k << " = (const PSK_G " << T << "*)L->slot[slot" << k << "] + e0;\n";
+            o << "    float";
+            for (int j = 0; j < NE; ++j) o << (j ? ", x" : " x") << k << "_" << j;
+            o << ";\n";
+        }
+        o << "    if (full) {\n";
+        for (size_t k : vin) {
+            const InputInfo& in = an.inputs[k];
             const int nw = NE * esize(in.dtype) / 4;   // 32-bit words of the thread's elements
             std::string w = "w" + std::to_string(k);
-            o << "    unsigned " << w << "[" << nw << "];\n";
-            o << "    if (full) {\n";
-            if (nw == 2) {
-                o << "      const psk_u2v t = psk_ld((const PSK_G psk_u2v*)in" << k << ");\n";
-                o << "      " << w << "[0] = t[0]; " << w << "[1] = t[1];\n";
+            o << "      unsigned " << w << "[" << nw << "];\n";
+            if (nw == 1) {
+                o << "      " << w << "[0] = psk_ld((const PSK_G unsigned*)in" << k << ");\n";
+            } else if (nw == 2) {
+                o << "      const psk_u2v t" << k << " = psk_ld((const PSK_G psk_u2v*)in" << k << ");\n";
+                o << "      " << w << "[0] = t" << k << "[0]; " << w << "[1] = t" << k << "[1];\n";
             } else {
                 for (int q = 0; q < nw / 4; ++q) {
-                    o << "      const psk_u4v t" << q << " = psk_ld((const PSK_G psk_u4v*)in" << k << " + " << q
-                      << ");\n";
-                    for (int j = 0; j < 4; ++j) o << "      " << w << "[" << 4 * q + j << "] = t" << q << "[" << j << "];\n";
+                    std::string t = "t" + std::to_string(k) + "_" + std::to_string(q);
+                    o << "      const psk_u4v " << t << " = psk_ld((const PSK_G psk_u4v*)in" << k << " + " << q << ");\n";
+                    for (int j = 0; j < 4; ++j) o << "      " << w << "[" << 4 * q + j << "] = " << t << "[" << j << "];\n";
                 }
             }
-            o << "    }\n";
+        }
+        for (size_t k : vin) {
+            const InputInfo& in = an.inputs[k];
+            std::string w = "w" + std::to_string(k);
             for (int j = 0; j < NE; ++j) {
-                o << "    const float x" << k << "_" << j << " = full ? ";
-                if (in.dtype == PSK_F32) o << "__uint_as_float(" << w << "[" << j << "])";
-                else o << (j % 2 == 0 ? "psk_lo(" : "psk_hi(") << w << "[" << j / 2 << "])";
-                o << " : (" << j << " < cnt ? " << (in.dtype == PSK_BF16 ? "psk_h(in" : "(in") << k << "[" << j
-                  << "]) : 0.0f);\n";
+                o << "      x" << k << "_" << j << " = ";
+                if (in.dtype == PSK_F32) o << "__uint_as_float(" << w << "[" << j << "]);\n";
+                else o << (j % 2 == 0 ? "psk_lo(" : "psk_hi(") << w << "[" << j / 2 << "]);\n";
             }
         }
+        o << "    } else {\n";
+        for (size_t k : vin) {
+            const InputInfo& in = an.inputs[k];
+            for (int j = 0; j < NE; ++j)
+                o << "      x" << k << "_" << j << " = " << j << " < cnt ? " << (in.dtype == PSK_BF16 ? "psk_h(in" : "(in")
+                  << k << "[" << j << "]) : 0.0f;\n";
+        }
+        o << "    }\n";
         leaves();
         members_at(0);
         for (size_t k = 0; k < an.extras.size(); ++k)
@@ -1171,12 +1193,17 @@ struct Emitter {
         o << "    PSK_G " << T << "* " << name << " = (PSK_G " << T << "*)L->slot[slot" << slot_arg << "] + e0;\n";
         const std::string out = name;
         o << "    if (full) {\n";
-        if (dt == PSK_F32) {
+        if (dt == PSK_F32 && NE == 2) {
+            o << "      psk_st((PSK_G psk_u2v*)" << out << ", (psk_u2v){__float_as_uint(" << val(root, 0)
+              << "), __float_as_uint(" << val(root, 1) << ")});\n";
+        } else if (dt == PSK_F32) {
             for (int q = 0; q < NE / 4; ++q) {
                 o << "      psk_st((PSK_G psk_u4v*)" << out << " + " << q << ", (psk_u4v){";
                 for (int j = 0; j < 4; ++j) o << (j ? ", " : "") << "__float_as_uint(" << val(root, 4 * q + j) << ")";
                 o << "});\n";
             }
+        } else if (NE == 2) {
+            o << "      psk_st((PSK_G unsigned*)" << out << ", psk_pack2(" << val(root, 0) << ", " << val(root, 1) << "));\n";
         } else if (NE == 4) {
             o << "      psk_st((PSK_G psk_u2v*)" << out << ", (psk_u2v){psk_pack2(" << val(root, 0) << ", " << val(root, 1)
               << "), psk_pack2(" << val(root, 2) << ", " << val(root, 3) << ")});\n";

@@ -24,7 +24,7 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //     (the split-product exponential for a softmax's f32 exp, else the
 //     library's), xcd=0|1 (XCD-contiguous block mapping), block=64..1024
 //     (threads per workgroup);
-//   tree kernels: tper=4|8|16 (elements per thread);
+//   tree kernels: tper=2|4|8|16 (elements per thread);
 //   row kernels: epl (elements of output a lane aims for), lanes=16|32|
 //     64..1024, epmax (most elements a lane holds before the tiled kernel
 //     takes over, default 32), persist=k (k persistent workgroups a CU),
@@ -80,21 +80,21 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector, int split_ept)
     p.fexp = layout_value("fexp", 1) != 0;
     if (an.tree) {
         // Workgroups of 128 threads; each thread takes `vec` consecutive
-        // elements, the fewest of 4, 8, 16 that move at least 48 bytes.
+        // elements, the fewest of 2, 4, 8, 16 that move at least 40 bytes.
         // Measured on the 887M-element Llama tree: an SGD step (6 bytes per
         // element) runs at 4.6 / 6.4 / 5.3 TB/s with 4 / 8 / 16, AdamW (22
-        // bytes) is fastest with 4.  A chunk splits into whole workgroups;
-        // XCD-contiguous mapping.
+        // bytes) at 6.14 / 5.99 TB/s with 2 / 4.  A chunk splits into whole
+        // workgroups; XCD-contiguous mapping.
         p.kind = 2;
         auto size_of = [](psk_dtype d) { return d == PSK_BF16 ? 2 : 4; };
         int bytes = size_of(an.out_dtype);
         for (const InputInfo& in : an.inputs)
             if (in.used && in.kind != InKind::Scalar) bytes += size_of(in.dtype);
         for (const auto& x : an.extras) bytes += size_of(x.dtype);
-        int per = 4;
-        while (per < 16 && per * bytes < 48) per *= 2;
+        int per = 2;
+        while (per < 16 && per * bytes < 40) per *= 2;
         per = layout_value("tper", per);
-        if (per != 4 && per != 8 && per != 16) per = 4;
+        if (per != 2 && per != 4 && per != 8 && per != 16) per = 4;
         int block = layout_value("block", 128);
         if (block < 64 || block > 256 || (block & (block - 1))) block = 128;
         p.vec = per;

@@ -160,9 +160,12 @@ struct TreePlan {
 psk_status plan_tree(const int64_t* numel, int32_t n_leaves, int64_t chunk_elems, TreePlan& plan);
 
 // ------------------------------------------------------------------ AdamW
-// f32 scalars of one step, each formed in f64 and rounded once.
+// f32 scalars of one step, each formed in f64 and rounded once.  rc1 and
+// rc2 are the correctly rounded reciprocals of bc1 and bc2 when both lie in
+// [2^-40, 2^40] (the kernel then divides by them with one multiply and a
+// correction), else 0 (the kernel divides).
 struct AdamwScalars {
-    float b1, b2, c1, c2, bc1, bc2, lr, eps, wd;
+    float b1, b2, c1, c2, bc1, bc2, lr, eps, wd, rc1, rc2;
 };
 AdamwScalars adamw_scalars(const psk_adamw_hp& hp);
 

@@ -373,7 +373,8 @@ def test_multi_output_kernels_compile(lib, tmp_path):
         if name == "add_rmsnorm_h":
             assert info.algorithmic_bytes == R * N * 2 * 4 + N * 2
         if name == "adamw_tree":
-            assert info.kind == 2 and info.vec == 4
+            # 22 bytes an element: 2 elements a thread (44 bytes)
+            assert info.kind == 2 and info.vec == 2
 
 
 def test_mask_refusals(lib):

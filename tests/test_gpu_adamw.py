@@ -118,6 +118,40 @@ def test_indexing_patterns_exact_special_cases():
         assert torch.equal(s["v"], p["grad"] * p["grad"])      # beta2 = 0
 
 
+def _assert_bits_nan(got, ref, what):
+    """Bit for bit, except that a NaN matches any NaN (payloads differ
+    between the host's and the GPU's default NaN)."""
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), f"{what}: NaN positions differ"
+    assert_bits(np.where(nan, 0, got).astype(got.dtype), np.where(nan, 0, ref).astype(ref.dtype), what)
+
+
+@pytest.mark.parametrize("t,beta2", [(1, HP["beta2"]), (7, HP["beta2"]), (1, 1.0 - 2.0 ** -45)])
+def test_bias_correction_edge_values_bit_exact(t, beta2):
+    # moments and gradients drawn per element from values that put the
+    # bias-corrected quotients outside the range where the kernel divides by
+    # a reciprocal (below 2^-86, above 2^87, subnormal, infinite), signed
+    # zeros, and ordinary values, mixed within every wave; beta2 = 1 - 2^-45
+    # makes 1 - beta2^t smaller than 2^-40, where no reciprocal is used
+    specials = np.array([0.0, -0.0, 1e-30, -1e-30, 1e-40, 3e-39, 1e30, -1e38, 0.5, -0.25, 1e-3, 2.0,
+                         np.inf, 1e20], np.float32)
+    n = 4099
+    rng = np.random.default_rng(t)
+    state = []
+    for leaf in range(3):
+        pick = lambda: specials[rng.integers(0, specials.size, n)]
+        v = np.abs(pick())
+        state.append({"theta": torch.from_numpy(rng.standard_normal(n).astype(np.float32)).to(DEV),
+                      "grad": torch.from_numpy(pick()).to(DEV), "m": torch.from_numpy(pick()).to(DEV),
+                      "v": torch.from_numpy(v).to(DEV)})
+    before = snapshot(state)
+    hp = hp_args(t=t, beta2=beta2)
+    _, outs = run_tree(state, hp)
+    for i, (s, o) in enumerate(zip(before, outs)):
+        for got, ref, name in zip(o, oracle_leaf(s, hp), ("theta'", "m'", "v'")):
+            _assert_bits_nan(to_np(got), ref, f"t={t} beta2={beta2} leaf {i} {name}")
+
+
 def test_empty_leaves_and_empty_tree():
     state = configs.adamw_state([(0,), (17,), (0,)], device=DEV, seed=3)
     before = snapshot(state)
