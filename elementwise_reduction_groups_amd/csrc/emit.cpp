@@ -232,15 +232,25 @@ __device__ __forceinline__ float psk_exp_np(float x) {
 // remainder a - b*q, and one more fma rounds q + remainder*y to the
 // correctly rounded quotient (Markstein's correction).  That holds while
 // b lies in [2^-40, 2^40] and a is zero or in [2^-86, 2^87] (no underflow of
-// the remainder, no overflow of q); `bad` records a lane where it may not,
-// and the caller then redoes that member's elements with IEEE division.
-// A zero a gives q itself: the correction would turn -0 into +0.
-__device__ __forceinline__ float psk_divr(float a, float b, float y, bool& bad) {
+// the remainder, no overflow of q).  The remainder is formed as
+// -(q*b - a), which is the same value and for a zero a has a's sign, so the
+// correction returns a zero of the right sign with no select.  The range of
+// a group of dividends is gathered two elements an instruction: `lo` keeps
+// the least of (bits(a) << 1) - 2 (the magnitude's bits less one, doubled;
+// a zero wraps to the top, so zeros never count as small), `hi` the largest
+// |a| (an infinity counts; a NaN dividend gives NaN either way).
+// psk_divr_bad then says whether the group must be redone with IEEE
+// division.
+__device__ __forceinline__ float psk_divr(float a, float b, float y, unsigned& lo, float& hi) {
   const float q = a * y;
-  const float rem = fmaf(-q, b, a);
-  const bool zero = a == 0.0f;
-  bad |= !((fabsf(a) >= 0x1p-86f || zero) && fabsf(a) <= 0x1p87f);
-  return zero ? q : fmaf(rem, y, q);
+  const float rem = -fmaf(q, b, -a);
+  const unsigned t = (__float_as_uint(a) << 1) - 2u;
+  lo = t < lo ? t : lo;
+  hi = fmaxf(hi, fabsf(a));
+  return fmaf(rem, y, q);
+}
+__device__ __forceinline__ bool psk_divr_bad(unsigned lo, float hi) {
+  return lo < (0x14800000u << 1) - 2u || !(hi <= 0x1p87f);   // 0x14800000: 2^-86
 }
 // +0.0 as an opaque register value (see the emitter's literals)
 __device__ __forceinline__ float psk_pz() { float z = 0.0f; __asm__("" : "+v"(z)); return z; }
@@ -523,16 +533,18 @@ struct Emitter {
     }
 
     // elements of member i (given as element indices) written through
-    // psk_divr: declare the lane flag before, redo with IEEE division after
+    // psk_divr: declare the group's range accumulators before, and after,
+    // redo the group with IEEE division where the divisor or a dividend
+    // lies outside the range the correction covers
     void divr_open(int i)
     {
-        if (divr_node(i)) o << "    bool bad" << i << " = !yok" << an.nodes[i].b << ";\n";
+        if (divr_node(i)) o << "    unsigned lo" << i << " = 0xffffffffu; float hi" << i << " = 0.0f;\n";
     }
     void divr_close(int i, const std::vector<int>& elems, const char* indent)
     {
         if (!divr_node(i)) return;
         const psk_node& nd = an.nodes[i];
-        o << indent << "if (bad" << i << ") {\n";
+        o << indent << "if (!yok" << nd.b << " || psk_divr_bad(lo" << i << ", hi" << i << ")) {\n";
         for (int e : elems)
             o << indent << "  v" << i << "_" << e << " = " << val(nd.a, e) << " / " << val(nd.b, e) << ";\n";
         o << indent << "}\n";
@@ -551,7 +563,8 @@ struct Emitter {
         case PSK_OP_DIV:
             if (recip_node(i)) return "(" + A() + " * y" + std::to_string(nd.b) + ")";
             if (divr_node(i))
-                return "psk_divr(" + A() + ", " + B() + ", y" + std::to_string(nd.b) + ", bad" + std::to_string(i) + ")";
+                return "psk_divr(" + A() + ", " + B() + ", y" + std::to_string(nd.b) + ", lo" + std::to_string(i) +
+                       ", hi" + std::to_string(i) + ")";
             return "(" + A() + " / " + B() + ")";
         case PSK_OP_MAX: return "psk_max(" + A() + ", " + B() + ")";
         case PSK_OP_MIN: return "psk_min(" + A() + ", " + B() + ")";
@@ -764,14 +777,17 @@ struct Emitter {
         return ps;
     }
 
-    // declare input k's pieces as `pfx`<name> and load them (zero when cond fails)
-    void load_pieces(int k, const std::string& off, int e0, const std::string& cond, const std::string& pfx)
+    // declare input k's pieces as `pfx`<name> and load them (zero when cond
+    // fails); with declare false, load into the pieces declared before
+    // (left as they were when cond fails)
+    void load_pieces(int k, const std::string& off, int e0, const std::string& cond, const std::string& pfx,
+                     bool declare = true)
     {
         const InputInfo& in = an.inputs[k];
         const std::string p = "(in" + std::to_string(k) + " + " + off + ")";
         const std::string fn = (in.numel < an.numel && !pl.bnt) ? "psk_ldc" : ld_fn();   // read again by other rows
         for (const Piece& pc : pieces(k, e0)) {
-            o << "    " << pc.type << " " << pfx << pc.name << " = {};\n";
+            if (declare) o << "    " << pc.type << " " << pfx << pc.name << " = {};\n";
             if (pc.type == "float")
                 o << "    if (" << cond << ") " << pfx << pc.name << " = " << widen(in.dtype, fn + "(" + p + ")")
                   << ";\n";
@@ -1641,9 +1657,10 @@ struct Emitter {
     }
 
     // Persistent rows: gridDim.x workgroups walk the rows (row, row + G,
-    // ...); the next row's element inputs are loaded before the current row
-    // is computed, so its loads are in flight during the arithmetic.  Column
-    // vectors (gamma) are loaded and widened once per workgroup.
+    // ...); the element inputs of the next rows are loaded before the
+    // current row is computed, so their loads are in flight during the
+    // arithmetic.  Column vectors (gamma) are loaded and widened once per
+    // workgroup.
     std::string row_persistent(const std::string& name)
     {
         o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n" << kPrelude;
@@ -1677,13 +1694,17 @@ struct Emitter {
         }
         o << "    " << I() << " row = (" << I() << ")blockIdx.x;\n";
         o << "    const " << I() << " G = (" << I() << ")gridDim.x;\n";
+        o << "    const " << I() << " rend = (" << I() << ")n_total;\n";
         o << "    int par = 0;\n";
-        // Prefetch depth D: when a row starts, the element inputs of rows
-        // row, row + G, ..., row + (D - 1) G are in registers (buffers cw,
-        // w1 .. w(D-1)); the row's iteration loads row + D G (buffer nw),
-        // and the buffers shift by one at its end.
+        // Prefetch depth D: buffers b0 .. b(D-1) hold the element inputs of
+        // rows row, row + G, ..., row + (D - 1) G when an iteration starts.
+        // The loop is unrolled D times, one row a buffer: a row widens its
+        // buffer's words, loads row + D G into the same buffer and then
+        // computes, so D rows are in flight during the arithmetic and no
+        // buffer is ever copied (a copy of registers still being loaded
+        // would wait for the load).
         const int D = std::max(1, std::min(4, pl.pf));
-        auto bufname = [&](int d) { return d == 0 ? std::string("cw") : "w" + std::to_string(d); };
+        auto bufname = [&](int d) { return "b" + std::to_string(d) + "_"; };
         for (int d = 0; d < D; ++d) {
             const std::string pr = "pr" + std::to_string(d);
             o << "    const " << I() << " " << pr << " = row + (" << I() << ")" << d << " * G;\n";
@@ -1694,41 +1715,40 @@ struct Emitter {
                 if (!streamed(in)) continue;
                 for (int v = 0; v < pl.nv; ++v)
                     load_pieces((int)k, elem_offset(in, pr, "c" + std::to_string(v)), v * V,
-                                vcond(v, pr + " < (" + std::string(I()) + ")n_total", "q" + pr, in), bufname(d));
+                                vcond(v, pr + " < rend", "q" + pr, in), bufname(d));
             }
         }
-        o << "    for (; row < (" << I() << ")n_total; row += G) {\n";
-        o << "    const " << I() << " nrow = row + (" << I() << ")" << D << " * G;\n";
-        o << "    const bool nok = nrow < (" << I() << ")n_total;\n";
-        if (period > 0) o << "    const int qn = (int)(nrow % (" << I() << ")" << period << ");\n";
-        for (size_t k = 0; k < an.inputs.size(); ++k) {
-            const InputInfo& in = an.inputs[k];
-            if (!streamed(in)) continue;
-            for (int v = 0; v < pl.nv; ++v)
-                load_pieces((int)k, elem_offset(in, "nrow", "c" + std::to_string(v)), v * V, vcond(v, "nok", "qn", in),
-                            "nw");
+        o << "    for (; row < rend; row += (" << I() << ")" << D << " * G) {\n";
+        for (int d = 0; d < D; ++d) {
+            o << "    if (row + (" << I() << ")" << d << " * G < rend) {\n";
+            o << "    const " << I() << " nrow = row + (" << I() << ")" << d + D << " * G;\n";
+            o << "    const bool nok = nrow < rend;\n";
+            if (period > 0) o << "    const int qn = (int)(nrow % (" << I() << ")" << period << ");\n";
+            o << "    {\n";
+            o << "    const " << I() << " row2 = row + (" << I() << ")" << d << " * G;\n";
+            o << "    {\n";
+            o << "    const " << I() << " row = row2;\n";
+            o << "    const bool rok = true;\n";
+            if (period > 0) o << "    const int q = (int)(row % (" << I() << ")" << period << ");\n";
+            row_inputs("row", "rok");
+            for (size_t k = 0; k < an.inputs.size(); ++k) {
+                const InputInfo& in = an.inputs[k];
+                if (!streamed(in)) continue;
+                for (int v = 0; v < pl.nv; ++v) decode_pieces((int)k, v * V, bufname(d));
+            }
+            for (size_t k = 0; k < an.inputs.size(); ++k) {
+                const InputInfo& in = an.inputs[k];
+                if (!streamed(in)) continue;
+                for (int v = 0; v < pl.nv; ++v)
+                    load_pieces((int)k, elem_offset(in, "nrow", "c" + std::to_string(v)), v * V,
+                                vcond(v, "nok", "qn", in), bufname(d), false);
+            }
+            row_body();
+            o << "    }\n";
+            o << "    }\n";
+            o << "    par ^= 1;\n";
+            o << "    }\n";
         }
-        o << "    {\n";
-        o << "    const bool rok = true;\n";
-        if (period > 0) o << "    const int q = (int)(row % (" << I() << ")" << period << ");\n";
-        row_inputs("row", "rok");
-        for (size_t k = 0; k < an.inputs.size(); ++k) {
-            const InputInfo& in = an.inputs[k];
-            if (!streamed(in)) continue;
-            for (int v = 0; v < pl.nv; ++v) decode_pieces((int)k, v * V, "cw");
-        }
-        row_body();
-        o << "    }\n";
-        for (size_t k = 0; k < an.inputs.size(); ++k) {
-            const InputInfo& in = an.inputs[k];
-            if (!streamed(in)) continue;
-            for (int v = 0; v < pl.nv; ++v)
-                for (const Piece& pc : pieces((int)k, v * V))
-                    for (int d = 0; d < D; ++d)
-                        o << "    " << bufname(d) << pc.name << " = " << (d + 1 < D ? bufname(d + 1) : std::string("nw"))
-                          << pc.name << ";\n";
-        }
-        o << "    par ^= 1;\n";
         o << "    }\n";
         o << "  }\n}\n";
         return o.str();

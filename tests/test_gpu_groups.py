@@ -289,6 +289,19 @@ def test_division_by_a_row_value_is_ieee_bit_exact(C):
     ref = oracle.eval_group(nodes, [x.numpy(), d.numpy()], (R, C))
     assert_bits(to_np(out), ref, f"x / row value, {C} columns")
     assert (to_np(out)[0, ::3].view(np.uint32) == 0x80000000).all()   # -0 / positive = -0
+    # dividends the divisor does not depend on: infinities, both zeros, and
+    # magnitudes on either side of 2^-86 and 2^87 mixed within every vector
+    vals = torch.tensor([float("inf"), float("-inf"), 0.0, -0.0, 2.0 ** -86, -(2.0 ** -86) * (1 - 2 ** -24),
+                         2.0 ** 87, -(2.0 ** 87) * (1 + 2 ** -23), 1e-40, 3.5, -1.25], dtype=torch.float32)
+    xs = torch.randn(R, C, generator=gen)
+    pick = torch.randint(0, 2 * vals.numel(), (R, C), generator=gen)
+    xs = torch.where(pick < vals.numel(), vals[pick.clamp(max=vals.numel() - 1)], xs)
+    xs[8] = torch.randn(C, generator=gen)             # a row with none of them
+    ys = torch.randn(R, C, generator=gen) * torch.logspace(-30, 30, R).reshape(R, 1)
+    nodes2 = parse_dag("%0 = input 0\n%1 = input 1\n%2 = abs %1\n%3 = row_max %2\n%4 = div %0 %3\n")
+    _, out2 = run_group(nodes2, [xs.to(DEV), ys.to(DEV)], (R, C), "f32")
+    ref2 = oracle.eval_group(nodes2, [xs.numpy(), ys.numpy()], (R, C))
+    assert_bits(to_np(out2), ref2, f"special dividends / row value, {C} columns")
 
 
 def test_persistent_row_layout_is_bit_identical(monkeypatch):
