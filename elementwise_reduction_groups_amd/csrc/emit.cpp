@@ -1423,16 +1423,34 @@ struct Emitter {
         o << "      __shared__ float " << arr << "[" << NR << "];\n";
         o << "      if (lane < " << NR * K << ") {\n";
         o << "        const float v = psk_take(psk_s + lane, psk_tag, psk_limit, psk_xstate + 2);\n";
-        for (int r = 0; r < NR; ++r) {
-            const bool mx = an.nodes[reds[r]].op == PSK_OP_ROW_MAX;
-            o << "        float a" << r << " = PSK_RL(v, " << r * K << ");\n";
-            for (int m = 1; m < K; ++m) {
-                const std::string b = "PSK_RL(v, " + std::to_string(r * K + m) + ")";
-                if (mx) o << "        a" << r << " = psk_rmax(a" << r << ", " << b << ");\n";
-                else o << "        a" << r << " = a" << r << " + " << b << ";\n";
+        // maxima and plain sums first; then an online sum, whose members'
+        // parts are each rescaled from their member's maximum to the row's
+        // (combined just before) and added in member order
+        for (int pass = 0; pass < 2; ++pass)
+            for (int r = 0; r < NR; ++r) {
+                const int i = reds[r], om = an.online_max[i];
+                if ((om >= 0) != (pass == 1)) continue;
+                const bool mx = an.nodes[i].op == PSK_OP_ROW_MAX;
+                auto lane_of = [&](int rr, int m) { return "PSK_RL(v, " + std::to_string(rr * K + m) + ")"; };
+                if (om >= 0) {
+                    const int rm = (int)(std::find(reds.begin(), reds.end(), om) - reds.begin());
+                    const std::string M = "a" + std::to_string(rm);
+                    for (int m = 0; m < K; ++m) {
+                        const std::string mm = lane_of(rm, m), sm = lane_of(r, m);
+                        const std::string t = "((" + mm + " == " + M + ") ? " + sm + " : " + sm + " * " +
+                                              online_exp(i) + "(" + mm + " - " + M + "))";
+                        if (m == 0) o << "        float a" << r << " = " << t << ";\n";
+                        else o << "        a" << r << " = a" << r << " + " << t << ";\n";
+                    }
+                } else {
+                    o << "        float a" << r << " = " << lane_of(r, 0) << ";\n";
+                    for (int m = 1; m < K; ++m) {
+                        if (mx) o << "        a" << r << " = psk_rmax(a" << r << ", " << lane_of(r, m) << ");\n";
+                        else o << "        a" << r << " = a" << r << " + " << lane_of(r, m) << ";\n";
+                    }
+                }
+                o << "        if (lane == 0) " << arr << "[" << r << "] = a" << r << ";\n";
             }
-            o << "        if (lane == 0) " << arr << "[" << r << "] = a" << r << ";\n";
-        }
         o << "      }\n";
         o << "      __syncthreads();\n";
         for (int r = 0; r < NR; ++r) o << "      p" << reds[r] << " = " << arr << "[" << r << "];\n";

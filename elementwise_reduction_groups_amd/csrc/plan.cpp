@@ -172,10 +172,11 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector, int split_ept)
         // partial row values.  Measured on a [8192, 131072] f32 softmax:
         // K = 4 at 64 elements a lane 1.51 ms, K = 8 at 32 elements 1.57 ms,
         // against 1.95 ms for one workgroup a row (the tiled kernel, which
-        // re-reads what its registers and LDS cannot hold).  Not for the
-        // online normalizer (its partials are pairs rescaled on combining);
-        // at most 32 workgroups a row (the first wave takes every member's
-        // partial of every reduction of a phase: at most 64).
+        // re-reads what its registers and LDS cannot hold).  The online
+        // normalizer's partials are (maximum, sum relative to it) pairs,
+        // rescaled when the members combine.  At most 32 workgroups a row
+        // (the first wave takes every member's partial of every reduction of
+        // a phase: at most 64).
         int streamed_inputs = 0, streamed_bytes = 0;
         for (const InputInfo& in : an.inputs)
             if (in.used && (in.kind == InKind::General || in.kind == InKind::Full)) {
@@ -183,7 +184,7 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector, int split_ept)
                 streamed_bytes = std::max(streamed_bytes, (int)esz(in.dtype));
             }
         const bool wide = (int64_t)p.nv * p.vec > layout_value("epmax", 32);
-        if (wide && !online && split_ept != 0 && !layout_value("tiled", 0) && layout_value("split", 1)) {
+        if (wide && split_ept != 0 && !layout_value("tiled", 0) && layout_value("split", 1)) {
             const int Ls = 512;
             const bool lean = streamed_inputs <= 1 && streamed_bytes <= 4 && an.mask_period == 0 && an.where_mask < 0;
             const int ept = split_ept > 0 ? split_ept : layout_value("sept", lean ? 64 : 32);

@@ -398,9 +398,10 @@ def test_mask_refusals(lib):
 
 def test_wide_rows_take_split_or_tiled_kernels(lib, tmp_path, monkeypatch):
     """Rows too wide for one workgroup's registers: split over workgroups
-    (kind 4) by default, at the widest segment that compiles without
-    spilling registers; the tiled kernel (kind 3) when forced, for the online
-    normalizer, and for rows a split would need more than 32 workgroups for."""
+    (kind 4) by default, the online normalizer included, at the widest
+    segment that compiles without spilling registers; the tiled kernel
+    (kind 3) when forced and for rows a split would need more than 32
+    workgroups for."""
     from synth import configs as C
     # up to 32 elements per lane at 1024 lanes the row stays in registers
     g = P.psk_group_create(P.GroupDesc(C.softmax_causal_dag(0.125, 32768), [((4, 32768), "f32")], (4, 32768), "f32"))
@@ -450,7 +451,7 @@ def test_wide_rows_take_split_or_tiled_kernels(lib, tmp_path, monkeypatch):
             if forced:
                 monkeypatch.setenv("PSK_LAYOUT", "tiled=1")
             g = P.psk_group_create(d)
-            assert P.psk_group_get_info(g).kind == (3 if forced or name.startswith("online") else 4), name
+            assert P.psk_group_get_info(g).kind == (3 if forced else 4), name
             P.psk_group_destroy(g)
             _, notes = _isa(P.psk_group_code_object(d), tmp_path, f"wide_{name}{forced}")
             assert re.search(r"\.private_segment_fixed_size:\s+0\b", notes), name
@@ -540,13 +541,19 @@ def test_online_normalizer_flag(lib, monkeypatch):
     src = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((8, 64), "f32")], (8, 64), "f32", flags=O))
     body = src[src.index('extern "C"'):]
     assert "float tm = " in body and "psk_exp_np(q" in body
+    monkeypatch.setenv("PSK_LAYOUT", "tiled=1")      # the tiled kernel, online and exact
     wide = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((4, 70000), "f32")], (4, 70000), "f32",
                                           flags=O))
-    monkeypatch.setenv("PSK_LAYOUT", "tiled=1")      # the exact sum through the tiled kernel, for comparison
     plain = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((4, 70000), "f32")], (4, 70000), "f32"))
     monkeypatch.delenv("PSK_LAYOUT")
     # tiled: two walks of the row (register, LDS and memory tile loops each) instead of three
     assert wide.count("for (int t = ") * 3 == plain.count("for (int t = ") * 2
+    # split rows: one exchange of (maximum, sum) pairs instead of two exchanges
+    split = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((4, 70000), "f32")], (4, 70000), "f32",
+                                           flags=O))
+    exact = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((4, 70000), "f32")], (4, 70000), "f32"))
+    assert split.count("psk_take(") == 1 + 1 and exact.count("psk_take(") == 2 + 1   # + the prelude's definition
+    assert "psk_exp_np(PSK_RL(v, 0) - a0)" in split or "psk_exp_np(PSK_RL(v, 0) - a1)" in split
     # masked and causal softmax take it too
     P.psk_group_source(P.GroupDesc(C.softmax_masked_dag(0.125), [((8, 64), "f32"), ((8, 64), "u8")], (8, 64), "f32",
                                    flags=O))

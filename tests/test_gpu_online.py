@@ -71,6 +71,29 @@ def test_online_masked_softmax_with_emptied_rows(R, C):
     assert np.all(got[~m.cpu().numpy()].view(np.uint32) == 0)
 
 
+@pytest.mark.parametrize("layout,C,kind", [("split=0", 131072, 3), ("sept=32", 131072, 4), ("sept=16", 70000, 4),
+                                           ("", 300000, 4)])
+def test_online_wide_rows_split_and_tiled(layout, C, kind, monkeypatch):
+    """The online normalizer over rows shared by several workgroups (each
+    member's (maximum, sum) rescaled to the row's maximum when combined)
+    and over the tiled kernel, against the exact oracle; rows whose maximum
+    sits in different members, a rising row, and a masked row."""
+    monkeypatch.setenv("PSK_LAYOUT", layout)
+    R = 6
+    x = configs.softmax_scores(R, C, device=DEV, seed=C + len(layout))
+    x[1] = torch.linspace(-30.0, 30.0, C, device=DEV)          # maximum in the last member
+    x[2] = torch.linspace(30.0, -30.0, C, device=DEV)          # in the first
+    x[3, C // 2] = 40.0                                         # one spike in a middle member
+    dag = configs.softmax_dag(0.125)
+    g = P.Group(dag, [((R, C), "f32")], (R, C), "f32", online=True)
+    assert g.info.kind == kind
+    out = torch.full_like(x, float("nan"))
+    g.run([x], out)
+    torch.cuda.synchronize()
+    assert_f32_close(to_np(out), oracle.eval_group(dag, [to_np(x)], (R, C), F32), f"online wide {layout} {C}")
+    g.check()                                                    # no bounded wait ran out
+
+
 @pytest.mark.parametrize("C", [1024, 131072])
 def test_online_softmax_rising_rows(C):
     """Rows that rise from start to end: the running maximum grows in every
@@ -91,7 +114,7 @@ def test_online_wide_full_size_sampled_rows():
     x = configs.softmax_scores(R, C, device=DEV)
     dag = configs.softmax_dag(0.125)
     g = P.Group(dag, [((R, C), "f32")], (R, C), "f32", online=True)
-    assert g.info.kind == 3
+    assert g.info.kind == 4 and g.info.split == 4      # split rows: (maximum, sum) pairs exchanged
     out = torch.empty_like(x)
     g.run([x], out)
     torch.cuda.synchronize()
