@@ -42,9 +42,10 @@
  *   - The library allocates no device memory for data in *_run / *_step
  *     (tree tables and the clipping pass's partials are allocated by
  *     psk_tree_create).  The first run of a group on a device loads its
- *     code object there (hipModuleLoadData); later runs only launch, so a
- *     group run or an AdamW step may be captured in a HIP graph once it has
- *     run once on that device.
+ *     code object there (hipModuleLoadData), and a group with split rows
+ *     (see psk_group_check) allocates its exchange buffer there; later runs
+ *     only launch, so a group run or an AdamW step may be captured in a HIP
+ *     graph once it has run once on that device.
  *   - All functions are thread-safe.
  */
 #ifndef PSK_FUSED_H
