@@ -13,7 +13,10 @@ of elements compared equals the output's size:
   * add + RMSNorm + gamma + GELU, bf16 [16384, 4096]: all 67M outputs within
     one bf16 ulp;
   * the 64-node chain, f32 [16384, 16384]: all 268M outputs within
-    1e-7 + 2e-6 |ref|.
+    1e-7 + 2e-6 |ref|;
+  * and the other timed workloads at their sizes: the wide softmax
+    [8192, 131072] f32 (split rows), LayerNorm with its statistics, the
+    byte-mask softmax and the bf16 causal softmax.
 """
 import math
 import sys
@@ -115,3 +118,63 @@ def test_wide_softmax_every_element():
     say(f"wide softmax: oracle on {THREADS} host threads")
     ref = OP.eval_group(configs.softmax_dag(0.125), [to_np(x)], (R, C), 0, THREADS)
     assert compare_all(to_np(out), ref, "f32", "wide softmax") == R * C
+
+
+def test_layernorm_stats_every_element():
+    """LayerNorm storing mean and rstd, bf16 [16384, 4096] (persistent rows):
+    all 67M outputs within one bf16 ulp or the derived bound near a
+    cancellation (y * gamma + beta), every row's statistics within the
+    bound of its own summation tree."""
+    from tests.test_gpu_multi import assert_layernorm_close, check_stats, layernorm_group
+    R, C = 16384, 4096
+    x, gm, bt = configs.layernorm_inputs(R, C, device=DEV)
+    g = layernorm_group(R, C)
+    out = torch.full_like(x, float("nan"))
+    mean = torch.full((R, 1), float("nan"), device=DEV)
+    rstd = torch.full((R, 1), float("nan"), device=DEV)
+    say("LayerNorm + statistics [16384, 4096] bf16 on the GPU")
+    g.run([x, gm, bt], out, extra_outs=[mean, rstd])
+    torch.cuda.synchronize()
+    say(f"LayerNorm: oracle on {THREADS} host threads")
+    ref = OP.eval_group(configs.layernorm_dag(EPS), [to_np(x), to_np(gm), to_np(bt)], (R, C), 1, THREADS,
+                        root=configs.LAYERNORM_ROOT)
+    got = to_np(out)
+    assert got.size == ref.size == R * C
+    assert_layernorm_close(got, ref, x, gm, bt, C, "LayerNorm full size")
+    check_stats(g.info, x, mean, rstd, C, "LayerNorm full size")
+
+
+def test_byte_mask_softmax_every_element():
+    """Softmax with a [1024, 1024] causal byte mask broadcast over 8 x 16
+    heads, f32: all 134M outputs within 1e-7 + 2e-6 |ref| (refused
+    positions +0)."""
+    shape = (8, 16, 1024, 1024)
+    x = configs.softmax_scores(8 * 16 * 1024, 1024, device=DEV).view(shape)
+    m = configs.causal_mask_bytes(1024, device=DEV)
+    dag = configs.softmax_masked_dag(0.125)
+    g = P.Group(dag, [(shape, "f32"), ((1024, 1024), "u8")], shape, "f32")
+    out = torch.full_like(x, float("nan"))
+    say("byte-mask softmax [8, 16, 1024, 1024] f32 on the GPU")
+    g.run([x, m], out)
+    torch.cuda.synchronize()
+    say(f"byte-mask softmax: oracle on {THREADS} host threads")
+    ref = OP.eval_group(dag, [to_np(x), m.cpu().numpy().view(np.uint8)], shape, 0, THREADS)
+    assert compare_all(to_np(out), ref, "f32", "byte-mask softmax") == math.prod(shape)
+    refused = ~m.cpu().numpy()
+    assert np.all(to_np(out).reshape(-1, 1024, 1024)[:, refused].view(np.uint32) == 0)
+
+
+def test_causal_softmax_bf16_every_element():
+    """Causal softmax with bf16 scores and probabilities [131072, 1024]: all
+    134M outputs within one bf16 ulp."""
+    R, C = 131072, 1024
+    x = configs.softmax_scores(R, C, device=DEV).to(torch.bfloat16)
+    dag = configs.softmax_causal_dag(0.125, 1024)
+    g = P.Group(dag, [((R, C), "bf16")], (R, C), "bf16")
+    out = torch.empty_like(x)
+    say("causal softmax [131072, 1024] bf16 on the GPU")
+    g.run([x], out)
+    torch.cuda.synchronize()
+    say(f"bf16 causal softmax: oracle on {THREADS} host threads")
+    ref = OP.eval_group(dag, [to_np(x)], (R, C), 1, THREADS)
+    assert compare_all(to_np(out), ref, "bf16", "bf16 causal softmax") == R * C
