@@ -594,10 +594,59 @@ PROFILE_RUNS = {
 }
 
 
+# The SQ counters behind the LayerNorm diagnosis (one pass of 8 SQ counters,
+# the two row groups only), summarized into profiles/SQ_SUMMARY.
+SQ_RUN = ("p_sq", "sq", "--pmc SQ_WAIT_ANY SQ_WAVE_CYCLES SQ_INST_LEVEL_VMEM SQ_INSTS_VMEM SQ_ACTIVE_INST_ANY "
+          "SQ_INSTS_VALU SQ_WAVES SQ_BUSY_CYCLES", "--only layernorm_stats_bf16,rmsnorm_gelu_bf16 --steps 1 --warmup 0")
+SQ_SUMMARY = "sq_counters_layernorm_rmsnorm_16384x4096_bf16.txt"
+
+
 def profile_command(key, base="gpurun_out"):
-    sub, pre, prof, extra = PROFILE_RUNS[key]
+    sub, pre, prof, extra = SQ_RUN if key == "sq" else PROFILE_RUNS[key]
     return (f"rocprofv3 {prof} --output-format csv -d {base}/{sub} -o {pre} -- python3 bench.py --profile-step "
             f"--profile-all {extra}")
+
+
+def summarize_sq(base, P, configs):
+    """profiles/SQ_SUMMARY from the SQ counter run: per-dispatch means for the
+    LayerNorm and RMSNorm+GELU kernels, with the ratios the diagnosis uses."""
+    import csv
+    import collections
+    path = os.path.join(base, SQ_RUN[0], SQ_RUN[1] + "_counter_collection.csv")
+    if not os.path.exists(path):
+        return None
+    ws = {w.name: w for w in build_workloads(P, configs)}
+    names = {ws[n].group().info.kernel.decode(): n for n in ("layernorm_stats_bf16", "rmsnorm_gelu_bf16")}
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        for kn, n in names.items():
+            if kn in r["Kernel_Name"]:
+                agg[n][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = ["# SQ counters: LayerNorm + mean + rstd (persistent rows) and add + RMSNorm + gamma + GELU (one row a "
+             "workgroup), both [16384,4096] bf16, on one MI355X (gfx950)",
+             "# commands (from the repository root, TMPDIR=/tmp):",
+             f"#   {profile_command('sq')}",
+             f"#   python3 bench.py --summarize-profiles {base}",
+             "# per-dispatch means; SQ_WAVE_CYCLES, SQ_WAIT_ANY and SQ_ACTIVE_INST_ANY are wave-cycles (quad-cycle "
+             "units) summed over waves"]
+    for n in ("layernorm_stats_bf16", "rmsnorm_gelu_bf16"):
+        if n not in agg:
+            continue
+        m = {c: statistics.fmean(v) for c, v in agg[n].items()}
+        lines.append(f"[{n}]   dispatches {len(next(iter(agg[n].values())))}")
+        for c in sorted(m):
+            lines.append(f"{c} = {m[c]:.0f}")
+        wc = m.get("SQ_WAVE_CYCLES", 0.0)
+        if wc:
+            lines.append(f"wait_fraction = {m['SQ_WAIT_ANY'] / wc:.3f}          # SQ_WAIT_ANY / SQ_WAVE_CYCLES")
+            lines.append(f"issue_fraction = {m['SQ_ACTIVE_INST_ANY'] / wc:.3f}         # SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES")
+        if m.get("SQ_BUSY_CYCLES"):
+            lines.append(f"vmem_in_flight_per_busy_cycle = {m['SQ_INST_LEVEL_VMEM'] / m['SQ_BUSY_CYCLES']:.2f}")
+        if m.get("SQ_WAVES"):
+            lines.append(f"valu_per_wave = {m['SQ_INSTS_VALU'] / m['SQ_WAVES']:.0f}")
+    with open(os.path.join(ROOT, "profiles", SQ_SUMMARY), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return SQ_SUMMARY
 
 
 def kernel_source_sha(paths):
@@ -734,6 +783,9 @@ def summarize_profiles(base):
         written.append((k, avg_ns, (fetch_b + write_b) / w.bytes))
     for k, avg, ratio in written:
         print(f"{k}: average {avg / 1e3:.1f} us, traffic / algorithmic {ratio:.4f}")
+    sq = summarize_sq(base, P, configs)
+    if sq:
+        print(f"{sq}: written")
     return written
 
 
