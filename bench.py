@@ -889,7 +889,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 arithmetic; bf16/f32 storage",
+        "dtype": "f32",
+        "storage": "bf16 theta/g, f32 m/v (AdamW); f32 scores and probabilities (softmax)",
         "data": "synthetic (seeded), resident in HBM",
         "config": {
             "workload": "AdamW step over a Llama-style tree (16 layers, D=2048, FFN 5632, vocab 32000: 145 leaves, "
