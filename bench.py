@@ -303,7 +303,7 @@ def build_workloads(P, configs, layers=16):
     W.append(Workload("softmax_wide_8192x131072_f32", "psk_rows_softmax_wide_8192x131072_f32", 4 * RW * CW,
                       4 * RW * CW, s_wide(False), group=g_wide(False),
                       note="rows too wide for one workgroup's registers and LDS; bytes counted once"))
-    W.append(Workload("softmax_wide_8192x131072_f32_online", "psk_rowt_softmax_wide_online_8192x131072_f32",
+    W.append(Workload("softmax_wide_8192x131072_f32_online", "psk_rows_softmax_wide_online_8192x131072_f32",
                       4 * RW * CW, 4 * RW * CW, s_wide(True), group=g_wide(True),
                       note="PSK_GROUP_ONLINE: the sum taken in the maximum's pass; its rounding differs from the "
                            "exact sum (declared differs, within the f32 tolerance)"))
@@ -322,19 +322,19 @@ def build_workloads(P, configs, layers=16):
                       note="VALU-bound: 64 node evaluations per element"))
 
     def g_valu():
-        return P.Group(C.valu_ceiling_dag(), [((N4, 1), "f32"), ((1, N4), "f32")], (N4, N4), "f32")
+        return P.Group(C.valu_ceiling_dag(), [((N4, 1), "f32"), ((1, N4), "f32")], (N4, N4), "bf16")
 
     def s_valu(ctx):
         B = ctx.configs.chain_inputs(N4, 1, device=ctx.dev)[1]       # [N, 1]
         Cc = ctx.configs.chain_inputs(1, N4, device=ctx.dev)[2]      # [1, N]
-        Z = ctx.torch.empty((N4, N4), dtype=ctx.torch.float32, device=ctx.dev)
+        Z = ctx.torch.empty((N4, N4), dtype=ctx.torch.bfloat16, device=ctx.dev)
         grp = g_valu()
         return lambda: grp.run([B, Cc], Z, stream=ctx.stream)
-    W.append(Workload("valu_ceiling_f32", "psk_pw_valu_ceiling_16384x16384_f32", 8 * N4, 4 * N4 * N4, s_valu,
+    W.append(Workload("valu_ceiling_f32", "psk_pw_valu_ceiling_16384x16384_bf16", 8 * N4, 2 * N4 * N4, s_valu,
                       group=g_valu, hbm=False, node_evals=64 * N4 * N4,
-                      note="64 add/mul members in 8 independent chains over broadcast [R,1] and [1,N] inputs: "
-                           "one vector instruction per member and 4 bytes of output per 64: the VALU rate an "
-                           "emitted kernel sustains"))
+                      note="64 f32 add/mul members in 8 independent chains over broadcast [R,1] and [1,N] inputs: "
+                           "one vector instruction per member and 2 bytes of output (bf16) per 64: the VALU rate "
+                           "an emitted kernel sustains (with an f32 output its 1 GiB of writes held it 16% lower)"))
 
     # -- streaming references
     def s_copy_torch(ctx):
@@ -927,8 +927,8 @@ def main():
                 if (only and w.name not in only) or not w.profile:
                     continue
                 fn = w.setup(ctx)
-                fn()
-                fn()
+                for _ in range(6):      # the first call touches freshly allocated memory; 6 keep it to a sixth
+                    fn()
                 torch.cuda.synchronize()
                 del fn
                 torch.cuda.empty_cache()

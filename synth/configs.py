@@ -359,8 +359,8 @@ def softmax_dag(scale: float = 0.125) -> List[Node]:
 # A measurement workload: the VALU rate an emitted pointwise kernel sustains.
 def valu_ceiling_dag(chains: int = 8, depth: int = 7) -> List[Node]:
     """64 members of add and mul only: x = B + C over a [R, 1] and a [1, N]
-    input (so the output's 4 bytes are the only HBM traffic an element
-    costs), then `chains` independent chains of `depth` alternating
+    input (so the output's bytes are the only HBM traffic an element costs),
+    then `chains` independent chains of `depth` alternating
     multiplications and additions by constants starting from x (values stay
     within a few units: each chain contracts towards a fixed point), summed
     pairwise at the end.  Every member is one f32 operation, so it is one
