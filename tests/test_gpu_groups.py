@@ -306,8 +306,9 @@ def test_division_by_a_row_value_is_ieee_bit_exact(C):
 
 def test_persistent_row_layout_is_bit_identical(monkeypatch):
     """The persistent row kernel (a layout switch: a few workgroups per CU
-    walk the rows and prefetch the next one) gives the one-row-per-workgroup
-    kernel's bits: same reduction order, LDS halves alternating by row."""
+    walk the rows and load the next 1 to 4 ahead, the loop unrolled over
+    its buffers) gives the one-row-per-workgroup kernel's bits: same
+    reduction order, LDS halves alternating by row."""
     R, C = 3000, 4096
     x, r, g = configs.rmsnorm_inputs(R, C, device=DEV, seed=5)
     xl, gl, bl = configs.layernorm_inputs(R, C, device=DEV, seed=6)
@@ -325,7 +326,7 @@ def test_persistent_row_layout_is_bit_identical(monkeypatch):
     ]
     for nodes, ins, shape, dt, kw, tensors, xs in cases:
         outs = []
-        for layout in ("persist=0", "persist=4", "persist=2", ""):
+        for layout in ("persist=0", "persist=4", "persist=2", "persist=4,pf=2", "persist=3,pf=4", ""):
             monkeypatch.setenv("PSK_LAYOUT", layout)
             grp = P.Group(nodes, ins, shape, dt, **kw)
             out = torch.full(shape, float("nan"), dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device=DEV)
