@@ -221,11 +221,13 @@ typedef struct psk_group_desc {
  * online-softmax generator).  A row sum of exp(y - m) where m is the row
  * maximum of the same y is taken in the maximum's pass: each lane keeps a
  * running maximum and a sum of exponentials relative to it, rescaled by
- * exp(old - new) when the maximum grows, and lanes and waves combine their
- * pairs the same way.  One pass over the row fewer, so wide rows are read
- * once less; the sum's rounding differs from the exact two-pass sum (a few
- * f32 ulps: declared differs, tested within the f32 tolerance).  Refused
- * (PSK_E_UNSUPPORTED) unless the group holds such a sum, and for trees. */
+ * exp(old - new) when the maximum grows, and lanes, waves and the
+ * workgroups sharing a split row combine their pairs the same way.  One pass
+ * over the row fewer (a row walked from memory by the tiled kernel is read
+ * once less; split rows exchange once instead of twice); the sum's rounding
+ * differs from the exact two-pass sum (a few f32 ulps: declared differs,
+ * tested within the f32 tolerance).  Refused (PSK_E_UNSUPPORTED) unless the
+ * group holds such a sum, and for trees. */
 #define PSK_GROUP_ONLINE 2u
 
 typedef struct psk_group psk_group;
