@@ -293,8 +293,10 @@ typedef struct psk_group_info {
     int32_t rows_per_block;  /* row kernel */
     int64_t algorithmic_bytes; /* inputs read once at their own size + outputs written once */
     char kernel[48];         /* the emitted kernel's name (as profilers show it), NUL-terminated */
-    int32_t tiles;           /* tiled row kernel (kind 3, rows too wide for registers): tiles per
-                                row; each reduction phase re-reads the row.  0 otherwise */
+    int32_t tiles;           /* tiled row kernel (kind 3: rows too wide for registers that split
+                                rows cannot take, i.e. more than 32 workgroups a row or more
+                                than 64 partials a phase): tiles per row; each reduction phase
+                                re-reads the row.  0 otherwise */
     int32_t split;           /* split rows (kind 4): workgroups that share one row, each holding
                                 a segment in registers and exchanging partial row values with
                                 the others.  0 otherwise */
