@@ -353,7 +353,10 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
             return fail(PSK_E_OP, at(i) + "pow n with n > 2 never joins a group");
 
     // ---- online normalizer: ROW_SUM(EXP(SUB(y, ROW_MAX(y)))), y an element
-    // value read through exactly these nodes' operands
+    // value read through exactly these nodes' operands.  Not where the
+    // maximum, the difference or the exponential is read rounded (stored as
+    // bf16): the maximum's pass would sum exponentials that the group's
+    // readers never see.
     an.online_max.assign(n, -1);
     an.online_sum.assign(n, -1);
     if (desc->flags & PSK_GROUP_ONLINE) {
@@ -368,6 +371,7 @@ psk_status analyse(const psk_group_desc* desc, Analysis& an)
             if (d.op != PSK_OP_SUB) continue;
             const psk_node& m = an.nodes[d.b];
             if (m.op != PSK_OP_ROW_MAX || m.a != d.a || an.online_sum[d.b] >= 0) continue;
+            if (an.rounded(d.b) || an.rounded(e.a) || an.rounded(s.a)) continue;
             an.online_max[i] = d.b;
             an.online_sum[d.b] = i;
         }

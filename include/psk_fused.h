@@ -227,7 +227,9 @@ typedef struct psk_group_desc {
  * once less; split rows exchange once instead of twice); the sum's rounding
  * differs from the exact two-pass sum (a few f32 ulps: declared differs,
  * tested within the f32 tolerance).  Refused (PSK_E_UNSUPPORTED) unless the
- * group holds such a sum, and for trees. */
+ * group holds such a sum whose maximum, difference and exponential are not
+ * stored as bf16 (their readers would see rounded values the maximum's pass
+ * never sums), and for trees. */
 #define PSK_GROUP_ONLINE 2u
 
 typedef struct psk_group psk_group;

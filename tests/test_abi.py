@@ -568,6 +568,13 @@ def test_online_normalizer_flag(lib, monkeypatch):
                    "%6 = div %4 %5\n", F + F, (8, 16), flags=O), P.PSK_E_UNSUPPORTED)
     _refused(P.GroupDesc(C.tree_sgd_dag(), [((1,), "f32"), ((1,), "f32"), ((), "f32")], (1,), "f32",
                          flags=P.PSK_GROUP_TREE | O), P.PSK_E_UNSUPPORTED)
+    # the maximum, the difference or the exponential stored as bf16 (read
+    # rounded): the maximum's pass cannot sum what the readers see; stored
+    # as f32 they pair as before
+    sm = "%0 = input 0\n%1 = row_max %0\n%2 = sub %0 %1\n%3 = exp %2\n%4 = row_sum %3\n%5 = div %3 %4\n"
+    for node, shape in [(1, (8, 1)), (2, (8, 16)), (3, (8, 16))]:
+        _refused(_desc(sm, F, (8, 16), extras=[(node, shape, "bf16")], flags=O), P.PSK_E_UNSUPPORTED)
+        P.psk_group_source(_desc(sm, F, (8, 16), extras=[(node, shape, "f32")], flags=O))
 
 
 def test_persistent_rows_where_column_vectors_weigh(lib):
