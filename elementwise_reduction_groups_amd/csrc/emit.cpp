@@ -413,6 +413,12 @@ struct Emitter {
         big = an.numel >= (int64_t(1) << 31) - 4096 || an.max_span >= (int64_t(1) << 31) - 4096;
         for (auto& nd : an.nodes)
             if (nd.op == PSK_OP_CAUSAL_MASK) period = nd.iparam;
+        // online sums whose exponentials the maximum's pass keeps: on rows
+        // held in registers that pass sees every element of the lane at once
+        kept_sum.assign(n, -1);
+        if ((pl.kind == 1 || pl.kind == 4) && !pl.persist)
+            for (int i = 0; i < n; ++i)
+                if (an.online_max[i] >= 0) kept_sum[an.nodes[i].a] = i;
         if (pl.kind == 1)
             ragged = (int64_t)pl.nv * pl.lanes * pl.vec != an.cols;
         if (pl.kind == 3)
@@ -461,6 +467,7 @@ struct Emitter {
     }
 
     bool use_refused = false;
+    std::vector<int> kept_sum;    // exp node -> the online sum whose pass keeps its values, or -1
     bool divr_ok = true;          // row-value divisors use psk_divr
     bool cached_loads = false;    // loads whose data a later phase reads again
     std::string ld_fn() const { return cached_loads ? "psk_ldc" : "psk_ld"; }
@@ -553,6 +560,12 @@ struct Emitter {
     std::string expr(int i, int e) const
     {
         const psk_node& nd = an.nodes[i];
+        if (!use_refused && kept_sum[i] >= 0) {
+            // exp(y - row maximum) as the maximum's pass left it: exp(y - m)
+            // for the lane's maximum m, times exp(m - row maximum)
+            const std::string s = std::to_string(kept_sum[i]);
+            return "(oe" + s + "_" + std::to_string(e) + " * osc" + s + ")";
+        }
         auto A = [&] { return val(nd.a, e); };
         auto B = [&] { return val(nd.b, e); };
         auto C = [&] { return val(nd.c, e); };
@@ -1294,30 +1307,43 @@ struct Emitter {
     // the sum p<sm> of exp(y - running maximum), rescaled by
     // exp(old - new) when the maximum grows.  While the maximum is still
     // -inf every y so far is -inf, and the exponentials are taken against 0
-    // (giving exp(-inf) = 0 rather than exp(NaN)).
+    // (giving exp(-inf) = 0 rather than exp(NaN)).  Where the pass is the
+    // lane's only one (kept_sum), the exponentials stay in registers as
+    // oe<sm>_<e> for the exp member, which rescales them once the row's
+    // maximum is known instead of taking each again.
     void online_accumulate(int mx, int sm, const char* indent)
     {
         const int y = an.nodes[mx].a;
         const std::string P = "p" + std::to_string(mx), S = "p" + std::to_string(sm);
         const std::string ex = online_exp(sm);
-        o << indent << "{\n" << indent << "  float tm = (-__builtin_inff());\n";
+        const bool keep = kept_sum[an.nodes[sm].a] == sm;
+        const std::string in = keep ? std::string(indent) : std::string(indent) + "  ";
+        const std::string tm = "tm" + std::to_string(sm), mref = "mref" + std::to_string(sm);
+        if (!keep) o << indent << "{\n";
+        o << in << "float " << tm << " = (-__builtin_inff());\n";
         for (int e = 0; e < NE; ++e) {
-            std::string acc = std::string("tm = ") + (pl.kind == 3 ? "psk_rmax_s" : "psk_rmax") + "(tm, " +
-                              val(y, e) + ");";
-            if (ragged) o << indent << "  if (" << col(e) << " < " << an.cols << ") " << acc << "\n";
-            else o << indent << "  " << acc << "\n";
+            std::string acc = tm + " = " + (pl.kind == 3 ? "psk_rmax_s" : "psk_rmax") + "(" + tm + ", " + val(y, e) +
+                              ");";
+            if (ragged) o << in << "if (" << col(e) << " < " << an.cols << ") " << acc << "\n";
+            else o << in << acc << "\n";
         }
         // the running maximum becomes the maximum with this group's; the sum
         // is rescaled when it changes (a NaN maximum makes the sum NaN)
-        o << indent << "  { const float pn = psk_rmax(" << P << ", tm); if (!(pn == " << P << ")) " << S << " = " << S
-          << " * " << ex << "(" << P << " - pn); " << P << " = pn; }\n";
-        o << indent << "  const float mref = " << P << " == (-__builtin_inff()) ? 0.0f : " << P << ";\n";
+        o << in << "{ const float pn = psk_rmax(" << P << ", " << tm << "); if (!(pn == " << P << ")) " << S << " = "
+          << S << " * " << ex << "(" << P << " - pn); " << P << " = pn; }\n";
+        o << in << "const float " << mref << " = " << P << " == (-__builtin_inff()) ? 0.0f : " << P << ";\n";
         for (int e = 0; e < NE; ++e) {
-            std::string acc = S + " = (" + S + " + " + ex + "(" + val(y, e) + " - mref));";
-            if (ragged) o << indent << "  if (" << col(e) << " < " << an.cols << ") " << acc << "\n";
-            else o << indent << "  " << acc << "\n";
+            std::string term = ex + "(" + val(y, e) + " - " + mref + ")";
+            if (keep) {
+                const std::string oe = "oe" + std::to_string(sm) + "_" + std::to_string(e);
+                o << in << "const float " << oe << " = " << term << ";\n";
+                term = oe;
+            }
+            std::string acc = S + " = (" + S + " + " + term + ");";
+            if (ragged) o << in << "if (" << col(e) << " < " << an.cols << ") " << acc << "\n";
+            else o << in << acc << "\n";
         }
-        o << indent << "}\n";
+        if (!keep) o << indent << "}\n";
     }
 
     // lanes of a wave (DPP), then waves (LDS), then the row values
@@ -1397,6 +1423,20 @@ struct Emitter {
             else
                 o << "    const float r" << i << " = " << rt(i, "p" + std::to_string(i)) << ";\n";
             row_reciprocal(i);
+        }
+        // kept exponentials: the factor exp(q - M) from the lane's maximum q
+        // to the row's M (neither is rounded: such pairs are not formed).
+        // exp(y - q) * 1 is exp(y - M) itself where q = M; a lane of -inf
+        // holds zeros, which stay zero (NaN when M is -inf or NaN, as
+        // exp(y - M) is then)
+        for (int i : reds) {
+            const int m = an.online_max[i];
+            if (m < 0 || kept_sum[an.nodes[i].a] != i) continue;
+            const std::string q = "q" + std::to_string(m), M = "r" + std::to_string(m);
+            const std::string ninf = "(-__builtin_inff())", nan = "__builtin_nanf(\"\")";
+            o << "    const float osc" << i << " = (" << q << " == " << M << ") ? ((" << q << " == " << ninf << ") ? "
+              << nan << " : 1.0f) : (" << q << " == " << ninf << ") ? ((" << M << " == " << M << ") ? 0.0f : " << nan
+              << ") : " << online_exp(i) << "(" << q << " - " << M << ");\n";
         }
     }
 

@@ -540,7 +540,10 @@ def test_online_normalizer_flag(lib, monkeypatch):
     # a softmax: its sum moves into the maximum's pass (one reduction phase)
     src = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((8, 64), "f32")], (8, 64), "f32", flags=O))
     body = src[src.index('extern "C"'):]
-    assert "float tm = " in body and "psk_exp_np(q" in body
+    assert "float tm6 = " in body and "psk_exp_np(q" in body
+    # a row held in registers: one exponential an element, kept from the
+    # maximum's pass and rescaled to the row's maximum by the exp member
+    assert body.count("psk_exp_np(v2_") == 4 and "(oe6_0 * osc6)" in body
     monkeypatch.setenv("PSK_LAYOUT", "tiled=1")      # the tiled kernel, online and exact
     wide = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((4, 70000), "f32")], (4, 70000), "f32",
                                           flags=O))
@@ -548,12 +551,14 @@ def test_online_normalizer_flag(lib, monkeypatch):
     monkeypatch.delenv("PSK_LAYOUT")
     # tiled: two walks of the row (register, LDS and memory tile loops each) instead of three
     assert wide.count("for (int t = ") * 3 == plain.count("for (int t = ") * 2
+    assert " * osc" not in wide              # tiles walked again: nothing kept
     # split rows: one exchange of (maximum, sum) pairs instead of two exchanges
     split = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((4, 70000), "f32")], (4, 70000), "f32",
                                            flags=O))
     exact = P.psk_group_source(P.GroupDesc(C.softmax_dag(0.125), [((4, 70000), "f32")], (4, 70000), "f32"))
     assert split.count("psk_take(") == 1 + 1 and exact.count("psk_take(") == 2 + 1   # + the prelude's definition
     assert "psk_exp_np(PSK_RL(v, 0) - a0)" in split or "psk_exp_np(PSK_RL(v, 0) - a1)" in split
+    assert " * osc" in split
     # masked and causal softmax take it too
     P.psk_group_source(P.GroupDesc(C.softmax_masked_dag(0.125), [((8, 64), "f32"), ((8, 64), "u8")], (8, 64), "f32",
                                    flags=O))
