@@ -949,21 +949,20 @@ struct Emitter {
         for (int k = 0; k < pl.nv; ++k) {
             for (int i : elems)
                 for (int j = 0; j < pl.vec; ++j) o << "    float v" << i << "_" << k * pl.vec + j << ";\n";
+            // a member stored as bf16 is rounded as soon as it is computed:
+            // the members after it in the branch read the rounded value
+            std::vector<int> es;
+            for (int j = 0; j < pl.vec; ++j) es.push_back(k * pl.vec + j);
             o << "    if (" << allowed_vec(k) << ") {\n";
             for (int i : elems) {
                 divr_open(i);
-                std::vector<int> es;
-                for (int j = 0; j < pl.vec; ++j) {
-                    int e = k * pl.vec + j;
-                    o << "      v" << i << "_" << e << " = " << expr(i, e) << ";\n";
-                    es.push_back(e);
-                }
+                for (int e : es) o << "      v" << i << "_" << e << " = " << expr(i, e) << ";\n";
                 divr_close(i, es, "      ");
+                round_elems(i, es, "      ");
             }
             o << "    } else {\n";
-            for (int i : elems)
-                for (int j = 0; j < pl.vec; ++j) {
-                    int e = k * pl.vec + j;
+            for (int i : elems) {
+                for (int e : es) {
                     o << "      v" << i << "_" << e << " = ";
                     if (an.uniform[i]) o << "u" << i;
                     else if (an.irrelevant[i]) o << "0.0f";
@@ -971,17 +970,9 @@ struct Emitter {
                     else o << expr(i, e);
                     o << ";\n";
                 }
-            o << "    }\n";
-            for (int i : elems) {
-                std::vector<int> es;
-                for (int j = 0; j < pl.vec; ++j) es.push_back(k * pl.vec + j);
-                if (!an.uniform[i]) round_elems(i, es, "    ");   // u is rounded already
-                else if (an.rounded(i)) {
-                    o << "    if (" << allowed_vec(k) << ") {\n";
-                    round_elems(i, es, "      ");
-                    o << "    }\n";
-                }
+                if (!an.uniform[i] && !an.irrelevant[i]) round_elems(i, es, "      ");   // u is rounded already
             }
+            o << "    }\n";
         }
     }
 
@@ -1420,6 +1411,11 @@ struct Emitter {
             if (an.nodes[i].op == PSK_OP_ROW_MEAN)
                 o << "    const float r" << i << " = " << rt(i, "p" + std::to_string(i) + " / " + flit((float)an.cols))
                   << ";\n";
+            else if (an.online_max[i] >= 0)
+                // an online sum over a row of -inf is NaN, as the exact sum
+                // of exp(-inf - (-inf)) is; its lanes summed zeros
+                o << "    const float r" << i << " = (r" << an.online_max[i]
+                  << " == (-__builtin_inff())) ? __builtin_nanf(\"\") : p" << i << ";\n";
             else
                 o << "    const float r" << i << " = " << rt(i, "p" + std::to_string(i)) << ";\n";
             row_reciprocal(i);

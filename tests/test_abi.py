@@ -685,3 +685,16 @@ def test_strided_inputs_compile(lib, tmp_path):
             assert "long long" in src[src.index('extern "C"'):]
         asm, _ = _isa(P.psk_group_code_object(d), tmp_path, name)
         assert "scratch_" not in asm
+
+
+def test_stored_bf16_member_rounded_before_its_readers_in_skipping_branches(lib):
+    """Where a kernel skips refused vectors, the allowed ones are computed in
+    a branch of their own; a member stored as bf16 is rounded right after
+    it is computed there, before the members that read it."""
+    from synth import configs as C
+    dag = C.softmax_causal_dag(0.125, 256)        # %2 scaled scores, %3 the causal mask reading them
+    src = P.psk_group_source(P.GroupDesc(dag, [((64, 1000), "f32")], (64, 1000), "f32",
+                                         extras=[(2, (64, 1000), "bf16")]))
+    body = src[src.index('extern "C"'):]
+    branch = body[body.index("    if ("):]
+    assert branch.index("v2_0 = psk_rt(v2_0);") < branch.index("v3_0 = ")

@@ -3,13 +3,16 @@ taken in its maximum's pass, rescaled as the running maximum grows) against
 the oracle's exact two-pass softmax.  The sum's rounding differs from the
 exact one (declared differs), so the bar is the f32 tolerance (one bf16
 ulp for bf16 results), and refused positions must still be +0 bits."""
+import random
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from synth import configs
-from tests.gpu_util import assert_bf16_close, assert_f32_close, to_np
+from tests.gpu_util import assert_bf16_close, assert_bits, assert_f32_close, to_np
+from tests.random_groups import random_online_group
 
 P = pytest.importorskip("elementwise_reduction_groups_amd")
 
@@ -122,3 +125,79 @@ def test_online_wide_full_size_sampled_rows():
     ri = torch.from_numpy(rows).to(DEV)
     assert_f32_close(to_np(out[ri]), oracle.eval_group(dag, [to_np(x[ri])], (len(rows), C), F32),
                      "online wide full size")
+
+
+def _check_stored_sum(got, nodes, node, ins, shape, extras, info, what):
+    """A stored row sum of n terms is compared with the float64 sum of the
+    oracle's own exponentials, not with the oracle's sequential f32 sum
+    (whose rounding alone reaches about n ulps: 40 000 terms already part
+    the two orders by more than 2e-6).  Bound: the kernel's own order adds
+    at most `per_lane` terms in sequence on a lane, each with at most one
+    rescaling product, then at most 64 more steps across lanes, waves and
+    workgroups, one rounding of 2^-24 each; the terms themselves are within
+    2e-6 of the oracle's."""
+    e = nodes[node].args[0]
+    # the group's own stored values too: a value stored as bf16 is read rounded
+    refx = [(m, np.zeros(xsh, np.float32 if xdt == "f32" else np.uint16)) for m, xsh, xdt in extras if m != e]
+    ex = np.zeros(shape, np.float32)
+    oracle.eval_group(nodes, ins, shape, F32, root=len(nodes) - 1, extras=refx + [(e, ex)])
+    s64 = ex.astype(np.float64).sum(axis=-1, keepdims=True)
+    per_lane = -(-shape[-1] // (max(1, info.lanes_per_row) * max(1, info.split)))
+    rel = 2e-6 + (2 * per_lane + 64) * 2.0 ** -24
+    g = got.astype(np.float64)
+    fin = np.isfinite(s64)
+    ok = np.isnan(g) == np.isnan(s64)
+    ok[fin] &= np.abs(g[fin] - s64[fin]) <= 1e-7 + rel * np.abs(s64[fin])
+    if not ok.all():
+        i = tuple(np.argwhere(~ok)[0])
+        raise AssertionError(f"{what}: {int((~ok).sum())} of {ok.size} row sums outside {rel:.2e} of the f64 sum; "
+                             f"first at {i}: gpu {g[i]!r} f64 sum {s64[i]!r}")
+
+
+def _make(shape, dt, gen):
+    if dt == "u8":
+        return (torch.randint(0, 3, shape, generator=gen).to(torch.uint8) * 3).to(DEV)     # 0, 3, 6
+    x = torch.rand(shape, generator=gen) * 4.0 - 2.0
+    return x.to(torch.bfloat16 if dt == "bf16" else torch.float32).to(DEV)
+
+
+@pytest.mark.parametrize("layout,chunk", [("", 0), ("", 1), ("lanes=16", 2), ("lanes=32", 3), ("sept=16", 4),
+                                          ("tiled=1", 5)])
+def test_random_online_groups(layout, chunk, monkeypatch):
+    """Seeded random groups holding the normalizer's pattern
+    (tests/random_groups.py: element chains before the maximum, causal and
+    byte masks, broadcast inputs, f32 and bf16 storage, rows of 3 to
+    300 000 columns, stored maxima, differences, exponentials and sums),
+    under the default launch layouts and forced ones, against the oracle's
+    exact evaluation: within the f32 tolerance (one bf16 ulp for bf16
+    values), the chain's members (exact operations) bit for bit.  Rows a
+    byte mask empties (short rows) hold a NaN sum, as the exact sum is."""
+    if layout:
+        monkeypatch.setenv("PSK_LAYOUT", layout)
+    rng = random.Random(4000 + chunk)
+    gen = torch.Generator().manual_seed(4100 + chunk)
+    for trial in range(8):
+        nodes, inputs, shape, dt, extras = random_online_group(rng)
+        tensors = [_make(s, t, gen) for s, t in inputs]
+        g = P.Group(nodes, inputs, shape, dt, root=len(nodes) - 1, extras=extras, online=True)
+        out = torch.full(shape, float("nan"), dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device=DEV)
+        xs = [torch.full(xsh, float("nan"), dtype=torch.bfloat16 if xdt == "bf16" else torch.float32, device=DEV)
+              for _, xsh, xdt in extras]
+        g.run(tensors, out, extra_outs=xs or None)
+        torch.cuda.synchronize()
+        ins = [t.cpu().numpy().view(np.uint8) if t.dtype == torch.uint8 else to_np(t) for t in tensors]
+        refx = [(m, np.zeros(xsh, np.float32 if xdt == "f32" else np.uint16)) for m, xsh, xdt in extras]
+        ref = oracle.eval_group(nodes, ins, shape, F32 if dt == "f32" else BF16, root=len(nodes) - 1, extras=refx)
+        what = (f"{layout or 'default'} chunk {chunk} trial {trial}: kind {g.info.kind} shape {shape} {dt} "
+                f"inputs {inputs} extras {extras} ops {[n.op for n in nodes]}")
+        first_max = next(i for i, n in enumerate(nodes) if n.op == "row_max")
+        for name, node, got, r in [("root", len(nodes) - 1, to_np(out), ref)] + [
+                (f"extra {m}", m, to_np(x), r) for (m, r), x in zip(refx, xs)]:
+            if node < first_max and nodes[node].op not in ("causal_mask", "where"):
+                assert_bits(got, r, f"{what}: {name}")        # finite exact operations
+            elif nodes[node].op == "row_sum":
+                _check_stored_sum(got, nodes, node, ins, shape, extras, g.info, f"{what}: {name}")
+            elif got.dtype == np.uint16:
+                assert_bf16_close(got, r, f"{what}: {name}")
+            else:
+                assert_f32_close(got, r, f"{what}: {name}")

@@ -123,22 +123,33 @@ def test_random_exact_row_groups_bit_for_bit(chunk):
     maximum's operand holds a NaN (0/0 of equal values, say) are compared
     too: a row maximum over a NaN is NaN on both sides, whatever order the
     lanes combine in."""
+    _row_groups(random.Random(3000 + chunk), torch.Generator().manual_seed(55 + chunk), chunk, masks=False)
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_random_masked_row_groups_bit_for_bit(chunk):
+    """The same with one causal or byte mask over the first input: the row
+    kernels skip refused vectors (neither loaded nor computed; members
+    uniform there take their one refused value), and a member stored as
+    bf16 is read rounded by the members after it in either branch."""
+    _row_groups(random.Random(3500 + chunk), torch.Generator().manual_seed(65 + chunk), chunk, masks=True)
+
+
+def _row_groups(rng, gen, chunk, masks):
     from tests.random_groups import random_row_group
-    rng = random.Random(3000 + chunk)
-    gen = torch.Generator().manual_seed(55 + chunk)
     for trial in range(10):
-        nodes, inputs, shape, dt, extras = random_row_group(rng)
+        nodes, inputs, shape, dt, extras = random_row_group(rng, masks=masks)
         tensors = []
         for s, t in inputs:
             x = make_input(s, t, gen, False)
-            tensors.append(torch.where(x == 0, torch.ones_like(x), x))        # no exact zeros
+            tensors.append(x if t == "u8" else torch.where(x == 0, torch.ones_like(x), x))   # no exact zeros
         g = P.Group(nodes, inputs, shape, dt, root=len(nodes) - 1, extras=extras)
         out = torch.full(shape, float("nan"), dtype=TD[dt], device=DEV)
         xs = [torch.full(xsh, float("nan"), dtype=TD[xdt], device=DEV) for _, xsh, xdt in extras]
         g.run(tensors, out, extra_outs=xs or None)
         torch.cuda.synchronize()
         refx = [(m, np.zeros(xsh, np.float32 if xdt == "f32" else np.uint16)) for m, xsh, xdt in extras]
-        ins = [to_np(t) for t in tensors]
+        ins = [t.cpu().numpy().view(np.uint8) if t.dtype == torch.uint8 else to_np(t) for t in tensors]
         ref = oracle.eval_group(nodes, ins, shape, OD[dt], root=len(nodes) - 1, extras=refx)
         what = (f"chunk {chunk} trial {trial}: kind {g.info.kind} shape {shape} {dt} inputs {inputs} "
                 f"extras {extras} ops {[n.op for n in nodes]}")

@@ -137,3 +137,33 @@ def test_groups_differing_only_in_where_fill():
         torch.cuda.synchronize()
         ref = oracle.eval_group(nodes, ins, (64, 96))
         assert_bits(to_np(out), ref, f"where fill {fill}")
+
+
+@pytest.mark.parametrize("mask", ["causal", "bytes"])
+@pytest.mark.parametrize("online", [False, True])
+def test_scaled_scores_stored_bf16_are_read_rounded(mask, online):
+    """The scaled scores stored as a bf16 extra output: every member after
+    them (the mask, the maximum, the exponentials) reads the rounded value,
+    also where the kernel skips refused vectors and computes the allowed
+    ones in a branch of their own.  f32 probabilities against the oracle,
+    which evaluates the group with the same stored value."""
+    R, C = 300, 1000
+    x = configs.softmax_scores(R, C, device=DEV, seed=31)
+    if mask == "causal":
+        dag = configs.softmax_causal_dag(0.125, 256)
+        ins, specs = [x], [((R, C), "f32")]
+    else:
+        dag = configs.softmax_masked_dag(0.125)
+        m = configs.random_mask(R, C, 0.4, device=DEV, seed=32)
+        ins, specs = [x, m], [((R, C), "f32"), ((R, C), "u8")]
+    scaled = [i for i, n in enumerate(dag) if n.op == "mul"][0]
+    g = P.Group(dag, specs, (R, C), "f32", extras=[(scaled, (R, C), "bf16")], online=online)
+    out = torch.full_like(x, float("nan"))
+    xs = torch.full((R, C), float("nan"), dtype=torch.bfloat16, device=DEV)
+    g.run(ins, out, extra_outs=[xs])
+    torch.cuda.synchronize()
+    ins_np = [to_np(x)] + ([mask_np(m)] if mask == "bytes" else [])
+    refx = [(scaled, np.zeros((R, C), np.uint16))]
+    ref = oracle.eval_group(dag, ins_np, (R, C), F32, extras=refx)
+    assert_bits(to_np(xs), refx[0][1], f"{mask} online={online}: stored scaled scores")
+    assert_f32_close(to_np(out), ref, f"{mask} online={online}: probabilities")
