@@ -127,31 +127,73 @@ def test_online_wide_full_size_sampled_rows():
                      "online wide full size")
 
 
-def _check_stored_sum(got, nodes, node, ins, shape, extras, info, what):
-    """A stored row sum of n terms is compared with the float64 sum of the
-    oracle's own exponentials, not with the oracle's sequential f32 sum
-    (whose rounding alone reaches about n ulps: 40 000 terms already part
-    the two orders by more than 2e-6).  Bound: the kernel's own order adds
-    at most `per_lane` terms in sequence on a lane, each with at most one
-    rescaling product, then at most 64 more steps across lanes, waves and
-    workgroups, one rounding of 2^-24 each; the terms themselves are within
-    2e-6 of the oracle's."""
-    e = nodes[node].args[0]
-    # the group's own stored values too: a value stored as bf16 is read rounded
-    refx = [(m, np.zeros(xsh, np.float32 if xdt == "f32" else np.uint16)) for m, xsh, xdt in extras if m != e]
-    ex = np.zeros(shape, np.float32)
-    oracle.eval_group(nodes, ins, shape, F32, root=len(nodes) - 1, extras=refx + [(e, ex)])
-    s64 = ex.astype(np.float64).sum(axis=-1, keepdims=True)
-    per_lane = -(-shape[-1] // (max(1, info.lanes_per_row) * max(1, info.split)))
-    rel = 2e-6 + (2 * per_lane + 64) * 2.0 ** -24
-    g = got.astype(np.float64)
-    fin = np.isfinite(s64)
-    ok = np.isnan(g) == np.isnan(s64)
-    ok[fin] &= np.abs(g[fin] - s64[fin]) <= 1e-7 + rel * np.abs(s64[fin])
-    if not ok.all():
-        i = tuple(np.argwhere(~ok)[0])
-        raise AssertionError(f"{what}: {int((~ok).sum())} of {ok.size} row sums outside {rel:.2e} of the f64 sum; "
-                             f"first at {i}: gpu {g[i]!r} f64 sum {s64[i]!r}")
+def _widen(a):
+    return (a.astype(np.uint32) << 16).view(np.float32) if a.dtype == np.uint16 else a
+
+
+class _Normalized:
+    """The group's softmax evaluated with an exact normalizer: the oracle's
+    own exponentials e (f32, as the oracle computes them, the group's stored
+    values included, since a value stored as bf16 is read rounded), their
+    float64 row sum s64, and the members after the sum (e / s, a product
+    with an input, a WHERE) applied in float64.  The oracle's sequential f32
+    sum of n terms is itself within about n ulps only, so a kernel that adds
+    in another order is compared with the exact sum instead, within its own
+    order's bound: at most `per_lane` terms in sequence on a lane, each with
+    at most one rescaling product, then at most 64 more steps across lanes,
+    waves and workgroups, one rounding of 2^-24 each; the terms themselves
+    are within 2e-6 of the oracle's, and each later member rounds once."""
+
+    def __init__(self, nodes, ins, shape, extras, info):
+        self.s_node = next(i for i, n in enumerate(nodes) if n.op == "row_sum")
+        e = nodes[self.s_node].args[0]
+        refx = [(m, np.zeros(xsh, np.float32 if xdt == "f32" else np.uint16)) for m, xsh, xdt in extras if m != e]
+        ex = np.zeros(shape, np.float32)
+        oracle.eval_group(nodes, ins, shape, F32, root=len(nodes) - 1, extras=refx + [(e, ex)])
+        self.s64 = ex.astype(np.float64).sum(axis=-1, keepdims=True)
+        v = {}
+        for i in range(self.s_node + 1, len(nodes)):
+            nd = nodes[i]
+            if nd.op == "div":
+                v[i] = ex.astype(np.float64) / self.s64
+            elif nd.op == "mul":
+                v[i] = v[nd.args[0]] * _widen(ins[nodes[nd.args[1]].iparam]).astype(np.float64)
+            elif nd.op == "where":
+                v[i] = np.where(ins[nodes[nd.args[0]].iparam] != 0, v[nd.args[1]], nd.imm)
+            else:
+                raise AssertionError(f"no float64 form for {nd.op}")
+        self.root64 = v[len(nodes) - 1]
+        per_lane = -(-shape[-1] // (max(1, info.lanes_per_row) * max(1, info.split)))
+        self.sum_rel = 2e-6 + (2 * per_lane + 64) * 2.0 ** -24
+        self.root_rel = self.sum_rel + 4e-6 + 3 * 2.0 ** -24
+
+    @staticmethod
+    def _close(got, ref, rel, what):
+        g = _widen(got).astype(np.float64)
+        ref = np.broadcast_to(ref, g.shape)
+        fin = np.isfinite(ref)
+        ok = np.isnan(g) == np.isnan(ref)
+        ok[fin] &= np.abs(g[fin] - ref[fin]) <= 1e-7 + rel * np.abs(ref[fin])
+        if not ok.all():
+            i = tuple(np.argwhere(~ok)[0])
+            raise AssertionError(f"{what}: {int((~ok).sum())} of {ok.size} outside 1e-7 + {rel:.2e}|exact|; "
+                                 f"first at {i}: gpu {g[i]!r} exact {ref[i]!r}")
+
+    def check_oracle(self, ref, cols, what):
+        """The oracle's own root (sequential f32 sum) lies within its
+        summation bound of the exact reference: a check of the float64 tail."""
+        if ref.dtype == np.float32:
+            self._close(ref, self.root64, 4e-6 + (2 * cols + 8) * 2.0 ** -24, what)
+
+    def check_sum(self, got, what):
+        self._close(got, self.s64, self.sum_rel, what)
+
+    def check_root(self, got, what):
+        if got.dtype == np.uint16:       # bf16: within one ulp of the exact value rounded once
+            ref = torch.from_numpy(self.root64.astype(np.float32)).to(torch.bfloat16)
+            assert_bf16_close(got, to_np(ref), what)
+        else:
+            self._close(got, self.root64, self.root_rel, what)
 
 
 def _make(shape, dt, gen):
@@ -168,10 +210,12 @@ def test_random_online_groups(layout, chunk, monkeypatch):
     (tests/random_groups.py: element chains before the maximum, causal and
     byte masks, broadcast inputs, f32 and bf16 storage, rows of 3 to
     300 000 columns, stored maxima, differences, exponentials and sums),
-    under the default launch layouts and forced ones, against the oracle's
-    exact evaluation: within the f32 tolerance (one bf16 ulp for bf16
-    values), the chain's members (exact operations) bit for bit.  Rows a
-    byte mask empties (short rows) hold a NaN sum, as the exact sum is."""
+    under the default launch layouts and forced ones, against the oracle:
+    the chain's members (exact operations) bit for bit, the stored maxima,
+    differences and exponentials within the f32 tolerance (one bf16 ulp for
+    bf16 values), the stored sums and the root against the oracle's
+    exponentials normalized exactly (_Normalized).  Rows a byte mask
+    empties (short rows) hold a NaN sum, as the exact sum is."""
     if layout:
         monkeypatch.setenv("PSK_LAYOUT", layout)
     rng = random.Random(4000 + chunk)
@@ -191,13 +235,16 @@ def test_random_online_groups(layout, chunk, monkeypatch):
         what = (f"{layout or 'default'} chunk {chunk} trial {trial}: kind {g.info.kind} shape {shape} {dt} "
                 f"inputs {inputs} extras {extras} ops {[n.op for n in nodes]}")
         first_max = next(i for i, n in enumerate(nodes) if n.op == "row_max")
-        for name, node, got, r in [("root", len(nodes) - 1, to_np(out), ref)] + [
-                (f"extra {m}", m, to_np(x), r) for (m, r), x in zip(refx, xs)]:
-            if node < first_max and nodes[node].op not in ("causal_mask", "where"):
-                assert_bits(got, r, f"{what}: {name}")        # finite exact operations
-            elif nodes[node].op == "row_sum":
-                _check_stored_sum(got, nodes, node, ins, shape, extras, g.info, f"{what}: {name}")
+        exact = _Normalized(nodes, ins, shape, extras, g.info)
+        exact.check_oracle(ref, shape[-1], f"{what}: the oracle's root")
+        exact.check_root(to_np(out), f"{what}: root")
+        for (m, r), x in zip(refx, xs):
+            name, got = f"{what}: extra {m}", to_np(x)
+            if m < first_max and nodes[m].op not in ("causal_mask", "where"):
+                assert_bits(got, r, name)          # finite exact operations
+            elif m == exact.s_node:
+                exact.check_sum(got, name)
             elif got.dtype == np.uint16:
-                assert_bf16_close(got, r, f"{what}: {name}")
+                assert_bf16_close(got, r, name)
             else:
-                assert_f32_close(got, r, f"{what}: {name}")
+                assert_f32_close(got, r, name)
