@@ -87,10 +87,11 @@ class Workload:
     read once at its own size, each output written once."""
 
     def __init__(self, name, profile, read, write, setup, group=None, kernel=None, note=None, hbm=True,
-                 node_evals=0):
+                 node_evals=0, size_copy=None):
         self.name, self.profile, self.read, self.write = name, profile, read, write
         self.setup, self.group, self.kernel, self.note, self.hbm = setup, group, kernel, note, hbm
         self.node_evals = node_evals
+        self.size_copy = size_copy      # an emitted copy moving about the same bytes, timed alongside
 
     @property
     def bytes(self):
@@ -262,7 +263,8 @@ def build_workloads(P, configs, layers=16):
         return lambda: grp.run([x, g, b], y, stream=ctx.stream, extra_outs=[m, r])
     W.append(Workload("layernorm_stats_bf16", "psk_row_layernorm_stats_16384x4096_bf16", 2 * R3 * C3 + 4 * C3,
                       2 * R3 * C3 + 8 * R3, s_ln, group=g_ln,
-                      note="mean, x - mean read twice, variance, normalise; mean and rstd stored per row"))
+                      note="mean, x - mean read twice, variance, normalise; mean and rstd stored per row",
+                      size_copy="copy_emitted_16384x4096_bf16"))
 
     def g_masked():
         return P.Group(C.softmax_masked_dag(0.125), [((8, 16, 1024, 1024), "f32"), ((1024, 1024), "u8")],
@@ -355,6 +357,22 @@ def build_workloads(P, configs, layers=16):
         return lambda: grp.run([src], dst, stream=ctx.stream)
     W.append(Workload("copy_emitted", "psk_pw_copy_1GiB_f32", 1 << 30, 1 << 30, s_copy, group=g_copy,
                       note="emitted pointwise y = -(-x): the r1:w1 streaming rate of an emitted kernel"))
+
+    # the same copy at LayerNorm's size (256 MiB moved): a launch this short
+    # streams below the 1 GiB rate (ramp-up and drain weigh more)
+    def g_copy_ln():
+        from synth.dag import parse_dag
+        return P.Group(parse_dag("%0 = input 0\n%1 = neg %0\n%2 = neg %1\n"), [((R3, C3), "bf16")], (R3, C3),
+                       "bf16")
+
+    def s_copy_ln(ctx):
+        src = ctx.torch.empty((R3, C3), dtype=ctx.torch.bfloat16, device=ctx.dev)
+        dst = ctx.torch.empty_like(src)
+        grp = g_copy_ln()
+        return lambda: grp.run([src], dst, stream=ctx.stream)
+    W.append(Workload("copy_emitted_16384x4096_bf16", "psk_pw_copy_16384x4096_bf16", 2 * R3 * C3, 2 * R3 * C3,
+                      s_copy_ln, group=g_copy_ln,
+                      note="emitted y = -(-x) over LayerNorm's [16384,4096] bf16 rows: the r1:w1 rate at its size"))
     return W
 
 
@@ -457,6 +475,8 @@ def combine_processes(runs, workloads):
     for w in workloads:
         if ref and w.name in out and w.hbm and not w.name.startswith("copy_"):
             out[w.name]["frac_of_emitted_copy"] = round(out[w.name]["GBps"] / ref, 3)
+        if w.size_copy and w.name in out and w.size_copy in out:
+            out[w.name]["frac_of_same_size_copy"] = round(out[w.name]["GBps"] / out[w.size_copy]["GBps"], 3)
     # the 64-node chain against the measured VALU rate of add/mul members
     if "chain64_f32" in out and "valu_ceiling_f32" in out:
         out["chain64_f32"]["frac_of_valu_ceiling_node_evals"] = round(

@@ -38,7 +38,7 @@ def test_pointwise_chain_layouts(monkeypatch):
         g.run([A, B, C], out)
         torch.cuda.synchronize()
         return [to_np(out)]
-    run_layouts(make, ["", "block=64", "block=1024", "xcd=0", "nt=0", "block=128,xcd=0,nt=0"], monkeypatch)
+    run_layouts(make, ["", "block=64", "block=1024", "xcd=0", "xcd=1", "nt=0", "block=128,xcd=0,nt=0"], monkeypatch)
     for t, b in zip((A, B, C), before):
         assert_bits(to_np(t), b, "inputs unchanged")
 
