@@ -63,12 +63,16 @@ namespace {
 // Launch shape, chosen by measurement on MI355X over the 145-leaf tree
 // (bf16 theta and g, f32 m and v; medians of 12 runs): workgroups of 128
 // threads, 2 elements per thread (4-byte bf16 and 8-byte f32 accesses, one
-// per stream), nontemporal loads and stores (every byte is touched once),
-// and each XCD given one contiguous eighth of the chunks: 6.14 TB/s,
+// per stream), nontemporal loads and stores (every byte is touched once):
+// 6.14 TB/s with each XCD given one contiguous eighth of the chunks,
 // against 5.99 with 4 elements per thread, 6.03 with 2 elements and
 // 64-thread workgroups, 6.09 with 512-thread workgroups.  Storing theta'
 // first, loading the moments first or reading the leaf pointers from the
-// chunk table change nothing measurable.
+// chunk table change nothing measurable.  Workgroups taken in the
+// dispatcher's round-robin order instead (consecutive blocks on
+// consecutive XCDs, every XCD in the same stretch of the tree) run at 6.62
+// TB/s against 6.10 for the contiguous eighths in the same process (2.951
+// against 3.204 ms), so that is the default.
 constexpr int kBlock = 128;
 constexpr int kPer = 2;                                   // elements per thread
 constexpr int kSub = PSK_TREE_CHUNK / (kBlock * kPer);   // workgroups per chunk
@@ -160,9 +164,10 @@ template <> struct Io<__bf16> {
 };
 
 // Workgroups are dispatched to the XCDs round robin (block b runs on XCD
-// b mod 8).  The grid is padded to 8 * per blocks and block b takes virtual
-// block (b mod 8) * per + b / 8, so XCD x works through the contiguous range
-// [x * per, (x + 1) * per); virtual blocks past the end exit.
+// b mod 8).  The grid is padded to 8 * per blocks; with per_xcd given,
+// block b takes virtual block (b mod 8) * per + b / 8, so XCD x works
+// through the contiguous range [x * per, (x + 1) * per); with per_xcd 0
+// block b is virtual block b.  Virtual blocks past the end exit.
 __device__ __forceinline__ unsigned xcd_block(unsigned b, unsigned per) { return (b % kXcds) * per + b / kXcds; }
 
 // a / b for a divisor b in [2^-40, 2^40] shared by every element, given y,
@@ -186,7 +191,7 @@ __global__ void __launch_bounds__(kBlock)
 adamw_tree_kernel(const LeafDev* __restrict__ leaves, const ChunkDev* __restrict__ chunks, unsigned n_virtual,
                   unsigned per_xcd, AdamwScalars s, const float* __restrict__ gscale)
 {
-    const unsigned vb = xcd_block(blockIdx.x, per_xcd);
+    const unsigned vb = per_xcd ? xcd_block(blockIdx.x, per_xcd) : blockIdx.x;
     if (vb >= n_virtual) return;
     const ChunkDev ch = chunks[vb / kSub];
     const LeafDev L = leaves[ch.leaf];     // the seven slots and the flags, read together
@@ -274,12 +279,13 @@ hipError_t launch(const LeafDev* l, const ChunkDev* c, int64_t n_chunks, const A
     const int64_t n_virtual = n_chunks * kSub;
     const int64_t per = (n_virtual + kXcds - 1) / kXcds;
     if (per * kXcds > 0x7fffffffLL) return hipErrorInvalidValue;
+    const unsigned pv = layout_value("axcd", 0) ? (unsigned)per : 0u;
     if (gscale)
         hipLaunchKernelGGL((adamw_tree_kernel<TP, TG, TM, true>), dim3((unsigned)(per * kXcds)), dim3(kBlock), 0, st,
-                           l, c, (unsigned)n_virtual, (unsigned)per, s, gscale);
+                           l, c, (unsigned)n_virtual, pv, s, gscale);
     else
         hipLaunchKernelGGL((adamw_tree_kernel<TP, TG, TM, false>), dim3((unsigned)(per * kXcds)), dim3(kBlock), 0,
-                           st, l, c, (unsigned)n_virtual, (unsigned)per, s, gscale);
+                           st, l, c, (unsigned)n_virtual, pv, s, gscale);
     return hipGetLastError();
 }
 

@@ -1130,7 +1130,8 @@ struct Emitter {
         for (size_t k = 0; k <= an.inputs.size() + an.extras.size(); ++k) o << ", int slot" << k;
         for (size_t k = 0; k < an.inputs.size(); ++k) o << ", const void* s" << k;
         o << ")\n{\n";
-        o << "  const unsigned vb = (blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;\n";
+        if (pl.xcd) o << "  const unsigned vb = (blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;\n";
+        else o << "  const unsigned vb = blockIdx.x;\n";
         o << "  if (vb >= n_virtual) return;\n";
         o << "  const psk_chunk_dev ch = chunks[vb / " << TS << "u];\n";
         o << "  const psk_leaf_dev* L = leaves + ch.leaf;\n";

@@ -25,6 +25,7 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //     library's), xcd=0|1 (XCD-contiguous block mapping), block=64..1024
 //     (threads per workgroup);
 //   tree kernels: tper=2|4|8|16 (elements per thread);
+//   the AdamW kernel: axcd=0|1 (XCD-contiguous block mapping);
 //   row kernels: epl (elements of output a lane aims for), lanes=16|32|
 //     64..1024, epmax (most elements a lane holds before the tiled kernel
 //     takes over, default 32), persist=k (k persistent workgroups a CU),
@@ -39,7 +40,7 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // A layout never changes which elements are computed; lanes, epl, epmax,
 // tiled, tn and alt change a reduction's bracketing (within tolerance), fexp
 // an exponential's last bits (within tolerance), the others change no bit.
-static int layout_value(const char* key, int dflt)
+int layout_value(const char* key, int dflt)
 {
     const char* env = std::getenv("PSK_LAYOUT");
     if (!env) return dflt;
@@ -79,12 +80,15 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector, int split_ept)
     p.bnt = layout_value("bnt", 0) != 0;
     p.fexp = layout_value("fexp", 1) != 0;
     if (an.tree) {
-        // Workgroups of 128 threads; each thread takes `vec` consecutive
-        // elements, the fewest of 2, 4, 8, 16 that move at least 40 bytes.
-        // Measured on the 887M-element Llama tree: an SGD step (6 bytes per
-        // element) runs at 4.6 / 6.4 / 5.3 TB/s with 4 / 8 / 16, AdamW (22
-        // bytes) at 6.14 / 5.99 TB/s with 2 / 4.  A chunk splits into whole
-        // workgroups; XCD-contiguous mapping.
+        // Each thread takes `vec` consecutive elements, the fewest of 2, 4,
+        // 8, 16 that move at least 40 bytes.  Measured on the 887M-element
+        // Llama tree: an SGD step (6 bytes per element) runs at 4.6 / 6.4 /
+        // 5.3 TB/s with 4 / 8 / 16, AdamW (22 bytes) at 6.14 / 5.99 TB/s with
+        // 2 / 4.  A chunk splits into whole workgroups, which reach the XCDs
+        // in the dispatcher's round-robin order: with 64-thread workgroups
+        // SGD runs at 6.58 TB/s and AdamW at 6.45, against 6.24 / 6.46 with
+        // 128 threads, 6.37 / 6.26 with 256, and 6.47 / 6.09 (128 threads)
+        // when each XCD takes a contiguous eighth of the chunks.
         p.kind = 2;
         auto size_of = [](psk_dtype d) { return d == PSK_BF16 ? 2 : 4; };
         int bytes = size_of(an.out_dtype);
@@ -95,12 +99,12 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector, int split_ept)
         while (per < 16 && per * bytes < 40) per *= 2;
         per = layout_value("tper", per);
         if (per != 2 && per != 4 && per != 8 && per != 16) per = 4;
-        int block = layout_value("block", 128);
-        if (block < 64 || block > 256 || (block & (block - 1))) block = 128;
+        int block = layout_value("block", 64);
+        if (block < 64 || block > 256 || (block & (block - 1))) block = 64;
         p.vec = per;
         p.block = block;
         p.blocks = PSK_TREE_CHUNK / (block * per);   // workgroups per chunk
-        p.xcd = true;
+        p.xcd = layout_value("xcd", 0) != 0;
         return p;
     }
     // Pointwise workgroups either reach the XCDs round robin (the

@@ -129,6 +129,8 @@ struct KernelPlan {
 // split_ept: elements a lane holds in a split-rows kernel (-1: the default
 // rule, 0: no split rows, > 0: that many)
 KernelPlan plan_kernel(const Analysis& an, bool allow_vector, int split_ept = -1);
+// a key of PSK_LAYOUT ("key=value,..."), else dflt: launch shapes for measurement
+int layout_value(const char* key, int dflt);
 // Bytes of scratch (register spills) a compiled code object's kernel uses,
 // from its metadata; -1 when the metadata does not say.
 int64_t code_scratch_bytes(const std::vector<char>& code);

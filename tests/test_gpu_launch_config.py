@@ -57,7 +57,8 @@ def test_tree_group_layouts(monkeypatch):
         g.run_tree(tree, [0, 1, -1], 2, [None, None, lr])
         torch.cuda.synchronize()
         return [to_np(o) for o in outs]
-    run_layouts(make, ["", "tper=4", "tper=8", "tper=16", "block=64", "block=256", "xcd=0", "nt=0"], monkeypatch)
+    run_layouts(make, ["", "tper=4", "tper=8", "tper=16", "block=128", "block=256", "xcd=1", "xcd=1,block=128",
+                       "nt=0"], monkeypatch)
     for t, b in zip(theta + grad, before):
         assert_bits(to_np(t), b, "inputs unchanged")
 
@@ -78,3 +79,23 @@ def test_row_group_rows_per_workgroup(monkeypatch):
     run_layouts(make, ["", "block=64", "block=512", "block=1024", "xcd=1", "nt=0"], monkeypatch)
     for t, b in zip((x, r, gm), before):
         assert_bits(to_np(t), b, "inputs unchanged")
+
+
+def test_adamw_kernel_block_orders(monkeypatch):
+    """The hand-written AdamW kernel with workgroups in round-robin order
+    (the default) and with each XCD taking a contiguous eighth of the
+    chunks: the same bits, every leaf of a ragged tree."""
+    sizes = [(1,), (7,), (4095,), (4097,), (20000,), (70000,)]
+    init = [configs.tree_leaf_values(sizes, dt, DEV, seed=71 + k)
+            for k, dt in enumerate([torch.bfloat16, torch.bfloat16, torch.float32, torch.float32])]
+    results = []
+    for lay in ["", "axcd=1"]:
+        monkeypatch.setenv("PSK_LAYOUT", lay)
+        th, g, m, v = [[t.clone() for t in ts] for ts in init]
+        v = [t.abs() for t in v]
+        tree = P.Tree([list(x) for x in zip(th, g, m, v)])
+        tree.adamw_step(3e-4, 0.9, 0.999, 1e-8, 0.01, 10)
+        torch.cuda.synchronize()
+        results.append([to_np(t) for t in th + m + v])
+    for a, b in zip(*results):
+        assert_bits(a, b, "AdamW: round-robin against XCD-contiguous blocks")
