@@ -227,21 +227,24 @@ __device__ __forceinline__ float psk_exp_np(float x) {
   const float p = __builtin_amdgcn_exp2f(t);
   return (t > -128.0f) ? fmaf(p, r * 0.693147180559945309f, p) : p;
 }
-// a / b for a value b shared by the whole row, given y = 1/b correctly
-// rounded: q = a*y is within an ulp of a/b; the fma gives the exact
-// remainder a - b*q, and one more fma rounds q + remainder*y to the
+// a / b for a value b shared by the whole row, given b's magnitude, the
+// correctly rounded y = 1/|b| and b's sign bit sg: the quotient is
+// (a with sg applied) / |b|, the same value (rounding to nearest is
+// symmetric).  q = a*y is within an ulp of a/|b|; the fma gives the exact
+// remainder a - |b|*q, and one more fma rounds q + remainder*y to the
 // correctly rounded quotient (Markstein's correction).  That holds while
-// b lies in [2^-40, 2^40] and a is zero or in [2^-86, 2^87] (no underflow of
-// the remainder, no overflow of q).  The remainder is formed as
-// -(q*b - a), which is the same value and for a zero a has a's sign, so the
-// correction returns a zero of the right sign with no select.  The range of
-// a group of dividends is gathered two elements an instruction: `lo` keeps
-// the least of (bits(a) << 1) - 2 (the magnitude's bits less one, doubled;
-// a zero wraps to the top, so zeros never count as small), `hi` the largest
-// |a| (an infinity counts; a NaN dividend gives NaN either way).
-// psk_divr_bad then says whether the group must be redone with IEEE
-// division.
-__device__ __forceinline__ float psk_divr(float a, float b, float y, unsigned& lo, float& hi) {
+// |b| lies in [2^-40, 2^40] and a is zero or in [2^-86, 2^87] (no underflow
+// of the remainder, no overflow of q).  For a zero a the remainder, formed
+// as -(q*|b| - a), is -0, and -0 * y added to q leaves q, a zero of a's
+// sign (with a negative y it would not: +0 / -2 would come out +0, hence
+// the positive divisor).  The range of a group of dividends is gathered two
+// elements an instruction: `lo` keeps the least of (bits(a) << 1) - 2 (the
+// magnitude's bits less one, doubled; a zero wraps to the top, so zeros
+// never count as small), `hi` the largest |a| (an infinity counts; a NaN
+// dividend gives NaN either way).  psk_divr_bad then says whether the group
+// must be redone with IEEE division.
+__device__ __forceinline__ float psk_divr(float a, float b, float y, unsigned sg, unsigned& lo, float& hi) {
+  a = __uint_as_float(__float_as_uint(a) ^ sg);
   const float q = a * y;
   const float rem = -fmaf(q, b, -a);
   const unsigned t = (__float_as_uint(a) << 1) - 2u;
@@ -489,8 +492,14 @@ struct Emitter {
         for (size_t j = 0; j < an.nodes.size(); ++j)
             if (an.nodes[j].op == PSK_OP_DIV && an.nodes[j].b == i && !an.is_row[j]) used = true;
         if (!used) return;
+        // the correctly rounded reciprocal; for psk_divr the divisor's
+        // magnitude, its reciprocal's (the same rounding, mirrored) and its
+        // sign bit
         o << "    const float y" << i << " = 1.0f / r" << i << ";\n";
-        o << "    const bool yok" << i << " = fabsf(r" << i << ") >= 0x1p-40f && fabsf(r" << i << ") <= 0x1p40f;\n";
+        o << "    const float ra" << i << " = fabsf(r" << i << ");\n";
+        o << "    const float ya" << i << " = fabsf(y" << i << ");\n";
+        o << "    const unsigned sg" << i << " = __float_as_uint(r" << i << ") & 0x80000000u;\n";
+        o << "    const bool yok" << i << " = ra" << i << " >= 0x1p-40f && ra" << i << " <= 0x1p40f;\n";
     }
 
     // element divided by a row value (a reduction's result, or a scalar)
@@ -576,7 +585,8 @@ struct Emitter {
         case PSK_OP_DIV:
             if (recip_node(i)) return "(" + A() + " * y" + std::to_string(nd.b) + ")";
             if (divr_node(i))
-                return "psk_divr(" + A() + ", " + B() + ", y" + std::to_string(nd.b) + ", lo" + std::to_string(i) +
+                return "psk_divr(" + A() + ", ra" + std::to_string(nd.b) + ", ya" + std::to_string(nd.b) + ", sg" +
+                       std::to_string(nd.b) + ", lo" + std::to_string(i) +
                        ", hi" + std::to_string(i) + ")";
             return "(" + A() + " / " + B() + ")";
         case PSK_OP_MAX: return "psk_max(" + A() + ", " + B() + ")";
@@ -1744,7 +1754,7 @@ struct Emitter {
                 std::string c = "c" + std::to_string(v);
                 std::string cond = "true";
                 if ((int64_t)(v + 1) * L * V > an.cols) cond = c + " < " + std::to_string(an.cols);
-                load_vec((int)k, c, v * V, cond);
+                load_vec((int)k, elem_offset(in, "0", c), v * V, cond);
             }
         }
         o << "    " << I() << " row = (" << I() << ")blockIdx.x;\n";

@@ -273,6 +273,9 @@ def test_division_by_a_row_value_is_ieee_bit_exact(C):
     x[2, ::7] = 1e-30                       # below 2^-86: the IEEE fallback
     x[3, ::11] = -3e38
     x[4] = x[4] * 1e-38                     # subnormal-range numerators
+    x[5, 0] = 3.0                           # so that row 5's divisor is negative (below)
+    x[5, 1::4] = 0.0                        # +0 / negative = -0, -0 / negative = +0
+    x[5, 2::4] = -0.0
     d = torch.ones(R, 1)
     d[5] = -2.0                             # negative divisors after the negation below
     d[6] = 1e30
@@ -289,6 +292,8 @@ def test_division_by_a_row_value_is_ieee_bit_exact(C):
     ref = oracle.eval_group(nodes, [x.numpy(), d.numpy()], (R, C))
     assert_bits(to_np(out), ref, f"x / row value, {C} columns")
     assert (to_np(out)[0, ::3].view(np.uint32) == 0x80000000).all()   # -0 / positive = -0
+    assert (to_np(out)[5, 1::4].view(np.uint32) == 0x80000000).all()  # +0 / negative = -0
+    assert (to_np(out)[5, 2::4].view(np.uint32) == 0).all()           # -0 / negative = +0
     # dividends the divisor does not depend on: infinities, both zeros, and
     # magnitudes on either side of 2^-86 and 2^87 mixed within every vector
     vals = torch.tensor([float("inf"), float("-inf"), 0.0, -0.0, 2.0 ** -86, -(2.0 ** -86) * (1 - 2 ** -24),
@@ -302,6 +307,11 @@ def test_division_by_a_row_value_is_ieee_bit_exact(C):
     _, out2 = run_group(nodes2, [xs.to(DEV), ys.to(DEV)], (R, C), "f32")
     ref2 = oracle.eval_group(nodes2, [xs.numpy(), ys.numpy()], (R, C))
     assert_bits(to_np(out2), ref2, f"special dividends / row value, {C} columns")
+    # the same dividends over negative row values
+    nodes3 = parse_dag("%0 = input 0\n%1 = input 1\n%2 = abs %1\n%3 = row_max %2\n%4 = neg %3\n%5 = div %0 %4\n")
+    _, out3 = run_group(nodes3, [xs.to(DEV), ys.to(DEV)], (R, C), "f32")
+    ref3 = oracle.eval_group(nodes3, [xs.numpy(), ys.numpy()], (R, C))
+    assert_bits(to_np(out3), ref3, f"special dividends / negative row value, {C} columns")
 
 
 def test_persistent_row_layout_is_bit_identical(monkeypatch):

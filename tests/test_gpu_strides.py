@@ -111,3 +111,78 @@ def test_output_inside_a_strided_span_is_refused():
     assert ei.value.status == P.PSK_E_ALIAS
     torch.cuda.synchronize()
     assert not big.any().item(), "nothing was launched"
+
+
+def _strided_copy(x, how, gen):
+    """A view with x's values and shape over a larger buffer: rows padded
+    (row step longer than the row, first element at an offset), every
+    second element of the last axis, or the last two axes stored
+    transposed."""
+    S = tuple(x.shape)
+    if how == "pad":
+        off = int(torch.randint(0, 3, (1,), generator=gen))
+        buf = torch.full(S[:-1] + (S[-1] + 5 + off,), 7.0, device=DEV).to(x.dtype)
+        v = buf[..., off:off + S[-1]]
+    elif how == "step":
+        buf = torch.full(S[:-1] + (2 * S[-1],), 7.0, device=DEV).to(x.dtype)
+        v = buf[..., ::2]
+    else:
+        buf = torch.full(S[:-2] + (S[-1], S[-2]), 7.0, device=DEV).to(x.dtype)
+        v = buf.transpose(-1, -2)
+    v.copy_(x)
+    return v
+
+
+@pytest.mark.parametrize("kind,chunk", [("pw", 0), ("pw", 1), ("row", 0), ("row", 1), ("masked", 0)])
+def test_random_groups_over_strided_views(kind, chunk):
+    """Seeded random groups of exact operations (tests/random_groups.py:
+    pointwise, row, and row under a causal or byte mask) whose float inputs
+    are given as strided views (padded rows at an offset, every second
+    element, transposed storage), against the oracle on the contiguous
+    inputs: bit for bit (bf16 row results within one ulp, as in the dense
+    tests); the buffers around the views unchanged."""
+    import random
+    from tests.random_groups import random_group, random_row_group
+    from tests.test_gpu_random_groups import make_input, same_bits
+    rng = random.Random(6000 + 10 * chunk + len(kind))
+    gen = torch.Generator().manual_seed(6100 + chunk)
+    TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+    for trial in range(8):
+        if kind == "pw":
+            nodes, inputs, shape, dt, ex = random_group(rng)
+            extras = [(m, shape, xdt) for m, xdt in ex]
+        else:
+            nodes, inputs, shape, dt, extras = random_row_group(rng, masks=kind == "masked")
+        dense = [make_input(s, t, gen, False) for s, t in inputs]
+        if kind != "pw":
+            dense = [x if t == "u8" else torch.where(x == 0, torch.ones_like(x), x) for x, (_, t) in zip(dense, inputs)]
+        specs, views = [], []
+        for x, (s, t) in zip(dense, inputs):
+            hows = ["pad", "step"] + (["transpose"] if len(s) >= 2 else [])
+            if t == "u8" or len(s) == 0 or rng.random() < 0.3:
+                specs.append((s, t)); views.append(x)
+                continue
+            v = _strided_copy(x, rng.choice(hows), gen)
+            specs.append((s, t, tuple(v.stride()))); views.append(v)
+        g = P.Group(nodes, specs, shape, dt, root=len(nodes) - 1, extras=extras)
+        out = torch.full(shape, float("nan"), dtype=TD[dt], device=DEV)
+        xs = [torch.full(xsh, float("nan"), dtype=TD[xdt], device=DEV) for _, xsh, xdt in extras]
+        bufs = [to_np(v.as_strided((v.untyped_storage().nbytes() // v.element_size(),), (1,), 0))
+                for v in views if not v.is_contiguous()]
+        g.run(views, out, extra_outs=xs or None)
+        torch.cuda.synchronize()
+        ins = [x.cpu().numpy().view(np.uint8) if x.dtype == torch.uint8 else to_np(x) for x in dense]
+        refx = [(m, np.zeros(xsh, np.float32 if xdt == "f32" else np.uint16)) for m, xsh, xdt in extras]
+        ref = oracle.eval_group(nodes, ins, shape, P.PSK_F32 if dt == "f32" else P.PSK_BF16, root=len(nodes) - 1,
+                                extras=refx)
+        what = f"{kind} chunk {chunk} trial {trial}: kind {g.info.kind} shape {shape} {dt} specs {specs}"
+        for name, got, r in [("root", to_np(out), ref)] + [(f"extra {m}", to_np(x), r) for (m, r), x in zip(refx, xs)]:
+            if got.dtype == np.uint16 and kind != "pw":
+                assert_bf16_close(got, r, f"{what}: {name}")
+            else:
+                ok = same_bits(got, r)
+                assert ok.all(), f"{what}: {name} differs at {int((~ok).sum())} of {ok.size}"
+        after = [to_np(v.as_strided((v.untyped_storage().nbytes() // v.element_size(),), (1,), 0))
+                 for v in views if not v.is_contiguous()]
+        for b, a in zip(bufs, after):
+            assert_bits(a, b, f"{what}: buffer around a view unchanged")
