@@ -218,22 +218,54 @@ def test_random_online_groups(layout, chunk, monkeypatch):
     empties (short rows) hold a NaN sum, as the exact sum is."""
     if layout:
         monkeypatch.setenv("PSK_LAYOUT", layout)
-    rng = random.Random(4000 + chunk)
-    gen = torch.Generator().manual_seed(4100 + chunk)
+    _online_groups(random.Random(4000 + chunk), torch.Generator().manual_seed(4100 + chunk), layout, chunk, False)
+
+
+@pytest.mark.parametrize("chunk", range(2))
+def test_random_online_groups_over_strided_views(chunk):
+    """The same random groups with their float inputs given as strided
+    views (padded rows at an offset, every second element, transposed
+    storage), against the oracle on the contiguous inputs."""
+    _online_groups(random.Random(4500 + chunk), torch.Generator().manual_seed(4600 + chunk), "", chunk, True)
+
+
+def _strided(x, gen, rng):
+    """x's values in a view over a larger buffer (padded rows at an offset,
+    every second element, or the last two axes stored transposed)."""
+    S = tuple(x.shape)
+    how = rng.choice(["pad", "step"] + (["transpose"] if len(S) >= 2 else []))
+    if how == "pad":
+        off = int(torch.randint(0, 3, (1,), generator=gen))
+        v = torch.full(S[:-1] + (S[-1] + 5 + off,), 7.0, device=DEV).to(x.dtype)[..., off:off + S[-1]]
+    elif how == "step":
+        v = torch.full(S[:-1] + (2 * S[-1],), 7.0, device=DEV).to(x.dtype)[..., ::2]
+    else:
+        v = torch.full(S[:-2] + (S[-1], S[-2]), 7.0, device=DEV).to(x.dtype).transpose(-1, -2)
+    v.copy_(x)
+    return v
+
+
+def _online_groups(rng, gen, layout, chunk, strided):
     for trial in range(8):
         nodes, inputs, shape, dt, extras = random_online_group(rng)
         tensors = [_make(s, t, gen) for s, t in inputs]
-        g = P.Group(nodes, inputs, shape, dt, root=len(nodes) - 1, extras=extras, online=True)
+        specs, views = list(inputs), list(tensors)
+        if strided:
+            for k, ((s, t), x) in enumerate(zip(inputs, tensors)):
+                if t != "u8" and len(s) > 0 and rng.random() < 0.7:
+                    views[k] = _strided(x, gen, rng)
+                    specs[k] = (s, t, tuple(views[k].stride()))
+        g = P.Group(nodes, specs, shape, dt, root=len(nodes) - 1, extras=extras, online=True)
         out = torch.full(shape, float("nan"), dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device=DEV)
         xs = [torch.full(xsh, float("nan"), dtype=torch.bfloat16 if xdt == "bf16" else torch.float32, device=DEV)
               for _, xsh, xdt in extras]
-        g.run(tensors, out, extra_outs=xs or None)
+        g.run(views, out, extra_outs=xs or None)
         torch.cuda.synchronize()
         ins = [t.cpu().numpy().view(np.uint8) if t.dtype == torch.uint8 else to_np(t) for t in tensors]
         refx = [(m, np.zeros(xsh, np.float32 if xdt == "f32" else np.uint16)) for m, xsh, xdt in extras]
         ref = oracle.eval_group(nodes, ins, shape, F32 if dt == "f32" else BF16, root=len(nodes) - 1, extras=refx)
         what = (f"{layout or 'default'} chunk {chunk} trial {trial}: kind {g.info.kind} shape {shape} {dt} "
-                f"inputs {inputs} extras {extras} ops {[n.op for n in nodes]}")
+                f"inputs {specs} extras {extras} ops {[n.op for n in nodes]}")
         first_max = next(i for i, n in enumerate(nodes) if n.op == "row_max")
         exact = _Normalized(nodes, ins, shape, extras, g.info)
         exact.check_oracle(ref, shape[-1], f"{what}: the oracle's root")
