@@ -207,7 +207,7 @@ static psk_status split_launch(psk_group* g, Kernel& k, int which, hipFunction_t
                                        "row needs " + std::to_string(K));
     teams = cap / K;
     xmap = 0;
-    if (cap >= 8 * K) {
+    if (cap >= 8 * K && layout_value("xmap", 1)) {
         teams = (cap / (8 * K)) * 8;
         xmap = 1;
     }
