@@ -120,8 +120,28 @@ template <typename T> __device__ __forceinline__ T psk_ld(const T* p) {
   return *p;
 #endif
 }
+// a relaxed store of device scope (the sc1 cache policy), 16 bytes as two
+// of 8
+template <typename T> __device__ __forceinline__ void psk_st_dev(T* p, T v) {
+  if constexpr (sizeof(T) == 16) {
+    unsigned long long* q = (unsigned long long*)p;
+    const psk_u4v w = __builtin_bit_cast(psk_u4v, v);
+    __hip_atomic_store(q, ((unsigned long long)w[1] << 32) | w[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, ((unsigned long long)w[3] << 32) | w[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if constexpr (sizeof(T) == 8) {
+    __hip_atomic_store((unsigned long long*)p, __builtin_bit_cast(unsigned long long, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  } else if constexpr (sizeof(T) == 4) {
+    __hip_atomic_store((unsigned*)p, __builtin_bit_cast(unsigned, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    __hip_atomic_store((unsigned short*)p, __builtin_bit_cast(unsigned short, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
 template <typename T> __device__ __forceinline__ void psk_st(T* p, T v) {
-#if PSK_NT
+#if PSK_SC1
+  psk_st_dev(p, v);
+#elif PSK_NT
   __builtin_nontemporal_store(v, p);
 #else
   *p = v;
@@ -140,7 +160,9 @@ template <typename T> __device__ __forceinline__ T psk_ld(const PSK_G T* p) {
 #endif
 }
 template <typename T> __device__ __forceinline__ void psk_st(PSK_G T* p, T v) {
-#if PSK_NT
+#if PSK_SC1
+  psk_st_dev((T*)p, v);
+#elif PSK_NT
   __builtin_nontemporal_store(v, p);
 #else
   *p = v;
@@ -1081,7 +1103,7 @@ struct Emitter {
     // ------------------------------------------------------------ pointwise
     std::string pointwise(const std::string& name)
     {
-        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n" << kPrelude;
+        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n#define PSK_SC1 " << (pl.sc1 ? 1 : 0) << "\n" << kPrelude;
         signature(name);
         const int V = pl.vec;
         o << "  {\n";
@@ -1130,7 +1152,7 @@ struct Emitter {
     std::string tree(const std::string& name)
     {
         const int TB = pl.block, TS = (int)pl.blocks;
-        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n" << kPrelude;
+        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n#define PSK_SC1 " << (pl.sc1 ? 1 : 0) << "\n" << kPrelude;
         o << "struct psk_leaf_dev { void* slot[" << PSK_MAX_SLOTS << "]; long long flags; };\n";
         o << "struct psk_chunk_dev { int leaf; int count; long long start; };\n";
         o << "extern \"C\" __global__ void __launch_bounds__(" << TB << ") " << name
@@ -1550,7 +1572,7 @@ struct Emitter {
     // extra outputs.
     std::string row_tiled(const std::string& name)
     {
-        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n" << kPrelude;
+        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n#define PSK_SC1 " << (pl.sc1 ? 1 : 0) << "\n" << kPrelude;
         signature(name);
         const int L = pl.lanes, V = pl.vec, TN = pl.nv;
         const int64_t tile = (int64_t)L * TN * V;
@@ -1728,7 +1750,7 @@ struct Emitter {
     // workgroup.
     std::string row_persistent(const std::string& name)
     {
-        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n" << kPrelude;
+        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n#define PSK_SC1 " << (pl.sc1 ? 1 : 0) << "\n" << kPrelude;
         signature(name);
         const int L = pl.lanes, V = pl.vec;
         auto streamed = [&](const InputInfo& in) {
@@ -1831,7 +1853,7 @@ struct Emitter {
     // launch (or graph replay) to the next.
     std::string row_split(const std::string& name)
     {
-        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n" << kPrelude << kSplitPrelude;
+        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n#define PSK_SC1 " << (pl.sc1 ? 1 : 0) << "\n" << kPrelude << kSplitPrelude;
         signature(name);
         const int L = pl.lanes, V = pl.vec, K = pl.split;
         const int64_t S = (int64_t)L * pl.nv * V;
@@ -1902,7 +1924,7 @@ struct Emitter {
     std::string row(const std::string& name)
     {
         if (pl.persist) return row_persistent(name);
-        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n" << kPrelude;
+        o << "#define PSK_NT " << (pl.nt ? 1 : 0) << "\n#define PSK_SC1 " << (pl.sc1 ? 1 : 0) << "\n" << kPrelude;
         signature(name);
         const int L = pl.lanes, V = pl.vec;
         o << "  {\n";

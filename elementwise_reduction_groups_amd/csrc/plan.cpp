@@ -25,6 +25,9 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //     library's), xcd=0|1 (XCD-contiguous block mapping), block=64..1024
 //     (threads per workgroup);
 //   tree kernels: tper=2|4|8|16 (elements per thread);
+//   stores: sc1=0|1 (relaxed stores of device scope instead of nontemporal
+//     ones; 16 bytes go as two of 8), vbytes=8 (8-byte vectors where no
+//     byte mask is read);
 //   the AdamW kernel: axcd=0|1 (XCD-contiguous block mapping);
 //   row kernels: epl (elements of output a lane aims for), lanes=16|32|
 //     64..1024, epmax (most elements a lane holds before the tiled kernel
@@ -61,9 +64,9 @@ int layout_value(const char* key, int dflt)
 std::string KernelPlan::key() const
 {
     char b[200];
-    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d x%d g%lld t%d c%d w%d m%d p%d r%d s%d bn%d fe%d", kind, vec,
-                  block, lanes, nv, (int)nt, (int)xcd, (long long)blocks, tiles, (int)tcache, wpe, wmin, persist, rcache,
-                  lcache, (int)bnt, (int)fexp);
+    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d sc%d x%d g%lld t%d c%d w%d m%d p%d r%d s%d bn%d fe%d", kind,
+                  vec, block, lanes, nv, (int)nt, (int)sc1, (int)xcd, (long long)blocks, tiles, (int)tcache, wpe, wmin,
+                  persist, rcache, lcache, (int)bnt, (int)fexp);
     if (kind == 4) return std::string(b) + " K" + std::to_string(split);
     if (persist) return std::string(b) + " pf" + std::to_string(pf);
     return kind == 3 ? std::string(b) + (alt ? " a1" : " a0") + " u" + std::to_string(munroll) + " y" +
@@ -74,11 +77,19 @@ std::string KernelPlan::key() const
 KernelPlan plan_kernel(const Analysis& an, bool allow_vector, int split_ept)
 {
     KernelPlan p;
-    const int V = an.out_dtype == PSK_BF16 ? 8 : 4;
+    int V = an.out_dtype == PSK_BF16 ? 8 : 4;
+    {
+        // vbytes=8 (measurement): 8-byte vectors, where no byte mask is read
+        // (a mask's vector would be narrower than its 4-byte load)
+        bool u8 = false;
+        for (const InputInfo& in : an.inputs) u8 = u8 || (in.used && in.dtype == PSK_U8);
+        if (layout_value("vbytes", 16) == 8 && !u8 && !an.tree) V /= 2;
+    }
     // 16-byte accesses where every per-element input allows them: a
     // last-axis step of 1 and row starts at whole vectors
     p.vec = (allow_vector && an.cols % V == 0 && inputs_vector_ok(an, V)) ? V : 1;
     p.nt = layout_value("nt", 1) != 0;
+    p.sc1 = layout_value("sc1", 0) != 0;   // trees choose their own below
     p.bnt = layout_value("bnt", 0) != 0;
     p.fexp = layout_value("fexp", 1) != 0;
     if (an.tree) {
@@ -107,6 +118,15 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector, int split_ept)
         p.block = block;
         p.blocks = PSK_TREE_CHUNK / (block * per);   // workgroups per chunk
         p.xcd = layout_value("xcd", 0) != 0;
+        // Stores of device scope (the sc1 cache policy) where every output
+        // moves at most 8 bytes a thread, so that one store instruction
+        // covers whole lines: AdamW as a group (bf16 theta', f32 m', v', 2
+        // elements a thread) 3.06 -> 2.96 ms after the per-group flush and
+        // 3.29 -> 3.00 ms back to back, as for the hand-written kernel; a
+        // 16-byte store split in two 8-byte ones halves SGD's rate
+        int widest = size_of(an.out_dtype);
+        for (const auto& x : an.extras) widest = std::max(widest, size_of(x.dtype));
+        p.sc1 = layout_value("sc1", per * widest <= 8 ? 1 : 0) != 0;
         return p;
     }
     // Pointwise workgroups either reach the XCDs round robin (the

@@ -117,6 +117,7 @@ struct KernelPlan {
                              // lanes * nv * vec columns kept in registers
     int exch = 0;            // split rows: row values exchanged per row (one per reduction)
     bool nt = true;          // nontemporal loads and stores
+    bool sc1 = false;        // stores of device scope (the sc1 cache policy)
     bool bnt = false;        // nontemporal loads also for inputs read again by other rows (broadcast)
     bool fexp = true;        // exp(y - max y) with f32 results by the split-product exponential
     bool xcd = true;         // each XCD takes a contiguous eighth of the blocks

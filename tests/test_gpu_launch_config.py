@@ -58,7 +58,7 @@ def test_tree_group_layouts(monkeypatch):
         torch.cuda.synchronize()
         return [to_np(o) for o in outs]
     run_layouts(make, ["", "tper=4", "tper=8", "tper=16", "block=128", "block=256", "xcd=1", "xcd=1,block=128",
-                       "nt=0"], monkeypatch)
+                       "nt=0", "sc1=1", "sc1=0", "tper=2,sc1=1"], monkeypatch)
     for t, b in zip(theta + grad, before):
         assert_bits(to_np(t), b, "inputs unchanged")
 
