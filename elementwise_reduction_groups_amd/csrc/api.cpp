@@ -194,10 +194,21 @@ static psk_status split_launch(psk_group* g, Kernel& k, int which, hipFunction_t
     {
         std::lock_guard<std::mutex> lk2(k.mu);
         if (!k.capacity[dev]) {
-            int per_cu = 0, cus = 0;
+            int per_cu = 0, cus = 0, regs = 0;
             e = hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, k.plan.block, 0);
             if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            if (e == hipSuccess) e = hipFuncGetAttribute(&regs, HIP_FUNC_ATTRIBUTE_NUM_REGS, fn);
             if (e != hipSuccess) return fail(PSK_E_HIP, std::string("occupancy query: ") + hipGetErrorString(e));
+            // never more than the register file holds by gfx950's rules: 512
+            // registers a lane, allocated in granules of 8, at most 8 waves
+            // a SIMD, a workgroup's waves spread over the CU's 4 SIMDs
+            // (a grid larger than what is resident at once would leave a
+            // team waiting for members that start only as others finish)
+            if (regs > 0) {
+                const int waves_simd = std::min(8, 512 / (((regs + 7) / 8) * 8));
+                const int waves_wg = (k.plan.block + 63) / 64;
+                per_cu = std::min(per_cu, 4 * waves_simd / waves_wg);
+            }
             k.capacity[dev] = per_cu * cus;
         }
     }

@@ -34,7 +34,8 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //     takes over, default 32), persist=k (k persistent workgroups a CU),
 //     pf=1..4 (rows a persistent workgroup loads ahead), tiled=1 (force the
 //     tiled kernel), split=0 (no split rows), sept (elements a lane of a
-//     split row holds), xmap=0|1 (a split row's workgroups on one XCD;
+//     split row holds), slanes=256|512|1024 (lanes of a split row's
+//     workgroup), xmap=0|1 (a split row's workgroups on one XCD;
 //     measured at [8192,131072] f32: 1.461 / 1.457 ms exact, 1.507 / 1.553
 //     ms online with / without);
 //   tiled kernel: lanes=64..1024, tn (vectors a lane per tile), tcache=0|1
@@ -226,7 +227,8 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector, int split_ept)
             }
         const bool wide = (int64_t)p.nv * p.vec > layout_value("epmax", 32);
         if (wide && split_ept != 0 && !layout_value("tiled", 0) && layout_value("split", 1)) {
-            const int Ls = 512;
+            int Ls = layout_value("slanes", 512);
+            if (Ls != 256 && Ls != 512 && Ls != 1024) Ls = 512;
             const bool lean = streamed_inputs <= 1 && streamed_bytes <= 4 && an.mask_period == 0 && an.where_mask < 0;
             const int ept = split_ept > 0 ? split_ept : layout_value("sept", lean ? 64 : 32);
             const int nvs = std::max(1, ept / p.vec);
