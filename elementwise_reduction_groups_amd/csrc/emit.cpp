@@ -184,13 +184,16 @@ __device__ __forceinline__ float psk_rt(float a) { return psk_h(psk_r1(a)); }
 // is the Chebyshev-fitted form of Press, Teukolsky, Vetterling and Flannery,
 // Numerical Recipes (2nd ed.), section 6.2: erfc(w) = t exp(-w^2 + P(t)),
 // t = 1/(1 + w/2), fractional error below 1.2e-7 for all w >= 0.  The
-// exponent z = P(t) - w^2 is formed with one rounding (an fma) and taken to
-// base 2, split into an integer k and |r| <= 1/2 for the hardware 2^x, and
-// scaled back by 2^k (so tiny results come out subnormal, not zero).  The
-// rounding of z costs a relative error of about w^2 2^-24 in erfc, below
-// 6e-7 where |x| < 4.3 and negligible beside gelu's size beyond.  For
-// x > 0, Phi = 1 - erfc(w)/2.  w is clamped at 10, where erfc(w) < 2^-149:
-// Phi is then 0 or 1, also for infinite x (a NaN x stays NaN).
+// exponent z = P(t) - w^2 is formed with one rounding (an fma), taken to
+// base 2 and passed to the hardware 2^x.  The roundings of z and of its
+// base-2 form grow with w^2: against erfc of the same rounded w the result
+// is within 1.2e-6 relative where |x| <= 4.3 (emulated in f32 with a
+// correctly rounded 2^x and reciprocal), negligible beside gelu's size
+// beyond.  Results of 2^x below 2^-126 (|x|
+// above about 13.2) may be flushed to zero: gelu is then below 1e-37 in
+// magnitude, inside the f32 tolerance's absolute part.  For x > 0,
+// Phi = 1 - erfc(w)/2.  w is clamped at 10, where erfc(w) < 2^-149: Phi is
+// then 0 or 1, also for infinite x (a NaN x stays NaN).
 __device__ __forceinline__ float psk_gelu(float x) {
   const float w = fminf(fabsf(x) * 0.70710678118654752440f, 10.0f);
   const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, w, 1.0f));
@@ -198,9 +201,7 @@ __device__ __forceinline__ float psk_gelu(float x) {
   p = fmaf(p, t, -0.82215223f); p = fmaf(p, t, 1.48851587f); p = fmaf(p, t, -1.13520398f);
   p = fmaf(p, t, 0.27886807f);  p = fmaf(p, t, -0.18628806f); p = fmaf(p, t, 0.09678418f);
   p = fmaf(p, t, 0.37409196f);  p = fmaf(p, t, 1.00002368f);  p = fmaf(p, t, -1.26551223f);
-  const float z2 = fmaf(-w, w, p) * 1.44269504088896341f;
-  const float k = __builtin_rintf(z2);
-  const float ec = t * __builtin_ldexpf(__builtin_amdgcn_exp2f(z2 - k), (int)k);
+  const float ec = t * __builtin_amdgcn_exp2f(fmaf(-w, w, p) * 1.44269504088896341f);
   const float phi = (x > 0.0f) ? fmaf(-0.5f, ec, 1.0f) : 0.5f * ec;
   return x * phi;
 }
@@ -224,6 +225,50 @@ __device__ __forceinline__ float psk_gelu_b(float x) {
   const float half_ec = t * (__builtin_amdgcn_exp2f(z) * 0x1p-64f);
   const float phi = (x > 0.0f) ? 1.0f - half_ec : half_ec;
   return x * phi;
+}
+// tanh of a = |x| >= 0 on either side of 0.625.  Below: a + a^3 P(a^2), P
+// of degree 4 fitted here (Lawson-weighted least squares towards minimax
+// relative error on [0, 0.625]; 0.07 ulp as a real polynomial, below 0.75
+// ulp evaluated in f32).  Above: 1 - 2/(1 + e^{2a}), e^{2a} formed as
+// 2^t (1 + r ln 2) with t = fl(2a log2 e) and r its remainder from two fmas
+// (2 log2 e to about 2^-48), so the argument's rounding does not grow with
+// a; with the hardware 2^x and reciprocal each within an ulp the result is
+// within 2.5 ulps (emulated in f32 with both off by an ulp either way).  a
+// is clamped at 16, where tanh rounds to 1, so e stays finite.
+__device__ __forceinline__ float psk_tanh_lo(float a) {
+  const float u = a * a;
+  float p = -0x1.75e62ap-8f;
+  p = fmaf(p, u, 0x1.52279p-6f); p = fmaf(p, u, -0x1.b83c7ep-5f); p = fmaf(p, u, 0x1.110728p-3f);
+  p = fmaf(p, u, -0x1.555532p-2f);
+  return fmaf(a * u, p, a);
+}
+__device__ __forceinline__ float psk_tanh_hi(float a) {
+  const float ac = fminf(a, 16.0f);
+  const float t = ac * 0x1.715476p+1f;
+  const float r = fmaf(ac, 0x1.4ae0cp-25f, fmaf(ac, 0x1.715476p+1f, -t));
+  const float e2 = __builtin_amdgcn_exp2f(t);
+  const float e = fmaf(e2, r * 0x1.62e43p-1f, e2);
+  return fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
+}
+// tanh(x): the side for |x| taken with the sign of x last (-0 stays -0,
+// infinite x gives +-1, a NaN x takes the lower side: NaN).  A wave whose
+// active lanes all fall on one side evaluates that side alone (the test is
+// wave-uniform, so the branch is a scalar one); a mixed wave evaluates both
+// and selects.
+__device__ __forceinline__ float psk_tanh(float x) {
+  const float a = fabsf(x);
+  const bool hi = a >= 0.625f;
+  const unsigned long long m = __builtin_amdgcn_ballot_w64(hi);
+  float r;
+  if (m == 0) r = psk_tanh_lo(a);
+  else if (m == __builtin_amdgcn_read_exec()) r = psk_tanh_hi(a);
+  else r = hi ? psk_tanh_hi(a) : psk_tanh_lo(a);
+  return __builtin_copysignf(r, x);
+}
+// the same values without the wave-uniform test
+__device__ __forceinline__ float psk_tanh_s(float x) {
+  const float a = fabsf(x);
+  return __builtin_copysignf(a >= 0.625f ? psk_tanh_hi(a) : psk_tanh_lo(a), x);
 }
 // exp(x) for an argument known to be <= 0 (an element minus its row's
 // maximum) whose value only reaches bf16 results: 2^(x log2 e + 64) 2^-64,
@@ -619,7 +664,8 @@ struct Emitter {
                                 A() + ")";
         case PSK_OP_LOG: return "logf(" + A() + ")";
         case PSK_OP_SQRT: return "sqrtf(" + A() + ")";
-        case PSK_OP_TANH: return "tanhf(" + A() + ")";
+        case PSK_OP_TANH: return std::string(pl.ftanh == 0 ? "tanhf(" : pl.ftanh == 2 ? "psk_tanh_s(" : "psk_tanh(") +
+                                 A() + ")";
         case PSK_OP_ERF: return "erff(" + A() + ")";
         case PSK_OP_GELU: return (bf16_terminal(i) ? "psk_gelu_b(" : "psk_gelu(") + A() + ")";
         case PSK_OP_SQRTABS: return "sqrtf(fabsf(" + A() + "))";

@@ -22,7 +22,8 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //   every kernel: nt=0|1 (nontemporal accesses), bnt=0|1 (nontemporal loads
 //     also for broadcast inputs, which other rows read again), fexp=0|1
 //     (the split-product exponential for a softmax's f32 exp, else the
-//     library's), xcd=0|1 (XCD-contiguous block mapping), block=64..1024
+//     library's), ftanh=0|1|2 (tanh: the library's, the emitted one, the
+//     emitted one without its wave-uniform branch), xcd=0|1 (XCD-contiguous block mapping), block=64..1024
 //     (threads per workgroup);
 //   tree kernels: tper=2|4|8|16 (elements per thread);
 //   stores: sc1=0|1 (relaxed stores of device scope instead of nontemporal
@@ -45,7 +46,8 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //     loops over tiles read from memory / kept in LDS).
 // A layout never changes which elements are computed; lanes, epl, epmax,
 // tiled, tn and alt change a reduction's bracketing (within tolerance), fexp
-// an exponential's last bits (within tolerance), the others change no bit.
+// an exponential's last bits and ftanh=0 a tanh's (within tolerance), the
+// others change no bit.
 int layout_value(const char* key, int dflt)
 {
     const char* env = std::getenv("PSK_LAYOUT");
@@ -65,9 +67,9 @@ int layout_value(const char* key, int dflt)
 std::string KernelPlan::key() const
 {
     char b[200];
-    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d sc%d x%d g%lld t%d c%d w%d m%d p%d r%d s%d bn%d fe%d", kind,
-                  vec, block, lanes, nv, (int)nt, (int)sc1, (int)xcd, (long long)blocks, tiles, (int)tcache, wpe, wmin,
-                  persist, rcache, lcache, (int)bnt, (int)fexp);
+    std::snprintf(b, sizeof b, "k%d v%d b%d l%d n%d nt%d sc%d x%d g%lld t%d c%d w%d m%d p%d r%d s%d bn%d fe%d ft%d",
+                  kind, vec, block, lanes, nv, (int)nt, (int)sc1, (int)xcd, (long long)blocks, tiles, (int)tcache,
+                  wpe, wmin, persist, rcache, lcache, (int)bnt, (int)fexp, ftanh);
     if (kind == 4) return std::string(b) + " K" + std::to_string(split);
     if (persist) return std::string(b) + " pf" + std::to_string(pf);
     return kind == 3 ? std::string(b) + (alt ? " a1" : " a0") + " u" + std::to_string(munroll) + " y" +
@@ -93,6 +95,8 @@ KernelPlan plan_kernel(const Analysis& an, bool allow_vector, int split_ept)
     p.sc1 = layout_value("sc1", 0) != 0;   // trees choose their own below
     p.bnt = layout_value("bnt", 0) != 0;
     p.fexp = layout_value("fexp", 1) != 0;
+    p.ftanh = layout_value("ftanh", 1);
+    if (p.ftanh < 0 || p.ftanh > 2) p.ftanh = 1;
     if (an.tree) {
         // Each thread takes `vec` consecutive elements, the fewest of 2, 4,
         // 8, 16 that move at least 40 bytes.  Measured on the 887M-element

@@ -120,6 +120,7 @@ struct KernelPlan {
     bool sc1 = false;        // stores of device scope (the sc1 cache policy)
     bool bnt = false;        // nontemporal loads also for inputs read again by other rows (broadcast)
     bool fexp = true;        // exp(y - max y) with f32 results by the split-product exponential
+    int ftanh = 1;           // tanh: 1 the emitted one, 2 its branch-free form, 0 the device library's
     bool xcd = true;         // each XCD takes a contiguous eighth of the blocks
     int64_t blocks = 0;      // workgroups that carry work
     int64_t per_xcd = 0;     // blocks per XCD (xcd layout)

@@ -448,3 +448,87 @@ def test_split_product_exponential_within_three_ulps():
     assert err.max() <= 3.0, f"split-product exponential: {err.max():.2f} ulps"
     assert np.all(np.abs(got[~normal] - ref[~normal]) <= 2.0 ** -126)
     assert np.all(got[:, 1] == 0.0)
+
+
+@pytest.mark.gpu
+def test_emitted_tanh_within_three_ulps():
+    """The emitted tanh (polynomial below |x| = 0.625, 1 - 2/(1 + e^{2|x|})
+    above): against float64 tanh of the same f32 arguments, within 3 f32
+    ulps wherever the result is normal (the f32 emulation with the hardware
+    2^x and reciprocal off by an ulp gives 2.45), odd in x bit for bit, ±0
+    kept, ±inf to ±1, NaN to NaN; subnormal results within 2^-126 (they
+    may be flushed, as the f32 tolerance's absolute part allows)."""
+    nodes = parse_dag("%0 = input 0\n%1 = tanh %0\n")
+    rng = np.random.default_rng(47)
+    n = 1 << 22
+    x = np.concatenate([
+        rng.uniform(-1.0, 1.0, n // 4), rng.uniform(-20.0, 20.0, n // 4),
+        np.linspace(0.6, 0.65, n // 8), -np.linspace(0.6, 0.65, n // 8),      # either side of the split
+        np.exp(rng.uniform(np.log(1e-30), np.log(1e-3), n // 4)) * rng.choice([-1.0, 1.0], n // 4)]).astype(np.float32)
+    specials = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 0.625, -0.625, np.nextafter(np.float32(0.625), np.float32(0)),
+                         1e-40, -1e-40, 9.0, 16.0, 17.0, 1e30, -1e30], dtype=np.float32)
+    x = np.concatenate([x, specials])
+    g = P.Group(nodes, [((x.size,), "f32")], (x.size,), "f32")
+    assert "psk_tanh(" in P.psk_group_source(g.desc)
+    out = torch.full((x.size,), float("nan"), device=DEV)
+    g.run([torch.from_numpy(x).to(DEV)], out)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    ref = np.tanh(x.astype(np.float64))
+    fin = np.isfinite(x)
+    normal = fin & (np.abs(ref) >= 2.0 ** -126)
+    ulp = np.spacing(np.abs(ref[normal]).astype(np.float32)).astype(np.float64)
+    err = np.abs(got[normal].astype(np.float64) - ref[normal]) / ulp
+    assert err.max() <= 3.0, f"tanh: {err.max():.2f} ulps at x = {x[normal][err.argmax()]!r}"
+    sub = fin & ~normal                      # tanh(x) is x there; subnormals may be flushed
+    assert np.all(np.abs(got[sub].astype(np.float64) - x[sub]) <= 2.0 ** -126)
+    k = x.size - specials.size
+    s = got[k:]
+    assert s[0] == 0.0 and not np.signbit(s[0]) and s[1] == 0.0 and np.signbit(s[1])
+    assert s[2] == 1.0 and s[3] == -1.0 and np.isnan(s[4])
+    assert np.all(s[11:13] == 1.0) and s[13] == 1.0 and s[14] == -1.0
+    # odd: tanh(-x) is -tanh(x) bit for bit
+    h = k // 2
+    neg = P.Group(nodes, [((h,), "f32")], (h,), "f32")
+    o2 = torch.full((h,), float("nan"), device=DEV)
+    neg.run([torch.from_numpy(-x[:h]).to(DEV)], o2)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(o2).view(np.uint32), (-got[:h]).view(np.uint32))
+
+
+@pytest.mark.gpu
+def test_emitted_gelu_within_its_bound():
+    """The emitted f32 gelu (x Phi(x), Phi from the Chebyshev-fitted erfc,
+    fractional error 1.2e-7, and a rounded exponent whose error grows with
+    w^2): against x erfc(-w)/2 in float64, w = x/sqrt 2 rounded to f32 as the
+    oracle rounds it, relative error below 2e-6 where |x| <= 4.3 (1.2e-6 in
+    an f32 emulation with a correctly rounded 2^x and reciprocal; the
+    hardware's add about an ulp each), and within the f32 tolerance (1e-7 +
+    2e-6 |ref|) of the unrounded definition everywhere; ±0 keep their sign,
+    +inf gives +inf, NaN gives NaN."""
+    from scipy.special import erfc
+    nodes = parse_dag("%0 = input 0\n%1 = gelu %0\n")
+    rng = np.random.default_rng(53)
+    n = 1 << 22
+    x = np.concatenate([rng.uniform(-4.3, 4.3, n // 2), rng.uniform(-30.0, 30.0, n // 4),
+                        rng.normal(0.0, 1.0, n // 4)]).astype(np.float32)
+    specials = np.array([0.0, -0.0, np.inf, np.nan], dtype=np.float32)
+    x = np.concatenate([x, specials])
+    g = P.Group(nodes, [((x.size,), "f32")], (x.size,), "f32")
+    assert "psk_gelu(" in P.psk_group_source(g.desc)
+    out = torch.full((x.size,), float("nan"), device=DEV)
+    g.run([torch.from_numpy(x).to(DEV)], out)
+    torch.cuda.synchronize()
+    got = to_np(out).astype(np.float64)
+    xd = x.astype(np.float64)
+    ref = 0.5 * xd * erfc(-xd / np.sqrt(2.0))
+    fin = np.isfinite(x)
+    assert np.all(np.abs(got[fin] - ref[fin]) <= 1e-7 + 2e-6 * np.abs(ref[fin]))
+    w32 = (x * np.float32(0.70710678118654752440)).astype(np.float64)
+    ref32 = 0.5 * xd * erfc(-w32)
+    mid = fin & (np.abs(xd) <= 4.3) & (ref32 != 0)
+    rel = np.abs(got[mid] - ref32[mid]) / np.abs(ref32[mid])
+    assert rel.max() <= 2e-6, f"gelu: relative error {rel.max():.3g} at x = {x[mid][rel.argmax()]!r}"
+    s = got[-4:]
+    assert s[0] == 0.0 and not np.signbit(s[0]) and s[1] == 0.0 and np.signbit(s[1])
+    assert s[2] == np.inf and np.isnan(s[3])
