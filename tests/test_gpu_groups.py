@@ -349,6 +349,43 @@ def test_persistent_row_layout_is_bit_identical(monkeypatch):
                 assert_bits(a, b, f"persistent layout, {shape}")
 
 
+@pytest.mark.gpu
+def test_layernorm_many_rows_two_a_workgroup(monkeypatch):
+    """Past 32 rows a persistent workgroup the planner gives LayerNorm two
+    rows a 512-thread workgroup (an odd row count leaves the last
+    workgroup one row): the bits of one row a workgroup and of the
+    persistent kernel, and every statistic and sampled rows against the
+    oracle."""
+    R, C = 32 * 1024 + 3, 4096
+    xl, gl, bl = configs.layernorm_inputs(R, C, device=DEV, seed=11)
+    nodes, ins = configs.layernorm_dag(EPS), [((R, C), "bf16"), ((C,), "bf16"), ((C,), "bf16")]
+    kw = dict(root=configs.LAYERNORM_ROOT, extras=[(configs.LAYERNORM_MEAN, (R, 1), "f32"),
+                                                   (configs.LAYERNORM_RSTD, (R, 1), "f32")])
+    from tests.test_gpu_multi import assert_layernorm_close, check_stats
+    outs, info = [], None
+    for layout in ("", "persist=0,block=256", "persist=4"):
+        monkeypatch.setenv("PSK_LAYOUT", layout)
+        grp = P.Group(nodes, ins, (R, C), "bf16", **kw)
+        if not layout:
+            src = P.psk_group_source(grp.desc)
+            assert "__launch_bounds__(512)" in src and "gridDim" not in src[src.index('extern "C"'):]
+            info = grp.info
+        out = torch.full((R, C), float("nan"), dtype=torch.bfloat16, device=DEV)
+        ex = [torch.full((R, 1), float("nan"), device=DEV) for _ in range(2)]
+        grp.run([xl, gl, bl], out, extra_outs=ex)
+        torch.cuda.synchronize()
+        outs.append((out, ex[0], ex[1]))
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert_bits(to_np(a), to_np(b), "LayerNorm, two rows a workgroup")
+    rows = torch.tensor(np.r_[0:3, R // 2 - 1:R // 2 + 2, R - 3:R], device=DEV)
+    xr = xl[rows].contiguous()
+    ref = oracle.eval_group(nodes, [to_np(xr), to_np(gl), to_np(bl)], (rows.numel(), C), 1,
+                            root=configs.LAYERNORM_ROOT)
+    assert_layernorm_close(to_np(outs[0][0][rows]), ref, xr, gl, bl, C, "LayerNorm rows vs oracle")
+    check_stats(info, xr, outs[0][1][rows], outs[0][2][rows], C, "LayerNorm statistics, two rows a workgroup")
+
+
 def test_signed_zeros_through_fused_expressions():
     """0 - x is +0 for x = +0 also when another member reads it (the compiler
     must not turn it into -x), x + 0 is +0 for x = -0: every sign of zero the
